@@ -1,0 +1,128 @@
+"""Dion3 row-subsampled update with error feedback, written from the pages.
+
+Sources:
+  * "Dion3：全栈正交更新" (paper.rainbus.top), section 方法步骤详情, Algorithm 4:
+    M <- M + G; pick the k = ceil(f n) rows of largest l1 norm (index set S);
+    orthogonalise the submatrix M[S, :] with Gram NS; decay the weights
+    W <- (1 - lr wd) W; update the selected weight rows W[S, :] <- W[S, :] - lr O;
+    error feedback decays only the selected momentum rows, M[S, :] <- mu M[S, :].
+  * Same page, section 前置知识 (error feedback): M <- mu M_hat + (M - M_hat), where
+    M_hat keeps only the selected rows; unselected rows keep their value.
+  * Same page, 核心方法: the learning rate is rescaled as lr = eta / sqrt(f).
+  * "Dion3: Full-Stack Orthogonal Updates" (m.montaan.com): f = 1 is Muon.
+
+Storage model (the pages leave rounding open; the reading stated here is the one the
+GPU path follows): W, M, G are stored in bf16.  Every stored result is rounded once
+to bf16 (nearest, ties to even).  The element-wise updates are carried out in fp32
+op by op (numpy float32 arithmetic, each operation correctly rounded, no fused
+multiply-add).  Row scores are sums in float64 of the stored (rounded) values.
+
+Two storage modes:
+  storage="bf16"  the model above (what the GPU computes);
+  storage="f64"   no rounding anywhere (used to pin f = 1 against Muon exactly).
+
+Parity status: select_topk pinned by brute force; accumulate / error_feedback /
+weight_update pinned by their bit-level definitions and invariants; dion3_step
+pinned by the f = 1 == Muon identity and the error-feedback invariants.
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+from .bf16 import bf16_to_f64, f64_to_bf16_rne
+from .newton_schulz import newton_schulz, JORDAN_ABC, EPS
+
+
+def k_from_fraction(f, n: int) -> int:
+    """k = ceil(f n), computed exactly (f may be a float such as 0.25 or 1/8)."""
+    from fractions import Fraction
+    return int(math.ceil(Fraction(f).limit_denominator(1 << 20) * n))
+
+
+def accumulate(m_bits, g_bits):
+    """M <- bf16(M + G).  The fp64 sum of two bf16 values rounded once more to bf16
+    equals the correctly rounded bf16 sum (binary64 has at least 2*8+2 bits)."""
+    return f64_to_bf16_rne(bf16_to_f64(m_bits) + bf16_to_f64(g_bits))
+
+
+def row_scores(m_bits, norm="l1"):
+    """Per-row score of the stored momentum: sum_j |M_ij| (l1) or sum_j M_ij^2 (l2),
+    each the correctly rounded float64 value of the exact sum (math.fsum)."""
+    x = bf16_to_f64(m_bits)
+    terms = np.abs(x) if norm == "l1" else x * x      # squares of bf16 values are exact
+    return np.array([math.fsum(row) for row in terms], dtype=np.float64)
+
+
+def select_topk(scores, k: int):
+    """Indices of the k largest scores, ties broken toward the lower index, returned
+    in ascending index order."""
+    scores = [float(s) for s in scores]
+    order = sorted(range(len(scores)), key=lambda i: (-scores[i], i))
+    return np.array(sorted(order[:k]), dtype=np.int64)
+
+
+def gather_rows(m_bits, S):
+    return np.asarray(m_bits)[np.asarray(S)]
+
+
+def error_feedback(m_bits, S, mu):
+    """M[S, :] <- bf16(fl32(mu) * M[S, :]); other rows unchanged."""
+    out = np.array(m_bits, dtype=np.uint16, copy=True)
+    mu32 = np.float32(mu)
+    rows = bf16_to_f64(out[S]).astype(np.float32)
+    out[S] = f64_to_bf16_rne((mu32 * rows).astype(np.float64))
+    return out
+
+
+def weight_update(w_bits, S, o, lr, wd):
+    """Decoupled weight decay on all rows and the orthogonalised update on rows S.
+
+    d = fl32(1 - fl32(lr * wd));
+    W[S]     <- bf16( fl32( fl32(d * W[S]) - fl32(lr * O) ) )
+    W[not S] <- W                     if wd == 0
+                bf16( fl32(d * W) )   otherwise
+    o: the update rows, [k, m] float values (as stored by the caller, e.g. bf16)."""
+    out = np.array(w_bits, dtype=np.uint16, copy=True)
+    lr32, wd32 = np.float32(lr), np.float32(wd)
+    d = np.float32(np.float32(1.0) - lr32 * wd32)
+    o32 = np.asarray(o, dtype=np.float64).astype(np.float32)
+    if wd32 != 0:
+        allw = bf16_to_f64(out).astype(np.float32)
+        out = f64_to_bf16_rne((d * allw).astype(np.float64))
+    wsel = bf16_to_f64(np.asarray(w_bits)[S]).astype(np.float32)
+    upd = (d * wsel) - (lr32 * o32)
+    out[S] = f64_to_bf16_rne(upd.astype(np.float64))
+    return out
+
+
+def dion3_step(w, m, g, k, lr, wd=0.0, mu=0.95, norm="l1", steps=5, abc=JORDAN_ABC,
+               eps=EPS, storage="bf16", orthogonalize=None):
+    """One Dion3 step.  Returns (W', M', S, O) where O is the orthogonalised
+    submatrix (float64) of the selected rows.
+
+    storage="bf16": w, m, g are uint16 bf16 bit patterns, results likewise.
+    storage="f64":  w, m, g are float64 arrays and nothing is rounded.
+    orthogonalize: function X -> O (default: standard Newton-Schulz, the oracle of
+    record for Gram NS, which it equals in exact arithmetic)."""
+    ortho = orthogonalize or (lambda x: newton_schulz(x, steps, abc, eps))
+    if storage == "f64":
+        m1 = np.asarray(m, np.float64) + np.asarray(g, np.float64)
+        terms = np.abs(m1) if norm == "l1" else m1 * m1
+        scores = np.array([math.fsum(r) for r in terms])
+        S = select_topk(scores, k)
+        O = ortho(m1[S])
+        w1 = (1.0 - lr * wd) * np.asarray(w, np.float64)
+        w1[S] = w1[S] - lr * O
+        m2 = m1.copy()
+        m2[S] = mu * m1[S]
+        return w1, m2, S, O
+    m1 = accumulate(m, g)
+    scores = row_scores(m1, norm)
+    S = select_topk(scores, k)
+    X = bf16_to_f64(gather_rows(m1, S))
+    O = ortho(X)
+    O_stored = bf16_to_f64(f64_to_bf16_rne(O))
+    w2 = weight_update(w, S, O_stored, lr, wd)
+    m2 = error_feedback(m1, S, mu)
+    return w2, m2, S, O

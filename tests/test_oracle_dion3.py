@@ -1,0 +1,145 @@
+"""Pins for the oracle's Dion3 step:
+
+* top-k selection against brute force over all k-subsets on tiny inputs with ties;
+* bf16 accumulate / error feedback / weight update against torch's CPU bf16 and fp32
+  arithmetic (independent library routines);
+* the error-feedback invariant (unselected momentum rows untouched, selected rows
+  decayed by mu) from the Dion3 page, 前置知识 (error feedback) / Algorithm 4;
+* f = 1 reproduces Muon's momentum recursion M <- mu M + G exactly (float64),
+  stated on the Dion3 summary page (m.montaan.com).
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import (accumulate, row_scores, select_topk, error_feedback, weight_update,
+                    dion3_step, newton_schulz, bf16_to_f64, f64_to_bf16_rne, k_from_fraction)
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")))
+
+
+def tbf(bits):
+    return torch.from_numpy(np.asarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def bits_of(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def brute_topk(scores, k):
+    n = len(scores)
+    valid = []
+    for S in itertools.combinations(range(n), k):
+        s = set(S)
+        ok = all((scores[i] > scores[j]) or (scores[i] == scores[j] and i < j)
+                 for i in s for j in range(n) if j not in s)
+        if ok:
+            valid.append(S)
+    assert len(valid) == 1
+    return np.array(valid[0])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    n = 9
+    scores = rng.integers(0, 4, size=n).astype(np.float64)   # many ties
+    for k in (1, 3, 5, 9):
+        assert np.array_equal(select_topk(scores, k), brute_topk(list(scores), k))
+
+
+def test_k_rule():
+    assert k_from_fraction(0.25, 8192) == 2048
+    assert k_from_fraction(1 / 8, 8192) == 1024
+    assert k_from_fraction(0.3, 10) == 3
+    assert k_from_fraction(0.31, 10) == 4
+    assert k_from_fraction(1.0, 77) == 77
+
+
+def test_accumulate_matches_torch_bf16_add():
+    rng = np.random.default_rng(1)
+    m = synth.to_storage(rng.standard_normal((64, 300)) * 0.02, "bf16")
+    g = synth.to_storage(rng.standard_normal((64, 300)) * np.exp(rng.uniform(-20, 5, (64, 300))), "bf16")
+    ref = bits_of(tbf(m) + tbf(g))          # torch: fp32 add, one rounding to bf16
+    assert np.array_equal(accumulate(m, g), ref)
+
+
+def test_row_scores():
+    rng = np.random.default_rng(2)
+    m = synth.to_storage(rng.standard_normal((32, 1000)) * 0.02, "bf16")
+    x = bf16_to_f64(m)
+    assert np.allclose(row_scores(m, "l1"), np.abs(x).sum(1), rtol=1e-13, atol=0)
+    assert np.allclose(row_scores(m, "l2"), (x * x).sum(1), rtol=1e-13, atol=0)
+    small = synth.to_storage(np.array([[1.0, -2.0, 0.5], [0.0, 0.0, -3.0]]), "bf16")
+    assert list(row_scores(small, "l1")) == [3.5, 3.0]
+    assert list(row_scores(small, "l2")) == [5.25, 9.0]
+
+
+def test_error_feedback_matches_torch():
+    rng = np.random.default_rng(3)
+    m = synth.to_storage(rng.standard_normal((40, 256)) * 0.02, "bf16")
+    S = np.array([0, 3, 7, 39])
+    out = error_feedback(m, S, 0.95)
+    ref = tbf(m).clone()
+    ref[S] = (torch.tensor(0.95, dtype=torch.float32) * tbf(m)[S].float()).to(torch.bfloat16)
+    assert np.array_equal(out, bits_of(ref))
+    rest = np.setdiff1d(np.arange(40), S)
+    assert np.array_equal(out[rest], m[rest])
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_weight_update_matches_torch(wd):
+    rng = np.random.default_rng(4)
+    w = synth.to_storage(rng.standard_normal((30, 128)) * 0.02, "bf16")
+    S = np.array([1, 2, 10, 29])
+    o = bf16_to_f64(synth.to_storage(rng.standard_normal((4, 128)) * 0.1, "bf16"))
+    lr = 0.02
+    out = weight_update(w, S, o, lr, wd)
+    f = torch.float32
+    lr_t, wd_t = torch.tensor(lr, dtype=f), torch.tensor(wd, dtype=f)
+    d = torch.tensor(1.0, dtype=f) - lr_t * wd_t
+    wt = tbf(w).float()
+    ref = (d * wt).to(torch.bfloat16) if wd else tbf(w).clone()
+    upd = d * wt[S] - lr_t * torch.from_numpy(o).to(f)
+    ref[S] = upd.to(torch.bfloat16)
+    assert np.array_equal(out, bits_of(ref))
+
+
+def test_dion3_error_feedback_invariants():
+    w, g, m = synth.dion3_state(n=48, m=256, seed=5)
+    k = k_from_fraction(0.25, 48)
+    w2, m2, S, O = dion3_step(w, m, g, k, lr=0.02, wd=0.0, mu=0.95)
+    m1 = accumulate(m, g)
+    rest = np.setdiff1d(np.arange(48), S)
+    assert np.array_equal(m2[rest], m1[rest])               # unselected rows keep M + G
+    assert np.array_equal(m2[S], error_feedback(m1, S, 0.95)[S])
+    assert np.array_equal(w2[rest], w[rest])                 # wd = 0: unselected W untouched
+    assert len(S) == k and np.all(np.diff(S) > 0)
+    # the selected rows are those with the largest l1 norms of M + G
+    sc = np.abs(bf16_to_f64(m1)).sum(1)
+    assert sc[S].min() >= sc[rest].max()
+    assert np.allclose(O, newton_schulz(bf16_to_f64(m1[S])), rtol=0, atol=1e-15)
+
+
+def test_f_equals_one_is_muon():
+    assert GOLD["f_equals_one_is_muon"]["value"] is True
+    rng = np.random.default_rng(6)
+    n, mm, mu, lr = 12, 40, 0.95, 0.01
+    w = rng.standard_normal((n, mm))
+    state = np.zeros((n, mm))
+    w_muon, m_muon = w.copy(), np.zeros((n, mm))
+    for step in range(3):
+        g = rng.standard_normal((n, mm))
+        w, state, S, O = dion3_step(w, state, g, k=n, lr=lr, wd=0.0, mu=mu, storage="f64")
+        m_muon = mu * m_muon + g                 # Muon's heavy-ball momentum
+        o_muon = newton_schulz(m_muon)
+        w_muon = w_muon - lr * o_muon
+        assert np.array_equal(S, np.arange(n))
+        assert np.allclose(O, o_muon, rtol=0, atol=1e-12)
+        assert np.allclose(w, w_muon, rtol=0, atol=1e-12)
