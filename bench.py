@@ -1,0 +1,233 @@
+"""Benchmark of the Gram Newton-Schulz hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--compute f16|bf16]
+                    [--no-cpu-baseline] [--gpus 1]
+
+Default workload: one 1024 x 4096 bf16 momentum matrix (aspect ratio 4), Gram NS with
+T = 5 quintic steps of (3.4445, -4.7750, 2.0315), restart after step 2, fp16 iterates
+with fp32 accumulation.  A step is one gns_orthogonalize_batched call over the batch;
+inputs are resident in HBM before the timed region.  One JSON line is printed.
+
+Also measured in the same run:
+  * roofline of the dominant kernel (the lower-tile symmetric MFMA product), timed
+    live with HIP events by replaying its per-step launch mix through the C ABI;
+  * the standard-NS baseline on the same kernels;
+  * cpu_baseline: the float64 numpy oracle on the host cores, on a bounded sample.
+Other workloads (--workload) print the same line for that workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "orthogonalized matrices/s + TFLOP/s (% bf16 MFMA peak), batched Gram NS, α=4"
+PEAK_16BIT_TFLOPS = 2516.6        # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="gns_1024x4096_bf16")
+    p.add_argument("--compute", default="f16")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "
+              "requested). The batch dimension would shard across GPUs; see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import muon_gram_ns_amd as gns
+    import synth
+    from muon_gram_ns_amd import flops as F
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.workload(args.workload)
+    if w.name.startswith("dion3"):
+        return bench_dion3(args, w)
+
+    st = synth.gns_batch(w)
+    if w.dtype == "bf16":
+        X = torch.from_numpy(st.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        X = torch.from_numpy(st).to(dev)
+    B, n, m = X.shape
+    compute = args.compute if w.dtype != "f32" else "f32"
+    out = torch.empty_like(X)
+    sched = gns.default_schedule()
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gns.orthogonalize(X, out=out, compute=compute, schedule=sched)
+
+    _, issued = gns.orthogonalize(X, out=out, compute=compute, schedule=sched, return_flops=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = 1e3 * elapsed / args.steps
+    mats_per_s = B * args.steps / elapsed
+    square = (n == m) and sched.square_fallback
+    alg = B * (F.standard_schedule(n, m) if square else F.gram_schedule(n, m))
+    nominal = B * F.standard_ns_nominal(n, m)
+
+    # standard-NS baseline on the same kernels
+    for _ in range(max(2, args.warmup // 4)):
+        gns.newton_schulz(X, out=out, compute=compute, schedule=sched)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nstd = max(10, args.steps // 4)
+    for _ in range(nstd):
+        gns.newton_schulz(X, out=out, compute=compute, schedule=sched)
+    torch.cuda.synchronize()
+    ms_std = 1e3 * (time.perf_counter() - t1) / nstd
+
+    roof = dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, args.steps)
+    line = {
+        "metric": METRIC,
+        "value": round(mats_per_s, 3),
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f16": "fp16", "bf16": "bf16", "f32": "fp32"}[compute],
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "n": n, "m": m, "alpha": m / n, "T": sched.steps,
+                   "restart_after": [s for s in range(1, 16) if (sched.restart_after_mask >> s) & 1],
+                   "input_dtype": w.dtype, "iterate_dtype": compute, "accumulate": "fp32",
+                   "method": "standard NS (aspect ratio 1 fallback)" if square else "Gram NS"},
+        "tflops_standard_ns_equivalent": round(nominal / (ms * 1e-3) / 1e12, 3),
+        "tflops_algorithmic": round(alg / (ms * 1e-3) / 1e12, 3),
+        "tflops_issued": round(issued / (ms * 1e-3) / 1e12, 3),
+        "pct_peak_issued": round(100 * issued / (ms * 1e-3) / 1e12 / PEAK_16BIT_TFLOPS, 3),
+        "standard_ns_same_kernels": {"ms_per_step": round(ms_std, 5),
+                                     "matrices_per_s": round(B / (ms_std * 1e-3), 3),
+                                     "gram_speedup": round(ms_std / ms, 3)},
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(st, w, args.cpu_seconds),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps):
+    """The lower-tile symmetric MFMA product in the iterate dtype dominates a Gram NS
+    call.  Replay its per-call launch mix (the n x n products with K = n, plus the
+    restart Gram product with K = m) through symm_gemm on the current stream and time
+    it with HIP events; achieved = algorithmic flops per launch / average launch."""
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[compute]
+    # Gram NS (T=5, restart after 2), n x n products per call: t1: Z, Y, R (3); t2: Z, Q (2);
+    # t3: Z, Y, R (3); t4: Z, Q, Y, R (4); t5: Z, Q (2) = 14; plus the Gram product of the
+    # restarted X (K = m).  Standard NS: per step one X X^T (K = m) and one A A (K = n).
+    nn_k, mm_k = (5, 5) if square else (14, 1)
+    R = torch.randn(B, n, n, device="cuda").to(dt)
+    R = (R + R.transpose(1, 2)) * 0.5
+    Xh = (torch.randn(B, n, m, device="cuda") / m ** 0.5).to(dt)
+    D = torch.empty(B, n, n, device="cuda", dtype=dt)
+
+    def mix():
+        for _ in range(nn_k):
+            gns.symm_gemm(R, R, C=R, alpha=2.0, beta=-4.0, out=D)
+        for _ in range(mm_k):
+            gns.symm_gemm(Xh, Xh, out=D)
+
+    reps = max(5, steps // 4)
+    for _ in range(3):
+        mix()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        mix()
+    e.record()
+    torch.cuda.synchronize()
+    launches = reps * (nn_k + mm_k)
+    avg_s = s.elapsed_time(e) * 1e-3 / launches
+    alg_per_launch = B * (nn_k * F.sym(n, n) + mm_k * F.sym(n, m)) / (nn_k + mm_k)
+    achieved = alg_per_launch / avg_s / 1e12
+    return {"bound": "mfma", "kernel": f"gemm_kernel<{compute}, lower-triangle symmetric>",
+            "shape_mix": f"{nn_k} x (n={n}, K={n}) + {mm_k} x (n={n}, K={m}) per call, batch {B}",
+            "avg_launch_us": round(avg_s * 1e6, 3),
+            "achieved": round(achieved, 3), "peak": PEAK_16BIT_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_16BIT_TFLOPS, 5), "traffic": None}
+
+
+def cpu_baseline(st, w, seconds):
+    """The float64 oracle (standard NS) on the host, on a bounded sample."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    x = oracle.bf16_to_f64(st[0]) if w.dtype == "bf16" else st[0].astype(np.float64)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle.newton_schulz(x)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= 1000:
+            break
+    return {"value": round(done / el, 4), "unit": "matrices/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} x one {w.n}x{w.m} matrix of the workload, float64 standard NS (numpy/OpenBLAS), "
+                      f"{el:.1f} s"}
+
+
+def bench_dion3(args, w):
+    import numpy as np
+    import torch
+    import muon_gram_ns_amd as gns
+    import synth
+    from muon_gram_ns_amd import flops as F
+    wb, gb, mb = synth.dion3_state()
+    tb = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    W, M, G = tb(wb), tb(mb), tb(gb)
+    N, m = W.shape
+    res = {}
+    for f in (0.25, 0.125):
+        k = int(round(f * N))
+        lr = 0.01 / f ** 0.5
+        for _ in range(args.warmup):
+            gns.dion3_step(W, M, G, k, lr, 0.0, 0.95, score_norm=2, compute=args.compute)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            gns.dion3_step(W, M, G, k, lr, 0.0, 0.95, score_norm=2, compute=args.compute)
+        torch.cuda.synchronize()
+        ms = 1e3 * (time.perf_counter() - t0) / args.steps
+        res[f] = {"k": k, "ms_per_step": round(ms, 4), "gram_tflops_algorithmic":
+                  round(F.gram_schedule(k, m) / (ms * 1e-3) / 1e12, 2)}
+    ms = res[0.25]["ms_per_step"]
+    print(json.dumps({"metric": "Dion3 steps/s", "value": round(1e3 / ms, 3), "unit": "steps/s", "n_gpus": 1,
+                      "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": args.compute, "data": "synthetic",
+                      "config": {"workload": w.name, "N": N, "m": m, "score": "l2", "fractions": res},
+                      "roofline": None, "cpu_baseline": None}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

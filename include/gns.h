@@ -1,0 +1,198 @@
+/*
+ * gns.h - C ABI of the MI355X (gfx950) Gram Newton-Schulz / Dion3 library (libgns.so).
+ *
+ * What the library computes (sources are the pages on the Dion3 method):
+ *   - Muon's orthogonalisation step, computed by Gram Newton-Schulz: normalise X by
+ *     its Frobenius norm, form the Gram matrix R = X X^T, run T quintic steps on the
+ *     small n x n iterates with a restart, apply the result once as Q X.
+ *     ["Dion3: Full-Stack Orthogonal Updates", paper.rainbus.top summary, sections
+ *      核心方法 (theorem 2) and 方法步骤详情 (Algorithm 3)]
+ *   - standard quintic Newton-Schulz on the same kernels (the baseline).
+ *     ["Muon: Orthogonalized Momentum and Why It Trains LLMs 2x Cheaper", section
+ *      "Doing an SVD without an SVD"]
+ *   - symmetric-output GEMM alpha A B^T + beta C (+ gamma I), lower tiles only,
+ *     mirrored.  [paper.rainbus.top, 前置知识 "对称 GEMM 内核" and 方法步骤详情 (2)]
+ *   - one Dion3 step: accumulate, row scores, top-k rows, Gram NS on the submatrix,
+ *     decoupled weight decay + row update, error feedback.
+ *     [paper.rainbus.top, 方法步骤详情 (3), Algorithm 4; 前置知识 error feedback]
+ *
+ * Conventions (all entry points):
+ *   - Pointers named X, O, A, B, C, D, W, M, G, S, score, sumsq, workspace, s_out are
+ *     DEVICE pointers; gns_schedule and issued_flops are HOST pointers.
+ *   - Matrices are row-major.  "ld" is the row stride in elements, "stride" the batch
+ *     stride in elements.  Rows must start 16-byte aligned: ld, stride, and the
+ *     column counts n, m, k must be multiples of 8 (16-bit types) or 4 (fp32), and
+ *     device pointers 16-byte aligned; otherwise GNS_ERR_UNSUPPORTED.
+ *   - The caller owns every buffer, including the workspace.  The library allocates
+ *     nothing and keeps no state between calls (apart from the per-thread text of
+ *     gns_last_error); every call is asynchronous on
+ *     `stream` (no host synchronisation), so results are ready when the stream is.
+ *   - Arguments are checked before any launch; a failed check returns a negative
+ *     gns_status and launches nothing.  A launch failure returns GNS_ERR_HIP.
+ *   - Outputs must not alias inputs unless stated (dion3 updates W and M in place).
+ */
+#ifndef GNS_H
+#define GNS_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GNS_OK = 0,
+  GNS_ERR_INVALID_ARG = -1,   /* null pointer, bad shape (n > m, k > N, k < 1), bad enum */
+  GNS_ERR_UNSUPPORTED = -2,   /* alignment / dtype combination not supported */
+  GNS_ERR_WORKSPACE = -3,     /* workspace null or smaller than the *_workspace_size query */
+  GNS_ERR_HIP = -4            /* a HIP launch or runtime call failed */
+} gns_status;
+
+typedef enum { GNS_BF16 = 0, GNS_F16 = 1, GNS_F32 = 2 } gns_dtype;
+
+#define GNS_MAX_STEPS 16
+
+/* Iteration schedule.  a/b/c: per-step coefficients of p_t(x) = a x + b x^3 + c x^5.
+ * restart_after_mask: bit s (1 <= s < steps) set = restart after step s (recompute
+ * X <- Q X, R = X X^T, Q = I).  eps: added to the Frobenius norm.
+ * square_fallback: when 1 and n == m, gns_orthogonalize_batched runs standard NS
+ * (the Gram form saves nothing at aspect ratio 1; the Dion3 page's limitations
+ * section says to fall back to kernelized standard NS there).
+ * Gram Newton-Schulz: paper.rainbus.top 方法步骤详情 Algorithm 3 (restart at t = 3). */
+typedef struct {
+  int steps;
+  float a[GNS_MAX_STEPS];
+  float b[GNS_MAX_STEPS];
+  float c[GNS_MAX_STEPS];
+  unsigned restart_after_mask;
+  float eps;
+  int square_fallback;
+} gns_schedule;
+
+/* Fills: 5 steps of (3.4445, -4.7750, 2.0315), restart after step 2, eps 1e-7,
+ * square_fallback 1.  [Muon blog, "Doing an SVD without an SVD"; Algorithm 3] */
+void gns_default_schedule(gns_schedule* sched);
+
+/* Human-readable name of a gns_status value (static string). */
+const char* gns_status_string(int status);
+
+/* Description of the last HIP failure (GNS_ERR_HIP) seen by the calling thread: the
+ * failing call and HIP's error name.  Empty if none.  This per-thread text is the
+ * library's only state; it never affects results. */
+const char* gns_last_error(void);
+
+/* s[b] = 1 / (||X_b||_F + eps) for each of `batch` n x m matrices, fp32 accumulation.
+ * X: bf16/f16/f32 [batch][n][ldx] (batch stride stride_x).  s_out: device float[batch].
+ * workspace: >= gns_frobenius_workspace_size(batch, n, m) bytes.
+ * [Muon blog, "Doing an SVD without an SVD": X / (norm + 1e-7)] */
+size_t gns_frobenius_workspace_size(int batch, int n, int m);
+int gns_frobenius_scale(const void* X, gns_dtype x_dtype, long long ldx, long long stride_x,
+                        int batch, int n, int m, float eps, float* s_out,
+                        void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by gns_orthogonalize_batched / gns_newton_schulz_batched. */
+size_t gns_workspace_size(int batch, int n, int m, gns_dtype compute);
+
+/* Gram Newton-Schulz on `batch` same-shape matrices in one pass (one launch per step
+ * over the whole batch).  X: [batch][n][ldx], 1 <= n <= m (iterate on the short side;
+ * transpose a tall matrix before the call).  O: [batch][n][ldo], dtype o_dtype.
+ * compute: dtype of the n x n iterates and of the MFMA operands after the first Gram
+ * product: GNS_F16 (the pages' half precision, default), GNS_BF16, or GNS_F32.  All
+ * products accumulate in fp32.  With x_dtype GNS_F32, compute must be GNS_F32.
+ * sched: NULL = gns_default_schedule.  issued_flops (nullable, host): receives the
+ * MFMA flops the call issues.  X is read-only; O must not alias X or the workspace.
+ * A zero matrix gives a zero result.
+ * [paper.rainbus.top 方法步骤详情 Algorithm 3; 核心方法 theorem 2] */
+int gns_orthogonalize_batched(const void* X, gns_dtype x_dtype, long long ldx, long long stride_x,
+                              void* O, gns_dtype o_dtype, long long ldo, long long stride_o,
+                              int batch, int n, int m, gns_dtype compute,
+                              const gns_schedule* sched, void* workspace, size_t ws_bytes,
+                              hipStream_t stream, double* issued_flops);
+
+/* Standard quintic Newton-Schulz (A = X X^T; B = b A + c A A; X <- a X + B X) on the
+ * same kernels; same arguments and rules as gns_orthogonalize_batched (the restart
+ * mask and square_fallback are ignored).
+ * [Muon blog, "Doing an SVD without an SVD"; paper.rainbus.top 前置知识] */
+int gns_newton_schulz_batched(const void* X, gns_dtype x_dtype, long long ldx, long long stride_x,
+                              void* O, gns_dtype o_dtype, long long ldo, long long stride_o,
+                              int batch, int n, int m, gns_dtype compute,
+                              const gns_schedule* sched, void* workspace, size_t ws_bytes,
+                              hipStream_t stream, double* issued_flops);
+
+/* Symmetric-output GEMM: D = alpha * A * B^T + beta * C + gamma * I, for `batch`
+ * problems.  A, B: n x k (row-major, dtype in_dtype); with B symmetric (k == n) this
+ * is A * B, with A == B it is the Gram product A A^T.  Only output tiles on or below
+ * the diagonal are computed; each is also written transposed above the diagonal, so
+ * D is bitwise symmetric.  C: n x n in out_dtype, read from its lower triangle only
+ * (may be NULL when beta == 0; may alias D).  D: n x n in out_dtype.
+ * in_dtype: GNS_BF16, GNS_F16 or GNS_F32; out_dtype any.
+ * [paper.rainbus.top 前置知识 symmetric GEMM kernel; 方法步骤详情 (2): lower-triangle
+ *  tile scheduler + transposed-write epilogue; 技术新颖性: alpha A B + beta C] */
+int symm_gemm(int batch, int n, int k, float alpha,
+              const void* A, long long lda, long long stride_a,
+              const void* B, long long ldb, long long stride_b,
+              float beta, const void* C, long long ldc, long long stride_c,
+              float gamma, void* D, long long ldd, long long stride_d,
+              gns_dtype in_dtype, gns_dtype out_dtype, hipStream_t stream);
+
+/* Rectangular GEMM: D = alpha * A * B + beta * C for `batch` problems.  A: n x k
+ * (a_dtype, the MFMA operand type); B: k x m (b_dtype; converted to a_dtype on load,
+ * after multiplying by b_prescale); C (nullable when beta == 0), D: n x m in
+ * out_dtype.  b_prescale must be 1 when b_dtype == a_dtype.  This is the Q X product
+ * of Gram NS and the B X product of standard NS.
+ * [paper.rainbus.top 核心方法: the two rectangular products X X^T and Q X] */
+int rect_gemm(int batch, int n, int k, int m, float alpha,
+              const void* A, long long lda, long long stride_a, gns_dtype a_dtype,
+              const void* B, long long ldb, long long stride_b, gns_dtype b_dtype,
+              float b_prescale, float beta, const void* C, long long ldc, long long stride_c,
+              void* D, long long ldd, long long stride_d, gns_dtype out_dtype,
+              hipStream_t stream);
+
+/* ---- Dion3 (row-subsampled update with error feedback) -------------------------
+ * W, M, G: N x m bf16 row-major with row stride ld.  S: device int32[k], ascending
+ * row indices.  Rounding model: each stored value is rounded once to bf16 (nearest
+ * even); element-wise updates are fp32 op by op, no fused multiply-add.
+ * [paper.rainbus.top 方法步骤详情 (3) Algorithm 4; 前置知识 error feedback] */
+
+/* M <- bf16(M + G); score[i] = sum_j |M_ij| (score_norm 1) or sum_j M_ij^2
+ * (score_norm 2) of the updated M, float64 accumulation; sumsq[i] = sum_j M_ij^2
+ * (float64; nullable).  score, sumsq: device double[N]. */
+int dion3_accumulate_score(void* M, const void* G, int N, int m, long long ld, int score_norm,
+                           double* score, double* sumsq, hipStream_t stream);
+
+/* S = indices of the k largest scores (ties -> lower index), written ascending.
+ * 1 <= k <= N.  One workgroup; no workspace. */
+int dion3_select_topk(const double* score, int N, int k, int* S, hipStream_t stream);
+
+/* X[r, :] = M[S[r], :] (bf16, row stride ldx) and then M[S[r], :] <- bf16(mu * M[S[r], :])
+ * (error feedback: only selected rows decay). */
+int dion3_gather_feedback(void* M, int N, int m, long long ld, const int* S, int k, float mu,
+                          void* X, long long ldx, hipStream_t stream);
+
+/* d = fl32(1 - fl32(lr * wd)); W[S[r], :] <- bf16(fl32(d * W) - fl32(lr * O[r, :]));
+ * when wd != 0 every other row W <- bf16(fl32(d * W)).  O: k x m, o_dtype bf16 or f32.
+ * S must be ascending and hold distinct indices in [0, N). */
+int dion3_apply_update(void* W, int N, int m, long long ld, const int* S, int k,
+                       const void* O, gns_dtype o_dtype, long long ldo,
+                       float lr, float wd, hipStream_t stream);
+
+/* Workspace bytes needed by dion3_step. */
+size_t dion3_workspace_size(int N, int m, int k, gns_dtype compute);
+
+/* One Dion3 step (in place on W and M):
+ *   M <- M + G; S = top-k rows by score (score_norm 1 = l1 as on the pages, 2 = l2);
+ *   X = M[S, :]; O = GramNS(X) (sched, compute as in gns_orthogonalize_batched, the
+ *   Frobenius norm taken from the per-row sums of squares); W <- decay + row update
+ *   with lr (the caller passes lr = eta / sqrt(f)); M[S, :] <- mu M[S, :].
+ * S_out: device int32[k] (ascending).  O_out: nullable device bf16 [k][m] (row stride
+ * m) receiving O.  k must satisfy 1 <= k <= min(N, m). */
+int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int k,
+               float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
+               const gns_schedule* sched, int* S_out, void* O_out,
+               void* workspace, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GNS_H */

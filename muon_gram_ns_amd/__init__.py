@@ -1,0 +1,12 @@
+"""MI355X-native Gram Newton-Schulz and Dion3 hot path.
+
+The computation lives in libgns.so (hand-written HIP kernels for gfx950 behind a
+C ABI declared in include/gns.h); this package is its thin Python binding.
+"""
+from ._lib import (  # noqa: F401
+    lib, LIB_PATH, GnsError, Schedule, default_schedule, header_functions,
+    GNS_BF16, GNS_F16, GNS_F32, orthogonalize, newton_schulz, frobenius_scale, symm_gemm,
+    rect_gemm, dion3_accumulate_score, dion3_select_topk, dion3_gather_feedback,
+    dion3_apply_update, dion3_step, workspace,
+)
+from . import flops  # noqa: F401

@@ -1,0 +1,324 @@
+"""ctypes binding of libgns.so: argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; this module only turns
+torch tensors into device pointers, sizes and the current HIP stream, allocates the
+caller-owned workspace with torch (device memory plumbing) and raises on a non-zero
+status.  If libgns.so is missing the import fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgns.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "gns.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python muon_gram_ns_amd/build.py` "
+                      "(the HIP library is required; there is no CPU path)")
+# Load torch (when installed) BEFORE libgns: PyTorch for ROCm ships its own HIP
+# runtime, and the dynamic linker reuses it for libgns's libamdhip64.so.7 dependency
+# only if it is already loaded.  Loading libgns first would bring in /opt/rocm's copy,
+# after which torch loads a second runtime of its own; the two cannot share the GPU.
+try:
+    import torch as _torch_for_runtime  # noqa: F401
+except ImportError:        # plain use without torch: libgns uses the system runtime
+    pass
+lib = ctypes.CDLL(LIB_PATH)
+
+GNS_BF16, GNS_F16, GNS_F32 = 0, 1, 2
+GNS_MAX_STEPS = 16
+STATUS = {0: "GNS_OK", -1: "GNS_ERR_INVALID_ARG", -2: "GNS_ERR_UNSUPPORTED",
+          -3: "GNS_ERR_WORKSPACE", -4: "GNS_ERR_HIP"}
+
+F = ctypes.c_float
+I = ctypes.c_int
+LL = ctypes.c_longlong
+P = ctypes.c_void_p
+SZ = ctypes.c_size_t
+DP = ctypes.POINTER(ctypes.c_double)
+
+
+class Schedule(ctypes.Structure):
+    _fields_ = [("steps", I), ("a", F * GNS_MAX_STEPS), ("b", F * GNS_MAX_STEPS),
+                ("c", F * GNS_MAX_STEPS), ("restart_after_mask", ctypes.c_uint), ("eps", F),
+                ("square_fallback", I)]
+
+
+def _sig(name, res, *args):
+    f = getattr(lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_sig("gns_default_schedule", None, ctypes.POINTER(Schedule))
+_sig("gns_status_string", ctypes.c_char_p, I)
+_sig("gns_last_error", ctypes.c_char_p)
+_sig("gns_frobenius_workspace_size", SZ, I, I, I)
+_sig("gns_frobenius_scale", I, P, I, LL, LL, I, I, I, F, P, P, SZ, P)
+_sig("gns_workspace_size", SZ, I, I, I, I)
+_NS_ARGS = (P, I, LL, LL, P, I, LL, LL, I, I, I, I, ctypes.POINTER(Schedule), P, SZ, P, DP)
+_sig("gns_orthogonalize_batched", I, *_NS_ARGS)
+_sig("gns_newton_schulz_batched", I, *_NS_ARGS)
+_sig("symm_gemm", I, I, I, I, F, P, LL, LL, P, LL, LL, F, P, LL, LL, F, P, LL, LL, I, I, P)
+_sig("rect_gemm", I, I, I, I, I, F, P, LL, LL, I, P, LL, LL, I, F, F, P, LL, LL, P, LL, LL, I, P)
+_sig("dion3_accumulate_score", I, P, P, I, I, LL, I, P, P, P)
+_sig("dion3_select_topk", I, P, I, I, P, P)
+_sig("dion3_gather_feedback", I, P, I, I, LL, P, I, F, P, LL, P)
+_sig("dion3_apply_update", I, P, I, I, LL, P, I, P, I, LL, F, F, P)
+_sig("dion3_workspace_size", SZ, I, I, I, I)
+_sig("dion3_step", I, P, P, P, I, I, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/gns.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z][a-z0-9_]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+class GnsError(RuntimeError):
+    pass
+
+
+def check(status: int, what: str):
+    if status != 0:
+        detail = lib.gns_last_error().decode() if status == -4 else ""
+        raise GnsError(f"{what} failed: {STATUS.get(status, status)} {detail}".rstrip())
+
+
+def default_schedule(steps=5, abc=(3.4445, -4.7750, 2.0315), restart_after=(2,), eps=1e-7,
+                     square_fallback=True) -> Schedule:
+    s = Schedule()
+    lib.gns_default_schedule(ctypes.byref(s))
+    s.steps = steps
+    table = [abc] * steps if len(abc) == 3 and not hasattr(abc[0], "__len__") else list(abc)
+    for t, (a, b, c) in enumerate(table):
+        s.a[t], s.b[t], s.c[t] = a, b, c
+    mask = 0
+    for r in restart_after:
+        mask |= 1 << r
+    s.restart_after_mask = mask
+    s.eps = eps
+    s.square_fallback = 1 if square_fallback else 0
+    return s
+
+
+# ---- torch marshalling ---------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.bfloat16: GNS_BF16, torch.float16: GNS_F16, torch.float32: GNS_F32}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def torch_dtype(code: int):
+    torch = _torch()
+    return {GNS_BF16: torch.bfloat16, GNS_F16: torch.float16, GNS_F32: torch.float32}[code]
+
+
+def code_of(name) -> int:
+    if isinstance(name, int):
+        return name
+    return {"bf16": GNS_BF16, "f16": GNS_F16, "fp16": GNS_F16, "f32": GNS_F32, "fp32": GNS_F32}[name]
+
+
+def _dev(t):
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU (the HIP library has no CPU path)")
+    return t
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+_WS = {}
+
+
+def workspace(nbytes: int, device):
+    """Grow-only per-device workspace (torch-allocated device memory)."""
+    torch = _torch()
+    key = torch.device(device).index
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+def _mat3(x):
+    """(batch, n, m, ld, batch_stride) of a [B, n, m] or [n, m] tensor with unit column stride."""
+    if x.dim() == 2:
+        x = x.unsqueeze(0)
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("expected a [B, n, m] or [n, m] tensor with contiguous rows")
+    B, n, m = x.shape
+    return x, B, n, m, x.stride(1), (x.stride(0) if B > 1 else n * x.stride(1))
+
+
+def _ns(fn_name, X, out, compute, schedule, want_flops):
+    torch = _torch()
+    _dev(X)
+    squeeze = X.dim() == 2
+    X3, B, n, m, ldx, sx = _mat3(X)
+    if out is None:
+        out = torch.empty((B, n, m), dtype=X.dtype, device=X.device)
+    O3, Bo, no, mo, ldo, so = _mat3(out)
+    if (Bo, no, mo) != (B, n, m):
+        raise ValueError("output shape mismatch")
+    cdt = code_of(compute)
+    sched = schedule if schedule is not None else default_schedule()
+    ws_n = lib.gns_workspace_size(B, n, m, cdt)
+    ws = workspace(ws_n, X.device)
+    flops = ctypes.c_double(0.0)
+    st = getattr(lib, fn_name)(X3.data_ptr(), dtype_code(X3), ldx, sx, O3.data_ptr(), dtype_code(O3), ldo, so,
+                               B, n, m, cdt, ctypes.byref(sched), ws.data_ptr(), ws.numel(),
+                               _stream(X.device), ctypes.byref(flops))
+    check(st, fn_name)
+    res = out.squeeze(0) if (squeeze and out.dim() == 3) else out
+    return (res, flops.value) if want_flops else res
+
+
+def orthogonalize(X, out=None, compute="f16", schedule=None, return_flops=False):
+    """Gram Newton-Schulz of X ([B, n, m] or [n, m], n <= m) -> same shape/dtype as X."""
+    return _ns("gns_orthogonalize_batched", X, out, compute, schedule, return_flops)
+
+
+def newton_schulz(X, out=None, compute="f16", schedule=None, return_flops=False):
+    """Standard quintic Newton-Schulz on the same kernels."""
+    return _ns("gns_newton_schulz_batched", X, out, compute, schedule, return_flops)
+
+
+def frobenius_scale(X, eps=1e-7):
+    torch = _torch()
+    _dev(X)
+    X3, B, n, m, ldx, sx = _mat3(X)
+    s = torch.empty(B, dtype=torch.float32, device=X.device)
+    ws = workspace(lib.gns_frobenius_workspace_size(B, n, m), X.device)
+    check(lib.gns_frobenius_scale(X3.data_ptr(), dtype_code(X3), ldx, sx, B, n, m, eps, s.data_ptr(),
+                                  ws.data_ptr(), ws.numel(), _stream(X.device)), "gns_frobenius_scale")
+    return s
+
+
+def symm_gemm(A, B=None, C=None, alpha=1.0, beta=0.0, gamma=0.0, out=None, out_dtype=None):
+    """D = alpha A B^T + beta C + gamma I (lower tiles, mirrored) for [batch, n, k] A, B."""
+    torch = _torch()
+    _dev(A)
+    B = A if B is None else B
+    A3, nb, n, k, lda, sa = _mat3(A)
+    B3, nb2, n2, k2, ldb, sb = _mat3(B)
+    if (nb2, n2, k2) != (nb, n, k):
+        raise ValueError("A and B shapes differ")
+    odt = dtype_code(A3) if out_dtype is None else code_of(out_dtype)
+    if out is None:
+        out = torch.empty((nb, n, n), dtype=torch_dtype(odt), device=A.device)
+    D3, _, _, _, ldd, sd = _mat3(out)
+    if C is not None:
+        C3, _, _, _, ldc, sc = _mat3(C)
+        cptr = C3.data_ptr()
+    else:
+        cptr, ldc, sc = None, n, n * n
+    check(lib.symm_gemm(nb, n, k, alpha, A3.data_ptr(), lda, sa, B3.data_ptr(), ldb, sb, beta, cptr, ldc, sc,
+                        gamma, D3.data_ptr(), ldd, sd, dtype_code(A3), dtype_code(D3), _stream(A.device)),
+          "symm_gemm")
+    return out.squeeze(0) if A.dim() == 2 else out
+
+
+def rect_gemm(A, Bm, C=None, alpha=1.0, beta=0.0, b_prescale=1.0, out=None, out_dtype=None):
+    """D = alpha A B + beta C for A [batch, n, k], B [batch, k, m]."""
+    torch = _torch()
+    _dev(A)
+    A3, nb, n, k, lda, sa = _mat3(A)
+    B3, nb2, k2, m, ldb, sb = _mat3(Bm)
+    if (nb2, k2) != (nb, k):
+        raise ValueError("A and B shapes differ")
+    odt = dtype_code(A3) if out_dtype is None else code_of(out_dtype)
+    if out is None:
+        out = torch.empty((nb, n, m), dtype=torch_dtype(odt), device=A.device)
+    D3, _, _, _, ldd, sd = _mat3(out)
+    if C is not None:
+        C3, _, _, _, ldc, sc = _mat3(C)
+        cptr = C3.data_ptr()
+    else:
+        cptr, ldc, sc = None, m, n * m
+    check(lib.rect_gemm(nb, n, k, m, alpha, A3.data_ptr(), lda, sa, dtype_code(A3), B3.data_ptr(), ldb, sb,
+                        dtype_code(B3), b_prescale, beta, cptr, ldc, sc, D3.data_ptr(), ldd, sd, dtype_code(D3),
+                        _stream(A.device)), "rect_gemm")
+    return out.squeeze(0) if A.dim() == 2 else out
+
+
+# ---- Dion3 -------------------------------------------------------------------------
+
+def _rows(x):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("expected a [N, m] tensor with contiguous rows")
+    return x.shape[0], x.shape[1], x.stride(0)
+
+
+def dion3_accumulate_score(M, G, score_norm=1):
+    torch = _torch()
+    N, m, ld = _rows(_dev(M))
+    if _rows(G)[2] != ld:
+        raise ValueError("M and G must share the row stride")
+    score = torch.empty(N, dtype=torch.float64, device=M.device)
+    sumsq = torch.empty(N, dtype=torch.float64, device=M.device)
+    check(lib.dion3_accumulate_score(M.data_ptr(), G.data_ptr(), N, m, ld, score_norm, score.data_ptr(),
+                                     sumsq.data_ptr(), _stream(M.device)), "dion3_accumulate_score")
+    return score, sumsq
+
+
+def dion3_select_topk(score, k):
+    torch = _torch()
+    S = torch.empty(k, dtype=torch.int32, device=score.device)
+    check(lib.dion3_select_topk(_dev(score).data_ptr(), score.numel(), k, S.data_ptr(), _stream(score.device)),
+          "dion3_select_topk")
+    return S
+
+
+def dion3_gather_feedback(M, S, mu):
+    torch = _torch()
+    N, m, ld = _rows(_dev(M))
+    k = S.numel()
+    X = torch.empty((k, m), dtype=M.dtype, device=M.device)
+    check(lib.dion3_gather_feedback(M.data_ptr(), N, m, ld, S.data_ptr(), k, mu, X.data_ptr(), m,
+                                    _stream(M.device)), "dion3_gather_feedback")
+    return X
+
+
+def dion3_apply_update(W, S, O, lr, wd):
+    N, m, ld = _rows(_dev(W))
+    k = S.numel()
+    check(lib.dion3_apply_update(W.data_ptr(), N, m, ld, S.data_ptr(), k, O.data_ptr(), dtype_code(O),
+                                 O.stride(0), lr, wd, _stream(W.device)), "dion3_apply_update")
+    return W
+
+
+def dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute="f16", schedule=None,
+               return_O=False):
+    """One Dion3 step in place on W and M; returns S (and O when return_O)."""
+    torch = _torch()
+    N, m, ld = _rows(_dev(W))
+    if _rows(M)[2] != ld or _rows(G)[2] != ld:
+        raise ValueError("W, M, G must share the row stride")
+    cdt = code_of(compute)
+    S = torch.empty(k, dtype=torch.int32, device=W.device)
+    O = torch.empty((k, m), dtype=torch.bfloat16, device=W.device) if return_O else None
+    sched = schedule if schedule is not None else default_schedule()
+    ws = workspace(lib.dion3_workspace_size(N, m, k, cdt), W.device)
+    check(lib.dion3_step(W.data_ptr(), M.data_ptr(), G.data_ptr(), N, m, ld, k, lr, weight_decay, mu,
+                         score_norm, cdt, ctypes.byref(sched), S.data_ptr(),
+                         O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
+                         _stream(W.device)), "dion3_step")
+    return (S, O) if return_O else S

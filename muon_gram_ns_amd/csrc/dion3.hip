@@ -1,0 +1,297 @@
+// Dion3 element-wise and selection kernels (all HBM- or latency-bound).
+//
+// The update rule ("Dion3: Full-Stack Orthogonal Updates", paper.rainbus.top,
+// 方法步骤详情 (3), Algorithm 4): M <- M + G; pick the k rows of largest norm;
+// orthogonalise that submatrix; decay all weights by (1 - lr wd) and subtract
+// lr O from the selected weight rows; decay only the selected momentum rows by mu
+// (error feedback, same page, 前置知识).
+//
+// Rounding model (the pages do not fix it; this is the reading the oracle emulates):
+// W, M, G are bf16; each stored value is rounded once, to nearest even, from fp32
+// results computed op by op.  This file is compiled with -ffp-contract=off and uses
+// explicit __fmul_rn/__fsub_rn so no multiply-add is fused.  Row scores accumulate
+// in fp64 (the per-element terms are exact in fp64).
+#include "common.h"
+#include "internal.h"
+
+namespace gns {
+
+constexpr int kRowThreads = 256;
+
+__device__ __forceinline__ double block_sum_f64(double v, double* sh) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0)
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += sh[i];
+  return t;
+}
+
+// ---- M <- bf16(M + G); per-row score and sum of squares ---------------------------
+__global__ void __launch_bounds__(kRowThreads)
+accumulate_score_kernel(uint16_t* M, const uint16_t* G, int m, long long ld, int score_norm,
+                        double* score, double* sumsq) {
+  __shared__ double sh[kRowThreads / 64];
+  const int r = blockIdx.x;
+  uint4* mr = reinterpret_cast<uint4*>(M + (size_t)r * ld);
+  const uint4* gr = reinterpret_cast<const uint4*>(G + (size_t)r * ld);
+  double acc_s = 0.0, acc_q = 0.0;
+  for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
+    uint4 mv = mr[c];
+    const uint4 gv = gr[c];
+    uint32_t* mw = reinterpret_cast<uint32_t*>(&mv);
+    const uint32_t* gw = reinterpret_cast<const uint32_t*>(&gv);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t out = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float a = bf16_bits_to_f32((mw[i] >> (16 * h)) & 0xffffu);
+        const float g = bf16_bits_to_f32((gw[i] >> (16 * h)) & 0xffffu);
+        const uint32_t nb = f32_to_bf16_bits(__fadd_rn(a, g));
+        out |= nb << (16 * h);
+        const double v = (double)bf16_bits_to_f32(nb);
+        acc_s += (score_norm == 1) ? fabs(v) : v * v;
+        acc_q += v * v;
+      }
+      mw[i] = out;
+    }
+    mr[c] = mv;
+  }
+  const double ts = block_sum_f64(acc_s, sh);
+  const double tq = block_sum_f64(acc_q, sh);
+  if (threadIdx.x == 0) {
+    score[r] = ts;
+    if (sumsq) sumsq[r] = tq;
+  }
+}
+
+hipError_t launch_accumulate_score(uint16_t* M, const uint16_t* G, int N, int m, long long ld, int score_norm,
+                                   double* score, double* sumsq, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  clear_stale_error();
+  hipLaunchKernelGGL(accumulate_score_kernel, dim3(N), dim3(kRowThreads), 0, s, M, G, m, ld, score_norm,
+                     score, sumsq);
+  return hipGetLastError();
+}
+
+// ---- top-k rows: radix select on the fp64 bit patterns, then ordered compaction ----
+// Scores are >= +0 (sums of |x| or x^2), so their IEEE bit patterns order like the
+// values; a NaN score orders above +inf.  Ties at the threshold go to lower indices.
+constexpr int kTopkThreads = 1024;
+
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* sh, unsigned& total) {
+  // inclusive scan within each wave, then across the 16 wave totals
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  unsigned x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned run = 0;
+    for (int i = 0; i < kTopkThreads / 64; ++i) { const unsigned t = sh[i]; sh[i] = run; run += t; }
+    sh[kTopkThreads / 64] = run;
+  }
+  __syncthreads();
+  total = sh[kTopkThreads / 64];
+  return sh[w] + x - v;
+}
+
+__global__ void __launch_bounds__(kTopkThreads)
+topk_kernel(const double* score, int N, int k, int* S) {
+  __shared__ unsigned hist[256];
+  __shared__ unsigned scan_sh[kTopkThreads / 64 + 1];
+  __shared__ unsigned long long sh_prefix;
+  __shared__ unsigned sh_krem;
+  const unsigned long long* key = reinterpret_cast<const unsigned long long*>(score);
+  unsigned long long prefix = 0, mask = 0;
+  unsigned krem = (unsigned)k;
+  for (int d = 7; d >= 0; --d) {
+    const int shift = 8 * d;
+    for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < N; i += kTopkThreads) {
+      const unsigned long long kv = key[i];
+      if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned above = 0;
+      int bin = 255;
+      for (; bin > 0; --bin) {
+        if (above + hist[bin] >= krem) break;
+        above += hist[bin];
+      }
+      sh_prefix = prefix | ((unsigned long long)bin << shift);
+      sh_krem = krem - above;
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    krem = sh_krem;
+    mask |= (255ull << shift);
+    __syncthreads();
+  }
+  // prefix is now the k-th largest key; take every key above it and the first krem
+  // keys equal to it (lowest indices), writing indices in ascending order.
+  const unsigned long long tau = prefix;
+  unsigned eq_base = 0, sel_base = 0;
+  for (int base = 0; base < N; base += kTopkThreads) {
+    const int i = base + threadIdx.x;
+    unsigned long long kv = 0;
+    bool valid = i < N;
+    if (valid) kv = key[i];
+    const unsigned is_eq = (valid && kv == tau) ? 1u : 0u;
+    unsigned eq_total;
+    const unsigned eq_before = eq_base + block_excl_scan(is_eq, scan_sh, eq_total);
+    const bool take = valid && (kv > tau || (is_eq && eq_before < krem));
+    unsigned sel_total;
+    const unsigned pos = sel_base + block_excl_scan(take ? 1u : 0u, scan_sh, sel_total);
+    if (take && pos < (unsigned)k) S[pos] = i;
+    eq_base += eq_total;
+    sel_base += sel_total;
+  }
+}
+
+hipError_t launch_topk(const double* score, int N, int k, int* S, hipStream_t s) {
+  clear_stale_error();
+  hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(kTopkThreads), 0, s, score, N, k, S);
+  return hipGetLastError();
+}
+
+// ---- X[r] = M[S[r]]; M[S[r]] <- bf16(mu * M[S[r]]) ----------------------------------
+__global__ void __launch_bounds__(kRowThreads)
+gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, const int* S, float mu, uint16_t* X,
+                       long long ldx) {
+  const int r = blockIdx.x;
+  const int src = S[r];
+  if (src < 0 || src >= N) return;     // precondition violated: leave this row alone
+  uint4* mr = reinterpret_cast<uint4*>(M + (size_t)src * ld);
+  uint4* xr = reinterpret_cast<uint4*>(X + (size_t)r * ldx);
+  for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
+    uint4 v = mr[c];
+    xr[c] = v;
+    uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = f32_to_bf16_bits(__fmul_rn(mu, bf16_bits_to_f32(w[i] & 0xffffu)));
+      const uint32_t hi = f32_to_bf16_bits(__fmul_rn(mu, bf16_bits_to_f32(w[i] >> 16)));
+      w[i] = lo | (hi << 16);
+    }
+    mr[c] = v;
+  }
+}
+
+hipError_t launch_gather_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, float mu,
+                                  uint16_t* X, long long ldx, hipStream_t s) {
+  if (k <= 0) return hipSuccess;
+  clear_stale_error();
+  hipLaunchKernelGGL(gather_feedback_kernel, dim3(k), dim3(kRowThreads), 0, s, M, N, m, ld, S, mu, X, ldx);
+  return hipGetLastError();
+}
+
+// ---- weight decay + selected-row update, one rounding per element --------------------
+template <bool O_F32>
+__global__ void __launch_bounds__(kRowThreads)
+apply_update_kernel(uint16_t* W, int N, int m, long long ld, const int* S, int k, const void* O,
+                    long long ldo, float lr, float wd, int all_rows) {
+  const int d_over = blockIdx.x;
+  int row, oi;
+  if (all_rows) {
+    row = d_over;
+    // binary search for row in the ascending list S
+    int lo = 0, hi = k - 1;
+    oi = -1;
+    while (lo <= hi) {
+      const int mid = (lo + hi) >> 1;
+      const int v = S[mid];
+      if (v == row) { oi = mid; break; }
+      if (v < row) lo = mid + 1; else hi = mid - 1;
+    }
+  } else {
+    oi = d_over;
+    row = S[oi];
+    if (row < 0 || row >= N) return;
+  }
+  const float d = __fsub_rn(1.0f, __fmul_rn(lr, wd));
+  uint4* wr = reinterpret_cast<uint4*>(W + (size_t)row * ld);
+  for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
+    uint4 v = wr[c];
+    uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+    float o[8];
+    if (oi >= 0) {
+      if constexpr (O_F32) {
+        const float4* op = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(O) + (size_t)oi * ldo + (size_t)c * 8);
+        const float4 a = op[0], b = op[1];
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+      } else {
+        const uint4 q = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(O) + (size_t)oi * ldo)[c];
+        const uint32_t* qw = reinterpret_cast<const uint32_t*>(&q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = bf16_bits_to_f32(qw[i] & 0xffffu);
+          o[2 * i + 1] = bf16_bits_to_f32(qw[i] >> 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t out = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float x = bf16_bits_to_f32((w[i] >> (16 * h)) & 0xffffu);
+        float y = __fmul_rn(d, x);
+        if (oi >= 0) y = __fsub_rn(y, __fmul_rn(lr, o[2 * i + h]));
+        out |= f32_to_bf16_bits(y) << (16 * h);
+      }
+      w[i] = out;
+    }
+    wr[c] = v;
+  }
+}
+
+hipError_t launch_apply_update(uint16_t* W, int N, int m, long long ld, const int* S, int k, const void* O,
+                               gns_dtype o_dtype, long long ldo, float lr, float wd, hipStream_t s) {
+  const int all_rows = (wd != 0.0f) ? 1 : 0;
+  const int blocks = all_rows ? N : k;
+  if (blocks <= 0) return hipSuccess;
+  clear_stale_error();
+  if (o_dtype == GNS_F32)
+    hipLaunchKernelGGL(apply_update_kernel<true>, dim3(blocks), dim3(kRowThreads), 0, s, W, N, m, ld, S, k, O, ldo,
+                       lr, wd, all_rows);
+  else
+    hipLaunchKernelGGL(apply_update_kernel<false>, dim3(blocks), dim3(kRowThreads), 0, s, W, N, m, ld, S, k, O, ldo,
+                       lr, wd, all_rows);
+  return hipGetLastError();
+}
+
+// ---- s = 1 / (sqrt(sum_i sumsq[S[i]]) + eps) ------------------------------------------
+__global__ void __launch_bounds__(kRowThreads)
+selected_sumsq_kernel(const double* sumsq, const int* S, int k, int N, float eps, float* s_out) {
+  __shared__ double sh[kRowThreads / 64];
+  const int per = (k + kRowThreads - 1) / kRowThreads;
+  double acc = 0.0;
+  for (int i = threadIdx.x * per; i < min(k, (int)(threadIdx.x + 1) * per); ++i) {
+    const int r = S[i];
+    if (r >= 0 && r < N) acc += sumsq[r];
+  }
+  const double t = block_sum_f64(acc, sh);
+  if (threadIdx.x == 0) s_out[0] = (float)(1.0 / (sqrt(t) + (double)eps));
+}
+
+hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int k, int N, float eps, float* s_out,
+                                 hipStream_t s) {
+  clear_stale_error();
+  hipLaunchKernelGGL(selected_sumsq_kernel, dim3(1), dim3(kRowThreads), 0, s, sumsq, S, k, N, eps, s_out);
+  return hipGetLastError();
+}
+
+}  // namespace gns

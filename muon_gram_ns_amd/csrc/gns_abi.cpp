@@ -1,0 +1,524 @@
+// C ABI of libgns: argument checks, workspace carving and the launch schedules of
+// Gram Newton-Schulz, standard Newton-Schulz and the Dion3 step.
+//
+// Gram Newton-Schulz ("Dion3: Full-Stack Orthogonal Updates", paper.rainbus.top,
+// 核心方法 theorem 2 and 方法步骤详情 Algorithm 3), per matrix, s = 1/(||X||_F + eps):
+//   R = s^2 X X^T, Q = I
+//   step t:  Z = c_t R R + b_t R
+//            Q <- Q Z + a_t Q            (Q = Z + a_t I while Q is the identity)
+//            R <- (Z + a_t I) R (Z + a_t I), as Y = R Z + a_t R, R = Z Y + a_t Y
+//                                        (skipped when no later step reads R)
+//   restart after step s: X <- Q X, R = X X^T, Q = I
+//   output Q X
+// Every launch covers the whole batch.  The normalised X is never stored: s stays on
+// the device and enters the epilogues (R = s^2 X X^T, X2 = s Q X, O = s Q X).
+// With fp16 iterates, matrices shaped like X are stored times a power of two
+// P ~ sqrt(n m) so their entries sit near 1, well inside fp16's normal range; the
+// factor is divided out exactly in the epilogues.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+using namespace gns;
+
+namespace {
+
+size_t esize(gns_dtype d) { return d == GNS_F32 ? 4 : 2; }
+bool valid_dtype(int d) { return d == GNS_BF16 || d == GNS_F16 || d == GNS_F32; }
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Carver {
+  uint8_t* base;
+  size_t off;
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+struct NsLayout {
+  float* s;
+  float* partials;
+  void *R, *Z, *Y, *Q0, *Q1, *Xa, *Xb;   // Gram NS
+  void *A, *Bm, *Sa, *Sb;                // standard NS (overlaps the Gram region)
+  size_t bytes;
+};
+
+NsLayout ns_layout(void* base, int batch, int n, int m, gns_dtype cdt) {
+  Carver c{reinterpret_cast<uint8_t*>(base), 0};
+  NsLayout L{};
+  const size_t e = esize(cdt);
+  const size_t nn = (size_t)n * n * e * batch, nm = (size_t)n * m * e * batch;
+  L.s = (float*)c.take(sizeof(float) * (size_t)batch);
+  L.partials = (float*)c.take(sizeof(float) * (size_t)batch * frob_partials_per_batch(n, m));
+  const size_t common = c.off;
+  L.R = c.take(nn); L.Z = c.take(nn); L.Y = c.take(nn); L.Q0 = c.take(nn); L.Q1 = c.take(nn);
+  L.Xa = c.take(nm); L.Xb = c.take(nm);
+  const size_t gram_end = c.off;
+  c.off = common;
+  L.A = c.take(nn); L.Bm = c.take(nn); L.Sa = c.take(nm); L.Sb = c.take(nm);
+  L.bytes = std::max(gram_end, c.off);
+  return L;
+}
+
+float pow2_scale(gns_dtype cdt, int n, int m) {
+  if (cdt != GNS_F16) return 1.0f;
+  const int e = (int)std::lround(0.5 * std::log2((double)n * (double)m));
+  return std::ldexp(1.0f, e);
+}
+
+struct NsCall {
+  const void* X; gns_dtype xdt; long long ldx, sx;
+  void* O; gns_dtype odt; long long ldo, so;
+  int batch, n, m; gns_dtype cdt;
+  gns_schedule sch;
+  void* ws; size_t ws_bytes;
+  hipStream_t stream;
+  double* flops;
+  const float* s_given;   // precomputed device scale (Dion3), or null
+};
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int check_schedule(const gns_schedule& s) {
+  if (s.steps < 1 || s.steps > GNS_MAX_STEPS) return GNS_ERR_INVALID_ARG;
+  const unsigned allowed = ((1u << s.steps) - 1u) & ~1u;    // bits 1..steps-1
+  if (s.restart_after_mask & ~allowed) return GNS_ERR_INVALID_ARG;
+  if (!(s.eps >= 0.0f) || !std::isfinite(s.eps)) return GNS_ERR_INVALID_ARG;
+  for (int t = 0; t < s.steps; ++t)
+    if (!std::isfinite(s.a[t]) || !std::isfinite(s.b[t]) || !std::isfinite(s.c[t])) return GNS_ERR_INVALID_ARG;
+  return GNS_OK;
+}
+
+int check_ns(const NsCall& c) {
+  if (!valid_dtype(c.xdt) || !valid_dtype(c.odt) || !valid_dtype(c.cdt)) return GNS_ERR_INVALID_ARG;
+  if (c.batch < 0 || c.n < 1 || c.m < 1 || c.n > c.m) return GNS_ERR_INVALID_ARG;
+  if (!c.X || !c.O) return GNS_ERR_INVALID_ARG;
+  if (c.ldx < c.m || c.ldo < c.m) return GNS_ERR_INVALID_ARG;
+  if (c.batch > 1 && (c.sx < (long long)c.n * c.ldx || c.so < (long long)c.n * c.ldo)) return GNS_ERR_INVALID_ARG;
+  int st = check_schedule(c.sch);
+  if (st) return st;
+  if ((c.xdt == GNS_F32) != (c.cdt == GNS_F32)) return GNS_ERR_UNSUPPORTED;
+  if (c.n % 8 || c.m % 8 || c.ldx % 8 || c.ldo % 8) return GNS_ERR_UNSUPPORTED;
+  if (c.batch > 1 && (c.sx % 8 || c.so % 8)) return GNS_ERR_UNSUPPORTED;
+  if (!aligned16(c.X) || !aligned16(c.O) || !aligned16(c.ws)) return GNS_ERR_UNSUPPORTED;
+  const size_t xb = ((size_t)(c.batch > 0 ? c.batch - 1 : 0) * c.sx + (size_t)(c.n - 1) * c.ldx + c.m) * esize(c.xdt);
+  const size_t ob = ((size_t)(c.batch > 0 ? c.batch - 1 : 0) * c.so + (size_t)(c.n - 1) * c.ldo + c.m) * esize(c.odt);
+  if (overlaps(c.X, xb, c.O, ob)) return GNS_ERR_INVALID_ARG;
+  const size_t need = ns_layout(nullptr, c.batch, c.n, c.m, c.cdt).bytes;
+  if (c.batch > 0 && (!c.ws || c.ws_bytes < need)) return GNS_ERR_WORKSPACE;
+  if (c.ws && c.batch > 0 && (overlaps(c.ws, need, c.O, ob) || overlaps(c.ws, need, c.X, xb))) return GNS_ERR_INVALID_ARG;
+  return GNS_OK;
+}
+
+// The only library state: a per-thread description of the last HIP failure, for
+// gns_last_error().  It never influences a computation.
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e, const char* what) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+  return GNS_ERR_HIP;
+}
+
+#define HIP_OK(expr)                                   \
+  do {                                                 \
+    const hipError_t e_ = (expr);                      \
+    if (e_ != hipSuccess) return hip_fail(e_, #expr);  \
+  } while (0)
+
+// Symmetric product on n x n (or the Gram product with K = m) for the whole batch.
+GemmParams symm_params(int n, int K, const void* A, long long lda, long long sA, const void* B, long long ldb,
+                       long long sB, void* D, long long ldd, long long sD) {
+  GemmParams g;
+  g.M = g.N = n;
+  g.K = K;
+  g.A = A; g.lda = lda; g.sA = sA;
+  g.B = B; g.ldb = ldb; g.sB = sB;
+  g.D = D; g.ldd = ldd; g.sD = sD;
+  return g;
+}
+
+int run_standard(const NsCall& c);
+
+int run_gram(const NsCall& c) {
+  const NsLayout L = ns_layout(c.ws, c.batch, c.n, c.m, c.cdt);
+  const int n = c.n, m = c.m, B = c.batch;
+  const long long nn = (long long)n * n, nm = (long long)n * m;
+  const float P = pow2_scale(c.cdt, n, m);
+  const gns_dtype cdt = c.cdt;
+  const float* s = c.s_given ? c.s_given : L.s;
+  if (!c.s_given) HIP_OK(launch_frob(c.X, c.xdt, c.ldx, c.sx, B, n, m, c.sch.eps, L.s, L.partials, c.stream));
+
+  // R0 = s^2 X X^T: operands in X's dtype, result in the iterate dtype
+  {
+    GemmParams g = symm_params(n, m, c.X, c.ldx, c.sx, c.X, c.ldx, c.sx, L.R, n, nn);
+    g.scale = s; g.alpha_pow = 2;
+    HIP_OK(launch_symm(c.xdt, cdt, g, B, c.stream, c.flops));
+  }
+  const void* cx = c.X; gns_dtype cxdt = c.xdt; long long cld = c.ldx, csx = c.sx; bool cx_orig = true;
+  bool q_identity = true;
+  void* Q = L.Q0; void* Qn = L.Q1;
+  const unsigned mask = c.sch.restart_after_mask;
+  auto restart_before = [&](int t) { return t >= 2 && (mask >> (t - 1)) & 1u; };
+
+  // rect product  out = (alpha) Q cx, with the scaling rules for cx described above
+  auto apply_q = [&](void* out, gns_dtype odt, long long ldo, long long so, bool final_out) -> int {
+    GemmParams g;
+    g.M = n; g.N = m; g.K = n;
+    g.A = Q; g.lda = n; g.sA = nn;
+    g.B = cx; g.ldb = cld; g.sB = csx;
+    g.D = out; g.ldd = ldo; g.sD = so;
+    const float out_mul = final_out ? 1.0f : P;      // stored X-like iterates carry P
+    if (cx_orig) {
+      if (cxdt == cdt) {
+        g.alpha = out_mul; g.scale = s; g.alpha_pow = 1;
+      } else {
+        g.b_mul = P; g.scale = s; g.b_pow = 1; g.alpha = out_mul / P;
+      }
+    } else {
+      g.alpha = out_mul / P;
+    }
+    HIP_OK(launch_rect(cdt, cxdt, odt, g, B, c.stream, c.flops));
+    return GNS_OK;
+  };
+
+  for (int t = 1; t <= c.sch.steps; ++t) {
+    const float a = c.sch.a[t - 1], b = c.sch.b[t - 1], cc = c.sch.c[t - 1];
+    if (restart_before(t) && !q_identity) {
+      void* xn = (cx == L.Xa) ? L.Xb : L.Xa;
+      int st = apply_q(xn, cdt, m, nm, false);
+      if (st) return st;
+      cx = xn; cxdt = cdt; cld = m; csx = nm; cx_orig = false;
+      GemmParams g = symm_params(n, m, cx, m, nm, cx, m, nm, L.R, n, nn);
+      g.alpha = 1.0f / (P * P);
+      HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
+      q_identity = true;
+    }
+    {  // Z = c R R + b R   (and Q = Z + a I while Q is the identity)
+      GemmParams g = symm_params(n, n, L.R, n, nn, L.R, n, nn, L.Z, n, nn);
+      g.alpha = cc; g.beta = b; g.C = L.R; g.ldc = n; g.sC = nn;
+      if (q_identity) { g.D2 = Q; g.ldd2 = n; g.sD2 = nn; g.delta = a; }
+      HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
+    }
+    if (!q_identity) {  // Q <- Q Z + a Q
+      GemmParams g = symm_params(n, n, Q, n, nn, L.Z, n, nn, Qn, n, nn);
+      g.beta = a; g.C = Q; g.ldc = n; g.sC = nn;
+      HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
+      std::swap(Q, Qn);
+    }
+    q_identity = false;
+    const bool need_r = t < c.sch.steps && !restart_before(t + 1);
+    if (need_r) {
+      GemmParams g1 = symm_params(n, n, L.R, n, nn, L.Z, n, nn, L.Y, n, nn);    // Y = R Z + a R
+      g1.beta = a; g1.C = L.R; g1.ldc = n; g1.sC = nn;
+      HIP_OK(launch_symm(cdt, cdt, g1, B, c.stream, c.flops));
+      GemmParams g2 = symm_params(n, n, L.Z, n, nn, L.Y, n, nn, L.R, n, nn);    // R = Z Y + a Y
+      g2.beta = a; g2.C = L.Y; g2.ldc = n; g2.sC = nn;
+      HIP_OK(launch_symm(cdt, cdt, g2, B, c.stream, c.flops));
+    }
+  }
+  return apply_q(c.O, c.odt, c.ldo, c.so, true);
+}
+
+// Standard quintic NS on the same kernels: X0 = P s X (iterate dtype), then per step
+// A = X X^T / P^2, B = c A A + b A, X <- B X + a X; finally O = X / P.
+int run_standard(const NsCall& c) {
+  const NsLayout L = ns_layout(c.ws, c.batch, c.n, c.m, c.cdt);
+  const int n = c.n, m = c.m, B = c.batch;
+  const long long nn = (long long)n * n, nm = (long long)n * m;
+  const float P = pow2_scale(c.cdt, n, m);
+  const float* s = c.s_given ? c.s_given : L.s;
+  if (!c.s_given) HIP_OK(launch_frob(c.X, c.xdt, c.ldx, c.sx, B, n, m, c.sch.eps, L.s, L.partials, c.stream));
+  HIP_OK(launch_cast_scale(c.X, c.xdt, c.ldx, c.sx, L.Sa, c.cdt, m, nm, B, n, m, P, s, 1, c.stream));
+  void* cur = L.Sa; void* nxt = L.Sb;
+  for (int t = 1; t <= c.sch.steps; ++t) {
+    const float a = c.sch.a[t - 1], b = c.sch.b[t - 1], cc = c.sch.c[t - 1];
+    GemmParams g1 = symm_params(n, m, cur, m, nm, cur, m, nm, L.A, n, nn);
+    g1.alpha = 1.0f / (P * P);
+    HIP_OK(launch_symm(c.cdt, c.cdt, g1, B, c.stream, c.flops));
+    GemmParams g2 = symm_params(n, n, L.A, n, nn, L.A, n, nn, L.Bm, n, nn);
+    g2.alpha = cc; g2.beta = b; g2.C = L.A; g2.ldc = n; g2.sC = nn;
+    HIP_OK(launch_symm(c.cdt, c.cdt, g2, B, c.stream, c.flops));
+    GemmParams g3;
+    g3.M = n; g3.N = m; g3.K = n;
+    g3.A = L.Bm; g3.lda = n; g3.sA = nn;
+    g3.B = cur; g3.ldb = m; g3.sB = nm;
+    g3.C = cur; g3.ldc = m; g3.sC = nm; g3.beta = a;
+    g3.D = nxt; g3.ldd = m; g3.sD = nm;
+    HIP_OK(launch_rect(c.cdt, c.cdt, c.cdt, g3, B, c.stream, c.flops));
+    std::swap(cur, nxt);
+  }
+  HIP_OK(launch_cast_scale(cur, c.cdt, m, nm, c.O, c.odt, c.ldo, c.so, B, n, m, 1.0f / P, nullptr, 0, c.stream));
+  return GNS_OK;
+}
+
+NsCall make_call(const void* X, gns_dtype xdt, long long ldx, long long sx, void* O, gns_dtype odt, long long ldo,
+                 long long so, int batch, int n, int m, gns_dtype cdt, const gns_schedule* sched, void* ws,
+                 size_t ws_bytes, hipStream_t stream, double* flops) {
+  NsCall c{};
+  c.X = X; c.xdt = xdt; c.ldx = ldx; c.sx = sx;
+  c.O = O; c.odt = odt; c.ldo = ldo; c.so = so;
+  c.batch = batch; c.n = n; c.m = m; c.cdt = cdt;
+  if (sched) c.sch = *sched; else gns_default_schedule(&c.sch);
+  c.ws = ws; c.ws_bytes = ws_bytes; c.stream = stream; c.flops = flops; c.s_given = nullptr;
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+void gns_default_schedule(gns_schedule* s) {
+  if (!s) return;
+  std::memset(s, 0, sizeof(*s));
+  s->steps = 5;
+  for (int t = 0; t < 5; ++t) { s->a[t] = 3.4445f; s->b[t] = -4.7750f; s->c[t] = 2.0315f; }
+  s->restart_after_mask = 1u << 2;    // restart after step 2 (before step 3)
+  s->eps = 1e-7f;
+  s->square_fallback = 1;
+}
+
+const char* gns_last_error(void) { return g_last_error; }
+
+const char* gns_status_string(int status) {
+  switch (status) {
+    case GNS_OK: return "GNS_OK";
+    case GNS_ERR_INVALID_ARG: return "GNS_ERR_INVALID_ARG";
+    case GNS_ERR_UNSUPPORTED: return "GNS_ERR_UNSUPPORTED";
+    case GNS_ERR_WORKSPACE: return "GNS_ERR_WORKSPACE";
+    case GNS_ERR_HIP: return "GNS_ERR_HIP";
+  }
+  return "GNS_UNKNOWN_STATUS";
+}
+
+size_t gns_frobenius_workspace_size(int batch, int n, int m) {
+  if (batch < 0 || n < 1 || m < 1) return 0;
+  return align_up(sizeof(float) * (size_t)batch * frob_partials_per_batch(n, m));
+}
+
+int gns_frobenius_scale(const void* X, gns_dtype x_dtype, long long ldx, long long stride_x, int batch, int n,
+                        int m, float eps, float* s_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(x_dtype) || batch < 0 || n < 1 || m < 1 || ldx < m) return GNS_ERR_INVALID_ARG;
+  if (batch == 0) return GNS_OK;
+  if (!X || !s_out) return GNS_ERR_INVALID_ARG;
+  if (batch > 1 && stride_x < (long long)n * ldx) return GNS_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return GNS_ERR_INVALID_ARG;
+  const int q = x_dtype == GNS_F32 ? 4 : 8;
+  if (m % q || ldx % q || (batch > 1 && stride_x % q) || !aligned16(X)) return GNS_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < gns_frobenius_workspace_size(batch, n, m)) return GNS_ERR_WORKSPACE;
+  HIP_OK(launch_frob(X, x_dtype, ldx, stride_x, batch, n, m, eps, s_out, (float*)workspace, stream));
+  return GNS_OK;
+}
+
+size_t gns_workspace_size(int batch, int n, int m, gns_dtype compute) {
+  if (batch < 0 || n < 1 || m < 1 || !valid_dtype(compute)) return 0;
+  return ns_layout(nullptr, batch, n, m, compute).bytes;
+}
+
+int gns_orthogonalize_batched(const void* X, gns_dtype x_dtype, long long ldx, long long stride_x, void* O,
+                              gns_dtype o_dtype, long long ldo, long long stride_o, int batch, int n, int m,
+                              gns_dtype compute, const gns_schedule* sched, void* workspace, size_t ws_bytes,
+                              hipStream_t stream, double* issued_flops) {
+  NsCall c = make_call(X, x_dtype, ldx, stride_x, O, o_dtype, ldo, stride_o, batch, n, m, compute, sched, workspace,
+                       ws_bytes, stream, issued_flops);
+  if (issued_flops) *issued_flops = 0.0;
+  const int st = check_ns(c);
+  if (st) return st;
+  if (batch == 0) return GNS_OK;
+  if (c.sch.square_fallback && n == m) return run_standard(c);
+  return run_gram(c);
+}
+
+int gns_newton_schulz_batched(const void* X, gns_dtype x_dtype, long long ldx, long long stride_x, void* O,
+                              gns_dtype o_dtype, long long ldo, long long stride_o, int batch, int n, int m,
+                              gns_dtype compute, const gns_schedule* sched, void* workspace, size_t ws_bytes,
+                              hipStream_t stream, double* issued_flops) {
+  NsCall c = make_call(X, x_dtype, ldx, stride_x, O, o_dtype, ldo, stride_o, batch, n, m, compute, sched, workspace,
+                       ws_bytes, stream, issued_flops);
+  c.sch.restart_after_mask = 0;
+  if (issued_flops) *issued_flops = 0.0;
+  const int st = check_ns(c);
+  if (st) return st;
+  if (batch == 0) return GNS_OK;
+  return run_standard(c);
+}
+
+static int check_gemm_common(int batch, gns_dtype in, gns_dtype out, const void* A, long long lda, long long sA,
+                             const void* D, long long ldd, long long sD) {
+  (void)sA; (void)sD;
+  if (!valid_dtype(in) || !valid_dtype(out) || batch < 0) return GNS_ERR_INVALID_ARG;
+  if (batch > 0 && (!A || !D)) return GNS_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(D)) return GNS_ERR_UNSUPPORTED;
+  (void)lda; (void)ldd;
+  return GNS_OK;
+}
+
+int symm_gemm(int batch, int n, int k, float alpha, const void* A, long long lda, long long stride_a, const void* B,
+              long long ldb, long long stride_b, float beta, const void* C, long long ldc, long long stride_c,
+              float gamma, void* D, long long ldd, long long stride_d, gns_dtype in_dtype, gns_dtype out_dtype,
+              hipStream_t stream) {
+  int st = check_gemm_common(batch, in_dtype, out_dtype, A, lda, stride_a, D, ldd, stride_d);
+  if (st) return st;
+  if (n < 0 || k < 0) return GNS_ERR_INVALID_ARG;
+  if (batch == 0 || n == 0) return GNS_OK;
+  if (!B || (beta != 0.0f && !C)) return GNS_ERR_INVALID_ARG;
+  if (lda < k || ldb < k || ldd < n || (C && ldc < n)) return GNS_ERR_INVALID_ARG;
+  if (batch > 1 && (stride_a < (long long)n * lda || stride_b < (long long)n * ldb || stride_d < (long long)n * ldd ||
+                    (C && stride_c < (long long)n * ldc)))
+    return GNS_ERR_INVALID_ARG;
+  const int q = in_dtype == GNS_F32 ? 4 : 8, qo = out_dtype == GNS_F32 ? 4 : 8;
+  if (n % 8 || k % q || lda % q || ldb % q || ldd % qo || (C && ldc % qo)) return GNS_ERR_UNSUPPORTED;
+  if (batch > 1 && (stride_a % q || stride_b % q || stride_d % qo || (C && stride_c % qo))) return GNS_ERR_UNSUPPORTED;
+  if (!aligned16(B) || (C && !aligned16(C))) return GNS_ERR_UNSUPPORTED;
+  GemmParams g = symm_params(n, k, A, lda, stride_a, B, ldb, stride_b, D, ldd, stride_d);
+  g.alpha = alpha; g.beta = beta; g.gamma = gamma;
+  if (C && beta != 0.0f) { g.C = C; g.ldc = ldc; g.sC = stride_c; }
+  HIP_OK(launch_symm(in_dtype, out_dtype, g, batch, stream, nullptr));
+  return GNS_OK;
+}
+
+int rect_gemm(int batch, int n, int k, int m, float alpha, const void* A, long long lda, long long stride_a,
+              gns_dtype a_dtype, const void* B, long long ldb, long long stride_b, gns_dtype b_dtype,
+              float b_prescale, float beta, const void* C, long long ldc, long long stride_c, void* D, long long ldd,
+              long long stride_d, gns_dtype out_dtype, hipStream_t stream) {
+  int st = check_gemm_common(batch, a_dtype, out_dtype, A, lda, stride_a, D, ldd, stride_d);
+  if (st) return st;
+  if (!valid_dtype(b_dtype) || n < 0 || k < 0 || m < 0) return GNS_ERR_INVALID_ARG;
+  if (batch == 0 || n == 0 || m == 0) return GNS_OK;
+  if (!rect_pair_supported(a_dtype, b_dtype)) return GNS_ERR_UNSUPPORTED;
+  if (a_dtype == b_dtype && b_prescale != 1.0f) return GNS_ERR_INVALID_ARG;
+  if (!B || (beta != 0.0f && !C)) return GNS_ERR_INVALID_ARG;
+  if (lda < k || ldb < m || ldd < m || (C && ldc < m)) return GNS_ERR_INVALID_ARG;
+  if (batch > 1 && (stride_a < (long long)n * lda || stride_b < (long long)k * ldb || stride_d < (long long)n * ldd ||
+                    (C && stride_c < (long long)n * ldc)))
+    return GNS_ERR_INVALID_ARG;
+  const int q = a_dtype == GNS_F32 ? 4 : 8, qo = out_dtype == GNS_F32 ? 4 : 8;
+  if (k % q || m % 8 || lda % q || ldb % q || ldd % qo || (C && ldc % qo)) return GNS_ERR_UNSUPPORTED;
+  if (batch > 1 && (stride_a % q || stride_b % q || stride_d % qo || (C && stride_c % qo))) return GNS_ERR_UNSUPPORTED;
+  if (!aligned16(B) || (C && !aligned16(C))) return GNS_ERR_UNSUPPORTED;
+  GemmParams g;
+  g.M = n; g.N = m; g.K = k;
+  g.A = A; g.lda = lda; g.sA = stride_a;
+  g.B = B; g.ldb = ldb; g.sB = stride_b;
+  g.D = D; g.ldd = ldd; g.sD = stride_d;
+  g.alpha = alpha; g.beta = beta; g.b_mul = b_prescale;
+  if (C && beta != 0.0f) { g.C = C; g.ldc = ldc; g.sC = stride_c; }
+  HIP_OK(launch_rect(a_dtype, b_dtype, out_dtype, g, batch, stream, nullptr));
+  return GNS_OK;
+}
+
+// ---- Dion3 ------------------------------------------------------------------------
+
+static int check_dion3_matrix(const void* P, int N, int m, long long ld) {
+  if (!P || N < 1 || m < 1 || ld < m) return GNS_ERR_INVALID_ARG;
+  if (m % 8 || ld % 8 || !aligned16(P)) return GNS_ERR_UNSUPPORTED;
+  return GNS_OK;
+}
+
+int dion3_accumulate_score(void* M, const void* G, int N, int m, long long ld, int score_norm, double* score,
+                           double* sumsq, hipStream_t stream) {
+  int st = check_dion3_matrix(M, N, m, ld);
+  if (st) return st;
+  st = check_dion3_matrix(G, N, m, ld);
+  if (st) return st;
+  if (!score || (score_norm != 1 && score_norm != 2)) return GNS_ERR_INVALID_ARG;
+  HIP_OK(launch_accumulate_score((uint16_t*)M, (const uint16_t*)G, N, m, ld, score_norm, score, sumsq, stream));
+  return GNS_OK;
+}
+
+int dion3_select_topk(const double* score, int N, int k, int* S, hipStream_t stream) {
+  if (!score || !S || N < 1 || k < 1 || k > N) return GNS_ERR_INVALID_ARG;
+  HIP_OK(launch_topk(score, N, k, S, stream));
+  return GNS_OK;
+}
+
+int dion3_gather_feedback(void* M, int N, int m, long long ld, const int* S, int k, float mu, void* X, long long ldx,
+                          hipStream_t stream) {
+  int st = check_dion3_matrix(M, N, m, ld);
+  if (st) return st;
+  if (!S || !X || k < 1 || k > N || ldx < m || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
+  if (ldx % 8 || !aligned16(X)) return GNS_ERR_UNSUPPORTED;
+  HIP_OK(launch_gather_feedback((uint16_t*)M, N, m, ld, S, k, mu, (uint16_t*)X, ldx, stream));
+  return GNS_OK;
+}
+
+int dion3_apply_update(void* W, int N, int m, long long ld, const int* S, int k, const void* O, gns_dtype o_dtype,
+                       long long ldo, float lr, float wd, hipStream_t stream) {
+  int st = check_dion3_matrix(W, N, m, ld);
+  if (st) return st;
+  if (!S || !O || k < 1 || k > N || ldo < m || !std::isfinite(lr) || !std::isfinite(wd)) return GNS_ERR_INVALID_ARG;
+  if (o_dtype != GNS_BF16 && o_dtype != GNS_F32) return GNS_ERR_UNSUPPORTED;
+  if (ldo % 8 || !aligned16(O)) return GNS_ERR_UNSUPPORTED;
+  HIP_OK(launch_apply_update((uint16_t*)W, N, m, ld, S, k, O, o_dtype, ldo, lr, wd, stream));
+  return GNS_OK;
+}
+
+struct Dion3Layout {
+  double* score; double* sumsq; float* s; void* X; void* O; void* gns_ws; size_t gns_bytes; size_t bytes;
+};
+
+static Dion3Layout dion3_layout(void* base, int N, int m, int k, gns_dtype cdt) {
+  Carver c{reinterpret_cast<uint8_t*>(base), 0};
+  Dion3Layout L{};
+  L.score = (double*)c.take(sizeof(double) * (size_t)N);
+  L.sumsq = (double*)c.take(sizeof(double) * (size_t)N);
+  L.s = (float*)c.take(sizeof(float));
+  L.X = c.take((size_t)k * m * 2);
+  L.O = c.take((size_t)k * m * 2);
+  L.gns_bytes = ns_layout(nullptr, 1, k, m, cdt).bytes;
+  L.gns_ws = c.take(L.gns_bytes);
+  L.bytes = c.off;
+  return L;
+}
+
+size_t dion3_workspace_size(int N, int m, int k, gns_dtype compute) {
+  if (N < 1 || m < 1 || k < 1 || !valid_dtype(compute)) return 0;
+  return dion3_layout(nullptr, N, m, k, compute).bytes;
+}
+
+int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int k, float lr, float weight_decay,
+               float mu, int score_norm, gns_dtype compute, const gns_schedule* sched, int* S_out, void* O_out,
+               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dion3_matrix(W, N, m, ld);
+  if (st) return st;
+  if ((st = check_dion3_matrix(M, N, m, ld))) return st;
+  if ((st = check_dion3_matrix(G, N, m, ld))) return st;
+  if (!S_out || k < 1 || k > N || k > m) return GNS_ERR_INVALID_ARG;
+  if (score_norm != 1 && score_norm != 2) return GNS_ERR_INVALID_ARG;
+  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
+  if (!valid_dtype(compute)) return GNS_ERR_INVALID_ARG;
+  if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
+  if (k % 8) return GNS_ERR_UNSUPPORTED;
+  if (O_out && !aligned16(O_out)) return GNS_ERR_UNSUPPORTED;
+  gns_schedule sch;
+  if (sched) sch = *sched; else gns_default_schedule(&sch);
+  if ((st = check_schedule(sch))) return st;
+  const Dion3Layout L = dion3_layout(workspace, N, m, k, compute);
+  if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
+
+  HIP_OK(launch_accumulate_score((uint16_t*)M, (const uint16_t*)G, N, m, ld, score_norm, L.score, L.sumsq, stream));
+  HIP_OK(launch_topk(L.score, N, k, S_out, stream));
+  HIP_OK(launch_gather_feedback((uint16_t*)M, N, m, ld, S_out, k, mu, (uint16_t*)L.X, m, stream));
+  HIP_OK(launch_selected_sumsq(L.sumsq, S_out, k, N, sch.eps, L.s, stream));
+  void* O = O_out ? O_out : L.O;
+  NsCall c = make_call(L.X, GNS_BF16, m, (long long)k * m, O, GNS_BF16, m, (long long)k * m, 1, k, m, compute, &sch,
+                       L.gns_ws, L.gns_bytes, stream, nullptr);
+  c.s_given = L.s;
+  if ((st = check_ns(c))) return st;
+  st = (sch.square_fallback && k == m) ? run_standard(c) : run_gram(c);
+  if (st) return st;
+  HIP_OK(launch_apply_update((uint16_t*)W, N, m, ld, S_out, k, O, GNS_BF16, m, lr, weight_decay, stream));
+  return GNS_OK;
+}
+
+}  // extern "C"

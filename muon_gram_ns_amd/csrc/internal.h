@@ -1,0 +1,58 @@
+// Internal (C++) interface between the C-ABI / orchestration layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gns.h"
+
+namespace gns {
+
+// Parameters of one batched GEMM launch (see gemm.hip).
+//   symmetric (NT, lower tiles):  D = alpha' A B^T + beta C + gamma I, A,B: M x K
+//   rectangular (NN):             D = alpha' A B + beta C,            A: M x K, B: K x N
+// alpha' = alpha * scale[b]^alpha_pow.  NN with B of another 16-bit type converts
+// B on load after multiplying by b_mul * scale[b]^b_pow.  D2 (symmetric only,
+// nullable) receives the same values + delta on the diagonal.
+struct GemmParams {
+  int M = 0, N = 0, K = 0;
+  const void* A = nullptr; long long lda = 0, sA = 0;
+  const void* B = nullptr; long long ldb = 0, sB = 0;
+  const void* C = nullptr; long long ldc = 0, sC = 0;
+  void* D = nullptr; long long ldd = 0, sD = 0;
+  void* D2 = nullptr; long long ldd2 = 0, sD2 = 0;
+  float alpha = 1.f, beta = 0.f, gamma = 0.f, delta = 0.f;
+  const float* scale = nullptr; int alpha_pow = 0;
+  float b_mul = 1.f; int b_pow = 0;
+  int tiles_m = 0, tiles_n = 0;
+};
+
+// flops (nullable): incremented by the MFMA flops the launch issues.
+hipError_t launch_symm(gns_dtype in, gns_dtype out, const GemmParams& p, int batch,
+                       hipStream_t stream, double* flops);
+hipError_t launch_rect(gns_dtype a, gns_dtype b, gns_dtype out, const GemmParams& p, int batch,
+                       hipStream_t stream, double* flops);
+bool rect_pair_supported(gns_dtype a, gns_dtype b);
+
+// Frobenius scale: partial sums of squares, then s[b] = mul / (sqrt(sum) + eps).
+int frob_partials_per_batch(int n, int m);
+hipError_t launch_frob(const void* X, gns_dtype dt, long long ldx, long long stride_x, int batch,
+                       int n, int m, float eps, float* s_out, float* partials, hipStream_t stream);
+// Y = cast(mul * scale[b]^pow * X) elementwise, for batch x n x m matrices.
+hipError_t launch_cast_scale(const void* X, gns_dtype xdt, long long ldx, long long sx, void* Y,
+                             gns_dtype ydt, long long ldy, long long sy, int batch, int n, int m,
+                             float mul, const float* scale, int pow, hipStream_t stream);
+
+// Dion3 element-wise kernels (dion3.hip).
+hipError_t launch_accumulate_score(uint16_t* M, const uint16_t* G, int N, int m, long long ld,
+                                   int score_norm, double* score, double* sumsq, hipStream_t s);
+hipError_t launch_topk(const double* score, int N, int k, int* S, hipStream_t s);
+hipError_t launch_gather_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, float mu,
+                                  uint16_t* X, long long ldx, hipStream_t s);
+hipError_t launch_apply_update(uint16_t* W, int N, int m, long long ld, const int* S, int k,
+                               const void* O, gns_dtype o_dtype, long long ldo, float lr, float wd,
+                               hipStream_t s);
+// s[0] = 1 / (sqrt(sum_i sumsq[S[i]]) + eps): the Frobenius scale of the rows S.
+hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int k, int N, float eps,
+                                 float* s_out, hipStream_t s);
+
+}  // namespace gns

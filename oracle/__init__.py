@@ -30,6 +30,7 @@ from .newton_schulz import (  # noqa: F401
     JORDAN_ABC, EPS, quintic, quintic_composed, normalize, newton_schulz,
     gram_newton_schulz, gram_newton_schulz_schedule,
 )
+from .gemm import symm_gemm_ref, rect_gemm_ref  # noqa: F401
 from .dion3 import (  # noqa: F401
     k_from_fraction, accumulate, row_scores, select_topk, gather_rows, error_feedback, weight_update,
     dion3_step,

@@ -1,0 +1,134 @@
+"""GPU parity of the Dion3 step against the oracle.
+
+Bit-exact: the accumulated momentum M, the selected row set S (ascending), the error
+feedback on M, and the weight update given the same (seeded) O.  Within tolerance:
+the orthogonalised submatrix O (relative Frobenius <= 2e-2 against float64 standard
+NS of the oracle's gathered rows) and the selected rows of W after a full step (they
+depend on O: elementwise within one bf16 rounding plus lr times O's tolerance);
+unselected rows of W are bit-exact.
+"""
+import numpy as np
+import pytest
+
+import synth
+import oracle
+from oracle import (accumulate, row_scores, select_topk, error_feedback, weight_update, newton_schulz,
+                    bf16_to_f64, f64_to_bf16_rne, k_from_fraction)
+from gpu_helpers import to_dev, to_f64, rel_fro, announce, bits
+
+pytestmark = pytest.mark.gpu
+
+
+def w_within_bound(w_gpu_bits, w_ref_bits, lr, o_ref, o_tol=2e-2):
+    """W after a step depends on O, which is only required within o_tol (relative).
+    Elementwise bound: one bf16 rounding of the larger magnitude, plus lr times the
+    allowed error of O (o_tol * max |O|).  Near W ~ lr O the result crosses zero,
+    where an ulp count would be meaningless, hence an absolute bound."""
+    a, b = bf16_to_f64(w_gpu_bits), bf16_to_f64(w_ref_bits)
+    # one bf16 ulp is at most 2^-7 of the magnitude (8 significant bits)
+    bound = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + lr * o_tol * np.abs(o_ref).max()
+    ratio = np.abs(a - b) / bound
+    print(f"W: max |dW|/bound = {ratio.max():.3f}, changed elements {(a != b).mean():.4f}")
+    return bool(np.all(ratio <= 1.0))
+
+
+@pytest.mark.parametrize("norm", [1, 2])
+def test_accumulate_score_bit_exact(gns_mod, norm):
+    announce(f"dion3 accumulate_score norm={norm}")
+    w, g, m = synth.dion3_state(n=300, m=1024, seed=11)
+    M = to_dev(m, "bf16")
+    score, sumsq = gns_mod.dion3_accumulate_score(M, to_dev(g, "bf16"), norm)
+    m1 = accumulate(m, g)
+    assert np.array_equal(bits(M), m1)
+    ref = row_scores(m1, "l1" if norm == 1 else "l2")
+    assert np.allclose(score.cpu().numpy(), ref, rtol=1e-13, atol=0)
+    assert np.allclose(sumsq.cpu().numpy(), row_scores(m1, "l2"), rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("N,k", [(1, 1), (9, 4), (1000, 250), (8192, 2048), (8192, 1024), (20000, 3)])
+def test_topk_bit_exact_with_ties(gns_mod, N, k):
+    announce(f"dion3 topk N={N} k={k}")
+    rng = np.random.default_rng(N + k)
+    scores = rng.integers(0, 50, size=N).astype(np.float64) * 0.125   # many exact ties
+    torch = __import__("torch")
+    S = gns_mod.dion3_select_topk(torch.from_numpy(scores).cuda(), k).cpu().numpy()
+    assert np.array_equal(S, select_topk(scores, k))
+
+
+def test_topk_distinct_scores(gns_mod):
+    announce("dion3 topk distinct")
+    rng = np.random.default_rng(5)
+    scores = rng.random(8192) * 100
+    torch = __import__("torch")
+    for k in (1, 17, 2048, 8192):
+        S = gns_mod.dion3_select_topk(torch.from_numpy(scores).cuda(), k).cpu().numpy()
+        assert np.array_equal(S, select_topk(scores, k))
+
+
+def test_gather_feedback_bit_exact(gns_mod):
+    announce("dion3 gather_feedback")
+    _, _, m = synth.dion3_state(n=200, m=512, seed=12)
+    S = np.array(sorted(np.random.default_rng(1).choice(200, 37, replace=False)), dtype=np.int32)
+    torch = __import__("torch")
+    M = to_dev(m, "bf16")
+    X = gns_mod.dion3_gather_feedback(M, torch.from_numpy(S).cuda(), 0.95)
+    assert np.array_equal(bits(X), m[S])
+    assert np.array_equal(bits(M), error_feedback(m, S, 0.95))
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+@pytest.mark.parametrize("o_dt", ["bf16", "f32"])
+def test_apply_update_bit_exact(gns_mod, wd, o_dt):
+    announce(f"dion3 apply_update wd={wd} O={o_dt}")
+    w, _, _ = synth.dion3_state(n=160, m=768, seed=13)
+    rng = np.random.default_rng(2)
+    S = np.array(sorted(rng.choice(160, 40, replace=False)), dtype=np.int32)
+    o_st = synth.to_storage(rng.standard_normal((40, 768)) * 0.01, o_dt)
+    o = synth.bf16_bits_to_f32(o_st).astype(np.float64) if o_dt == "bf16" else o_st.astype(np.float64)
+    torch = __import__("torch")
+    W = to_dev(w, "bf16")
+    gns_mod.dion3_apply_update(W, torch.from_numpy(S).cuda(), to_dev(o_st, o_dt), 0.02, wd)
+    assert np.array_equal(bits(W), weight_update(w, S, o, 0.02, wd))
+
+
+@pytest.mark.parametrize("norm", [1, 2])
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_dion3_step_small(gns_mod, norm, wd):
+    announce(f"dion3 step 512x2048 norm={norm} wd={wd}")
+    w, g, m = synth.dion3_state(n=512, m=2048, seed=14)
+    k = k_from_fraction(0.25, 512)
+    lr = 0.01 / np.sqrt(0.25)
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    S, O = gns_mod.dion3_step(W, M, G, k, lr, weight_decay=wd, mu=0.95, score_norm=norm, return_O=True)
+    w_ref, m_ref, S_ref, O_ref = oracle.dion3_step(w, m, g, k, lr, wd=wd, mu=0.95, norm="l1" if norm == 1 else "l2")
+    assert np.array_equal(S.cpu().numpy(), S_ref)
+    assert np.array_equal(bits(M), m_ref)
+    assert rel_fro(to_f64(O), O_ref) <= 2e-2
+    wg = bits(W)
+    assert w_within_bound(wg, w_ref, lr, O_ref)
+    rest = np.setdiff1d(np.arange(512), S_ref)
+    assert np.array_equal(wg[rest], w_ref[rest])     # unselected rows do not depend on O
+
+
+@pytest.mark.timeout(900)
+def test_dion3_step_full_size(gns_mod):
+    """The 8192 x 28672 workload at f = 1/4 and 1/8 with l2 row scores."""
+    w, g, m = synth.dion3_state()
+    m1 = accumulate(m, g)
+    sc = row_scores(m1, "l2")
+    for f in (0.25, 0.125):
+        announce(f"dion3 step 8192x28672 f={f}")
+        k = k_from_fraction(f, 8192)
+        S_ref = select_topk(sc, k)
+        W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+        S, O = gns_mod.dion3_step(W, M, G, k, 0.01 / np.sqrt(f), weight_decay=0.0, mu=0.95, score_norm=2,
+                                  return_O=True)
+        assert np.array_equal(S.cpu().numpy(), S_ref)
+        assert np.array_equal(bits(M), error_feedback(m1, S_ref, 0.95))
+        rest = np.setdiff1d(np.arange(8192), S_ref)
+        assert np.array_equal(bits(W)[rest], w[rest])
+        if f == 0.125:   # one full-size orthogonalisation check (oracle cost ~1e12 flops)
+            O_ref = newton_schulz(bf16_to_f64(m1[S_ref]))
+            e = rel_fro(to_f64(O), O_ref)
+            print(f"f={f} O rel err {e:.3e}")
+            assert e <= 2e-2

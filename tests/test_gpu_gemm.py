@@ -1,0 +1,98 @@
+"""GPU parity of the two MFMA GEMM kernels against the oracle's float64 definitions.
+
+Shapes span several 128 x 128 output tiles and ragged tails (n, k, m not multiples
+of the tile), every operand/output dtype combination the library accepts, the
+alpha/beta/gamma epilogue, batching, and bitwise symmetry of the symmetric output.
+Tolerances (relative Frobenius, and max-abs relative to max |ref|): the inputs are
+exact in their stored dtype and products accumulate in fp32, so the error is the
+final rounding to the output dtype plus fp32 accumulation:
+  bf16 out 6e-3, f16 out 1e-3, f32 out 2e-5 (K <= 1024).
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import symm_gemm_ref, rect_gemm_ref
+from gpu_helpers import to_dev, to_f64, rel_fro, announce
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 6e-3, "f16": 1e-3, "f32": 2e-5}
+
+
+def stored(rng, shape, dt, scale=1.0):
+    x = scale * rng.standard_normal(shape)
+    st = synth.to_storage(x, dt)
+    if dt == "bf16":
+        return st, synth.bf16_bits_to_f32(st).astype(np.float64)
+    return st, st.astype(np.float64)
+
+
+def check(got, ref, tol):
+    e = rel_fro(got, ref)
+    mx = float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-300))
+    assert e <= tol and mx <= 4 * tol, (e, mx)
+
+
+@pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("bf16", "f16"), ("bf16", "f32"), ("f16", "f16"),
+                                          ("f16", "f32"), ("f32", "f32"), ("f16", "bf16")])
+@pytest.mark.parametrize("n,k", [(8, 8), (136, 72), (256, 512), (264, 200)])
+def test_symm_gemm_parity(gns_mod, in_dt, out_dt, n, k):
+    announce(f"symm_gemm {in_dt}->{out_dt} n={n} k={k}")
+    rng = np.random.default_rng(n * 1000 + k)
+    batch = 2
+    a_st, a = stored(rng, (batch, n, k), in_dt)
+    b_st, b = stored(rng, (batch, n, k), in_dt)
+    c_st, c = stored(rng, (batch, n, n), out_dt)
+    A, B, C = to_dev(a_st, in_dt), to_dev(b_st, in_dt), to_dev(c_st, out_dt)
+    D = gns_mod.symm_gemm(A, B, C, alpha=0.75, beta=-0.5, gamma=1.25, out_dtype=out_dt)
+    got = to_f64(D)
+    ref = symm_gemm_ref(a, b, c, alpha=0.75, beta=-0.5, gamma=1.25)
+    check(got, ref, TOL[out_dt])
+    Dh = D.cpu()
+    assert bool((Dh == Dh.transpose(1, 2)).all()), "output not bitwise symmetric"
+
+
+@pytest.mark.parametrize("in_dt", ["bf16", "f16", "f32"])
+def test_syrk_same_operand(gns_mod, in_dt):
+    announce(f"syrk {in_dt}")
+    rng = np.random.default_rng(7)
+    x_st, x = stored(rng, (3, 200, 776), in_dt, scale=0.05)
+    X = to_dev(x_st, in_dt)
+    D = gns_mod.symm_gemm(X, X, out_dtype="f32")
+    check(to_f64(D), symm_gemm_ref(x, x), TOL["f32"])
+
+
+@pytest.mark.parametrize("a_dt,b_dt,out_dt", [("bf16", "bf16", "bf16"), ("f16", "f16", "f16"),
+                                              ("f32", "f32", "f32"), ("f16", "bf16", "f32"),
+                                              ("bf16", "f16", "bf16"), ("f16", "f16", "f32")])
+@pytest.mark.parametrize("n,k,m", [(8, 8, 8), (136, 72, 200), (256, 256, 512), (120, 264, 1032)])
+def test_rect_gemm_parity(gns_mod, a_dt, b_dt, out_dt, n, k, m):
+    announce(f"rect_gemm {a_dt}x{b_dt}->{out_dt} n={n} k={k} m={m}")
+    rng = np.random.default_rng(n + 7 * k + 13 * m)
+    batch = 2
+    a_st, a = stored(rng, (batch, n, k), a_dt)
+    b_st, b = stored(rng, (batch, k, m), b_dt)
+    c_st, c = stored(rng, (batch, n, m), out_dt)
+    pre = 1.0 if a_dt == b_dt else 0.5
+    D = gns_mod.rect_gemm(to_dev(a_st, a_dt), to_dev(b_st, b_dt), to_dev(c_st, out_dt), alpha=1.5, beta=0.25,
+                          b_prescale=pre, out_dtype=out_dt)
+    # with a dtype conversion the B operand is rounded to a_dt after the prescale
+    if a_dt != b_dt:
+        b = synth.to_storage(pre * b, a_dt)
+        b = (synth.bf16_bits_to_f32(b) if a_dt == "bf16" else b).astype(np.float64)
+        pre_ref = 1.0
+    else:
+        pre_ref = 1.0
+    ref = rect_gemm_ref(a, pre_ref * b, c, alpha=1.5, beta=0.25)
+    check(to_f64(D), ref, TOL[out_dt] if out_dt != "f32" else (2e-5 if a_dt == b_dt else 2e-5))
+
+
+def test_frobenius_scale(gns_mod):
+    announce("frobenius_scale")
+    rng = np.random.default_rng(3)
+    for dt in ("bf16", "f16", "f32"):
+        x_st, x = stored(rng, (5, 40, 264), dt, scale=0.3)
+        s = gns_mod.frobenius_scale(to_dev(x_st, dt), eps=1e-7).cpu().numpy()
+        ref = 1.0 / (np.sqrt((x * x).sum(axis=(1, 2))) + 1e-7)
+        assert np.allclose(s, ref, rtol=2e-6, atol=0)

@@ -1,0 +1,134 @@
+"""CPU-only checks of the boundary and host logic (no kernel is launched):
+
+* libgns.so loads and exports every function include/gns.h declares;
+* argument validation rejects bad calls before any launch (n > m, null pointers,
+  misalignment, short workspace, bad schedule, unsupported dtype pairs);
+* workspace-size queries;
+* the FLOP formulas against the savings the Dion3 pages state (55% / 68% at T = 5,
+  alpha = 4) and the restart cost 3 (alpha - 1) n^3.
+"""
+import ctypes
+import json
+import os
+
+import pytest
+
+import muon_gram_ns_amd as gns
+from muon_gram_ns_amd import flops
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")))
+L = gns.lib
+BF16, F16, F32 = gns.GNS_BF16, gns.GNS_F16, gns.GNS_F32
+OK, INVALID, UNSUP, WS = 0, -1, -2, -3
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: every call here fails validation
+
+
+def test_exports_every_declared_symbol():
+    names = gns.header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert L.gns_status_string(0) == b"GNS_OK"
+    assert L.gns_status_string(-3) == b"GNS_ERR_WORKSPACE"
+
+
+def test_default_schedule_matches_pages():
+    s = gns.default_schedule()
+    a, b, c = GOLD["ns_coefficients"]["value"]
+    assert s.steps == GOLD["ns_steps"]["value"]
+    assert all(abs(s.a[t] - a) < 1e-6 and abs(s.b[t] - b) < 1e-6 and abs(s.c[t] - c) < 1e-6 for t in range(5))
+    # restart before step 3 == after step 2
+    assert s.restart_after_mask == 1 << (GOLD["restart_before_step"]["value"] - 1)
+    assert abs(s.eps - GOLD["ns_eps"]["value"]) < 1e-12
+
+
+def ortho(X=FAKE, xdt=BF16, ldx=256, sx=64 * 256, O=FAKE * 3, odt=BF16, ldo=256, so=64 * 256, B=1, n=64, m=256,
+          cdt=F16, sched=None, ws=FAKE * 50, wsb=None, fn="gns_orthogonalize_batched"):
+    if wsb is None:
+        wsb = L.gns_workspace_size(B, n, m, cdt)
+    return getattr(L, fn)(X, xdt, ldx, sx, O, odt, ldo, so, B, n, m, cdt,
+                          ctypes.byref(sched) if sched else None, ws, wsb, None, None)
+
+
+def test_validation_rejects_before_launch():
+    assert ortho(n=512, m=256) == INVALID                 # n > m
+    assert ortho(X=None) == INVALID
+    assert ortho(O=None) == INVALID
+    assert ortho(ldx=128) == INVALID                       # ld < m
+    assert ortho(n=60, m=256) == UNSUP                     # n not a multiple of 8
+    assert ortho(X=FAKE + 2) == UNSUP                      # misaligned
+    assert ortho(wsb=16) == WS
+    assert ortho(ws=None) == WS
+    assert ortho(xdt=F32, cdt=F16) == UNSUP                # fp32 input needs fp32 iterates
+    assert ortho(xdt=BF16, cdt=F32) == UNSUP
+    assert ortho(cdt=7) == INVALID
+    assert ortho(O=FAKE) == INVALID                        # O aliases X
+    bad = gns.default_schedule()
+    bad.restart_after_mask = 1 << 5                        # restart after the last step
+    assert ortho(sched=bad) == INVALID
+    bad = gns.default_schedule()
+    bad.steps = 0
+    assert ortho(sched=bad) == INVALID
+    assert ortho(fn="gns_newton_schulz_batched", n=512, m=256) == INVALID
+    assert ortho(B=0) == OK                                # empty batch: nothing to do
+
+
+def test_gemm_and_dion3_validation():
+    # symm_gemm: k not a multiple of 8 for 16-bit operands
+    assert L.symm_gemm(1, 64, 60, 1.0, FAKE, 64, 0, FAKE, 64, 0, 0.0, None, 64, 0, 0.0, FAKE * 2, 64, 0,
+                       BF16, BF16, None) == UNSUP
+    assert L.symm_gemm(1, 64, 64, 1.0, FAKE, 64, 0, None, 64, 0, 0.0, None, 64, 0, 0.0, FAKE * 2, 64, 0,
+                       BF16, BF16, None) == INVALID
+    # rect_gemm: unsupported dtype pair, prescale with equal dtypes
+    assert L.rect_gemm(1, 64, 64, 64, 1.0, FAKE, 64, 0, F32, FAKE, 64, 0, BF16, 1.0, 0.0, None, 64, 0,
+                       FAKE * 2, 64, 0, F32, None) == UNSUP
+    assert L.rect_gemm(1, 64, 64, 64, 1.0, FAKE, 64, 0, BF16, FAKE, 64, 0, BF16, 2.0, 0.0, None, 64, 0,
+                       FAKE * 2, 64, 0, BF16, None) == INVALID
+    # dion3: k > N, k > m, bad norm, short workspace
+    sched = gns.default_schedule()
+    args = lambda k, norm=1, wsb=1 << 40: (FAKE, FAKE * 2, FAKE * 3, 64, 256, 256, k, 0.02, 0.0, 0.95, norm, F16,
+                                            ctypes.byref(sched), FAKE * 4, None, FAKE * 5, wsb, None)
+    assert L.dion3_step(*args(65)) == INVALID
+    assert L.dion3_step(*args(16, norm=3)) == INVALID
+    assert L.dion3_step(*args(16, wsb=8)) == WS
+    assert L.dion3_select_topk(FAKE, 10, 11, FAKE, None) == INVALID
+    assert L.dion3_select_topk(FAKE, 10, 0, FAKE, None) == INVALID
+
+
+def test_workspace_sizes_grow_with_problem():
+    a = L.gns_workspace_size(1, 1024, 4096, F16)
+    b = L.gns_workspace_size(2, 1024, 4096, F16)
+    c = L.gns_workspace_size(1, 1024, 4096, F32)
+    assert 0 < a < b and a < c
+    # 5 n x n iterates + 2 X-shaped buffers in fp16, plus small scalars
+    assert a >= (5 * 1024 * 1024 + 2 * 1024 * 4096) * 2
+    assert L.dion3_workspace_size(8192, 28672, 2048, F16) > 2 * 2048 * 28672 * 2
+
+
+def test_pages_flop_savings():
+    g = GOLD["flop_savings_T5_alpha4"]
+    gram = flops.pages_gram(5, 4)
+    assert abs((1 - gram / flops.pages_standard_symmetric(5, 4)) - g["vs_standard_symmetric"]) < 0.01
+    assert abs((1 - gram / flops.pages_standard_plain(5, 4)) - g["vs_standard_plain"]) < 0.01
+    # equal cost at alpha = 1 without restart is NOT claimed; with one restart the schedule
+    # costs pages_gram + restart_extra, which is what libgns runs
+    n, m = 1024, 4096
+    exact = flops.gram_schedule(n, m, 5, (2,))
+    approx = (flops.pages_gram(5, 4) + flops.pages_restart_extra(4)) * n ** 3
+    assert abs(exact / approx - 1) < 0.01
+    assert flops.standard_ns_nominal(n, m) == flops.pages_standard_plain(5, 4) * n ** 3
+
+
+@pytest.mark.parametrize("alpha", [1, 2, 4, 8, 14, 28])
+def test_gram_cheaper_than_standard_for_alpha_above_one(alpha):
+    n = 512
+    g = flops.gram_schedule(n, alpha * n)
+    s = flops.standard_schedule(n, alpha * n)
+    if alpha == 1:
+        assert g >= s * 0.99     # no saving (and the restart is not free) at alpha = 1
+    else:
+        assert g < s
