@@ -22,7 +22,9 @@
  *   - Matrices are row-major.  "ld" is the row stride in elements, "stride" the batch
  *     stride in elements.  Rows must start 16-byte aligned: ld, stride, and the
  *     column counts n, m, k must be multiples of 8 (16-bit types) or 4 (fp32), and
- *     device pointers 16-byte aligned; otherwise GNS_ERR_UNSUPPORTED.
+ *     device pointers 16-byte aligned; each operand matrix must span less than
+ *     2 GiB (the kernels address it with 32-bit offsets); otherwise
+ *     GNS_ERR_UNSUPPORTED (GNS_ERR_HIP from symm_gemm / rect_gemm).
  *   - The caller owns every buffer, including the workspace.  The library allocates
  *     nothing and keeps no state between calls (apart from the per-thread text of
  *     gns_last_error); every call is asynchronous on

@@ -12,7 +12,8 @@ import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgns.so")
+# GNS_LIBRARY may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("GNS_LIBRARY") or os.path.join(HERE, "libgns.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "gns.h")
 
 if not os.path.exists(LIB_PATH):
@@ -175,6 +176,7 @@ def _ns(fn_name, X, out, compute, schedule, want_flops):
     X3, B, n, m, ldx, sx = _mat3(X)
     if out is None:
         out = torch.empty((B, n, m), dtype=X.dtype, device=X.device)
+    _expect(out, "out", device=X.device)
     O3, Bo, no, mo, ldo, so = _mat3(out)
     if (Bo, no, mo) != (B, n, m):
         raise ValueError("output shape mismatch")
@@ -212,51 +214,80 @@ def frobenius_scale(X, eps=1e-7):
     return s
 
 
+def _expect(t, name, dtype=None, shape=None, device=None):
+    """The C ABI receives raw pointers, so every tensor's dtype, shape and device are
+    checked here: a mismatch would make a kernel read or write past an allocation."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    _dev(t)
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
 def symm_gemm(A, B=None, C=None, alpha=1.0, beta=0.0, gamma=0.0, out=None, out_dtype=None):
-    """D = alpha A B^T + beta C + gamma I (lower tiles, mirrored) for [batch, n, k] A, B."""
+    """D = alpha A B^T + beta C + gamma I (lower tiles, mirrored) for [batch, n, k] A, B.
+    C and the output are [batch, n, n] in the output dtype."""
     torch = _torch()
     _dev(A)
+    squeeze = A.dim() == 2
     B = A if B is None else B
     A3, nb, n, k, lda, sa = _mat3(A)
-    B3, nb2, n2, k2, ldb, sb = _mat3(B)
-    if (nb2, n2, k2) != (nb, n, k):
-        raise ValueError("A and B shapes differ")
+    _expect(B, "B", dtype=A.dtype, shape=A.shape, device=A.device)
+    B3, _, _, _, ldb, sb = _mat3(B)
     odt = dtype_code(A3) if out_dtype is None else code_of(out_dtype)
+    tdt = torch_dtype(odt)
     if out is None:
-        out = torch.empty((nb, n, n), dtype=torch_dtype(odt), device=A.device)
+        out = torch.empty((nb, n, n), dtype=tdt, device=A.device)
+    _expect(out, "out", dtype=tdt, shape=(n, n) if (squeeze and out.dim() == 2) else (nb, n, n), device=A.device)
     D3, _, _, _, ldd, sd = _mat3(out)
     if C is not None:
+        _expect(C, "C", dtype=tdt, shape=tuple(out.shape), device=A.device)
         C3, _, _, _, ldc, sc = _mat3(C)
         cptr = C3.data_ptr()
     else:
         cptr, ldc, sc = None, n, n * n
     check(lib.symm_gemm(nb, n, k, alpha, A3.data_ptr(), lda, sa, B3.data_ptr(), ldb, sb, beta, cptr, ldc, sc,
-                        gamma, D3.data_ptr(), ldd, sd, dtype_code(A3), dtype_code(D3), _stream(A.device)),
+                        gamma, D3.data_ptr(), ldd, sd, dtype_code(A3), odt, _stream(A.device)),
           "symm_gemm")
-    return out.squeeze(0) if A.dim() == 2 else out
+    return out.squeeze(0) if (squeeze and out.dim() == 3) else out
 
 
 def rect_gemm(A, Bm, C=None, alpha=1.0, beta=0.0, b_prescale=1.0, out=None, out_dtype=None):
-    """D = alpha A B + beta C for A [batch, n, k], B [batch, k, m]."""
+    """D = alpha A B + beta C for A [batch, n, k], B [batch, k, m]; C and the output are
+    [batch, n, m] in the output dtype."""
     torch = _torch()
     _dev(A)
+    squeeze = A.dim() == 2
     A3, nb, n, k, lda, sa = _mat3(A)
+    _expect(Bm, "B", device=A.device)
+    if Bm.dim() != A.dim():
+        raise ValueError("A and B must both be 2-D or both 3-D")
     B3, nb2, k2, m, ldb, sb = _mat3(Bm)
     if (nb2, k2) != (nb, k):
         raise ValueError("A and B shapes differ")
     odt = dtype_code(A3) if out_dtype is None else code_of(out_dtype)
+    tdt = torch_dtype(odt)
+    oshape = (n, m) if squeeze else (nb, n, m)
     if out is None:
-        out = torch.empty((nb, n, m), dtype=torch_dtype(odt), device=A.device)
+        out = torch.empty(oshape, dtype=tdt, device=A.device)
+    _expect(out, "out", dtype=tdt, shape=oshape, device=A.device)
     D3, _, _, _, ldd, sd = _mat3(out)
     if C is not None:
+        _expect(C, "C", dtype=tdt, shape=oshape, device=A.device)
         C3, _, _, _, ldc, sc = _mat3(C)
         cptr = C3.data_ptr()
     else:
         cptr, ldc, sc = None, m, n * m
     check(lib.rect_gemm(nb, n, k, m, alpha, A3.data_ptr(), lda, sa, dtype_code(A3), B3.data_ptr(), ldb, sb,
-                        dtype_code(B3), b_prescale, beta, cptr, ldc, sc, D3.data_ptr(), ldd, sd, dtype_code(D3),
+                        dtype_code(B3), b_prescale, beta, cptr, ldc, sc, D3.data_ptr(), ldd, sd, odt,
                         _stream(A.device)), "rect_gemm")
-    return out.squeeze(0) if A.dim() == 2 else out
+    return out
 
 
 # ---- Dion3 -------------------------------------------------------------------------
@@ -267,9 +298,24 @@ def _rows(x):
     return x.shape[0], x.shape[1], x.stride(0)
 
 
+def _bf16_rows(x, name):
+    torch = _torch()
+    _expect(x, name, dtype=torch.bfloat16)
+    return _rows(x)
+
+
+def _index_vector(S, k_max, device):
+    torch = _torch()
+    _expect(S, "S", dtype=torch.int32, device=device)
+    if S.dim() != 1 or not S.is_contiguous() or not (1 <= S.numel() <= k_max):
+        raise ValueError("S must be a contiguous 1-D int32 tensor of 1..N indices")
+    return S.numel()
+
+
 def dion3_accumulate_score(M, G, score_norm=1):
     torch = _torch()
-    N, m, ld = _rows(_dev(M))
+    N, m, ld = _bf16_rows(M, "M")
+    _expect(G, "G", dtype=torch.bfloat16, shape=M.shape, device=M.device)
     if _rows(G)[2] != ld:
         raise ValueError("M and G must share the row stride")
     score = torch.empty(N, dtype=torch.float64, device=M.device)
@@ -281,6 +327,9 @@ def dion3_accumulate_score(M, G, score_norm=1):
 
 def dion3_select_topk(score, k):
     torch = _torch()
+    _expect(score, "score", dtype=torch.float64)
+    if score.dim() != 1 or not score.is_contiguous():
+        raise ValueError("score must be a contiguous 1-D float64 tensor")
     S = torch.empty(k, dtype=torch.int32, device=score.device)
     check(lib.dion3_select_topk(_dev(score).data_ptr(), score.numel(), k, S.data_ptr(), _stream(score.device)),
           "dion3_select_topk")
@@ -289,8 +338,8 @@ def dion3_select_topk(score, k):
 
 def dion3_gather_feedback(M, S, mu):
     torch = _torch()
-    N, m, ld = _rows(_dev(M))
-    k = S.numel()
+    N, m, ld = _bf16_rows(M, "M")
+    k = _index_vector(S, N, M.device)
     X = torch.empty((k, m), dtype=M.dtype, device=M.device)
     check(lib.dion3_gather_feedback(M.data_ptr(), N, m, ld, S.data_ptr(), k, mu, X.data_ptr(), m,
                                     _stream(M.device)), "dion3_gather_feedback")
@@ -298,8 +347,13 @@ def dion3_gather_feedback(M, S, mu):
 
 
 def dion3_apply_update(W, S, O, lr, wd):
-    N, m, ld = _rows(_dev(W))
-    k = S.numel()
+    torch = _torch()
+    N, m, ld = _bf16_rows(W, "W")
+    k = _index_vector(S, N, W.device)
+    _expect(O, "O", device=W.device)
+    if O.dtype not in (torch.bfloat16, torch.float32) or O.dim() != 2 or O.shape[0] != k or O.shape[1] != m \
+            or O.stride(1) != 1:
+        raise ValueError("O must be a [k, m] bf16 or fp32 tensor with contiguous rows")
     check(lib.dion3_apply_update(W.data_ptr(), N, m, ld, S.data_ptr(), k, O.data_ptr(), dtype_code(O),
                                  O.stride(0), lr, wd, _stream(W.device)), "dion3_apply_update")
     return W
@@ -309,7 +363,9 @@ def dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute=
                return_O=False):
     """One Dion3 step in place on W and M; returns S (and O when return_O)."""
     torch = _torch()
-    N, m, ld = _rows(_dev(W))
+    N, m, ld = _bf16_rows(W, "W")
+    _expect(M, "M", dtype=torch.bfloat16, shape=W.shape, device=W.device)
+    _expect(G, "G", dtype=torch.bfloat16, shape=W.shape, device=W.device)
     if _rows(M)[2] != ld or _rows(G)[2] != ld:
         raise ValueError("W, M, G must share the row stride")
     cdt = code_of(compute)

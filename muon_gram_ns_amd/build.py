@@ -23,7 +23,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgns.so")
 
 SOURCES = {
-    "gemm.hip": [],
+    "gemm_symm.hip": [],
+    "gemm_rect.hip": [],
     "elementwise.hip": [],
     "dion3.hip": ["-ffp-contract=off"],
     "gns_abi.cpp": [],
@@ -71,7 +72,7 @@ def clangxx() -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
         objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], verbose), SOURCES.items()))
     tmp = LIB + ".tmp"
     # host link only (each object already embeds its gfx950 code object); plain

@@ -1,0 +1,753 @@
+// MFMA GEMM kernels for gfx950: the symmetric-output product (lower-triangle tiles,
+// mirrored epilogue) and the rectangular product Q X.
+//
+// Symmetric GEMM: only output tiles on or below the diagonal are scheduled, and each
+// computed tile is also written transposed above the diagonal, which halves the
+// multiply work for a symmetric result ("Dion3: Full-Stack Orthogonal Updates",
+// paper.rainbus.top, 前置知识 "symmetric GEMM kernel" and 方法步骤详情 (2)).  The
+// epilogue forms alpha*acc + beta*C + gamma*I in fp32 before a single rounding, and
+// can emit a second output shifted by delta*I (Q_1 = Z_1 + a_1 I in Gram NS).
+//
+// Both kernels read their operands as rows that are contiguous along K:
+//   NT  (symmetric): A is n x K, B is n x K; D = A B^T.  With B symmetric and K = n
+//       this is A B, with A == B the Gram product.
+//   NN  (rectangular): A is n x K, B is K x m (rows contiguous along m).  B's tile
+//       is transposed in registers on its way to LDS, so the MFMA loop is shared.
+// LDS holds two stages of [rows][128 bytes] tiles for A and B (K-contiguous,
+// 16-byte chunks XOR-swizzled, see swz()).  Each wave owns a WM x WN sub-tile made
+// of 16x16 MFMA fragments accumulated in fp32.
+#pragma once
+#include "common.h"
+#include "internal.h"
+
+namespace gns {
+
+__device__ __forceinline__ void tri_decode(int t, int& i, int& j) {
+  int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+  while ((r + 1) * (r + 2) / 2 <= t) ++r;
+  while (r * (r + 1) / 2 > t) --r;
+  i = r;
+  j = t - r * (r + 1) / 2;
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on XCD i % 8),
+// and each XCD has its own L2.  Give XCD x one contiguous range of logical ids so the
+// tiles it runs share operand panels (and, for batched problems, whole matrices).
+__device__ __forceinline__ int xcd_remap(int L, int total) {
+  constexpr int kXcds = 8;
+  const int xcd = L % kXcds, idx = L / kXcds;
+  const int per = total / kXcds, rem = total % kXcds;
+  return xcd * per + min(xcd, rem) + idx;
+}
+
+template <class TOut>
+__device__ __forceinline__ void store1(void* base, long long off, float v) {
+  if constexpr (TOut::kBytes == 4) {
+    reinterpret_cast<float*>(base)[off] = v;
+  } else {
+    reinterpret_cast<uint16_t*>(base)[off] = (uint16_t)TOut::from_f32(v);
+  }
+}
+
+template <class TOut>
+__device__ __forceinline__ void store4(void* base, long long off, const float v[4]) {
+  if constexpr (TOut::kBytes == 4) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint2 w;
+    w.x = TOut::from_f32(v[0]) | (TOut::from_f32(v[1]) << 16);
+    w.y = TOut::from_f32(v[2]) | (TOut::from_f32(v[3]) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + off) = w;
+  }
+}
+
+template <class TOut>
+__device__ __forceinline__ void load4(const void* base, long long off, float v[4]) {
+  if constexpr (TOut::kBytes == 4) {
+    float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+    uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
+    v[0] = TOut::to_f32(w.x & 0xffffu); v[1] = TOut::to_f32(w.x >> 16);
+    v[2] = TOut::to_f32(w.y & 0xffffu); v[3] = TOut::to_f32(w.y >> 16);
+  }
+}
+
+// Convert a 16-byte chunk of TB elements (times mul) to TIn elements.  Only 16-bit
+// to 16-bit conversions are used, so the chunk geometry is unchanged.
+template <class TIn, class TB>
+__device__ __forceinline__ uint4 convert_chunk(uint4 c, float mul) {
+  if constexpr (TIn::kId == TB::kId) {
+    return c;
+  } else {
+    static_assert(TIn::kBytes == 2 && TB::kBytes == 2, "only 16-bit conversions");
+    uint32_t* w = reinterpret_cast<uint32_t*>(&c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo = TIn::from_f32(TB::to_f32(w[i] & 0xffffu) * mul);
+      uint32_t hi = TIn::from_f32(TB::to_f32(w[i] >> 16) * mul);
+      w[i] = lo | (hi << 16);
+    }
+    return c;
+  }
+}
+
+// Epilogue element group: row gm, columns gn .. gn+3 of the output tile.
+// v = alpha' acc + beta C + gamma [diag] is written to D (and D2 = v + delta [diag]);
+// symmetric outputs write the lower-triangle elements and their mirror images, so D
+// is bitwise symmetric.  N % 4 == 0, so gn < N covers gn .. gn+3.
+template <class TOut, bool LOWER>
+__device__ __forceinline__ void emit_row4(const GemmParams& p, uint8_t* Db, uint8_t* D2b, const uint8_t* Cb,
+                                          float alpha, int gm, int gn, const float* a4) {
+  if (gm >= p.M || gn >= p.N) return;
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = alpha * a4[e];
+  if (Cb && p.beta != 0.0f) {
+    float c[4];
+    load4<TOut>(Cb, (long long)gm * p.ldc + gn, c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += p.beta * c[e];
+  }
+  if (p.gamma != 0.0f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (gn + e == gm) v[e] += p.gamma;
+  }
+  if constexpr (!LOWER) {
+    store4<TOut>(Db, (long long)gm * p.ldd + gn, v);
+  } else {
+    const bool all_lower = gn + 3 <= gm;
+    if (all_lower) {
+      store4<TOut>(Db, (long long)gm * p.ldd + gn, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (gn + e <= gm) store1<TOut>(Db, (long long)gm * p.ldd + gn + e, v[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (gn + e < gm) store1<TOut>(Db, (long long)(gn + e) * p.ldd + gm, v[e]);
+    if (D2b) {
+      float w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = v[e] + ((gn + e == gm) ? p.delta : 0.0f);
+      if (all_lower) {
+        store4<TOut>(D2b, (long long)gm * p.ldd2 + gn, w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (gn + e <= gm) store1<TOut>(D2b, (long long)gm * p.ldd2 + gn + e, w[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (gn + e < gm) store1<TOut>(D2b, (long long)(gn + e) * p.ldd2 + gm, w[e]);
+    }
+  }
+}
+
+struct EpiPtrs {
+  uint8_t* D;
+  uint8_t* D2;
+  const uint8_t* C;
+  float alpha;
+};
+
+template <class TOut>
+__device__ __forceinline__ EpiPtrs epi_ptrs(const GemmParams& p, int bz) {
+  EpiPtrs e;
+  e.alpha = p.alpha;
+  if (p.scale) for (int i = 0; i < p.alpha_pow; ++i) e.alpha *= p.scale[bz];
+  e.D = reinterpret_cast<uint8_t*>(p.D) + (size_t)bz * p.sD * TOut::kBytes;
+  e.D2 = p.D2 ? reinterpret_cast<uint8_t*>(p.D2) + (size_t)bz * p.sD2 * TOut::kBytes : nullptr;
+  e.C = p.C ? reinterpret_cast<const uint8_t*>(p.C) + (size_t)bz * p.sC * TOut::kBytes : nullptr;
+  return e;
+}
+
+// 16x16 fragments (v_mfma_f32_16x16x*, operands passed swapped): lane l owns row
+// (l % 16) and columns 4 (l / 16) + e of each fragment.
+template <class TOut, bool LOWER, int FM, int FN>
+__device__ __forceinline__ void epilogue(const GemmParams& p, f32x4_t (&acc)[FM][FN], int bz, int mw, int nw,
+                                         int lane) {
+  const EpiPtrs e = epi_ptrs<TOut>(p, bz);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      float a4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      emit_row4<TOut, LOWER>(p, e.D, e.D2, e.C, e.alpha, mw + i * 16 + (lane & 15), nw + j * 16 + 4 * (lane >> 4), a4);
+    }
+}
+
+// 32x32 fragments (v_mfma_f32_32x32x16, operands passed swapped): lane l owns row
+// (l % 32) and, for q = 0..3, columns 8 q + 4 (l / 32) + e of each fragment.
+template <class TOut, bool LOWER, int FM, int FN>
+__device__ __forceinline__ void epilogue32(const GemmParams& p, f32x16_t (&acc)[FM][FN], int bz, int mw, int nw,
+                                           int lane) {
+  const EpiPtrs e = epi_ptrs<TOut>(p, bz);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float a4[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        emit_row4<TOut, LOWER>(p, e.D, e.D2, e.C, e.alpha, mw + i * 32 + (lane & 31),
+                               nw + j * 32 + 8 * q + 4 * (lane >> 5), a4);
+      }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+struct Tile {
+  static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+  static constexpr int kWM = BM / WAVES_M;
+  static constexpr int kWN = BN / WAVES_N;
+  static constexpr int kFM = kWM / 16;
+  static constexpr int kFN = kWN / 16;
+  static constexpr int kLdsBytes = 2 * (BM + BN) * 128;
+};
+
+// One kernel for both products.  LOWER: symmetric output (triangle schedule +
+// mirror); otherwise a plain tile grid.  NN: B is K x N (transposed on load).
+template <class TIn, class TB, class TOut, int BM, int BN, int WAVES_M, int WAVES_N, bool LOWER, bool NN>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+gemm_kernel(GemmParams p) {
+  using Cfg = Tile<BM, BN, WAVES_M, WAVES_N>;
+  constexpr int NT = Cfg::kThreads;
+  constexpr int FM = Cfg::kFM, FN = Cfg::kFN;
+  constexpr int EPC = TIn::kPerChunk;          // elements per 16-byte chunk
+  constexpr int BK = 8 * EPC;                  // K elements per LDS tile row
+  constexpr int A_LOADS = BM * 8 / NT;         // 16-byte chunks per thread per stage
+  constexpr int B_LOADS_NT = BN * 8 / NT;
+  constexpr int NN_COLS = BN / EPC;            // NN: column groups of one k-row
+  constexpr int NN_TOTAL = (BK / 4) * NN_COLS;         // NN: 4(k) x EPC(n) blocks per tile
+  constexpr int NN_BLOCKS = (NN_TOTAL + NT - 1) / NT;  // ... per thread
+  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/thread mismatch");
+  static_assert(!LOWER || BM == BN, "symmetric tiles must be square");
+
+  extern __shared__ __align__(16) uint4 smem[];
+  uint4* As = smem;                      // [2][BM][8]
+  uint4* Bs = smem + 2 * BM * 8;         // [2][BN][8]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  // one flat grid over (batch, tile), remapped so each XCD gets a contiguous range
+  const int rid = xcd_remap((int)blockIdx.x, p.batch * p.tiles);
+  const int bz = rid / p.tiles;
+  const int tile = rid - bz * p.tiles;
+  int tm, tn;
+  if constexpr (LOWER) {
+    tri_decode(tile, tm, tn);
+  } else {
+    tm = tile / p.tiles_n;
+    tn = tile % p.tiles_n;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int M = p.M, N = p.N, K = p.K;
+
+  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A) + (size_t)bz * p.sA * TIn::kBytes;
+  const uint8_t* Bb = reinterpret_cast<const uint8_t*>(p.B) + (size_t)bz * p.sB * TB::kBytes;
+
+  float bmul = 1.0f;
+  if constexpr (NN && TIn::kId != TB::kId) {
+    bmul = p.b_mul;
+    if (p.scale) for (int i = 0; i < p.b_pow; ++i) bmul *= p.scale[bz];
+  }
+
+  uint4 ra[A_LOADS];
+  uint4 rb[NN ? 4 * NN_BLOCKS : B_LOADS_NT];
+
+  // Buffer resources over this matrix's operands: out-of-range rows/columns load as
+  // zero without branches (the extents are checked to be < 2 GiB on the host).
+  const auto rsA = make_rsrc(Ab, (uint32_t)(((size_t)(M - 1) * p.lda + K) * TIn::kBytes));
+  const auto rsB = NN ? make_rsrc(Bb, (uint32_t)(((size_t)(K - 1) * p.ldb + N) * TB::kBytes))
+                      : make_rsrc(Bb, (uint32_t)(((size_t)(N - 1) * p.ldb + K) * TB::kBytes));
+
+  auto load_a = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int c = tid + i * NT, row = c >> 3, ch = c & 7;
+      const int gr = m0 + row, gk = k0 + ch * EPC;
+      const uint32_t off = (gr < M && gk < K) ? (uint32_t)(((size_t)gr * p.lda + gk) * TIn::kBytes) : kOutOfRange;
+      ra[i] = buffer_load16(rsA, off);
+    }
+  };
+  auto load_b = [&](int k0) {
+    if constexpr (!NN) {
+#pragma unroll
+      for (int i = 0; i < B_LOADS_NT; ++i) {
+        const int c = tid + i * NT, row = c >> 3, ch = c & 7;
+        const int gr = n0 + row, gk = k0 + ch * EPC;
+        const uint32_t off = (gr < N && gk < K) ? (uint32_t)(((size_t)gr * p.ldb + gk) * TB::kBytes) : kOutOfRange;
+        rb[i] = buffer_load16(rsB, off);
+      }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < NN_BLOCKS; ++blk) {
+        const int t = tid + blk * NT;
+        const int kb = t % (BK / 4), nb = t / (BK / 4);
+        const int gn = n0 + nb * EPC;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int gk = k0 + kb * 4 + r;
+          const uint32_t off = (t < NN_TOTAL && gk < K && gn < N)
+                                   ? (uint32_t)(((size_t)gk * p.ldb + gn) * TB::kBytes) : kOutOfRange;
+          rb[blk * 4 + r] = buffer_load16(rsB, off);
+        }
+      }
+    }
+  };
+  auto store_a = [&](int stage) {
+    uint4* dst = As + stage * BM * 8;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int c = tid + i * NT, row = c >> 3, ch = c & 7;
+      dst[row * 8 + swz(row, ch)] = ra[i];
+    }
+  };
+  auto store_b = [&](int stage) {
+    uint4* dst = Bs + stage * BN * 8;
+    if constexpr (!NN) {
+#pragma unroll
+      for (int i = 0; i < B_LOADS_NT; ++i) {
+        const int c = tid + i * NT, row = c >> 3, ch = c & 7;
+        dst[row * 8 + swz(row, ch)] = rb[i];
+      }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < NN_BLOCKS; ++blk) {
+        const int t = tid + blk * NT;
+        if (NN_TOTAL % NT != 0 && t >= NN_TOTAL) break;
+        const int kb = t % (BK / 4), nb = t / (BK / 4);
+        uint4 rows[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rows[r] = convert_chunk<TIn, TB>(rb[blk * 4 + r], bmul);
+        if constexpr (TIn::kBytes == 2) {
+          // 4 k-rows x 8 n-columns of 16-bit values -> for each column, 4 k-values
+          // (8 bytes) at k offset 4*kb of row n: chunk kb/2, half kb&1.
+          const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&rows[0]);
+          const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&rows[1]);
+          const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&rows[2]);
+          const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&rows[3]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int sh = (j & 1) * 16;
+            const uint32_t e0 = (w0[j >> 1] >> sh) & 0xffffu, e1 = (w1[j >> 1] >> sh) & 0xffffu;
+            const uint32_t e2 = (w2[j >> 1] >> sh) & 0xffffu, e3 = (w3[j >> 1] >> sh) & 0xffffu;
+            const int n = nb * 8 + j;
+            uint8_t* rowp = reinterpret_cast<uint8_t*>(dst + n * 8 + swz(n, kb >> 1)) + (kb & 1) * 8;
+            *reinterpret_cast<uint2*>(rowp) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+          }
+        } else {
+          // fp32: 4 k-rows x 4 n-columns -> each column's 4 k-values fill chunk kb.
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = nb * 4 + j;
+            const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&rows[0]);
+            const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&rows[1]);
+            const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&rows[2]);
+            const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&rows[3]);
+            dst[n * 8 + swz(n, kb)] = make_uint4(r0[j], r1[j], r2[j], r3[j]);
+          }
+        }
+      }
+    }
+  };
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int KT = (K + BK - 1) / BK;
+  load_a(0);
+  load_b(0);
+  store_a(0);
+  store_b(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int stage = kt & 1;
+    if (kt + 1 < KT) {
+      load_a((kt + 1) * BK);
+      load_b((kt + 1) * BK);
+    }
+    const uint4* as = As + stage * BM * 8;
+    const uint4* bs = Bs + stage * BN * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = ks * 4 + (lane >> 4);
+      uint4 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * Cfg::kWM + i * 16 + (lane & 15);
+        af[i] = as[row * 8 + swz(row, ch)];
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wn * Cfg::kWN + j * 16 + (lane & 15);
+        bfr[j] = bs[row * 8 + swz(row, ch)];
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma_step<TIn>(acc[i][j], af[i], bfr[j]);
+    }
+    if (kt + 1 < KT) {
+      store_a(stage ^ 1);
+      store_b(stage ^ 1);
+    }
+    __syncthreads();
+  }
+
+  epilogue<TOut, LOWER, FM, FN>(p, acc, bz, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane);
+}
+
+
+// ---------------------------------------------------------------------------------
+// 16-bit kernel (fp16 / bf16 operands) on v_mfma_f32_32x32x16.  On gfx950 this MFMA
+// shape runs at the full dense rate (measured 2405 TFLOP/s chip-wide), while
+// v_mfma_f32_16x16x32 issues at half rate (1266 TFLOP/s), so all 16-bit products use
+// 32x32 fragments.
+//
+// Operands go from HBM straight into LDS with buffer loads carrying the LDS flag (no
+// staging registers).  They are issued through inline assembly, so the compiler does
+// not track them and does not make every later LDS read wait for them; the kernel
+// waits explicitly (s_waitcnt vmcnt(0)) before the barrier that publishes a stage.
+//
+// LDS per stage: A tile [BM rows][128 B] (64 k values, K-contiguous, 16-byte chunks
+// swizzled by swz()); B tile the same (NT) or, for the rectangular product, X's
+// natural layout [64 rows (k)][BN * 2 B] with 16-byte chunks XOR-ed by 2 (k & 3).
+// NN fragments are read with ds_read_b64_tr_b16: lane i of a 16-lane group passes
+// the address of row k0 + i/4, columns n0 + 4 (i % 4) .. +3 and receives column
+// n0 + i at rows k0 .. k0+3 -- an MFMA operand column (verified on gfx950).
+//
+// Per 64-k stage each wave runs 4 k-steps of 16; fragments alternate between two
+// register sets so the LDS reads of k-step s+1 overlap the MFMAs of k-step s, and the
+// barrier sits inside the last k-step: the MFMAs after it cover the first LDS reads
+// of the next stage.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef int int4v_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+__device__ __forceinline__ uint2 lds_read_tr16(const void* lds) {
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)lds);
+  return __builtin_bit_cast(uint2, v);
+}
+
+// raw buffer descriptor of [base, base + bytes) in scalar registers
+__device__ __forceinline__ int4v_t sgpr_rsrc(const void* base, uint32_t bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  int4v_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from the buffer at voffset into LDS at lds_addr + 16 * lane;
+// offsets past the end of the buffer write zeros.
+__device__ __forceinline__ void dma16(int4v_t rsrc, uint32_t lds_addr, uint32_t voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory", "m0");
+}
+
+template <class T>
+__device__ __forceinline__ void mfma32_step(f32x16_t& acc, const uint4& a, const uint4& b) {
+  if constexpr (T::kId == GNS_BF16) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b),
+                                                 __builtin_bit_cast(bf16x8_t, a), acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, b),
+                                                __builtin_bit_cast(f16x8_t, a), acc, 0, 0, 0);
+  }
+}
+
+// s_waitcnt immediate (gfx9 family) that waits until at most `vm` vector-memory
+// instructions of this wave are outstanding, leaving the other counters alone.
+constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | (0x7 << 4) | (0xF << 8) | (((vm >> 4) & 0x3) << 14); }
+
+// Workgroup barrier that is also a compiler memory barrier (no LDS access moves
+// across it) but, unlike __syncthreads(), adds no waits on outstanding loads: the
+// kernel waits for exactly the stage it needs before calling it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+struct Tile32 {
+  static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+  static constexpr int kWM = BM / WAVES_M;
+  static constexpr int kWN = BN / WAVES_N;
+  static constexpr int kFM = kWM / 32;
+  static constexpr int kFN = kWN / 32;
+  static constexpr int kStages = 4;           // LDS ring depth
+  static constexpr int kBK = 32;              // k values per stage (64-byte rows)
+  static constexpr int kLdsBytes = kStages * (BM + BN) * kBK * 2;
+};
+
+// 64-byte LDS rows (4 chunks): 16 rows read at the same logical chunk land in 16
+// distinct 16-byte slots of the 256-byte bank window (rows 4j .. 4j+3 share a window
+// and sit in different quarters; j selects the chunk within the quarter).
+__device__ __forceinline__ int swz64(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+template <class TIn, class TB, class TOut, int BM, int BN, int WAVES_M, int WAVES_N, bool LOWER, bool NN>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+gemm16_kernel(GemmParams p) {
+  static_assert(TIn::kBytes == 2 && TB::kBytes == 2, "16-bit operands only");
+  static_assert(!LOWER || (BM == BN && !NN), "symmetric tiles are square NT tiles");
+  using Cfg = Tile32<BM, BN, WAVES_M, WAVES_N>;
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int FM = Cfg::kFM, FN = Cfg::kFN;
+  static_assert(FM >= 1 && FN >= 1, "wave tile must be a multiple of 32");
+  constexpr int NS = Cfg::kStages, BK = Cfg::kBK;
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_INSTR = A_BYTES / (1024 * NW), B_INSTR = B_BYTES / (1024 * NW);   // 1 KB per wave instruction
+  constexpr int LOADS = A_INSTR + B_INSTR;                                           // per wave per stage
+  constexpr int NCH = BN / 8;                                                        // NN: chunks per k row
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "tile/wave mismatch");
+  static_assert(!NN || NCH >= 8, "NN tiles need >= 64 columns");
+  static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
+
+  extern __shared__ __align__(16) uint8_t smem16[];
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)smem16);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  // block-level indices are uniform; readfirstlane keeps them in scalar registers
+  const int rid = xcd_remap((int)blockIdx.x, p.batch * p.tiles);
+  const int bz = __builtin_amdgcn_readfirstlane(rid / p.tiles);
+  const int tile = __builtin_amdgcn_readfirstlane(rid - bz * p.tiles);
+  int tm, tn;
+  if constexpr (LOWER) {
+    tri_decode(tile, tm, tn);
+  } else {
+    tm = tile / p.tiles_n;
+    tn = tile % p.tiles_n;
+  }
+  const int m0 = __builtin_amdgcn_readfirstlane(tm * BM), n0 = __builtin_amdgcn_readfirstlane(tn * BN);
+  const int M = p.M, N = p.N, K = p.K;
+  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A) + (size_t)bz * p.sA * 2;
+  const uint8_t* Bb = reinterpret_cast<const uint8_t*>(p.B) + (size_t)bz * p.sB * 2;
+  const int4v_t rsA = sgpr_rsrc(Ab, (uint32_t)(((size_t)(M - 1) * p.lda + K) * 2));
+  const int4v_t rsB = NN ? sgpr_rsrc(Bb, (uint32_t)(((size_t)(K - 1) * p.ldb + N) * 2))
+                         : sgpr_rsrc(Bb, (uint32_t)(((size_t)(N - 1) * p.ldb + K) * 2));
+  float bmul = 1.0f;
+  if constexpr (NN && TIn::kId != TB::kId) {
+    bmul = p.b_mul;
+    if (p.scale) for (int i = 0; i < p.b_pow; ++i) bmul *= p.scale[bz];
+  }
+
+  // issue the direct HBM -> LDS loads of k-stage kt into LDS ring slot kt % NS
+  auto issue_stage = [&](int kt) {
+    const int k0 = kt * BK;
+    const uint32_t sb = lds0 + (kt % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_INSTR; ++i) {
+      const int blk = i * NW + wave;
+      const int q = blk * 64 + lane;                      // LDS chunk this lane fills
+      const int row = q >> 2, lc = swz64(row, q & 3);
+      const int gr = m0 + row, gk = k0 + lc * 8;
+      const uint32_t off = (gr < M && gk < K) ? (uint32_t)(((size_t)gr * p.lda + gk) * 2) : kOutOfRange;
+      dma16(rsA, __builtin_amdgcn_readfirstlane(sb + blk * 1024), off);
+    }
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i) {
+      const int blk = i * NW + wave;
+      const int q = blk * 64 + lane;
+      uint32_t off;
+      if constexpr (!NN) {
+        const int row = q >> 2, lc = swz64(row, q & 3);
+        const int gr = n0 + row, gk = k0 + lc * 8;
+        off = (gr < N && gk < K) ? (uint32_t)(((size_t)gr * p.ldb + gk) * 2) : kOutOfRange;
+      } else {
+        const int kr = q / NCH, lc = (q % NCH) ^ (2 * (kr & 3));
+        const int gk = k0 + kr, gn = n0 + lc * 8;
+        off = (gk < K && gn < N) ? (uint32_t)(((size_t)gk * p.ldb + gn) * 2) : kOutOfRange;
+      }
+      dma16(rsB, __builtin_amdgcn_readfirstlane(sb + A_BYTES + blk * 1024), off);
+    }
+  };
+
+  // fragments of k-step ks (16 k values) of the stage in ring slot `slot`
+  auto read_frags = [&](int slot, int ks, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
+    const uint8_t* sb = smem16 + slot * STAGE;
+    const uint4* as = reinterpret_cast<const uint4*>(sb);
+    const int ch = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * Cfg::kWM + i * 32 + (lane & 31);
+      fa[i] = as[row * 4 + swz64(row, ch)];
+    }
+    if constexpr (!NN) {
+      const uint4* bs = reinterpret_cast<const uint4*>(sb + A_BYTES);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wn * Cfg::kWN + j * 32 + (lane & 31);
+        fb[j] = bs[row * 4 + swz64(row, ch)];
+      }
+    } else {
+      const uint16_t* bh = reinterpret_cast<const uint16_t*>(sb + A_BYTES);
+      const int g = lane >> 4, i16 = lane & 15;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int nb = wn * Cfg::kWN + j * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+        uint2 h[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int kr = ks * 16 + 8 * (g >> 1) + 4 * hh + (i16 >> 2);
+          const int pc = (nb >> 3) ^ (2 * (kr & 3));
+          h[hh] = lds_read_tr16(bh + kr * BN + pc * 8 + (nb & 7));
+        }
+        fb[j] = convert_chunk<TIn, TB>(make_uint4(h[0].x, h[0].y, h[1].x, h[1].y), bmul);
+      }
+    }
+  };
+
+  auto mma = [&](f32x16_t (&acc)[FM][FN], const uint4 (&fa)[FM], const uint4 (&fb)[FN], int i0, int i1) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i < i0 || i >= i1) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma32_step<TIn>(acc[i][j], fa[i], fb[j]);
+    }
+  };
+
+  // wait until k-stage `next` has landed; `last` is the last stage issued so far, and
+  // the (last - next) stages issued after `next` may stay in flight (vmcnt counts
+  // this wave's loads, which complete in issue order)
+  auto wait_for_stage = [&](int next, int last) {
+    const int later = last - next;
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int KT = (K + BK - 1) / BK;
+  constexpr int H = (FM + 1) / 2;     // fragment rows before / after the barrier
+  uint4 a0[FM], b0[FN], a1[FM], b1[FN];
+  for (int t = 0; t < NS - 1 && t < KT; ++t) issue_stage(t);
+  wait_for_stage(0, min(NS - 2, KT - 1));
+  lds_barrier();
+  read_frags(0, 0, a0, b0);
+
+  // Stage kt (ring slot kt % NS) holds its k-step 0 fragments in a0/b0 on entry:
+  //   read k-step 1 | MFMAs of k-step 0 | first rows of k-step 1
+  //   wait for stage kt+1, barrier (stage kt-1's slot is then free everywhere)
+  //   issue stage kt+NS-1 into that slot | read k-step 0 of stage kt+1
+  //   remaining rows of k-step 1
+  for (int kt = 0; kt < KT; ++kt) {
+    const int slot = kt % NS;
+    read_frags(slot, 1, a1, b1);
+    mma(acc, a0, b0, 0, FM);
+    mma(acc, a1, b1, 0, H);
+    if (kt + 1 < KT) {
+      wait_for_stage(kt + 1, min(kt + NS - 2, KT - 1));   // stage kt+NS-1 is issued below
+      lds_barrier();
+      if (kt + NS - 1 < KT) issue_stage(kt + NS - 1);
+      read_frags((kt + 1) % NS, 0, a0, b0);
+    }
+    mma(acc, a1, b1, H, FM);
+  }
+
+  epilogue32<TOut, LOWER, FM, FN>(p, acc, bz, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane);
+}
+
+// ---------------------------------------------------------------------------------
+// Host side: tile configurations and the launch of one configuration.
+
+// Output-tile configurations: (BM, BN, waves along M, waves along N).
+//   big:   256 x 256, 4 waves of 128 x 128 (128 KB of LDS, one workgroup per CU,
+//          one wave per SIMD with up to 512 registers: accumulators in AGPRs)
+//   mid:   128 x 128, 4 waves of 64 x 64   (64 KB)
+//   small:  64 x 64,  4 waves of 32 x 32   (32 KB) for problems with few tiles
+enum class TileCfg { kBig = 0, kMid = 1, kSmall = 2 };
+
+inline long long gemm_tiles(int M, int N, int bm, int bn, bool lower) {
+  const long long tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
+  return lower ? tm * (tm + 1) / 2 : tm * tn;
+}
+
+// The kernels address each operand matrix through a 32-bit buffer offset.
+inline bool operand_extents_ok(const GemmParams& p, int a_bytes, int b_bytes, bool nn) {
+  if (p.M <= 0 || p.N <= 0 || p.K <= 0) return true;
+  const size_t lim = size_t(1) << 31;
+  const size_t a = ((size_t)(p.M - 1) * p.lda + p.K) * a_bytes;
+  const size_t b = nn ? ((size_t)(p.K - 1) * p.ldb + p.N) * b_bytes : ((size_t)(p.N - 1) * p.ldb + p.K) * b_bytes;
+  return a < lim && b < lim;
+}
+
+// Pick the largest tile that still gives every CU at least one workgroup.
+inline TileCfg pick_tile(int M, int N, int batch, bool lower) {
+  constexpr long long kCUs = 256;
+  if ((long long)batch * gemm_tiles(M, N, 256, 256, lower) >= kCUs) return TileCfg::kBig;
+  if ((long long)batch * gemm_tiles(M, N, 128, 128, lower) >= kCUs) return TileCfg::kMid;
+  return TileCfg::kSmall;
+}
+
+template <class TIn, class TB, class TOut, int BM, int BN, int WM_, int WN_, bool LOWER, bool NN>
+hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops) {
+  using Cfg = Tile<BM, BN, WM_, WN_>;
+  static_assert(Cfg::kLdsBytes == Tile32<BM, BN, WM_, WN_>::kLdsBytes, "same LDS footprint");
+  // 16-bit operands: direct-to-LDS kernel; fp32 operands: register-staged kernel
+  void (*kern)(GemmParams);
+  if constexpr (TIn::kBytes == 2 && TB::kBytes == 2)
+    kern = gemm16_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, LOWER, NN>;
+  else
+    kern = gemm_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, LOWER, NN>;
+  static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  p.tiles_m = (p.M + BM - 1) / BM;
+  p.tiles_n = (p.N + BN - 1) / BN;
+  const long long tiles = gemm_tiles(p.M, p.N, BM, BN, LOWER);
+  if (!operand_extents_ok(p, TIn::kBytes, TB::kBytes, NN)) return hipErrorInvalidValue;
+  constexpr int BK = 8 * TIn::kPerChunk;
+  const long long kpad = ((long long)(p.K + BK - 1) / BK) * BK;
+  if (flops) *flops += 2.0 * (double)tiles * BM * BN * (double)kpad * batch;
+  if (tiles == 0 || batch == 0) return hipSuccess;
+  p.batch = batch;
+  p.tiles = (int)tiles;
+  clear_stale_error();
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * batch)), dim3(Cfg::kThreads), Cfg::kLdsBytes, stream, p);
+  return hipGetLastError();
+}
+
+template <class TIn, class TB, class TOut, bool LOWER, bool NN>
+hipError_t launch_cfg(GemmParams p, int batch, hipStream_t stream, double* flops) {
+#ifdef GNS_FORCE_TILE
+  const TileCfg cfg = static_cast<TileCfg>(GNS_FORCE_TILE);
+#else
+  const TileCfg cfg = pick_tile(p.M, p.N, batch, LOWER);
+#endif
+  switch (cfg) {
+    case TileCfg::kBig: return launch_one<TIn, TB, TOut, 256, 256, 2, 4, LOWER, NN>(p, batch, stream, flops);
+    case TileCfg::kMid: return launch_one<TIn, TB, TOut, 128, 128, 2, 2, LOWER, NN>(p, batch, stream, flops);
+    case TileCfg::kSmall: return launch_one<TIn, TB, TOut, 64, 64, 2, 2, LOWER, NN>(p, batch, stream, flops);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class TIn, class TB, bool LOWER, bool NN>
+hipError_t dispatch_out(gns_dtype out, const GemmParams& p, int batch, hipStream_t s, double* f) {
+  switch (out) {
+    case GNS_BF16: return launch_cfg<TIn, TB, TBF16, LOWER, NN>(p, batch, s, f);
+    case GNS_F16: return launch_cfg<TIn, TB, TF16, LOWER, NN>(p, batch, s, f);
+    case GNS_F32: return launch_cfg<TIn, TB, TF32, LOWER, NN>(p, batch, s, f);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gns

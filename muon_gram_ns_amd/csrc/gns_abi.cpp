@@ -114,6 +114,10 @@ int check_ns(const NsCall& c) {
   const size_t xb = ((size_t)(c.batch > 0 ? c.batch - 1 : 0) * c.sx + (size_t)(c.n - 1) * c.ldx + c.m) * esize(c.xdt);
   const size_t ob = ((size_t)(c.batch > 0 ? c.batch - 1 : 0) * c.so + (size_t)(c.n - 1) * c.ldo + c.m) * esize(c.odt);
   if (overlaps(c.X, xb, c.O, ob)) return GNS_ERR_INVALID_ARG;
+  // every operand matrix is addressed with 32-bit offsets inside the kernels
+  if (((size_t)(c.n - 1) * c.ldx + c.m) * esize(c.xdt) >= (size_t(1) << 31) ||
+      (size_t)c.n * c.m * 4 >= (size_t(1) << 31))
+    return GNS_ERR_UNSUPPORTED;
   const size_t need = ns_layout(nullptr, c.batch, c.n, c.m, c.cdt).bytes;
   if (c.batch > 0 && (!c.ws || c.ws_bytes < need)) return GNS_ERR_WORKSPACE;
   if (c.ws && c.batch > 0 && (overlaps(c.ws, need, c.O, ob) || overlaps(c.ws, need, c.X, xb))) return GNS_ERR_INVALID_ARG;

@@ -23,7 +23,8 @@ struct GemmParams {
   float alpha = 1.f, beta = 0.f, gamma = 0.f, delta = 0.f;
   const float* scale = nullptr; int alpha_pow = 0;
   float b_mul = 1.f; int b_pow = 0;
-  int tiles_m = 0, tiles_n = 0;
+  int tiles_m = 0, tiles_n = 0;   // set by the launcher
+  int batch = 0, tiles = 0;       // set by the launcher: grid = batch * tiles workgroups
 };
 
 // flops (nullable): incremented by the MFMA flops the launch issues.

@@ -81,11 +81,8 @@ def test_rect_gemm_parity(gns_mod, a_dt, b_dt, out_dt, n, k, m):
     if a_dt != b_dt:
         b = synth.to_storage(pre * b, a_dt)
         b = (synth.bf16_bits_to_f32(b) if a_dt == "bf16" else b).astype(np.float64)
-        pre_ref = 1.0
-    else:
-        pre_ref = 1.0
-    ref = rect_gemm_ref(a, pre_ref * b, c, alpha=1.5, beta=0.25)
-    check(to_f64(D), ref, TOL[out_dt] if out_dt != "f32" else (2e-5 if a_dt == b_dt else 2e-5))
+    ref = rect_gemm_ref(a, b, c, alpha=1.5, beta=0.25)
+    check(to_f64(D), ref, TOL[out_dt])
 
 
 def test_frobenius_scale(gns_mod):
@@ -96,3 +93,45 @@ def test_frobenius_scale(gns_mod):
         s = gns_mod.frobenius_scale(to_dev(x_st, dt), eps=1e-7).cpu().numpy()
         ref = 1.0 / (np.sqrt((x * x).sum(axis=(1, 2))) + 1e-7)
         assert np.allclose(s, ref, rtol=2e-6, atol=0)
+
+
+# Large batches select the 256 x 256 and 128 x 128 tile configurations (the small
+# shapes above run on 64 x 64 tiles); ragged sizes keep partial tiles in play.
+@pytest.mark.parametrize("batch,n,k,expect", [(48, 776, 264, "256x256"), (12, 520, 136, "128x128")])
+def test_symm_gemm_tile_configs(gns_mod, batch, n, k, expect):
+    announce(f"symm_gemm batch={batch} n={n} k={k} ({expect})")
+    rng = np.random.default_rng(batch + n)
+    a_st, a = stored(rng, (batch, n, k), "f16")
+    c_st, c = stored(rng, (batch, n, n), "f32")          # C is in the output dtype
+    D = gns_mod.symm_gemm(to_dev(a_st, "f16"), to_dev(a_st, "f16"), to_dev(c_st, "f32"), alpha=0.5, beta=1.0,
+                          gamma=-2.0, out_dtype="f32")
+    for i in (0, batch // 2, batch - 1):
+        check(to_f64(D[i]), symm_gemm_ref(a[i], a[i], c[i], alpha=0.5, beta=1.0, gamma=-2.0), TOL["f32"])
+    Dh = D.cpu()
+    assert bool((Dh == Dh.transpose(1, 2)).all())
+
+
+@pytest.mark.parametrize("batch,n,k,m,expect", [(24, 776, 264, 1032, "256x256"), (8, 520, 136, 1032, "128x128")])
+def test_rect_gemm_tile_configs(gns_mod, batch, n, k, m, expect):
+    announce(f"rect_gemm batch={batch} n={n} k={k} m={m} ({expect})")
+    rng = np.random.default_rng(batch + n + m)
+    a_st, a = stored(rng, (batch, n, k), "f16")
+    b_st, b = stored(rng, (batch, k, m), "bf16")
+    D = gns_mod.rect_gemm(to_dev(a_st, "f16"), to_dev(b_st, "bf16"), alpha=2.0, b_prescale=0.25, out_dtype="f32")
+    for i in (0, batch - 1):
+        bc = synth.to_storage(0.25 * b[i], "f16").astype(np.float64)
+        check(to_f64(D[i]), rect_gemm_ref(a[i], bc, alpha=2.0), TOL["f32"])
+
+
+def test_binding_rejects_operands_the_abi_cannot_check(gns_mod):
+    """C in a dtype other than the output's (or a wrongly shaped output) is refused
+    by the binding before any launch: the ABI only receives raw pointers."""
+    import torch
+    a = torch.zeros(2, 64, 64, dtype=torch.float16, device="cuda")
+    c16 = torch.zeros(2, 64, 64, dtype=torch.float16, device="cuda")
+    with pytest.raises(TypeError):
+        gns_mod.symm_gemm(a, a, C=c16, beta=1.0, out_dtype="f32")
+    with pytest.raises(ValueError):
+        gns_mod.symm_gemm(a, a, out=torch.empty(2, 64, 32, dtype=torch.float16, device="cuda"))
+    with pytest.raises(TypeError):
+        gns_mod.rect_gemm(a, a, C=c16, beta=1.0, out_dtype="f32")

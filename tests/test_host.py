@@ -132,3 +132,17 @@ def test_gram_cheaper_than_standard_for_alpha_above_one(alpha):
         assert g >= s * 0.99     # no saving (and the restart is not free) at alpha = 1
     else:
         assert g < s
+
+
+def test_binding_rejects_mismatched_tensors_before_any_call():
+    """The binding checks dtype/shape/device of every tensor it turns into a raw
+    pointer (a C operand in the wrong dtype would make the kernel read past the
+    allocation).  CPU tensors are rejected first, so this runs without a GPU."""
+    import torch
+    a = torch.zeros(2, 64, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        gns.symm_gemm(a, a)                       # not on the GPU
+    with pytest.raises(ValueError):
+        gns.rect_gemm(a, a)
+    with pytest.raises(ValueError):
+        gns.orthogonalize(a)
