@@ -11,11 +11,11 @@
 // Both kernels read their operands as rows that are contiguous along K:
 //   NT  (symmetric): A is n x K, B is n x K; D = A B^T.  With B symmetric and K = n
 //       this is A B, with A == B the Gram product.
-//   NN  (rectangular): A is n x K, B is K x m (rows contiguous along m).  B's tile
-//       is transposed in registers on its way to LDS, so the MFMA loop is shared.
-// LDS holds two stages of [rows][128 bytes] tiles for A and B (K-contiguous,
-// 16-byte chunks XOR-swizzled, see swz()).  Each wave owns a WM x WN sub-tile made
-// of 16x16 MFMA fragments accumulated in fp32.
+//   NN  (rectangular): A is n x K, B is K x m (rows contiguous along m).
+// Two kernels share the epilogues: gemm16_kernel for fp16/bf16 operands (32x32x16
+// MFMA, direct HBM -> LDS loads into a ring of k-stages) and gemm_kernel for fp32
+// operands (16x16x4 MFMA, register-staged double buffer).  Each wave owns a WM x WN
+// sub-tile of MFMA fragments accumulated in fp32.
 #pragma once
 #include "common.h"
 #include "internal.h"
@@ -177,24 +177,6 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4_t (&acc)[FM]
       float a4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
       emit_row4<TOut, LOWER>(p, e.D, e.D2, e.C, e.alpha, mw + i * 16 + (lane & 15), nw + j * 16 + 4 * (lane >> 4), a4);
     }
-}
-
-// 32x32 fragments (v_mfma_f32_32x32x16, operands passed swapped): lane l owns row
-// (l % 32) and, for q = 0..3, columns 8 q + 4 (l / 32) + e of each fragment.
-template <class TOut, bool LOWER, int FM, int FN>
-__device__ __forceinline__ void epilogue32(const GemmParams& p, f32x16_t (&acc)[FM][FN], int bz, int mw, int nw,
-                                           int lane) {
-  const EpiPtrs e = epi_ptrs<TOut>(p, bz);
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float a4[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        emit_row4<TOut, LOWER>(p, e.D, e.D2, e.C, e.alpha, mw + i * 32 + (lane & 31),
-                               nw + j * 32 + 8 * q + 4 * (lane >> 5), a4);
-      }
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
@@ -416,19 +398,21 @@ gemm_kernel(GemmParams p) {
 // Operands go from HBM straight into LDS with buffer loads carrying the LDS flag (no
 // staging registers).  They are issued through inline assembly, so the compiler does
 // not track them and does not make every later LDS read wait for them; the kernel
-// waits explicitly (s_waitcnt vmcnt(0)) before the barrier that publishes a stage.
+// waits with explicit vmcnt counts for exactly the stage it is about to read, and
+// the loads of younger stages stay in flight.
 //
-// LDS per stage: A tile [BM rows][128 B] (64 k values, K-contiguous, 16-byte chunks
-// swizzled by swz()); B tile the same (NT) or, for the rectangular product, X's
-// natural layout [64 rows (k)][BN * 2 B] with 16-byte chunks XOR-ed by 2 (k & 3).
-// NN fragments are read with ds_read_b64_tr_b16: lane i of a 16-lane group passes
-// the address of row k0 + i/4, columns n0 + 4 (i % 4) .. +3 and receives column
-// n0 + i at rows k0 .. k0+3 -- an MFMA operand column (verified on gfx950).
+// LDS ring of STAGES slots, each one k-stage of 32 k values: the A tile as
+// [BM rows][64 B] (16-byte chunks swizzled by swz64()); the B tile the same (NT) or,
+// for the rectangular product, X's natural layout [32 rows (k)][BN * 2 B] with
+// 16-byte chunks XOR-ed by 2 (k & 3).  NN fragments are read with
+// ds_read_b64_tr_b16: lane i of a 16-lane group passes the address of row k0 + i/4,
+// columns n0 + 4 (i % 4) .. +3 and receives column n0 + i at rows k0 .. k0+3 -- an
+// MFMA operand column (verified on gfx950).
 //
-// Per 64-k stage each wave runs 4 k-steps of 16; fragments alternate between two
-// register sets so the LDS reads of k-step s+1 overlap the MFMAs of k-step s, and the
-// barrier sits inside the last k-step: the MFMAs after it cover the first LDS reads
-// of the next stage.
+// Per stage each wave runs 2 k-steps of 16; fragments alternate between two register
+// sets so the LDS reads of one k-step overlap the MFMAs of the other, and the barrier
+// that publishes the next stage sits between the two halves of the second k-step's
+// MFMAs, which cover the first LDS reads of the next stage.
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef int int4v_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -470,21 +454,35 @@ __device__ __forceinline__ void mfma32_step(f32x16_t& acc, const uint4& a, const
 // s_waitcnt immediate (gfx9 family) that waits until at most `vm` vector-memory
 // instructions of this wave are outstanding, leaving the other counters alone.
 constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | (0x7 << 4) | (0xF << 8) | (((vm >> 4) & 0x3) << 14); }
+// ... and until at most `n` LDS / scalar-memory operations are outstanding
+constexpr int waitcnt_lgkm(int n) { return 0xF | (0x7 << 4) | ((n & 0xF) << 8) | (0x3 << 14); }
+
+// Wait until at most `later` stages of LOADS loads each are outstanding (later is
+// uniform, 0 .. L).  s_waitcnt takes an immediate, hence one scalar branch per count.
+template <int L, int LOADS>
+__device__ __forceinline__ void wait_vm_stages(int later) {
+  if constexpr (L <= 0) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  } else {
+    if (later >= L) __builtin_amdgcn_s_waitcnt(waitcnt_vm(L * LOADS));
+    else wait_vm_stages<L - 1, LOADS>(later);
+  }
+}
 
 // Workgroup barrier that is also a compiler memory barrier (no LDS access moves
 // across it) but, unlike __syncthreads(), adds no waits on outstanding loads: the
 // kernel waits for exactly the stage it needs before calling it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK>
 struct Tile32 {
   static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
   static constexpr int kWM = BM / WAVES_M;
   static constexpr int kWN = BN / WAVES_N;
   static constexpr int kFM = kWM / 32;
   static constexpr int kFN = kWN / 32;
-  static constexpr int kStages = 4;           // LDS ring depth
-  static constexpr int kBK = 32;              // k values per stage (64-byte rows)
+  static constexpr int kStages = STAGES;      // LDS ring depth
+  static constexpr int kBK = BK;              // k values per stage (32: 64-byte rows, 64: 128-byte rows)
   static constexpr int kLdsBytes = kStages * (BM + BN) * kBK * 2;
 };
 
@@ -493,12 +491,155 @@ struct Tile32 {
 // and sit in different quarters; j selects the chunk within the quarter).
 __device__ __forceinline__ int swz64(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
-template <class TIn, class TB, class TOut, int BM, int BN, int WAVES_M, int WAVES_N, bool LOWER, bool NN>
+// physical chunk of logical chunk c in row r of a K-contiguous tile with BK values per row
+template <int BK>
+__device__ __forceinline__ int swz_k(int row, int chunk) {
+  if constexpr (BK == 32) return swz64(row, chunk);
+  else return swz(row, chunk);
+}
+
+// 16 bytes of TOut elements <-> fp32 values
+template <class TOut>
+__device__ __forceinline__ void unpack16(const uint4& c, float (&v)[16 / TOut::kBytes]) {
+#pragma unroll
+  for (int e = 0; e < 16 / TOut::kBytes; ++e) v[e] = chunk_elem<TOut>(c, e);
+}
+template <class TOut>
+__device__ __forceinline__ uint4 pack16(const float (&v)[16 / TOut::kBytes]) {
+  uint4 r;
+  uint32_t* w = reinterpret_cast<uint32_t*>(&r);
+  if constexpr (TOut::kBytes == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(v[e]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = TOut::from_f32(v[2 * i]) | (TOut::from_f32(v[2 * i + 1]) << 16);
+  }
+  return r;
+}
+
+// Write the 16-byte vector v to row `row`, columns col .. col+VE-1, keeping only the
+// elements whose column c satisfies lo <= c - col (all of them when lo <= 0) and
+// c - col <= hi (all when hi >= VE - 1): full vectors take one 16-byte store.
+template <class TOut>
+__device__ __forceinline__ void store_vec(uint8_t* base, long long ld, int row, int col, const float (&v)[16 / TOut::kBytes],
+                                          int lo, int hi) {
+  constexpr int VE = 16 / TOut::kBytes;
+  const long long off = (long long)row * ld + col;
+  if (lo <= 0 && hi >= VE - 1) {
+    *reinterpret_cast<uint4*>(base + off * TOut::kBytes) = pack16<TOut>(v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < VE; ++e)
+      if (e >= lo && e <= hi) store1<TOut>(base, off + e, v[e]);
+  }
+}
+
+// Epilogue of gemm16_kernel, staged through LDS (called after a workgroup barrier:
+// the operand ring is free).  Each wave takes its WM x WN sub-tile in slabs of 32
+// rows (one fragment row): the raw fp32 accumulators go to a per-wave slab
+// [32][WN + 4] (the padding spreads the 16 rows of a 128-bit access over distinct
+// banks); the row pass forms v = alpha acc + beta C + gamma [diagonal] for 16-byte
+// vectors along the output rows, stores them with coalesced 16-byte writes (D, and
+// D2 = v + delta [diagonal]) and puts v back in the slab; for a symmetric output the
+// mirror pass reads the slab down its columns and writes the strictly-lower elements
+// at their transposed positions.  Both triangles round the same fp32 value, so the
+// output is bitwise symmetric.  Only the slab writes index the accumulators, so
+// they stay in registers.
+template <class TOut, bool LOWER, int FM, int FN>
+__device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc)[FM][FN], int bz, int mw, int nw,
+                                             int lane, float* slab) {
+  constexpr int WN = FN * 32;
+  constexpr int S = WN + 4;
+  constexpr int VE = 16 / TOut::kBytes;          // output elements per 16-byte vector
+  constexpr int RV = WN / VE;                    // vectors per slab row
+  constexpr int MV = 32 / VE;                    // vectors per mirrored row
+  const EpiPtrs ep = epi_ptrs<TOut>(p, bz);
+  const bool has_c = ep.C != nullptr && p.beta != 0.0f;
+  const int M = p.M, N = p.N;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r0 = mw + 32 * i;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(slab + (lane & 31) * S + j * 32 + 8 * q + 4 * (lane >> 5)) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    // row pass
+    for (int t = lane; t < 32 * RV; t += 64) {
+      const int r = t / RV, c = (t % RV) * VE;
+      const int gm = r0 + r, gn = nw + c;
+      if (gm >= M || gn >= N) continue;          // N % 8 == 0: a vector is all in or all out
+      float* sp = slab + r * S + c;
+      float v[VE];
+#pragma unroll
+      for (int e = 0; e < VE; e += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(sp + e);
+        v[e] = ep.alpha * f.x; v[e + 1] = ep.alpha * f.y; v[e + 2] = ep.alpha * f.z; v[e + 3] = ep.alpha * f.w;
+      }
+      if (has_c) {
+        float cv[VE];
+        unpack16<TOut>(*reinterpret_cast<const uint4*>(ep.C + ((long long)gm * p.ldc + gn) * TOut::kBytes), cv);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) v[e] += p.beta * cv[e];
+      }
+      if (p.gamma != 0.0f) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+          if (gn + e == gm) v[e] += p.gamma;
+      }
+      const int hi = LOWER ? gm - gn : VE - 1;   // symmetric: columns up to the diagonal
+      if (hi >= 0) {
+        store_vec<TOut>(ep.D, p.ldd, gm, gn, v, 0, hi);
+        if (ep.D2) {
+          float w[VE];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) w[e] = v[e] + ((gn + e == gm) ? p.delta : 0.0f);
+          store_vec<TOut>(ep.D2, p.ldd2, gm, gn, w, 0, hi);
+        }
+      }
+      if constexpr (LOWER) {
+#pragma unroll
+        for (int e = 0; e < VE; e += 4) *reinterpret_cast<float4*>(sp + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+      }
+    }
+
+    if constexpr (LOWER) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // mirror pass: output row gn = nw + c, columns gm0 .. gm0+VE-1 from slab column c
+      for (int t = lane; t < WN * MV; t += 64) {
+        const int c = t / MV, rr = (t % MV) * VE;
+        const int gn = nw + c, gm0 = r0 + rr;
+        if (gn >= N || gm0 >= M) continue;       // M % 8 == 0 and gm0 % VE == 0
+        const int lo = gn + 1 - gm0;             // strictly lower sources: gm0 + e > gn
+        if (lo > VE - 1) continue;
+        float v[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) v[e] = slab[(rr + e) * S + c];
+        store_vec<TOut>(ep.D, p.ldd, gn, gm0, v, lo, VE - 1);
+        if (ep.D2) store_vec<TOut>(ep.D2, p.ldd2, gn, gm0, v, lo, VE - 1);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
+// A 128 x 128 wave tile keeps 256 fp32 accumulators per lane: such configurations
+// run one wave per SIMD with the full 512-register file (accumulators in AGPRs).
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+constexpr int max_waves_per_eu() { return (BM / WAVES_M) * (BN / WAVES_N) >= 128 * 128 ? 1 : 8; }
+
+template <class TIn, class TB, class TOut, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BKV, bool LOWER,
+          bool NN>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+__attribute__((amdgpu_waves_per_eu(1, max_waves_per_eu<BM, BN, WAVES_M, WAVES_N>())))
 gemm16_kernel(GemmParams p) {
   static_assert(TIn::kBytes == 2 && TB::kBytes == 2, "16-bit operands only");
   static_assert(!LOWER || (BM == BN && !NN), "symmetric tiles are square NT tiles");
-  using Cfg = Tile32<BM, BN, WAVES_M, WAVES_N>;
+  using Cfg = Tile32<BM, BN, WAVES_M, WAVES_N, STAGES, BKV>;
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int FM = Cfg::kFM, FN = Cfg::kFN;
   static_assert(FM >= 1 && FN >= 1, "wave tile must be a multiple of 32");
@@ -507,9 +648,12 @@ gemm16_kernel(GemmParams p) {
   constexpr int A_INSTR = A_BYTES / (1024 * NW), B_INSTR = B_BYTES / (1024 * NW);   // 1 KB per wave instruction
   constexpr int LOADS = A_INSTR + B_INSTR;                                           // per wave per stage
   constexpr int NCH = BN / 8;                                                        // NN: chunks per k row
+  constexpr int CPR = BK / 8;                                                        // NT: chunks per tile row
+  constexpr int KS = BK / 16;                                                        // MFMA k-steps per stage
+  static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "tile/wave mismatch");
   static_assert(!NN || NCH >= 8, "NN tiles need >= 64 columns");
-  static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
+  static_assert(NS >= 2 && LOADS * (NS - 1) < 64, "ring depth / vmcnt range");
 
   extern __shared__ __align__(16) uint8_t smem16[];
   const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)smem16);
@@ -550,7 +694,7 @@ gemm16_kernel(GemmParams p) {
     for (int i = 0; i < A_INSTR; ++i) {
       const int blk = i * NW + wave;
       const int q = blk * 64 + lane;                      // LDS chunk this lane fills
-      const int row = q >> 2, lc = swz64(row, q & 3);
+      const int row = q / CPR, lc = swz_k<BK>(row, q % CPR);
       const int gr = m0 + row, gk = k0 + lc * 8;
       const uint32_t off = (gr < M && gk < K) ? (uint32_t)(((size_t)gr * p.lda + gk) * 2) : kOutOfRange;
       dma16(rsA, __builtin_amdgcn_readfirstlane(sb + blk * 1024), off);
@@ -561,7 +705,7 @@ gemm16_kernel(GemmParams p) {
       const int q = blk * 64 + lane;
       uint32_t off;
       if constexpr (!NN) {
-        const int row = q >> 2, lc = swz64(row, q & 3);
+        const int row = q / CPR, lc = swz_k<BK>(row, q % CPR);
         const int gr = n0 + row, gk = k0 + lc * 8;
         off = (gr < N && gk < K) ? (uint32_t)(((size_t)gr * p.ldb + gk) * 2) : kOutOfRange;
       } else {
@@ -581,14 +725,14 @@ gemm16_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = wm * Cfg::kWM + i * 32 + (lane & 31);
-      fa[i] = as[row * 4 + swz64(row, ch)];
+      fa[i] = as[row * CPR + swz_k<BK>(row, ch)];
     }
     if constexpr (!NN) {
       const uint4* bs = reinterpret_cast<const uint4*>(sb + A_BYTES);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int row = wn * Cfg::kWN + j * 32 + (lane & 31);
-        fb[j] = bs[row * 4 + swz64(row, ch)];
+        fb[j] = bs[row * CPR + swz_k<BK>(row, ch)];
       }
     } else {
       const uint16_t* bh = reinterpret_cast<const uint16_t*>(sb + A_BYTES);
@@ -620,12 +764,7 @@ gemm16_kernel(GemmParams p) {
   // wait until k-stage `next` has landed; `last` is the last stage issued so far, and
   // the (last - next) stages issued after `next` may stay in flight (vmcnt counts
   // this wave's loads, which complete in issue order)
-  auto wait_for_stage = [&](int next, int last) {
-    const int later = last - next;
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  };
+  auto wait_for_stage = [&](int next, int last) { wait_vm_stages<NS - 1, LOADS>(last - next); };
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -636,43 +775,77 @@ gemm16_kernel(GemmParams p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int KT = (K + BK - 1) / BK;
-  constexpr int H = (FM + 1) / 2;     // fragment rows before / after the barrier
-  uint4 a0[FM], b0[FN], a1[FM], b1[FN];
-  for (int t = 0; t < NS - 1 && t < KT; ++t) issue_stage(t);
-  wait_for_stage(0, min(NS - 2, KT - 1));
+  constexpr int H = (FM + 1) / 2;     // fragment rows of the last k-step before / after the barrier
+  uint4 fa[2][FM], fb[2][FN];         // two fragment sets: k-step s in set s & 1
+  for (int t = 0; t < NS && t < KT; ++t) issue_stage(t);
+  wait_for_stage(0, min(NS - 1, KT - 1));
   lds_barrier();
-  read_frags(0, 0, a0, b0);
+  read_frags(0, 0, fa[0], fb[0]);
 
-  // Stage kt (ring slot kt % NS) holds its k-step 0 fragments in a0/b0 on entry:
-  //   read k-step 1 | MFMAs of k-step 0 | first rows of k-step 1
-  //   wait for stage kt+1, barrier (stage kt-1's slot is then free everywhere)
-  //   issue stage kt+NS-1 into that slot | read k-step 0 of stage kt+1
-  //   remaining rows of k-step 1
+  // Stage kt (ring slot kt % NS) holds its k-step 0 fragments in set 0 on entry:
+  //   k-steps 0 .. KS-2: read the fragments of the next k-step, MFMAs of this one
+  //   last k-step: MFMAs of its first fragment rows; all LDS reads of this stage are
+  //   now in registers (lgkmcnt 0); wait for stage kt+1, barrier -- stage kt+1 is
+  //   visible and slot kt % NS is free in every wave; refill that slot with stage
+  //   kt+NS; read k-step 0 of stage kt+1; MFMAs of the remaining rows.
   for (int kt = 0; kt < KT; ++kt) {
     const int slot = kt % NS;
-    read_frags(slot, 1, a1, b1);
-    mma(acc, a0, b0, 0, FM);
-    mma(acc, a1, b1, 0, H);
-    if (kt + 1 < KT) {
-      wait_for_stage(kt + 1, min(kt + NS - 2, KT - 1));   // stage kt+NS-1 is issued below
-      lds_barrier();
-      if (kt + NS - 1 < KT) issue_stage(kt + NS - 1);
-      read_frags((kt + 1) % NS, 0, a0, b0);
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      read_frags(slot, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      mma(acc, fa[ks & 1], fb[ks & 1], 0, FM);
     }
-    mma(acc, a1, b1, H, FM);
+    constexpr int L = (KS - 1) & 1;
+    mma(acc, fa[L], fb[L], 0, H);
+    if (kt + 1 < KT) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));              // this stage's LDS reads are done
+      wait_for_stage(kt + 1, min(kt + NS - 1, KT - 1));
+      lds_barrier();
+      if (kt + NS < KT) issue_stage(kt + NS);
+      read_frags((kt + 1) % NS, 0, fa[0], fb[0]);
+    }
+    mma(acc, fa[L], fb[L], H, FM);
   }
 
-  epilogue32<TOut, LOWER, FM, FN>(p, acc, bz, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane);
+  // every wave is done with the operand ring: reuse it for the epilogue slabs
+  static_assert(NW * 32 * (Cfg::kWN + 4) * 4 <= Cfg::kLdsBytes, "epilogue slabs exceed the LDS ring");
+  lds_barrier();
+  float* slab = reinterpret_cast<float*>(smem16) + wave * 32 * (Cfg::kWN + 4);
+  epilogue_lds<TOut, LOWER, FM, FN>(p, acc, bz, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane, slab);
 }
 
 // ---------------------------------------------------------------------------------
 // Host side: tile configurations and the launch of one configuration.
 
-// Output-tile configurations: (BM, BN, waves along M, waves along N).
-//   big:   256 x 256, 4 waves of 128 x 128 (128 KB of LDS, one workgroup per CU,
-//          one wave per SIMD with up to 512 registers: accumulators in AGPRs)
+// Output-tile configurations: (BM, BN, waves along M, waves along N, LDS ring depth
+// of the 16-bit kernel).  Measured on MI355X, a deeper ring does not help any of
+// them (3, 4 and 5 stages of the big tile run within 3% of each other; 8 or 16
+// stages of the small tiles are slower than 4), so all use 4 stages.
+//   big:   256 x 256, 8 waves of 128 x 64 (128 KB of LDS)
 //   mid:   128 x 128, 4 waves of 64 x 64   (64 KB)
 //   small:  64 x 64,  4 waves of 32 x 32   (32 KB) for problems with few tiles
+#ifndef GNS_BIG_WM
+#define GNS_BIG_WM 2
+#define GNS_BIG_WN 2
+#endif
+#ifndef GNS_BK_BIG
+#define GNS_BK_BIG 64
+#endif
+#ifndef GNS_STAGES_BIG
+#define GNS_STAGES_BIG 2
+#endif
+#ifndef GNS_BK_MID
+#define GNS_BK_MID 64
+#endif
+#ifndef GNS_STAGES_MID
+#define GNS_STAGES_MID 4
+#endif
+#ifndef GNS_BK_SMALL
+#define GNS_BK_SMALL 64
+#endif
+#ifndef GNS_STAGES_SMALL
+#define GNS_STAGES_SMALL 4
+#endif
 enum class TileCfg { kBig = 0, kMid = 1, kSmall = 2 };
 
 inline long long gemm_tiles(int M, int N, int bm, int bn, bool lower) {
@@ -697,31 +870,33 @@ inline TileCfg pick_tile(int M, int N, int batch, bool lower) {
   return TileCfg::kSmall;
 }
 
-template <class TIn, class TB, class TOut, int BM, int BN, int WM_, int WN_, bool LOWER, bool NN>
+template <class TIn, class TB, class TOut, int BM, int BN, int WM_, int WN_, int NS, int BKV, bool LOWER, bool NN>
 hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops) {
-  using Cfg = Tile<BM, BN, WM_, WN_>;
-  static_assert(Cfg::kLdsBytes == Tile32<BM, BN, WM_, WN_>::kLdsBytes, "same LDS footprint");
   // 16-bit operands: direct-to-LDS kernel; fp32 operands: register-staged kernel
+  constexpr bool k16 = TIn::kBytes == 2 && TB::kBytes == 2;
+  constexpr int threads = 64 * WM_ * WN_;
+  using T32 = Tile32<BM, BN, WM_, WN_, NS, BKV>;
+  constexpr int lds = k16 ? T32::kLdsBytes : Tile<BM, BN, WM_, WN_>::kLdsBytes;
+  constexpr int BK = k16 ? T32::kBK : 8 * TIn::kPerChunk;    // k per stage
   void (*kern)(GemmParams);
-  if constexpr (TIn::kBytes == 2 && TB::kBytes == 2)
-    kern = gemm16_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, LOWER, NN>;
+  if constexpr (k16)
+    kern = gemm16_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, NS, BKV, LOWER, NN>;
   else
     kern = gemm_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, LOWER, NN>;
   static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   const long long tiles = gemm_tiles(p.M, p.N, BM, BN, LOWER);
   if (!operand_extents_ok(p, TIn::kBytes, TB::kBytes, NN)) return hipErrorInvalidValue;
-  constexpr int BK = 8 * TIn::kPerChunk;
   const long long kpad = ((long long)(p.K + BK - 1) / BK) * BK;
   if (flops) *flops += 2.0 * (double)tiles * BM * BN * (double)kpad * batch;
   if (tiles == 0 || batch == 0) return hipSuccess;
   p.batch = batch;
   p.tiles = (int)tiles;
   clear_stale_error();
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * batch)), dim3(Cfg::kThreads), Cfg::kLdsBytes, stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * batch)), dim3(threads), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -733,9 +908,13 @@ hipError_t launch_cfg(GemmParams p, int batch, hipStream_t stream, double* flops
   const TileCfg cfg = pick_tile(p.M, p.N, batch, LOWER);
 #endif
   switch (cfg) {
-    case TileCfg::kBig: return launch_one<TIn, TB, TOut, 256, 256, 2, 4, LOWER, NN>(p, batch, stream, flops);
-    case TileCfg::kMid: return launch_one<TIn, TB, TOut, 128, 128, 2, 2, LOWER, NN>(p, batch, stream, flops);
-    case TileCfg::kSmall: return launch_one<TIn, TB, TOut, 64, 64, 2, 2, LOWER, NN>(p, batch, stream, flops);
+    case TileCfg::kBig:
+      return launch_one<TIn, TB, TOut, 256, 256, GNS_BIG_WM, GNS_BIG_WN, GNS_STAGES_BIG, GNS_BK_BIG, LOWER, NN>(
+          p, batch, stream, flops);
+    case TileCfg::kMid:
+      return launch_one<TIn, TB, TOut, 128, 128, 2, 2, GNS_STAGES_MID, GNS_BK_MID, LOWER, NN>(p, batch, stream, flops);
+    case TileCfg::kSmall:
+      return launch_one<TIn, TB, TOut, 64, 64, 2, 2, GNS_STAGES_SMALL, GNS_BK_SMALL, LOWER, NN>(p, batch, stream, flops);
   }
   return hipErrorInvalidValue;
 }
