@@ -30,6 +30,45 @@ __device__ __forceinline__ void tri_decode(int t, int& i, int& j) {
   j = t - r * (r + 1) / 2;
 }
 
+// Tile orders that keep the workgroups running at the same time on one XCD on a few
+// operand panels: tiles go in groups of G tile-rows, column by column within a group
+// (32 concurrent 256 x 256 tiles then read 4 A panels and 8 B panels instead of 2
+// and 16), so a k-slice fetched from HBM is reused from L2 by more tiles.
+__device__ __forceinline__ void rect_tile_grouped(int t, int tiles_m, int tiles_n, int G, int& tm, int& tn) {
+  const int per_group = G * tiles_n;
+  const int group = t / per_group;
+  const int first = group * G;
+  const int gm = min(tiles_m - first, G);
+  const int r = t - group * per_group;
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
+// The same for the lower triangle (tile t in row-major triangle order): the group of
+// tile-rows R0 .. R0+gm-1 is taken column by column; columns 0 .. R0 hold gm tiles
+// each, column R0+k (k >= 1) holds the gm-k tiles on or below the diagonal.
+__device__ __forceinline__ void lower_tile_grouped(int t, int tiles, int G, int& tm, int& tn) {
+  int r, c;
+  tri_decode(t, r, c);
+  const int R0 = (r / G) * G;
+  const int gm = min(G, tiles - R0);
+  int idx = t - R0 * (R0 + 1) / 2;
+  const int full = (R0 + 1) * gm;
+  if (idx < full) {
+    tn = idx / gm;
+    tm = R0 + idx % gm;
+  } else {
+    idx -= full;
+    int k = 1;
+    while (idx >= gm - k) {
+      idx -= gm - k;
+      ++k;
+    }
+    tn = R0 + k;
+    tm = R0 + k + idx;
+  }
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on XCD i % 8),
 // and each XCD has its own L2.  Give XCD x one contiguous range of logical ids so the
 // tiles it runs share operand panels (and, for batched problems, whole matrices).
@@ -667,11 +706,11 @@ gemm16_kernel(GemmParams p) {
   const int bz = __builtin_amdgcn_readfirstlane(rid / p.tiles);
   const int tile = __builtin_amdgcn_readfirstlane(rid - bz * p.tiles);
   int tm, tn;
+  constexpr int kGroup = BM >= 256 ? 4 : 8;
   if constexpr (LOWER) {
-    tri_decode(tile, tm, tn);
+    lower_tile_grouped(tile, p.tiles_m, kGroup, tm, tn);
   } else {
-    tm = tile / p.tiles_n;
-    tn = tile % p.tiles_n;
+    rect_tile_grouped(tile, p.tiles_m, p.tiles_n, kGroup, tm, tn);
   }
   const int m0 = __builtin_amdgcn_readfirstlane(tm * BM), n0 = __builtin_amdgcn_readfirstlane(tn * BN);
   const int M = p.M, N = p.N, K = p.K;
@@ -686,22 +725,20 @@ gemm16_kernel(GemmParams p) {
     if (p.scale) for (int i = 0; i < p.b_pow; ++i) bmul *= p.scale[bz];
   }
 
-  // issue the direct HBM -> LDS loads of k-stage kt into LDS ring slot kt % NS
-  auto issue_stage = [&](int kt) {
+  // load g (0 .. LOADS-1) of k-stage kt: one direct HBM -> LDS instruction (1 KB per
+  // wave) into ring slot kt % NS; loads 0 .. A_INSTR-1 fill the A tile, the rest B
+  auto issue_load = [&](int kt, int g) {
     const int k0 = kt * BK;
     const uint32_t sb = lds0 + (kt % NS) * STAGE;
-#pragma unroll
-    for (int i = 0; i < A_INSTR; ++i) {
-      const int blk = i * NW + wave;
+    if (g < A_INSTR) {
+      const int blk = g * NW + wave;
       const int q = blk * 64 + lane;                      // LDS chunk this lane fills
       const int row = q / CPR, lc = swz_k<BK>(row, q % CPR);
       const int gr = m0 + row, gk = k0 + lc * 8;
       const uint32_t off = (gr < M && gk < K) ? (uint32_t)(((size_t)gr * p.lda + gk) * 2) : kOutOfRange;
       dma16(rsA, __builtin_amdgcn_readfirstlane(sb + blk * 1024), off);
-    }
-#pragma unroll
-    for (int i = 0; i < B_INSTR; ++i) {
-      const int blk = i * NW + wave;
+    } else {
+      const int blk = (g - A_INSTR) * NW + wave;
       const int q = blk * 64 + lane;
       uint32_t off;
       if constexpr (!NN) {
@@ -715,6 +752,10 @@ gemm16_kernel(GemmParams p) {
       }
       dma16(rsB, __builtin_amdgcn_readfirstlane(sb + A_BYTES + blk * 1024), off);
     }
+  };
+  auto issue_stage = [&](int kt) {
+#pragma unroll
+    for (int g = 0; g < LOADS; ++g) issue_load(kt, g);
   };
 
   // fragments of k-step ks (16 k values) of the stage in ring slot `slot`
@@ -776,18 +817,27 @@ gemm16_kernel(GemmParams p) {
 
   const int KT = (K + BK - 1) / BK;
   constexpr int H = (FM + 1) / 2;     // fragment rows of the last k-step before / after the barrier
+  constexpr int L = (KS - 1) & 1;     // fragment set of the last k-step
+  static_assert(L == 1, "the last k-step's fragments must not sit in set 0");
+  constexpr int TAIL = (FM - H) * FN; // MFMAs after the barrier
+  constexpr int PER = TAIL > 0 ? (LOADS + TAIL - 1) / TAIL : LOADS;
   uint4 fa[2][FM], fb[2][FN];         // two fragment sets: k-step s in set s & 1
-  for (int t = 0; t < NS && t < KT; ++t) issue_stage(t);
-  wait_for_stage(0, min(NS - 1, KT - 1));
+  // Stages at or past KT are issued like the others: all their offsets are out of
+  // range, so they only write zeros into ring slots whose data is never used, and
+  // every iteration runs the same code (NS - 1 younger stages in flight at each wait).
+#pragma unroll
+  for (int t = 0; t < NS; ++t) issue_stage(t);
+  wait_for_stage(0, NS - 1);
   lds_barrier();
   read_frags(0, 0, fa[0], fb[0]);
 
   // Stage kt (ring slot kt % NS) holds its k-step 0 fragments in set 0 on entry:
-  //   k-steps 0 .. KS-2: read the fragments of the next k-step, MFMAs of this one
+  //   k-steps 0 .. KS-2: read the fragments of the next k-step, MFMAs of this one;
   //   last k-step: MFMAs of its first fragment rows; all LDS reads of this stage are
-  //   now in registers (lgkmcnt 0); wait for stage kt+1, barrier -- stage kt+1 is
-  //   visible and slot kt % NS is free in every wave; refill that slot with stage
-  //   kt+NS; read k-step 0 of stage kt+1; MFMAs of the remaining rows.
+  //   now in registers (lgkmcnt 0); wait for stage kt+1; barrier -- stage kt+1 is
+  //   visible and slot kt % NS is free in every wave; read k-step 0 of stage kt+1;
+  //   the remaining MFMAs, with the loads of stage kt+NS (into the freed slot)
+  //   issued between them so the MFMA pipe stays busy meanwhile.
   for (int kt = 0; kt < KT; ++kt) {
     const int slot = kt % NS;
 #pragma unroll
@@ -795,17 +845,23 @@ gemm16_kernel(GemmParams p) {
       read_frags(slot, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
       mma(acc, fa[ks & 1], fb[ks & 1], 0, FM);
     }
-    constexpr int L = (KS - 1) & 1;
     mma(acc, fa[L], fb[L], 0, H);
-    if (kt + 1 < KT) {
-      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));              // this stage's LDS reads are done
-      wait_for_stage(kt + 1, min(kt + NS - 1, KT - 1));
-      lds_barrier();
-      if (kt + NS < KT) issue_stage(kt + NS);
-      read_frags((kt + 1) % NS, 0, fa[0], fb[0]);
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+    wait_for_stage(kt + 1, kt + NS - 1);
+    lds_barrier();
+    read_frags((kt + 1) % NS, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int t = 0; t < (TAIL > 0 ? TAIL : 1); ++t) {
+      if constexpr (TAIL > 0) {
+        const int i = H + t / FN, j = t % FN;
+        mfma32_step<TIn>(acc[i][j], fa[L][i], fb[L][j]);
+      }
+#pragma unroll
+      for (int r = 0; r < PER; ++r)
+        if (t * PER + r < LOADS) issue_load(kt + NS, t * PER + r);
     }
-    mma(acc, fa[L], fb[L], H, FM);
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the trailing out-of-range loads have written their zeros
 
   // every wave is done with the operand ring: reuse it for the epilogue slabs
   static_assert(NW * 32 * (Cfg::kWN + 4) * 4 <= Cfg::kLdsBytes, "epilogue slabs exceed the LDS ring");
