@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--compute", default="f16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 512 MiB device copy 5 times (reference for rocprofv3 "
+                        "FETCH_SIZE / WRITE_SIZE scale factors) and exit")
     return p.parse_args()
 
 
@@ -58,6 +61,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(256 << 20, device=dev, dtype=torch.float16)     # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": src.numel() * 2,
+                          "bytes_written": dst.numel() * 2, "launches": 5}), flush=True)
+        return
     w = synth.workload(args.workload)
     if w.name.startswith("dion3"):
         return bench_dion3(args, w)
@@ -102,7 +114,7 @@ def main():
     torch.cuda.synchronize()
     ms_std = 1e3 * (time.perf_counter() - t1) / nstd
 
-    roof = dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, args.steps)
+    roof = dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, args.steps, w.name)
     line = {
         "metric": METRIC,
         "value": round(mats_per_s, 3),
@@ -133,11 +145,39 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps):
+GEMM_SOURCES = ("muon_gram_ns_amd/csrc/gemm_kernel.h", "muon_gram_ns_amd/csrc/gemm_symm.hip",
+                "muon_gram_ns_amd/csrc/common.h", "muon_gram_ns_amd/csrc/internal.h")
+TRAFFIC_FILE = "profiles/traffic_gemm16_lower_f16_gns_1024x4096.json"
+
+
+def gemm_source_digest():
+    """sha256 over the GEMM kernel sources: HBM traffic counted with rocprofv3 is
+    only reported while the kernel is the one it was counted on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name):
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("workload") != workload_name or t.get("gemm_source_sha256") != gemm_source_digest():
+        return None
+    return t["bytes_per_launch"]
+
+
+def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, workload_name):
     """The lower-tile symmetric MFMA product in the iterate dtype dominates a Gram NS
-    call.  Replay its per-call launch mix (the n x n products with K = n, plus the
-    restart Gram product with K = m) through symm_gemm on the current stream and time
-    it with HIP events; achieved = algorithmic flops per launch / average launch."""
+    call.  Its per-call launch mix (the n x n products with K = n, plus the restart
+    Gram product with K = m) is replayed through the C ABI on the current stream,
+    captured once in a HIP graph so the events time back-to-back kernels rather than
+    host launch overhead; achieved = algorithmic flops per launch / average launch."""
     dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[compute]
     # Gram NS (T=5, restart after 2), n x n products per call: t1: Z, Y, R (3); t2: Z, Q (2);
     # t3: Z, Y, R (3); t4: Z, Q, Y, R (4); t5: Z, Q (2) = 14; plus the Gram product of the
@@ -147,6 +187,7 @@ def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps):
     R = (R + R.transpose(1, 2)) * 0.5
     Xh = (torch.randn(B, n, m, device="cuda") / m ** 0.5).to(dt)
     D = torch.empty(B, n, n, device="cuda", dtype=dt)
+    per_graph = 10
 
     def mix():
         for _ in range(nn_k):
@@ -154,25 +195,41 @@ def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps):
         for _ in range(mm_k):
             gns.symm_gemm(Xh, Xh, out=D)
 
-    reps = max(5, steps // 4)
     for _ in range(3):
         mix()
+    torch.cuda.synchronize()
+    timing = "HIP graph replay"
+    try:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                mix()
+        run = graph.replay
+        launches_per_run = per_graph * (nn_k + mm_k)
+    except Exception as exc:  # capture unavailable: eager launches, host overhead included
+        timing = f"eager launches (graph capture failed: {type(exc).__name__})"
+        run = mix
+        launches_per_run = nn_k + mm_k
+    reps = max(5, steps // (4 * per_graph))
+    run()
+    stream = torch.cuda.current_stream()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    s.record()
+    s.record(stream)
     for _ in range(reps):
-        mix()
-    e.record()
+        run()
+    e.record(stream)
     torch.cuda.synchronize()
-    launches = reps * (nn_k + mm_k)
-    avg_s = s.elapsed_time(e) * 1e-3 / launches
+    avg_s = s.elapsed_time(e) * 1e-3 / (reps * launches_per_run)
     alg_per_launch = B * (nn_k * F.sym(n, n) + mm_k * F.sym(n, m)) / (nn_k + mm_k)
     achieved = alg_per_launch / avg_s / 1e12
-    return {"bound": "mfma", "kernel": f"gemm_kernel<{compute}, lower-triangle symmetric>",
+    traffic = measured_traffic(workload_name) if not square else None
+    return {"bound": "mfma", "kernel": f"gemm16_kernel ({compute}, lower-triangle symmetric)",
             "shape_mix": f"{nn_k} x (n={n}, K={n}) + {mm_k} x (n={n}, K={m}) per call, batch {B}",
-            "avg_launch_us": round(avg_s * 1e6, 3),
+            "timing": timing, "avg_launch_us": round(avg_s * 1e6, 3),
+            "algorithmic_flops_per_launch": alg_per_launch,
             "achieved": round(achieved, 3), "peak": PEAK_16BIT_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_16BIT_TFLOPS, 5), "traffic": None}
+            "frac": round(achieved / PEAK_16BIT_TFLOPS, 5), "traffic": traffic}
 
 
 def cpu_baseline(st, w, seconds):
