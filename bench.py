@@ -18,6 +18,7 @@ Other workloads (--workload) print the same line for that workload.
 from __future__ import annotations
 
 import argparse
+import math
 import json
 import os
 import sys
@@ -255,35 +256,66 @@ def cpu_baseline(st, w, seconds):
 
 
 def bench_dion3(args, w):
-    import numpy as np
+    """Dion3 step on the 8192 x 28672 workload at f = 1/4 and 1/8 (l2 row scores).
+    Inputs are drawn on the device from a seeded generator with the workload's
+    distribution (W, G, M ~ N(0, 0.02), bf16); the parity tests use synth's bytes.
+    Besides whole steps/s, each HBM-bound step is timed alone through its own ABI
+    entry point (HIP events on the current stream) and reported in GB/s of
+    algorithmic traffic; the roofline names the dominant one."""
     import torch
     import muon_gram_ns_amd as gns
-    import synth
     from muon_gram_ns_amd import flops as F
-    wb, gb, mb = synth.dion3_state()
-    tb = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-    W, M, G = tb(wb), tb(mb), tb(gb)
-    N, m = W.shape
+    N, m = w.n, w.m
+    gen = torch.Generator(device="cuda").manual_seed(1000 + w.index)
+    dev_bf16 = lambda: (torch.randn(N, m, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    W, G, M = dev_bf16(), dev_bf16(), dev_bf16()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(reps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e-3 / reps
+
     res = {}
     for f in (0.25, 0.125):
-        k = int(round(f * N))
+        k = math.ceil(f * N)                  # f = 1/4, 1/8: exact
         lr = 0.01 / f ** 0.5
+        step = lambda: gns.dion3_step(W, M, G, k, lr, 0.0, 0.95, score_norm=2, compute=args.compute)
         for _ in range(args.warmup):
-            gns.dion3_step(W, M, G, k, lr, 0.0, 0.95, score_norm=2, compute=args.compute)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            gns.dion3_step(W, M, G, k, lr, 0.0, 0.95, score_norm=2, compute=args.compute)
-        torch.cuda.synchronize()
-        ms = 1e3 * (time.perf_counter() - t0) / args.steps
-        res[f] = {"k": k, "ms_per_step": round(ms, 4), "gram_tflops_algorithmic":
-                  round(F.gram_schedule(k, m) / (ms * 1e-3) / 1e12, 2)}
+            step()
+        t = timed(step, args.steps)
+        res[f] = {"k": k, "ms_per_step": round(t * 1e3, 4),
+                  "gram_ns_tflops_algorithmic": round(F.gram_schedule(k, m) / t / 1e12, 2)}
+    # the HBM-bound pieces, alone (k = 2048)
+    k = N // 4
+    reps = max(5, args.steps)
+    S = gns.dion3_select_topk(gns.dion3_accumulate_score(M, G, 2)[0], k)
+    X = gns.dion3_gather_feedback(M, S, 0.95)
+    t_acc = timed(lambda: gns.dion3_accumulate_score(M, G, 2), reps)
+    t_sel = timed(lambda: gns.dion3_select_topk(gns.dion3_accumulate_score(M, G, 2)[0], k), reps) - t_acc
+    t_gat = timed(lambda: gns.dion3_gather_feedback(M, S, 0.95), reps)
+    t_upd = timed(lambda: gns.dion3_apply_update(W, S, X, 0.02, 0.0), reps)
+    b_acc, b_gat, b_upd = 3.0 * N * m * 2, 3.0 * k * m * 2, 3.0 * k * m * 2
+    pieces = {"accumulate_score": {"us": round(t_acc * 1e6, 2), "bytes": b_acc, "GB_s": round(b_acc / t_acc / 1e9, 1)},
+              "select_topk": {"us": round(t_sel * 1e6, 2)},
+              "gather_feedback": {"us": round(t_gat * 1e6, 2), "bytes": b_gat, "GB_s": round(b_gat / t_gat / 1e9, 1)},
+              "apply_update": {"us": round(t_upd * 1e6, 2), "bytes": b_upd, "GB_s": round(b_upd / t_upd / 1e9, 1)}}
     ms = res[0.25]["ms_per_step"]
+    roof = {"bound": "hbm", "kernel": "accumulate_score_kernel", "achieved": pieces["accumulate_score"]["GB_s"],
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pieces["accumulate_score"]["GB_s"] / PEAK_HBM_GBS, 4),
+            "traffic": None, "algorithmic_bytes_per_launch": b_acc}
     print(json.dumps({"metric": "Dion3 steps/s", "value": round(1e3 / ms, 3), "unit": "steps/s", "n_gpus": 1,
                       "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
                       "scaling": "weak", "vs_baseline": None, "dtype": args.compute, "data": "synthetic",
-                      "config": {"workload": w.name, "N": N, "m": m, "score": "l2", "fractions": res},
-                      "roofline": None, "cpu_baseline": None}), flush=True)
+                      "config": {"workload": w.name, "N": N, "m": m, "score": "l2", "mu": 0.95, "wd": 0.0,
+                                 "fractions": res},
+                      "hbm_pieces_k2048": pieces, "roofline": roof, "cpu_baseline": None}), flush=True)
 
 
 if __name__ == "__main__":

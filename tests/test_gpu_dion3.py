@@ -113,8 +113,11 @@ def test_dion3_step_small(gns_mod, norm, wd):
 @pytest.mark.timeout(900)
 def test_dion3_step_full_size(gns_mod):
     """The 8192 x 28672 workload at f = 1/4 and 1/8 with l2 row scores."""
+    announce("dion3 8192x28672: generating inputs")
     w, g, m = synth.dion3_state()
+    announce("dion3 8192x28672: oracle accumulate")
     m1 = accumulate(m, g)
+    announce("dion3 8192x28672: oracle row scores")
     sc = row_scores(m1, "l2")
     for f in (0.25, 0.125):
         announce(f"dion3 step 8192x28672 f={f}")
@@ -124,10 +127,12 @@ def test_dion3_step_full_size(gns_mod):
         S, O = gns_mod.dion3_step(W, M, G, k, 0.01 / np.sqrt(f), weight_decay=0.0, mu=0.95, score_norm=2,
                                   return_O=True)
         assert np.array_equal(S.cpu().numpy(), S_ref)
+        announce(f"dion3 8192x28672 f={f}: comparing M and W")
         assert np.array_equal(bits(M), error_feedback(m1, S_ref, 0.95))
         rest = np.setdiff1d(np.arange(8192), S_ref)
         assert np.array_equal(bits(W)[rest], w[rest])
         if f == 0.125:   # one full-size orthogonalisation check (oracle cost ~1e12 flops)
+            announce(f"dion3 8192x28672 f={f}: oracle Newton-Schulz on the selected rows")
             O_ref = newton_schulz(bf16_to_f64(m1[S_ref]))
             e = rel_fro(to_f64(O), O_ref)
             print(f"f={f} O rel err {e:.3e}")
