@@ -275,10 +275,8 @@ hipError_t launch_apply_update(uint16_t* W, int N, int m, long long ld, const in
 
 // ---- s = 1 / (sqrt(sum_i sumsq[S[i]]) + eps) ------------------------------------------
 __global__ void __launch_bounds__(kRowThreads)
-selected_sumsq_kernel(const double* sumsq, const int* S, int k, int N, float eps, float* s_out, unsigned* zero,
-                      int nzero) {
+selected_sumsq_kernel(const double* sumsq, const int* S, int k, int N, float eps, float* s_out) {
   __shared__ double sh[kRowThreads / 64];
-  for (int i = threadIdx.x; i < nzero; i += kRowThreads) zero[i] = 0u;     // split-K counters of the next products
   const int per = (k + kRowThreads - 1) / kRowThreads;
   double acc = 0.0;
   for (int i = threadIdx.x * per; i < min(k, (int)(threadIdx.x + 1) * per); ++i) {
@@ -290,10 +288,9 @@ selected_sumsq_kernel(const double* sumsq, const int* S, int k, int N, float eps
 }
 
 hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int k, int N, float eps, float* s_out,
-                                 hipStream_t s, unsigned* zero, int nzero) {
+                                 hipStream_t s) {
   clear_stale_error();
-  hipLaunchKernelGGL(selected_sumsq_kernel, dim3(1), dim3(kRowThreads), 0, s, sumsq, S, k, N, eps, s_out, zero,
-                     zero ? nzero : 0);
+  hipLaunchKernelGGL(selected_sumsq_kernel, dim3(1), dim3(kRowThreads), 0, s, sumsq, S, k, N, eps, s_out);
   return hipGetLastError();
 }
 

@@ -65,11 +65,9 @@ frob_partial_kernel(const uint8_t* X, long long ldx, long long sx, int n, int m,
 }
 
 __global__ void __launch_bounds__(kRedThreads)
-frob_finish_kernel(const float* partials, int P, float eps, float* s_out, unsigned* zero, int nzero) {
+frob_finish_kernel(const float* partials, int P, float eps, float* s_out) {
   __shared__ float sh[kRedThreads / 64];
   const int b = blockIdx.x;
-  if (b == 0)
-    for (int i = threadIdx.x; i < nzero; i += kRedThreads) zero[i] = 0u;
   // each thread adds a contiguous slice in order, then the fixed tree
   const int per = (P + kRedThreads - 1) / kRedThreads;
   float acc = 0.f;
@@ -79,8 +77,7 @@ frob_finish_kernel(const float* partials, int P, float eps, float* s_out, unsign
 }
 
 hipError_t launch_frob(const void* X, gns_dtype dt, long long ldx, long long stride_x, int batch, int n,
-                       int m, float eps, float* s_out, float* partials, hipStream_t stream, unsigned* zero,
-                       int nzero) {
+                       int m, float eps, float* s_out, float* partials, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
   const int P = frob_partials_per_batch(n, m);
   dim3 grid(P, batch);
@@ -93,8 +90,7 @@ hipError_t launch_frob(const void* X, gns_dtype dt, long long ldx, long long str
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   clear_stale_error();
-  hipLaunchKernelGGL(frob_finish_kernel, dim3(batch), dim3(kRedThreads), 0, stream, partials, P, eps, s_out,
-                     zero, zero ? nzero : 0);
+  hipLaunchKernelGGL(frob_finish_kernel, dim3(batch), dim3(kRedThreads), 0, stream, partials, P, eps, s_out);
   return hipGetLastError();
 }
 

@@ -701,11 +701,8 @@ gemm16_kernel(GemmParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  // block-level indices are uniform; readfirstlane keeps them in scalar registers.
-  // The K ranges (splits) of one output tile are consecutive logical ids.
-  const int rid0 = xcd_remap((int)blockIdx.x, p.batch * p.tiles * p.splits);
-  const int rid = __builtin_amdgcn_readfirstlane(rid0 / p.splits);
-  const int split = __builtin_amdgcn_readfirstlane(rid0 - rid * p.splits);
+  // block-level indices are uniform; readfirstlane keeps them in scalar registers
+  const int rid = xcd_remap((int)blockIdx.x, p.batch * p.tiles);
   const int bz = __builtin_amdgcn_readfirstlane(rid / p.tiles);
   const int tile = __builtin_amdgcn_readfirstlane(rid - bz * p.tiles);
   int tm, tn;
@@ -717,11 +714,6 @@ gemm16_kernel(GemmParams p) {
   }
   const int m0 = __builtin_amdgcn_readfirstlane(tm * BM), n0 = __builtin_amdgcn_readfirstlane(tn * BN);
   const int M = p.M, N = p.N, K = p.K;
-  // this workgroup's K range: stages kt0 .. kt0+KT-1 of 64 (or 32) k values
-  const int KT_all = (K + BK - 1) / BK;
-  const int kt0 = p.splits > 1 ? split * p.kt_per_split : 0;
-  const int KT = p.splits > 1 ? min(KT_all, kt0 + p.kt_per_split) - kt0 : KT_all;
-  const int kend = min(K, (kt0 + KT) * BK);
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A) + (size_t)bz * p.sA * 2;
   const uint8_t* Bb = reinterpret_cast<const uint8_t*>(p.B) + (size_t)bz * p.sB * 2;
   const int4v_t rsA = sgpr_rsrc(Ab, (uint32_t)(((size_t)(M - 1) * p.lda + K) * 2));
@@ -736,14 +728,14 @@ gemm16_kernel(GemmParams p) {
   // load g (0 .. LOADS-1) of k-stage kt: one direct HBM -> LDS instruction (1 KB per
   // wave) into ring slot kt % NS; loads 0 .. A_INSTR-1 fill the A tile, the rest B
   auto issue_load = [&](int kt, int g) {
-    const int k0 = (kt0 + kt) * BK;                       // kt counts stages of this K range
+    const int k0 = kt * BK;
     const uint32_t sb = lds0 + (kt % NS) * STAGE;
     if (g < A_INSTR) {
       const int blk = g * NW + wave;
       const int q = blk * 64 + lane;                      // LDS chunk this lane fills
       const int row = q / CPR, lc = swz_k<BK>(row, q % CPR);
       const int gr = m0 + row, gk = k0 + lc * 8;
-      const uint32_t off = (gr < M && gk < kend) ? (uint32_t)(((size_t)gr * p.lda + gk) * 2) : kOutOfRange;
+      const uint32_t off = (gr < M && gk < K) ? (uint32_t)(((size_t)gr * p.lda + gk) * 2) : kOutOfRange;
       dma16(rsA, __builtin_amdgcn_readfirstlane(sb + blk * 1024), off);
     } else {
       const int blk = (g - A_INSTR) * NW + wave;
@@ -752,11 +744,11 @@ gemm16_kernel(GemmParams p) {
       if constexpr (!NN) {
         const int row = q / CPR, lc = swz_k<BK>(row, q % CPR);
         const int gr = n0 + row, gk = k0 + lc * 8;
-        off = (gr < N && gk < kend) ? (uint32_t)(((size_t)gr * p.ldb + gk) * 2) : kOutOfRange;
+        off = (gr < N && gk < K) ? (uint32_t)(((size_t)gr * p.ldb + gk) * 2) : kOutOfRange;
       } else {
         const int kr = q / NCH, lc = (q % NCH) ^ (2 * (kr & 3));
         const int gk = k0 + kr, gn = n0 + lc * 8;
-        off = (gk < kend && gn < N) ? (uint32_t)(((size_t)gk * p.ldb + gn) * 2) : kOutOfRange;
+        off = (gk < K && gn < N) ? (uint32_t)(((size_t)gk * p.ldb + gn) * 2) : kOutOfRange;
       }
       dma16(rsB, __builtin_amdgcn_readfirstlane(sb + A_BYTES + blk * 1024), off);
     }
@@ -823,6 +815,7 @@ gemm16_kernel(GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  const int KT = (K + BK - 1) / BK;
   constexpr int H = (FM + 1) / 2;     // fragment rows of the last k-step before / after the barrier
   constexpr int L = (KS - 1) & 1;     // fragment set of the last k-step
   static_assert(L == 1, "the last k-step's fragments must not sit in set 0");
@@ -869,55 +862,6 @@ gemm16_kernel(GemmParams p) {
     }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the trailing out-of-range loads have written their zeros
-
-  if (LOWER && p.splits > 1) {
-    // Split K: park this range's fp32 partial tile in the workspace (each lane its own
-    // registers, coalesced across lanes); the last of the tile's workgroups to arrive
-    // sums all partials in split order -- a fixed order, so the result is the same
-    // whichever arrives last -- and runs the epilogue.  The arrival counter goes back
-    // to zero for the next launch.
-    // The partials and the counter use system-coherent accesses, which go past the
-    // per-XCD L2s to memory; after vmcnt(0) the stores are complete there.  This
-    // avoids fences, which would write back and invalidate a whole L2 per workgroup.
-    __shared__ int last_arrival;
-    constexpr int PER_WAVE = FM * FN * 16 * 64;
-    float* mine = p.partial + (size_t)rid0 * (BM * BN) + wave * PER_WAVE + lane;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          __hip_atomic_store(mine + ((i * FN + j) * 16 + e) * 64, acc[i][j][e], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_SYSTEM);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));     // this wave's partial stores are complete
-    lds_barrier();                                 // ... and every other wave's
-    if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(p.counters + rid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      last_arrival = prev == (unsigned)(p.splits - 1);
-      if (last_arrival) __hip_atomic_store(p.counters + rid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-    lds_barrier();
-    if (!last_arrival) return;
-    const float* base = p.partial + (size_t)rid * p.splits * (BM * BN) + wave * PER_WAVE + lane;
-    auto part_at = [&](int sp, int idx) {
-      return __hip_atomic_load(base + (size_t)sp * (BM * BN) + idx * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    };
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = part_at(0, (i * FN + j) * 16 + e);
-    for (int sp = 1; sp < p.splits; ++sp) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][j][e] += part_at(sp, (i * FN + j) * 16 + e);
-    }
-  }
 
   // every wave is done with the operand ring: reuse it for the epilogue slabs
   static_assert(NW * 32 * (Cfg::kWN + 4) * 4 <= Cfg::kLdsBytes, "epilogue slabs exceed the LDS ring");
@@ -982,12 +926,6 @@ inline TileCfg pick_tile(int M, int N, int batch, bool lower) {
   return TileCfg::kSmall;
 }
 
-// output tile edge and k values per ring stage of the 16-bit kernel, per configuration
-inline int tile_edge(TileCfg c) { return c == TileCfg::kBig ? 256 : c == TileCfg::kMid ? 128 : 64; }
-inline int stage_k(TileCfg c) {
-  return c == TileCfg::kBig ? GNS_BK_BIG : c == TileCfg::kMid ? GNS_BK_MID : GNS_BK_SMALL;
-}
-
 template <class TIn, class TB, class TOut, int BM, int BN, int WM_, int WN_, int NS, int BKV, bool LOWER, bool NN>
 hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops) {
   // 16-bit operands: direct-to-LDS kernel; fp32 operands: register-staged kernel
@@ -1013,30 +951,18 @@ hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops
   if (tiles == 0 || batch == 0) return hipSuccess;
   p.batch = batch;
   p.tiles = (int)tiles;
-  if (!k16 || !LOWER || p.splits < 1) p.splits = 1;
   clear_stale_error();
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * batch * p.splits)), dim3(threads), lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * batch)), dim3(threads), lds, stream, p);
   return hipGetLastError();
 }
 
 template <class TIn, class TB, class TOut, bool LOWER, bool NN>
 hipError_t launch_cfg(GemmParams p, int batch, hipStream_t stream, double* flops) {
 #ifdef GNS_FORCE_TILE
-  TileCfg cfg = static_cast<TileCfg>(GNS_FORCE_TILE);
+  const TileCfg cfg = static_cast<TileCfg>(GNS_FORCE_TILE);
 #else
-  TileCfg cfg = pick_tile(p.M, p.N, batch, LOWER);
+  const TileCfg cfg = pick_tile(p.M, p.N, batch, LOWER);
 #endif
-  p.splits = 1;
-  if constexpr (LOWER && TIn::kBytes == 2) {
-    // symmetric products with too few tiles to fill the chip split K when the caller
-    // provides the split-K workspace (and it is large enough)
-    const SymmPlan pl = plan_symm(p.M, p.K, batch, p.partial != nullptr && p.counters != nullptr);
-    if (pl.splits > 1 && pl.partial_floats <= p.partial_cap && pl.counters <= p.counter_cap) {
-      cfg = static_cast<TileCfg>(pl.cfg);
-      p.splits = pl.splits;
-      p.kt_per_split = pl.kt_per_split;
-    }
-  }
   switch (cfg) {
     case TileCfg::kBig:
       return launch_one<TIn, TB, TOut, 256, 256, GNS_BIG_WM, GNS_BIG_WN, GNS_STAGES_BIG, GNS_BK_BIG, LOWER, NN>(

@@ -47,8 +47,6 @@ struct NsLayout {
   float* partials;
   void *R, *Z, *Y, *Q0, *Q1, *Xa, *Xb;   // Gram NS
   void *A, *Bm, *Sa, *Sb;                // standard NS (overlaps the Gram region)
-  unsigned* counters; int counter_cap;   // split-K arrival counters (zeroed by the call's first kernel)
-  float* splitk; size_t splitk_cap;      // split-K fp32 partial tiles
   size_t bytes;
 };
 
@@ -65,22 +63,7 @@ NsLayout ns_layout(void* base, int batch, int n, int m, gns_dtype cdt) {
   const size_t gram_end = c.off;
   c.off = common;
   L.A = c.take(nn); L.Bm = c.take(nn); L.Sa = c.take(nm); L.Sb = c.take(nm);
-  c.off = std::max(gram_end, c.off);
-  // split K for the symmetric products of the call: K = n and K = m
-  size_t cap = 0;
-  int ctr = 0;
-  if (cdt != GNS_F32) {
-    for (int K : {n, m}) {
-      const SymmPlan pl = plan_symm(n, K, batch, true);
-      cap = std::max(cap, pl.partial_floats);
-      ctr = std::max(ctr, pl.counters);
-    }
-  }
-  L.counter_cap = ctr;
-  L.counters = ctr ? (unsigned*)c.take(sizeof(unsigned) * (size_t)ctr) : nullptr;
-  L.splitk_cap = cap;
-  L.splitk = cap ? (float*)c.take(sizeof(float) * cap) : nullptr;
-  L.bytes = c.off;
+  L.bytes = std::max(gram_end, c.off);
   return L;
 }
 
@@ -157,11 +140,9 @@ int hip_fail(hipError_t e, const char* what) {
   } while (0)
 
 // Symmetric product on n x n (or the Gram product with K = m) for the whole batch.
-GemmParams symm_params(const NsLayout& L, int n, int K, const void* A, long long lda, long long sA, const void* B,
-                       long long ldb, long long sB, void* D, long long ldd, long long sD) {
+GemmParams symm_params(int n, int K, const void* A, long long lda, long long sA, const void* B, long long ldb,
+                       long long sB, void* D, long long ldd, long long sD) {
   GemmParams g;
-  g.partial = L.splitk; g.partial_cap = L.splitk_cap;
-  g.counters = L.counters; g.counter_cap = L.counter_cap;
   g.M = g.N = n;
   g.K = K;
   g.A = A; g.lda = lda; g.sA = sA;
@@ -179,13 +160,11 @@ int run_gram(const NsCall& c) {
   const float P = pow2_scale(c.cdt, n, m);
   const gns_dtype cdt = c.cdt;
   const float* s = c.s_given ? c.s_given : L.s;
-  if (!c.s_given)
-    HIP_OK(launch_frob(c.X, c.xdt, c.ldx, c.sx, B, n, m, c.sch.eps, L.s, L.partials, c.stream, L.counters,
-                       L.counter_cap));
+  if (!c.s_given) HIP_OK(launch_frob(c.X, c.xdt, c.ldx, c.sx, B, n, m, c.sch.eps, L.s, L.partials, c.stream));
 
   // R0 = s^2 X X^T: operands in X's dtype, result in the iterate dtype
   {
-    GemmParams g = symm_params(L, n, m, c.X, c.ldx, c.sx, c.X, c.ldx, c.sx, L.R, n, nn);
+    GemmParams g = symm_params(n, m, c.X, c.ldx, c.sx, c.X, c.ldx, c.sx, L.R, n, nn);
     g.scale = s; g.alpha_pow = 2;
     HIP_OK(launch_symm(c.xdt, cdt, g, B, c.stream, c.flops));
   }
@@ -223,19 +202,19 @@ int run_gram(const NsCall& c) {
       int st = apply_q(xn, cdt, m, nm, false);
       if (st) return st;
       cx = xn; cxdt = cdt; cld = m; csx = nm; cx_orig = false;
-      GemmParams g = symm_params(L, n, m, cx, m, nm, cx, m, nm, L.R, n, nn);
+      GemmParams g = symm_params(n, m, cx, m, nm, cx, m, nm, L.R, n, nn);
       g.alpha = 1.0f / (P * P);
       HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
       q_identity = true;
     }
     {  // Z = c R R + b R   (and Q = Z + a I while Q is the identity)
-      GemmParams g = symm_params(L, n, n, L.R, n, nn, L.R, n, nn, L.Z, n, nn);
+      GemmParams g = symm_params(n, n, L.R, n, nn, L.R, n, nn, L.Z, n, nn);
       g.alpha = cc; g.beta = b; g.C = L.R; g.ldc = n; g.sC = nn;
       if (q_identity) { g.D2 = Q; g.ldd2 = n; g.sD2 = nn; g.delta = a; }
       HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
     }
     if (!q_identity) {  // Q <- Q Z + a Q
-      GemmParams g = symm_params(L, n, n, Q, n, nn, L.Z, n, nn, Qn, n, nn);
+      GemmParams g = symm_params(n, n, Q, n, nn, L.Z, n, nn, Qn, n, nn);
       g.beta = a; g.C = Q; g.ldc = n; g.sC = nn;
       HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
       std::swap(Q, Qn);
@@ -243,10 +222,10 @@ int run_gram(const NsCall& c) {
     q_identity = false;
     const bool need_r = t < c.sch.steps && !restart_before(t + 1);
     if (need_r) {
-      GemmParams g1 = symm_params(L, n, n, L.R, n, nn, L.Z, n, nn, L.Y, n, nn);    // Y = R Z + a R
+      GemmParams g1 = symm_params(n, n, L.R, n, nn, L.Z, n, nn, L.Y, n, nn);    // Y = R Z + a R
       g1.beta = a; g1.C = L.R; g1.ldc = n; g1.sC = nn;
       HIP_OK(launch_symm(cdt, cdt, g1, B, c.stream, c.flops));
-      GemmParams g2 = symm_params(L, n, n, L.Z, n, nn, L.Y, n, nn, L.R, n, nn);    // R = Z Y + a Y
+      GemmParams g2 = symm_params(n, n, L.Z, n, nn, L.Y, n, nn, L.R, n, nn);    // R = Z Y + a Y
       g2.beta = a; g2.C = L.Y; g2.ldc = n; g2.sC = nn;
       HIP_OK(launch_symm(cdt, cdt, g2, B, c.stream, c.flops));
     }
@@ -262,17 +241,15 @@ int run_standard(const NsCall& c) {
   const long long nn = (long long)n * n, nm = (long long)n * m;
   const float P = pow2_scale(c.cdt, n, m);
   const float* s = c.s_given ? c.s_given : L.s;
-  if (!c.s_given)
-    HIP_OK(launch_frob(c.X, c.xdt, c.ldx, c.sx, B, n, m, c.sch.eps, L.s, L.partials, c.stream, L.counters,
-                       L.counter_cap));
+  if (!c.s_given) HIP_OK(launch_frob(c.X, c.xdt, c.ldx, c.sx, B, n, m, c.sch.eps, L.s, L.partials, c.stream));
   HIP_OK(launch_cast_scale(c.X, c.xdt, c.ldx, c.sx, L.Sa, c.cdt, m, nm, B, n, m, P, s, 1, c.stream));
   void* cur = L.Sa; void* nxt = L.Sb;
   for (int t = 1; t <= c.sch.steps; ++t) {
     const float a = c.sch.a[t - 1], b = c.sch.b[t - 1], cc = c.sch.c[t - 1];
-    GemmParams g1 = symm_params(L, n, m, cur, m, nm, cur, m, nm, L.A, n, nn);
+    GemmParams g1 = symm_params(n, m, cur, m, nm, cur, m, nm, L.A, n, nn);
     g1.alpha = 1.0f / (P * P);
     HIP_OK(launch_symm(c.cdt, c.cdt, g1, B, c.stream, c.flops));
-    GemmParams g2 = symm_params(L, n, n, L.A, n, nn, L.A, n, nn, L.Bm, n, nn);
+    GemmParams g2 = symm_params(n, n, L.A, n, nn, L.A, n, nn, L.Bm, n, nn);
     g2.alpha = cc; g2.beta = b; g2.C = L.A; g2.ldc = n; g2.sC = nn;
     HIP_OK(launch_symm(c.cdt, c.cdt, g2, B, c.stream, c.flops));
     GemmParams g3;
@@ -406,8 +383,7 @@ int symm_gemm(int batch, int n, int k, float alpha, const void* A, long long lda
   if (n % 8 || k % q || lda % q || ldb % q || ldd % qo || (C && ldc % qo)) return GNS_ERR_UNSUPPORTED;
   if (batch > 1 && (stride_a % q || stride_b % q || stride_d % qo || (C && stride_c % qo))) return GNS_ERR_UNSUPPORTED;
   if (!aligned16(B) || (C && !aligned16(C))) return GNS_ERR_UNSUPPORTED;
-  const NsLayout no_split{};            // no workspace here: symm_gemm never splits K
-  GemmParams g = symm_params(no_split, n, k, A, lda, stride_a, B, ldb, stride_b, D, ldd, stride_d);
+  GemmParams g = symm_params(n, k, A, lda, stride_a, B, ldb, stride_b, D, ldd, stride_d);
   g.alpha = alpha; g.beta = beta; g.gamma = gamma;
   if (C && beta != 0.0f) { g.C = C; g.ldc = ldc; g.sC = stride_c; }
   HIP_OK(launch_symm(in_dtype, out_dtype, g, batch, stream, nullptr));
@@ -537,8 +513,7 @@ int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int 
   HIP_OK(launch_accumulate_score((uint16_t*)M, (const uint16_t*)G, N, m, ld, score_norm, L.score, L.sumsq, stream));
   HIP_OK(launch_topk(L.score, N, k, S_out, stream));
   HIP_OK(launch_gather_feedback((uint16_t*)M, N, m, ld, S_out, k, mu, (uint16_t*)L.X, m, stream));
-  const NsLayout G_L = ns_layout(L.gns_ws, 1, k, m, compute);   // its split-K counters start at zero here
-  HIP_OK(launch_selected_sumsq(L.sumsq, S_out, k, N, sch.eps, L.s, stream, G_L.counters, G_L.counter_cap));
+  HIP_OK(launch_selected_sumsq(L.sumsq, S_out, k, N, sch.eps, L.s, stream));
   void* O = O_out ? O_out : L.O;
   NsCall c = make_call(L.X, GNS_BF16, m, (long long)k * m, O, GNS_BF16, m, (long long)k * m, 1, k, m, compute, &sch,
                        L.gns_ws, L.gns_bytes, stream, nullptr);

@@ -24,24 +24,8 @@ struct GemmParams {
   const float* scale = nullptr; int alpha_pow = 0;
   float b_mul = 1.f; int b_pow = 0;
   int tiles_m = 0, tiles_n = 0;   // set by the launcher
-  int batch = 0, tiles = 0;       // set by the launcher: grid = batch * tiles * splits workgroups
-  // Split-K workspace of symmetric products (nullable = never split): fp32 partial
-  // tiles (partial_cap floats) and one arrival counter per output tile (counter_cap
-  // of them), which must be zero before the launch; a split launch leaves them zero.
-  float* partial = nullptr; size_t partial_cap = 0;
-  unsigned* counters = nullptr; int counter_cap = 0;
-  int splits = 1, kt_per_split = 0;   // set by the launcher
+  int batch = 0, tiles = 0;       // set by the launcher: grid = batch * tiles workgroups
 };
-
-// Split-K plan of a symmetric product (tile configuration and number of K ranges)
-// and the workspace it needs; the launcher follows the same plan.
-struct SymmPlan {
-  int cfg = 2, splits = 1, kt_per_split = 0;
-  long long tiles = 0;       // output tiles per matrix
-  size_t partial_floats = 0;
-  int counters = 0;
-};
-SymmPlan plan_symm(int n, int K, int batch, bool may_split);
 
 // flops (nullable): incremented by the MFMA flops the launch issues.
 hipError_t launch_symm(gns_dtype in, gns_dtype out, const GemmParams& p, int batch,
@@ -52,10 +36,8 @@ bool rect_pair_supported(gns_dtype a, gns_dtype b);
 
 // Frobenius scale: partial sums of squares, then s[b] = mul / (sqrt(sum) + eps).
 int frob_partials_per_batch(int n, int m);
-// zero (nullable): nzero split-K arrival counters this launch sets to zero on the way.
 hipError_t launch_frob(const void* X, gns_dtype dt, long long ldx, long long stride_x, int batch,
-                       int n, int m, float eps, float* s_out, float* partials, hipStream_t stream,
-                       unsigned* zero = nullptr, int nzero = 0);
+                       int n, int m, float eps, float* s_out, float* partials, hipStream_t stream);
 // Y = cast(mul * scale[b]^pow * X) elementwise, for batch x n x m matrices.
 hipError_t launch_cast_scale(const void* X, gns_dtype xdt, long long ldx, long long sx, void* Y,
                              gns_dtype ydt, long long ldy, long long sy, int batch, int n, int m,
@@ -72,6 +54,6 @@ hipError_t launch_apply_update(uint16_t* W, int N, int m, long long ld, const in
                                hipStream_t s);
 // s[0] = 1 / (sqrt(sum_i sumsq[S[i]]) + eps): the Frobenius scale of the rows S.
 hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int k, int N, float eps,
-                                 float* s_out, hipStream_t s, unsigned* zero = nullptr, int nzero = 0);
+                                 float* s_out, hipStream_t s);
 
 }  // namespace gns

@@ -116,14 +116,9 @@ def test_zero_input_gives_zero(gns_mod):
         assert np.all(got == 0.0)
 
 
-@pytest.mark.parametrize("n,m", [(256, 2048), (1024, 4096)])
-def test_batch_independence_and_determinism(gns_mod, n, m):
-    """Bitwise: repeated calls agree, and a matrix's result does not depend on its
-    position in the batch.  Across batch sizes the symmetric products may cut K into
-    a different number of ranges (the split depends on the total tile count), which
-    changes the fp32 summation order only: there the bar is a rounding-level one."""
-    announce(f"gns batch independence n={n} m={m}")
-    st = synth.gns_batch("gns_128x768x6144_bf16", batch=2, n=n, m=m)
+def test_batch_independence_and_determinism(gns_mod):
+    announce("gns batch independence")
+    st = synth.gns_batch("gns_128x768x6144_bf16", batch=2, n=256, m=2048)
     rep = np.stack([st[0], st[1], st[0], st[0]])
     X = to_dev(rep, "bf16")
     o1 = bits(gns_mod.orthogonalize(X))
@@ -131,10 +126,7 @@ def test_batch_independence_and_determinism(gns_mod, n, m):
     assert np.array_equal(o1, o2)                       # deterministic
     assert np.array_equal(o1[0], o1[2]) and np.array_equal(o1[0], o1[3])   # position-independent
     single = bits(gns_mod.orthogonalize(to_dev(st[1:2], "bf16")))
-    again = bits(gns_mod.orthogonalize(to_dev(st[1:2], "bf16")))
-    assert np.array_equal(single, again)
-    a, b = decode(single[0], "bf16"), decode(o1[1], "bf16")
-    assert rel_fro(a, b) <= 5e-3
+    assert np.array_equal(single[0], o1[1])
 
 
 def test_issued_flops_reported(gns_mod):
