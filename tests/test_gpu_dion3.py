@@ -110,6 +110,20 @@ def test_dion3_step_small(gns_mod, norm, wd):
     assert np.array_equal(wg[rest], w_ref[rest])     # unselected rows do not depend on O
 
 
+def test_dion3_step_repeatable(gns_mod):
+    """The same step from the same state gives the same bits (S, O, W, M), ten times."""
+    announce("dion3 step repeatable 1024x4096")
+    w, g, m = synth.dion3_state(n=1024, m=4096, seed=15)
+    k = k_from_fraction(0.25, 1024)
+    runs = []
+    for _ in range(10):
+        W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+        S, O = gns_mod.dion3_step(W, M, G, k, 0.02, weight_decay=0.1, mu=0.95, score_norm=2, return_O=True)
+        runs.append((S.cpu().numpy(), bits(O), bits(W), bits(M)))
+    for r in runs[1:]:
+        assert all(np.array_equal(a, b) for a, b in zip(r, runs[0]))
+
+
 @pytest.mark.timeout(900)
 def test_dion3_step_full_size(gns_mod):
     """The 8192 x 28672 workload at f = 1/4 and 1/8 with l2 row scores."""
