@@ -17,6 +17,8 @@
 // operands (16x16x4 MFMA, register-staged double buffer).  Each wave owns a WM x WN
 // sub-tile of MFMA fragments accumulated in fp32.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -816,49 +818,95 @@ gemm16_kernel(GemmParams p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int KT = (K + BK - 1) / BK;
-  constexpr int H = (FM + 1) / 2;     // fragment rows of the last k-step before / after the barrier
-  constexpr int L = (KS - 1) & 1;     // fragment set of the last k-step
-  static_assert(L == 1, "the last k-step's fragments must not sit in set 0");
-  constexpr int TAIL = (FM - H) * FN; // MFMAs after the barrier
-  constexpr int PER = TAIL > 0 ? (LOADS + TAIL - 1) / TAIL : LOADS;
-  uint4 fa[2][FM], fb[2][FN];         // two fragment sets: k-step s in set s & 1
-  // Stages at or past KT are issued like the others: all their offsets are out of
-  // range, so they only write zeros into ring slots whose data is never used, and
-  // every iteration runs the same code (NS - 1 younger stages in flight at each wait).
+  // Small wave tiles (few MFMAs per k-step) keep a whole stage of fragments in
+  // registers, twice: the LDS reads of stage kt+1 then overlap all MFMAs of stage
+  // kt instead of one k-step, which is what bounds them otherwise (one 32-cycle
+  // MFMA per k-step against ~130 cycles of LDS latency).
+  constexpr bool kStageFrags = 2 * KS * (FM + FN) * 4 <= 128;
+  if constexpr (!kStageFrags) {
+    constexpr int H = (FM + 1) / 2;     // fragment rows of the last k-step before / after the barrier
+    constexpr int L = (KS - 1) & 1;     // fragment set of the last k-step
+    static_assert(L == 1, "the last k-step's fragments must not sit in set 0");
+    constexpr int TAIL = (FM - H) * FN; // MFMAs after the barrier
+    constexpr int PER = TAIL > 0 ? (LOADS + TAIL - 1) / TAIL : LOADS;
+    uint4 fa[2][FM], fb[2][FN];         // two fragment sets: k-step s in set s & 1
+    // Stages at or past KT are issued like the others: all their offsets are out of
+    // range, so they only write zeros into ring slots whose data is never used, and
+    // every iteration runs the same code (NS - 1 younger stages in flight at each wait).
 #pragma unroll
-  for (int t = 0; t < NS; ++t) issue_stage(t);
-  wait_for_stage(0, NS - 1);
-  lds_barrier();
-  read_frags(0, 0, fa[0], fb[0]);
-
-  // Stage kt (ring slot kt % NS) holds its k-step 0 fragments in set 0 on entry:
-  //   k-steps 0 .. KS-2: read the fragments of the next k-step, MFMAs of this one;
-  //   last k-step: MFMAs of its first fragment rows; all LDS reads of this stage are
-  //   now in registers (lgkmcnt 0); wait for stage kt+1; barrier -- stage kt+1 is
-  //   visible and slot kt % NS is free in every wave; read k-step 0 of stage kt+1;
-  //   the remaining MFMAs, with the loads of stage kt+NS (into the freed slot)
-  //   issued between them so the MFMA pipe stays busy meanwhile.
-  for (int kt = 0; kt < KT; ++kt) {
-    const int slot = kt % NS;
-#pragma unroll
-    for (int ks = 0; ks + 1 < KS; ++ks) {
-      read_frags(slot, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-      mma(acc, fa[ks & 1], fb[ks & 1], 0, FM);
-    }
-    mma(acc, fa[L], fb[L], 0, H);
-    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
-    wait_for_stage(kt + 1, kt + NS - 1);
+    for (int t = 0; t < NS; ++t) issue_stage(t);
+    wait_for_stage(0, NS - 1);
     lds_barrier();
-    read_frags((kt + 1) % NS, 0, fa[0], fb[0]);
+    read_frags(0, 0, fa[0], fb[0]);
+
+    // Stage kt (ring slot kt % NS) holds its k-step 0 fragments in set 0 on entry:
+    //   k-steps 0 .. KS-2: read the fragments of the next k-step, MFMAs of this one;
+    //   last k-step: MFMAs of its first fragment rows; all LDS reads of this stage are
+    //   now in registers (lgkmcnt 0); wait for stage kt+1; barrier -- stage kt+1 is
+    //   visible and slot kt % NS is free in every wave; read k-step 0 of stage kt+1;
+    //   the remaining MFMAs, with the loads of stage kt+NS (into the freed slot)
+    //   issued between them so the MFMA pipe stays busy meanwhile.
+    for (int kt = 0; kt < KT; ++kt) {
+      const int slot = kt % NS;
 #pragma unroll
-    for (int t = 0; t < (TAIL > 0 ? TAIL : 1); ++t) {
-      if constexpr (TAIL > 0) {
-        const int i = H + t / FN, j = t % FN;
-        mfma32_step<TIn>(acc[i][j], fa[L][i], fb[L][j]);
+      for (int ks = 0; ks + 1 < KS; ++ks) {
+        read_frags(slot, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        mma(acc, fa[ks & 1], fb[ks & 1], 0, FM);
       }
+      mma(acc, fa[L], fb[L], 0, H);
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      wait_for_stage(kt + 1, kt + NS - 1);
+      lds_barrier();
+      read_frags((kt + 1) % NS, 0, fa[0], fb[0]);
 #pragma unroll
-      for (int r = 0; r < PER; ++r)
-        if (t * PER + r < LOADS) issue_load(kt + NS, t * PER + r);
+      for (int t = 0; t < (TAIL > 0 ? TAIL : 1); ++t) {
+        if constexpr (TAIL > 0) {
+          const int i = H + t / FN, j = t % FN;
+          mfma32_step<TIn>(acc[i][j], fa[L][i], fb[L][j]);
+        }
+#pragma unroll
+        for (int r = 0; r < PER; ++r)
+          if (t * PER + r < LOADS) issue_load(kt + NS, t * PER + r);
+      }
+    }
+  } else {
+    uint4 sa[2][KS][FM], sb[2][KS][FN];
+    auto read_stage = [&](int slot, uint4 (&fa)[KS][FM], uint4 (&fb)[KS][FN]) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) read_frags(slot, ks, fa[ks], fb[ks]);
+    };
+    constexpr int MMAS = KS * FM * FN;
+    constexpr int PER2 = (LOADS + MMAS - 1) / MMAS;
+    // One stage: its fragments are in set S; make stage kt+1 visible (its slot was
+    // filled NS-1 stages ago) and free slot kt % NS (every wave has its stage-kt
+    // fragments in registers); read stage kt+1 into set S^1; the MFMAs of stage kt
+    // with the loads of stage kt+NS into the freed slot issued between them.
+    auto stage_iter = [&](auto set_tag, int kt) {
+      constexpr int S = decltype(set_tag)::value;
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      wait_for_stage(kt + 1, kt + NS - 1);
+      lds_barrier();
+      read_stage((kt + 1) % NS, sa[S ^ 1], sb[S ^ 1]);
+#pragma unroll
+      for (int t = 0; t < MMAS; ++t) {
+        const int ks = t / (FM * FN), i = (t / FN) % FM, j = t % FN;
+        mfma32_step<TIn>(acc[i][j], sa[S][ks][i], sb[S][ks][j]);
+#pragma unroll
+        for (int r = 0; r < PER2; ++r)
+          if (t * PER2 + r < LOADS) issue_load(kt + NS, t * PER2 + r);
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < NS; ++t) issue_stage(t);
+    wait_for_stage(0, NS - 1);
+    lds_barrier();
+    read_stage(0, sa[0], sb[0]);
+    // pairs of stages keep the register sets compile-time; with KT odd the last pair
+    // runs one stage past the end, whose loads were all out of range: its fragments
+    // are zeros and its MFMAs add exact zeros
+    for (int kt = 0; kt < KT; kt += 2) {
+      stage_iter(std::integral_constant<int, 0>{}, kt);
+      stage_iter(std::integral_constant<int, 1>{}, kt + 1);
     }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the trailing out-of-range loads have written their zeros
