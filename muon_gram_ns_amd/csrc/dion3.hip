@@ -32,6 +32,34 @@ __device__ __forceinline__ double block_sum_f64(double v, double* sh) {
 }
 
 // ---- M <- bf16(M + G); per-row score and sum of squares ---------------------------
+// One workgroup per row.  Each thread takes chunks c, c+256, c+512, ... of 8 values;
+// four chunks' loads are issued before any is used (more bytes in flight per wave),
+// and the chunks are then summed in that same order, so each thread's fp64 sums do
+// not depend on the unrolling.
+constexpr int kAccUnroll = 4;
+
+__device__ __forceinline__ uint4 accumulate_chunk(uint4 mv, const uint4& gv, int score_norm, double& acc_s,
+                                                  double& acc_q) {
+  uint32_t* mw = reinterpret_cast<uint32_t*>(&mv);
+  const uint32_t* gw = reinterpret_cast<const uint32_t*>(&gv);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float a = bf16_bits_to_f32((mw[i] >> (16 * h)) & 0xffffu);
+      const float g = bf16_bits_to_f32((gw[i] >> (16 * h)) & 0xffffu);
+      const uint32_t nb = f32_to_bf16_bits(__fadd_rn(a, g));
+      out |= nb << (16 * h);
+      const double v = (double)bf16_bits_to_f32(nb);
+      acc_s += (score_norm == 1) ? fabs(v) : v * v;
+      acc_q += v * v;
+    }
+    mw[i] = out;
+  }
+  return mv;
+}
+
 __global__ void __launch_bounds__(kRowThreads)
 accumulate_score_kernel(uint16_t* M, const uint16_t* G, int m, long long ld, int score_norm,
                         double* score, double* sumsq) {
@@ -39,28 +67,23 @@ accumulate_score_kernel(uint16_t* M, const uint16_t* G, int m, long long ld, int
   const int r = blockIdx.x;
   uint4* mr = reinterpret_cast<uint4*>(M + (size_t)r * ld);
   const uint4* gr = reinterpret_cast<const uint4*>(G + (size_t)r * ld);
+  const int nch = m / 8;
   double acc_s = 0.0, acc_q = 0.0;
-  for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
-    uint4 mv = mr[c];
-    const uint4 gv = gr[c];
-    uint32_t* mw = reinterpret_cast<uint32_t*>(&mv);
-    const uint32_t* gw = reinterpret_cast<const uint32_t*>(&gv);
+  for (int c0 = threadIdx.x; c0 < nch; c0 += kAccUnroll * kRowThreads) {
+    uint4 mv[kAccUnroll], gv[kAccUnroll];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t out = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float a = bf16_bits_to_f32((mw[i] >> (16 * h)) & 0xffffu);
-        const float g = bf16_bits_to_f32((gw[i] >> (16 * h)) & 0xffffu);
-        const uint32_t nb = f32_to_bf16_bits(__fadd_rn(a, g));
-        out |= nb << (16 * h);
-        const double v = (double)bf16_bits_to_f32(nb);
-        acc_s += (score_norm == 1) ? fabs(v) : v * v;
-        acc_q += v * v;
+    for (int u = 0; u < kAccUnroll; ++u) {
+      const int c = c0 + u * kRowThreads;
+      if (c < nch) {
+        mv[u] = mr[c];
+        gv[u] = gr[c];
       }
-      mw[i] = out;
     }
-    mr[c] = mv;
+#pragma unroll
+    for (int u = 0; u < kAccUnroll; ++u) {
+      const int c = c0 + u * kRowThreads;
+      if (c < nch) mr[c] = accumulate_chunk(mv[u], gv[u], score_norm, acc_s, acc_q);
+    }
   }
   const double ts = block_sum_f64(acc_s, sh);
   const double tq = block_sum_f64(acc_q, sh);
@@ -106,13 +129,24 @@ __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* sh, un
   return sh[w] + x - v;
 }
 
+// Keys are staged in LDS when they fit (N <= kTopkLdsKeys), else read from memory.
+// The bin holding the k-th largest key is found by one wave: each lane holds 4
+// bins (from the top), a prefix sum over lanes finds the crossing lane.
+constexpr int kTopkLdsKeys = 12288;
+
 __global__ void __launch_bounds__(kTopkThreads)
 topk_kernel(const double* score, int N, int k, int* S) {
   __shared__ unsigned hist[256];
   __shared__ unsigned scan_sh[kTopkThreads / 64 + 1];
   __shared__ unsigned long long sh_prefix;
   __shared__ unsigned sh_krem;
-  const unsigned long long* key = reinterpret_cast<const unsigned long long*>(score);
+  __shared__ unsigned long long keys_lds[kTopkLdsKeys];
+  const unsigned long long* gkey = reinterpret_cast<const unsigned long long*>(score);
+  const bool in_lds = N <= kTopkLdsKeys;
+  if (in_lds)
+    for (int i = threadIdx.x; i < N; i += kTopkThreads) keys_lds[i] = gkey[i];
+  const unsigned long long* key = in_lds ? keys_lds : gkey;
+  __syncthreads();
   unsigned long long prefix = 0, mask = 0;
   unsigned krem = (unsigned)k;
   for (int d = 7; d >= 0; --d) {
@@ -124,15 +158,39 @@ topk_kernel(const double* score, int N, int k, int* S) {
       if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      unsigned above = 0;
-      int bin = 255;
-      for (; bin > 0; --bin) {
-        if (above + hist[bin] >= krem) break;
-        above += hist[bin];
+    if (threadIdx.x < 64) {
+      // lane l holds bins 255-4l .. 252-4l; counts above a lane's bins by prefix sum
+      const int lane = threadIdx.x;
+      unsigned c[4], local = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[q] = hist[255 - 4 * lane - q];
+        local += c[q];
       }
-      sh_prefix = prefix | ((unsigned long long)bin << shift);
-      sh_krem = krem - above;
+      unsigned incl = local;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const unsigned excl = incl - local;
+      // the crossing lane: the k-th largest candidate lies in one of its bins
+      // (the last lane always crosses: krem never exceeds the candidate count)
+      if (excl < krem && (krem <= incl || lane == 63)) {
+        unsigned above = excl;
+        int bin = 255 - 4 * lane - 3;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int b = 255 - 4 * lane - q;
+          if (above + c[q] >= krem || b == 0) {
+            bin = b;
+            break;
+          }
+          above += c[q];
+        }
+        sh_prefix = prefix | ((unsigned long long)bin << shift);
+        sh_krem = krem - above;
+      }
     }
     __syncthreads();
     prefix = sh_prefix;
