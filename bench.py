@@ -302,6 +302,14 @@ def bench_dion3(args, w):
     t_gat = timed(lambda: gns.dion3_gather_feedback(M, S, 0.95), reps)
     t_upd = timed(lambda: gns.dion3_apply_update(W, S, X, 0.02, 0.0), reps)
     b_acc, b_gat, b_upd = 3.0 * N * m * 2, 3.0 * k * m * 2, 3.0 * k * m * 2
+    # what the memory system sustains for the same traffic patterns, with torch's own
+    # kernels on the same tensors: an in-place add (read 2, write 1) and a copy
+    t_add = timed(lambda: M.add_(G), reps)
+    scratch = torch.empty_like(M)
+    t_cpy = timed(lambda: scratch.copy_(M), reps)
+    reference = {"torch_add_inplace_GB_s": round(b_acc / t_add / 1e9, 1),
+                 "torch_copy_GB_s": round(2.0 * N * m * 2 / t_cpy / 1e9, 1)}
+    del scratch
     pieces = {"accumulate_score": {"us": round(t_acc * 1e6, 2), "bytes": b_acc, "GB_s": round(b_acc / t_acc / 1e9, 1)},
               "select_topk": {"us": round(t_sel * 1e6, 2)},
               "gather_feedback": {"us": round(t_gat * 1e6, 2), "bytes": b_gat, "GB_s": round(b_gat / t_gat / 1e9, 1)},
@@ -315,7 +323,8 @@ def bench_dion3(args, w):
                       "scaling": "weak", "vs_baseline": None, "dtype": args.compute, "data": "synthetic",
                       "config": {"workload": w.name, "N": N, "m": m, "score": "l2", "mu": 0.95, "wd": 0.0,
                                  "fractions": res},
-                      "hbm_pieces_k2048": pieces, "roofline": roof, "cpu_baseline": None}), flush=True)
+                      "hbm_pieces_k2048": pieces, "hbm_reference_same_tensors": reference,
+                      "roofline": roof, "cpu_baseline": None}), flush=True)
 
 
 if __name__ == "__main__":
