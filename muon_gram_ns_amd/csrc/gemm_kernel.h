@@ -123,11 +123,24 @@ __device__ __forceinline__ uint4 convert_chunk(uint4 c, float mul) {
   } else {
     static_assert(TIn::kBytes == 2 && TB::kBytes == 2, "only 16-bit conversions");
     uint32_t* w = reinterpret_cast<uint32_t*>(&c);
+    if constexpr (TIn::kId == GNS_F16 && TB::kId == GNS_BF16) {
+      // bf16 -> fp32 is a bit shift (low half) or a mask (high half); the product with
+      // mul is rounded to fp16 straight into the low / high half of one register
+      typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo = TIn::from_f32(TB::to_f32(w[i] & 0xffffu) * mul);
-      uint32_t hi = TIn::from_f32(TB::to_f32(w[i] >> 16) * mul);
-      w[i] = lo | (hi << 16);
+      for (int i = 0; i < 4; ++i) {
+        half2_t h;
+        h.x = (_Float16)(__uint_as_float(w[i] << 16) * mul);
+        h.y = (_Float16)(__uint_as_float(w[i] & 0xffff0000u) * mul);
+        w[i] = __builtin_bit_cast(uint32_t, h);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t lo = TIn::from_f32(TB::to_f32(w[i] & 0xffffu) * mul);
+        uint32_t hi = TIn::from_f32(TB::to_f32(w[i] >> 16) * mul);
+        w[i] = lo | (hi << 16);
+      }
     }
     return c;
   }
