@@ -536,7 +536,7 @@ struct Tile32 {
   static constexpr int kFM = kWM / 32;
   static constexpr int kFN = kWN / 32;
   static constexpr int kStages = STAGES;      // LDS ring depth
-  static constexpr int kBK = BK;              // k values per stage (32: 64-byte rows, 64: 128-byte rows)
+  static constexpr int kBK = BK;              // k values per stage (rows of BK * 2 bytes)
   static constexpr int kLdsBytes = kStages * (BM + BN) * kBK * 2;
 };
 
@@ -545,11 +545,14 @@ struct Tile32 {
 // and sit in different quarters; j selects the chunk within the quarter).
 __device__ __forceinline__ int swz64(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
-// physical chunk of logical chunk c in row r of a K-contiguous tile with BK values per row
+// physical chunk of logical chunk c in row r of a K-contiguous tile with BK values per
+// row.  With 256-byte rows (BK = 128) a row fills the whole bank window, so the 16
+// rows of a fragment read take slots c ^ (r mod 16): 16 distinct 16-byte slots.
 template <int BK>
 __device__ __forceinline__ int swz_k(int row, int chunk) {
   if constexpr (BK == 32) return swz64(row, chunk);
-  else return swz(row, chunk);
+  else if constexpr (BK == 64) return swz(row, chunk);
+  else return chunk ^ (row & 15);
 }
 
 // 16 bytes of TOut elements <-> fp32 values
@@ -704,7 +707,7 @@ gemm16_kernel(GemmParams p) {
   constexpr int NCH = BN / 8;                                                        // NN: chunks per k row
   constexpr int CPR = BK / 8;                                                        // NT: chunks per tile row
   constexpr int KS = BK / 16;                                                        // MFMA k-steps per stage
-  static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(BK == 32 || BK == 64 || BK == 128, "stage depth");
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "tile/wave mismatch");
   static_assert(!NN || NCH >= 8, "NN tiles need >= 64 columns");
   static_assert(NS >= 2 && LOADS * (NS - 1) < 64, "ring depth / vmcnt range");
@@ -979,11 +982,21 @@ inline bool operand_extents_ok(const GemmParams& p, int a_bytes, int b_bytes, bo
   return a < lim && b < lim;
 }
 
-// Pick the largest tile that still gives every CU at least one workgroup.
-inline TileCfg pick_tile(int M, int N, int batch, bool lower) {
+// Pick the largest tile that still gives every CU at least one workgroup.  One
+// exception, for long K: when 64 x 64 tiles would need several rounds of workgroups
+// while 128 x 128 tiles fit in one, the larger tile wins (each of its k-stages costs
+// about twice a small tile's for four times the flops; measured on MI355X, the
+// n = 2048, K = 28672 Gram product takes 181 us on 128 x 128 tiles, one round of 136
+// workgroups, against 248 us on 64 x 64 tiles, three rounds of 528).
+inline TileCfg pick_tile(int M, int N, int K, int batch, bool lower) {
   constexpr long long kCUs = 256;
-  if ((long long)batch * gemm_tiles(M, N, 256, 256, lower) >= kCUs) return TileCfg::kBig;
-  if ((long long)batch * gemm_tiles(M, N, 128, 128, lower) >= kCUs) return TileCfg::kMid;
+  constexpr int kLongK = 64 * 64;       // 64 stages of 64 k values
+  const long long big = (long long)batch * gemm_tiles(M, N, 256, 256, lower);
+  const long long mid = (long long)batch * gemm_tiles(M, N, 128, 128, lower);
+  const long long small = (long long)batch * gemm_tiles(M, N, 64, 64, lower);
+  if (big >= kCUs) return TileCfg::kBig;
+  if (mid >= kCUs) return TileCfg::kMid;
+  if (K >= kLongK && small > kCUs) return TileCfg::kMid;
   return TileCfg::kSmall;
 }
 
@@ -1022,7 +1035,7 @@ hipError_t launch_cfg(GemmParams p, int batch, hipStream_t stream, double* flops
 #ifdef GNS_FORCE_TILE
   const TileCfg cfg = static_cast<TileCfg>(GNS_FORCE_TILE);
 #else
-  const TileCfg cfg = pick_tile(p.M, p.N, batch, LOWER);
+  const TileCfg cfg = pick_tile(p.M, p.N, p.K, batch, LOWER);
 #endif
   switch (cfg) {
     case TileCfg::kBig:
