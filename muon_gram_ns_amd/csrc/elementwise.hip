@@ -9,8 +9,9 @@
 //
 // Reduction: each workgroup sums squares of a band of rows in fp32 (16-byte loads,
 // grid-stride over the band), reduces across the workgroup in a fixed order and
-// writes one partial; a second kernel adds a batch's partials in index order.  No
-// atomics, so the result is bitwise reproducible.
+// writes one partial; a second kernel (or, in Gram NS, the first Gram product's
+// epilogue) adds a batch's partials in a fixed order.  No atomics, so the result is
+// bitwise reproducible.
 #include "common.h"
 #include "internal.h"
 
@@ -76,8 +77,8 @@ frob_finish_kernel(const float* partials, int P, float eps, float* s_out) {
   if (threadIdx.x == 0) s_out[b] = 1.0f / (sqrtf(t) + eps);
 }
 
-hipError_t launch_frob(const void* X, gns_dtype dt, long long ldx, long long stride_x, int batch, int n,
-                       int m, float eps, float* s_out, float* partials, hipStream_t stream) {
+hipError_t launch_frob_partials(const void* X, gns_dtype dt, long long ldx, long long stride_x, int batch, int n,
+                                int m, float* partials, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
   const int P = frob_partials_per_batch(n, m);
   dim3 grid(P, batch);
@@ -87,7 +88,14 @@ hipError_t launch_frob(const void* X, gns_dtype dt, long long ldx, long long str
     case GNS_F16: clear_stale_error(); hipLaunchKernelGGL(frob_partial_kernel<TF16>, grid, dim3(kRedThreads), 0, stream, x, ldx, stride_x, n, m, P, partials); break;
     case GNS_F32: clear_stale_error(); hipLaunchKernelGGL(frob_partial_kernel<TF32>, grid, dim3(kRedThreads), 0, stream, x, ldx, stride_x, n, m, P, partials); break;
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_frob(const void* X, gns_dtype dt, long long ldx, long long stride_x, int batch, int n,
+                       int m, float eps, float* s_out, float* partials, hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  const int P = frob_partials_per_batch(n, m);
+  hipError_t e = launch_frob_partials(X, dt, ldx, stride_x, batch, n, m, partials, stream);
   if (e != hipSuccess) return e;
   clear_stale_error();
   hipLaunchKernelGGL(frob_finish_kernel, dim3(batch), dim3(kRedThreads), 0, stream, partials, P, eps, s_out);

@@ -22,6 +22,11 @@
 #include "common.h"
 #include "internal.h"
 
+// Ping-pong schedule of the 8-wave tiles (see gemm16_kernel); 0 selects the plain loop.
+#ifndef GNS_PP
+#define GNS_PP 1
+#endif
+
 namespace gns {
 
 __device__ __forceinline__ void tri_decode(int t, int& i, int& j) {
@@ -207,23 +212,77 @@ struct EpiPtrs {
   float alpha;
 };
 
+// The Frobenius scale of batch entry bz from its partial sums of squares (at most
+// 1024): lane l adds partials l, l + 64, ... in order (16 independent loads, one
+// latency), then an xor butterfly, whose result is bitwise the same in every lane
+// (each level adds the same two values in either order), so every wave and
+// workgroup forms the same s.  1 when the launch has no partials.
+constexpr int kMaxPartials = 1024;
+__device__ __forceinline__ float scale_from_partials(const GemmParams& p, int bz) {
+  if (!p.partials) return 1.0f;
+  const int lane = threadIdx.x & 63;
+  const float* q = p.partials + (size_t)bz * p.n_partials;
+  float v[kMaxPartials / 64];
+#pragma unroll
+  for (int r = 0; r < kMaxPartials / 64; ++r) {
+    const int i = lane + 64 * r;
+    v[r] = i < p.n_partials ? q[i] : 0.0f;
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int r = 0; r < kMaxPartials / 64; ++r) t += v[r];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
+  return 1.0f / (sqrtf(t) + p.eps);
+}
+
 template <class TOut>
-__device__ __forceinline__ EpiPtrs epi_ptrs(const GemmParams& p, int bz) {
+__device__ __forceinline__ EpiPtrs epi_ptrs(const GemmParams& p, int bz, bool second, float psc) {
   EpiPtrs e;
   e.alpha = p.alpha;
-  if (p.scale) for (int i = 0; i < p.alpha_pow; ++i) e.alpha *= p.scale[bz];
-  e.D = reinterpret_cast<uint8_t*>(p.D) + (size_t)bz * p.sD * TOut::kBytes;
-  e.D2 = p.D2 ? reinterpret_cast<uint8_t*>(p.D2) + (size_t)bz * p.sD2 * TOut::kBytes : nullptr;
-  e.C = p.C ? reinterpret_cast<const uint8_t*>(p.C) + (size_t)bz * p.sC * TOut::kBytes : nullptr;
+  if (p.partials) {
+    for (int i = 0; i < p.alpha_pow; ++i) e.alpha *= psc;
+  } else if (p.scale) {
+    for (int i = 0; i < p.alpha_pow; ++i) e.alpha *= p.scale[bz];
+  }
+  void* D = second ? p.Dp : p.D;
+  const void* C = second ? p.C2 : p.C;
+  e.D = reinterpret_cast<uint8_t*>(D) + (size_t)bz * p.sD * TOut::kBytes;
+  e.D2 = (p.D2 && !second) ? reinterpret_cast<uint8_t*>(p.D2) + (size_t)bz * p.sD2 * TOut::kBytes : nullptr;
+  e.C = C ? reinterpret_cast<const uint8_t*>(C) + (size_t)bz * p.sC * TOut::kBytes : nullptr;
   return e;
+}
+
+// Flat workgroup id -> (batch entry, second product of a pair, tile), with the XCD
+// remap applied over all batch * tiles (* 2 for a pair) workgroups; psc is the scale
+// formed from partial sums (1 without).
+struct GridPos {
+  int bz, tile;
+  bool second;
+  float psc;
+};
+__device__ __forceinline__ GridPos grid_pos(const GemmParams& p) {
+  const int total = p.batch * p.tiles * (p.pair ? 2 : 1);
+  const int rid = xcd_remap((int)blockIdx.x, total);
+  GridPos g;
+  int bz = __builtin_amdgcn_readfirstlane(rid / p.tiles);
+  g.tile = __builtin_amdgcn_readfirstlane(rid - bz * p.tiles);
+  g.second = p.pair && bz >= p.batch;
+  if (g.second) bz -= p.batch;
+  g.bz = bz;
+  g.psc = scale_from_partials(p, bz);
+  // tile 0 of each batch entry publishes the scale (read by later launches only)
+  if (p.partials && p.s_out && !g.second && g.tile == 0 && threadIdx.x == 0) p.s_out[bz] = g.psc;
+  return g;
 }
 
 // 16x16 fragments (v_mfma_f32_16x16x*, operands passed swapped): lane l owns row
 // (l % 16) and columns 4 (l / 16) + e of each fragment.
 template <class TOut, bool LOWER, int FM, int FN>
-__device__ __forceinline__ void epilogue(const GemmParams& p, f32x4_t (&acc)[FM][FN], int bz, int mw, int nw,
-                                         int lane) {
-  const EpiPtrs e = epi_ptrs<TOut>(p, bz);
+__device__ __forceinline__ void epilogue(const GemmParams& p, f32x4_t (&acc)[FM][FN], const GridPos& gp, int mw,
+                                         int nw, int lane) {
+  const int bz = gp.bz;
+  const EpiPtrs e = epi_ptrs<TOut>(p, bz, gp.second, gp.psc);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -270,9 +329,8 @@ gemm_kernel(GemmParams p) {
   const int wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   // one flat grid over (batch, tile), remapped so each XCD gets a contiguous range
-  const int rid = xcd_remap((int)blockIdx.x, p.batch * p.tiles);
-  const int bz = rid / p.tiles;
-  const int tile = rid - bz * p.tiles;
+  const GridPos gp = grid_pos(p);
+  const int bz = gp.bz, tile = gp.tile;
   int tm, tn;
   if constexpr (LOWER) {
     tri_decode(tile, tm, tn);
@@ -283,7 +341,7 @@ gemm_kernel(GemmParams p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
 
-  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A) + (size_t)bz * p.sA * TIn::kBytes;
+  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(gp.second ? p.A2 : p.A) + (size_t)bz * p.sA * TIn::kBytes;
   const uint8_t* Bb = reinterpret_cast<const uint8_t*>(p.B) + (size_t)bz * p.sB * TB::kBytes;
 
   float bmul = 1.0f;
@@ -439,7 +497,7 @@ gemm_kernel(GemmParams p) {
     __syncthreads();
   }
 
-  epilogue<TOut, LOWER, FM, FN>(p, acc, bz, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane);
+  epilogue<TOut, LOWER, FM, FN>(p, acc, gp, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane);
 }
 
 
@@ -604,14 +662,15 @@ __device__ __forceinline__ void store_vec(uint8_t* base, long long ld, int row, 
 // output is bitwise symmetric.  Only the slab writes index the accumulators, so
 // they stay in registers.
 template <class TOut, bool LOWER, int FM, int FN>
-__device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc)[FM][FN], int bz, int mw, int nw,
-                                             int lane, float* slab) {
+__device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc)[FM][FN], const GridPos& gp,
+                                             int mw, int nw, int lane, float* slab) {
+  const int bz = gp.bz;
   constexpr int WN = FN * 32;
   constexpr int S = WN + 4;
   constexpr int VE = 16 / TOut::kBytes;          // output elements per 16-byte vector
   constexpr int RV = WN / VE;                    // vectors per slab row
   constexpr int MV = 32 / VE;                    // vectors per mirrored row
-  const EpiPtrs ep = epi_ptrs<TOut>(p, bz);
+  const EpiPtrs ep = epi_ptrs<TOut>(p, bz, gp.second, gp.psc);
   const bool has_c = ep.C != nullptr && p.beta != 0.0f;
   const int M = p.M, N = p.N;
 #pragma unroll
@@ -720,9 +779,8 @@ gemm16_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   // block-level indices are uniform; readfirstlane keeps them in scalar registers
-  const int rid = xcd_remap((int)blockIdx.x, p.batch * p.tiles);
-  const int bz = __builtin_amdgcn_readfirstlane(rid / p.tiles);
-  const int tile = __builtin_amdgcn_readfirstlane(rid - bz * p.tiles);
+  const GridPos gp = grid_pos(p);
+  const int bz = gp.bz, tile = gp.tile;
   int tm, tn;
   constexpr int kGroup = BM >= 256 ? 4 : 8;
   if constexpr (LOWER) {
@@ -732,7 +790,7 @@ gemm16_kernel(GemmParams p) {
   }
   const int m0 = __builtin_amdgcn_readfirstlane(tm * BM), n0 = __builtin_amdgcn_readfirstlane(tn * BN);
   const int M = p.M, N = p.N, K = p.K;
-  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A) + (size_t)bz * p.sA * 2;
+  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(gp.second ? p.A2 : p.A) + (size_t)bz * p.sA * 2;
   const uint8_t* Bb = reinterpret_cast<const uint8_t*>(p.B) + (size_t)bz * p.sB * 2;
   const int4v_t rsA = sgpr_rsrc(Ab, (uint32_t)(((size_t)(M - 1) * p.lda + K) * 2));
   const int4v_t rsB = NN ? sgpr_rsrc(Bb, (uint32_t)(((size_t)(K - 1) * p.ldb + N) * 2))
@@ -839,7 +897,56 @@ gemm16_kernel(GemmParams p) {
   // kt instead of one k-step, which is what bounds them otherwise (one 32-cycle
   // MFMA per k-step against ~130 cycles of LDS latency).
   constexpr bool kStageFrags = 2 * KS * (FM + FN) * 4 <= 128;
-  if constexpr (!kStageFrags) {
+  // Two waves per SIMD (8 waves, WAVES_M = 2): the waves of tile row 0 (waves 0..3,
+  // one per SIMD) and of tile row 1 (waves 4..7) alternate between a compute phase
+  // (all MFMAs of one stage from registers) and a memory phase (all fragment reads of
+  // the next stage, plus this wave's share of the direct loads of a later stage), so
+  // each SIMD's MFMA pipe is fed by one wave while the other reads LDS.
+  constexpr bool kPingPong = GNS_PP && NW == 8 && WAVES_M == 2 && NS >= 3;
+  if constexpr (kPingPong) {
+    // Phases are separated by workgroup barriers.  Group 1 reads stage i in phase 2i
+    // and multiplies it in phase 2i+1; group 0 runs one phase behind (reads in 2i+1,
+    // multiplies in 2i+2).  Stage i's ring slot is therefore free after phase 2i+1,
+    // and the memory phase of stage i+1 (2i+2 or 2i+3) refills it with stage i+NS.
+    // At the end of phase 2i+1 every wave waits for its loads of stage i+1, which the
+    // barrier then publishes before group 1 reads it in phase 2i+2; the loads of the
+    // NS-2 younger stages stay in flight.  Every wave executes the same number of
+    // barriers (group 0 one extra at the start, group 1 one extra at the end).
+    const int grp = wm;
+    uint4 fa[KS][FM], fb[KS][FN];
+    constexpr int kAhead = (NS - 2) * LOADS;
+    auto memory_phase = [&](int i) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) read_frags(i % NS, ks, fa[ks], fb[ks]);
+#pragma unroll
+      for (int g = 0; g < LOADS; ++g) issue_load(i + NS - 1, g);
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));   // slot i % NS may be refilled after the barrier
+    };
+    auto compute_phase = [&]() {
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) mfma32_step<TIn>(acc[i][j], fa[ks][i], fb[ks][j]);
+      __builtin_amdgcn_s_setprio(0);
+    };
+#pragma unroll
+    for (int t = 0; t + 1 < NS; ++t) issue_stage(t);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAhead));
+    lds_barrier();
+    if (grp == 0) lds_barrier();
+    for (int i = 0; i < KT; ++i) {
+      memory_phase(i);
+      if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAhead));
+      lds_barrier();
+      compute_phase();
+      if (grp == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAhead));
+      lds_barrier();
+    }
+    if (grp == 1) lds_barrier();
+  } else if constexpr (!kStageFrags) {
     constexpr int H = (FM + 1) / 2;     // fragment rows of the last k-step before / after the barrier
     constexpr int L = (KS - 1) & 1;     // fragment set of the last k-step
     static_assert(L == 1, "the last k-step's fragments must not sit in set 0");
@@ -931,28 +1038,33 @@ gemm16_kernel(GemmParams p) {
   static_assert(NW * 32 * (Cfg::kWN + 4) * 4 <= Cfg::kLdsBytes, "epilogue slabs exceed the LDS ring");
   lds_barrier();
   float* slab = reinterpret_cast<float*>(smem16) + wave * 32 * (Cfg::kWN + 4);
-  epilogue_lds<TOut, LOWER, FM, FN>(p, acc, bz, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane, slab);
+  epilogue_lds<TOut, LOWER, FM, FN>(p, acc, gp, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane, slab);
 }
 
 // ---------------------------------------------------------------------------------
 // Host side: tile configurations and the launch of one configuration.
 
-// Output-tile configurations: (BM, BN, waves along M, waves along N, LDS ring depth
-// of the 16-bit kernel).  Measured on MI355X, a deeper ring does not help any of
-// them (3, 4 and 5 stages of the big tile run within 3% of each other; 8 or 16
-// stages of the small tiles are slower than 4), so all use 4 stages.
-//   big:   256 x 256, 8 waves of 128 x 64 (128 KB of LDS)
-//   mid:   128 x 128, 4 waves of 64 x 64   (64 KB)
-//   small:  64 x 64,  4 waves of 32 x 32   (32 KB) for problems with few tiles
+// Output-tile configurations: (BM, BN, waves along M, waves along N, LDS ring depth,
+// k values per stage of the 16-bit kernel).
+//   big:   256 x 256, 8 waves of 128 x 64 (two per SIMD, ping-pong schedule), a ring
+//          of 4 stages of 32 k values (128 KB of LDS)
+//   mid:   128 x 128, 4 waves of 64 x 64, 4 stages of 64 (128 KB)
+//   small:  64 x 64,  4 waves of 32 x 32, 4 stages of 64 (64 KB), for problems with
+//          few tiles
+// Measured on MI355X (alone, fp16 operands): the 8-wave big tile beats 4 waves of
+// 128 x 128 (one per SIMD) by 8-10% on 4096^3 products and by 30% on the n = 768
+// products of a 128-matrix batch; with 8 waves, 3, 4 and 5 stages of 32 and 2
+// stages of 64 run within 3% of each other, and 8 or 16 stages of the small tiles
+// are slower than 4.
 #ifndef GNS_BIG_WM
 #define GNS_BIG_WM 2
-#define GNS_BIG_WN 2
+#define GNS_BIG_WN 4
 #endif
 #ifndef GNS_BK_BIG
-#define GNS_BK_BIG 64
+#define GNS_BK_BIG 32
 #endif
 #ifndef GNS_STAGES_BIG
-#define GNS_STAGES_BIG 2
+#define GNS_STAGES_BIG 4
 #endif
 #ifndef GNS_BK_MID
 #define GNS_BK_MID 64
@@ -1020,13 +1132,16 @@ hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops
   p.tiles_n = (p.N + BN - 1) / BN;
   const long long tiles = gemm_tiles(p.M, p.N, BM, BN, LOWER);
   if (!operand_extents_ok(p, TIn::kBytes, TB::kBytes, NN)) return hipErrorInvalidValue;
+  if (p.pair && (NN || !LOWER || !p.A2 || !p.Dp || (p.C && !p.C2))) return hipErrorInvalidValue;
+  if (p.partials && (NN || !LOWER || p.n_partials < 1 || p.n_partials > kMaxPartials)) return hipErrorInvalidValue;
   const long long kpad = ((long long)(p.K + BK - 1) / BK) * BK;
-  if (flops) *flops += 2.0 * (double)tiles * BM * BN * (double)kpad * batch;
+  const int products = p.pair ? 2 : 1;
+  if (flops) *flops += 2.0 * (double)tiles * BM * BN * (double)kpad * batch * products;
   if (tiles == 0 || batch == 0) return hipSuccess;
   p.batch = batch;
   p.tiles = (int)tiles;
   clear_stale_error();
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * batch)), dim3(threads), lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * batch * products)), dim3(threads), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -1035,7 +1150,7 @@ hipError_t launch_cfg(GemmParams p, int batch, hipStream_t stream, double* flops
 #ifdef GNS_FORCE_TILE
   const TileCfg cfg = static_cast<TileCfg>(GNS_FORCE_TILE);
 #else
-  const TileCfg cfg = pick_tile(p.M, p.N, p.K, batch, LOWER);
+  const TileCfg cfg = pick_tile(p.M, p.N, p.K, p.pair ? 2 * batch : batch, LOWER);
 #endif
   switch (cfg) {
     case TileCfg::kBig:

@@ -160,12 +160,18 @@ int run_gram(const NsCall& c) {
   const float P = pow2_scale(c.cdt, n, m);
   const gns_dtype cdt = c.cdt;
   const float* s = c.s_given ? c.s_given : L.s;
-  if (!c.s_given) HIP_OK(launch_frob(c.X, c.xdt, c.ldx, c.sx, B, n, m, c.sch.eps, L.s, L.partials, c.stream));
+  if (!c.s_given) HIP_OK(launch_frob_partials(c.X, c.xdt, c.ldx, c.sx, B, n, m, L.partials, c.stream));
 
-  // R0 = s^2 X X^T: operands in X's dtype, result in the iterate dtype
+  // R0 = s^2 X X^T: operands in X's dtype, result in the iterate dtype.  Without a
+  // given scale, the product forms s from the partial sums and stores it to L.s.
   {
     GemmParams g = symm_params(n, m, c.X, c.ldx, c.sx, c.X, c.ldx, c.sx, L.R, n, nn);
-    g.scale = s; g.alpha_pow = 2;
+    g.alpha_pow = 2;
+    if (c.s_given) {
+      g.scale = s;
+    } else {
+      g.partials = L.partials; g.n_partials = frob_partials_per_batch(n, m); g.eps = c.sch.eps; g.s_out = L.s;
+    }
     HIP_OK(launch_symm(c.xdt, cdt, g, B, c.stream, c.flops));
   }
   const void* cx = c.X; gns_dtype cxdt = c.xdt; long long cld = c.ldx, csx = c.sx; bool cx_orig = true;
@@ -213,18 +219,24 @@ int run_gram(const NsCall& c) {
       if (q_identity) { g.D2 = Q; g.ldd2 = n; g.sD2 = nn; g.delta = a; }
       HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
     }
-    if (!q_identity) {  // Q <- Q Z + a Q
+    const bool need_r = t < c.sch.steps && !restart_before(t + 1);
+    // Q <- Q Z + a Q and Y = R Z + a R read the same Z: with both needed, one launch
+    // computes the pair
+    const bool q_update = !q_identity;
+    if (q_update) {
       GemmParams g = symm_params(n, n, Q, n, nn, L.Z, n, nn, Qn, n, nn);
       g.beta = a; g.C = Q; g.ldc = n; g.sC = nn;
+      if (need_r) { g.pair = 1; g.A2 = L.R; g.C2 = L.R; g.Dp = L.Y; }
       HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
       std::swap(Q, Qn);
     }
     q_identity = false;
-    const bool need_r = t < c.sch.steps && !restart_before(t + 1);
     if (need_r) {
-      GemmParams g1 = symm_params(n, n, L.R, n, nn, L.Z, n, nn, L.Y, n, nn);    // Y = R Z + a R
-      g1.beta = a; g1.C = L.R; g1.ldc = n; g1.sC = nn;
-      HIP_OK(launch_symm(cdt, cdt, g1, B, c.stream, c.flops));
+      if (!q_update) {
+        GemmParams g1 = symm_params(n, n, L.R, n, nn, L.Z, n, nn, L.Y, n, nn);  // Y = R Z + a R
+        g1.beta = a; g1.C = L.R; g1.ldc = n; g1.sC = nn;
+        HIP_OK(launch_symm(cdt, cdt, g1, B, c.stream, c.flops));
+      }
       GemmParams g2 = symm_params(n, n, L.Z, n, nn, L.Y, n, nn, L.R, n, nn);    // R = Z Y + a Y
       g2.beta = a; g2.C = L.Y; g2.ldc = n; g2.sC = nn;
       HIP_OK(launch_symm(cdt, cdt, g2, B, c.stream, c.flops));

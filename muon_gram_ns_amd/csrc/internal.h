@@ -7,7 +7,7 @@
 
 namespace gns {
 
-// Parameters of one batched GEMM launch (see gemm.hip).
+// Parameters of one batched GEMM launch (see gemm_kernel.h).
 //   symmetric (NT, lower tiles):  D = alpha' A B^T + beta C + gamma I, A,B: M x K
 //   rectangular (NN):             D = alpha' A B + beta C,            A: M x K, B: K x N
 // alpha' = alpha * scale[b]^alpha_pow.  NN with B of another 16-bit type converts
@@ -23,6 +23,15 @@ struct GemmParams {
   float alpha = 1.f, beta = 0.f, gamma = 0.f, delta = 0.f;
   const float* scale = nullptr; int alpha_pow = 0;
   float b_mul = 1.f; int b_pow = 0;
+  // pair (symmetric only): one launch also computes D' = alpha' A' B^T + beta C' for
+  // the same B, shapes and coefficients; workgroups of batch index >= batch take
+  // (A2, C2, Dp) at the same strides.  D2 is not written for the second product.
+  int pair = 0;
+  const void* A2 = nullptr; const void* C2 = nullptr; void* Dp = nullptr;
+  // partials (symmetric only, instead of scale): scale[b] = 1 / (sqrt(sum of the
+  // n_partials sums of squares of batch entry b) + eps), formed in every workgroup
+  // in one fixed order; tile 0 of entry b also stores it to s_out[b].
+  const float* partials = nullptr; int n_partials = 0; float eps = 0.f; float* s_out = nullptr;
   int tiles_m = 0, tiles_n = 0;   // set by the launcher
   int batch = 0, tiles = 0;       // set by the launcher: grid = batch * tiles workgroups
 };
@@ -34,10 +43,14 @@ hipError_t launch_rect(gns_dtype a, gns_dtype b, gns_dtype out, const GemmParams
                        hipStream_t stream, double* flops);
 bool rect_pair_supported(gns_dtype a, gns_dtype b);
 
-// Frobenius scale: partial sums of squares, then s[b] = mul / (sqrt(sum) + eps).
+// Frobenius scale: partial sums of squares, then s[b] = 1 / (sqrt(sum) + eps).
 int frob_partials_per_batch(int n, int m);
 hipError_t launch_frob(const void* X, gns_dtype dt, long long ldx, long long stride_x, int batch,
                        int n, int m, float eps, float* s_out, float* partials, hipStream_t stream);
+// ... only the partial sums (frob_partials_per_batch of them per batch entry), for a
+// GEMM that forms the scale itself (GemmParams::partials).
+hipError_t launch_frob_partials(const void* X, gns_dtype dt, long long ldx, long long stride_x, int batch,
+                                int n, int m, float* partials, hipStream_t stream);
 // Y = cast(mul * scale[b]^pow * X) elementwise, for batch x n x m matrices.
 hipError_t launch_cast_scale(const void* X, gns_dtype xdt, long long ldx, long long sx, void* Y,
                              gns_dtype ydt, long long ldy, long long sy, int batch, int n, int m,

@@ -135,3 +135,18 @@ def test_binding_rejects_operands_the_abi_cannot_check(gns_mod):
         gns_mod.symm_gemm(a, a, out=torch.empty(2, 64, 32, dtype=torch.float16, device="cuda"))
     with pytest.raises(TypeError):
         gns_mod.rect_gemm(a, a, C=c16, beta=1.0, out_dtype="f32")
+
+
+def test_symm_gemm_fp32_big_tiles(gns_mod):
+    """fp32 operands on the 256 x 256 tile configuration (a batch with >= 256 such
+    tiles), ragged n; the fp32 kernel shares the 8-wave tile layout."""
+    announce("symm_gemm f32 batch=64 n=520 k=72 (256x256)")
+    rng = np.random.default_rng(520)
+    a_st, a = stored(rng, (64, 520, 72), "f32")
+    c_st, c = stored(rng, (64, 520, 520), "f32")
+    D = gns_mod.symm_gemm(to_dev(a_st, "f32"), to_dev(a_st, "f32"), to_dev(c_st, "f32"), alpha=1.5, beta=-1.0,
+                          gamma=0.5, out_dtype="f32")
+    for i in (0, 31, 63):
+        check(to_f64(D[i]), symm_gemm_ref(a[i], a[i], c[i], alpha=1.5, beta=-1.0, gamma=0.5), TOL["f32"])
+    Dh = D.cpu()
+    assert bool((Dh == Dh.transpose(1, 2)).all())
