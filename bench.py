@@ -5,8 +5,9 @@
 
 Default workload: one 1024 x 4096 bf16 momentum matrix (aspect ratio 4), Gram NS with
 T = 5 quintic steps of (3.4445, -4.7750, 2.0315), restart after step 2, fp16 iterates
-with fp32 accumulation.  A step is one gns_orthogonalize_batched call over the batch;
-inputs are resident in HBM before the timed region.  One JSON line is printed.
+with fp32 accumulation.  A step is one gns_orthogonalize_batched call over the batch,
+launched eagerly (a HIP-graph replay of the same call is timed too); inputs are
+resident in HBM before the timed region.  One JSON line is printed.
 
 Also measured in the same run:
   * roofline of the dominant kernel (the lower-tile symmetric MFMA product), timed
@@ -86,34 +87,37 @@ def main():
     sched = gns.default_schedule()
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        gns.orthogonalize(X, out=out, compute=compute, schedule=sched)
+    def timed_ms(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t0) / steps
 
     _, issued = gns.orthogonalize(X, out=out, compute=compute, schedule=sched, return_flops=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = 1e3 * elapsed / args.steps
-    mats_per_s = B * args.steps / elapsed
+    # the step: one whole Gram NS call over the batch, launched eagerly on the current
+    # stream; the same call captured once in a HIP graph (own output and workspace) and
+    # replayed is timed too (on ROCm the replay does not beat eager launches here)
+    ms = timed_ms(lambda: gns.orthogonalize(X, out=out, compute=compute, schedule=sched),
+                  args.steps, args.warmup)
+    graphed = gns.graphed_orthogonalize(X, out=torch.empty_like(X), compute=compute, schedule=sched)
+    ms_graph = timed_ms(graphed.replay, args.steps, args.warmup)
+    mats_per_s = B / (ms * 1e-3)
     square = (n == m) and sched.square_fallback
     alg = B * (F.standard_schedule(n, m) if square else F.gram_schedule(n, m))
     nominal = B * F.standard_ns_nominal(n, m)
 
-    # standard-NS baseline on the same kernels
-    for _ in range(max(2, args.warmup // 4)):
-        gns.newton_schulz(X, out=out, compute=compute, schedule=sched)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    # standard-NS baseline on the same kernels, timed the same two ways
+    out_std = torch.empty_like(X)
     nstd = max(10, args.steps // 4)
-    for _ in range(nstd):
-        gns.newton_schulz(X, out=out, compute=compute, schedule=sched)
-    torch.cuda.synchronize()
-    ms_std = 1e3 * (time.perf_counter() - t1) / nstd
+    ms_std = timed_ms(lambda: gns.newton_schulz(X, out=out_std, compute=compute, schedule=sched),
+                      nstd, max(2, args.warmup // 4))
+    graphed_std = gns.graphed_newton_schulz(X, out=torch.empty_like(X), compute=compute, schedule=sched)
+    ms_std_graph = timed_ms(graphed_std.replay, nstd, max(2, args.warmup // 4))
+    del graphed, graphed_std
 
     roof = dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, args.steps, w.name)
     line = {
@@ -137,9 +141,12 @@ def main():
         "tflops_algorithmic": round(alg / (ms * 1e-3) / 1e12, 3),
         "tflops_issued": round(issued / (ms * 1e-3) / 1e12, 3),
         "pct_peak_issued": round(100 * issued / (ms * 1e-3) / 1e12 / PEAK_16BIT_TFLOPS, 3),
+        "timing": "eager launches of the whole call on one stream (inputs resident in HBM)",
+        "graph_replay": {"ms_per_step": round(ms_graph, 5), "matrices_per_s": round(B / (ms_graph * 1e-3), 3)},
         "standard_ns_same_kernels": {"ms_per_step": round(ms_std, 5),
                                      "matrices_per_s": round(B / (ms_std * 1e-3), 3),
-                                     "gram_speedup": round(ms_std / ms, 3)},
+                                     "gram_speedup": round(ms_std / ms, 3),
+                                     "graph_replay_ms_per_step": round(ms_std_graph, 5)},
         "roofline": roof,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(st, w, args.cpu_seconds),
     }
@@ -290,7 +297,12 @@ def bench_dion3(args, w):
         for _ in range(args.warmup):
             step()
         t = timed(step, args.steps)
-        res[f] = {"k": k, "ms_per_step": round(t * 1e3, 4),
+        graphed = gns.graphed_dion3_step(W, M, G, k, lr, 0.0, 0.95, score_norm=2, compute=args.compute)
+        for _ in range(args.warmup):
+            graphed.replay()
+        t_graph = timed(graphed.replay, args.steps)
+        del graphed
+        res[f] = {"k": k, "ms_per_step": round(t * 1e3, 4), "graph_replay_ms_per_step": round(t_graph * 1e3, 4),
                   "gram_ns_tflops_algorithmic": round(F.gram_schedule(k, m) / t / 1e12, 2)}
     # the HBM-bound pieces, alone (k = 2048)
     k = N // 4
@@ -321,6 +333,7 @@ def bench_dion3(args, w):
     print(json.dumps({"metric": "Dion3 steps/s", "value": round(1e3 / ms, 3), "unit": "steps/s", "n_gpus": 1,
                       "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
                       "scaling": "weak", "vs_baseline": None, "dtype": args.compute, "data": "synthetic",
+                      "timing": "eager launches of the whole step (inputs resident in HBM); graph replay also given",
                       "config": {"workload": w.name, "N": N, "m": m, "score": "l2", "mu": 0.95, "wd": 0.0,
                                  "fractions": res},
                       "hbm_pieces_k2048": pieces, "hbm_reference_same_tensors": reference,

@@ -169,7 +169,19 @@ def _mat3(x):
     return x, B, n, m, x.stride(1), (x.stride(0) if B > 1 else n * x.stride(1))
 
 
-def _ns(fn_name, X, out, compute, schedule, want_flops):
+def _workspace_arg(ws, nbytes, device):
+    """A caller-given workspace tensor (uint8 on the same device, >= nbytes), or the
+    shared grow-only one."""
+    torch = _torch()
+    if ws is None:
+        return workspace(nbytes, device)
+    _expect(ws, "workspace", dtype=torch.uint8, device=torch.device(device))
+    if not ws.is_contiguous() or ws.numel() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} contiguous bytes, got {ws.numel()}")
+    return ws
+
+
+def _ns(fn_name, X, out, compute, schedule, want_flops, ws=None):
     torch = _torch()
     _dev(X)
     squeeze = X.dim() == 2
@@ -183,7 +195,7 @@ def _ns(fn_name, X, out, compute, schedule, want_flops):
     cdt = code_of(compute)
     sched = schedule if schedule is not None else default_schedule()
     ws_n = lib.gns_workspace_size(B, n, m, cdt)
-    ws = workspace(ws_n, X.device)
+    ws = _workspace_arg(ws, ws_n, X.device)
     flops = ctypes.c_double(0.0)
     st = getattr(lib, fn_name)(X3.data_ptr(), dtype_code(X3), ldx, sx, O3.data_ptr(), dtype_code(O3), ldo, so,
                                B, n, m, cdt, ctypes.byref(sched), ws.data_ptr(), ws.numel(),
@@ -193,14 +205,19 @@ def _ns(fn_name, X, out, compute, schedule, want_flops):
     return (res, flops.value) if want_flops else res
 
 
-def orthogonalize(X, out=None, compute="f16", schedule=None, return_flops=False):
-    """Gram Newton-Schulz of X ([B, n, m] or [n, m], n <= m) -> same shape/dtype as X."""
-    return _ns("gns_orthogonalize_batched", X, out, compute, schedule, return_flops)
+def orthogonalize(X, out=None, compute="f16", schedule=None, return_flops=False, workspace=None):
+    """Gram Newton-Schulz of X ([B, n, m] or [n, m], n <= m) -> same shape/dtype as X.
+    workspace: optional uint8 device tensor of >= gns_workspace_size bytes."""
+    return _ns("gns_orthogonalize_batched", X, out, compute, schedule, return_flops, workspace)
 
 
-def newton_schulz(X, out=None, compute="f16", schedule=None, return_flops=False):
+def newton_schulz(X, out=None, compute="f16", schedule=None, return_flops=False, workspace=None):
     """Standard quintic Newton-Schulz on the same kernels."""
-    return _ns("gns_newton_schulz_batched", X, out, compute, schedule, return_flops)
+    return _ns("gns_newton_schulz_batched", X, out, compute, schedule, return_flops, workspace)
+
+
+def workspace_size(batch, n, m, compute="f16") -> int:
+    return int(lib.gns_workspace_size(batch, n, m, code_of(compute)))
 
 
 def frobenius_scale(X, eps=1e-7):
@@ -360,8 +377,10 @@ def dion3_apply_update(W, S, O, lr, wd):
 
 
 def dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute="f16", schedule=None,
-               return_O=False):
-    """One Dion3 step in place on W and M; returns S (and O when return_O)."""
+               return_O=False, S=None, O=None, workspace=None):
+    """One Dion3 step in place on W and M; returns S (and O when return_O).  S ([k]
+    int32), O ([k, m] bf16) and workspace may be given (fixed buffers for graph
+    replay)."""
     torch = _torch()
     N, m, ld = _bf16_rows(W, "W")
     _expect(M, "M", dtype=torch.bfloat16, shape=W.shape, device=W.device)
@@ -369,12 +388,21 @@ def dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute=
     if _rows(M)[2] != ld or _rows(G)[2] != ld:
         raise ValueError("W, M, G must share the row stride")
     cdt = code_of(compute)
-    S = torch.empty(k, dtype=torch.int32, device=W.device)
-    O = torch.empty((k, m), dtype=torch.bfloat16, device=W.device) if return_O else None
+    if S is None:
+        S = torch.empty(k, dtype=torch.int32, device=W.device)
+    _expect(S, "S", dtype=torch.int32, shape=(k,), device=W.device)
+    if return_O and O is None:
+        O = torch.empty((k, m), dtype=torch.bfloat16, device=W.device)
+    if O is not None:
+        _expect(O, "O", dtype=torch.bfloat16, shape=(k, m), device=W.device)
+        if not O.is_contiguous():
+            raise ValueError("O must be contiguous")
+    if not S.is_contiguous():
+        raise ValueError("S must be contiguous")
     sched = schedule if schedule is not None else default_schedule()
-    ws = workspace(lib.dion3_workspace_size(N, m, k, cdt), W.device)
+    ws = _workspace_arg(workspace, lib.dion3_workspace_size(N, m, k, cdt), W.device)
     check(lib.dion3_step(W.data_ptr(), M.data_ptr(), G.data_ptr(), N, m, ld, k, lr, weight_decay, mu,
                          score_norm, cdt, ctypes.byref(sched), S.data_ptr(),
                          O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
                          _stream(W.device)), "dion3_step")
-    return (S, O) if return_O else S
+    return (S, O) if (return_O or O is not None) else S

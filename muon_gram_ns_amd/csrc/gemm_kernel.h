@@ -515,8 +515,8 @@ gemm_kernel(GemmParams p) {
 //
 // LDS ring of STAGES slots, each one k-stage of 32 k values: the A tile as
 // [BM rows][64 B] (16-byte chunks swizzled by swz64()); the B tile the same (NT) or,
-// for the rectangular product, X's natural layout [32 rows (k)][BN * 2 B] with
-// 16-byte chunks XOR-ed by 2 (k & 3).  NN fragments are read with
+// for the rectangular product, X's natural layout [BK rows (k)][BN * 2 B] with
+// 16-byte chunks XOR-ed by nn_swz(k).  NN fragments are read with
 // ds_read_b64_tr_b16: lane i of a 16-lane group passes the address of row k0 + i/4,
 // columns n0 + 4 (i % 4) .. +3 and receives column n0 + i at rows k0 .. k0+3 -- an
 // MFMA operand column (verified on gfx950).
@@ -764,6 +764,13 @@ gemm16_kernel(GemmParams p) {
   constexpr int A_INSTR = A_BYTES / (1024 * NW), B_INSTR = B_BYTES / (1024 * NW);   // 1 KB per wave instruction
   constexpr int LOADS = A_INSTR + B_INSTR;                                           // per wave per stage
   constexpr int NCH = BN / 8;                                                        // NN: chunks per k row
+  // NN B tile: physical 16-byte chunk of logical chunk c in k-row kr is c ^ nn_swz(kr).
+  // A transposing fragment read has 32 lanes on 4 consecutive k-rows x 4 chunks; with
+  // 128-byte rows (BN = 64) consecutive rows already sit in opposite halves of the
+  // 256-byte bank window and 2 (kr & 3) separates the rest, while rows of 256 bytes or
+  // more overlay the same banks and need 4 (kr & 3) to put the 4 rows in 4 disjoint
+  // 64-byte groups.
+  auto nn_swz = [](int kr) { return NCH >= 16 ? 4 * (kr & 3) : 2 * (kr & 3); };
   constexpr int CPR = BK / 8;                                                        // NT: chunks per tile row
   constexpr int KS = BK / 16;                                                        // MFMA k-steps per stage
   static_assert(BK == 32 || BK == 64 || BK == 128, "stage depth");
@@ -822,7 +829,7 @@ gemm16_kernel(GemmParams p) {
         const int gr = n0 + row, gk = k0 + lc * 8;
         off = (gr < N && gk < K) ? (uint32_t)(((size_t)gr * p.ldb + gk) * 2) : kOutOfRange;
       } else {
-        const int kr = q / NCH, lc = (q % NCH) ^ (2 * (kr & 3));
+        const int kr = q / NCH, lc = (q % NCH) ^ nn_swz(kr);
         const int gk = k0 + kr, gn = n0 + lc * 8;
         off = (gk < K && gn < N) ? (uint32_t)(((size_t)gk * p.ldb + gn) * 2) : kOutOfRange;
       }
@@ -861,7 +868,7 @@ gemm16_kernel(GemmParams p) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int kr = ks * 16 + 8 * (g >> 1) + 4 * hh + (i16 >> 2);
-          const int pc = (nb >> 3) ^ (2 * (kr & 3));
+          const int pc = (nb >> 3) ^ nn_swz(kr);
           h[hh] = lds_read_tr16(bh + kr * BN + pc * 8 + (nb & 7));
         }
         fb[j] = convert_chunk<TIn, TB>(make_uint4(h[0].x, h[0].y, h[1].x, h[1].y), bmul);

@@ -33,3 +33,54 @@ def test_graph_replays_match_eager(gns_mod, fn):
         assert np.array_equal(bits(out), ref)
         f(X)                          # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("method", ["orthogonalize", "newton_schulz"])
+def test_graphed_call_owns_buffers_and_follows_input(gns_mod, method):
+    """graphed_* captures one call on its own workspace and output; a replay after the
+    input is refilled in place gives the eager result for the new contents, bitwise,
+    also after an eager call that needs a larger shared workspace."""
+    import torch
+    announce(f"graphed {method}")
+    st1 = synth.gns_batch("gns_1024x4096_bf16", batch=2, n=256, m=1024, seed=31)
+    st2 = synth.gns_batch("gns_1024x4096_bf16", batch=2, n=256, m=1024, seed=32)
+    X = to_dev(st1, "bf16")
+    eager = getattr(gns_mod, method)
+    g = getattr(gns_mod, f"graphed_{method}")(X)
+    ref1 = bits(eager(to_dev(st1, "bf16")))
+    ref2 = bits(eager(to_dev(st2, "bf16")))
+    for rep in range(3):
+        assert np.array_equal(bits(g.replay()), ref1)
+        torch.cuda.synchronize()
+        big = to_dev(synth.gns_batch("gns_1024x4096_bf16", batch=1, n=512, m=2048, seed=33), "bf16")
+        eager(big)                    # grows the shared workspace; the graph's is its own
+        torch.cuda.synchronize()
+    X.copy_(to_dev(st2, "bf16"))
+    for rep in range(2):
+        assert np.array_equal(bits(g.replay()), ref2)
+        torch.cuda.synchronize()
+
+
+def test_graphed_dion3_steps_match_eager_steps(gns_mod):
+    """Three replays of a captured Dion3 step equal three eager steps from the same
+    state, bitwise (W, M and S), with the gradient refilled in place between steps."""
+    import torch
+    announce("graphed dion3")
+    w, g0, m = synth.dion3_state(n=512, m=2048, seed=41)
+    grads = [synth.dion3_state(n=512, m=2048, seed=50 + i)[1] for i in range(3)]
+    tb = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    k, lr = 128, 0.02
+    We, Me = tb(w), tb(m)
+    Se = []
+    for gr in grads:
+        Se.append(gns_mod.dion3_step(We, Me, tb(gr), k, lr, 0.1, 0.95, score_norm=2).cpu().numpy())
+    Wg, Mg, Gg = tb(w), tb(m), tb(g0)
+    step = gns_mod.graphed_dion3_step(Wg, Mg, Gg, k, lr, 0.1, 0.95, score_norm=2)
+    assert np.array_equal(bits(Wg), w.view(np.uint16)) and np.array_equal(bits(Mg), m.view(np.uint16))
+    for i, gr in enumerate(grads):
+        Gg.copy_(tb(gr))
+        S = step.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(S.cpu().numpy(), Se[i])
+    assert np.array_equal(bits(Wg), bits(We))
+    assert np.array_equal(bits(Mg), bits(Me))
