@@ -45,7 +45,7 @@ extern "C" {
 
 typedef enum {
   GNS_OK = 0,
-  GNS_ERR_INVALID_ARG = -1,   /* null pointer, bad shape (n > m, k > N, k < 1), bad enum */
+  GNS_ERR_INVALID_ARG = -1,   /* null pointer, bad shape (k > N, k < 1, ld < m), bad enum */
   GNS_ERR_UNSUPPORTED = -2,   /* alignment / dtype combination not supported */
   GNS_ERR_WORKSPACE = -3,     /* workspace null or smaller than the *_workspace_size query */
   GNS_ERR_HIP = -4            /* a HIP launch or runtime call failed */
@@ -97,8 +97,10 @@ int gns_frobenius_scale(const void* X, gns_dtype x_dtype, long long ldx, long lo
 size_t gns_workspace_size(int batch, int n, int m, gns_dtype compute);
 
 /* Gram Newton-Schulz on `batch` same-shape matrices in one pass (one launch per step
- * over the whole batch).  X: [batch][n][ldx], 1 <= n <= m (iterate on the short side;
- * transpose a tall matrix before the call).  O: [batch][n][ldo], dtype o_dtype.
+ * over the whole batch).  X: [batch][n][ldx], n, m >= 1.  The iteration runs on the
+ * short side: for n > m the library transposes X into the workspace, runs on X^T and
+ * transposes the result back (polar(X^T) = polar(X)^T) [Muon blog, "Doing an SVD
+ * without an SVD"].  O: [batch][n][ldo], dtype o_dtype.
  * compute: dtype of the n x n iterates and of the MFMA operands after the first Gram
  * product: GNS_F16 (the pages' half precision, default), GNS_BF16, or GNS_F32.  All
  * products accumulate in fp32.  With x_dtype GNS_F32, compute must be GNS_F32.
@@ -188,7 +190,8 @@ size_t dion3_workspace_size(int N, int m, int k, gns_dtype compute);
  *   Frobenius norm taken from the per-row sums of squares); W <- decay + row update
  *   with lr (the caller passes lr = eta / sqrt(f)); M[S, :] <- mu M[S, :].
  * S_out: device int32[k] (ascending).  O_out: nullable device bf16 [k][m] (row stride
- * m) receiving O.  k must satisfy 1 <= k <= min(N, m). */
+ * m) receiving O.  1 <= k <= N, k a multiple of 8; with k > m the k x m submatrix is
+ * orthogonalized through its transpose, as in gns_orthogonalize_batched. */
 int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int k,
                float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
                const gns_schedule* sched, int* S_out, void* O_out,

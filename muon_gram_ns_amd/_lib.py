@@ -206,7 +206,8 @@ def _ns(fn_name, X, out, compute, schedule, want_flops, ws=None):
 
 
 def orthogonalize(X, out=None, compute="f16", schedule=None, return_flops=False, workspace=None):
-    """Gram Newton-Schulz of X ([B, n, m] or [n, m], n <= m) -> same shape/dtype as X.
+    """Gram Newton-Schulz of X ([B, n, m] or [n, m]; a tall X runs on its transpose)
+    -> same shape/dtype as X.
     workspace: optional uint8 device tensor of >= gns_workspace_size bytes."""
     return _ns("gns_orthogonalize_batched", X, out, compute, schedule, return_flops, workspace)
 

@@ -12,6 +12,8 @@
 // writes one partial; a second kernel (or, in Gram NS, the first Gram product's
 // epilogue) adds a batch's partials in a fixed order.  No atomics, so the result is
 // bitwise reproducible.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -163,6 +165,68 @@ hipError_t launch_cast_scale(const void* X, gns_dtype xdt, long long ldx, long l
     case GNS_F32: return cast_to<TF32>(ydt, grid, stream, x, ldx, sx, y, ldy, sy, n, m, mul, scale, pow);
   }
   return hipErrorInvalidValue;
+}
+
+// ---- batched transpose: Y[b] = X[b]^T for rows x cols matrices -------------------
+// Newton-Schulz runs on the short side of a matrix ("Muon: Orthogonalized Momentum
+// ...", section "Doing an SVD without an SVD": a tall input is transposed first).
+// 64 x 64 tiles staged through LDS with a pitch of 65 elements, so both the row-wise
+// writes and the column-wise reads of a wave hit distinct banks; global loads and
+// stores move 16-byte vectors along rows (rows and cols are multiples of 8, so a
+// vector is wholly inside or outside the matrix).
+template <class T>
+__global__ void __launch_bounds__(256)
+transpose_kernel(const uint8_t* X, long long ldx, long long sx, uint8_t* Y, long long ldy, long long sy, int rows,
+                 int cols) {
+  using U = typename std::conditional<T::kBytes == 2, uint16_t, uint32_t>::type;
+  constexpr int VE = 16 / T::kBytes;                 // elements per 16-byte vector
+  constexpr int NV = 16 / VE;                        // vectors per thread (16 elements)
+  __shared__ U tile[64][65];
+  const int b = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int t = threadIdx.x;
+  const U* xs = reinterpret_cast<const U*>(X + (size_t)b * sx * T::kBytes);
+  U* ys = reinterpret_cast<U*>(Y + (size_t)b * sy * T::kBytes);
+  {  // load: thread t takes row t / 4, columns 16 (t % 4) .. +15 of the tile
+    const int r = t >> 2, cb = (t & 3) * 16;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int gr = r0 + r, gc = c0 + cb + v * VE;
+      uint4 q = make_uint4(0, 0, 0, 0);
+      if (gr < rows && gc < cols) q = *reinterpret_cast<const uint4*>(xs + (size_t)gr * ldx + gc);
+      const U* e = reinterpret_cast<const U*>(&q);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) tile[r][cb + v * VE + i] = e[i];
+    }
+  }
+  __syncthreads();
+  {  // store: thread t takes output row (= input column) t / 4, output columns 16 (t % 4) ..
+    const int oc = t >> 2, rb = (t & 3) * 16;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      uint4 q;
+      U* e = reinterpret_cast<U*>(&q);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) e[i] = tile[rb + v * VE + i][oc];
+      const int grow = c0 + oc, gcol = r0 + rb + v * VE;
+      if (grow < cols && gcol < rows) *reinterpret_cast<uint4*>(ys + (size_t)grow * ldy + gcol) = q;
+    }
+  }
+}
+
+hipError_t launch_transpose(const void* X, gns_dtype dt, long long ldx, long long sx, int batch, int rows, int cols,
+                            void* Y, long long ldy, long long sy, hipStream_t stream) {
+  if (batch <= 0 || rows <= 0 || cols <= 0) return hipSuccess;
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64, batch);
+  const uint8_t* x = reinterpret_cast<const uint8_t*>(X);
+  uint8_t* y = reinterpret_cast<uint8_t*>(Y);
+  clear_stale_error();
+  switch (dt) {
+    case GNS_BF16: hipLaunchKernelGGL(transpose_kernel<TBF16>, grid, dim3(256), 0, stream, x, ldx, sx, y, ldy, sy, rows, cols); break;
+    case GNS_F16: hipLaunchKernelGGL(transpose_kernel<TF16>, grid, dim3(256), 0, stream, x, ldx, sx, y, ldy, sy, rows, cols); break;
+    case GNS_F32: hipLaunchKernelGGL(transpose_kernel<TF32>, grid, dim3(256), 0, stream, x, ldx, sx, y, ldy, sy, rows, cols); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace gns

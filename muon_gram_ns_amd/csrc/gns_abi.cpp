@@ -67,6 +67,30 @@ NsLayout ns_layout(void* base, int batch, int n, int m, gns_dtype cdt) {
   return L;
 }
 
+// A tall call (n > m) runs on the transposes: Xt = X^T and Ot (both [batch][m][n]),
+// then the wide call's workspace.  Element sizes: X's is 4 bytes iff the iterates are
+// fp32; O may be any dtype, so Ot is sized for 4 bytes.
+struct TallLayout {
+  void *Xt, *Ot, *inner;
+  size_t inner_bytes, bytes;
+};
+
+TallLayout tall_layout(void* base, int batch, int n, int m, gns_dtype cdt) {
+  Carver c{reinterpret_cast<uint8_t*>(base), 0};
+  TallLayout L{};
+  const size_t elems = (size_t)batch * n * m;
+  L.Xt = c.take(elems * (cdt == GNS_F32 ? 4 : 2));
+  L.Ot = c.take(elems * 4);
+  L.inner_bytes = ns_layout(nullptr, batch, m, n, cdt).bytes;
+  L.inner = c.take(L.inner_bytes);
+  L.bytes = c.off;
+  return L;
+}
+
+size_t ns_workspace_bytes(int batch, int n, int m, gns_dtype cdt) {
+  return n > m ? tall_layout(nullptr, batch, n, m, cdt).bytes : ns_layout(nullptr, batch, n, m, cdt).bytes;
+}
+
 float pow2_scale(gns_dtype cdt, int n, int m) {
   if (cdt != GNS_F16) return 1.0f;
   const int e = (int)std::lround(0.5 * std::log2((double)n * (double)m));
@@ -101,7 +125,7 @@ int check_schedule(const gns_schedule& s) {
 
 int check_ns(const NsCall& c) {
   if (!valid_dtype(c.xdt) || !valid_dtype(c.odt) || !valid_dtype(c.cdt)) return GNS_ERR_INVALID_ARG;
-  if (c.batch < 0 || c.n < 1 || c.m < 1 || c.n > c.m) return GNS_ERR_INVALID_ARG;
+  if (c.batch < 0 || c.n < 1 || c.m < 1) return GNS_ERR_INVALID_ARG;
   if (!c.X || !c.O) return GNS_ERR_INVALID_ARG;
   if (c.ldx < c.m || c.ldo < c.m) return GNS_ERR_INVALID_ARG;
   if (c.batch > 1 && (c.sx < (long long)c.n * c.ldx || c.so < (long long)c.n * c.ldo)) return GNS_ERR_INVALID_ARG;
@@ -118,7 +142,7 @@ int check_ns(const NsCall& c) {
   if (((size_t)(c.n - 1) * c.ldx + c.m) * esize(c.xdt) >= (size_t(1) << 31) ||
       (size_t)c.n * c.m * 4 >= (size_t(1) << 31))
     return GNS_ERR_UNSUPPORTED;
-  const size_t need = ns_layout(nullptr, c.batch, c.n, c.m, c.cdt).bytes;
+  const size_t need = ns_workspace_bytes(c.batch, c.n, c.m, c.cdt);
   if (c.batch > 0 && (!c.ws || c.ws_bytes < need)) return GNS_ERR_WORKSPACE;
   if (c.ws && c.batch > 0 && (overlaps(c.ws, need, c.O, ob) || overlaps(c.ws, need, c.X, xb))) return GNS_ERR_INVALID_ARG;
   return GNS_OK;
@@ -277,6 +301,26 @@ int run_standard(const NsCall& c) {
   return GNS_OK;
 }
 
+// Gram NS (gram) or standard NS for any orientation.  n > m: Newton-Schulz iterates
+// on the short side, so the call runs on X^T and transposes the result back ("Muon:
+// Orthogonalized Momentum ...", section "Doing an SVD without an SVD"); polar(X^T) =
+// polar(X)^T, and so does every step of the iteration.
+int run_ns(const NsCall& c, bool gram) {
+  if (c.n <= c.m) return (gram && !(c.sch.square_fallback && c.n == c.m)) ? run_gram(c) : run_standard(c);
+  const TallLayout L = tall_layout(c.ws, c.batch, c.n, c.m, c.cdt);
+  const long long tn = (long long)c.m * c.n;     // batch stride of the transposes
+  HIP_OK(launch_transpose(c.X, c.xdt, c.ldx, c.sx, c.batch, c.n, c.m, L.Xt, c.n, tn, c.stream));
+  NsCall w = c;
+  w.X = L.Xt; w.ldx = c.n; w.sx = tn;
+  w.O = L.Ot; w.ldo = c.n; w.so = tn;
+  w.n = c.m; w.m = c.n;
+  w.ws = L.inner; w.ws_bytes = L.inner_bytes;
+  const int st = (gram && !(w.sch.square_fallback && w.n == w.m)) ? run_gram(w) : run_standard(w);
+  if (st) return st;
+  HIP_OK(launch_transpose(L.Ot, c.odt, c.n, tn, c.batch, c.m, c.n, c.O, c.ldo, c.so, c.stream));
+  return GNS_OK;
+}
+
 NsCall make_call(const void* X, gns_dtype xdt, long long ldx, long long sx, void* O, gns_dtype odt, long long ldo,
                  long long so, int batch, int n, int m, gns_dtype cdt, const gns_schedule* sched, void* ws,
                  size_t ws_bytes, hipStream_t stream, double* flops) {
@@ -337,7 +381,7 @@ int gns_frobenius_scale(const void* X, gns_dtype x_dtype, long long ldx, long lo
 
 size_t gns_workspace_size(int batch, int n, int m, gns_dtype compute) {
   if (batch < 0 || n < 1 || m < 1 || !valid_dtype(compute)) return 0;
-  return ns_layout(nullptr, batch, n, m, compute).bytes;
+  return ns_workspace_bytes(batch, n, m, compute);
 }
 
 int gns_orthogonalize_batched(const void* X, gns_dtype x_dtype, long long ldx, long long stride_x, void* O,
@@ -350,8 +394,7 @@ int gns_orthogonalize_batched(const void* X, gns_dtype x_dtype, long long ldx, l
   const int st = check_ns(c);
   if (st) return st;
   if (batch == 0) return GNS_OK;
-  if (c.sch.square_fallback && n == m) return run_standard(c);
-  return run_gram(c);
+  return run_ns(c, true);
 }
 
 int gns_newton_schulz_batched(const void* X, gns_dtype x_dtype, long long ldx, long long stride_x, void* O,
@@ -365,7 +408,7 @@ int gns_newton_schulz_batched(const void* X, gns_dtype x_dtype, long long ldx, l
   const int st = check_ns(c);
   if (st) return st;
   if (batch == 0) return GNS_OK;
-  return run_standard(c);
+  return run_ns(c, false);
 }
 
 static int check_gemm_common(int batch, gns_dtype in, gns_dtype out, const void* A, long long lda, long long sA,
@@ -490,7 +533,7 @@ static Dion3Layout dion3_layout(void* base, int N, int m, int k, gns_dtype cdt) 
   L.s = (float*)c.take(sizeof(float));
   L.X = c.take((size_t)k * m * 2);
   L.O = c.take((size_t)k * m * 2);
-  L.gns_bytes = ns_layout(nullptr, 1, k, m, cdt).bytes;
+  L.gns_bytes = ns_workspace_bytes(1, k, m, cdt);
   L.gns_ws = c.take(L.gns_bytes);
   L.bytes = c.off;
   return L;
@@ -508,7 +551,7 @@ int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int 
   if (st) return st;
   if ((st = check_dion3_matrix(M, N, m, ld))) return st;
   if ((st = check_dion3_matrix(G, N, m, ld))) return st;
-  if (!S_out || k < 1 || k > N || k > m) return GNS_ERR_INVALID_ARG;
+  if (!S_out || k < 1 || k > N) return GNS_ERR_INVALID_ARG;
   if (score_norm != 1 && score_norm != 2) return GNS_ERR_INVALID_ARG;
   if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
   if (!valid_dtype(compute)) return GNS_ERR_INVALID_ARG;
@@ -531,8 +574,7 @@ int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int 
                        L.gns_ws, L.gns_bytes, stream, nullptr);
   c.s_given = L.s;
   if ((st = check_ns(c))) return st;
-  st = (sch.square_fallback && k == m) ? run_standard(c) : run_gram(c);
-  if (st) return st;
+  if ((st = run_ns(c, true))) return st;
   HIP_OK(launch_apply_update((uint16_t*)W, N, m, ld, S_out, k, O, GNS_BF16, m, lr, weight_decay, stream));
   return GNS_OK;
 }

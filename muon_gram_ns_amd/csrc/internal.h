@@ -56,6 +56,11 @@ hipError_t launch_cast_scale(const void* X, gns_dtype xdt, long long ldx, long l
                              gns_dtype ydt, long long ldy, long long sy, int batch, int n, int m,
                              float mul, const float* scale, int pow, hipStream_t stream);
 
+// Y[b] = X[b]^T for batch x rows x cols matrices (rows, cols, ldx, ldy multiples of 8
+// for 16-bit types, of 4 for fp32).
+hipError_t launch_transpose(const void* X, gns_dtype dt, long long ldx, long long sx, int batch, int rows, int cols,
+                            void* Y, long long ldy, long long sy, hipStream_t stream);
+
 // Dion3 element-wise kernels (dion3.hip).
 hipError_t launch_accumulate_score(uint16_t* M, const uint16_t* G, int N, int m, long long ld,
                                    int score_norm, double* score, double* sumsq, hipStream_t s);

@@ -151,3 +151,20 @@ def test_dion3_step_full_size(gns_mod):
             e = rel_fro(to_f64(O), O_ref)
             print(f"f={f} O rel err {e:.3e}")
             assert e <= 2e-2
+
+
+def test_dion3_step_tall_submatrix(gns_mod):
+    """k > m: the gathered k x m rows form a tall matrix, orthogonalised through its
+    transpose (the iteration runs on the short side)."""
+    announce("dion3 step 1024x256 k=512 (tall submatrix)")
+    w, g, m = synth.dion3_state(n=1024, m=256, seed=16)
+    k, lr = 512, 0.02
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    S, O = gns_mod.dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, return_O=True)
+    w_ref, m_ref, S_ref, O_ref = oracle.dion3_step(w, m, g, k, lr, wd=0.0, mu=0.95, norm="l1")
+    assert np.array_equal(S.cpu().numpy(), S_ref)
+    assert np.array_equal(bits(M), m_ref)
+    e = rel_fro(to_f64(O), O_ref)
+    print(f"tall O rel err {e:.3e}")
+    assert e <= 2e-2
+    assert w_within_bound(bits(W), w_ref, lr, O_ref)

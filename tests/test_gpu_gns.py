@@ -150,3 +150,30 @@ def test_issued_flops_reported(gns_mod):
     _, fl = gns_mod.orthogonalize(to_dev(st, "bf16"), return_flops=True)
     alg = gns_mod.flops.gram_schedule(512, 2048)
     assert alg <= fl <= 1.3 * alg
+
+
+@pytest.mark.parametrize("n,m,dt,compute,batch", [(4096, 1024, "bf16", "f16", 1), (256, 64, "f32", "f32", 1),
+                                                  (520, 264, "bf16", "f16", 3), (776, 264, "bf16", "bf16", 2)])
+@pytest.mark.parametrize("fn", ["orthogonalize", "newton_schulz"])
+def test_tall_matrices(gns_mod, n, m, dt, compute, batch, fn):
+    """n > m: the library runs on X^T and transposes back.  Parity against the oracle
+    (which also iterates on the short side), and bitwise equality with the caller
+    transposing: orthogonalize(X) == orthogonalize(X^T)^T."""
+    announce(f"gns tall {n}x{m} {dt} compute={compute} batch={batch} {fn}")
+    rng = np.random.default_rng(n + m)
+    st = synth.gns_batch("gns_1024x4096_bf16", batch=batch, n=m, m=n, seed=n + m)   # wide, then transposed
+    st = np.ascontiguousarray(np.swapaxes(st, 1, 2))
+    if dt == "f32":
+        st = synth.bf16_bits_to_f32(st).astype(np.float32)
+    got = run(gns_mod, st, dt, compute, fn=fn)
+    tol = 1e-4 if dt == "f32" else (6e-2 if compute == "bf16" else 2e-2)
+    for b in range(batch):
+        ref = newton_schulz(decode(st[b], dt))
+        e = rel_fro(got[b], ref)
+        print(f"tall {n}x{m} [{b}] rel err {e:.3e}")
+        assert e <= tol
+    f = getattr(gns_mod, fn)
+    X = to_dev(st, dt)
+    direct = f(X, compute=compute)
+    via_t = f(X.transpose(1, 2).contiguous(), compute=compute).transpose(1, 2).contiguous()
+    assert bool((direct == via_t).all())

@@ -1,8 +1,9 @@
 """CPU-only checks of the boundary and host logic (no kernel is launched):
 
 * libgns.so loads and exports every function include/gns.h declares;
-* argument validation rejects bad calls before any launch (n > m, null pointers,
-  misalignment, short workspace, bad schedule, unsupported dtype pairs);
+* argument validation rejects bad calls before any launch (null pointers, short
+  leading dimensions, misalignment, short workspace, bad schedule, unsupported dtype
+  pairs);
 * workspace-size queries;
 * the FLOP formulas against the savings the Dion3 pages state (55% / 68% at T = 5,
   alpha = 4) and the restart cost 3 (alpha - 1) n^3.
@@ -55,7 +56,11 @@ def ortho(X=FAKE, xdt=BF16, ldx=256, sx=64 * 256, O=FAKE * 3, odt=BF16, ldo=256,
 
 
 def test_validation_rejects_before_launch():
-    assert ortho(n=512, m=256) == INVALID                 # n > m
+    # n > m is valid (the library runs on the transpose) but needs the larger workspace
+    tall = L.gns_workspace_size(1, 512, 256, F16)
+    assert tall > L.gns_workspace_size(1, 256, 512, F16)
+    assert ortho(n=512, m=256, ldx=256, ldo=256, O=FAKE * 20, wsb=tall - 256) == WS
+    assert ortho(n=512, m=256, ldx=128) == INVALID         # ld < m still checked
     assert ortho(X=None) == INVALID
     assert ortho(O=None) == INVALID
     assert ortho(ldx=128) == INVALID                       # ld < m
@@ -73,7 +78,7 @@ def test_validation_rejects_before_launch():
     bad = gns.default_schedule()
     bad.steps = 0
     assert ortho(sched=bad) == INVALID
-    assert ortho(fn="gns_newton_schulz_batched", n=512, m=256) == INVALID
+    assert ortho(fn="gns_newton_schulz_batched", n=512, m=256, ldx=128) == INVALID
     assert ortho(B=0) == OK                                # empty batch: nothing to do
 
 
@@ -88,7 +93,7 @@ def test_gemm_and_dion3_validation():
                        FAKE * 2, 64, 0, F32, None) == UNSUP
     assert L.rect_gemm(1, 64, 64, 64, 1.0, FAKE, 64, 0, BF16, FAKE, 64, 0, BF16, 2.0, 0.0, None, 64, 0,
                        FAKE * 2, 64, 0, BF16, None) == INVALID
-    # dion3: k > N, k > m, bad norm, short workspace
+    # dion3: k > N, bad norm, short workspace
     sched = gns.default_schedule()
     args = lambda k, norm=1, wsb=1 << 40: (FAKE, FAKE * 2, FAKE * 3, 64, 256, 256, k, 0.02, 0.0, 0.95, norm, F16,
                                             ctypes.byref(sched), FAKE * 4, None, FAKE * 5, wsb, None)
