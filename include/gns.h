@@ -197,6 +197,23 @@ int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int 
                const gns_schedule* sched, int* S_out, void* O_out,
                void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes needed by dion3_step_batched. */
+size_t dion3_batched_workspace_size(int batch, int N, int m, int k, gns_dtype compute);
+
+/* dion3_step on `batch` same-shape N x m states at once (W, M, G: [batch][N][ld], entry
+ * b at offset b * stride elements, stride >= N * ld): per entry the same scores, top-k,
+ * gather, error feedback and update as dion3_step; the batch's k x m submatrices are
+ * orthogonalized by one batched Gram NS (one launch per step for all entries, the
+ * single-GPU form of the pages' megabatching of same-shape parameters)
+ * [paper.rainbus.top 方法步骤详情 (3) and (4); m.montaan.com summary].
+ * S_out: device int32 [batch][k] (each row ascending).  O_out: nullable device bf16
+ * [batch][k][m].  W, M and G must not overlap.  Each entry's result is bitwise the
+ * result of dion3_step on that entry alone.  Errors as dion3_step. */
+int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m, long long ld,
+                       long long stride, int k, float lr, float weight_decay, float mu,
+                       int score_norm, gns_dtype compute, const gns_schedule* sched, int* S_out,
+                       void* O_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -72,6 +72,8 @@ _sig("dion3_gather_feedback", I, P, I, I, LL, P, I, F, P, LL, P)
 _sig("dion3_apply_update", I, P, I, I, LL, P, I, P, I, LL, F, F, P)
 _sig("dion3_workspace_size", SZ, I, I, I, I)
 _sig("dion3_step", I, P, P, P, I, I, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
+_sig("dion3_batched_workspace_size", SZ, I, I, I, I, I)
+_sig("dion3_step_batched", I, P, P, P, I, I, I, LL, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
 
 
 def header_functions() -> list[str]:
@@ -407,3 +409,37 @@ def dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute=
                          O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
                          _stream(W.device)), "dion3_step")
     return (S, O) if (return_O or O is not None) else S
+
+
+def dion3_step_batched(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute="f16", schedule=None,
+                       return_O=False, S=None, O=None, workspace=None):
+    """One Dion3 step on each of the [B, N, m] bf16 states W, M (in place) with gradients
+    G; the B selected k x m submatrices are orthogonalized by one batched Gram NS.
+    Returns S [B, k] int32 (and O [B, k, m] when return_O or O is given)."""
+    torch = _torch()
+    _expect(W, "W", dtype=torch.bfloat16)
+    if W.dim() != 3 or W.stride(2) != 1:
+        raise ValueError("W must be a [B, N, m] tensor with contiguous rows")
+    B, N, m = W.shape
+    ld, stride = W.stride(1), W.stride(0)
+    for t, name in ((M, "M"), (G, "G")):
+        _expect(t, name, dtype=torch.bfloat16, shape=W.shape, device=W.device)
+        if t.stride() != W.stride():
+            raise ValueError("W, M, G must share their strides")
+    cdt = code_of(compute)
+    if S is None:
+        S = torch.empty((B, k), dtype=torch.int32, device=W.device)
+    _expect(S, "S", dtype=torch.int32, shape=(B, k), device=W.device)
+    if return_O and O is None:
+        O = torch.empty((B, k, m), dtype=torch.bfloat16, device=W.device)
+    if O is not None:
+        _expect(O, "O", dtype=torch.bfloat16, shape=(B, k, m), device=W.device)
+    if not S.is_contiguous() or (O is not None and not O.is_contiguous()):
+        raise ValueError("S and O must be contiguous")
+    sched = schedule if schedule is not None else default_schedule()
+    ws = _workspace_arg(workspace, lib.dion3_batched_workspace_size(B, N, m, k, cdt), W.device)
+    check(lib.dion3_step_batched(W.data_ptr(), M.data_ptr(), G.data_ptr(), B, N, m, ld, stride, k, lr,
+                                 weight_decay, mu, score_norm, cdt, ctypes.byref(sched), S.data_ptr(),
+                                 O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
+                                 _stream(W.device)), "dion3_step_batched")
+    return (S, O) if O is not None else S

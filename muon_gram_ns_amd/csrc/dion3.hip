@@ -61,12 +61,14 @@ __device__ __forceinline__ uint4 accumulate_chunk(uint4 mv, const uint4& gv, int
 }
 
 __global__ void __launch_bounds__(kRowThreads)
-accumulate_score_kernel(uint16_t* M, const uint16_t* G, int m, long long ld, int score_norm,
+accumulate_score_kernel(uint16_t* M, const uint16_t* G, int N, int m, long long ld, long long stride, int score_norm,
                         double* score, double* sumsq) {
   __shared__ double sh[kRowThreads / 64];
-  const int r = blockIdx.x;
-  uint4* mr = reinterpret_cast<uint4*>(M + (size_t)r * ld);
-  const uint4* gr = reinterpret_cast<const uint4*>(G + (size_t)r * ld);
+  const int r = blockIdx.x, b = blockIdx.y;
+  uint4* mr = reinterpret_cast<uint4*>(M + (size_t)b * stride + (size_t)r * ld);
+  const uint4* gr = reinterpret_cast<const uint4*>(G + (size_t)b * stride + (size_t)r * ld);
+  score += (size_t)b * N;
+  if (sumsq) sumsq += (size_t)b * N;
   const int nch = m / 8;
   double acc_s = 0.0, acc_q = 0.0;
   for (int c0 = threadIdx.x; c0 < nch; c0 += kAccUnroll * kRowThreads) {
@@ -93,12 +95,12 @@ accumulate_score_kernel(uint16_t* M, const uint16_t* G, int m, long long ld, int
   }
 }
 
-hipError_t launch_accumulate_score(uint16_t* M, const uint16_t* G, int N, int m, long long ld, int score_norm,
-                                   double* score, double* sumsq, hipStream_t s) {
-  if (N <= 0) return hipSuccess;
+hipError_t launch_accumulate_score(uint16_t* M, const uint16_t* G, int batch, int N, int m, long long ld,
+                                   long long stride, int score_norm, double* score, double* sumsq, hipStream_t s) {
+  if (N <= 0 || batch <= 0) return hipSuccess;
   clear_stale_error();
-  hipLaunchKernelGGL(accumulate_score_kernel, dim3(N), dim3(kRowThreads), 0, s, M, G, m, ld, score_norm,
-                     score, sumsq);
+  hipLaunchKernelGGL(accumulate_score_kernel, dim3(N, batch), dim3(kRowThreads), 0, s, M, G, N, m, ld, stride,
+                     score_norm, score, sumsq);
   return hipGetLastError();
 }
 
@@ -136,6 +138,8 @@ constexpr int kTopkLdsKeys = 12288;
 
 __global__ void __launch_bounds__(kTopkThreads)
 topk_kernel(const double* score, int N, int k, int* S) {
+  score += (size_t)blockIdx.x * N;     // one workgroup per batch entry
+  S += (size_t)blockIdx.x * k;
   __shared__ unsigned hist[256];
   __shared__ unsigned scan_sh[kTopkThreads / 64 + 1];
   __shared__ unsigned long long sh_prefix;
@@ -219,21 +223,22 @@ topk_kernel(const double* score, int N, int k, int* S) {
   }
 }
 
-hipError_t launch_topk(const double* score, int N, int k, int* S, hipStream_t s) {
+hipError_t launch_topk(const double* score, int batch, int N, int k, int* S, hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
   clear_stale_error();
-  hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(kTopkThreads), 0, s, score, N, k, S);
+  hipLaunchKernelGGL(topk_kernel, dim3(batch), dim3(kTopkThreads), 0, s, score, N, k, S);
   return hipGetLastError();
 }
 
 // ---- X[r] = M[S[r]]; M[S[r]] <- bf16(mu * M[S[r]]) ----------------------------------
 __global__ void __launch_bounds__(kRowThreads)
-gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, const int* S, float mu, uint16_t* X,
-                       long long ldx) {
-  const int r = blockIdx.x;
-  const int src = S[r];
+gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, long long stride, const int* S, int k, float mu,
+                       uint16_t* X, long long ldx) {
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int src = S[(size_t)b * k + r];
   if (src < 0 || src >= N) return;     // precondition violated: leave this row alone
-  uint4* mr = reinterpret_cast<uint4*>(M + (size_t)src * ld);
-  uint4* xr = reinterpret_cast<uint4*>(X + (size_t)r * ldx);
+  uint4* mr = reinterpret_cast<uint4*>(M + (size_t)b * stride + (size_t)src * ld);
+  uint4* xr = reinterpret_cast<uint4*>(X + ((size_t)b * k + r) * ldx);
   for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
     uint4 v = mr[c];
     xr[c] = v;
@@ -248,20 +253,24 @@ gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, const int* S, fl
   }
 }
 
-hipError_t launch_gather_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, float mu,
-                                  uint16_t* X, long long ldx, hipStream_t s) {
-  if (k <= 0) return hipSuccess;
+hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long long ld, long long stride, const int* S,
+                                  int k, float mu, uint16_t* X, long long ldx, hipStream_t s) {
+  if (k <= 0 || batch <= 0) return hipSuccess;
   clear_stale_error();
-  hipLaunchKernelGGL(gather_feedback_kernel, dim3(k), dim3(kRowThreads), 0, s, M, N, m, ld, S, mu, X, ldx);
+  hipLaunchKernelGGL(gather_feedback_kernel, dim3(k, batch), dim3(kRowThreads), 0, s, M, N, m, ld, stride, S, k, mu,
+                     X, ldx);
   return hipGetLastError();
 }
 
 // ---- weight decay + selected-row update, one rounding per element --------------------
 template <bool O_F32>
 __global__ void __launch_bounds__(kRowThreads)
-apply_update_kernel(uint16_t* W, int N, int m, long long ld, const int* S, int k, const void* O,
+apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, const int* S, int k, const void* O,
                     long long ldo, float lr, float wd, int all_rows) {
-  const int d_over = blockIdx.x;
+  const int d_over = blockIdx.x, b = blockIdx.y;
+  W += (size_t)b * stride;
+  S += (size_t)b * k;
+  O = reinterpret_cast<const uint8_t*>(O) + (size_t)b * k * ldo * (O_F32 ? 4 : 2);
   int row, oi;
   if (all_rows) {
     row = d_over;
@@ -316,18 +325,18 @@ apply_update_kernel(uint16_t* W, int N, int m, long long ld, const int* S, int k
   }
 }
 
-hipError_t launch_apply_update(uint16_t* W, int N, int m, long long ld, const int* S, int k, const void* O,
-                               gns_dtype o_dtype, long long ldo, float lr, float wd, hipStream_t s) {
+hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long ld, long long stride, const int* S, int k,
+                               const void* O, gns_dtype o_dtype, long long ldo, float lr, float wd, hipStream_t s) {
   const int all_rows = (wd != 0.0f) ? 1 : 0;
   const int blocks = all_rows ? N : k;
-  if (blocks <= 0) return hipSuccess;
+  if (blocks <= 0 || batch <= 0) return hipSuccess;
   clear_stale_error();
   if (o_dtype == GNS_F32)
-    hipLaunchKernelGGL(apply_update_kernel<true>, dim3(blocks), dim3(kRowThreads), 0, s, W, N, m, ld, S, k, O, ldo,
-                       lr, wd, all_rows);
+    hipLaunchKernelGGL(apply_update_kernel<true>, dim3(blocks, batch), dim3(kRowThreads), 0, s, W, N, m, ld, stride, S,
+                       k, O, ldo, lr, wd, all_rows);
   else
-    hipLaunchKernelGGL(apply_update_kernel<false>, dim3(blocks), dim3(kRowThreads), 0, s, W, N, m, ld, S, k, O, ldo,
-                       lr, wd, all_rows);
+    hipLaunchKernelGGL(apply_update_kernel<false>, dim3(blocks, batch), dim3(kRowThreads), 0, s, W, N, m, ld, stride,
+                       S, k, O, ldo, lr, wd, all_rows);
   return hipGetLastError();
 }
 
@@ -335,6 +344,9 @@ hipError_t launch_apply_update(uint16_t* W, int N, int m, long long ld, const in
 __global__ void __launch_bounds__(kRowThreads)
 selected_sumsq_kernel(const double* sumsq, const int* S, int k, int N, float eps, float* s_out) {
   __shared__ double sh[kRowThreads / 64];
+  sumsq += (size_t)blockIdx.x * N;     // one workgroup per batch entry
+  S += (size_t)blockIdx.x * k;
+  s_out += blockIdx.x;
   const int per = (k + kRowThreads - 1) / kRowThreads;
   double acc = 0.0;
   for (int i = threadIdx.x * per; i < min(k, (int)(threadIdx.x + 1) * per); ++i) {
@@ -345,10 +357,11 @@ selected_sumsq_kernel(const double* sumsq, const int* S, int k, int N, float eps
   if (threadIdx.x == 0) s_out[0] = (float)(1.0 / (sqrt(t) + (double)eps));
 }
 
-hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int k, int N, float eps, float* s_out,
+hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int batch, int k, int N, float eps, float* s_out,
                                  hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
   clear_stale_error();
-  hipLaunchKernelGGL(selected_sumsq_kernel, dim3(1), dim3(kRowThreads), 0, s, sumsq, S, k, N, eps, s_out);
+  hipLaunchKernelGGL(selected_sumsq_kernel, dim3(batch), dim3(kRowThreads), 0, s, sumsq, S, k, N, eps, s_out);
   return hipGetLastError();
 }
 

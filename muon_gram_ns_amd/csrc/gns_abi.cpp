@@ -490,13 +490,13 @@ int dion3_accumulate_score(void* M, const void* G, int N, int m, long long ld, i
   st = check_dion3_matrix(G, N, m, ld);
   if (st) return st;
   if (!score || (score_norm != 1 && score_norm != 2)) return GNS_ERR_INVALID_ARG;
-  HIP_OK(launch_accumulate_score((uint16_t*)M, (const uint16_t*)G, N, m, ld, score_norm, score, sumsq, stream));
+  HIP_OK(launch_accumulate_score((uint16_t*)M, (const uint16_t*)G, 1, N, m, ld, 0, score_norm, score, sumsq, stream));
   return GNS_OK;
 }
 
 int dion3_select_topk(const double* score, int N, int k, int* S, hipStream_t stream) {
   if (!score || !S || N < 1 || k < 1 || k > N) return GNS_ERR_INVALID_ARG;
-  HIP_OK(launch_topk(score, N, k, S, stream));
+  HIP_OK(launch_topk(score, 1, N, k, S, stream));
   return GNS_OK;
 }
 
@@ -506,7 +506,7 @@ int dion3_gather_feedback(void* M, int N, int m, long long ld, const int* S, int
   if (st) return st;
   if (!S || !X || k < 1 || k > N || ldx < m || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
   if (ldx % 8 || !aligned16(X)) return GNS_ERR_UNSUPPORTED;
-  HIP_OK(launch_gather_feedback((uint16_t*)M, N, m, ld, S, k, mu, (uint16_t*)X, ldx, stream));
+  HIP_OK(launch_gather_feedback((uint16_t*)M, 1, N, m, ld, 0, S, k, mu, (uint16_t*)X, ldx, stream));
   return GNS_OK;
 }
 
@@ -517,7 +517,7 @@ int dion3_apply_update(void* W, int N, int m, long long ld, const int* S, int k,
   if (!S || !O || k < 1 || k > N || ldo < m || !std::isfinite(lr) || !std::isfinite(wd)) return GNS_ERR_INVALID_ARG;
   if (o_dtype != GNS_BF16 && o_dtype != GNS_F32) return GNS_ERR_UNSUPPORTED;
   if (ldo % 8 || !aligned16(O)) return GNS_ERR_UNSUPPORTED;
-  HIP_OK(launch_apply_update((uint16_t*)W, N, m, ld, S, k, O, o_dtype, ldo, lr, wd, stream));
+  HIP_OK(launch_apply_update((uint16_t*)W, 1, N, m, ld, 0, S, k, O, o_dtype, ldo, lr, wd, stream));
   return GNS_OK;
 }
 
@@ -525,32 +525,42 @@ struct Dion3Layout {
   double* score; double* sumsq; float* s; void* X; void* O; void* gns_ws; size_t gns_bytes; size_t bytes;
 };
 
-static Dion3Layout dion3_layout(void* base, int N, int m, int k, gns_dtype cdt) {
+static Dion3Layout dion3_layout(void* base, int batch, int N, int m, int k, gns_dtype cdt) {
   Carver c{reinterpret_cast<uint8_t*>(base), 0};
   Dion3Layout L{};
-  L.score = (double*)c.take(sizeof(double) * (size_t)N);
-  L.sumsq = (double*)c.take(sizeof(double) * (size_t)N);
-  L.s = (float*)c.take(sizeof(float));
-  L.X = c.take((size_t)k * m * 2);
-  L.O = c.take((size_t)k * m * 2);
-  L.gns_bytes = ns_workspace_bytes(1, k, m, cdt);
+  const size_t B = (size_t)batch;
+  L.score = (double*)c.take(sizeof(double) * B * N);
+  L.sumsq = (double*)c.take(sizeof(double) * B * N);
+  L.s = (float*)c.take(sizeof(float) * B);
+  L.X = c.take(B * k * m * 2);
+  L.O = c.take(B * k * m * 2);
+  L.gns_bytes = ns_workspace_bytes(batch, k, m, cdt);
   L.gns_ws = c.take(L.gns_bytes);
   L.bytes = c.off;
   return L;
 }
 
-size_t dion3_workspace_size(int N, int m, int k, gns_dtype compute) {
-  if (N < 1 || m < 1 || k < 1 || !valid_dtype(compute)) return 0;
-  return dion3_layout(nullptr, N, m, k, compute).bytes;
+size_t dion3_batched_workspace_size(int batch, int N, int m, int k, gns_dtype compute) {
+  if (batch < 1 || N < 1 || m < 1 || k < 1 || !valid_dtype(compute)) return 0;
+  return dion3_layout(nullptr, batch, N, m, k, compute).bytes;
 }
 
-int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int k, float lr, float weight_decay,
-               float mu, int score_norm, gns_dtype compute, const gns_schedule* sched, int* S_out, void* O_out,
-               void* workspace, size_t ws_bytes, hipStream_t stream) {
+size_t dion3_workspace_size(int N, int m, int k, gns_dtype compute) {
+  return dion3_batched_workspace_size(1, N, m, k, compute);
+}
+
+int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m, long long ld, long long stride, int k,
+                       float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
+                       const gns_schedule* sched, int* S_out, void* O_out, void* workspace, size_t ws_bytes,
+                       hipStream_t stream) {
+  if (batch < 0) return GNS_ERR_INVALID_ARG;
+  if (batch == 0) return GNS_OK;
   int st = check_dion3_matrix(W, N, m, ld);
   if (st) return st;
   if ((st = check_dion3_matrix(M, N, m, ld))) return st;
   if ((st = check_dion3_matrix(G, N, m, ld))) return st;
+  if (batch > 1 && stride < (long long)N * ld) return GNS_ERR_INVALID_ARG;
+  if (batch > 1 && stride % 8) return GNS_ERR_UNSUPPORTED;
   if (!S_out || k < 1 || k > N) return GNS_ERR_INVALID_ARG;
   if (score_norm != 1 && score_norm != 2) return GNS_ERR_INVALID_ARG;
   if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
@@ -558,25 +568,40 @@ int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int 
   if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
   if (k % 8) return GNS_ERR_UNSUPPORTED;
   if (O_out && !aligned16(O_out)) return GNS_ERR_UNSUPPORTED;
+  // W, M and G must be distinct (each is read and written by different passes)
+  const size_t span = ((size_t)(batch - 1) * (size_t)(batch > 1 ? stride : 0) + (size_t)(N - 1) * ld + m) * 2;
+  if (overlaps(W, span, M, span) || overlaps(W, span, G, span) || overlaps(M, span, G, span))
+    return GNS_ERR_INVALID_ARG;
   gns_schedule sch;
   if (sched) sch = *sched; else gns_default_schedule(&sch);
   if ((st = check_schedule(sch))) return st;
-  const Dion3Layout L = dion3_layout(workspace, N, m, k, compute);
+  const Dion3Layout L = dion3_layout(workspace, batch, N, m, k, compute);
   if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
 
-  HIP_OK(launch_accumulate_score((uint16_t*)M, (const uint16_t*)G, N, m, ld, score_norm, L.score, L.sumsq, stream));
-  HIP_OK(launch_topk(L.score, N, k, S_out, stream));
-  HIP_OK(launch_gather_feedback((uint16_t*)M, N, m, ld, S_out, k, mu, (uint16_t*)L.X, m, stream));
-  HIP_OK(launch_selected_sumsq(L.sumsq, S_out, k, N, sch.eps, L.s, stream));
+  uint16_t* Mh = (uint16_t*)M;
+  HIP_OK(launch_accumulate_score(Mh, (const uint16_t*)G, batch, N, m, ld, stride, score_norm, L.score, L.sumsq, stream));
+  HIP_OK(launch_topk(L.score, batch, N, k, S_out, stream));
+  HIP_OK(launch_gather_feedback(Mh, batch, N, m, ld, stride, S_out, k, mu, (uint16_t*)L.X, m, stream));
+  HIP_OK(launch_selected_sumsq(L.sumsq, S_out, batch, k, N, sch.eps, L.s, stream));
   void* O = O_out ? O_out : L.O;
-  NsCall c = make_call(L.X, GNS_BF16, m, (long long)k * m, O, GNS_BF16, m, (long long)k * m, 1, k, m, compute, &sch,
-                       L.gns_ws, L.gns_bytes, stream, nullptr);
+  const long long km = (long long)k * m;
+  // one batched Gram NS over the selected k x m submatrices of every entry
+  NsCall c = make_call(L.X, GNS_BF16, m, km, O, GNS_BF16, m, km, batch, k, m, compute, &sch, L.gns_ws, L.gns_bytes,
+                       stream, nullptr);
   c.s_given = L.s;
   if ((st = check_ns(c))) return st;
   if ((st = run_ns(c, true))) return st;
-  HIP_OK(launch_apply_update((uint16_t*)W, N, m, ld, S_out, k, O, GNS_BF16, m, lr, weight_decay, stream));
+  HIP_OK(launch_apply_update((uint16_t*)W, batch, N, m, ld, stride, S_out, k, O, GNS_BF16, m, lr, weight_decay,
+                             stream));
   return GNS_OK;
+}
+
+int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int k, float lr, float weight_decay,
+               float mu, int score_norm, gns_dtype compute, const gns_schedule* sched, int* S_out, void* O_out,
+               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return dion3_step_batched(W, M, G, 1, N, m, ld, (long long)N * ld, k, lr, weight_decay, mu, score_norm, compute,
+                            sched, S_out, O_out, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -61,17 +61,18 @@ hipError_t launch_cast_scale(const void* X, gns_dtype xdt, long long ldx, long l
 hipError_t launch_transpose(const void* X, gns_dtype dt, long long ldx, long long sx, int batch, int rows, int cols,
                             void* Y, long long ldy, long long sy, hipStream_t stream);
 
-// Dion3 element-wise kernels (dion3.hip).
-hipError_t launch_accumulate_score(uint16_t* M, const uint16_t* G, int N, int m, long long ld,
-                                   int score_norm, double* score, double* sumsq, hipStream_t s);
-hipError_t launch_topk(const double* score, int N, int k, int* S, hipStream_t s);
-hipError_t launch_gather_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, float mu,
-                                  uint16_t* X, long long ldx, hipStream_t s);
-hipError_t launch_apply_update(uint16_t* W, int N, int m, long long ld, const int* S, int k,
-                               const void* O, gns_dtype o_dtype, long long ldo, float lr, float wd,
-                               hipStream_t s);
-// s[0] = 1 / (sqrt(sum_i sumsq[S[i]]) + eps): the Frobenius scale of the rows S.
-hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int k, int N, float eps,
+// Dion3 element-wise kernels (dion3.hip), over `batch` same-shape N x m matrices whose
+// entries are `stride` elements apart; per-entry vectors (score, sumsq: N; S: k;
+// X, O: k rows; s: 1) are packed back to back.
+hipError_t launch_accumulate_score(uint16_t* M, const uint16_t* G, int batch, int N, int m, long long ld,
+                                   long long stride, int score_norm, double* score, double* sumsq, hipStream_t s);
+hipError_t launch_topk(const double* score, int batch, int N, int k, int* S, hipStream_t s);
+hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long long ld, long long stride, const int* S,
+                                  int k, float mu, uint16_t* X, long long ldx, hipStream_t s);
+hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long ld, long long stride, const int* S, int k,
+                               const void* O, gns_dtype o_dtype, long long ldo, float lr, float wd, hipStream_t s);
+// s[b] = 1 / (sqrt(sum_i sumsq[b][S[b][i]]) + eps): the Frobenius scale of the rows S.
+hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int batch, int k, int N, float eps,
                                  float* s_out, hipStream_t s);
 
 }  // namespace gns

@@ -168,3 +168,30 @@ def test_dion3_step_tall_submatrix(gns_mod):
     print(f"tall O rel err {e:.3e}")
     assert e <= 2e-2
     assert w_within_bound(bits(W), w_ref, lr, O_ref)
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_dion3_step_batched_matches_oracle_and_single(gns_mod, wd):
+    """A batch of 3 same-shape states: per entry S and M bit-exact against the oracle,
+    O within 2e-2, W within the bound of the single test; and every entry bitwise equal
+    to dion3_step on that entry alone (batching changes no arithmetic)."""
+    import torch
+    announce(f"dion3 step batched 3x512x1024 wd={wd}")
+    B, N, m, k, lr = 3, 512, 1024, 128, 0.02
+    states = [synth.dion3_state(n=N, m=m, seed=60 + b) for b in range(B)]
+    stack = lambda i: torch.stack([to_dev(st[i], "bf16") for st in states])
+    W, G, M = stack(0), stack(1), stack(2)
+    S, O = gns_mod.dion3_step_batched(W, M, G, k, lr, weight_decay=wd, mu=0.95, score_norm=2, return_O=True)
+    Sb, Ob, Wb, Mb = S.cpu().numpy(), bits(O.reshape(B * k, m)), bits(W.reshape(B * N, m)), bits(M.reshape(B * N, m))
+    for b, (w, g, mm) in enumerate(states):
+        w_ref, m_ref, S_ref, O_ref = oracle.dion3_step(w, mm, g, k, lr, wd=wd, mu=0.95, norm="l2")
+        assert np.array_equal(Sb[b], S_ref)
+        assert np.array_equal(Mb[b * N:(b + 1) * N], m_ref)
+        assert rel_fro(to_f64(O[b]), O_ref) <= 2e-2
+        assert w_within_bound(Wb[b * N:(b + 1) * N], w_ref, lr, O_ref)
+        W1, M1, G1 = to_dev(w, "bf16"), to_dev(mm, "bf16"), to_dev(g, "bf16")
+        S1, O1 = gns_mod.dion3_step(W1, M1, G1, k, lr, weight_decay=wd, mu=0.95, score_norm=2, return_O=True)
+        assert np.array_equal(S1.cpu().numpy(), Sb[b])
+        assert np.array_equal(bits(O1), Ob[b * k:(b + 1) * k])
+        assert np.array_equal(bits(W1), Wb[b * N:(b + 1) * N])
+        assert np.array_equal(bits(M1), Mb[b * N:(b + 1) * N])

@@ -100,6 +100,15 @@ def test_gemm_and_dion3_validation():
     assert L.dion3_step(*args(65)) == INVALID
     assert L.dion3_step(*args(16, norm=3)) == INVALID
     assert L.dion3_step(*args(16, wsb=8)) == WS
+    # batched dion3: empty batch, short batch stride, aliased state, short workspace
+    bargs = lambda B, stride, W=FAKE, M=FAKE * 8, G=FAKE * 16, wsb=1 << 40: (
+        W, M, G, B, 64, 256, 256, stride, 16, 0.02, 0.0, 0.95, 1, F16, ctypes.byref(sched), FAKE * 30, None,
+        FAKE * 40, wsb, None)
+    assert L.dion3_step_batched(*bargs(0, 0)) == OK
+    assert L.dion3_step_batched(*bargs(2, 64 * 256 - 8)) == INVALID
+    assert L.dion3_step_batched(*bargs(2, 64 * 256, M=FAKE + 64 * 256 * 2)) == INVALID   # M overlaps W's 2nd entry
+    assert L.dion3_step_batched(*bargs(2, 64 * 256, wsb=8)) == WS
+    assert L.dion3_batched_workspace_size(2, 64, 256, 16, F16) > L.dion3_workspace_size(64, 256, 16, F16)
     assert L.dion3_select_topk(FAKE, 10, 11, FAKE, None) == INVALID
     assert L.dion3_select_topk(FAKE, 10, 0, FAKE, None) == INVALID
 
