@@ -42,6 +42,10 @@ def parse():
     p.add_argument("--compute", default="f16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--restart-sweep", action="store_true",
+                   help="only measure Gram NS error against the float64 oracle for each restart "
+                        "position (fp16 and bf16 iterates) on the 1024x4096 and square 2048^2 inputs, "
+                        "one JSON line per case, and exit")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 512 MiB device copy 5 times (reference for rocprofv3 "
                         "FETCH_SIZE / WRITE_SIZE scale factors) and exit")
@@ -72,6 +76,8 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": src.numel() * 2,
                           "bytes_written": dst.numel() * 2, "launches": 5}), flush=True)
         return
+    if args.restart_sweep:
+        return restart_sweep(gns, synth, torch, np)
     w = synth.workload(args.workload)
     if w.name.startswith("dion3"):
         return bench_dion3(args, w)
@@ -262,6 +268,63 @@ def cpu_baseline(st, w, seconds):
                       f"{el:.1f} s"}
 
 
+def restart_sweep(gns, synth, torch, np):
+    """Relative Frobenius error of Gram NS (T = 5, the blog's coefficients) against the
+    float64 oracle for each restart position, with fp16 and bf16 iterates.  The pages
+    restart once to flush the spurious negative eigenvalues that half-precision Gram
+    iterates acquire; where to restart is left to a sweep the pages do not print."""
+    import oracle
+    cases = [("gns_1024x4096_bf16", 1, 1024, 4096), ("gns_32x4096x4096_bf16", 1, 2048, 2048)]
+    masks = {"none": (), "after 1": (1,), "after 2": (2,), "after 3": (3,), "after 4": (4,),
+             "after 1 and 3": (1, 3), "after 2 and 4": (2, 4)}
+    for name, B, n, m in cases:
+        st = synth.gns_batch(name, batch=B, n=n, m=m)
+        X = torch.from_numpy(st.view(np.int16)).view(torch.bfloat16).cuda()
+        t0 = time.perf_counter()
+        ref = oracle.newton_schulz(oracle.bf16_to_f64(st[0]))
+        t_ref = time.perf_counter() - t0
+        for compute in ("f16", "bf16"):
+            for label, ra in masks.items():
+                sched = gns.default_schedule(restart_after=ra, square_fallback=False)
+                got = gns.orthogonalize(X, compute=compute, schedule=sched)[0].float().cpu().double().numpy()
+                finite = bool(np.isfinite(got).all())
+                err = float(np.linalg.norm(np.nan_to_num(got) - ref) / np.linalg.norm(ref)) if finite else None
+                print(json.dumps({"restart_sweep": name, "n": n, "m": m, "iterates": compute, "restart": label,
+                                  "rel_err_vs_oracle": err, "finite": finite,
+                                  "oracle_seconds": round(t_ref, 2)}), flush=True)
+
+
+def megabatch_dion3(gns, torch, args, B=16, N=2048, m=8192, f=0.25):
+    """One batched Dion3 step over B same-shape states against B single steps on the
+    same states (the single-GPU analogue of the pages' megabatching)."""
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    mk = lambda: (torch.randn(B, N, m, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    W, G, M = mk(), mk(), mk()
+    k = math.ceil(f * N)
+    lr = 0.01 / f ** 0.5
+    batched = lambda: gns.dion3_step_batched(W, M, G, k, lr, 0.0, 0.95, score_norm=2, compute=args.compute)
+
+    def loop():
+        for b in range(B):
+            gns.dion3_step(W[b], M[b], G[b], k, lr, 0.0, 0.95, score_norm=2, compute=args.compute)
+
+    res = {}
+    for name, fn in (("batched", batched), ("loop", loop)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        reps = max(5, args.steps // 5)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) / reps
+    del W, G, M
+    return {"states": f"{B} x {N}x{m} bf16", "k": k, "batched_ms": round(res["batched"] * 1e3, 4),
+            "loop_of_single_steps_ms": round(res["loop"] * 1e3, 4),
+            "speedup": round(res["loop"] / res["batched"], 3)}
+
+
 def bench_dion3(args, w):
     """Dion3 step on the 8192 x 28672 workload at f = 1/4 and 1/8 (l2 row scores).
     Inputs are drawn on the device from a seeded generator with the workload's
@@ -330,6 +393,9 @@ def bench_dion3(args, w):
     roof = {"bound": "hbm", "kernel": "accumulate_score_kernel", "achieved": pieces["accumulate_score"]["GB_s"],
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pieces["accumulate_score"]["GB_s"] / PEAK_HBM_GBS, 4),
             "traffic": None, "algorithmic_bytes_per_launch": b_acc}
+    del W, G, M
+    torch.cuda.empty_cache()
+    mega = megabatch_dion3(gns, torch, args)
     print(json.dumps({"metric": "Dion3 steps/s", "value": round(1e3 / ms, 3), "unit": "steps/s", "n_gpus": 1,
                       "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
                       "scaling": "weak", "vs_baseline": None, "dtype": args.compute, "data": "synthetic",
@@ -337,6 +403,7 @@ def bench_dion3(args, w):
                       "config": {"workload": w.name, "N": N, "m": m, "score": "l2", "mu": 0.95, "wd": 0.0,
                                  "fractions": res},
                       "hbm_pieces_k2048": pieces, "hbm_reference_same_tensors": reference,
+                      "megabatch_f_quarter": mega,
                       "roofline": roof, "cpu_baseline": None}), flush=True)
 
 

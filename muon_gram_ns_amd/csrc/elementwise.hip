@@ -229,4 +229,30 @@ hipError_t launch_transpose(const void* X, gns_dtype dt, long long ldx, long lon
   return hipGetLastError();
 }
 
+// ---- sum of the K-range partial products of a split Gram product ------------------
+// One float4 per thread: block 0 of tile t receives the sum of its `ranges` blocks,
+// added in range order (the same order for every element and every call).
+__global__ void __launch_bounds__(256)
+sum_ranges_kernel(float4* part, long long quads_per_block, int ranges, long long total) {
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= total) return;
+  const long long t = g / quads_per_block, x = g - t * quads_per_block;
+  float4* base = part + (size_t)t * ranges * quads_per_block + x;
+  float4 acc = base[0];
+  for (int r = 1; r < ranges; ++r) {
+    const float4 v = base[(size_t)r * quads_per_block];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  base[0] = acc;
+}
+
+hipError_t launch_sum_ranges(float* part, long long tiles, int ranges, long long block_floats, hipStream_t stream) {
+  if (tiles <= 0 || ranges <= 1) return hipSuccess;
+  const long long quads = block_floats / 4, total = tiles * quads;
+  clear_stale_error();
+  hipLaunchKernelGGL(sum_ranges_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<float4*>(part), quads, ranges, total);
+  return hipGetLastError();
+}
+
 }  // namespace gns

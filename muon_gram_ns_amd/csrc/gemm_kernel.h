@@ -17,6 +17,7 @@
 // operands (16x16x4 MFMA, register-staged double buffer).  Each wave owns a WM x WN
 // sub-tile of MFMA fragments accumulated in fp32.
 #pragma once
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -257,14 +258,17 @@ __device__ __forceinline__ EpiPtrs epi_ptrs(const GemmParams& p, int bz, bool se
 // remap applied over all batch * tiles (* 2 for a pair) workgroups; psc is the scale
 // formed from partial sums (1 without).
 struct GridPos {
-  int bz, tile;
+  int bz, tile, ks;     // ks: K range of a split partial launch (0 otherwise)
   bool second;
   float psc;
 };
 __device__ __forceinline__ GridPos grid_pos(const GemmParams& p) {
-  const int total = p.batch * p.tiles * (p.pair ? 2 : 1);
-  const int rid = xcd_remap((int)blockIdx.x, total);
+  const int splits = (p.ksplit > 1 && !p.reduce) ? p.ksplit : 1;
+  const int total = p.batch * p.tiles * (p.pair ? 2 : 1) * splits;
+  const int rid0 = xcd_remap((int)blockIdx.x, total);
   GridPos g;
+  g.ks = __builtin_amdgcn_readfirstlane(rid0 % splits);
+  const int rid = rid0 / splits;
   int bz = __builtin_amdgcn_readfirstlane(rid / p.tiles);
   g.tile = __builtin_amdgcn_readfirstlane(rid - bz * p.tiles);
   g.second = p.pair && bz >= p.batch;
@@ -797,6 +801,10 @@ gemm16_kernel(GemmParams p) {
   }
   const int m0 = __builtin_amdgcn_readfirstlane(tm * BM), n0 = __builtin_amdgcn_readfirstlane(tn * BN);
   const int M = p.M, N = p.N, K = p.K;
+  // K range of this workgroup: all of K, or one range of a split partial launch
+  const bool split_part = p.ksplit > 1 && !p.reduce;
+  const int kbeg = split_part ? gp.ks * p.kchunk : 0;
+  const int kend = split_part ? min(K, kbeg + p.kchunk) : K;
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(gp.second ? p.A2 : p.A) + (size_t)bz * p.sA * 2;
   const uint8_t* Bb = reinterpret_cast<const uint8_t*>(p.B) + (size_t)bz * p.sB * 2;
   const int4v_t rsA = sgpr_rsrc(Ab, (uint32_t)(((size_t)(M - 1) * p.lda + K) * 2));
@@ -811,14 +819,14 @@ gemm16_kernel(GemmParams p) {
   // load g (0 .. LOADS-1) of k-stage kt: one direct HBM -> LDS instruction (1 KB per
   // wave) into ring slot kt % NS; loads 0 .. A_INSTR-1 fill the A tile, the rest B
   auto issue_load = [&](int kt, int g) {
-    const int k0 = kt * BK;
+    const int k0 = kbeg + kt * BK;
     const uint32_t sb = lds0 + (kt % NS) * STAGE;
     if (g < A_INSTR) {
       const int blk = g * NW + wave;
       const int q = blk * 64 + lane;                      // LDS chunk this lane fills
       const int row = q / CPR, lc = swz_k<BK>(row, q % CPR);
       const int gr = m0 + row, gk = k0 + lc * 8;
-      const uint32_t off = (gr < M && gk < K) ? (uint32_t)(((size_t)gr * p.lda + gk) * 2) : kOutOfRange;
+      const uint32_t off = (gr < M && gk < kend) ? (uint32_t)(((size_t)gr * p.lda + gk) * 2) : kOutOfRange;
       dma16(rsA, __builtin_amdgcn_readfirstlane(sb + blk * 1024), off);
     } else {
       const int blk = (g - A_INSTR) * NW + wave;
@@ -827,11 +835,11 @@ gemm16_kernel(GemmParams p) {
       if constexpr (!NN) {
         const int row = q / CPR, lc = swz_k<BK>(row, q % CPR);
         const int gr = n0 + row, gk = k0 + lc * 8;
-        off = (gr < N && gk < K) ? (uint32_t)(((size_t)gr * p.ldb + gk) * 2) : kOutOfRange;
+        off = (gr < N && gk < kend) ? (uint32_t)(((size_t)gr * p.ldb + gk) * 2) : kOutOfRange;
       } else {
         const int kr = q / NCH, lc = (q % NCH) ^ nn_swz(kr);
         const int gk = k0 + kr, gn = n0 + lc * 8;
-        off = (gk < K && gn < N) ? (uint32_t)(((size_t)gk * p.ldb + gn) * 2) : kOutOfRange;
+        off = (gk < kend && gn < N) ? (uint32_t)(((size_t)gk * p.ldb + gn) * 2) : kOutOfRange;
       }
       dma16(rsB, __builtin_amdgcn_readfirstlane(sb + A_BYTES + blk * 1024), off);
     }
@@ -898,7 +906,32 @@ gemm16_kernel(GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int KT = (K + BK - 1) / BK;
+  const int KT = (kend - kbeg + BK - 1) / BK;
+  // fp32 partial accumulators of a split product, as float4 quads:
+  // [tile][range][wave][fragment][quad][lane], so every access of a wave moves 1 KB
+  // of consecutive bytes
+  constexpr int QUADS = FM * FN * 4;
+  auto part_ptr = [&](int ks) {
+    return reinterpret_cast<float4*>(p.part) + ((((size_t)bz * p.tiles + tile) * p.ksplit + ks) * NW + wave) * (QUADS * 64);
+  };
+  if (p.reduce) {
+    // sum of the ranges in order (reduce 2: already summed into range 0 by
+    // launch_sum_ranges), then the ordinary epilogue; each range's loads are all
+    // issued before any is added
+    const int nsum = p.reduce == 2 ? 1 : p.ksplit;
+    for (int ks = 0; ks < nsum; ++ks) {
+      const float4* q = part_ptr(ks);
+      float4 v[QUADS];
+#pragma unroll
+      for (int t = 0; t < QUADS; ++t) v[t] = q[t * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < QUADS; ++t) {
+        const int f = t / 4, c = t % 4;
+        f32x16_t& a = acc[f / FN][f % FN];
+        a[4 * c] += v[t].x; a[4 * c + 1] += v[t].y; a[4 * c + 2] += v[t].z; a[4 * c + 3] += v[t].w;
+      }
+    }
+  } else {
   // Small wave tiles (few MFMAs per k-step) keep a whole stage of fragments in
   // registers, twice: the LDS reads of stage kt+1 then overlap all MFMAs of stage
   // kt instead of one k-step, which is what bounds them otherwise (one 32-cycle
@@ -1039,7 +1072,18 @@ gemm16_kernel(GemmParams p) {
       stage_iter(std::integral_constant<int, 1>{}, kt + 1);
     }
   }
+  }  // k-loop
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the trailing out-of-range loads have written their zeros
+  if (split_part) {
+    float4* q = part_ptr(gp.ks);
+#pragma unroll
+    for (int t = 0; t < QUADS; ++t) {
+      const f32x16_t& a = acc[(t / 4) / FN][(t / 4) % FN];
+      const int c = t % 4;
+      q[t * 64 + lane] = make_float4(a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]);
+    }
+    return;
+  }
 
   // every wave is done with the operand ring: reuse it for the epilogue slabs
   static_assert(NW * 32 * (Cfg::kWN + 4) * 4 <= Cfg::kLdsBytes, "epilogue slabs exceed the LDS ring");
@@ -1141,14 +1185,19 @@ hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops
   if (!operand_extents_ok(p, TIn::kBytes, TB::kBytes, NN)) return hipErrorInvalidValue;
   if (p.pair && (NN || !LOWER || !p.A2 || !p.Dp || (p.C && !p.C2))) return hipErrorInvalidValue;
   if (p.partials && (NN || !LOWER || p.n_partials < 1 || p.n_partials > kMaxPartials)) return hipErrorInvalidValue;
-  const long long kpad = ((long long)(p.K + BK - 1) / BK) * BK;
+  if (p.ksplit > 1 && (!k16 || !LOWER || NN || p.pair || !p.part || p.kchunk % BK)) return hipErrorInvalidValue;
   const int products = p.pair ? 2 : 1;
-  if (flops) *flops += 2.0 * (double)tiles * BM * BN * (double)kpad * batch * products;
+  const int splits = (p.ksplit > 1 && !p.reduce) ? p.ksplit : 1;
+  if (flops && !p.reduce) {
+    // issued: K padded to whole stages (split ranges are whole stages but the last)
+    const long long kpad = ((long long)(p.K + BK - 1) / BK) * BK;
+    *flops += 2.0 * (double)tiles * BM * BN * (double)kpad * batch * products;
+  }
   if (tiles == 0 || batch == 0) return hipSuccess;
   p.batch = batch;
   p.tiles = (int)tiles;
   clear_stale_error();
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * batch * products)), dim3(threads), lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * batch * products * splits)), dim3(threads), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -1169,6 +1218,42 @@ hipError_t launch_cfg(GemmParams p, int batch, hipStream_t stream, double* flops
       return launch_one<TIn, TB, TOut, 64, 64, 2, 2, GNS_STAGES_SMALL, GNS_BK_SMALL, LOWER, NN>(p, batch, stream, flops);
   }
   return hipErrorInvalidValue;
+}
+
+// K split of the symmetric product: a single matrix (batch 1) with K >= 16384 and 32 to
+// 127 output tiles of 256 x 256 is cut into S ranges of at least 2048 values, S as
+// large as the CUs allow (at most 8).  The n = 2048, K = 28672 Gram product of the
+// Dion3 workload (36 tiles) runs on 7 ranges.  With fewer tiles each workgroup of the
+// sum would read too many partial tiles.  Only batch 1 splits: the sum order, and with
+// it the last bits, then differ from the same matrix in a batch.
+constexpr int kSplitMinK = 16384, kSplitMinChunk = 2048, kSplitBK = GNS_BK_BIG, kSplitMinTiles = 32;
+inline int symm_ksplit(int batch, int n, int K, int& kchunk) {
+  kchunk = 0;
+  if (batch != 1 || K < kSplitMinK) return 1;
+  const long long tiles = gemm_tiles(n, n, 256, 256, true);
+  if (tiles < kSplitMinTiles) return 1;
+  const long long S = std::min<long long>(std::min<long long>(256 / tiles, 8), K / kSplitMinChunk);
+  if (S < 2) return 1;
+  kchunk = (int)(((K + S - 1) / S + kSplitBK - 1) / kSplitBK * kSplitBK);
+  return (K + kchunk - 1) / kchunk;
+}
+
+// Three launches: the partial products (one workgroup per tile and K range), the sum
+// of each tile's ranges into its first range (element-parallel, fixed order), and the
+// epilogue over the summed tiles.
+template <class TIn, class TOut>
+hipError_t launch_symm_split(GemmParams p, int batch, float* part, hipStream_t stream, double* flops) {
+  p.part = part;
+  p.reduce = 0;
+  hipError_t e = launch_one<TIn, TIn, TOut, 256, 256, GNS_BIG_WM, GNS_BIG_WN, GNS_STAGES_BIG, GNS_BK_BIG, true, false>(
+      p, batch, stream, flops);
+  if (e != hipSuccess) return e;
+  const long long tiles = gemm_tiles(p.M, p.N, 256, 256, true) * batch;
+  e = launch_sum_ranges(part, tiles, p.ksplit, 256 * 256, stream);
+  if (e != hipSuccess) return e;
+  p.reduce = 2;
+  return launch_one<TIn, TIn, TOut, 256, 256, GNS_BIG_WM, GNS_BIG_WN, GNS_STAGES_BIG, GNS_BK_BIG, true, false>(
+      p, batch, stream, flops);
 }
 
 template <class TIn, class TB, bool LOWER, bool NN>

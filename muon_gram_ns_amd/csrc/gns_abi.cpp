@@ -45,6 +45,8 @@ struct Carver {
 struct NsLayout {
   float* s;
   float* partials;
+  float* part;            // fp32 partial products of a K-split Gram product (may be empty)
+  size_t part_bytes;
   void *R, *Z, *Y, *Q0, *Q1, *Xa, *Xb;   // Gram NS
   void *A, *Bm, *Sa, *Sb;                // standard NS (overlaps the Gram region)
   size_t bytes;
@@ -57,6 +59,9 @@ NsLayout ns_layout(void* base, int batch, int n, int m, gns_dtype cdt) {
   const size_t nn = (size_t)n * n * e * batch, nm = (size_t)n * m * e * batch;
   L.s = (float*)c.take(sizeof(float) * (size_t)batch);
   L.partials = (float*)c.take(sizeof(float) * (size_t)batch * frob_partials_per_batch(n, m));
+  // both Gram products of a call (and standard NS's) have K = m
+  L.part_bytes = symm_split_bytes(batch, n, m, cdt);
+  L.part = L.part_bytes ? (float*)c.take(L.part_bytes) : nullptr;
   const size_t common = c.off;
   L.R = c.take(nn); L.Z = c.take(nn); L.Y = c.take(nn); L.Q0 = c.take(nn); L.Q1 = c.take(nn);
   L.Xa = c.take(nm); L.Xb = c.take(nm);
@@ -196,7 +201,7 @@ int run_gram(const NsCall& c) {
     } else {
       g.partials = L.partials; g.n_partials = frob_partials_per_batch(n, m); g.eps = c.sch.eps; g.s_out = L.s;
     }
-    HIP_OK(launch_symm(c.xdt, cdt, g, B, c.stream, c.flops));
+    HIP_OK(launch_symm_ws(c.xdt, cdt, g, B, L.part, L.part_bytes, c.stream, c.flops));
   }
   const void* cx = c.X; gns_dtype cxdt = c.xdt; long long cld = c.ldx, csx = c.sx; bool cx_orig = true;
   bool q_identity = true;
@@ -234,7 +239,7 @@ int run_gram(const NsCall& c) {
       cx = xn; cxdt = cdt; cld = m; csx = nm; cx_orig = false;
       GemmParams g = symm_params(n, m, cx, m, nm, cx, m, nm, L.R, n, nn);
       g.alpha = 1.0f / (P * P);
-      HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
+      HIP_OK(launch_symm_ws(cdt, cdt, g, B, L.part, L.part_bytes, c.stream, c.flops));
       q_identity = true;
     }
     {  // Z = c R R + b R   (and Q = Z + a I while Q is the identity)
@@ -284,7 +289,7 @@ int run_standard(const NsCall& c) {
     const float a = c.sch.a[t - 1], b = c.sch.b[t - 1], cc = c.sch.c[t - 1];
     GemmParams g1 = symm_params(n, m, cur, m, nm, cur, m, nm, L.A, n, nn);
     g1.alpha = 1.0f / (P * P);
-    HIP_OK(launch_symm(c.cdt, c.cdt, g1, B, c.stream, c.flops));
+    HIP_OK(launch_symm_ws(c.cdt, c.cdt, g1, B, L.part, L.part_bytes, c.stream, c.flops));
     GemmParams g2 = symm_params(n, n, L.A, n, nn, L.A, n, nn, L.Bm, n, nn);
     g2.alpha = cc; g2.beta = b; g2.C = L.A; g2.ldc = n; g2.sC = nn;
     HIP_OK(launch_symm(c.cdt, c.cdt, g2, B, c.stream, c.flops));

@@ -32,6 +32,12 @@ struct GemmParams {
   // n_partials sums of squares of batch entry b) + eps), formed in every workgroup
   // in one fixed order; tile 0 of entry b also stores it to s_out[b].
   const float* partials = nullptr; int n_partials = 0; float eps = 0.f; float* s_out = nullptr;
+  // K split (symmetric, 16-bit operands): with ksplit > 1 and reduce == 0 each output
+  // tile is computed as ksplit partial products over K ranges of kchunk values whose
+  // raw fp32 accumulators go to part; reduce == 1 then sums them in range order and
+  // runs the epilogue.
+  int ksplit = 1, kchunk = 0, reduce = 0;
+  float* part = nullptr;
   int tiles_m = 0, tiles_n = 0;   // set by the launcher
   int batch = 0, tiles = 0;       // set by the launcher: grid = batch * tiles workgroups
 };
@@ -41,6 +47,13 @@ hipError_t launch_symm(gns_dtype in, gns_dtype out, const GemmParams& p, int bat
                        hipStream_t stream, double* flops);
 hipError_t launch_rect(gns_dtype a, gns_dtype b, gns_dtype out, const GemmParams& p, int batch,
                        hipStream_t stream, double* flops);
+// The symmetric product with K split over several workgroups per output tile when the
+// problem is one long-K matrix with too few tiles to fill the GPU (two launches: the
+// partial products, then their ordered sum and the epilogue), else launch_symm.
+// part: fp32 scratch of at least symm_split_bytes(batch, n, K) bytes (nullable: no split).
+hipError_t launch_symm_ws(gns_dtype in, gns_dtype out, const GemmParams& p, int batch, float* part,
+                          size_t part_bytes, hipStream_t stream, double* flops);
+size_t symm_split_bytes(int batch, int n, int K, gns_dtype in);
 bool rect_pair_supported(gns_dtype a, gns_dtype b);
 
 // Frobenius scale: partial sums of squares, then s[b] = 1 / (sqrt(sum) + eps).
@@ -55,6 +68,10 @@ hipError_t launch_frob_partials(const void* X, gns_dtype dt, long long ldx, long
 hipError_t launch_cast_scale(const void* X, gns_dtype xdt, long long ldx, long long sx, void* Y,
                              gns_dtype ydt, long long ldy, long long sy, int batch, int n, int m,
                              float mul, const float* scale, int pow, hipStream_t stream);
+
+// part[t][0][:] = sum over r = 0 .. ranges-1 of part[t][r][:] (in that order) for each
+// of `tiles` tiles of `ranges` blocks of `block_floats` floats (a multiple of 4).
+hipError_t launch_sum_ranges(float* part, long long tiles, int ranges, long long block_floats, hipStream_t stream);
 
 // Y[b] = X[b]^T for batch x rows x cols matrices (rows, cols, ldx, ldy multiples of 8
 // for 16-bit types, of 4 for fp32).

@@ -177,3 +177,27 @@ def test_tall_matrices(gns_mod, n, m, dt, compute, batch, fn):
     direct = f(X, compute=compute)
     via_t = f(X.transpose(1, 2).contiguous(), compute=compute).transpose(1, 2).contiguous()
     assert bool((direct == via_t).all())
+
+
+def test_long_k_single_matrix_split(gns_mod):
+    """One 2048 x 16384 matrix: its Gram products (K = 16384, 36 output tiles of 256 x
+    256) split K over 7 ranges per tile.  Parity against the oracle, bitwise
+    repeatable, and within rounding of the same matrix computed in a batch of two
+    (which does not split)."""
+    announce("gns 2048x16384 bf16 (K split)")
+    st = synth.gns_batch("gns_1024x4096_bf16", batch=1, n=2048, m=16384, seed=71)
+    st = np.concatenate([st, st])
+    announce("gns 2048x16384 bf16 (K split): oracle")
+    ref = newton_schulz(decode(st[0], "bf16"))
+    announce("gns 2048x16384 bf16 (K split): GPU")
+    one = to_dev(st[:1], "bf16")
+    o1 = gns_mod.orthogonalize(one)
+    o2 = gns_mod.orthogonalize(one)
+    assert np.array_equal(bits(o1), bits(o2))
+    e = rel_fro(to_f64(o1[0]), ref)
+    print(f"split rel err {e:.3e}")
+    assert e <= 2e-2
+    both = to_f64(gns_mod.orthogonalize(to_dev(st, "bf16"))[0])
+    assert rel_fro(to_f64(o1[0]), both) <= 5e-3
+    std = to_f64(gns_mod.newton_schulz(one)[0])
+    assert rel_fro(std, ref) <= 2e-2
