@@ -175,13 +175,14 @@ def gemm_source_digest():
     return h.hexdigest()
 
 
-def measured_traffic(workload_name):
+def measured_traffic(workload_name, launch_mix):
     path = os.path.join(ROOT, TRAFFIC_FILE)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("workload") != workload_name or t.get("gemm_source_sha256") != gemm_source_digest():
+    if (t.get("workload") != workload_name or t.get("launch_mix") != launch_mix
+            or t.get("gemm_source_sha256") != gemm_source_digest()):
         return None
     return t["bytes_per_launch"]
 
@@ -191,21 +192,32 @@ def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, wor
     call.  Its per-call launch mix (the n x n products with K = n, plus the restart
     Gram product with K = m) is replayed through the C ABI on the current stream,
     captured once in a HIP graph so the events time back-to-back kernels rather than
-    host launch overhead; achieved = algorithmic flops per launch / average launch."""
+    host launch overhead.
+
+    The roof is the lower of the MFMA peak and arithmetic intensity x HBM bandwidth,
+    with the algorithmic flops (n(n+1)K per product) and algorithmic bytes of the mix:
+    an n x n product with K = n reads its two distinct n x n operands (the beta C
+    term is one of them) and writes one; the Gram product reads X once and writes
+    n x n.  At n = 1024 the intensity is below the ridge (~315 flop/B), so the roof
+    is HBM and `achieved` is algorithmic GB/s; the MFMA fraction is given beside it."""
     dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[compute]
+    e = torch.tensor([], dtype=dt).element_size()
     # Gram NS (T=5, restart after 2), n x n products per call: t1: Z, Y, R (3); t2: Z, Q (2);
     # t3: Z, Y, R (3); t4: Z, Q, Y, R (4); t5: Z, Q (2) = 14; plus the Gram product of the
     # restarted X (K = m).  Standard NS: per step one X X^T (K = m) and one A A (K = n).
     nn_k, mm_k = (5, 5) if square else (14, 1)
-    R = torch.randn(B, n, n, device="cuda").to(dt)
-    R = (R + R.transpose(1, 2)) * 0.5
+    sym = lambda t: (t + t.transpose(1, 2)) * 0.5
+    R = sym(torch.randn(B, n, n, device="cuda")).to(dt)
+    Z = R if square else sym(torch.randn(B, n, n, device="cuda")).to(dt)
     Xh = (torch.randn(B, n, m, device="cuda") / m ** 0.5).to(dt)
     D = torch.empty(B, n, n, device="cuda", dtype=dt)
     per_graph = 10
+    nn_desc = "A A + beta A" if square else "R Z + beta R"
+    launch_mix = f"{nn_k} x (n={n}, K={n}, {nn_desc}) + {mm_k} x (n={n}, K={m}, X X^T), batch {B}"
 
     def mix():
         for _ in range(nn_k):
-            gns.symm_gemm(R, R, C=R, alpha=2.0, beta=-4.0, out=D)
+            gns.symm_gemm(R, Z, C=R, alpha=2.0, beta=-4.0, out=D)
         for _ in range(mm_k):
             gns.symm_gemm(Xh, Xh, out=D)
 
@@ -227,23 +239,38 @@ def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, wor
     reps = max(5, steps // (4 * per_graph))
     run()
     stream = torch.cuda.current_stream()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s, ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s.record(stream)
     for _ in range(reps):
         run()
-    e.record(stream)
+    ev.record(stream)
     torch.cuda.synchronize()
-    avg_s = s.elapsed_time(e) * 1e-3 / (reps * launches_per_run)
-    alg_per_launch = B * (nn_k * F.sym(n, n) + mm_k * F.sym(n, m)) / (nn_k + mm_k)
-    achieved = alg_per_launch / avg_s / 1e12
-    traffic = measured_traffic(workload_name) if not square else None
-    return {"bound": "mfma", "kernel": f"gemm16_kernel ({compute}, lower-triangle symmetric)",
-            "shape_mix": f"{nn_k} x (n={n}, K={n}) + {mm_k} x (n={n}, K={m}) per call, batch {B}",
-            "timing": timing, "avg_launch_us": round(avg_s * 1e6, 3),
-            "algorithmic_flops_per_launch": alg_per_launch,
-            "achieved": round(achieved, 3), "peak": PEAK_16BIT_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_16BIT_TFLOPS, 5), "traffic": traffic}
+    avg_s = s.elapsed_time(ev) * 1e-3 / (reps * launches_per_run)
+    alg_flops = B * (nn_k * F.sym(n, n) + mm_k * F.sym(n, m)) / (nn_k + mm_k)
+    nn_bytes = (2 if square else 3) * n * n * e
+    mm_bytes = (n * m + n * n) * e
+    alg_bytes = B * (nn_k * nn_bytes + mm_k * mm_bytes) / (nn_k + mm_k)
+    intensity = alg_flops / alg_bytes
+    tflops = alg_flops / avg_s / 1e12
+    gbs = alg_bytes / avg_s / 1e9
+    hbm_bound = intensity * PEAK_HBM_GBS * 1e9 < PEAK_16BIT_TFLOPS * 1e12
+    traffic = measured_traffic(workload_name, launch_mix)
+    roof = {"bound": "hbm" if hbm_bound else "mfma",
+            "kernel": f"gemm16_kernel ({compute}, lower-triangle symmetric)",
+            "shape_mix": launch_mix, "timing": timing, "avg_launch_us": round(avg_s * 1e6, 3),
+            "algorithmic_flops_per_launch": alg_flops, "algorithmic_bytes_per_launch": alg_bytes,
+            "intensity_flop_per_byte": round(intensity, 1),
+            "ridge_flop_per_byte": round(PEAK_16BIT_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9), 1)}
+    if hbm_bound:
+        roof.update({"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 5)})
+    else:
+        roof.update({"achieved": round(tflops, 3), "peak": PEAK_16BIT_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_16BIT_TFLOPS, 5)})
+    roof.update({"traffic": traffic, "mfma_tflops": round(tflops, 3),
+                 "mfma_frac": round(tflops / PEAK_16BIT_TFLOPS, 5)})
+    return roof
 
 
 def cpu_baseline(st, w, seconds):
