@@ -187,6 +187,28 @@ def measured_traffic(workload_name, launch_mix):
     return t["bytes_per_launch"]
 
 
+DION3_SOURCES = ("muon_gram_ns_amd/csrc/dion3.hip", "muon_gram_ns_amd/csrc/common.h")
+DION3_TRAFFIC_FILE = "profiles/traffic_accumulate_score_dion3_8192x28672.json"
+
+
+def measured_dion3_traffic(workload_name):
+    """HBM bytes per accumulate_score launch from rocprofv3 counters, reported only
+    while the Dion3 kernel sources are the ones they were counted on."""
+    import hashlib
+    path = os.path.join(ROOT, DION3_TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    h = hashlib.sha256()
+    for f in DION3_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if t.get("workload") != workload_name or t.get("dion3_source_sha256") != h.hexdigest():
+        return None
+    return t["bytes_per_launch"]
+
+
 def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, workload_name):
     """The lower-tile symmetric MFMA product in the iterate dtype dominates a Gram NS
     call.  Its per-call launch mix (the n x n products with K = n, plus the restart
@@ -419,7 +441,7 @@ def bench_dion3(args, w):
     ms = res[0.25]["ms_per_step"]
     roof = {"bound": "hbm", "kernel": "accumulate_score_kernel", "achieved": pieces["accumulate_score"]["GB_s"],
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pieces["accumulate_score"]["GB_s"] / PEAK_HBM_GBS, 4),
-            "traffic": None, "algorithmic_bytes_per_launch": b_acc}
+            "traffic": measured_dion3_traffic(w.name), "algorithmic_bytes_per_launch": b_acc}
     del W, G, M
     torch.cuda.empty_cache()
     mega = megabatch_dion3(gns, torch, args)
