@@ -7,7 +7,9 @@ Frobenius error <= 2e-2 for 16-bit paths, <= 1e-4 for the fp32 path.
 Cases: the 64x256 fp32 workload; the 1024x4096 bf16 MLP workload at full size
 (fp16 and bf16 iterates, Gram and standard); the 768x6144 MoE shape (alpha = 8) on a
 batch of full-size matrices; the 4096x4096 square shape (alpha = 1, where the pages
-fall back to standard NS); ragged and tiny shapes; a zero matrix; batch independence.
+fall back to standard NS); both batched workloads at their full batch (128 and 32
+matrices), sampled against the oracle; ragged and tiny shapes; a zero matrix; batch
+independence.
 """
 import numpy as np
 import pytest
@@ -75,6 +77,25 @@ def test_c3_square_full_size(gns_mod):
     e = rel_fro(got[0], ref)
     print(f"square fallback rel err {e:.3e}")
     assert e <= 2e-2
+
+
+# The two batched workloads at their full batch, i.e. in the launch configuration
+# bench.py times (256 x 256 tiles over all matrices of the batch); the oracle checks
+# sampled matrices one by one, and every output of the batch must be finite.
+@pytest.mark.parametrize("name,samples", [("gns_128x768x6144_bf16", (0, 64, 127)),
+                                          ("gns_32x4096x4096_bf16", (0, 31))])
+def test_full_batch_bench_configuration(gns_mod, name, samples):
+    announce(f"gns {name}: full batch, sampled matrices {samples}")
+    t = __import__("torch")
+    st = synth.gns_batch(name)
+    X = to_dev(st, "bf16")
+    O = gns_mod.orthogonalize(X, compute="f16")
+    assert bool(t.isfinite(O).all())
+    for i in samples:
+        ref = newton_schulz(decode(st[i], "bf16"))
+        e = rel_fro(to_f64(O[i]), ref)
+        print(f"matrix {i}: rel err {e:.3e}", flush=True)
+        assert e <= 2e-2
 
 
 # fp16 iterates (the default, the pages' half precision) meet 2e-2 everywhere.  The
