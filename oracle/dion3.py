@@ -23,7 +23,9 @@ Two storage modes:
 
 Parity status: select_topk pinned by brute force; accumulate / error_feedback /
 weight_update pinned by their bit-level definitions and invariants; dion3_step
-pinned by the f = 1 == Muon identity and the error-feedback invariants.
+pinned by the f = 1 == Muon identity and the error-feedback invariants;
+dion3_step_rows pinned by its invariants, by the all-rows case and by equality with
+dion3_step on the top-k set.
 """
 from __future__ import annotations
 
@@ -120,9 +122,38 @@ def dion3_step(w, m, g, k, lr, wd=0.0, mu=0.95, norm="l1", steps=5, abc=JORDAN_A
     m1 = accumulate(m, g)
     scores = row_scores(m1, norm)
     S = select_topk(scores, k)
+    w2, m2, O = _update_rows(w, m1, S, lr, wd, mu, ortho)
+    return w2, m2, S, O
+
+
+def _update_rows(w, m1, S, lr, wd, mu, ortho):
+    """The part of a step after the row set S is known: orthogonalise M[S, :],
+    store O in bf16, decay + row update of W, error feedback on M[S, :]."""
     X = bf16_to_f64(gather_rows(m1, S))
     O = ortho(X)
     O_stored = bf16_to_f64(f64_to_bf16_rne(O))
     w2 = weight_update(w, S, O_stored, lr, wd)
     m2 = error_feedback(m1, S, mu)
-    return w2, m2, S, O
+    return w2, m2, O
+
+
+def dion3_step_rows(w, m, g, S, lr, wd=0.0, mu=0.95, steps=5, abc=JORDAN_ABC, eps=EPS, orthogonalize=None):
+    """One Dion3 step on a row set S chosen by the caller instead of the top-k rows.
+
+    The pages report that rows picked at random train about as well as the rows of
+    largest l1 norm, and that a set S chosen without looking at M lets a data-parallel
+    step exchange only M[S, :] ("Dion3：全栈正交更新", paper.rainbus.top, 局限与改进 and
+    the future-work paragraph after it; the random draw itself is the caller's).
+    Everything else is Algorithm 4 as in dion3_step: M <- M + G, orthogonalise
+    M[S, :], decay + row update of W, error feedback on M[S, :].  w, m, g: uint16
+    bf16 bit patterns.  S: distinct row indices, ascending.  Returns (W', M', O).
+
+    Parity: pinned by its invariants, by S = all rows giving the orthogonalised
+    accumulated momentum, and by equality with dion3_step when S is its top-k set."""
+    S = np.asarray(S, dtype=np.int64)
+    n = np.asarray(m).shape[0]
+    if S.ndim != 1 or S.size == 0 or np.any(np.diff(S) <= 0) or S[0] < 0 or S[-1] >= n:
+        raise ValueError("S must hold distinct row indices in [0, N), ascending")
+    ortho = orthogonalize or (lambda x: newton_schulz(x, steps, abc, eps))
+    m1 = accumulate(m, g)
+    return _update_rows(w, m1, S, lr, wd, mu, ortho)

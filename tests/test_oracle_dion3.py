@@ -6,7 +6,10 @@
 * the error-feedback invariant (unselected momentum rows untouched, selected rows
   decayed by mu) from the Dion3 page, 前置知识 (error feedback) / Algorithm 4;
 * f = 1 reproduces Muon's momentum recursion M <- mu M + G exactly (float64),
-  stated on the Dion3 summary page (m.montaan.com).
+  stated on the Dion3 summary page (m.montaan.com);
+* the step on a caller-chosen row set (random selection): its invariants, the
+  all-rows case against the Newton-Schulz oracle, and equality with the top-k step
+  when given the top-k set.
 """
 import itertools
 import json
@@ -143,3 +146,47 @@ def test_f_equals_one_is_muon():
         assert np.array_equal(S, np.arange(n))
         assert np.allclose(O, o_muon, rtol=0, atol=1e-12)
         assert np.allclose(w, w_muon, rtol=0, atol=1e-12)
+
+
+# ---- a caller-chosen row set (random selection, the pages' alternative to top-k) ----
+
+def test_dion3_step_rows_invariants_random_set():
+    w, g, m = synth.dion3_state(n=64, m=256, seed=21)
+    rng = np.random.default_rng(22)
+    S = np.sort(rng.choice(64, size=16, replace=False))
+    w2, m2, O = oracle.dion3_step_rows(w, m, g, S, lr=0.02, wd=0.0, mu=0.95)
+    m1 = accumulate(m, g)
+    rest = np.setdiff1d(np.arange(64), S)
+    assert np.array_equal(m2[rest], m1[rest])                  # unselected: M + G only
+    assert np.array_equal(w2[rest], w[rest])                    # wd = 0: unselected W untouched
+    # selected momentum rows decay by mu, rounded once (torch's own bf16 arithmetic)
+    ref_m = (torch.tensor(np.float32(0.95)) * tbf(m1[S]).float()).to(torch.bfloat16)
+    assert np.array_equal(m2[S], bits_of(ref_m))
+    # O is the orthogonalised selected submatrix, and W[S] gets -lr O in one rounding
+    assert np.allclose(O, newton_schulz(bf16_to_f64(m1[S])), rtol=0, atol=1e-15)
+    o_b = tbf(f64_to_bf16_rne(O)).float()
+    ref_w = (tbf(w[S]).float() - torch.tensor(np.float32(0.02)) * o_b).to(torch.bfloat16)
+    assert np.array_equal(w2[S], bits_of(ref_w))
+
+
+def test_dion3_step_rows_all_rows_orthogonalises_accumulated_momentum():
+    w, g, m = synth.dion3_state(n=24, m=96, seed=23)
+    w2, m2, O = oracle.dion3_step_rows(w, m, g, np.arange(24), lr=0.01, wd=0.0, mu=0.9)
+    m1 = accumulate(m, g)
+    assert np.allclose(O, newton_schulz(bf16_to_f64(m1)), rtol=0, atol=1e-15)
+    assert np.array_equal(m2, error_feedback(m1, np.arange(24), 0.9))
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_dion3_step_rows_on_topk_set_equals_dion3_step(wd):
+    w, g, m = synth.dion3_state(n=40, m=128, seed=24)
+    w_a, m_a, S, O_a = dion3_step(w, m, g, 10, lr=0.02, wd=wd, mu=0.95, norm="l2")
+    w_b, m_b, O_b = oracle.dion3_step_rows(w, m, g, S, lr=0.02, wd=wd, mu=0.95)
+    assert np.array_equal(w_a, w_b) and np.array_equal(m_a, m_b) and np.array_equal(O_a, O_b)
+
+
+@pytest.mark.parametrize("S", [[3, 1], [1, 1, 2], [-1, 2], [0, 8], []])
+def test_dion3_step_rows_rejects_bad_sets(S):
+    w, g, m = synth.dion3_state(n=8, m=16, seed=25)
+    with pytest.raises(ValueError):
+        oracle.dion3_step_rows(w, m, g, S, lr=0.01)
