@@ -414,8 +414,16 @@ def bench_dion3(args, w):
             graphed.replay()
         t_graph = timed(graphed.replay, args.steps)
         del graphed
+        # the same step on k rows drawn at random (the pages' alternative to top-k; the
+        # draw, a seeded device permutation, is input generation outside the step)
+        S_rand = torch.randperm(N, device="cuda", generator=gen)[:k].sort().values.to(torch.int32)
+        step_rows = lambda: gns.dion3_step_rows(W, M, G, S_rand, lr, 0.0, 0.95, compute=args.compute)
+        for _ in range(args.warmup):
+            step_rows()
+        t_rows = timed(step_rows, args.steps)
         res[f] = {"k": k, "ms_per_step": round(t * 1e3, 4), "graph_replay_ms_per_step": round(t_graph * 1e3, 4),
-                  "gram_ns_tflops_algorithmic": round(F.gram_schedule(k, m) / t / 1e12, 2)}
+                  "gram_ns_tflops_algorithmic": round(F.gram_schedule(k, m) / t / 1e12, 2),
+                  "random_rows_ms_per_step": round(t_rows * 1e3, 4)}
     # the HBM-bound pieces, alone (k = 2048)
     k = N // 4
     reps = max(5, args.steps)

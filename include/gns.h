@@ -170,7 +170,8 @@ int dion3_accumulate_score(void* M, const void* G, int N, int m, long long ld, i
 int dion3_select_topk(const double* score, int N, int k, int* S, hipStream_t stream);
 
 /* X[r, :] = M[S[r], :] (bf16, row stride ldx) and then M[S[r], :] <- bf16(mu * M[S[r], :])
- * (error feedback: only selected rows decay). */
+ * (error feedback: only selected rows decay).  An index S[r] outside [0, N) gives a
+ * zero row X[r, :] and touches no row of M. */
 int dion3_gather_feedback(void* M, int N, int m, long long ld, const int* S, int k, float mu,
                           void* X, long long ldx, hipStream_t stream);
 
@@ -213,6 +214,24 @@ int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m,
                        long long stride, int k, float lr, float weight_decay, float mu,
                        int score_norm, gns_dtype compute, const gns_schedule* sched, int* S_out,
                        void* O_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* dion3_step on a row set S chosen by the caller instead of the top-k rows: the pages
+ * report that rows drawn at random train about as well as the rows of largest norm,
+ * and that a set chosen without reading M lets a data-parallel step exchange only
+ * M[S, :] [paper.rainbus.top, 局限与改进 and the future-work paragraph after it].  The
+ * draw is the caller's.  Otherwise as dion3_step: M <- M + G; X = M[S, :]; O =
+ * GramNS(X) (its Frobenius norm from the rows' sums of squares); W <- decay + row
+ * update with lr; M[S, :] <- mu M[S, :].
+ * S: device int32[k], distinct indices in [0, N), ascending; the library cannot check
+ * this without a host synchronisation.  An index outside [0, N) reads as a zero row of
+ * X and updates nothing; repeated or unordered indices give unspecified W and M (no
+ * out-of-bounds access).  O_out: nullable device bf16 [k][m].  Workspace:
+ * dion3_workspace_size(N, m, k, compute).  1 <= k <= N, k a multiple of 8; other
+ * errors as dion3_step. */
+int dion3_step_rows(void* W, void* M, const void* G, int N, int m, long long ld, const int* S, int k,
+                    float lr, float weight_decay, float mu, gns_dtype compute,
+                    const gns_schedule* sched, void* O_out, void* workspace, size_t ws_bytes,
+                    hipStream_t stream);
 
 #ifdef __cplusplus
 }

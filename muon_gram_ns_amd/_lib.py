@@ -74,6 +74,7 @@ _sig("dion3_workspace_size", SZ, I, I, I, I)
 _sig("dion3_step", I, P, P, P, I, I, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
 _sig("dion3_batched_workspace_size", SZ, I, I, I, I, I)
 _sig("dion3_step_batched", I, P, P, P, I, I, I, LL, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
+_sig("dion3_step_rows", I, P, P, P, I, I, LL, P, I, F, F, F, I, ctypes.POINTER(Schedule), P, P, SZ, P)
 
 
 def header_functions() -> list[str]:
@@ -409,6 +410,35 @@ def dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute=
                          O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
                          _stream(W.device)), "dion3_step")
     return (S, O) if (return_O or O is not None) else S
+
+
+def dion3_step_rows(W, M, G, S, lr, weight_decay=0.0, mu=0.95, compute="f16", schedule=None, O=None,
+                    workspace=None):
+    """One Dion3 step in place on W and M on the caller's row set S (a [k] int32 device
+    tensor of distinct ascending row indices, e.g. drawn at random).  Returns O
+    ([k, m] bf16) when O is given, else None."""
+    torch = _torch()
+    N, m, ld = _bf16_rows(W, "W")
+    _expect(M, "M", dtype=torch.bfloat16, shape=W.shape, device=W.device)
+    _expect(G, "G", dtype=torch.bfloat16, shape=W.shape, device=W.device)
+    if _rows(M)[2] != ld or _rows(G)[2] != ld:
+        raise ValueError("W, M, G must share the row stride")
+    _expect(S, "S", dtype=torch.int32, device=W.device)
+    if S.dim() != 1 or not S.is_contiguous():
+        raise ValueError("S must be a contiguous 1-D int32 tensor")
+    k = S.shape[0]
+    if O is not None:
+        _expect(O, "O", dtype=torch.bfloat16, shape=(k, m), device=W.device)
+        if not O.is_contiguous():
+            raise ValueError("O must be contiguous")
+    cdt = code_of(compute)
+    sched = schedule if schedule is not None else default_schedule()
+    ws = _workspace_arg(workspace, lib.dion3_workspace_size(N, m, k, cdt), W.device)
+    check(lib.dion3_step_rows(W.data_ptr(), M.data_ptr(), G.data_ptr(), N, m, ld, S.data_ptr(), k, lr,
+                              weight_decay, mu, cdt, ctypes.byref(sched),
+                              O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
+                              _stream(W.device)), "dion3_step_rows")
+    return O
 
 
 def dion3_step_batched(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute="f16", schedule=None,

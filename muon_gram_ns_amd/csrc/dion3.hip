@@ -239,9 +239,12 @@ gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, long long stride
                        uint16_t* X, long long ldx) {
   const int r = blockIdx.x, b = blockIdx.y;
   const int src = S[(size_t)b * k + r];
-  if (src < 0 || src >= N) return;     // precondition violated: leave this row alone
-  uint4* mr = reinterpret_cast<uint4*>(M + (size_t)b * stride + (size_t)src * ld);
   uint4* xr = reinterpret_cast<uint4*>(X + ((size_t)b * k + r) * ldx);
+  if (src < 0 || src >= N) {           // precondition violated: a zero row of X, M untouched
+    for (int c = threadIdx.x; c < m / 8; c += kRowThreads) xr[c] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
+  uint4* mr = reinterpret_cast<uint4*>(M + (size_t)b * stride + (size_t)src * ld);
   for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
     uint4 v = mr[c];
     xr[c] = v;

@@ -554,10 +554,12 @@ size_t dion3_workspace_size(int N, int m, int k, gns_dtype compute) {
   return dion3_batched_workspace_size(1, N, m, k, compute);
 }
 
-int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m, long long ld, long long stride, int k,
-                       float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
-                       const gns_schedule* sched, int* S_out, void* O_out, void* workspace, size_t ws_bytes,
-                       hipStream_t stream) {
+// One Dion3 step over `batch` states: the rows are the top-k by score (S_in null; S
+// receives them) or the caller's set S_in.
+static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, long long ld, long long stride, int k,
+                     float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
+                     const gns_schedule* sched, const int* S_in, int* S_out, void* O_out, void* workspace,
+                     size_t ws_bytes, hipStream_t stream) {
   if (batch < 0) return GNS_ERR_INVALID_ARG;
   if (batch == 0) return GNS_OK;
   int st = check_dion3_matrix(W, N, m, ld);
@@ -566,7 +568,7 @@ int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m,
   if ((st = check_dion3_matrix(G, N, m, ld))) return st;
   if (batch > 1 && stride < (long long)N * ld) return GNS_ERR_INVALID_ARG;
   if (batch > 1 && stride % 8) return GNS_ERR_UNSUPPORTED;
-  if (!S_out || k < 1 || k > N) return GNS_ERR_INVALID_ARG;
+  if ((!S_in && !S_out) || k < 1 || k > N) return GNS_ERR_INVALID_ARG;
   if (score_norm != 1 && score_norm != 2) return GNS_ERR_INVALID_ARG;
   if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
   if (!valid_dtype(compute)) return GNS_ERR_INVALID_ARG;
@@ -586,9 +588,13 @@ int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m,
 
   uint16_t* Mh = (uint16_t*)M;
   HIP_OK(launch_accumulate_score(Mh, (const uint16_t*)G, batch, N, m, ld, stride, score_norm, L.score, L.sumsq, stream));
-  HIP_OK(launch_topk(L.score, batch, N, k, S_out, stream));
-  HIP_OK(launch_gather_feedback(Mh, batch, N, m, ld, stride, S_out, k, mu, (uint16_t*)L.X, m, stream));
-  HIP_OK(launch_selected_sumsq(L.sumsq, S_out, batch, k, N, sch.eps, L.s, stream));
+  const int* S = S_in;
+  if (!S_in) {
+    HIP_OK(launch_topk(L.score, batch, N, k, S_out, stream));
+    S = S_out;
+  }
+  HIP_OK(launch_gather_feedback(Mh, batch, N, m, ld, stride, S, k, mu, (uint16_t*)L.X, m, stream));
+  HIP_OK(launch_selected_sumsq(L.sumsq, S, batch, k, N, sch.eps, L.s, stream));
   void* O = O_out ? O_out : L.O;
   const long long km = (long long)k * m;
   // one batched Gram NS over the selected k x m submatrices of every entry
@@ -597,9 +603,17 @@ int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m,
   c.s_given = L.s;
   if ((st = check_ns(c))) return st;
   if ((st = run_ns(c, true))) return st;
-  HIP_OK(launch_apply_update((uint16_t*)W, batch, N, m, ld, stride, S_out, k, O, GNS_BF16, m, lr, weight_decay,
-                             stream));
+  HIP_OK(launch_apply_update((uint16_t*)W, batch, N, m, ld, stride, S, k, O, GNS_BF16, m, lr, weight_decay, stream));
   return GNS_OK;
+}
+
+int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m, long long ld, long long stride, int k,
+                       float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
+                       const gns_schedule* sched, int* S_out, void* O_out, void* workspace, size_t ws_bytes,
+                       hipStream_t stream) {
+  if (!S_out) return GNS_ERR_INVALID_ARG;
+  return dion3_run(W, M, G, batch, N, m, ld, stride, k, lr, weight_decay, mu, score_norm, compute, sched, nullptr,
+                   S_out, O_out, workspace, ws_bytes, stream);
 }
 
 int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int k, float lr, float weight_decay,
@@ -607,6 +621,15 @@ int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int 
                void* workspace, size_t ws_bytes, hipStream_t stream) {
   return dion3_step_batched(W, M, G, 1, N, m, ld, (long long)N * ld, k, lr, weight_decay, mu, score_norm, compute,
                             sched, S_out, O_out, workspace, ws_bytes, stream);
+}
+
+int dion3_step_rows(void* W, void* M, const void* G, int N, int m, long long ld, const int* S, int k, float lr,
+                    float weight_decay, float mu, gns_dtype compute, const gns_schedule* sched, void* O_out,
+                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!S) return GNS_ERR_INVALID_ARG;
+  // the sums of squares of the rows (score_norm 2) give the submatrix's Frobenius norm
+  return dion3_run(W, M, G, 1, N, m, ld, (long long)N * ld, k, lr, weight_decay, mu, 2, compute, sched, S, nullptr,
+                   O_out, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

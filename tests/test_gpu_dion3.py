@@ -5,7 +5,9 @@ feedback on M, and the weight update given the same (seeded) O.  Within toleranc
 the orthogonalised submatrix O (relative Frobenius <= 2e-2 against float64 standard
 NS of the oracle's gathered rows) and the selected rows of W after a full step (they
 depend on O: elementwise within one bf16 rounding plus lr times O's tolerance);
-unselected rows of W are bit-exact.
+unselected rows of W are bit-exact.  The step on a caller-chosen row set (random
+selection) is held to the same bars, and to bitwise equality with the top-k step
+when given the top-k set.
 """
 import numpy as np
 import pytest
@@ -195,3 +197,80 @@ def test_dion3_step_batched_matches_oracle_and_single(gns_mod, wd):
         assert np.array_equal(bits(O1), Ob[b * k:(b + 1) * k])
         assert np.array_equal(bits(W1), Wb[b * N:(b + 1) * N])
         assert np.array_equal(bits(M1), Mb[b * N:(b + 1) * N])
+
+
+def _rows_tensor(S_np):
+    torch = __import__("torch")
+    return torch.from_numpy(np.asarray(S_np, dtype=np.int32)).cuda()
+
+
+def _bf16_empty(k, m):
+    torch = __import__("torch")
+    return torch.empty((k, m), dtype=torch.bfloat16, device="cuda")
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_dion3_step_rows_random_set(gns_mod, wd):
+    """A step on a random row set (the pages' alternative to top-k): M bit-exact, O
+    within 2e-2, W within O's tolerance and bit-exact on unselected rows."""
+    announce(f"dion3 step on a random row set 512x2048 wd={wd}")
+    w, g, m = synth.dion3_state(n=512, m=2048, seed=17)
+    S_np = np.sort(np.random.default_rng(18).choice(512, size=128, replace=False))
+    lr = 0.02
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    O = gns_mod.dion3_step_rows(W, M, G, _rows_tensor(S_np), lr, weight_decay=wd, mu=0.95, O=_bf16_empty(128, 2048))
+    w_ref, m_ref, O_ref = oracle.dion3_step_rows(w, m, g, S_np, lr, wd=wd, mu=0.95)
+    assert np.array_equal(bits(M), m_ref)
+    e = rel_fro(to_f64(O), O_ref)
+    print(f"O rel err {e:.3e}")
+    assert e <= 2e-2
+    wg = bits(W)
+    assert w_within_bound(wg, w_ref, lr, O_ref)
+    rest = np.setdiff1d(np.arange(512), S_np)
+    assert np.array_equal(wg[rest], w_ref[rest])
+
+
+def test_dion3_step_rows_on_topk_set_is_dion3_step(gns_mod):
+    """Given the set dion3_step picks, the caller-set step gives bitwise the same W, M, O."""
+    announce("dion3 step_rows on the top-k set 1024x4096")
+    w, g, m = synth.dion3_state(n=1024, m=4096, seed=19)
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    S, O = gns_mod.dion3_step(W, M, G, 256, 0.02, weight_decay=0.1, mu=0.95, score_norm=1, return_O=True)
+    W2, M2, G2 = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    O2 = gns_mod.dion3_step_rows(W2, M2, G2, S, 0.02, weight_decay=0.1, mu=0.95, O=_bf16_empty(256, 4096))
+    assert np.array_equal(bits(O), bits(O2))
+    assert np.array_equal(bits(W), bits(W2)) and np.array_equal(bits(M), bits(M2))
+
+
+def test_dion3_step_rows_index_out_of_range_is_a_zero_row(gns_mod):
+    """An index outside [0, N) reads as a zero row and updates nothing, so the step
+    equals the oracle's step on the valid indices (a zero row of X stays zero under
+    the iteration and does not change the Frobenius norm)."""
+    announce("dion3 step_rows with an out-of-range index 256x1024")
+    w, g, m = synth.dion3_state(n=256, m=1024, seed=20)
+    valid = np.sort(np.random.default_rng(21).choice(256, size=15, replace=False))
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    O = gns_mod.dion3_step_rows(W, M, G, _rows_tensor(np.append(valid, 256)), 0.02, mu=0.95, O=_bf16_empty(16, 1024))
+    w_ref, m_ref, O_ref = oracle.dion3_step_rows(w, m, g, valid, 0.02, wd=0.0, mu=0.95)
+    assert np.array_equal(bits(M), m_ref)
+    o = to_f64(O)
+    assert np.all(o[15] == 0)
+    assert rel_fro(o[:15], O_ref) <= 2e-2
+    rest = np.setdiff1d(np.arange(256), valid)
+    assert np.array_equal(bits(W)[rest], w[rest])
+
+
+@pytest.mark.timeout(600)
+def test_dion3_step_rows_full_size_random_set(gns_mod):
+    """The 8192 x 28672 state with 2048 random rows (f = 1/4): M bit-exact against the
+    oracle's accumulate + error feedback, unselected W rows untouched."""
+    announce("dion3 step_rows 8192x28672 random k=2048: generating inputs")
+    w, g, m = synth.dion3_state()
+    S_np = np.sort(np.random.default_rng(26).choice(8192, size=2048, replace=False))
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    announce("dion3 step_rows 8192x28672: GPU step")
+    gns_mod.dion3_step_rows(W, M, G, _rows_tensor(S_np), 0.02, mu=0.95)
+    announce("dion3 step_rows 8192x28672: oracle accumulate + error feedback")
+    assert np.array_equal(bits(M), error_feedback(accumulate(m, g), S_np, 0.95))
+    rest = np.setdiff1d(np.arange(8192), S_np)
+    assert np.array_equal(bits(W)[rest], w[rest])

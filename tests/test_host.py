@@ -109,6 +109,15 @@ def test_gemm_and_dion3_validation():
     assert L.dion3_step_batched(*bargs(2, 64 * 256, M=FAKE + 64 * 256 * 2)) == INVALID   # M overlaps W's 2nd entry
     assert L.dion3_step_batched(*bargs(2, 64 * 256, wsb=8)) == WS
     assert L.dion3_batched_workspace_size(2, 64, 256, 16, F16) > L.dion3_workspace_size(64, 256, 16, F16)
+    # dion3 on a caller-chosen row set: null S, k > N, k not a multiple of 8, short workspace, aliasing
+    rargs = lambda S=FAKE * 30, k=16, W=FAKE, wsb=1 << 40: (W, FAKE * 8, FAKE * 16, 64, 256, 256, S, k, 0.02, 0.0,
+                                                           0.95, F16, ctypes.byref(sched), None, FAKE * 40, wsb,
+                                                           None)
+    assert L.dion3_step_rows(*rargs(S=None)) == INVALID
+    assert L.dion3_step_rows(*rargs(k=72)) == INVALID
+    assert L.dion3_step_rows(*rargs(k=12)) == UNSUP
+    assert L.dion3_step_rows(*rargs(wsb=8)) == WS
+    assert L.dion3_step_rows(*rargs(W=FAKE * 8)) == INVALID                # W is M
     assert L.dion3_select_topk(FAKE, 10, 11, FAKE, None) == INVALID
     assert L.dion3_select_topk(FAKE, 10, 0, FAKE, None) == INVALID
 
