@@ -109,6 +109,8 @@ def main():
     # replayed is timed too (on ROCm the replay does not beat eager launches here)
     ms = timed_ms(lambda: gns.orthogonalize(X, out=out, compute=compute, schedule=sched),
                   args.steps, args.warmup)
+    per_call = per_call_ms(torch, stream, lambda: gns.orthogonalize(X, out=out, compute=compute, schedule=sched),
+                           max(20, min(args.steps, 200)))
     graphed = gns.graphed_orthogonalize(X, out=torch.empty_like(X), compute=compute, schedule=sched)
     ms_graph = timed_ms(graphed.replay, args.steps, args.warmup)
     mats_per_s = B / (ms * 1e-3)
@@ -148,6 +150,7 @@ def main():
         "tflops_issued": round(issued / (ms * 1e-3) / 1e12, 3),
         "pct_peak_issued": round(100 * issued / (ms * 1e-3) / 1e12 / PEAK_16BIT_TFLOPS, 3),
         "timing": "eager launches of the whole call on one stream (inputs resident in HBM)",
+        "per_call_ms": per_call,
         "graph_replay": {"ms_per_step": round(ms_graph, 5), "matrices_per_s": round(B / (ms_graph * 1e-3), 3)},
         "standard_ns_same_kernels": {"ms_per_step": round(ms_std, 5),
                                      "matrices_per_s": round(B / (ms_std * 1e-3), 3),
@@ -295,6 +298,43 @@ def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, wor
     return roof
 
 
+def per_call_ms(torch, stream, fn, n):
+    """HIP events around each of n calls on the launch stream (after the timed
+    region): median, 10th and 90th percentile in ms."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    pick = lambda q: round(t[min(len(t) - 1, int(q * (len(t) - 1) + 0.5))], 5)
+    return {"calls": n, "median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9)}
+
+
+def host_description():
+    """CPU model and the BLAS library numpy runs on (for the oracle baseline)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
+    return model, blas
+
+
 def cpu_baseline(st, w, seconds):
     """The float64 oracle (standard NS) on the host, on a bounded sample."""
     import numpy as np
@@ -312,7 +352,9 @@ def cpu_baseline(st, w, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or done >= 1000:
             break
+    model, blas = host_description()
     return {"value": round(done / el, 4), "unit": "matrices/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "blas": blas, "nproc": os.cpu_count(),
             "sample": f"{done} x one {w.n}x{w.m} matrix of the workload, float64 standard NS (numpy/OpenBLAS), "
                       f"{el:.1f} s"}
 

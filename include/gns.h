@@ -233,6 +233,20 @@ int dion3_step_rows(void* W, void* M, const void* G, int N, int m, long long ld,
                     const gns_schedule* sched, void* O_out, void* workspace, size_t ws_bytes,
                     hipStream_t stream);
 
+/* dion3_step with lr, weight decay and mu read from device memory when the step runs:
+ * lr_wd_mu is a device float[3] = {lr, weight_decay, mu}.  A step captured once in a
+ * HIP graph then follows a schedule that the caller writes into that buffer between
+ * replays, with no new capture [paper.rainbus.top 方法步骤详情 (4): the optimizer step
+ * captured in a CUDA graph].  Results are bitwise those of dion3_step with the same
+ * values.  The values are not checked (non-finite ones give non-finite W and M).  The
+ * update launch covers all N rows, since the host cannot see whether the weight decay
+ * is zero; without decay each unselected row returns at once.  lr_wd_mu must be 4-byte
+ * aligned (else GNS_ERR_UNSUPPORTED); other arguments and errors as dion3_step. */
+int dion3_step_dev_scalars(void* W, void* M, const void* G, int N, int m, long long ld, int k,
+                           const float* lr_wd_mu, int score_norm, gns_dtype compute,
+                           const gns_schedule* sched, int* S_out, void* O_out,
+                           void* workspace, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

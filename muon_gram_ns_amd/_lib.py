@@ -75,6 +75,7 @@ _sig("dion3_step", I, P, P, P, I, I, LL, I, F, F, F, I, I, ctypes.POINTER(Schedu
 _sig("dion3_batched_workspace_size", SZ, I, I, I, I, I)
 _sig("dion3_step_batched", I, P, P, P, I, I, I, LL, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
 _sig("dion3_step_rows", I, P, P, P, I, I, LL, P, I, F, F, F, I, ctypes.POINTER(Schedule), P, P, SZ, P)
+_sig("dion3_step_dev_scalars", I, P, P, P, I, I, LL, I, P, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
 
 
 def header_functions() -> list[str]:
@@ -410,6 +411,39 @@ def dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute=
                          O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
                          _stream(W.device)), "dion3_step")
     return (S, O) if (return_O or O is not None) else S
+
+
+def dion3_step_dev_scalars(W, M, G, k, scalars, score_norm=1, compute="f16", schedule=None, S=None, O=None,
+                           workspace=None):
+    """dion3_step with lr, weight decay and mu read on the device from `scalars`, a
+    float32 device tensor [lr, weight_decay, mu] (for steps replayed from a HIP graph
+    under a schedule).  Returns S (and O when O is given)."""
+    torch = _torch()
+    N, m, ld = _bf16_rows(W, "W")
+    _expect(M, "M", dtype=torch.bfloat16, shape=W.shape, device=W.device)
+    _expect(G, "G", dtype=torch.bfloat16, shape=W.shape, device=W.device)
+    if _rows(M)[2] != ld or _rows(G)[2] != ld:
+        raise ValueError("W, M, G must share the row stride")
+    _expect(scalars, "scalars", dtype=torch.float32, shape=(3,), device=W.device)
+    if not scalars.is_contiguous():
+        raise ValueError("scalars must be contiguous")
+    if S is None:
+        S = torch.empty(k, dtype=torch.int32, device=W.device)
+    _expect(S, "S", dtype=torch.int32, shape=(k,), device=W.device)
+    if O is not None:
+        _expect(O, "O", dtype=torch.bfloat16, shape=(k, m), device=W.device)
+        if not O.is_contiguous():
+            raise ValueError("O must be contiguous")
+    if not S.is_contiguous():
+        raise ValueError("S must be contiguous")
+    cdt = code_of(compute)
+    sched = schedule if schedule is not None else default_schedule()
+    ws = _workspace_arg(workspace, lib.dion3_workspace_size(N, m, k, cdt), W.device)
+    check(lib.dion3_step_dev_scalars(W.data_ptr(), M.data_ptr(), G.data_ptr(), N, m, ld, k, scalars.data_ptr(),
+                                     score_norm, cdt, ctypes.byref(sched), S.data_ptr(),
+                                     O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
+                                     _stream(W.device)), "dion3_step_dev_scalars")
+    return (S, O) if O is not None else S
 
 
 def dion3_step_rows(W, M, G, S, lr, weight_decay=0.0, mu=0.95, compute="f16", schedule=None, O=None,

@@ -235,9 +235,10 @@ hipError_t launch_topk(const double* score, int batch, int N, int k, int* S, hip
 
 // ---- X[r] = M[S[r]]; M[S[r]] <- bf16(mu * M[S[r]]) ----------------------------------
 __global__ void __launch_bounds__(kRowThreads)
-gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, long long stride, const int* S, int k, float mu,
-                       uint16_t* X, long long ldx) {
+gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, long long stride, const int* S, int k, float mu_host,
+                       const float* dev_scalars, uint16_t* X, long long ldx) {
   const int r = blockIdx.x, b = blockIdx.y;
+  const float mu = dev_scalars ? dev_scalars[2] : mu_host;
   const int src = S[(size_t)b * k + r];
   uint4* xr = reinterpret_cast<uint4*>(X + ((size_t)b * k + r) * ldx);
   if (src < 0 || src >= N) {           // precondition violated: a zero row of X, M untouched
@@ -260,11 +261,11 @@ gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, long long stride
 }
 
 hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long long ld, long long stride, const int* S,
-                                  int k, float mu, uint16_t* X, long long ldx, hipStream_t s) {
+                                  int k, float mu, const float* dev_scalars, uint16_t* X, long long ldx, hipStream_t s) {
   if (k <= 0 || batch <= 0) return hipSuccess;
   clear_stale_error();
   hipLaunchKernelGGL(gather_feedback_kernel, dim3(k, batch), dim3(kRowThreads), 0, s, M, N, m, ld, stride, S, k, mu,
-                     X, ldx);
+                     dev_scalars, X, ldx);
   return hipGetLastError();
 }
 
@@ -272,7 +273,9 @@ hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long lon
 template <bool O_F32>
 __global__ void __launch_bounds__(kRowThreads)
 apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, const int* S, int k, const void* O,
-                    long long ldo, float lr, float wd, int all_rows) {
+                    long long ldo, float lr_host, float wd_host, const float* dev_scalars, int all_rows) {
+  const float lr = dev_scalars ? dev_scalars[0] : lr_host;
+  const float wd = dev_scalars ? dev_scalars[1] : wd_host;
   const int d_over = blockIdx.x, b = blockIdx.y;
   W += (size_t)b * stride;
   S += (size_t)b * k;
@@ -294,6 +297,8 @@ apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, c
     row = S[oi];
     if (row < 0 || row >= N) return;
   }
+  // an unselected row without weight decay keeps its bits (d = 1 would not change it)
+  if (oi < 0 && wd == 0.0f) return;
   const float d = __fsub_rn(1.0f, __fmul_rn(lr, wd));
   uint4* wr = reinterpret_cast<uint4*>(W + (size_t)row * ld);
   for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
@@ -332,17 +337,20 @@ apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, c
 }
 
 hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long ld, long long stride, const int* S, int k,
-                               const void* O, gns_dtype o_dtype, long long ldo, float lr, float wd, hipStream_t s) {
-  const int all_rows = (wd != 0.0f) ? 1 : 0;
+                               const void* O, gns_dtype o_dtype, long long ldo, float lr, float wd,
+                               const float* dev_scalars, hipStream_t s) {
+  // with the weight decay on the device the host cannot tell whether unselected rows
+  // decay: cover all rows (each unselected row returns at once when wd == 0)
+  const int all_rows = (dev_scalars || wd != 0.0f) ? 1 : 0;
   const int blocks = all_rows ? N : k;
   if (blocks <= 0 || batch <= 0) return hipSuccess;
   clear_stale_error();
   if (o_dtype == GNS_F32)
     hipLaunchKernelGGL(apply_update_kernel<true>, dim3(blocks, batch), dim3(kRowThreads), 0, s, W, N, m, ld, stride, S,
-                       k, O, ldo, lr, wd, all_rows);
+                       k, O, ldo, lr, wd, dev_scalars, all_rows);
   else
     hipLaunchKernelGGL(apply_update_kernel<false>, dim3(blocks, batch), dim3(kRowThreads), 0, s, W, N, m, ld, stride,
-                       S, k, O, ldo, lr, wd, all_rows);
+                       S, k, O, ldo, lr, wd, dev_scalars, all_rows);
   return hipGetLastError();
 }
 

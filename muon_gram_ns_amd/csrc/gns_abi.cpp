@@ -511,7 +511,7 @@ int dion3_gather_feedback(void* M, int N, int m, long long ld, const int* S, int
   if (st) return st;
   if (!S || !X || k < 1 || k > N || ldx < m || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
   if (ldx % 8 || !aligned16(X)) return GNS_ERR_UNSUPPORTED;
-  HIP_OK(launch_gather_feedback((uint16_t*)M, 1, N, m, ld, 0, S, k, mu, (uint16_t*)X, ldx, stream));
+  HIP_OK(launch_gather_feedback((uint16_t*)M, 1, N, m, ld, 0, S, k, mu, nullptr, (uint16_t*)X, ldx, stream));
   return GNS_OK;
 }
 
@@ -522,7 +522,7 @@ int dion3_apply_update(void* W, int N, int m, long long ld, const int* S, int k,
   if (!S || !O || k < 1 || k > N || ldo < m || !std::isfinite(lr) || !std::isfinite(wd)) return GNS_ERR_INVALID_ARG;
   if (o_dtype != GNS_BF16 && o_dtype != GNS_F32) return GNS_ERR_UNSUPPORTED;
   if (ldo % 8 || !aligned16(O)) return GNS_ERR_UNSUPPORTED;
-  HIP_OK(launch_apply_update((uint16_t*)W, 1, N, m, ld, 0, S, k, O, o_dtype, ldo, lr, wd, stream));
+  HIP_OK(launch_apply_update((uint16_t*)W, 1, N, m, ld, 0, S, k, O, o_dtype, ldo, lr, wd, nullptr, stream));
   return GNS_OK;
 }
 
@@ -559,7 +559,7 @@ size_t dion3_workspace_size(int N, int m, int k, gns_dtype compute) {
 static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, long long ld, long long stride, int k,
                      float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
                      const gns_schedule* sched, const int* S_in, int* S_out, void* O_out, void* workspace,
-                     size_t ws_bytes, hipStream_t stream) {
+                     size_t ws_bytes, hipStream_t stream, const float* dev_scalars = nullptr) {
   if (batch < 0) return GNS_ERR_INVALID_ARG;
   if (batch == 0) return GNS_OK;
   int st = check_dion3_matrix(W, N, m, ld);
@@ -593,7 +593,7 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
     HIP_OK(launch_topk(L.score, batch, N, k, S_out, stream));
     S = S_out;
   }
-  HIP_OK(launch_gather_feedback(Mh, batch, N, m, ld, stride, S, k, mu, (uint16_t*)L.X, m, stream));
+  HIP_OK(launch_gather_feedback(Mh, batch, N, m, ld, stride, S, k, mu, dev_scalars, (uint16_t*)L.X, m, stream));
   HIP_OK(launch_selected_sumsq(L.sumsq, S, batch, k, N, sch.eps, L.s, stream));
   void* O = O_out ? O_out : L.O;
   const long long km = (long long)k * m;
@@ -603,7 +603,8 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
   c.s_given = L.s;
   if ((st = check_ns(c))) return st;
   if ((st = run_ns(c, true))) return st;
-  HIP_OK(launch_apply_update((uint16_t*)W, batch, N, m, ld, stride, S, k, O, GNS_BF16, m, lr, weight_decay, stream));
+  HIP_OK(launch_apply_update((uint16_t*)W, batch, N, m, ld, stride, S, k, O, GNS_BF16, m, lr, weight_decay,
+                             dev_scalars, stream));
   return GNS_OK;
 }
 
@@ -621,6 +622,16 @@ int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int 
                void* workspace, size_t ws_bytes, hipStream_t stream) {
   return dion3_step_batched(W, M, G, 1, N, m, ld, (long long)N * ld, k, lr, weight_decay, mu, score_norm, compute,
                             sched, S_out, O_out, workspace, ws_bytes, stream);
+}
+
+int dion3_step_dev_scalars(void* W, void* M, const void* G, int N, int m, long long ld, int k,
+                           const float* lr_wd_mu, int score_norm, gns_dtype compute, const gns_schedule* sched,
+                           int* S_out, void* O_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!S_out || !lr_wd_mu) return GNS_ERR_INVALID_ARG;
+  if ((uintptr_t)lr_wd_mu & 3u) return GNS_ERR_UNSUPPORTED;
+  // the host scalars are placeholders (finite, as checked); the kernels read the device values
+  return dion3_run(W, M, G, 1, N, m, ld, (long long)N * ld, k, 0.0f, 0.0f, 0.0f, score_norm, compute, sched,
+                   nullptr, S_out, O_out, workspace, ws_bytes, stream, lr_wd_mu);
 }
 
 int dion3_step_rows(void* W, void* M, const void* G, int N, int m, long long ld, const int* S, int k, float lr,

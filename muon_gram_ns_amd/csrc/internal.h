@@ -84,10 +84,13 @@ hipError_t launch_transpose(const void* X, gns_dtype dt, long long ldx, long lon
 hipError_t launch_accumulate_score(uint16_t* M, const uint16_t* G, int batch, int N, int m, long long ld,
                                    long long stride, int score_norm, double* score, double* sumsq, hipStream_t s);
 hipError_t launch_topk(const double* score, int batch, int N, int k, int* S, hipStream_t s);
+// dev_scalars (nullable): device float[3] = {lr, wd, mu} read when the kernel runs,
+// replacing the host values.
 hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long long ld, long long stride, const int* S,
-                                  int k, float mu, uint16_t* X, long long ldx, hipStream_t s);
+                                  int k, float mu, const float* dev_scalars, uint16_t* X, long long ldx, hipStream_t s);
 hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long ld, long long stride, const int* S, int k,
-                               const void* O, gns_dtype o_dtype, long long ldo, float lr, float wd, hipStream_t s);
+                               const void* O, gns_dtype o_dtype, long long ldo, float lr, float wd,
+                               const float* dev_scalars, hipStream_t s);
 // s[b] = 1 / (sqrt(sum_i sumsq[b][S[b][i]]) + eps): the Frobenius scale of the rows S.
 hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int batch, int k, int N, float eps,
                                  float* s_out, hipStream_t s);

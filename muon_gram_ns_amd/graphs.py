@@ -66,9 +66,13 @@ def graphed_newton_schulz(X, out=None, compute="f16", schedule=None) -> Graphed:
 
 
 def graphed_dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute="f16",
-                       schedule=None, return_O=False) -> Graphed:
+                       schedule=None, return_O=False, device_scalars=False) -> Graphed:
     """One Dion3 step on W, M (in place) and G, captured; each replay() runs one more
-    step on the buffers' current contents and returns S (and O)."""
+    step on the buffers' current contents and returns S (and O).
+
+    device_scalars=True captures the step that reads lr, weight decay and mu from a
+    device tensor the object owns (`scalars`); set_scalars() rewrites it between
+    replays, so one capture follows a learning-rate schedule."""
     torch = _lib._torch()
     N, m, _ = _lib._rows(W)
     S = torch.empty(k, dtype=torch.int32, device=W.device)
@@ -76,8 +80,14 @@ def graphed_dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, 
     ws = torch.empty(max(int(_lib.lib.dion3_workspace_size(N, m, k, _lib.code_of(compute))), 256),
                      dtype=torch.uint8, device=W.device)
     sched = schedule if schedule is not None else _lib.default_schedule()
-    fn = (lambda: _lib.dion3_step(W, M, G, k, lr, weight_decay, mu, score_norm, compute, sched, return_O,
-                                  S=S, O=O, workspace=ws))
+    scalars = None
+    if device_scalars:
+        scalars = torch.tensor([lr, weight_decay, mu], dtype=torch.float32, device=W.device)
+        fn = (lambda: _lib.dion3_step_dev_scalars(W, M, G, k, scalars, score_norm, compute, sched, S=S, O=O,
+                                                  workspace=ws))
+    else:
+        fn = (lambda: _lib.dion3_step(W, M, G, k, lr, weight_decay, mu, score_norm, compute, sched, return_O,
+                                      S=S, O=O, workspace=ws))
     # the warm-up calls run real steps (the capture itself executes nothing), so the
     # caller's W and M are saved before and restored after them
     saved = (W.clone(), M.clone())
@@ -85,5 +95,13 @@ def graphed_dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, 
     W.copy_(saved[0])
     M.copy_(saved[1])
     torch.cuda.synchronize()
-    g.W, g.M, g.G, g.S, g.O, g.workspace, g.schedule = W, M, G, S, O, ws, sched
+    g.W, g.M, g.G, g.S, g.O, g.workspace, g.schedule, g.scalars = W, M, G, S, O, ws, sched, scalars
+
+    def set_scalars(lr, weight_decay, mu):
+        """Values the next replays read (device_scalars=True only)."""
+        if g.scalars is None:
+            raise ValueError("captured with host scalars: capture with device_scalars=True")
+        g.scalars.copy_(torch.tensor([lr, weight_decay, mu], dtype=torch.float32))
+
+    g.set_scalars = set_scalars
     return g

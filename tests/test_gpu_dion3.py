@@ -274,3 +274,20 @@ def test_dion3_step_rows_full_size_random_set(gns_mod):
     assert np.array_equal(bits(M), error_feedback(accumulate(m, g), S_np, 0.95))
     rest = np.setdiff1d(np.arange(8192), S_np)
     assert np.array_equal(bits(W)[rest], w[rest])
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_dion3_step_dev_scalars_equals_host_scalars(gns_mod, wd):
+    """lr, weight decay and mu read from device memory give bitwise the step with the
+    same host values (S, O, W, M)."""
+    announce(f"dion3 step with device scalars 512x2048 wd={wd}")
+    torch = __import__("torch")
+    w, g, m = synth.dion3_state(n=512, m=2048, seed=27)
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    S, O = gns_mod.dion3_step(W, M, G, 128, 0.02, weight_decay=wd, mu=0.9, score_norm=2, return_O=True)
+    W2, M2, G2 = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    sc = torch.tensor([0.02, wd, 0.9], dtype=torch.float32, device="cuda")
+    S2, O2 = gns_mod.dion3_step_dev_scalars(W2, M2, G2, 128, sc, score_norm=2, O=_bf16_empty(128, 2048))
+    assert np.array_equal(S.cpu().numpy(), S2.cpu().numpy())
+    assert np.array_equal(bits(O), bits(O2))
+    assert np.array_equal(bits(W), bits(W2)) and np.array_equal(bits(M), bits(M2))

@@ -84,3 +84,30 @@ def test_graphed_dion3_steps_match_eager_steps(gns_mod):
         assert np.array_equal(S.cpu().numpy(), Se[i])
     assert np.array_equal(bits(Wg), bits(We))
     assert np.array_equal(bits(Mg), bits(Me))
+
+
+def test_graphed_dion3_with_device_scalars_follows_a_schedule(gns_mod):
+    """One capture with lr, weight decay and mu in device memory; three replays with a
+    different (lr, wd, mu) written before each equal three eager dion3_step calls with
+    those host values, bitwise (W, M and S)."""
+    import torch
+    announce("graphed dion3 with device scalars")
+    w, g0, m = synth.dion3_state(n=512, m=2048, seed=42)
+    grads = [synth.dion3_state(n=512, m=2048, seed=60 + i)[1] for i in range(3)]
+    sched = [(0.02, 0.1, 0.95), (0.015, 0.0, 0.9), (0.01, 0.05, 0.95)]
+    tb = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    k = 128
+    We, Me = tb(w), tb(m)
+    Se = []
+    for gr, (lr, wd, mu) in zip(grads, sched):
+        Se.append(gns_mod.dion3_step(We, Me, tb(gr), k, lr, wd, mu, score_norm=1).cpu().numpy())
+    Wg, Mg, Gg = tb(w), tb(m), tb(g0)
+    step = gns_mod.graphed_dion3_step(Wg, Mg, Gg, k, 0.5, 0.5, 0.5, score_norm=1, device_scalars=True)
+    for i, (gr, (lr, wd, mu)) in enumerate(zip(grads, sched)):
+        Gg.copy_(tb(gr))
+        step.set_scalars(lr, wd, mu)
+        S = step.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(S.cpu().numpy(), Se[i])
+    assert np.array_equal(bits(Wg), bits(We))
+    assert np.array_equal(bits(Mg), bits(Me))

@@ -118,6 +118,12 @@ def test_gemm_and_dion3_validation():
     assert L.dion3_step_rows(*rargs(k=12)) == UNSUP
     assert L.dion3_step_rows(*rargs(wsb=8)) == WS
     assert L.dion3_step_rows(*rargs(W=FAKE * 8)) == INVALID                # W is M
+    # dion3 with device scalars: null scalars, misaligned scalars, null S
+    dargs = lambda sc=FAKE * 50, S=FAKE * 30: (FAKE, FAKE * 8, FAKE * 16, 64, 256, 256, 16, sc, 1, F16,
+                                              ctypes.byref(sched), S, None, FAKE * 40, 1 << 40, None)
+    assert L.dion3_step_dev_scalars(*dargs(sc=None)) == INVALID
+    assert L.dion3_step_dev_scalars(*dargs(sc=FAKE * 50 + 2)) == UNSUP
+    assert L.dion3_step_dev_scalars(*dargs(S=None)) == INVALID
     assert L.dion3_select_topk(FAKE, 10, 11, FAKE, None) == INVALID
     assert L.dion3_select_topk(FAKE, 10, 0, FAKE, None) == INVALID
 
