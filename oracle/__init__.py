@@ -33,5 +33,5 @@ from .newton_schulz import (  # noqa: F401
 from .gemm import symm_gemm_ref, rect_gemm_ref  # noqa: F401
 from .dion3 import (  # noqa: F401
     k_from_fraction, accumulate, row_scores, select_topk, gather_rows, error_feedback, weight_update,
-    dion3_step, dion3_step_rows,
+    dion3_step, dion3_step_rows, dion3_step_cols,
 )

@@ -25,7 +25,8 @@ Parity status: select_topk pinned by brute force; accumulate / error_feedback /
 weight_update pinned by their bit-level definitions and invariants; dion3_step
 pinned by the f = 1 == Muon identity and the error-feedback invariants;
 dion3_step_rows pinned by its invariants, by the all-rows case and by equality with
-dion3_step on the top-k set.
+dion3_step on the top-k set; dion3_step_cols pinned by column-norm selection, its
+column invariants and the Newton-Schulz oracle on the gathered columns.
 """
 from __future__ import annotations
 
@@ -157,3 +158,23 @@ def dion3_step_rows(w, m, g, S, lr, wd=0.0, mu=0.95, steps=5, abc=JORDAN_ABC, ep
     ortho = orthogonalize or (lambda x: newton_schulz(x, steps, abc, eps))
     m1 = accumulate(m, g)
     return _update_rows(w, m1, S, lr, wd, mu, ortho)
+
+
+def dion3_step_cols(w, m, g, k, lr, wd=0.0, mu=0.95, norm="l1", steps=5, abc=JORDAN_ABC, eps=EPS,
+                    orthogonalize=None):
+    """One Dion3 step that subsamples columns instead of rows.
+
+    The pages let the fraction f select rows or columns ("Dion3：全栈正交更新",
+    paper.rainbus.top, 核心方法 and 方法步骤详情 (3); "Dion3: Full-Stack Orthogonal
+    Updates", m.montaan.com).  Selecting the k columns of largest norm of M, orthogonalising
+    M[:, S], updating W[:, S] and decaying M[:, S] is the row rule applied to the
+    transposes, which is how it is written here.  w, m, g: uint16 bf16 bit patterns,
+    N x m.  Returns (W', M', S, O) with O the k x N transpose of the orthogonalised
+    N x k submatrix (row j is the update of column S[j]).
+
+    Parity: pinned by column-norm selection against brute force, by the invariants on
+    the unselected and selected columns, and by O against the Newton-Schulz oracle on
+    the gathered columns."""
+    T = lambda a: np.ascontiguousarray(np.asarray(a).T)
+    wt, mt, S, O = dion3_step(T(w), T(m), T(g), k, lr, wd, mu, norm, steps, abc, eps, "bf16", orthogonalize)
+    return T(wt), T(mt), S, O

@@ -190,3 +190,27 @@ def test_dion3_step_rows_rejects_bad_sets(S):
     w, g, m = synth.dion3_state(n=8, m=16, seed=25)
     with pytest.raises(ValueError):
         oracle.dion3_step_rows(w, m, g, S, lr=0.01)
+
+
+# ---- column selection (the pages' "rows or columns") ----
+
+@pytest.mark.parametrize("norm", ["l1", "l2"])
+def test_dion3_step_cols_selects_columns_by_norm_and_keeps_invariants(norm):
+    w, g, m = synth.dion3_state(n=96, m=40, seed=31)       # tall: 96 rows, 40 columns
+    k = k_from_fraction(0.25, 40)
+    w2, m2, S, O = oracle.dion3_step_cols(w, m, g, k, lr=0.02, wd=0.0, mu=0.95, norm=norm)
+    m1 = accumulate(m, g)
+    x = bf16_to_f64(m1)
+    col = np.abs(x).sum(0) if norm == "l1" else (x * x).sum(0)
+    rest = np.setdiff1d(np.arange(40), S)
+    assert len(S) == k and np.all(np.diff(S) > 0)
+    assert col[S].min() > col[rest].max()                     # the k columns of largest norm
+    assert np.array_equal(m2[:, rest], m1[:, rest])          # unselected columns: M + G only
+    assert np.array_equal(w2[:, rest], w[:, rest])           # wd = 0: unselected W columns untouched
+    ref_m = (torch.tensor(np.float32(0.95)) * tbf(m1[:, S]).float()).to(torch.bfloat16)
+    assert np.array_equal(m2[:, S], bits_of(ref_m))
+    # O (k x N) is the transpose of the orthogonalised N x k column submatrix
+    assert np.allclose(O.T, newton_schulz(x[:, S]), rtol=0, atol=1e-14)
+    o_b = tbf(f64_to_bf16_rne(O.T)).float()
+    ref_w = (tbf(w[:, S]).float() - torch.tensor(np.float32(0.02)) * o_b).to(torch.bfloat16)
+    assert np.array_equal(w2[:, S], bits_of(ref_w))
