@@ -416,6 +416,35 @@ def megabatch_dion3(gns, torch, args, B=16, N=2048, m=8192, f=0.25):
             "speedup": round(res["loop"] / res["batched"], 3)}
 
 
+def tall_columns_vs_rows(gns, torch, args, N=28672, m=8192, f=0.25):
+    """The tall transpose of the Dion3 state (28672 x 8192): one step selecting
+    k = f m columns (dion3_step_cols, a 28672 x 2048 submatrix) against one step
+    selecting k = f N rows (dion3_step, a 7168 x 8192 submatrix)."""
+    gen = torch.Generator(device="cuda").manual_seed(88)
+    mk = lambda: (torch.randn(N, m, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    W, G, M = mk(), mk(), mk()
+    kc, kr = math.ceil(f * m), math.ceil(f * N)
+    lr = 0.01 / f ** 0.5
+    cols = lambda: gns.dion3_step_cols(W, M, G, kc, lr, 0.0, 0.95, score_norm=2, compute=args.compute)
+    rows = lambda: gns.dion3_step(W, M, G, kr, lr, 0.0, 0.95, score_norm=2, compute=args.compute)
+    res = {}
+    for name, fn in (("columns", cols), ("rows", rows)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        reps = max(3, args.steps // 10)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) / reps
+    del W, G, M
+    torch.cuda.empty_cache()
+    return {"state": f"{N}x{m} bf16", "f": f, "k_columns": kc, "k_rows": kr,
+            "columns_ms": round(res["columns"] * 1e3, 4), "rows_ms": round(res["rows"] * 1e3, 4),
+            "columns_speedup": round(res["rows"] / res["columns"], 3)}
+
+
 def bench_dion3(args, w):
     """Dion3 step on the 8192 x 28672 workload at f = 1/4 and 1/8 (l2 row scores).
     Inputs are drawn on the device from a seeded generator with the workload's
@@ -495,6 +524,7 @@ def bench_dion3(args, w):
     del W, G, M
     torch.cuda.empty_cache()
     mega = megabatch_dion3(gns, torch, args)
+    tall = tall_columns_vs_rows(gns, torch, args)
     print(json.dumps({"metric": "Dion3 steps/s", "value": round(1e3 / ms, 3), "unit": "steps/s", "n_gpus": 1,
                       "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
                       "scaling": "weak", "vs_baseline": None, "dtype": args.compute, "data": "synthetic",
@@ -502,7 +532,7 @@ def bench_dion3(args, w):
                       "config": {"workload": w.name, "N": N, "m": m, "score": "l2", "mu": 0.95, "wd": 0.0,
                                  "fractions": res},
                       "hbm_pieces_k2048": pieces, "hbm_reference_same_tensors": reference,
-                      "megabatch_f_quarter": mega,
+                      "megabatch_f_quarter": mega, "tall_state_columns_vs_rows": tall,
                       "roofline": roof, "cpu_baseline": None}), flush=True)
 
 

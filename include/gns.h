@@ -233,6 +233,26 @@ int dion3_step_rows(void* W, void* M, const void* G, int N, int m, long long ld,
                     const gns_schedule* sched, void* O_out, void* workspace, size_t ws_bytes,
                     hipStream_t stream);
 
+/* Workspace bytes needed by dion3_step_cols. */
+size_t dion3_cols_workspace_size(int N, int m, int k, gns_dtype compute);
+
+/* One Dion3 step that subsamples columns instead of rows (in place on W and M): the
+ * pages let f select rows or columns [paper.rainbus.top 核心方法 and 方法步骤详情 (3);
+ * m.montaan.com summary].  M <- M + G; S = the k columns of largest score (score_norm
+ * as in dion3_step); X = M[:, S] (N x k); O = GramNS(X); W <- decay + update of the
+ * columns S; M[:, S] <- mu M[:, S].  For a tall state (N > m) this keeps the
+ * orthogonalised submatrix wide: 28672 x 8192 at f = 1/4 gives a 28672 x 2048
+ * submatrix, where row selection would give 7168 x 8192.
+ * Computed as the row step on the transposes W^T, M^T, G^T held in the workspace,
+ * with W and M transposed back.  S_out: device int32[k], ascending column indices.
+ * O_out: nullable device bf16 [k][N]: row j is the update of column S[j] (the
+ * transpose of the orthogonalised N x k submatrix).  1 <= k <= m, k and N multiples of
+ * 8; W, M, G must not overlap; other errors as dion3_step. */
+int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld, int k,
+                    float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
+                    const gns_schedule* sched, int* S_out, void* O_out,
+                    void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* dion3_step with lr, weight decay and mu read from device memory when the step runs:
  * lr_wd_mu is a device float[3] = {lr, weight_decay, mu}.  A step captured once in a
  * HIP graph then follows a schedule that the caller writes into that buffer between

@@ -76,6 +76,8 @@ _sig("dion3_batched_workspace_size", SZ, I, I, I, I, I)
 _sig("dion3_step_batched", I, P, P, P, I, I, I, LL, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
 _sig("dion3_step_rows", I, P, P, P, I, I, LL, P, I, F, F, F, I, ctypes.POINTER(Schedule), P, P, SZ, P)
 _sig("dion3_step_dev_scalars", I, P, P, P, I, I, LL, I, P, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
+_sig("dion3_cols_workspace_size", SZ, I, I, I, I)
+_sig("dion3_step_cols", I, P, P, P, I, I, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
 
 
 def header_functions() -> list[str]:
@@ -411,6 +413,38 @@ def dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute=
                          O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
                          _stream(W.device)), "dion3_step")
     return (S, O) if (return_O or O is not None) else S
+
+
+def dion3_step_cols(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute="f16", schedule=None,
+                    return_O=False, S=None, O=None, workspace=None):
+    """One Dion3 step on the k columns of largest score of the [N, m] bf16 state (in
+    place on W and M).  Returns S ([k] int32, ascending column indices) and, when
+    return_O or O is given, O ([k, N] bf16: row j is the update of column S[j])."""
+    torch = _torch()
+    N, m, ld = _bf16_rows(W, "W")
+    _expect(M, "M", dtype=torch.bfloat16, shape=W.shape, device=W.device)
+    _expect(G, "G", dtype=torch.bfloat16, shape=W.shape, device=W.device)
+    if _rows(M)[2] != ld or _rows(G)[2] != ld:
+        raise ValueError("W, M, G must share the row stride")
+    if S is None:
+        S = torch.empty(k, dtype=torch.int32, device=W.device)
+    _expect(S, "S", dtype=torch.int32, shape=(k,), device=W.device)
+    if return_O and O is None:
+        O = torch.empty((k, N), dtype=torch.bfloat16, device=W.device)
+    if O is not None:
+        _expect(O, "O", dtype=torch.bfloat16, shape=(k, N), device=W.device)
+        if not O.is_contiguous():
+            raise ValueError("O must be contiguous")
+    if not S.is_contiguous():
+        raise ValueError("S must be contiguous")
+    cdt = code_of(compute)
+    sched = schedule if schedule is not None else default_schedule()
+    ws = _workspace_arg(workspace, lib.dion3_cols_workspace_size(N, m, k, cdt), W.device)
+    check(lib.dion3_step_cols(W.data_ptr(), M.data_ptr(), G.data_ptr(), N, m, ld, k, lr, weight_decay, mu,
+                              score_norm, cdt, ctypes.byref(sched), S.data_ptr(),
+                              O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
+                              _stream(W.device)), "dion3_step_cols")
+    return (S, O) if O is not None else S
 
 
 def dion3_step_dev_scalars(W, M, G, k, scalars, score_norm=1, compute="f16", schedule=None, S=None, O=None,

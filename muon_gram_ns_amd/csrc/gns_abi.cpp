@@ -634,6 +634,65 @@ int dion3_step_dev_scalars(void* W, void* M, const void* G, int N, int m, long l
                    nullptr, S_out, O_out, workspace, ws_bytes, stream, lr_wd_mu);
 }
 
+// Column selection runs the row step on the transposes: W^T, M^T, G^T (each m x N,
+// row stride N) in the workspace, then the row step's own workspace.
+struct Dion3ColsLayout {
+  void *Wt, *Mt, *Gt, *inner;
+  size_t inner_bytes, bytes;
+};
+
+static Dion3ColsLayout dion3_cols_layout(void* base, int N, int m, int k, gns_dtype cdt) {
+  Carver c{reinterpret_cast<uint8_t*>(base), 0};
+  Dion3ColsLayout L{};
+  const size_t bytes = (size_t)N * m * 2;
+  L.Wt = c.take(bytes); L.Mt = c.take(bytes); L.Gt = c.take(bytes);
+  L.inner_bytes = dion3_layout(nullptr, 1, m, N, k, cdt).bytes;
+  L.inner = c.take(L.inner_bytes);
+  L.bytes = c.off;
+  return L;
+}
+
+size_t dion3_cols_workspace_size(int N, int m, int k, gns_dtype compute) {
+  if (N < 1 || m < 1 || k < 1 || !valid_dtype(compute)) return 0;
+  return dion3_cols_layout(nullptr, N, m, k, compute).bytes;
+}
+
+int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld, int k, float lr, float weight_decay,
+                    float mu, int score_norm, gns_dtype compute, const gns_schedule* sched, int* S_out, void* O_out,
+                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dion3_matrix(W, N, m, ld);
+  if (st) return st;
+  if ((st = check_dion3_matrix(M, N, m, ld))) return st;
+  if ((st = check_dion3_matrix(G, N, m, ld))) return st;
+  if (!S_out || k < 1 || k > m) return GNS_ERR_INVALID_ARG;
+  if (N % 8) return GNS_ERR_UNSUPPORTED;       // N is the row length of the transposes
+  const size_t span = ((size_t)(N - 1) * ld + m) * 2;
+  if (overlaps(W, span, M, span) || overlaps(W, span, G, span) || overlaps(M, span, G, span))
+    return GNS_ERR_INVALID_ARG;
+  if (!valid_dtype(compute)) return GNS_ERR_INVALID_ARG;
+  const Dion3ColsLayout L = dion3_cols_layout(workspace, N, m, k, compute);
+  if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
+  // the remaining argument checks are the row step's, run before anything is launched
+  gns_schedule sch;
+  if (sched) sch = *sched; else gns_default_schedule(&sch);
+  if ((st = check_schedule(sch))) return st;
+  if (score_norm != 1 && score_norm != 2) return GNS_ERR_INVALID_ARG;
+  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
+  if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
+  if (k % 8) return GNS_ERR_UNSUPPORTED;
+  if (O_out && !aligned16(O_out)) return GNS_ERR_UNSUPPORTED;
+  HIP_OK(launch_transpose(W, GNS_BF16, ld, 0, 1, N, m, L.Wt, N, 0, stream));
+  HIP_OK(launch_transpose(M, GNS_BF16, ld, 0, 1, N, m, L.Mt, N, 0, stream));
+  HIP_OK(launch_transpose(G, GNS_BF16, ld, 0, 1, N, m, L.Gt, N, 0, stream));
+  st = dion3_run(L.Wt, L.Mt, L.Gt, 1, m, N, N, (long long)m * N, k, lr, weight_decay, mu, score_norm, compute,
+                 &sch, nullptr, S_out, O_out, L.inner, L.inner_bytes, stream);
+  if (st) return st;
+  HIP_OK(launch_transpose(L.Wt, GNS_BF16, N, 0, 1, m, N, W, ld, 0, stream));
+  HIP_OK(launch_transpose(L.Mt, GNS_BF16, N, 0, 1, m, N, M, ld, 0, stream));
+  return GNS_OK;
+}
+
 int dion3_step_rows(void* W, void* M, const void* G, int N, int m, long long ld, const int* S, int k, float lr,
                     float weight_decay, float mu, gns_dtype compute, const gns_schedule* sched, void* O_out,
                     void* workspace, size_t ws_bytes, hipStream_t stream) {

@@ -291,3 +291,46 @@ def test_dion3_step_dev_scalars_equals_host_scalars(gns_mod, wd):
     assert np.array_equal(S.cpu().numpy(), S2.cpu().numpy())
     assert np.array_equal(bits(O), bits(O2))
     assert np.array_equal(bits(W), bits(W2)) and np.array_equal(bits(M), bits(M2))
+
+
+@pytest.mark.parametrize("norm,wd", [(1, 0.0), (2, 0.1)])
+def test_dion3_step_cols_matches_oracle(gns_mod, norm, wd):
+    """Column selection on a tall state: S and M bit-exact, O within 2e-2, W within O's
+    tolerance (bit-exact on unselected columns when wd = 0)."""
+    announce(f"dion3 column step 512x256 norm={norm} wd={wd}")
+    w, g, m = synth.dion3_state(n=512, m=256, seed=32)
+    k, lr = 64, 0.02
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    S, O = gns_mod.dion3_step_cols(W, M, G, k, lr, weight_decay=wd, mu=0.95, score_norm=norm, return_O=True)
+    w_ref, m_ref, S_ref, O_ref = oracle.dion3_step_cols(w, m, g, k, lr, wd=wd, mu=0.95,
+                                                        norm="l1" if norm == 1 else "l2")
+    assert np.array_equal(S.cpu().numpy(), S_ref)
+    assert np.array_equal(bits(M), m_ref)
+    e = rel_fro(to_f64(O), O_ref)
+    print(f"O rel err {e:.3e}")
+    assert e <= 2e-2
+    wg = bits(W)
+    assert w_within_bound(wg, w_ref, lr, O_ref)
+    if wd == 0.0:
+        rest = np.setdiff1d(np.arange(256), S_ref)
+        assert np.array_equal(wg[:, rest], w_ref[:, rest])
+
+
+@pytest.mark.timeout(900)
+def test_dion3_step_cols_full_size_tall(gns_mod):
+    """The 8192 x 28672 workload's transpose (a tall 28672 x 8192 state) with 2048
+    columns (f = 1/4, l2): S and M bit-exact, unselected W columns untouched."""
+    announce("dion3 column step 28672x8192 k=2048: generating inputs")
+    w, g, m = synth.dion3_state(n=28672, m=8192, seed=33)
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    announce("dion3 column step 28672x8192: GPU step")
+    S = gns_mod.dion3_step_cols(W, M, G, 2048, 0.02, mu=0.95, score_norm=2).cpu().numpy()
+    announce("dion3 column step 28672x8192: oracle accumulate and column scores")
+    m1 = accumulate(m, g)
+    S_ref = select_topk(row_scores(np.ascontiguousarray(m1.T), "l2"), 2048)
+    assert np.array_equal(S, S_ref)
+    announce("dion3 column step 28672x8192: comparing M and W")
+    m_ref = np.ascontiguousarray(error_feedback(np.ascontiguousarray(m1.T), S_ref, 0.95).T)
+    assert np.array_equal(bits(M), m_ref)
+    rest = np.setdiff1d(np.arange(8192), S_ref)
+    assert np.array_equal(bits(W)[:, rest], w[:, rest])

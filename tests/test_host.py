@@ -124,6 +124,13 @@ def test_gemm_and_dion3_validation():
     assert L.dion3_step_dev_scalars(*dargs(sc=None)) == INVALID
     assert L.dion3_step_dev_scalars(*dargs(sc=FAKE * 50 + 2)) == UNSUP
     assert L.dion3_step_dev_scalars(*dargs(S=None)) == INVALID
+    # dion3 on columns: k > m, N not a multiple of 8, short workspace
+    cargs = lambda k=16, N=64, wsb=1 << 40: (FAKE, FAKE * 8, FAKE * 16, N, 256, 256, k, 0.02, 0.0, 0.95, 1, F16,
+                                            ctypes.byref(sched), FAKE * 30, None, FAKE * 40, wsb, None)
+    assert L.dion3_step_cols(*cargs(k=264)) == INVALID
+    assert L.dion3_step_cols(*cargs(N=60)) == UNSUP
+    assert L.dion3_step_cols(*cargs(wsb=8)) == WS
+    assert L.dion3_cols_workspace_size(64, 256, 16, F16) > 3 * 64 * 256 * 2
     assert L.dion3_select_topk(FAKE, 10, 11, FAKE, None) == INVALID
     assert L.dion3_select_topk(FAKE, 10, 0, FAKE, None) == INVALID
 
