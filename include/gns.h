@@ -243,8 +243,9 @@ size_t dion3_cols_workspace_size(int N, int m, int k, gns_dtype compute);
  * columns S; M[:, S] <- mu M[:, S].  For a tall state (N > m) this keeps the
  * orthogonalised submatrix wide: 28672 x 8192 at f = 1/4 gives a 28672 x 2048
  * submatrix, where row selection would give 7168 x 8192.
- * Computed as the row step on the transposes W^T, M^T, G^T held in the workspace,
- * with W and M transposed back.  S_out: device int32[k], ascending column indices.
+ * The columns are scored, gathered (into the k x N transpose of the submatrix, with
+ * the error feedback applied in place) and updated in the state's own row-major
+ * layout.  S_out: device int32[k], ascending column indices.
  * O_out: nullable device bf16 [k][N]: row j is the update of column S[j] (the
  * transpose of the orthogonalised N x k submatrix).  1 <= k <= m, k and N multiples of
  * 8; W, M, G must not overlap; other errors as dion3_step. */

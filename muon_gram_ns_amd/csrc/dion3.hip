@@ -379,4 +379,237 @@ hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int batch, i
   return hipGetLastError();
 }
 
+// ---- column selection: scores, gather + error feedback, update, decay -------------
+// The same rule as the row kernels with the roles of rows and columns swapped: the
+// step subsamples columns of the row-major N x m state.  Tiles of 64 selected columns
+// x 64 rows go through LDS so that X^T (row j = column S[j]) and O (k x N) are read
+// and written in 16-byte row vectors, while a wave's 64 lanes touch the 64 selected
+// columns of one state row (ascending, so a few cache lines per access).
+constexpr int kColThreads = 256;
+constexpr int kColRowsPerPart = 128;   // rows summed into one partial column score
+constexpr int kColTile = 64;
+
+// M <- bf16(M + G) and, per column, fp64 sums over a block of kColRowsPerPart rows:
+// part_s[rb][col] (|x| or x^2 by score_norm) and part_q[rb][col] (x^2).  Thread =
+// one 16-byte chunk (8 columns); rows in ascending order, four loaded at a time.
+__global__ void __launch_bounds__(kColThreads)
+accumulate_colscore_kernel(uint16_t* M, const uint16_t* G, int N, int m, long long ld, int score_norm,
+                           double* part_s, double* part_q) {
+  const int c = blockIdx.x * kColThreads + threadIdx.x;
+  const int nch = m / 8;
+  if (c >= nch) return;
+  const int rb = blockIdx.y;
+  const int i0 = rb * kColRowsPerPart, i1 = min(N, i0 + kColRowsPerPart);
+  double s[8], q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = q[e] = 0.0;
+  constexpr int U = 4;
+  for (int ib = i0; ib < i1; ib += U) {
+    uint4 mv[U], gv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = ib + u;
+      if (i < i1) {
+        mv[u] = reinterpret_cast<const uint4*>(M + (size_t)i * ld)[c];
+        gv[u] = reinterpret_cast<const uint4*>(G + (size_t)i * ld)[c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = ib + u;
+      if (i >= i1) continue;
+      uint32_t* mw = reinterpret_cast<uint32_t*>(&mv[u]);
+      const uint32_t* gw = reinterpret_cast<const uint32_t*>(&gv[u]);
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        uint32_t out = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float a = bf16_bits_to_f32((mw[e2] >> (16 * h)) & 0xffffu);
+          const float g = bf16_bits_to_f32((gw[e2] >> (16 * h)) & 0xffffu);
+          const uint32_t nb = f32_to_bf16_bits(__fadd_rn(a, g));
+          out |= nb << (16 * h);
+          const double v = (double)bf16_bits_to_f32(nb);
+          const int e = 2 * e2 + h;
+          s[e] += (score_norm == 1) ? fabs(v) : v * v;
+          q[e] += v * v;
+        }
+        mw[e2] = out;
+      }
+      reinterpret_cast<uint4*>(M + (size_t)i * ld)[c] = mv[u];
+    }
+  }
+  double* ps = part_s + (size_t)rb * m + 8 * (size_t)c;
+  double* pq = part_q + (size_t)rb * m + 8 * (size_t)c;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ps[e] = s[e];
+    pq[e] = q[e];
+  }
+}
+
+// score[col], sumsq[col]: the partials of the row blocks added in block order
+__global__ void __launch_bounds__(kColThreads)
+reduce_colscore_kernel(const double* part_s, const double* part_q, int nparts, int m, double* score, double* sumsq) {
+  const int col = blockIdx.x * kColThreads + threadIdx.x;
+  if (col >= m) return;
+  double s = 0.0, q = 0.0;
+  for (int rb = 0; rb < nparts; ++rb) {
+    s += part_s[(size_t)rb * m + col];
+    q += part_q[(size_t)rb * m + col];
+  }
+  score[col] = s;
+  sumsq[col] = q;
+}
+
+// Xt[j, i] = M[i, S[j]] (Xt: k x N, row stride ldx) and M[i, S[j]] <- bf16(mu M[i, S[j]]).
+// An index S[j] outside [0, m) gives a zero row of Xt and touches M nowhere.
+__global__ void __launch_bounds__(kColThreads)
+gather_cols_feedback_kernel(uint16_t* M, int N, int m, long long ld, const int* S, int k, float mu,
+                            uint16_t* Xt, long long ldx) {
+  __shared__ __align__(16) uint16_t tile[kColTile][kColTile + 2];   // [j][i]; rows of 132 bytes
+  const int j0 = blockIdx.x * kColTile, i0 = blockIdx.y * kColTile;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = j0 + lane;
+  const int col = (j < k) ? S[j] : -1;
+  const bool ok = col >= 0 && col < m;
+  for (int r = w; r < kColTile; r += kColThreads / 64) {
+    const int i = i0 + r;
+    uint16_t x = 0;
+    if (ok && i < N) {
+      uint16_t* p = M + (size_t)i * ld + col;
+      x = *p;
+      *p = (uint16_t)f32_to_bf16_bits(__fmul_rn(mu, bf16_bits_to_f32(x)));
+    }
+    tile[lane][r] = x;
+  }
+  __syncthreads();
+  // row jr of the tile, 16 values from column 16 q: two 16-byte stores
+  const int jr = threadIdx.x >> 2, qd = threadIdx.x & 3;
+  if (j0 + jr >= k) return;
+  const uint32_t* t32 = reinterpret_cast<const uint32_t*>(&tile[jr][0]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int a = 16 * qd + 8 * h;                   // tile column (even: 4-byte aligned)
+    if (i0 + a >= N) continue;                       // N % 8 == 0: 8 values all in or all out
+    const uint4 v = make_uint4(t32[a / 2], t32[a / 2 + 1], t32[a / 2 + 2], t32[a / 2 + 3]);
+    *reinterpret_cast<uint4*>(Xt + (size_t)(j0 + jr) * ldx + i0 + a) = v;
+  }
+}
+
+// W[i, S[j]] <- bf16(fl32(d W) - fl32(lr O[j, i])), d = fl32(1 - fl32(lr wd)); O: k x N
+// (row stride ldo).  An index S[j] outside [0, m) updates nothing.
+__global__ void __launch_bounds__(kColThreads)
+update_cols_kernel(uint16_t* W, int N, int m, long long ld, const int* S, int k, const uint16_t* O, long long ldo,
+                   float lr, float wd) {
+  __shared__ __align__(16) uint16_t tile[kColTile][kColTile + 2];   // [j][i]
+  const int j0 = blockIdx.x * kColTile, i0 = blockIdx.y * kColTile;
+  {
+    const int jr = threadIdx.x >> 2, qd = threadIdx.x & 3;
+    uint32_t* t32 = reinterpret_cast<uint32_t*>(&tile[jr][0]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int a = 16 * qd + 8 * h;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (j0 + jr < k && i0 + a < N) v = *reinterpret_cast<const uint4*>(O + (size_t)(j0 + jr) * ldo + i0 + a);
+      t32[a / 2] = v.x; t32[a / 2 + 1] = v.y; t32[a / 2 + 2] = v.z; t32[a / 2 + 3] = v.w;
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = j0 + lane;
+  const int col = (j < k) ? S[j] : -1;
+  if (col < 0 || col >= m) return;
+  const float d = __fsub_rn(1.0f, __fmul_rn(lr, wd));
+  for (int r = w; r < kColTile; r += kColThreads / 64) {
+    const int i = i0 + r;
+    if (i >= N) break;
+    uint16_t* p = W + (size_t)i * ld + col;
+    const float x = bf16_bits_to_f32(*p);
+    const float o = bf16_bits_to_f32(tile[lane][r]);
+    *p = (uint16_t)f32_to_bf16_bits(__fsub_rn(__fmul_rn(d, x), __fmul_rn(lr, o)));
+  }
+}
+
+// mark[col] = 1 for the selected columns (after clear_marks): the decay pass skips them
+__global__ void __launch_bounds__(kColThreads) clear_marks_kernel(uint8_t* mark, int m) {
+  const int c = blockIdx.x * kColThreads + threadIdx.x;
+  if (c < m) mark[c] = 0;
+}
+__global__ void __launch_bounds__(kColThreads) set_marks_kernel(uint8_t* mark, int m, const int* S, int k) {
+  const int j = blockIdx.x * kColThreads + threadIdx.x;
+  if (j >= k) return;
+  const int col = S[j];
+  if (col >= 0 && col < m) mark[col] = 1;
+}
+
+// W[i, c] <- bf16(fl32(d W[i, c])) for every column c not marked (decoupled weight decay)
+__global__ void __launch_bounds__(kColThreads)
+decay_unmarked_kernel(uint16_t* W, int N, int m, long long ld, const uint8_t* mark, float lr, float wd) {
+  const int c = blockIdx.x * kColThreads + threadIdx.x;   // 16-byte chunk
+  if (c >= m / 8) return;
+  const float d = __fsub_rn(1.0f, __fmul_rn(lr, wd));
+  for (int i = blockIdx.y; i < N; i += gridDim.y) {
+    uint4* p = reinterpret_cast<uint4*>(W + (size_t)i * ld) + c;
+    uint4 v = *p;
+    uint32_t* vw = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      uint32_t out = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t bits = (vw[e2] >> (16 * h)) & 0xffffu;
+        const int col = 8 * c + 2 * e2 + h;
+        const uint32_t nb = mark[col] ? bits : f32_to_bf16_bits(__fmul_rn(d, bf16_bits_to_f32(bits)));
+        out |= nb << (16 * h);
+      }
+      vw[e2] = out;
+    }
+    *p = v;
+  }
+}
+
+size_t dion3_cols_partials(int N) { return (size_t)((N + kColRowsPerPart - 1) / kColRowsPerPart); }
+
+hipError_t launch_accumulate_colscore(uint16_t* M, const uint16_t* G, int N, int m, long long ld, int score_norm,
+                                      double* part_s, double* part_q, double* score, double* sumsq, hipStream_t s) {
+  if (N <= 0 || m <= 0) return hipSuccess;
+  const int nparts = (int)dion3_cols_partials(N);
+  clear_stale_error();
+  hipLaunchKernelGGL(accumulate_colscore_kernel, dim3((m / 8 + kColThreads - 1) / kColThreads, nparts),
+                     dim3(kColThreads), 0, s, M, G, N, m, ld, score_norm, part_s, part_q);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reduce_colscore_kernel, dim3((m + kColThreads - 1) / kColThreads), dim3(kColThreads), 0, s,
+                     part_s, part_q, nparts, m, score, sumsq);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_cols_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, float mu,
+                                       uint16_t* Xt, long long ldx, hipStream_t s) {
+  if (k <= 0 || N <= 0) return hipSuccess;
+  clear_stale_error();
+  hipLaunchKernelGGL(gather_cols_feedback_kernel, dim3((k + kColTile - 1) / kColTile, (N + kColTile - 1) / kColTile),
+                     dim3(kColThreads), 0, s, M, N, m, ld, S, k, mu, Xt, ldx);
+  return hipGetLastError();
+}
+
+hipError_t launch_update_cols(uint16_t* W, int N, int m, long long ld, const int* S, int k, const uint16_t* O,
+                              long long ldo, float lr, float wd, uint8_t* mark, hipStream_t s) {
+  if (k <= 0 || N <= 0) return hipSuccess;
+  clear_stale_error();
+  if (wd != 0.0f) {
+    hipLaunchKernelGGL(clear_marks_kernel, dim3((m + kColThreads - 1) / kColThreads), dim3(kColThreads), 0, s, mark, m);
+    hipLaunchKernelGGL(set_marks_kernel, dim3((k + kColThreads - 1) / kColThreads), dim3(kColThreads), 0, s, mark, m,
+                       S, k);
+    hipLaunchKernelGGL(decay_unmarked_kernel, dim3((m / 8 + kColThreads - 1) / kColThreads, std::min(N, 4096)),
+                       dim3(kColThreads), 0, s, W, N, m, ld, mark, lr, wd);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(update_cols_kernel, dim3((k + kColTile - 1) / kColTile, (N + kColTile - 1) / kColTile),
+                     dim3(kColThreads), 0, s, W, N, m, ld, S, k, O, ldo, lr, wd);
+  return hipGetLastError();
+}
+
 }  // namespace gns

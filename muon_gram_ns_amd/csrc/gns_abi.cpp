@@ -634,20 +634,31 @@ int dion3_step_dev_scalars(void* W, void* M, const void* G, int N, int m, long l
                    nullptr, S_out, O_out, workspace, ws_bytes, stream, lr_wd_mu);
 }
 
-// Column selection runs the row step on the transposes: W^T, M^T, G^T (each m x N,
-// row stride N) in the workspace, then the row step's own workspace.
+// Column selection workspace: partial column sums, the column scores and sums of
+// squares, the column marks (for the decay), the scale, X^T and O (k x N), then the
+// Gram NS workspace for the k x N submatrix.
 struct Dion3ColsLayout {
-  void *Wt, *Mt, *Gt, *inner;
-  size_t inner_bytes, bytes;
+  double *part_s, *part_q, *score, *sumsq;
+  uint8_t* mark;
+  float* s;
+  void *Xt, *O, *gns_ws;
+  size_t gns_bytes, bytes;
 };
 
 static Dion3ColsLayout dion3_cols_layout(void* base, int N, int m, int k, gns_dtype cdt) {
   Carver c{reinterpret_cast<uint8_t*>(base), 0};
   Dion3ColsLayout L{};
-  const size_t bytes = (size_t)N * m * 2;
-  L.Wt = c.take(bytes); L.Mt = c.take(bytes); L.Gt = c.take(bytes);
-  L.inner_bytes = dion3_layout(nullptr, 1, m, N, k, cdt).bytes;
-  L.inner = c.take(L.inner_bytes);
+  const size_t parts = dion3_cols_partials(N) * (size_t)m;
+  L.part_s = (double*)c.take(sizeof(double) * parts);
+  L.part_q = (double*)c.take(sizeof(double) * parts);
+  L.score = (double*)c.take(sizeof(double) * (size_t)m);
+  L.sumsq = (double*)c.take(sizeof(double) * (size_t)m);
+  L.mark = (uint8_t*)c.take((size_t)m);
+  L.s = (float*)c.take(sizeof(float));
+  L.Xt = c.take((size_t)k * N * 2);
+  L.O = c.take((size_t)k * N * 2);
+  L.gns_bytes = ns_workspace_bytes(1, k, N, cdt);
+  L.gns_ws = c.take(L.gns_bytes);
   L.bytes = c.off;
   return L;
 }
@@ -665,31 +676,38 @@ int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld,
   if ((st = check_dion3_matrix(M, N, m, ld))) return st;
   if ((st = check_dion3_matrix(G, N, m, ld))) return st;
   if (!S_out || k < 1 || k > m) return GNS_ERR_INVALID_ARG;
-  if (N % 8) return GNS_ERR_UNSUPPORTED;       // N is the row length of the transposes
+  if (score_norm != 1 && score_norm != 2) return GNS_ERR_INVALID_ARG;
+  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
+  if (!valid_dtype(compute)) return GNS_ERR_INVALID_ARG;
+  if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
+  if (N % 8 || k % 8) return GNS_ERR_UNSUPPORTED;   // N is the row length of X^T and O
+  if (O_out && !aligned16(O_out)) return GNS_ERR_UNSUPPORTED;
   const size_t span = ((size_t)(N - 1) * ld + m) * 2;
   if (overlaps(W, span, M, span) || overlaps(W, span, G, span) || overlaps(M, span, G, span))
     return GNS_ERR_INVALID_ARG;
-  if (!valid_dtype(compute)) return GNS_ERR_INVALID_ARG;
-  const Dion3ColsLayout L = dion3_cols_layout(workspace, N, m, k, compute);
-  if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
-  // the remaining argument checks are the row step's, run before anything is launched
   gns_schedule sch;
   if (sched) sch = *sched; else gns_default_schedule(&sch);
   if ((st = check_schedule(sch))) return st;
-  if (score_norm != 1 && score_norm != 2) return GNS_ERR_INVALID_ARG;
-  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
-  if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
-  if (k % 8) return GNS_ERR_UNSUPPORTED;
-  if (O_out && !aligned16(O_out)) return GNS_ERR_UNSUPPORTED;
-  HIP_OK(launch_transpose(W, GNS_BF16, ld, 0, 1, N, m, L.Wt, N, 0, stream));
-  HIP_OK(launch_transpose(M, GNS_BF16, ld, 0, 1, N, m, L.Mt, N, 0, stream));
-  HIP_OK(launch_transpose(G, GNS_BF16, ld, 0, 1, N, m, L.Gt, N, 0, stream));
-  st = dion3_run(L.Wt, L.Mt, L.Gt, 1, m, N, N, (long long)m * N, k, lr, weight_decay, mu, score_norm, compute,
-                 &sch, nullptr, S_out, O_out, L.inner, L.inner_bytes, stream);
-  if (st) return st;
-  HIP_OK(launch_transpose(L.Wt, GNS_BF16, N, 0, 1, m, N, W, ld, 0, stream));
-  HIP_OK(launch_transpose(L.Mt, GNS_BF16, N, 0, 1, m, N, M, ld, 0, stream));
+  const Dion3ColsLayout L = dion3_cols_layout(workspace, N, m, k, compute);
+  if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
+
+  uint16_t* Mh = (uint16_t*)M;
+  HIP_OK(launch_accumulate_colscore(Mh, (const uint16_t*)G, N, m, ld, score_norm, L.part_s, L.part_q, L.score,
+                                    L.sumsq, stream));
+  HIP_OK(launch_topk(L.score, 1, m, k, S_out, stream));
+  HIP_OK(launch_gather_cols_feedback(Mh, N, m, ld, S_out, k, mu, (uint16_t*)L.Xt, N, stream));
+  HIP_OK(launch_selected_sumsq(L.sumsq, S_out, 1, k, m, sch.eps, L.s, stream));
+  void* O = O_out ? O_out : L.O;
+  const long long kN = (long long)k * N;
+  // the k x N transpose of the selected columns: Gram NS iterates on its short side
+  NsCall c = make_call(L.Xt, GNS_BF16, N, kN, O, GNS_BF16, N, kN, 1, k, N, compute, &sch, L.gns_ws, L.gns_bytes,
+                       stream, nullptr);
+  c.s_given = L.s;
+  if ((st = check_ns(c))) return st;
+  if ((st = run_ns(c, true))) return st;
+  HIP_OK(launch_update_cols((uint16_t*)W, N, m, ld, S_out, k, (const uint16_t*)O, N, lr, weight_decay, L.mark,
+                            stream));
   return GNS_OK;
 }
 

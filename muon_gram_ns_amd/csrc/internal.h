@@ -95,4 +95,18 @@ hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long l
 hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int batch, int k, int N, float eps,
                                  float* s_out, hipStream_t s);
 
+// Column selection (dion3.hip): the state is N x m row-major; S holds column indices.
+// Partial column sums: dion3_cols_partials(N) blocks of m doubles each, for the score
+// and for the sum of squares.
+size_t dion3_cols_partials(int N);
+hipError_t launch_accumulate_colscore(uint16_t* M, const uint16_t* G, int N, int m, long long ld, int score_norm,
+                                      double* part_s, double* part_q, double* score, double* sumsq, hipStream_t s);
+// Xt (k x N, row stride ldx): row j = column S[j] of M; then M[:, S] <- bf16(mu M[:, S])
+hipError_t launch_gather_cols_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, float mu,
+                                       uint16_t* Xt, long long ldx, hipStream_t s);
+// W[:, S[j]] <- bf16(d W - lr O[j, :]^T); with wd != 0 every other column decays (mark:
+// m bytes of scratch)
+hipError_t launch_update_cols(uint16_t* W, int N, int m, long long ld, const int* S, int k, const uint16_t* O,
+                              long long ldo, float lr, float wd, uint8_t* mark, hipStream_t s);
+
 }  // namespace gns
