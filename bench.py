@@ -445,6 +445,28 @@ def tall_columns_vs_rows(gns, torch, args, N=28672, m=8192, f=0.25):
             "columns_speedup": round(res["rows"] / res["columns"], 3)}
 
 
+def dion3_cpu_baseline(w):
+    """The float64 oracle's Dion3 step (accumulate, l2 row scores, top-k, standard NS
+    on the selected rows, update, error feedback) on the workload's full seeded state
+    at f = 1/4: one step is the bounded sample (about half a minute of CPU work)."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    W, G, M = synth.dion3_state(n=w.n, m=w.m)
+    k = oracle.k_from_fraction(0.25, w.n)
+    t0 = time.perf_counter()
+    oracle.dion3_step(W, M, G, k, 0.01 / 0.25 ** 0.5, wd=0.0, mu=0.95, norm="l2")
+    el = time.perf_counter() - t0
+    model, blas = host_description()
+    return {"value": round(1.0 / el, 5), "unit": "steps/s", "cores": threads, "kind": "oracle", "cpu_model": model,
+            "blas": blas, "nproc": os.cpu_count(),
+            "sample": f"one full f = 1/4 step on the {w.n}x{w.m} seeded state (k = {k}), {el:.1f} s"}
+
+
 def bench_dion3(args, w):
     """Dion3 step on the 8192 x 28672 workload at f = 1/4 and 1/8 (l2 row scores).
     Inputs are drawn on the device from a seeded generator with the workload's
@@ -525,6 +547,7 @@ def bench_dion3(args, w):
     torch.cuda.empty_cache()
     mega = megabatch_dion3(gns, torch, args)
     tall = tall_columns_vs_rows(gns, torch, args)
+    cpu = None if args.no_cpu_baseline else dion3_cpu_baseline(w)
     print(json.dumps({"metric": "Dion3 steps/s", "value": round(1e3 / ms, 3), "unit": "steps/s", "n_gpus": 1,
                       "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
                       "scaling": "weak", "vs_baseline": None, "dtype": args.compute, "data": "synthetic",
@@ -533,7 +556,7 @@ def bench_dion3(args, w):
                                  "fractions": res},
                       "hbm_pieces_k2048": pieces, "hbm_reference_same_tensors": reference,
                       "megabatch_f_quarter": mega, "tall_state_columns_vs_rows": tall,
-                      "roofline": roof, "cpu_baseline": None}), flush=True)
+                      "roofline": roof, "cpu_baseline": cpu}), flush=True)
 
 
 if __name__ == "__main__":

@@ -39,6 +39,20 @@ __device__ __forceinline__ double block_sum_f64(double v, double* sh) {
 // four chunks' loads are issued before any is used (more bytes in flight per wave),
 // and the chunks are then summed in that same order, so each thread's fp64 sums do
 // not depend on the unrolling.
+// Streaming accesses of the state (each element read and written once per pass):
+// non-temporal loads and stores.  Measured on MI355X on the 8192 x 28672 bf16 state,
+// the accumulate pass goes from 5.2 to 5.8 TB/s with them (torch's in-place add on
+// the same tensors: 5.8 TB/s).
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt(const uint4& v, uint4* p) {
+  const u32x4_nt x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4_nt*>(p));
+}
+
 constexpr int kAccUnroll = 4;
 
 __device__ __forceinline__ uint4 accumulate_chunk(uint4 mv, const uint4& gv, int score_norm, double& acc_s,
@@ -80,14 +94,14 @@ accumulate_score_kernel(uint16_t* M, const uint16_t* G, int N, int m, long long 
     for (int u = 0; u < kAccUnroll; ++u) {
       const int c = c0 + u * kRowThreads;
       if (c < nch) {
-        mv[u] = mr[c];
-        gv[u] = gr[c];
+        mv[u] = load_nt(&mr[c]);
+        gv[u] = load_nt(&gr[c]);
       }
     }
 #pragma unroll
     for (int u = 0; u < kAccUnroll; ++u) {
       const int c = c0 + u * kRowThreads;
-      if (c < nch) mr[c] = accumulate_chunk(mv[u], gv[u], score_norm, acc_s, acc_q);
+      if (c < nch) store_nt(accumulate_chunk(mv[u], gv[u], score_norm, acc_s, acc_q), &mr[c]);
     }
   }
   const double ts = block_sum_f64(acc_s, sh);
@@ -247,7 +261,7 @@ gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, long long stride
   }
   uint4* mr = reinterpret_cast<uint4*>(M + (size_t)b * stride + (size_t)src * ld);
   for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
-    uint4 v = mr[c];
+    uint4 v = load_nt(&mr[c]);
     xr[c] = v;
     uint32_t* w = reinterpret_cast<uint32_t*>(&v);
 #pragma unroll
@@ -256,7 +270,7 @@ gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, long long stride
       const uint32_t hi = f32_to_bf16_bits(__fmul_rn(mu, bf16_bits_to_f32(w[i] >> 16)));
       w[i] = lo | (hi << 16);
     }
-    mr[c] = v;
+    store_nt(v, &mr[c]);
   }
 }
 
@@ -302,7 +316,7 @@ apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, c
   const float d = __fsub_rn(1.0f, __fmul_rn(lr, wd));
   uint4* wr = reinterpret_cast<uint4*>(W + (size_t)row * ld);
   for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
-    uint4 v = wr[c];
+    uint4 v = load_nt(&wr[c]);
     uint32_t* w = reinterpret_cast<uint32_t*>(&v);
     float o[8];
     if (oi >= 0) {
@@ -332,7 +346,7 @@ apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, c
       }
       w[i] = out;
     }
-    wr[c] = v;
+    store_nt(v, &wr[c]);
   }
 }
 
@@ -410,8 +424,8 @@ accumulate_colscore_kernel(uint16_t* M, const uint16_t* G, int N, int m, long lo
     for (int u = 0; u < U; ++u) {
       const int i = ib + u;
       if (i < i1) {
-        mv[u] = reinterpret_cast<const uint4*>(M + (size_t)i * ld)[c];
-        gv[u] = reinterpret_cast<const uint4*>(G + (size_t)i * ld)[c];
+        mv[u] = load_nt(reinterpret_cast<const uint4*>(M + (size_t)i * ld) + c);
+        gv[u] = load_nt(reinterpret_cast<const uint4*>(G + (size_t)i * ld) + c);
       }
     }
 #pragma unroll
@@ -436,7 +450,7 @@ accumulate_colscore_kernel(uint16_t* M, const uint16_t* G, int N, int m, long lo
         }
         mw[e2] = out;
       }
-      reinterpret_cast<uint4*>(M + (size_t)i * ld)[c] = mv[u];
+      store_nt(mv[u], reinterpret_cast<uint4*>(M + (size_t)i * ld) + c);
     }
   }
   double* ps = part_s + (size_t)rb * m + 8 * (size_t)c;
@@ -551,7 +565,7 @@ decay_unmarked_kernel(uint16_t* W, int N, int m, long long ld, const uint8_t* ma
   const float d = __fsub_rn(1.0f, __fmul_rn(lr, wd));
   for (int i = blockIdx.y; i < N; i += gridDim.y) {
     uint4* p = reinterpret_cast<uint4*>(W + (size_t)i * ld) + c;
-    uint4 v = *p;
+    uint4 v = load_nt(p);
     uint32_t* vw = reinterpret_cast<uint32_t*>(&v);
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
@@ -565,7 +579,7 @@ decay_unmarked_kernel(uint16_t* W, int N, int m, long long ld, const uint8_t* ma
       }
       vw[e2] = out;
     }
-    *p = v;
+    store_nt(v, p);
   }
 }
 
