@@ -654,6 +654,16 @@ __device__ __forceinline__ void store_vec(uint8_t* base, long long ld, int row, 
   }
 }
 
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+// store_vec of a whole 16-byte vector with a non-temporal store (no cache allocation)
+template <class TOut>
+__device__ __forceinline__ void store_vec_nt(uint8_t* base, long long ld, int row, int col,
+                                             const float (&v)[16 / TOut::kBytes]) {
+  const uint4 q = pack16<TOut>(v);
+  const u32x4_nt x = {q.x, q.y, q.z, q.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4_nt*>(base + ((long long)row * ld + col) * TOut::kBytes));
+}
+
 // Epilogue of gemm16_kernel, staged through LDS (called after a workgroup barrier:
 // the operand ring is free).  Each wave takes its WM x WN sub-tile in slabs of 32
 // rows (one fragment row): the raw fp32 accumulators go to a per-wave slab
@@ -665,7 +675,7 @@ __device__ __forceinline__ void store_vec(uint8_t* base, long long ld, int row, 
 // at their transposed positions.  Both triangles round the same fp32 value, so the
 // output is bitwise symmetric.  Only the slab writes index the accumulators, so
 // they stay in registers.
-template <class TOut, bool LOWER, int FM, int FN>
+template <class TOut, bool LOWER, int FM, int FN, bool NT = false>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc)[FM][FN], const GridPos& gp,
                                              int mw, int nw, int lane, float* slab) {
   const int bz = gp.bz;
@@ -713,7 +723,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc
       }
       const int hi = LOWER ? gm - gn : VE - 1;   // symmetric: columns up to the diagonal
       if (hi >= 0) {
-        store_vec<TOut>(ep.D, p.ldd, gm, gn, v, 0, hi);
+        if (NT && hi >= VE - 1) store_vec_nt<TOut>(ep.D, p.ldd, gm, gn, v);
+        else store_vec<TOut>(ep.D, p.ldd, gm, gn, v, 0, hi);
         if (ep.D2) {
           float w[VE];
 #pragma unroll
@@ -753,7 +764,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N>
 constexpr int max_waves_per_eu() { return (BM / WAVES_M) * (BN / WAVES_N) >= 128 * 128 ? 1 : 8; }
 
 template <class TIn, class TB, class TOut, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BKV, bool LOWER,
-          bool NN>
+          bool NN, bool NT = false>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(1, max_waves_per_eu<BM, BN, WAVES_M, WAVES_N>())))
 gemm16_kernel(GemmParams p) {
@@ -1089,7 +1100,7 @@ gemm16_kernel(GemmParams p) {
   static_assert(NW * 32 * (Cfg::kWN + 4) * 4 <= Cfg::kLdsBytes, "epilogue slabs exceed the LDS ring");
   lds_barrier();
   float* slab = reinterpret_cast<float*>(smem16) + wave * 32 * (Cfg::kWN + 4);
-  epilogue_lds<TOut, LOWER, FM, FN>(p, acc, gp, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane, slab);
+  epilogue_lds<TOut, LOWER, FM, FN, NT>(p, acc, gp, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane, slab);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1163,6 +1174,8 @@ inline TileCfg pick_tile(int M, int N, int K, int batch, bool lower) {
   return TileCfg::kSmall;
 }
 
+constexpr double kNonTemporalOutBytes = 128.0 * (1 << 20);
+
 template <class TIn, class TB, class TOut, int BM, int BN, int WM_, int WN_, int NS, int BKV, bool LOWER, bool NN>
 hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops) {
   // 16-bit operands: direct-to-LDS kernel; fp32 operands: register-staged kernel
@@ -1171,14 +1184,28 @@ hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops
   using T32 = Tile32<BM, BN, WM_, WN_, NS, BKV>;
   constexpr int lds = k16 ? T32::kLdsBytes : Tile<BM, BN, WM_, WN_>::kLdsBytes;
   constexpr int BK = k16 ? T32::kBK : 8 * TIn::kPerChunk;    // k per stage
-  void (*kern)(GemmParams);
+  // An output too large to stay in the caches is written with non-temporal stores
+  // (measured on MI355X: 2-4% faster on the 128 x 768x6144 batch's products; the
+  // 8 MB outputs of a 1024 x 4096 call, read again by the next launch, are faster
+  // with ordinary stores).  Only the 256 x 256 tile is chosen for outputs that large.
+  const int products = p.pair ? 2 : 1;
+  const bool nt = (double)p.M * p.N * batch * products * TOut::kBytes >= kNonTemporalOutBytes;
+  void (*base)(GemmParams);
   if constexpr (k16)
-    kern = gemm16_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, NS, BKV, LOWER, NN>;
+    base = gemm16_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, NS, BKV, LOWER, NN, false>;
   else
-    kern = gemm_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, LOWER, NN>;
-  static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+    base = gemm_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, LOWER, NN>;
+  static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(base),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
+  void (*kern)(GemmParams) = base;
+  if constexpr (k16 && BM == 256) {
+    void (*with_nt)(GemmParams) = gemm16_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, NS, BKV, LOWER, NN, true>;
+    static hipError_t attr_nt = hipFuncSetAttribute(reinterpret_cast<const void*>(with_nt),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr_nt != hipSuccess) return attr_nt;
+    if (nt) kern = with_nt;
+  }
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   const long long tiles = gemm_tiles(p.M, p.N, BM, BN, LOWER);
@@ -1186,7 +1213,6 @@ hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops
   if (p.pair && (NN || !LOWER || !p.A2 || !p.Dp || (p.C && !p.C2))) return hipErrorInvalidValue;
   if (p.partials && (NN || !LOWER || p.n_partials < 1 || p.n_partials > kMaxPartials)) return hipErrorInvalidValue;
   if (p.ksplit > 1 && (!k16 || !LOWER || NN || p.pair || !p.part || p.kchunk % BK)) return hipErrorInvalidValue;
-  const int products = p.pair ? 2 : 1;
   const int splits = (p.ksplit > 1 && !p.reduce) ? p.ksplit : 1;
   if (flops && !p.reduce) {
     // issued: K padded to whole stages (split ranges are whole stages but the last)
