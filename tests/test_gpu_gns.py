@@ -129,6 +129,24 @@ def test_restart_schedules_match_gram_oracle(gns_mod):
         assert rel_fro(got[0], ref) <= 2e-2, restarts
 
 
+# The schedule is data: a per-step coefficient table and other step counts, with
+# restarts where they fit (the pages tune per-step tables such as Polar Express's,
+# whose values they do not print; these tables are made up and contract towards 1).
+@pytest.mark.parametrize("steps,restarts", [(5, (2,)), (3, (1,)), (7, (2, 5)), (1, ())])
+@pytest.mark.parametrize("fn", ["orthogonalize", "newton_schulz"])
+def test_per_step_coefficient_tables(gns_mod, steps, restarts, fn):
+    announce(f"gns per-step table T={steps} restarts={restarts} {fn}")
+    table = [(3.4445, -4.7750, 2.0315), (3.0, -3.5, 1.2), (2.5, -2.0, 0.6), (2.2, -1.8, 0.6),
+             (1.9, -1.3, 0.4), (1.875, -1.25, 0.375), (1.875, -1.25, 0.375)][:steps]
+    st = synth.gns_batch("gns_1024x4096_bf16", n=256, m=1024, seed=78)
+    sched = gns_mod.default_schedule(steps=steps, abc=table, restart_after=restarts)
+    got = run(gns_mod, st, "bf16", "f16", fn=fn, schedule=sched)
+    ref = newton_schulz(decode(st[0], "bf16"), steps=steps, abc=np.array(table))
+    e = rel_fro(got[0], ref)
+    print(f"rel err {e:.3e}")
+    assert e <= 2e-2
+
+
 def test_zero_input_gives_zero(gns_mod):
     announce("gns zero input")
     st = np.zeros((2, 64, 256), dtype=np.uint16)
