@@ -191,8 +191,10 @@ size_t dion3_workspace_size(int N, int m, int k, gns_dtype compute);
  *   Frobenius norm taken from the per-row sums of squares); W <- decay + row update
  *   with lr (the caller passes lr = eta / sqrt(f)); M[S, :] <- mu M[S, :].
  * S_out: device int32[k] (ascending).  O_out: nullable device bf16 [k][m] (row stride
- * m) receiving O.  1 <= k <= N, k a multiple of 8; with k > m the k x m submatrix is
- * orthogonalized through its transpose, as in gns_orthogonalize_batched. */
+ * m) receiving O; it must not overlap W, M, G or the workspace.  1 <= k <= N, k a
+ * multiple of 8; with k > m the k x m submatrix is orthogonalized through its
+ * transpose, as in gns_orthogonalize_batched.  Every argument, including those of the
+ * Gram NS on the submatrix, is checked before the first launch. */
 int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int k,
                float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
                const gns_schedule* sched, int* S_out, void* O_out,

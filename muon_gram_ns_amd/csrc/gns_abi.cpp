@@ -586,6 +586,19 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
   if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
 
+  void* O = O_out ? O_out : L.O;
+  const long long km = (long long)k * m;
+  // one batched Gram NS over the selected k x m submatrices of every entry; its
+  // arguments are checked before anything is launched
+  NsCall c = make_call(L.X, GNS_BF16, m, km, O, GNS_BF16, m, km, batch, k, m, compute, &sch, L.gns_ws, L.gns_bytes,
+                       stream, nullptr);
+  c.s_given = L.s;
+  if ((st = check_ns(c))) return st;
+  if (O_out && (overlaps(O_out, (size_t)batch * km * 2, workspace, L.bytes) ||
+                overlaps(O_out, (size_t)batch * km * 2, W, span) || overlaps(O_out, (size_t)batch * km * 2, M, span) ||
+                overlaps(O_out, (size_t)batch * km * 2, G, span)))
+    return GNS_ERR_INVALID_ARG;
+
   uint16_t* Mh = (uint16_t*)M;
   HIP_OK(launch_accumulate_score(Mh, (const uint16_t*)G, batch, N, m, ld, stride, score_norm, L.score, L.sumsq, stream));
   const int* S = S_in;
@@ -595,13 +608,6 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
   }
   HIP_OK(launch_gather_feedback(Mh, batch, N, m, ld, stride, S, k, mu, dev_scalars, (uint16_t*)L.X, m, stream));
   HIP_OK(launch_selected_sumsq(L.sumsq, S, batch, k, N, sch.eps, L.s, stream));
-  void* O = O_out ? O_out : L.O;
-  const long long km = (long long)k * m;
-  // one batched Gram NS over the selected k x m submatrices of every entry
-  NsCall c = make_call(L.X, GNS_BF16, m, km, O, GNS_BF16, m, km, batch, k, m, compute, &sch, L.gns_ws, L.gns_bytes,
-                       stream, nullptr);
-  c.s_given = L.s;
-  if ((st = check_ns(c))) return st;
   if ((st = run_ns(c, true))) return st;
   HIP_OK(launch_apply_update((uint16_t*)W, batch, N, m, ld, stride, S, k, O, GNS_BF16, m, lr, weight_decay,
                              dev_scalars, stream));
@@ -692,19 +698,24 @@ int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld,
   if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
 
+  void* O = O_out ? O_out : L.O;
+  const long long kN = (long long)k * N;
+  // the k x N transpose of the selected columns: Gram NS iterates on its short side;
+  // its arguments are checked before anything is launched
+  NsCall c = make_call(L.Xt, GNS_BF16, N, kN, O, GNS_BF16, N, kN, 1, k, N, compute, &sch, L.gns_ws, L.gns_bytes,
+                       stream, nullptr);
+  c.s_given = L.s;
+  if ((st = check_ns(c))) return st;
+  if (O_out && (overlaps(O_out, (size_t)kN * 2, workspace, L.bytes) || overlaps(O_out, (size_t)kN * 2, W, span) ||
+                overlaps(O_out, (size_t)kN * 2, M, span) || overlaps(O_out, (size_t)kN * 2, G, span)))
+    return GNS_ERR_INVALID_ARG;
+
   uint16_t* Mh = (uint16_t*)M;
   HIP_OK(launch_accumulate_colscore(Mh, (const uint16_t*)G, N, m, ld, score_norm, L.part_s, L.part_q, L.score,
                                     L.sumsq, stream));
   HIP_OK(launch_topk(L.score, 1, m, k, S_out, stream));
   HIP_OK(launch_gather_cols_feedback(Mh, N, m, ld, S_out, k, mu, (uint16_t*)L.Xt, N, stream));
   HIP_OK(launch_selected_sumsq(L.sumsq, S_out, 1, k, m, sch.eps, L.s, stream));
-  void* O = O_out ? O_out : L.O;
-  const long long kN = (long long)k * N;
-  // the k x N transpose of the selected columns: Gram NS iterates on its short side
-  NsCall c = make_call(L.Xt, GNS_BF16, N, kN, O, GNS_BF16, N, kN, 1, k, N, compute, &sch, L.gns_ws, L.gns_bytes,
-                       stream, nullptr);
-  c.s_given = L.s;
-  if ((st = check_ns(c))) return st;
   if ((st = run_ns(c, true))) return st;
   HIP_OK(launch_update_cols((uint16_t*)W, N, m, ld, S_out, k, (const uint16_t*)O, N, lr, weight_decay, L.mark,
                             stream));

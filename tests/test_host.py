@@ -131,6 +131,16 @@ def test_gemm_and_dion3_validation():
     assert L.dion3_step_cols(*cargs(N=60)) == UNSUP
     assert L.dion3_step_cols(*cargs(wsb=8)) == WS
     assert L.dion3_cols_workspace_size(64, 256, 16, F16) > 2 * 16 * 64 * 2 + 2 * 256 * 8
+    # O_out overlapping the workspace or the state is rejected before anything runs
+    # (without a GPU, a launch would report GNS_ERR_HIP instead)
+    oargs = lambda O: (FAKE, FAKE * 8, FAKE * 16, 64, 256, 256, 16, 0.02, 0.0, 0.95, 1, F16, ctypes.byref(sched),
+                       FAKE * 30, O, FAKE * 40, 1 << 30, None)
+    assert L.dion3_step(*oargs(FAKE * 40 + 4096)) == INVALID            # inside the workspace
+    assert L.dion3_step(*oargs(FAKE * 8)) == INVALID                    # O is M
+    coargs = lambda O: (FAKE, FAKE * 8, FAKE * 16, 64, 256, 256, 16, 0.02, 0.0, 0.95, 1, F16, ctypes.byref(sched),
+                        FAKE * 30, O, FAKE * 40, 1 << 30, None)
+    assert L.dion3_step_cols(*coargs(FAKE * 40 + 4096)) == INVALID
+    assert L.dion3_step_cols(*coargs(FAKE)) == INVALID                  # O is W
     assert L.dion3_select_topk(FAKE, 10, 11, FAKE, None) == INVALID
     assert L.dion3_select_topk(FAKE, 10, 0, FAKE, None) == INVALID
 
