@@ -55,7 +55,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested). The batch dimension would shard across GPUs; see the design notes.",
               file=sys.stderr)
         sys.exit(2)
