@@ -56,7 +56,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path (--gpus {args.gpus} "
-              "requested). The batch dimension would shard across GPUs; see the design notes.",
+              "requested). The batch of same-shape matrices would shard across GPUs, with one all-to-all "
+              "per shape group in each direction.",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
