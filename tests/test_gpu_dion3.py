@@ -336,3 +336,60 @@ def test_dion3_step_cols_full_size_tall(gns_mod):
     assert np.array_equal(bits(M), m_ref)
     rest = np.setdiff1d(np.arange(8192), S_ref)
     assert np.array_equal(bits(W)[:, rest], w[:, rest])
+
+
+# ---- degenerate cases of the step ----
+
+def test_dion3_step_all_rows_is_muon_step(gns_mod):
+    """k = N (f = 1): every row is selected, so the step is Muon's on M + G."""
+    announce("dion3 step k = N 256x1024")
+    w, g, m = synth.dion3_state(n=256, m=1024, seed=34)
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    S, O = gns_mod.dion3_step(W, M, G, 256, 0.01, weight_decay=0.0, mu=0.9, score_norm=1, return_O=True)
+    w_ref, m_ref, S_ref, O_ref = oracle.dion3_step(w, m, g, 256, 0.01, wd=0.0, mu=0.9, norm="l1")
+    assert np.array_equal(S.cpu().numpy(), np.arange(256))
+    assert np.array_equal(bits(M), m_ref)
+    assert rel_fro(to_f64(O), newton_schulz(bf16_to_f64(accumulate(m, g)))) <= 2e-2
+    assert w_within_bound(bits(W), w_ref, 0.01, O_ref)
+
+
+def test_dion3_step_tied_scores_pick_lower_rows(gns_mod):
+    """Rows repeated three times tie exactly in score, and k = 40 splits one group of
+    tied rows: the lower index wins, as in the oracle, and the whole step matches it."""
+    announce("dion3 step with tied rows 256x512")
+    w, g, m = synth.dion3_state(n=256, m=512, seed=35)
+    m = np.ascontiguousarray(np.repeat(m[:86], 3, axis=0)[:256])     # rows 3i .. 3i+2 identical
+    g = np.ascontiguousarray(np.repeat(g[:86], 3, axis=0)[:256])
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    S, O = gns_mod.dion3_step(W, M, G, 40, 0.02, weight_decay=0.0, mu=0.95, score_norm=2, return_O=True)
+    w_ref, m_ref, S_ref, O_ref = oracle.dion3_step(w, m, g, 40, 0.02, wd=0.0, mu=0.95, norm="l2")
+    assert np.array_equal(S.cpu().numpy(), S_ref)
+    assert np.array_equal(bits(M), m_ref)
+    assert rel_fro(to_f64(O), O_ref) <= 2e-2
+
+
+def test_dion3_step_zero_state(gns_mod):
+    """M = G = 0: every score ties at zero, the first k rows are selected, X = 0 gives
+    O = 0, so W keeps its bits (wd = 0) and M stays zero."""
+    announce("dion3 step on a zero state 128x256")
+    w, _, _ = synth.dion3_state(n=128, m=256, seed=36)
+    z = np.zeros((128, 256), dtype=np.uint16)
+    W, M, G = to_dev(w, "bf16"), to_dev(z, "bf16"), to_dev(z, "bf16")
+    S, O = gns_mod.dion3_step(W, M, G, 32, 0.02, weight_decay=0.0, mu=0.95, score_norm=1, return_O=True)
+    assert np.array_equal(S.cpu().numpy(), np.arange(32))
+    assert not np.any(bits(O) & 0x7fff)                   # +0 or -0 everywhere
+    assert np.array_equal(bits(W), w)
+    assert not np.any(bits(M) & 0x7fff)
+
+
+def test_dion3_step_smallest_k(gns_mod):
+    """k = 8, the smallest row count the step takes."""
+    announce("dion3 step k = 8 512x1024")
+    w, g, m = synth.dion3_state(n=512, m=1024, seed=37)
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    S, O = gns_mod.dion3_step(W, M, G, 8, 0.02, weight_decay=0.1, mu=0.95, score_norm=1, return_O=True)
+    w_ref, m_ref, S_ref, O_ref = oracle.dion3_step(w, m, g, 8, 0.02, wd=0.1, mu=0.95, norm="l1")
+    assert np.array_equal(S.cpu().numpy(), S_ref)
+    assert np.array_equal(bits(M), m_ref)
+    assert rel_fro(to_f64(O), O_ref) <= 2e-2
+    assert w_within_bound(bits(W), w_ref, 0.02, O_ref)
