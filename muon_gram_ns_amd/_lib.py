@@ -155,13 +155,19 @@ _WS = {}
 
 
 def workspace(nbytes: int, device):
-    """Grow-only per-device workspace (torch-allocated device memory)."""
+    """Grow-only per-device workspace (torch-allocated device memory) for calls made
+    without one.  Calls on one stream are ordered, so they share it safely; calls that
+    run concurrently on different streams must each pass their own workspace.  The
+    buffer is marked as used by the current stream, so when it grows, torch does not
+    hand the old block to another stream before this stream's kernels are done."""
     torch = _torch()
     key = torch.device(device).index
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
         _WS[key] = buf
+    if not torch.cuda.is_current_stream_capturing():
+        buf.record_stream(torch.cuda.current_stream(buf.device))
     return buf
 
 
