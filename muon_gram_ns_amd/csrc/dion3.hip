@@ -149,38 +149,102 @@ __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* sh, un
 }
 
 // Keys are staged in LDS when they fit (N <= kTopkLdsKeys), else read from memory.
-// The bin holding the k-th largest key is found by one wave: each lane holds 4
-// bins (from the top), a prefix sum over lanes finds the crossing lane.
+// The leading bits that every key shares (found from the OR and the AND of all keys)
+// are settled at once: scores of one magnitude share their sign, exponent and first
+// mantissa bits, and counting them digit by digit would send every key's atomic add
+// to one histogram bin.  The remaining bits are resolved 8 at a time from the top;
+// the bin holding the k-th largest key is found by one wave: each lane holds 4 bins
+// (from the top), a prefix sum over lanes finds the crossing lane.  The search stops
+// early once every candidate left is selected.
 constexpr int kTopkLdsKeys = 12288;
+
+__device__ __forceinline__ unsigned long long wave_or(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v |= __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_and(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v &= __shfl_xor(v, off, 64);
+  return v;
+}
 
 __global__ void __launch_bounds__(kTopkThreads)
 topk_kernel(const double* score, int N, int k, int* S) {
   score += (size_t)blockIdx.x * N;     // one workgroup per batch entry
   S += (size_t)blockIdx.x * k;
+  constexpr int kWaves = kTopkThreads / 64;
   __shared__ unsigned hist[256];
-  __shared__ unsigned scan_sh[kTopkThreads / 64 + 1];
+  __shared__ unsigned scan_sh[kWaves + 1];
+  __shared__ unsigned long long red_or[kWaves], red_and[kWaves];
   __shared__ unsigned long long sh_prefix;
-  __shared__ unsigned sh_krem;
+  __shared__ unsigned sh_krem, sh_done;
   __shared__ unsigned long long keys_lds[kTopkLdsKeys];
   const unsigned long long* gkey = reinterpret_cast<const unsigned long long*>(score);
   const bool in_lds = N <= kTopkLdsKeys;
-  if (in_lds)
-    for (int i = threadIdx.x; i < N; i += kTopkThreads) keys_lds[i] = gkey[i];
-  const unsigned long long* key = in_lds ? keys_lds : gkey;
+  unsigned long long vor = 0, vand = ~0ull;
+  if (in_lds) {
+    // all of a thread's loads are issued before the first is used, so the staging
+    // costs one memory latency instead of one per key
+    constexpr int kPer = kTopkLdsKeys / kTopkThreads;
+    static_assert(kTopkLdsKeys % kTopkThreads == 0, "whole rounds of keys per thread");
+    unsigned long long v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = threadIdx.x + j * kTopkThreads;
+      v[j] = i < N ? gkey[i] : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = threadIdx.x + j * kTopkThreads;
+      if (i < N) {
+        keys_lds[i] = v[j];
+        vor |= v[j];
+        vand &= v[j];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < N; i += kTopkThreads) {
+      const unsigned long long kv = gkey[i];
+      vor |= kv;
+      vand &= kv;
+    }
+  }
+  vor = wave_or(vor);
+  vand = wave_and(vand);
+  if ((threadIdx.x & 63) == 0) {
+    red_or[threadIdx.x >> 6] = vor;
+    red_and[threadIdx.x >> 6] = vand;
+  }
   __syncthreads();
-  unsigned long long prefix = 0, mask = 0;
+  vor = 0;
+  vand = ~0ull;
+  for (int w = 0; w < kWaves; ++w) {
+    vor |= red_or[w];
+    vand &= red_and[w];
+  }
+  const unsigned long long* key = in_lds ? keys_lds : gkey;
+  // bits 63 .. nbits are the same in every key; they form the starting prefix
+  const unsigned long long differ = vor ^ vand;
+  const int nbits = differ ? 64 - __clzll((long long)differ) : 0;
+  unsigned long long mask = nbits == 64 ? 0ull : ~((1ull << nbits) - 1ull);
+  unsigned long long prefix = vand & mask;
   unsigned krem = (unsigned)k;
-  for (int d = 7; d >= 0; --d) {
-    const int shift = 8 * d;
+  for (int top = nbits; top > 0;) {
+    const int width = top < 8 ? top : 8;
+    const int shift = top - width;
+    const unsigned dmask = (1u << width) - 1u;
     for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < N; i += kTopkThreads) {
       const unsigned long long kv = key[i];
-      if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
+      if ((kv & mask) == prefix) atomicAdd(&hist[(unsigned)(kv >> shift) & dmask], 1u);
     }
     __syncthreads();
     if (threadIdx.x < 64) {
       // lane l holds bins 255-4l .. 252-4l; counts above a lane's bins by prefix sum
+      // (bins at or above 2^width stay empty)
       const int lane = threadIdx.x;
       unsigned c[4], local = 0;
 #pragma unroll
@@ -198,45 +262,57 @@ topk_kernel(const double* score, int N, int k, int* S) {
       // the crossing lane: the k-th largest candidate lies in one of its bins
       // (the last lane always crosses: krem never exceeds the candidate count)
       if (excl < krem && (krem <= incl || lane == 63)) {
-        unsigned above = excl;
+        unsigned above = excl, cnt = c[3];
         int bin = 255 - 4 * lane - 3;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int b = 255 - 4 * lane - q;
           if (above + c[q] >= krem || b == 0) {
             bin = b;
+            cnt = c[q];
             break;
           }
           above += c[q];
         }
         sh_prefix = prefix | ((unsigned long long)bin << shift);
         sh_krem = krem - above;
+        sh_done = (cnt == krem - above) ? 1u : 0u;   // every key of the bin is taken
       }
     }
     __syncthreads();
     prefix = sh_prefix;
     krem = sh_krem;
-    mask |= (255ull << shift);
+    mask |= (unsigned long long)dmask << shift;
+    top = sh_done ? 0 : shift;
     __syncthreads();
   }
-  // prefix is now the k-th largest key; take every key above it and the first krem
-  // keys equal to it (lowest indices), writing indices in ascending order.
-  const unsigned long long tau = prefix;
-  unsigned eq_base = 0, sel_base = 0;
-  for (int base = 0; base < N; base += kTopkThreads) {
-    const int i = base + threadIdx.x;
-    unsigned long long kv = 0;
-    bool valid = i < N;
-    if (valid) kv = key[i];
-    const unsigned is_eq = (valid && kv == tau) ? 1u : 0u;
-    unsigned eq_total;
-    const unsigned eq_before = eq_base + block_excl_scan(is_eq, scan_sh, eq_total);
-    const bool take = valid && (kv > tau || (is_eq && eq_before < krem));
-    unsigned sel_total;
-    const unsigned pos = sel_base + block_excl_scan(take ? 1u : 0u, scan_sh, sel_total);
-    if (take && pos < (unsigned)k) S[pos] = i;
-    eq_base += eq_total;
-    sel_base += sel_total;
+  // Keys whose masked bits exceed the prefix are above every candidate and are all
+  // taken; of the candidates (masked bits equal to the prefix) the first krem by index
+  // are taken.  With all 64 bits resolved that is: every key above the k-th largest
+  // and the lowest-index keys equal to it.  Each thread owns one contiguous range of
+  // indices, so a block-wide scan of the counts gives ascending output positions.
+  const int per = (N + kTopkThreads - 1) / kTopkThreads;
+  const int lo = min(N, (int)threadIdx.x * per), hi = min(N, lo + per);
+  unsigned n_gt = 0, n_eq = 0;
+  for (int i = lo; i < hi; ++i) {
+    const unsigned long long kv = key[i] & mask;
+    n_gt += kv > prefix ? 1u : 0u;
+    n_eq += kv == prefix ? 1u : 0u;
+  }
+  unsigned eq_total;
+  const unsigned eq_before = block_excl_scan(n_eq, scan_sh, eq_total);
+  const unsigned eq_take = eq_before >= krem ? 0u : min(n_eq, krem - eq_before);
+  unsigned sel_total;
+  unsigned pos = block_excl_scan(n_gt + eq_take, scan_sh, sel_total);
+  unsigned eq_seen = 0;
+  for (int i = lo; i < hi; ++i) {
+    const unsigned long long kv = key[i] & mask;
+    bool take = kv > prefix;
+    if (kv == prefix) take = eq_seen++ < eq_take;
+    if (take) {
+      if (pos < (unsigned)k) S[pos] = i;
+      ++pos;
+    }
   }
 }
 
@@ -376,10 +452,21 @@ selected_sumsq_kernel(const double* sumsq, const int* S, int k, int N, float eps
   S += (size_t)blockIdx.x * k;
   s_out += blockIdx.x;
   const int per = (k + kRowThreads - 1) / kRowThreads;
+  const int lo = min(k, (int)threadIdx.x * per), hi = min(k, lo + per);
+  // each thread sums its range in index order; the loads of 8 terms are issued
+  // before the first is added
+  constexpr int kUnroll = 8;
   double acc = 0.0;
-  for (int i = threadIdx.x * per; i < min(k, (int)(threadIdx.x + 1) * per); ++i) {
-    const int r = S[i];
-    if (r >= 0 && r < N) acc += sumsq[r];
+  for (int i0 = lo; i0 < hi; i0 += kUnroll) {
+    int r[kUnroll];
+    double v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) r[u] = i0 + u < hi ? S[i0 + u] : -1;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = (r[u] >= 0 && r[u] < N) ? sumsq[r[u]] : 0.0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (r[u] >= 0 && r[u] < N) acc += v[u];
   }
   const double t = block_sum_f64(acc, sh);
   if (threadIdx.x == 0) s_out[0] = (float)(1.0 / (sqrt(t) + (double)eps));

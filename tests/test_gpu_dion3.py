@@ -67,6 +67,31 @@ def test_topk_distinct_scores(gns_mod):
         assert np.array_equal(S, select_topk(scores, k))
 
 
+@pytest.mark.parametrize("kind", ["equal", "zero", "two_values", "row_l2", "row_l1", "inf_and_zero"])
+@pytest.mark.parametrize("N,k", [(8192, 2048), (3000, 3000), (777, 776), (20000, 5000)])
+def test_topk_shared_bits_and_early_stop(gns_mod, kind, N, k):
+    """Scores whose bit patterns share their leading bits (one magnitude, all equal,
+    two values), the workload's row sums, and +inf among zeros."""
+    announce(f"dion3 topk {kind} N={N} k={k}")
+    rng = np.random.default_rng(N + k)
+    if kind == "equal":
+        scores = np.full(N, 3.5)
+    elif kind == "zero":
+        scores = np.zeros(N)
+    elif kind == "two_values":
+        scores = np.where(rng.random(N) < 0.5, 1.0, 2.0)
+    elif kind in ("row_l2", "row_l1"):
+        x = rng.normal(0.0, 0.02, size=(N, 256))
+        scores = (x * x).sum(1) if kind == "row_l2" else np.abs(x).sum(1)
+    else:
+        scores = rng.random(N)
+        scores[rng.random(N) < 0.3] = np.inf
+        scores[rng.random(N) < 0.2] = 0.0
+    torch = __import__("torch")
+    S = gns_mod.dion3_select_topk(torch.from_numpy(scores).cuda(), k).cpu().numpy()
+    assert np.array_equal(S, select_topk(scores, k))
+
+
 def test_gather_feedback_bit_exact(gns_mod):
     announce("dion3 gather_feedback")
     _, _, m = synth.dion3_state(n=200, m=512, seed=12)
