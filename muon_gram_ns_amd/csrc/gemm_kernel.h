@@ -1256,40 +1256,62 @@ hipError_t launch_cfg(GemmParams p, int batch, hipStream_t stream, double* flops
   return hipErrorInvalidValue;
 }
 
-// K split of the symmetric product: a single matrix (batch 1) with K >= 16384 and 32 to
-// 127 output tiles of 256 x 256 is cut into S ranges of at least 2048 values, S as
-// large as the CUs allow (at most 8).  The n = 2048, K = 28672 Gram product of the
-// Dion3 workload (36 tiles) runs on 7 ranges.  With fewer tiles each workgroup of the
-// sum would read too many partial tiles.  Only batch 1 splits: the sum order, and with
-// it the last bits, then differ from the same matrix in a batch.
-constexpr int kSplitMinK = 16384, kSplitMinChunk = 2048, kSplitBK = GNS_BK_BIG, kSplitMinTiles = 32;
-inline int symm_ksplit(int batch, int n, int K, int& kchunk) {
-  kchunk = 0;
-  if (batch != 1 || K < kSplitMinK) return 1;
-  const long long tiles = gemm_tiles(n, n, 256, 256, true);
-  if (tiles < kSplitMinTiles) return 1;
+// K split of the symmetric product: a single matrix (batch 1) with K >= 16384 whose
+// output has 32 to 127 tiles of 256 x 256 is cut into S ranges of at least 2048
+// values, S as large as the CUs allow (at most 8).  The n = 2048, K = 28672 Gram
+// product of the Dion3 workload (36 tiles) runs on 7 ranges.  A matrix with fewer
+// than 32 such tiles (n <= 1792) splits on tiles of 128 x 128 instead, when it has at
+// least 32 of those: the n = 1024, K = 28672 Gram product then runs on 36 tiles x 7
+// ranges instead of 136 unsplit 64 x 64 tiles that leave half the CUs idle.  With
+// fewer tiles each workgroup of the sum would read too many partial tiles.  Only
+// batch 1 splits: the sum order, and with it the last bits, then differ from the
+// same matrix in a batch.
+constexpr int kSplitMinK = 16384, kSplitMinChunk = 2048, kSplitMinTiles = 32;
+struct SymmSplit {
+  int S = 1;         // number of K ranges (1: no split)
+  int kchunk = 0;    // K values per range, a whole number of stages
+  int tile = 256;    // output tile edge
+};
+inline SymmSplit symm_split_plan(int batch, int n, int K) {
+  SymmSplit r;
+  if (batch != 1 || K < kSplitMinK) return r;
+  long long tiles = gemm_tiles(n, n, 256, 256, true);
+  int bk = GNS_BK_BIG;
+  if (tiles < kSplitMinTiles) {
+    tiles = gemm_tiles(n, n, 128, 128, true);
+    if (tiles < kSplitMinTiles) return r;
+    r.tile = 128;
+    bk = GNS_BK_MID;
+  }
   const long long S = std::min<long long>(std::min<long long>(256 / tiles, 8), K / kSplitMinChunk);
-  if (S < 2) return 1;
-  kchunk = (int)(((K + S - 1) / S + kSplitBK - 1) / kSplitBK * kSplitBK);
-  return (K + kchunk - 1) / kchunk;
+  if (S < 2) return SymmSplit{};
+  r.kchunk = (int)(((K + S - 1) / S + bk - 1) / bk * bk);
+  r.S = (K + r.kchunk - 1) / r.kchunk;
+  return r;
 }
 
 // Three launches: the partial products (one workgroup per tile and K range), the sum
 // of each tile's ranges into its first range (element-parallel, fixed order), and the
 // epilogue over the summed tiles.
-template <class TIn, class TOut>
-hipError_t launch_symm_split(GemmParams p, int batch, float* part, hipStream_t stream, double* flops) {
+template <class TIn, class TOut, int BM, int WM_, int WN_, int NS, int BKV>
+hipError_t launch_symm_split_cfg(GemmParams p, int batch, float* part, hipStream_t stream, double* flops) {
   p.part = part;
   p.reduce = 0;
-  hipError_t e = launch_one<TIn, TIn, TOut, 256, 256, GNS_BIG_WM, GNS_BIG_WN, GNS_STAGES_BIG, GNS_BK_BIG, true, false>(
-      p, batch, stream, flops);
+  hipError_t e = launch_one<TIn, TIn, TOut, BM, BM, WM_, WN_, NS, BKV, true, false>(p, batch, stream, flops);
   if (e != hipSuccess) return e;
-  const long long tiles = gemm_tiles(p.M, p.N, 256, 256, true) * batch;
-  e = launch_sum_ranges(part, tiles, p.ksplit, 256 * 256, stream);
+  const long long tiles = gemm_tiles(p.M, p.N, BM, BM, true) * batch;
+  e = launch_sum_ranges(part, tiles, p.ksplit, BM * BM, stream);
   if (e != hipSuccess) return e;
   p.reduce = 2;
-  return launch_one<TIn, TIn, TOut, 256, 256, GNS_BIG_WM, GNS_BIG_WN, GNS_STAGES_BIG, GNS_BK_BIG, true, false>(
-      p, batch, stream, flops);
+  return launch_one<TIn, TIn, TOut, BM, BM, WM_, WN_, NS, BKV, true, false>(p, batch, stream, flops);
+}
+
+template <class TIn, class TOut>
+hipError_t launch_symm_split(GemmParams p, int batch, float* part, int tile, hipStream_t stream, double* flops) {
+  if (tile == 128)
+    return launch_symm_split_cfg<TIn, TOut, 128, 2, 2, GNS_STAGES_MID, GNS_BK_MID>(p, batch, part, stream, flops);
+  return launch_symm_split_cfg<TIn, TOut, 256, GNS_BIG_WM, GNS_BIG_WN, GNS_STAGES_BIG, GNS_BK_BIG>(p, batch, part,
+                                                                                                 stream, flops);
 }
 
 template <class TIn, class TB, bool LOWER, bool NN>

@@ -15,31 +15,30 @@ hipError_t launch_symm(gns_dtype in, gns_dtype out, const GemmParams& p, int bat
 
 size_t symm_split_bytes(int batch, int n, int K, gns_dtype in) {
   if (in == GNS_F32) return 0;
-  int kchunk = 0;
-  const int S = symm_ksplit(batch, n, K, kchunk);
-  if (S < 2) return 0;
-  return (size_t)gemm_tiles(n, n, 256, 256, true) * S * 256 * 256 * sizeof(float);
+  const SymmSplit sp = symm_split_plan(batch, n, K);
+  if (sp.S < 2) return 0;
+  return (size_t)gemm_tiles(n, n, sp.tile, sp.tile, true) * sp.S * sp.tile * sp.tile * sizeof(float);
 }
 
 hipError_t launch_symm_ws(gns_dtype in, gns_dtype out, const GemmParams& p, int batch, float* part, size_t part_bytes,
                           hipStream_t s, double* flops) {
-  int kchunk = 0;
-  const int S = (in == GNS_F32 || p.pair) ? 1 : symm_ksplit(batch, p.M, p.K, kchunk);
-  if (S < 2 || !part || part_bytes < symm_split_bytes(batch, p.M, p.K, in)) return launch_symm(in, out, p, batch, s, flops);
+  const SymmSplit sp = (in == GNS_F32 || p.pair) ? SymmSplit{} : symm_split_plan(batch, p.M, p.K);
+  if (sp.S < 2 || !part || part_bytes < symm_split_bytes(batch, p.M, p.K, in))
+    return launch_symm(in, out, p, batch, s, flops);
   GemmParams q = p;
-  q.ksplit = S;
-  q.kchunk = kchunk;
+  q.ksplit = sp.S;
+  q.kchunk = sp.kchunk;
   if (in == GNS_BF16) {
     switch (out) {
-      case GNS_BF16: return launch_symm_split<TBF16, TBF16>(q, batch, part, s, flops);
-      case GNS_F16: return launch_symm_split<TBF16, TF16>(q, batch, part, s, flops);
-      case GNS_F32: return launch_symm_split<TBF16, TF32>(q, batch, part, s, flops);
+      case GNS_BF16: return launch_symm_split<TBF16, TBF16>(q, batch, part, sp.tile, s, flops);
+      case GNS_F16: return launch_symm_split<TBF16, TF16>(q, batch, part, sp.tile, s, flops);
+      case GNS_F32: return launch_symm_split<TBF16, TF32>(q, batch, part, sp.tile, s, flops);
     }
   } else {
     switch (out) {
-      case GNS_BF16: return launch_symm_split<TF16, TBF16>(q, batch, part, s, flops);
-      case GNS_F16: return launch_symm_split<TF16, TF16>(q, batch, part, s, flops);
-      case GNS_F32: return launch_symm_split<TF16, TF32>(q, batch, part, s, flops);
+      case GNS_BF16: return launch_symm_split<TF16, TBF16>(q, batch, part, sp.tile, s, flops);
+      case GNS_F16: return launch_symm_split<TF16, TF16>(q, batch, part, sp.tile, s, flops);
+      case GNS_F32: return launch_symm_split<TF16, TF32>(q, batch, part, sp.tile, s, flops);
     }
   }
   return hipErrorInvalidValue;

@@ -240,3 +240,29 @@ def test_long_k_single_matrix_split(gns_mod):
     assert rel_fro(to_f64(o1[0]), both) <= 5e-3
     std = to_f64(gns_mod.newton_schulz(one)[0])
     assert rel_fro(std, ref) <= 2e-2
+
+
+@pytest.mark.parametrize("n,m", [(1024, 16384), (1000, 16392)])
+def test_long_k_single_matrix_split_mid_tiles(gns_mod, n, m):
+    """One n x m matrix with n <= 1792: fewer than 32 output tiles of 256 x 256, so its
+    Gram products split K on tiles of 128 x 128 (36 tiles, 7 ranges; n = 1000 and
+    K = 16392 leave ragged tiles and a short last stage).  Parity against the oracle,
+    bitwise repeatable, and within rounding of the same matrix in a batch of two
+    (which does not split)."""
+    announce(f"gns {n}x{m} bf16 (K split, 128 tiles)")
+    st = synth.gns_batch("gns_1024x4096_bf16", batch=1, n=n, m=m, seed=73)
+    st = np.concatenate([st, st])
+    announce(f"gns {n}x{m} bf16 (K split, 128 tiles): oracle")
+    ref = newton_schulz(decode(st[0], "bf16"))
+    announce(f"gns {n}x{m} bf16 (K split, 128 tiles): GPU")
+    one = to_dev(st[:1], "bf16")
+    o1 = gns_mod.orthogonalize(one)
+    o2 = gns_mod.orthogonalize(one)
+    assert np.array_equal(bits(o1), bits(o2))
+    e = rel_fro(to_f64(o1[0]), ref)
+    print(f"split rel err {e:.3e}")
+    assert e <= 2e-2
+    both = to_f64(gns_mod.orthogonalize(to_dev(st, "bf16"))[0])
+    assert rel_fro(to_f64(o1[0]), both) <= 5e-3
+    std = to_f64(gns_mod.newton_schulz(one)[0])
+    assert rel_fro(std, ref) <= 2e-2
