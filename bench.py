@@ -364,9 +364,12 @@ def restart_sweep(gns, synth, torch, np):
     """Relative Frobenius error of Gram NS (T = 5, the blog's coefficients) against the
     float64 oracle for each restart position, with fp16 and bf16 iterates.  The pages
     restart once to flush the spurious negative eigenvalues that half-precision Gram
-    iterates acquire; where to restart is left to a sweep the pages do not print."""
+    iterates acquire; where to restart is left to a sweep the pages do not print.
+    Standard NS on the same kernels, at the same iterate precision, is measured beside
+    it: the pages compare the two only through loss curves."""
     import oracle
-    cases = [("gns_1024x4096_bf16", 1, 1024, 4096), ("gns_32x4096x4096_bf16", 1, 2048, 2048)]
+    cases = [("gns_1024x4096_bf16", 1, 1024, 4096), ("gns_128x768x6144_bf16", 1, 768, 6144),
+             ("gns_32x4096x4096_bf16", 1, 2048, 2048)]
     masks = {"none": (), "after 1": (1,), "after 2": (2,), "after 3": (3,), "after 4": (4,),
              "after 1 and 3": (1, 3), "after 2 and 4": (2, 4)}
     for name, B, n, m in cases:
@@ -381,9 +384,14 @@ def restart_sweep(gns, synth, torch, np):
                 got = gns.orthogonalize(X, compute=compute, schedule=sched)[0].float().cpu().double().numpy()
                 finite = bool(np.isfinite(got).all())
                 err = float(np.linalg.norm(np.nan_to_num(got) - ref) / np.linalg.norm(ref)) if finite else None
-                print(json.dumps({"restart_sweep": name, "n": n, "m": m, "iterates": compute, "restart": label,
-                                  "rel_err_vs_oracle": err, "finite": finite,
+                print(json.dumps({"restart_sweep": name, "n": n, "m": m, "iterates": compute, "method": "gram",
+                                  "restart": label, "rel_err_vs_oracle": err, "finite": finite,
                                   "oracle_seconds": round(t_ref, 2)}), flush=True)
+            got = gns.newton_schulz(X, compute=compute)[0].float().cpu().double().numpy()
+            finite = bool(np.isfinite(got).all())
+            err = float(np.linalg.norm(np.nan_to_num(got) - ref) / np.linalg.norm(ref)) if finite else None
+            print(json.dumps({"restart_sweep": name, "n": n, "m": m, "iterates": compute, "method": "standard",
+                              "rel_err_vs_oracle": err, "finite": finite}), flush=True)
 
 
 def megabatch_dion3(gns, torch, args, B=16, N=2048, m=8192, f=0.25):
