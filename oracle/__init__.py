@@ -21,6 +21,9 @@ Sources (pages on the Dion3 / Muon method):
     restart, Algorithm 4 = the Dion3 row-subsampled update with error feedback);
     section 前置知识 (prerequisites: polar factor, error feedback).
   * "Dion3: Full-Stack Orthogonal Updates" (m.montaan.com summary): f = 1 is Muon.
+  * The Muon blog named first above: the Muon step listed after "Doing an SVD
+    without an SVD" and its notes on decoupled weight decay and update-scale
+    matching (oracle/muon.py).
 
 Parity status of each function is stated in its docstring; "parity unpinned" marks
 a function with no independent pin.
@@ -35,3 +38,4 @@ from .dion3 import (  # noqa: F401
     k_from_fraction, accumulate, row_scores, select_topk, gather_rows, error_feedback, weight_update,
     dion3_step, dion3_step_rows, dion3_step_cols,
 )
+from .muon import muon_scale, momentum, decay_and_update, muon_step  # noqa: F401

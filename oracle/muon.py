@@ -1,0 +1,90 @@
+"""Muon optimizer step, written from the pages.  TEST INFRASTRUCTURE ONLY.
+
+Source: "Muon: Orthogonalized Momentum and Why It Trains LLMs 2x Cheaper" (blog by
+M. Chugh), the step listed after "Doing an SVD without an SVD" and the two practical
+notes that follow it (decoupled weight decay, per-parameter update-scale matching):
+  * heavy-ball momentum:   M <- mu M + G
+  * Nesterov lookahead:    U = G + mu M   (with the updated M); plain: U = M
+  * orthogonalise:         O = NS(U)       (quintic Newton-Schulz, the blog's iteration)
+  * RMS matching:          scale = 0.2 sqrt(max(d_out, d_in))
+  * decoupled decay first, then the update:  W <- (1 - lr wd) W - lr scale O
+The Dion3 pages state that Dion3 with f = 1 is this step ("Dion3: Full-Stack
+Orthogonal Updates", m.montaan.com; "Dion3：全栈正交更新", paper.rainbus.top,
+核心方法), which pins the momentum recursion and the update below.
+
+Storage model (the pages leave rounding open; this is the reading the GPU path
+follows, the same as for the Dion3 step): W, M, G are stored in bf16 and every stored
+result is rounded once to bf16 (nearest, ties to even) from float32 arithmetic
+carried out op by op (numpy float32, no fused multiply-add).  O is stored in bf16
+before the update reads it.  The scale is fl32(fl32(0.2) * fl32(sqrt(max(n, m)))).
+
+Two storage modes: storage="bf16" (the model above) and storage="f64" (no rounding
+anywhere, used to pin the step against Dion3 with f = 1).
+
+Parity status: momentum pinned by exact dyadic cases against its closed form and by
+the f = 1 identity; muon_scale by the page's formula at shapes where it is exact;
+muon_step by the f = 1 identity (float64), the zero-gradient decay closed form and
+the Newton-Schulz oracle on U.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .bf16 import bf16_to_f64, f64_to_bf16_rne
+from .newton_schulz import newton_schulz, JORDAN_ABC, EPS
+
+
+def muon_scale(n: int, m: int) -> np.float32:
+    """0.2 sqrt(max(n, m)) in float32: the update RMS matched to AdamW's."""
+    return np.float32(np.float32(0.2) * np.sqrt(np.float32(max(n, m))))
+
+
+def momentum(m_bits, g_bits, mu, nesterov=True):
+    """M' = bf16(fl32(fl32(mu) M) + G); U = bf16(G + fl32(mu M')) with the lookahead,
+    else U = M'.  Returns (M', U) as bf16 bit patterns."""
+    mu32 = np.float32(mu)
+    m32 = bf16_to_f64(m_bits).astype(np.float32)
+    g32 = bf16_to_f64(g_bits).astype(np.float32)
+    m_new = f64_to_bf16_rne(((mu32 * m32) + g32).astype(np.float64))
+    if not nesterov:
+        return m_new, m_new
+    mn32 = bf16_to_f64(m_new).astype(np.float32)
+    u = f64_to_bf16_rne((g32 + (mu32 * mn32)).astype(np.float64))
+    return m_new, u
+
+
+def decay_and_update(w_bits, o, lr, wd, scale):
+    """W' = bf16( fl32( fl32(d W) - fl32(fl32(lr scale) O) ) ), d = fl32(1 - fl32(lr wd));
+    o: the update (float values as stored, e.g. bf16)."""
+    lr32, wd32, sc32 = np.float32(lr), np.float32(wd), np.float32(scale)
+    d = np.float32(np.float32(1.0) - lr32 * wd32)
+    lre = np.float32(lr32 * sc32)
+    w32 = bf16_to_f64(w_bits).astype(np.float32)
+    o32 = np.asarray(o, dtype=np.float64).astype(np.float32)
+    return f64_to_bf16_rne(((d * w32) - (lre * o32)).astype(np.float64))
+
+
+def muon_step(w, m, g, lr, wd=0.0, mu=0.95, nesterov=True, scale=None, steps=5, abc=JORDAN_ABC, eps=EPS,
+              storage="bf16", orthogonalize=None):
+    """One Muon step on one matrix.  Returns (W', M', O) with O the orthogonalised
+    update in float64.
+
+    storage="bf16": w, m, g are uint16 bf16 bit patterns, results likewise.
+    storage="f64":  w, m, g are float64 arrays and nothing is rounded.
+    scale: None for 0.2 sqrt(max(n, m)).
+    orthogonalize: function U -> O (default: standard Newton-Schulz)."""
+    ortho = orthogonalize or (lambda x: newton_schulz(x, steps, abc, eps))
+    n, mm = np.asarray(m).shape
+    if storage == "f64":
+        sc = 0.2 * np.sqrt(max(n, mm)) if scale is None else float(scale)
+        m1 = mu * np.asarray(m, np.float64) + np.asarray(g, np.float64)
+        u = np.asarray(g, np.float64) + mu * m1 if nesterov else m1
+        O = ortho(u)
+        w1 = (1.0 - lr * wd) * np.asarray(w, np.float64) - lr * sc * O
+        return w1, m1, O
+    sc = muon_scale(n, mm) if scale is None else np.float32(scale)
+    m1, u = momentum(m, g, mu, nesterov)
+    O = ortho(bf16_to_f64(u))
+    O_stored = bf16_to_f64(f64_to_bf16_rne(O))
+    w1 = decay_and_update(w, O_stored, lr, wd, sc)
+    return w1, m1, O
