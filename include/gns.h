@@ -270,6 +270,36 @@ int dion3_step_dev_scalars(void* W, void* M, const void* G, int N, int m, long l
                            const gns_schedule* sched, int* S_out, void* O_out,
                            void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes needed by muon_step_batched (0 for invalid arguments). */
+size_t muon_workspace_size(int batch, int n, int m, gns_dtype compute, int nesterov);
+
+/* One Muon step on `batch` same-shape n x m matrices ("Muon: Orthogonalized Momentum
+ * and Why It Trains LLMs 2x Cheaper", the step listed after "Doing an SVD without an
+ * SVD" and the notes on decoupled weight decay and update-scale matching):
+ *   M <- mu M + G                     (heavy-ball momentum, in place)
+ *   U  = G + mu M  with nesterov = 1  (lookahead on the updated M); U = M with 0
+ *   O  = GramNS(U)                    (the schedule and iterate dtype of
+ *                                      gns_orthogonalize_batched; a tall U runs on U^T)
+ *   W <- (1 - lr weight_decay) W - lr scale O   (decoupled decay first, in place)
+ * scale <= 0 selects 0.2 sqrt(max(n, m)) (fp32), which matches the update's RMS to
+ * AdamW's.  Dion3 with every row selected is this step without the lookahead.
+ * W, M, G: device bf16 [batch][n][ld], entry b at offset b * stride elements
+ * (stride >= n * ld when batch > 1); they must not overlap.  Each stored value (M, U,
+ * O, W) is rounded once to bf16 from fp32 arithmetic done op by op.
+ * O_out: nullable device bf16 [batch][n][m] (contiguous) that receives O; it must not
+ * overlap W, M, G or the workspace.  Workspace: muon_workspace_size(batch, n, m,
+ * compute, nesterov) bytes, 16-byte aligned, owned by the caller.  Asynchronous on
+ * `stream`; no host synchronisation.
+ * Errors (nothing is launched): GNS_ERR_INVALID_ARG for a null matrix, n or m < 1,
+ * ld < m, a short stride, overlapping buffers, nesterov not 0 or 1, or a non-finite
+ * scalar; GNS_ERR_UNSUPPORTED for n, m, ld or stride not a multiple of 8, a pointer
+ * not 16-byte aligned, or compute = GNS_F32; GNS_ERR_WORKSPACE for a short or null
+ * workspace; GNS_ERR_HIP for a launch failure (gns_last_error() describes it). */
+int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, long long ld,
+                      long long stride, float lr, float weight_decay, float mu, int nesterov,
+                      float scale, gns_dtype compute, const gns_schedule* sched, void* O_out,
+                      void* workspace, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

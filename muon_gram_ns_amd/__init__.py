@@ -8,7 +8,7 @@ from ._lib import (  # noqa: F401
     GNS_BF16, GNS_F16, GNS_F32, orthogonalize, newton_schulz, frobenius_scale, symm_gemm,
     rect_gemm, dion3_accumulate_score, dion3_select_topk, dion3_gather_feedback,
     dion3_apply_update, dion3_step, dion3_step_batched, dion3_step_rows,
-    dion3_step_dev_scalars, dion3_step_cols, workspace, workspace_size,
+    dion3_step_dev_scalars, dion3_step_cols, muon_step, muon_workspace_size, workspace, workspace_size,
 )
 from . import flops  # noqa: F401
 from .graphs import Graphed, graphed_orthogonalize, graphed_newton_schulz, graphed_dion3_step  # noqa: F401

@@ -5,8 +5,8 @@
 (run it by path: importing the package loads the library it is about to rebuild)
 
 Every source is compiled for gfx950 only.  Packed-fp32 instructions are disabled
-(-Xclang -target-feature -Xclang -packed-fp32-ops); the Dion3 file is compiled with
--ffp-contract=off so its fp32 update arithmetic is not fused into multiply-adds.
+(-Xclang -target-feature -Xclang -packed-fp32-ops); the Dion3 and Muon files are compiled
+with -ffp-contract=off so their fp32 update arithmetic is not fused into multiply-adds.
 """
 from __future__ import annotations
 
@@ -27,6 +27,7 @@ SOURCES = {
     "gemm_rect.hip": [],
     "elementwise.hip": [],
     "dion3.hip": ["-ffp-contract=off"],
+    "muon.hip": ["-ffp-contract=off"],
     "gns_abi.cpp": [],
 }
 

@@ -22,6 +22,7 @@
 #include <cstring>
 
 #include "internal.h"
+#include "muon_kernels.h"
 
 using namespace gns;
 
@@ -731,4 +732,81 @@ int dion3_step_rows(void* W, void* M, const void* G, int N, int m, long long ld,
                    O_out, workspace, ws_bytes, stream);
 }
 
+// Muon step workspace: U (the lookahead, only with nesterov), O, then the Gram NS
+// workspace of the batch.
+struct MuonLayout {
+  void *U, *O, *gns_ws;
+  size_t gns_bytes, bytes;
+};
+
+static MuonLayout muon_layout(void* base, int batch, int n, int m, gns_dtype cdt, int nesterov) {
+  Carver c{reinterpret_cast<uint8_t*>(base), 0};
+  MuonLayout L{};
+  const size_t elems = (size_t)batch * n * m;
+  L.U = nesterov ? c.take(elems * 2) : nullptr;
+  L.O = c.take(elems * 2);
+  L.gns_bytes = ns_workspace_bytes(batch, n, m, cdt);
+  L.gns_ws = c.take(L.gns_bytes);
+  L.bytes = c.off;
+  return L;
+}
+
+size_t muon_workspace_size(int batch, int n, int m, gns_dtype compute, int nesterov) {
+  if (batch < 1 || n < 1 || m < 1 || !valid_dtype(compute) || (nesterov != 0 && nesterov != 1)) return 0;
+  return muon_layout(nullptr, batch, n, m, compute, nesterov).bytes;
+}
+
+int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, long long ld, long long stride,
+                      float lr, float weight_decay, float mu, int nesterov, float scale, gns_dtype compute,
+                      const gns_schedule* sched, void* O_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (batch < 0) return GNS_ERR_INVALID_ARG;
+  if (batch == 0) return GNS_OK;
+  int st = check_dion3_matrix(W, n, m, ld);
+  if (st) return st;
+  if ((st = check_dion3_matrix(M, n, m, ld))) return st;
+  if ((st = check_dion3_matrix(G, n, m, ld))) return st;
+  if (batch > 1 && stride < (long long)n * ld) return GNS_ERR_INVALID_ARG;
+  if (batch > 1 && stride % 8) return GNS_ERR_UNSUPPORTED;
+  if (nesterov != 0 && nesterov != 1) return GNS_ERR_INVALID_ARG;
+  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu) || !std::isfinite(scale))
+    return GNS_ERR_INVALID_ARG;
+  if (!valid_dtype(compute)) return GNS_ERR_INVALID_ARG;
+  if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
+  if (O_out && !aligned16(O_out)) return GNS_ERR_UNSUPPORTED;
+  // W, M and G must be distinct (each is read and written by different passes)
+  const size_t span = ((size_t)(batch - 1) * (size_t)(batch > 1 ? stride : 0) + (size_t)(n - 1) * ld + m) * 2;
+  if (overlaps(W, span, M, span) || overlaps(W, span, G, span) || overlaps(M, span, G, span))
+    return GNS_ERR_INVALID_ARG;
+  gns_schedule sch;
+  if (sched) sch = *sched; else gns_default_schedule(&sch);
+  if ((st = check_schedule(sch))) return st;
+  const MuonLayout L = muon_layout(workspace, batch, n, m, compute, nesterov);
+  if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
+  // the update's RMS matched to AdamW's: 0.2 sqrt(max(n, m)) unless the caller gives one
+  const float sc = scale > 0.0f ? scale : 0.2f * std::sqrt((float)std::max(n, m));
+
+  void* O = O_out ? O_out : L.O;
+  const long long nm = (long long)n * m;
+  // the batched Gram NS of U (or of M itself without the lookahead); its arguments
+  // are checked before anything is launched
+  NsCall c = nesterov ? make_call(L.U, GNS_BF16, m, nm, O, GNS_BF16, m, nm, batch, n, m, compute, &sch, L.gns_ws,
+                                  L.gns_bytes, stream, nullptr)
+                      : make_call(M, GNS_BF16, ld, stride, O, GNS_BF16, m, nm, batch, n, m, compute, &sch, L.gns_ws,
+                                  L.gns_bytes, stream, nullptr);
+  if ((st = check_ns(c))) return st;
+  if (O_out && (overlaps(O_out, (size_t)batch * nm * 2, workspace, L.bytes) ||
+                overlaps(O_out, (size_t)batch * nm * 2, W, span) || overlaps(O_out, (size_t)batch * nm * 2, M, span) ||
+                overlaps(O_out, (size_t)batch * nm * 2, G, span)))
+    return GNS_ERR_INVALID_ARG;
+
+  HIP_OK(launch_muon_momentum((uint16_t*)M, (const uint16_t*)G, batch, n, m, ld, stride, mu, (uint16_t*)L.U, m, nm,
+                              stream));
+  if ((st = run_ns(c, true))) return st;
+  HIP_OK(launch_muon_update((uint16_t*)W, batch, n, m, ld, stride, (const uint16_t*)O, m, nm, lr, weight_decay, sc,
+                            stream));
+  return GNS_OK;
+}
+
 }  // extern "C"
+

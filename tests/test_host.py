@@ -145,6 +145,46 @@ def test_gemm_and_dion3_validation():
     assert L.dion3_select_topk(FAKE, 10, 0, FAKE, None) == INVALID
 
 
+def test_muon_validation():
+    """The Muon step checks every argument before any launch: each rejected call
+    below returns its error code.  On a machine without a GPU a well-formed call
+    reaches the launch and reports GNS_ERR_HIP, which it could not before the checks
+    had passed; with a GPU present those two calls are left out (their pointers are
+    not real)."""
+    sched = gns.default_schedule()
+    HIP = -4
+
+    def margs(B=2, n=64, m=256, ld=256, stride=64 * 256, W=FAKE, M=FAKE * 8, G=FAKE * 16, nest=1, lr=0.02,
+              scale=0.0, compute=F16, O=None, ws=FAKE * 40, wsb=1 << 40):
+        return (W, M, G, B, n, m, ld, stride, lr, 0.0, 0.95, nest, scale, compute, ctypes.byref(sched), O, ws, wsb,
+                None)
+
+    assert L.muon_step_batched(*margs(B=0)) == OK
+    assert L.muon_step_batched(*margs(B=-1)) == INVALID
+    assert L.muon_step_batched(*margs(W=None)) == INVALID
+    assert L.muon_step_batched(*margs(ld=248)) == INVALID                # ld < m
+    assert L.muon_step_batched(*margs(stride=64 * 256 - 8)) == INVALID   # entries overlap
+    assert L.muon_step_batched(*margs(M=FAKE + 64 * 256 * 2)) == INVALID  # M overlaps W's 2nd entry
+    assert L.muon_step_batched(*margs(nest=2)) == INVALID
+    assert L.muon_step_batched(*margs(lr=float("nan"))) == INVALID
+    assert L.muon_step_batched(*margs(scale=float("inf"))) == INVALID
+    assert L.muon_step_batched(*margs(m=252, ld=256)) == UNSUP            # m not a multiple of 8
+    assert L.muon_step_batched(*margs(n=60, stride=60 * 256)) == UNSUP    # n not a multiple of 8
+    assert L.muon_step_batched(*margs(compute=F32)) == UNSUP
+    assert L.muon_step_batched(*margs(W=FAKE + 2)) == UNSUP               # misaligned
+    assert L.muon_step_batched(*margs(ws=None)) == WS
+    assert L.muon_step_batched(*margs(wsb=8)) == WS
+    assert L.muon_step_batched(*margs(O=FAKE * 40 + 4096)) == INVALID     # O inside the workspace
+    assert L.muon_step_batched(*margs(O=FAKE * 8)) == INVALID             # O is M
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert L.muon_step_batched(*margs()) == HIP                       # valid: reaches the launch
+        assert L.muon_step_batched(*margs(nest=0, B=1, n=512, m=64, ld=64, stride=0)) == HIP   # tall, no lookahead
+    with_u = L.muon_workspace_size(2, 64, 256, F16, 1)
+    assert with_u - L.muon_workspace_size(2, 64, 256, F16, 0) >= 2 * 64 * 256 * 2
+    assert L.muon_workspace_size(2, 64, 256, F16, 2) == 0
+
+
 def test_workspace_sizes_grow_with_problem():
     a = L.gns_workspace_size(1, 1024, 4096, F16)
     b = L.gns_workspace_size(2, 1024, 4096, F16)
