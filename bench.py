@@ -128,6 +128,8 @@ def main():
     ms_std_graph = timed_ms(graphed_std.replay, nstd, max(2, args.warmup // 4))
     del graphed, graphed_std
 
+    muon = muon_timing(gns, torch, X, compute, sched, timed_ms, nstd, max(2, args.warmup // 4), ms) \
+        if w.dtype == "bf16" else None
     roof = dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, args.steps, w.name)
     line = {
         "metric": METRIC,
@@ -157,6 +159,7 @@ def main():
                                      "matrices_per_s": round(B / (ms_std * 1e-3), 3),
                                      "gram_speedup": round(ms_std / ms, 3),
                                      "graph_replay_ms_per_step": round(ms_std_graph, 5)},
+        "muon_step_same_batch": muon,
         "roofline": roof,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(st, w, args.cpu_seconds),
     }
@@ -297,6 +300,25 @@ def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, wor
     roof.update({"traffic": traffic, "mfma_tflops": round(tflops, 3),
                  "mfma_frac": round(tflops / PEAK_16BIT_TFLOPS, 5)})
     return roof
+
+
+def muon_timing(gns, torch, X, compute, sched, timed_ms, steps, warmup, ms_gram):
+    """The whole Muon step (muon_step_batched: momentum with the lookahead, Gram NS,
+    decoupled decay and the scaled update) on the same batch, against the Gram NS call
+    alone.  The element-wise passes move 7 n m bf16 values per matrix (read M, G; write
+    M, U; read W, O; write W); their rate is estimated from the difference of the two
+    timings."""
+    B, n, m = X.shape
+    W, M, G = X.clone(), X.clone(), X
+    ms_muon = timed_ms(lambda: gns.muon_step(W, M, G, 1e-4, weight_decay=0.1, compute=compute, schedule=sched),
+                       steps, warmup)
+    extra = ms_muon - ms_gram
+    nbytes = 7.0 * B * n * m * 2
+    return {"ms_per_step": round(ms_muon, 5), "matrices_per_s": round(B / (ms_muon * 1e-3), 3),
+            "gram_ns_alone_ms": round(ms_gram, 5), "elementwise_ms_by_difference": round(extra, 5),
+            "elementwise_bytes": nbytes,
+            "elementwise_GB_s_by_difference": round(nbytes / (extra * 1e-3) / 1e9, 1) if extra > 0 else None,
+            "nesterov": True, "scale": "0.2 sqrt(max(n, m))"}
 
 
 def per_call_ms(torch, stream, fn, n):
