@@ -11,4 +11,6 @@ from ._lib import (  # noqa: F401
     dion3_step_dev_scalars, dion3_step_cols, muon_step, muon_workspace_size, workspace, workspace_size,
 )
 from . import flops  # noqa: F401
-from .graphs import Graphed, graphed_orthogonalize, graphed_newton_schulz, graphed_dion3_step  # noqa: F401
+from .graphs import (  # noqa: F401
+    Graphed, graphed_orthogonalize, graphed_newton_schulz, graphed_dion3_step, graphed_muon_step,
+)

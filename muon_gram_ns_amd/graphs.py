@@ -105,3 +105,25 @@ def graphed_dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, 
 
     g.set_scalars = set_scalars
     return g
+
+
+def graphed_muon_step(W, M, G, lr, weight_decay=0.0, mu=0.95, nesterov=True, scale=None, compute="f16",
+                      schedule=None, return_O=False) -> Graphed:
+    """One Muon step (muon_step) on W, M (in place) and G, each [n, m] or [B, n, m],
+    captured; each replay() runs one more step on the buffers' current contents and
+    returns O when return_O (else None)."""
+    torch = _lib._torch()
+    B, n, m = (1, *W.shape) if W.dim() == 2 else tuple(W.shape)
+    O = torch.empty(W.shape, dtype=torch.bfloat16, device=W.device) if return_O else None
+    ws = torch.empty(max(_lib.muon_workspace_size(B, n, m, compute, nesterov), 256), dtype=torch.uint8,
+                     device=W.device)
+    sched = schedule if schedule is not None else _lib.default_schedule()
+    fn = (lambda: _lib.muon_step(W, M, G, lr, weight_decay, mu, nesterov, scale, compute, sched, O=O, workspace=ws))
+    # the warm-up calls run real steps, so the caller's W and M are restored after them
+    saved = (W.clone(), M.clone())
+    g = Graphed(fn)
+    W.copy_(saved[0])
+    M.copy_(saved[1])
+    torch.cuda.synchronize()
+    g.W, g.M, g.G, g.O, g.workspace, g.schedule = W, M, G, O, ws, sched
+    return g

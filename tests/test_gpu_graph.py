@@ -111,3 +111,30 @@ def test_graphed_dion3_with_device_scalars_follows_a_schedule(gns_mod):
         assert np.array_equal(S.cpu().numpy(), Se[i])
     assert np.array_equal(bits(Wg), bits(We))
     assert np.array_equal(bits(Mg), bits(Me))
+
+
+def test_graphed_muon_steps_match_eager_steps(gns_mod):
+    """Three replays of a captured Muon step on a batch of three equal three eager
+    steps from the same state, bitwise (W, M and O), with the gradient refilled in
+    place between steps."""
+    import torch
+    announce("graphed muon")
+    st = [synth.dion3_state(n=256, m=1024, seed=60 + b) for b in range(3)]
+    w = np.stack([s[0] for s in st])
+    m = np.stack([s[2] for s in st])
+    grads = [np.stack([synth.dion3_state(n=256, m=1024, seed=70 + 3 * i + b)[1] for b in range(3)]) for i in range(3)]
+    tb = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    We, Me = tb(w), tb(m)
+    Oe = []
+    for gr in grads:
+        Oe.append(bits(gns_mod.muon_step(We, Me, tb(gr), 0.02, weight_decay=0.1, mu=0.95, return_O=True)))
+    Wg, Mg, Gg = tb(w), tb(m), tb(grads[0])
+    step = gns_mod.graphed_muon_step(Wg, Mg, Gg, 0.02, weight_decay=0.1, mu=0.95, return_O=True)
+    assert np.array_equal(bits(Wg), w.view(np.uint16)) and np.array_equal(bits(Mg), m.view(np.uint16))
+    for i, gr in enumerate(grads):
+        Gg.copy_(tb(gr))
+        O = step.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(O), Oe[i])
+    assert np.array_equal(bits(Wg), bits(We))
+    assert np.array_equal(bits(Mg), bits(Me))
