@@ -279,7 +279,9 @@ size_t muon_workspace_size(int batch, int n, int m, gns_dtype compute, int neste
  *   M <- mu M + G                     (heavy-ball momentum, in place)
  *   U  = G + mu M  with nesterov = 1  (lookahead on the updated M); U = M with 0
  *   O  = GramNS(U)                    (the schedule and iterate dtype of
- *                                      gns_orthogonalize_batched; a tall U runs on U^T)
+ *                                      gns_orthogonalize_batched; a tall U runs on U^T;
+ *                                      ||U||_F from fp64 row sums formed in the
+ *                                      momentum pass)
  *   W <- (1 - lr weight_decay) W - lr scale O   (decoupled decay first, in place)
  * scale <= 0 selects 0.2 sqrt(max(n, m)) (fp32), which matches the update's RMS to
  * AdamW's.  Dion3 with every row selected is this step without the lookahead.

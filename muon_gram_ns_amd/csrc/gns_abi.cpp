@@ -732,9 +732,11 @@ int dion3_step_rows(void* W, void* M, const void* G, int N, int m, long long ld,
                    O_out, workspace, ws_bytes, stream);
 }
 
-// Muon step workspace: U (the lookahead, only with nesterov), O, then the Gram NS
-// workspace of the batch.
+// Muon step workspace: the row sums of squares and the scale of each matrix, U (the
+// lookahead, only with nesterov), O, then the Gram NS workspace of the batch.
 struct MuonLayout {
+  double* rowsq;
+  float* s;
   void *U, *O, *gns_ws;
   size_t gns_bytes, bytes;
 };
@@ -743,6 +745,8 @@ static MuonLayout muon_layout(void* base, int batch, int n, int m, gns_dtype cdt
   Carver c{reinterpret_cast<uint8_t*>(base), 0};
   MuonLayout L{};
   const size_t elems = (size_t)batch * n * m;
+  L.rowsq = (double*)c.take(sizeof(double) * (size_t)batch * n);
+  L.s = (float*)c.take(sizeof(float) * (size_t)batch);
   L.U = nesterov ? c.take(elems * 2) : nullptr;
   L.O = c.take(elems * 2);
   L.gns_bytes = ns_workspace_bytes(batch, n, m, cdt);
@@ -794,6 +798,8 @@ int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, 
                                   L.gns_bytes, stream, nullptr)
                       : make_call(M, GNS_BF16, ld, stride, O, GNS_BF16, m, nm, batch, n, m, compute, &sch, L.gns_ws,
                                   L.gns_bytes, stream, nullptr);
+  // the momentum pass also forms each matrix's Frobenius scale
+  c.s_given = L.s;
   if ((st = check_ns(c))) return st;
   if (O_out && (overlaps(O_out, (size_t)batch * nm * 2, workspace, L.bytes) ||
                 overlaps(O_out, (size_t)batch * nm * 2, W, span) || overlaps(O_out, (size_t)batch * nm * 2, M, span) ||
@@ -801,7 +807,7 @@ int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, 
     return GNS_ERR_INVALID_ARG;
 
   HIP_OK(launch_muon_momentum((uint16_t*)M, (const uint16_t*)G, batch, n, m, ld, stride, mu, (uint16_t*)L.U, m, nm,
-                              stream));
+                              L.rowsq, sch.eps, L.s, stream));
   if ((st = run_ns(c, true))) return st;
   HIP_OK(launch_muon_update((uint16_t*)W, batch, n, m, ld, stride, (const uint16_t*)O, m, nm, lr, weight_decay, sc,
                             stream));

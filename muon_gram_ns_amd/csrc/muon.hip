@@ -38,12 +38,30 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// fp64 sum over the workgroup; the total is valid in thread 0
+__device__ __forceinline__ double muon_block_sum(double v, double* sh) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0)
+    for (int i = 0; i < kMuonThreads / 64; ++i) t += sh[i];
+  return t;
+}
+
 // M' = bf16(fl32(mu M) + G);  U = bf16(G + fl32(mu M')) when U is given.  M and G
-// share the row stride ld and matrix stride; U is [batch][n][ldu].
+// share the row stride ld and matrix stride; U is [batch][n][ldu].  rowsq[b][r]
+// receives the fp64 sum of squares of row r of the matrix the orthogonalisation reads
+// (U, or M' without the lookahead), so its Frobenius norm needs no further pass.
 __global__ void __launch_bounds__(kMuonThreads)
-muon_momentum_kernel(uint16_t* M, const uint16_t* G, int m, long long ld, long long stride, float mu, uint16_t* U,
-                     long long ldu, long long su) {
+muon_momentum_kernel(uint16_t* M, const uint16_t* G, int n, int m, long long ld, long long stride, float mu,
+                     uint16_t* U, long long ldu, long long su, double* rowsq) {
+  __shared__ double sh[kMuonThreads / 64];
   const int r = blockIdx.x, b = blockIdx.y;
+  double acc = 0.0;
   uint4* mr = reinterpret_cast<uint4*>(M + (size_t)b * stride + (size_t)r * ld);
   const uint4* gr = reinterpret_cast<const uint4*>(G + (size_t)b * stride + (size_t)r * ld);
   uint4* ur = U ? reinterpret_cast<uint4*>(U + (size_t)b * su + (size_t)r * ldu) : nullptr;
@@ -61,18 +79,43 @@ muon_momentum_kernel(uint16_t* M, const uint16_t* G, int m, long long ld, long l
                                     __fadd_rn(__fmul_rn(mu, hi_f32(mw[i])), g1));
       mw[i] = mn;
       uw[i] = pack_bf16(__fadd_rn(g0, __fmul_rn(mu, lo_f32(mn))), __fadd_rn(g1, __fmul_rn(mu, hi_f32(mn))));
+      const uint32_t x = ur ? uw[i] : mn;          // what the orthogonalisation reads
+      const double x0 = (double)lo_f32(x), x1 = (double)hi_f32(x);
+      acc += x0 * x0;
+      acc += x1 * x1;
     }
     store_stream(mv, &mr[c]);
     if (ur) ur[c] = uv;      // read next by the Gram product: an ordinary store
   }
+  const double t = muon_block_sum(acc, sh);
+  if (threadIdx.x == 0) rowsq[(size_t)b * n + r] = t;
+}
+
+// s[b] = 1 / (sqrt(sum_r rowsq[b][r]) + eps), one workgroup per matrix; each thread
+// adds a contiguous range of rows in order, so the result does not depend on the batch.
+__global__ void __launch_bounds__(kMuonThreads)
+muon_scale_kernel(const double* rowsq, int n, float eps, float* s) {
+  __shared__ double sh[kMuonThreads / 64];
+  const int b = blockIdx.x;
+  rowsq += (size_t)b * n;
+  const int per = (n + kMuonThreads - 1) / kMuonThreads;
+  const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
+  double acc = 0.0;
+  for (int i = lo; i < hi; ++i) acc += rowsq[i];
+  const double t = muon_block_sum(acc, sh);
+  if (threadIdx.x == 0) s[b] = (float)(1.0 / (sqrt(t) + (double)eps));
 }
 
 hipError_t launch_muon_momentum(uint16_t* M, const uint16_t* G, int batch, int n, int m, long long ld,
-                                long long stride, float mu, uint16_t* U, long long ldu, long long su, hipStream_t s) {
+                                long long stride, float mu, uint16_t* U, long long ldu, long long su, double* rowsq,
+                                float eps, float* s_out, hipStream_t s) {
   if (batch <= 0 || n <= 0) return hipSuccess;
   clear_stale_error();
-  hipLaunchKernelGGL(muon_momentum_kernel, dim3(n, batch), dim3(kMuonThreads), 0, s, M, G, m, ld, stride, mu, U, ldu,
-                     su);
+  hipLaunchKernelGGL(muon_momentum_kernel, dim3(n, batch), dim3(kMuonThreads), 0, s, M, G, n, m, ld, stride, mu, U,
+                     ldu, su, rowsq);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(muon_scale_kernel, dim3(batch), dim3(kMuonThreads), 0, s, rowsq, n, eps, s_out);
   return hipGetLastError();
 }
 
