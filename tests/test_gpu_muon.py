@@ -4,8 +4,9 @@ Bit-exact: the momentum M after each step, and W given the GPU's own O (the deca
 and the scaled update are element-wise with one rounding).  Within tolerance: O
 (relative Frobenius <= 2e-2 against float64 standard NS of the oracle's U), and W
 against the oracle's full step (elementwise within one bf16 rounding plus lr scale
-times O's tolerance).  Shapes cover a ragged batch, a tall matrix and the 1024 x 4096
-workload, with and without the lookahead and the weight decay.
+times O's tolerance).  Shapes cover a ragged batch, a tall matrix, rows with a
+stride wider than m, and the 1024 x 4096 workload, with and without the lookahead and
+the weight decay.
 """
 import numpy as np
 import pytest
@@ -106,3 +107,29 @@ def test_muon_explicit_scale(gns_mod):
     w_ref, _, o_ref = oracle.muon_step(w, mo, g, 0.02, nesterov=False, scale=1.0)
     assert rel_fro(to_f64(O), o_ref) <= 2e-2
     assert w_within_bound(bits(W), w_ref, 0.02, o_ref)
+
+
+@pytest.mark.parametrize("nesterov", [False, True])
+def test_muon_step_on_strided_rows(gns_mod, nesterov):
+    """W, M, G are column slices of wider buffers (row stride 320 for m = 256): the
+    momentum and update passes and, without the lookahead, the Gram NS read them in
+    place at that stride.  Same bars as the contiguous case; the padding columns are
+    left untouched."""
+    import torch
+    announce(f"muon strided rows nesterov={nesterov}")
+    n, m, ld = 128, 256, 320
+    w, g, mo = synth.dion3_state(n=n, m=m, seed=350)
+    pad = np.full((n, ld - m), 0x3F80, dtype=np.uint16)        # bf16 1.0
+    wide = lambda a: to_dev(np.concatenate([a, pad], axis=1), "bf16")
+    Wf, Mf, Gf = wide(w), wide(mo), wide(g)
+    W, M, G = Wf[:, :m], Mf[:, :m], Gf[:, :m]
+    assert W.stride() == (ld, 1)
+    O = gns_mod.muon_step(W, M, G, 0.02, weight_decay=0.1, nesterov=nesterov, return_O=True)
+    torch.cuda.synchronize()
+    w_ref, m_ref, o_ref = oracle.muon_step(w, mo, g, 0.02, wd=0.1, nesterov=nesterov)
+    assert np.array_equal(bits(M), m_ref)
+    assert rel_fro(to_f64(O), o_ref) <= 2e-2
+    sc = float(muon_scale(n, m))
+    assert np.array_equal(bits(W), decay_and_update(w, bf16_to_f64(bits(O)), 0.02, 0.1, sc))
+    for full in (Wf, Mf, Gf):
+        assert np.array_equal(bits(full[:, m:]), pad)
