@@ -4,9 +4,9 @@ Bit-exact: the momentum M after each step, and W given the GPU's own O (the deca
 and the scaled update are element-wise with one rounding).  Within tolerance: O
 (relative Frobenius <= 2e-2 against float64 standard NS of the oracle's U), and W
 against the oracle's full step (elementwise within one bf16 rounding plus lr scale
-times O's tolerance).  Shapes cover a ragged batch, a tall matrix, rows with a
-stride wider than m, and the 1024 x 4096 workload, with and without the lookahead and
-the weight decay.
+times O's tolerance).  Shapes cover a ragged batch, a tall matrix, square matrices
+(which run standard NS, the aspect-ratio-1 fallback), rows with a stride wider than m,
+and the 1024 x 4096 workload, with and without the lookahead and the weight decay.
 """
 import numpy as np
 import pytest
@@ -35,7 +35,8 @@ def w_within_bound(w_gpu_bits, w_ref_bits, lr_eff, o_ref, o_tol=2e-2):
 
 
 @pytest.mark.parametrize("B,n,m,nesterov,wd", [(1, 64, 256, True, 0.0), (3, 136, 200, False, 0.1),
-                                              (2, 256, 64, True, 0.1), (1, 1024, 4096, True, 0.0)])
+                                              (2, 256, 64, True, 0.1), (1, 1024, 4096, True, 0.0),
+                                              (2, 256, 256, True, 0.1), (2, 256, 256, False, 0.0)])
 def test_muon_step_matches_oracle(gns_mod, B, n, m, nesterov, wd):
     announce(f"muon step B={B} {n}x{m} nesterov={nesterov} wd={wd}")
     w, g, mo = states(B, n, m, seed=200 + n)
