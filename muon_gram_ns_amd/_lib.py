@@ -332,7 +332,7 @@ def _rows(x):
 
 def _bf16_rows(x, name):
     torch = _torch()
-    _expect(x, name, dtype=torch.bfloat16)
+    _expect(_dev(x), name, dtype=torch.bfloat16)
     return _rows(x)
 
 
@@ -523,7 +523,7 @@ def dion3_step_batched(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, 
     G; the B selected k x m submatrices are orthogonalized by one batched Gram NS.
     Returns S [B, k] int32 (and O [B, k, m] when return_O or O is given)."""
     torch = _torch()
-    _expect(W, "W", dtype=torch.bfloat16)
+    _expect(_dev(W), "W", dtype=torch.bfloat16)
     if W.dim() != 3 or W.stride(2) != 1:
         raise ValueError("W must be a [B, N, m] tensor with contiguous rows")
     B, N, m = W.shape
@@ -563,7 +563,7 @@ def muon_step(W, M, G, lr, weight_decay=0.0, mu=0.95, nesterov=True, scale=None,
     = 0.2 sqrt(max(n, m)) unless given.  Returns O ([.., n, m] bf16) when return_O or O
     is given, else None."""
     torch = _torch()
-    _expect(W, "W", dtype=torch.bfloat16)
+    _expect(_dev(W), "W", dtype=torch.bfloat16)
     if W.dim() not in (2, 3) or W.stride(-1) != 1:
         raise ValueError("W must be an [n, m] or [B, n, m] tensor with contiguous rows")
     W3 = W if W.dim() == 3 else W.unsqueeze(0)

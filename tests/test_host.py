@@ -232,3 +232,29 @@ def test_binding_rejects_mismatched_tensors_before_any_call():
         gns.rect_gemm(a, a)
     with pytest.raises(ValueError):
         gns.orthogonalize(a)
+
+
+def test_missing_library_fails_loudly():
+    """Without the built HIP library the package does not import: there is no CPU
+    fallback to fall back on."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, GNS_LIBRARY=os.path.join(root, "no_such_dir", "libgns.so"))
+    r = subprocess.run([sys.executable, "-c", "import muon_gram_ns_amd"], env=env, cwd=root, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0
+    assert "is missing" in r.stderr
+
+
+def test_binding_refuses_cpu_tensors():
+    """Host tensors are refused before any pointer reaches the library."""
+    import torch
+    x = torch.zeros(64, 256, dtype=torch.bfloat16)
+    calls = [lambda: gns.orthogonalize(x), lambda: gns.newton_schulz(x),
+             lambda: gns.muon_step(x, x.clone(), x.clone(), 0.01),
+             lambda: gns.dion3_step(x, x.clone(), x.clone(), 16, 0.01),
+             lambda: gns.dion3_step_batched(x[None], x.clone()[None], x.clone()[None], 16, 0.01)]
+    for call in calls:
+        with pytest.raises(ValueError, match="no CPU path"):
+            call()
