@@ -64,6 +64,16 @@ def decay_and_update(w_bits, o, lr, wd, scale):
     return f64_to_bf16_rne(((d * w32) - (lre * o32)).astype(np.float64))
 
 
+def _arith(storage):
+    """(number type, store) of a storage mode: "bf16" rounds every stored value once
+    to bf16 from float32 arithmetic; "f64" keeps float64 values and rounds nothing."""
+    if storage == "bf16":
+        return np.float32, lambda v: bf16_to_f64(f64_to_bf16_rne(np.asarray(v, np.float64)))
+    if storage == "f64":
+        return np.float64, lambda v: np.asarray(v, np.float64)
+    raise ValueError(storage)
+
+
 def muon_step(w, m, g, lr, wd=0.0, mu=0.95, nesterov=True, scale=None, steps=5, abc=JORDAN_ABC, eps=EPS,
               storage="bf16", orthogonalize=None):
     """One Muon step on one matrix.  Returns (W', M', O) with O the orthogonalised
@@ -72,19 +82,28 @@ def muon_step(w, m, g, lr, wd=0.0, mu=0.95, nesterov=True, scale=None, steps=5, 
     storage="bf16": w, m, g are uint16 bf16 bit patterns, results likewise.
     storage="f64":  w, m, g are float64 arrays and nothing is rounded.
     scale: None for 0.2 sqrt(max(n, m)).
-    orthogonalize: function U -> O (default: standard Newton-Schulz)."""
+    orthogonalize: function U -> O (default: standard Newton-Schulz).
+
+    Both modes run the same sequence: the momentum recursion and its lookahead, the
+    orthogonalised direction, then the decayed weights minus the scaled direction,
+    each formed in the mode's number type and stored through the mode's rounding."""
     ortho = orthogonalize or (lambda x: newton_schulz(x, steps, abc, eps))
+    num, store = _arith(storage)
     n, mm = np.asarray(m).shape
-    if storage == "f64":
-        sc = 0.2 * np.sqrt(max(n, mm)) if scale is None else float(scale)
-        m1 = mu * np.asarray(m, np.float64) + np.asarray(g, np.float64)
-        u = np.asarray(g, np.float64) + mu * m1 if nesterov else m1
-        O = ortho(u)
-        w1 = (1.0 - lr * wd) * np.asarray(w, np.float64) - lr * sc * O
-        return w1, m1, O
-    sc = muon_scale(n, mm) if scale is None else np.float32(scale)
-    m1, u = momentum(m, g, mu, nesterov)
-    O = ortho(bf16_to_f64(u))
-    O_stored = bf16_to_f64(f64_to_bf16_rne(O))
-    w1 = decay_and_update(w, O_stored, lr, wd, sc)
-    return w1, m1, O
+    if storage == "bf16":
+        W, Mo, Gr = (bf16_to_f64(v).astype(num) for v in (w, m, g))
+        sc = muon_scale(n, mm) if scale is None else num(scale)
+    else:
+        W, Mo, Gr = (np.asarray(v, np.float64) for v in (w, m, g))
+        sc = 0.2 * np.sqrt(max(n, mm)) if scale is None else num(scale)
+    mu_t, lr_t, wd_t = num(mu), num(lr), num(wd)
+    m_new = store(mu_t * Mo + Gr).astype(num)
+    direction = store(Gr + mu_t * m_new).astype(num) if nesterov else m_new
+    O = ortho(np.asarray(direction, np.float64))
+    o_stored = store(O).astype(num)
+    keep = num(1) - lr_t * wd_t
+    step = num(lr_t * num(sc))
+    w_new = store(keep * W - step * o_stored)
+    if storage == "bf16":
+        return f64_to_bf16_rne(w_new), f64_to_bf16_rne(m_new.astype(np.float64)), O
+    return w_new, np.asarray(m_new, np.float64), O

@@ -7,7 +7,8 @@ Sources:
     the input is divided by (Frobenius norm + 1e-7); a matrix with more rows than
     columns is transposed so the iteration runs on the short side.
   * "Dion3：全栈正交更新" (paper.rainbus.top), section 前置知识 (Newton-Schulz
-    iteration): one step maps X to a X + b X X^T X + c (X X^T)^2 X.
+    iteration): one step applies the odd quintic to X, which is the matrix
+    a X + b (X X^T) X + c (X X^T)^2 X.
   * Same page, section 核心方法 (theorem 2): writing each odd step as
     p_t(x) = x h_t(x^2) with h_t(r) = a_t + b_t r + c_t r^2, the composition
     p_T o ... o p_1 (x) equals q_T x, where r_0 = x^2, q_0 = 1, z_t = h_t(r_{t-1}),
@@ -63,22 +64,36 @@ def normalize(x, eps=EPS):
     return x / (np.sqrt(np.sum(x * x)) + eps)
 
 
+def _short_side(x):
+    """(Y, flipped): Y = X when X has no more rows than columns, else Y = X^T, so
+    that the iteration works with the smaller Gram matrix Y Y^T."""
+    return (x.T, True) if x.shape[0] > x.shape[1] else (x, False)
+
+
+def _odd_step_factor(gram, a, b, c):
+    """h(G) = a I + b G + c G^2 for the Gram matrix G = Y Y^T.
+
+    An odd quintic p(y) = a y + b y^3 + c y^5 factors as p(y) = h(y^2) y with
+    h(r) = a + b r + c r^2 (the factorisation behind theorem 2).  For a matrix Y,
+    p acts on every singular value, which is the left multiplication
+    p(Y) = h(Y Y^T) Y.  The factor is built here as a I + G (b I + c G)."""
+    eye = np.eye(gram.shape[0])
+    return a * eye + gram @ (b * eye + c * gram)
+
+
 def newton_schulz(x, steps=5, abc=JORDAN_ABC, eps=EPS):
     """Standard quintic Newton-Schulz on one matrix (the oracle of record).
 
-    For t = 1..T:  A = X X^T;  B = b_t A + c_t A A;  X <- a_t X + B X."""
+    Each step replaces Y by p_t(Y) = h_t(Y Y^T) Y, i.e. applies the odd quintic
+    p_t to every singular value of Y, starting from the Frobenius-normalised input
+    on its short side; T = `steps` steps with the per-step (a_t, b_t, c_t)."""
     x = np.asarray(x, dtype=np.float64)
     if x.ndim == 3:
         return np.stack([newton_schulz(xi, steps, abc, eps) for xi in x])
-    xn = normalize(x, eps)
-    transposed = xn.shape[0] > xn.shape[1]
-    if transposed:
-        xn = xn.T
+    y, flipped = _short_side(normalize(x, eps))
     for a, b, c in _coeffs(abc, steps):
-        A = xn @ xn.T
-        B = b * A + c * (A @ A)
-        xn = a * xn + B @ xn
-    return xn.T if transposed else xn
+        y = _odd_step_factor(y @ y.T, a, b, c) @ y
+    return y.T if flipped else y
 
 
 def gram_newton_schulz_schedule(steps=5, restart_after=(2,)):
@@ -98,10 +113,7 @@ def gram_newton_schulz(x, steps=5, abc=JORDAN_ABC, eps=EPS, restart_after=(2,),
     if x.ndim == 3:
         return np.stack([gram_newton_schulz(xi, steps, abc, eps, restart_after,
                                             perturb_r0, trace) for xi in x])
-    xn = normalize(x, eps)
-    transposed = xn.shape[0] > xn.shape[1]
-    if transposed:
-        xn = xn.T
+    xn, transposed = _short_side(normalize(x, eps))
     n = xn.shape[0]
     eye = np.eye(n)
     restarts = gram_newton_schulz_schedule(steps, restart_after)
