@@ -21,8 +21,8 @@
  *     DEVICE pointers; gns_schedule and issued_flops are HOST pointers.
  *   - Matrices are row-major.  "ld" is the row stride in elements, "stride" the batch
  *     stride in elements.  Rows must start 16-byte aligned: ld, stride, and the
- *     column counts n, m, k must be multiples of 8 (16-bit types) or 4 (fp32), and
- *     device pointers 16-byte aligned; each operand matrix must span less than
+ *     matrix dimensions n and m must be multiples of 8 (16-bit types) or 4 (fp32),
+ *     and device pointers 16-byte aligned (the Dion3 row count k may be any value); each operand matrix must span less than
  *     2 GiB (the kernels address it with 32-bit offsets); otherwise
  *     GNS_ERR_UNSUPPORTED (GNS_ERR_HIP from symm_gemm / rect_gemm).
  *   - The caller owns every buffer, including the workspace.  The library allocates
@@ -51,7 +51,7 @@ typedef enum {
   GNS_ERR_HIP = -4            /* a HIP launch or runtime call failed */
 } gns_status;
 
-typedef enum { GNS_BF16 = 0, GNS_F16 = 1, GNS_F32 = 2 } gns_dtype;
+typedef enum { GNS_BF16 = 0, GNS_F32 = 1, GNS_F16 = 2 } gns_dtype;
 
 #define GNS_MAX_STEPS 16
 
@@ -103,7 +103,12 @@ size_t gns_workspace_size(int batch, int n, int m, gns_dtype compute);
  * without an SVD"].  O: [batch][n][ldo], dtype o_dtype.
  * compute: dtype of the n x n iterates and of the MFMA operands after the first Gram
  * product: GNS_F16 (the pages' half precision, default), GNS_BF16, or GNS_F32.  All
- * products accumulate in fp32.  With x_dtype GNS_F32, compute must be GNS_F32.
+ * products accumulate in fp32.  With GNS_BF16 the Gram chain (R, Z and the R-update
+ * product) is stored as a hi/lo pair of bf16 planes, hi = bf16(v), lo = bf16(v - hi),
+ * and each of its products runs on bf16 MFMA as hi.hi + hi.lo + lo.hi: one bf16 R
+ * squares the condition number of X at 8 significant bits, which loses the small
+ * singular values on small and square inputs.  Q and the restarted X are single bf16
+ * matrices.  With x_dtype GNS_F32, compute must be GNS_F32.
  * sched: NULL = gns_default_schedule.  issued_flops (nullable, host): receives the
  * MFMA flops the call issues.  X is read-only; O must not alias X or the workspace.
  * A zero matrix gives a zero result.
@@ -191,9 +196,11 @@ size_t dion3_workspace_size(int N, int m, int k, gns_dtype compute);
  *   Frobenius norm taken from the per-row sums of squares); W <- decay + row update
  *   with lr (the caller passes lr = eta / sqrt(f)); M[S, :] <- mu M[S, :].
  * S_out: device int32[k] (ascending).  O_out: nullable device bf16 [k][m] (row stride
- * m) receiving O; it must not overlap W, M, G or the workspace.  1 <= k <= N, k a
- * multiple of 8; with k > m the k x m submatrix is orthogonalized through its
- * transpose, as in gns_orthogonalize_batched.  Every argument, including those of the
+ * m) receiving O; it must not overlap W, M, G or the workspace.  1 <= k <= N, any k
+ * (k = ceil(f N) on the pages): the submatrix is held with k rounded up to a multiple
+ * of 8 rows, the extra rows zero, which leaves O's k rows unchanged.  With k > m the
+ * k x m submatrix is orthogonalized through its transpose, as in
+ * gns_orthogonalize_batched.  Every argument, including those of the
  * Gram NS on the submatrix, is checked before the first launch. */
 int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int k,
                float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
@@ -211,7 +218,9 @@ size_t dion3_batched_workspace_size(int batch, int N, int m, int k, gns_dtype co
  * [paper.rainbus.top 方法步骤详情 (3) and (4); m.montaan.com summary].
  * S_out: device int32 [batch][k] (each row ascending).  O_out: nullable device bf16
  * [batch][k][m].  W, M and G must not overlap.  Each entry's result is bitwise the
- * result of dion3_step on that entry alone.  Errors as dion3_step. */
+ * result of dion3_step on that entry alone: every product's summation order depends
+ * on the matrix shape only, never on the batch size (a long-K Gram product that splits
+ * K splits the same way in any batch).  Errors as dion3_step. */
 int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m, long long ld,
                        long long stride, int k, float lr, float weight_decay, float mu,
                        int score_norm, gns_dtype compute, const gns_schedule* sched, int* S_out,
@@ -228,7 +237,7 @@ int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m,
  * this without a host synchronisation.  An index outside [0, N) reads as a zero row of
  * X and updates nothing; repeated or unordered indices give unspecified W and M (no
  * out-of-bounds access).  O_out: nullable device bf16 [k][m].  Workspace:
- * dion3_workspace_size(N, m, k, compute).  1 <= k <= N, k a multiple of 8; other
+ * dion3_workspace_size(N, m, k, compute).  1 <= k <= N (any k, as dion3_step); other
  * errors as dion3_step. */
 int dion3_step_rows(void* W, void* M, const void* G, int N, int m, long long ld, const int* S, int k,
                     float lr, float weight_decay, float mu, gns_dtype compute,
@@ -249,8 +258,9 @@ size_t dion3_cols_workspace_size(int N, int m, int k, gns_dtype compute);
  * the error feedback applied in place) and updated in the state's own row-major
  * layout.  S_out: device int32[k], ascending column indices.
  * O_out: nullable device bf16 [k][N]: row j is the update of column S[j] (the
- * transpose of the orthogonalised N x k submatrix).  1 <= k <= m, k and N multiples of
- * 8; W, M, G must not overlap; other errors as dion3_step. */
+ * transpose of the orthogonalised N x k submatrix).  1 <= k <= m (any k, padded as in
+ * dion3_step), N a multiple of 8; W, M, G must not overlap; other errors as
+ * dion3_step. */
 int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld, int k,
                     float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
                     const gns_schedule* sched, int* S_out, void* O_out,
@@ -283,8 +293,9 @@ size_t muon_workspace_size(int batch, int n, int m, gns_dtype compute, int neste
  *                                      ||U||_F from fp64 row sums formed in the
  *                                      momentum pass)
  *   W <- (1 - lr weight_decay) W - lr scale O   (decoupled decay first, in place)
- * scale <= 0 selects 0.2 sqrt(max(n, m)) (fp32), which matches the update's RMS to
- * AdamW's.  Dion3 with every row selected is this step without the lookahead.
+ * scale == 0 selects 0.2 sqrt(max(n, m)) (fp32), which matches the update's RMS to
+ * AdamW's; a negative scale is GNS_ERR_INVALID_ARG.  Dion3 with every row selected is
+ * this step without the lookahead.
  * W, M, G: device bf16 [batch][n][ld], entry b at offset b * stride elements
  * (stride >= n * ld when batch > 1); they must not overlap.  Each stored value (M, U,
  * O, W) is rounded once to bf16 from fp32 arithmetic done op by op.
@@ -293,9 +304,9 @@ size_t muon_workspace_size(int batch, int n, int m, gns_dtype compute, int neste
  * compute, nesterov) bytes, 16-byte aligned, owned by the caller.  Asynchronous on
  * `stream`; no host synchronisation.
  * Errors (nothing is launched): GNS_ERR_INVALID_ARG for a null matrix, n or m < 1,
- * ld < m, a short stride, overlapping buffers, nesterov not 0 or 1, or a non-finite
- * scalar; GNS_ERR_UNSUPPORTED for n, m, ld or stride not a multiple of 8, a pointer
- * not 16-byte aligned, or compute = GNS_F32; GNS_ERR_WORKSPACE for a short or null
+ * ld < m, a short stride, overlapping buffers, nesterov not 0 or 1, a negative
+ * scale, or a non-finite scalar; GNS_ERR_UNSUPPORTED for n, m, ld or stride not a
+ * multiple of 8, a pointer not 16-byte aligned, or compute = GNS_F32; GNS_ERR_WORKSPACE for a short or null
  * workspace; GNS_ERR_HIP for a launch failure (gns_last_error() describes it). */
 int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, long long ld,
                       long long stride, float lr, float weight_decay, float mu, int nesterov,

@@ -29,7 +29,7 @@ except ImportError:        # plain use without torch: libgns uses the system run
     pass
 lib = ctypes.CDLL(LIB_PATH)
 
-GNS_BF16, GNS_F16, GNS_F32 = 0, 1, 2
+GNS_BF16, GNS_F32, GNS_F16 = 0, 1, 2
 GNS_MAX_STEPS = 16
 STATUS = {0: "GNS_OK", -1: "GNS_ERR_INVALID_ARG", -2: "GNS_ERR_UNSUPPORTED",
           -3: "GNS_ERR_WORKSPACE", -4: "GNS_ERR_HIP"}
@@ -580,6 +580,8 @@ def muon_step(W, M, G, lr, weight_decay=0.0, mu=0.95, nesterov=True, scale=None,
         _expect(O, "O", dtype=torch.bfloat16, shape=W.shape, device=W.device)
         if not O.is_contiguous():
             raise ValueError("O must be contiguous")
+    if scale is not None and not float(scale) > 0.0:
+        raise ValueError(f"scale must be positive (None selects 0.2 sqrt(max(n, m))), got {scale}")
     sched = schedule if schedule is not None else default_schedule()
     nest = 1 if nesterov else 0
     ws = _workspace_arg(workspace, lib.muon_workspace_size(B, n, m, cdt, nest), W.device)

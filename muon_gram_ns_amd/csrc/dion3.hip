@@ -324,14 +324,16 @@ hipError_t launch_topk(const double* score, int batch, int N, int k, int* S, hip
 }
 
 // ---- X[r] = M[S[r]]; M[S[r]] <- bf16(mu * M[S[r]]) ----------------------------------
+// X holds kx >= k rows per batch entry: rows k .. kx-1 (the padding of the submatrix
+// to a whole number of 8-row groups) are written as zeros.
 __global__ void __launch_bounds__(kRowThreads)
-gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, long long stride, const int* S, int k, float mu_host,
-                       const float* dev_scalars, uint16_t* X, long long ldx) {
+gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, long long stride, const int* S, int k, int kx,
+                       float mu_host, const float* dev_scalars, uint16_t* X, long long ldx) {
   const int r = blockIdx.x, b = blockIdx.y;
   const float mu = dev_scalars ? dev_scalars[2] : mu_host;
-  const int src = S[(size_t)b * k + r];
-  uint4* xr = reinterpret_cast<uint4*>(X + ((size_t)b * k + r) * ldx);
-  if (src < 0 || src >= N) {           // precondition violated: a zero row of X, M untouched
+  const int src = r < k ? S[(size_t)b * k + r] : -1;
+  uint4* xr = reinterpret_cast<uint4*>(X + ((size_t)b * kx + r) * ldx);
+  if (src < 0 || src >= N) {           // padding row, or an index out of range: a zero row of X, M untouched
     for (int c = threadIdx.x; c < m / 8; c += kRowThreads) xr[c] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
@@ -351,11 +353,12 @@ gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, long long stride
 }
 
 hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long long ld, long long stride, const int* S,
-                                  int k, float mu, const float* dev_scalars, uint16_t* X, long long ldx, hipStream_t s) {
-  if (k <= 0 || batch <= 0) return hipSuccess;
+                                  int k, int kx, float mu, const float* dev_scalars, uint16_t* X, long long ldx,
+                                  hipStream_t s) {
+  if (k <= 0 || batch <= 0 || kx < k) return k <= 0 || batch <= 0 ? hipSuccess : hipErrorInvalidValue;
   clear_stale_error();
-  hipLaunchKernelGGL(gather_feedback_kernel, dim3(k, batch), dim3(kRowThreads), 0, s, M, N, m, ld, stride, S, k, mu,
-                     dev_scalars, X, ldx);
+  hipLaunchKernelGGL(gather_feedback_kernel, dim3(kx, batch), dim3(kRowThreads), 0, s, M, N, m, ld, stride, S, k, kx,
+                     mu, dev_scalars, X, ldx);
   return hipGetLastError();
 }
 
@@ -363,13 +366,13 @@ hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long lon
 template <bool O_F32>
 __global__ void __launch_bounds__(kRowThreads)
 apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, const int* S, int k, const void* O,
-                    long long ldo, float lr_host, float wd_host, const float* dev_scalars, int all_rows) {
+                    long long ldo, long long so, float lr_host, float wd_host, const float* dev_scalars, int all_rows) {
   const float lr = dev_scalars ? dev_scalars[0] : lr_host;
   const float wd = dev_scalars ? dev_scalars[1] : wd_host;
   const int d_over = blockIdx.x, b = blockIdx.y;
   W += (size_t)b * stride;
   S += (size_t)b * k;
-  O = reinterpret_cast<const uint8_t*>(O) + (size_t)b * k * ldo * (O_F32 ? 4 : 2);
+  O = reinterpret_cast<const uint8_t*>(O) + (size_t)b * so * (O_F32 ? 4 : 2);
   int row, oi;
   if (all_rows) {
     row = d_over;
@@ -427,7 +430,7 @@ apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, c
 }
 
 hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long ld, long long stride, const int* S, int k,
-                               const void* O, gns_dtype o_dtype, long long ldo, float lr, float wd,
+                               const void* O, gns_dtype o_dtype, long long ldo, long long so, float lr, float wd,
                                const float* dev_scalars, hipStream_t s) {
   // with the weight decay on the device the host cannot tell whether unselected rows
   // decay: cover all rows (each unselected row returns at once when wd == 0)
@@ -437,10 +440,10 @@ hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long l
   clear_stale_error();
   if (o_dtype == GNS_F32)
     hipLaunchKernelGGL(apply_update_kernel<true>, dim3(blocks, batch), dim3(kRowThreads), 0, s, W, N, m, ld, stride, S,
-                       k, O, ldo, lr, wd, dev_scalars, all_rows);
+                       k, O, ldo, so, lr, wd, dev_scalars, all_rows);
   else
     hipLaunchKernelGGL(apply_update_kernel<false>, dim3(blocks, batch), dim3(kRowThreads), 0, s, W, N, m, ld, stride,
-                       S, k, O, ldo, lr, wd, dev_scalars, all_rows);
+                       S, k, O, ldo, so, lr, wd, dev_scalars, all_rows);
   return hipGetLastError();
 }
 
@@ -566,7 +569,7 @@ reduce_colscore_kernel(const double* part_s, const double* part_q, int nparts, i
 // Xt[j, i] = M[i, S[j]] (Xt: k x N, row stride ldx) and M[i, S[j]] <- bf16(mu M[i, S[j]]).
 // An index S[j] outside [0, m) gives a zero row of Xt and touches M nowhere.
 __global__ void __launch_bounds__(kColThreads)
-gather_cols_feedback_kernel(uint16_t* M, int N, int m, long long ld, const int* S, int k, float mu,
+gather_cols_feedback_kernel(uint16_t* M, int N, int m, long long ld, const int* S, int k, int kx, float mu,
                             uint16_t* Xt, long long ldx) {
   __shared__ __align__(16) uint16_t tile[kColTile][kColTile + 2];   // [j][i]; rows of 132 bytes
   const int j0 = blockIdx.x * kColTile, i0 = blockIdx.y * kColTile;
@@ -585,9 +588,10 @@ gather_cols_feedback_kernel(uint16_t* M, int N, int m, long long ld, const int* 
     tile[lane][r] = x;
   }
   __syncthreads();
-  // row jr of the tile, 16 values from column 16 q: two 16-byte stores
+  // row jr of the tile, 16 values from column 16 q: two 16-byte stores; rows k .. kx-1
+  // (padding to a whole number of 8-row groups) are written as zeros
   const int jr = threadIdx.x >> 2, qd = threadIdx.x & 3;
-  if (j0 + jr >= k) return;
+  if (j0 + jr >= kx) return;
   const uint32_t* t32 = reinterpret_cast<const uint32_t*>(&tile[jr][0]);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -686,12 +690,13 @@ hipError_t launch_accumulate_colscore(uint16_t* M, const uint16_t* G, int N, int
   return hipGetLastError();
 }
 
-hipError_t launch_gather_cols_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, float mu,
-                                       uint16_t* Xt, long long ldx, hipStream_t s) {
+hipError_t launch_gather_cols_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, int kx,
+                                       float mu, uint16_t* Xt, long long ldx, hipStream_t s) {
   if (k <= 0 || N <= 0) return hipSuccess;
+  if (kx < k) return hipErrorInvalidValue;
   clear_stale_error();
-  hipLaunchKernelGGL(gather_cols_feedback_kernel, dim3((k + kColTile - 1) / kColTile, (N + kColTile - 1) / kColTile),
-                     dim3(kColThreads), 0, s, M, N, m, ld, S, k, mu, Xt, ldx);
+  hipLaunchKernelGGL(gather_cols_feedback_kernel, dim3((kx + kColTile - 1) / kColTile, (N + kColTile - 1) / kColTile),
+                     dim3(kColThreads), 0, s, M, N, m, ld, S, k, kx, mu, Xt, ldx);
   return hipGetLastError();
 }
 

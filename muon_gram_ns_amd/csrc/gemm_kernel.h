@@ -211,6 +211,7 @@ struct EpiPtrs {
   uint8_t* D2;
   const uint8_t* C;
   float alpha;
+  int c_planes, d_planes;     // 1, or 2 for a hi/lo pair of planes
 };
 
 // The Frobenius scale of batch entry bz from its partial sums of squares (at most
@@ -251,6 +252,8 @@ __device__ __forceinline__ EpiPtrs epi_ptrs(const GemmParams& p, int bz, bool se
   e.D = reinterpret_cast<uint8_t*>(D) + (size_t)bz * p.sD * TOut::kBytes;
   e.D2 = (p.D2 && !second) ? reinterpret_cast<uint8_t*>(p.D2) + (size_t)bz * p.sD2 * TOut::kBytes : nullptr;
   e.C = C ? reinterpret_cast<const uint8_t*>(C) + (size_t)bz * p.sC * TOut::kBytes : nullptr;
+  e.c_planes = second ? p.c2_planes : p.c_planes;
+  e.d_planes = second ? p.dp_planes : p.d_planes;
   return e;
 }
 
@@ -654,6 +657,29 @@ __device__ __forceinline__ void store_vec(uint8_t* base, long long ld, int row, 
   }
 }
 
+// store_vec of v into a matrix of `planes` planes: with 2, hi = round(v) goes to
+// base and lo = round(v - hi) to base + plane elements (v - hi is exact in fp32).
+template <class TOut>
+__device__ __forceinline__ void store_planes(uint8_t* base, long long ld, int row, int col,
+                                             const float (&v)[16 / TOut::kBytes], int lo, int hi, int planes,
+                                             long long plane) {
+  constexpr int VE = 16 / TOut::kBytes;
+  if constexpr (TOut::kBytes == 2) {
+    if (planes == 2) {
+      float h[VE], l[VE];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        h[e] = TOut::to_f32(TOut::from_f32(v[e]));
+        l[e] = v[e] - h[e];
+      }
+      store_vec<TOut>(base, ld, row, col, h, lo, hi);
+      store_vec<TOut>(base + plane * TOut::kBytes, ld, row, col, l, lo, hi);
+      return;
+    }
+  }
+  store_vec<TOut>(base, ld, row, col, v, lo, hi);
+}
+
 typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
 // store_vec of a whole 16-byte vector with a non-temporal store (no cache allocation)
 template <class TOut>
@@ -675,7 +701,7 @@ __device__ __forceinline__ void store_vec_nt(uint8_t* base, long long ld, int ro
 // at their transposed positions.  Both triangles round the same fp32 value, so the
 // output is bitwise symmetric.  Only the slab writes index the accumulators, so
 // they stay in registers.
-template <class TOut, bool LOWER, int FM, int FN, bool NT = false>
+template <class TOut, bool LOWER, int FM, int FN, bool NT = false, bool PL = false>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc)[FM][FN], const GridPos& gp,
                                              int mw, int nw, int lane, float* slab) {
   const int bz = gp.bz;
@@ -687,6 +713,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc
   const EpiPtrs ep = epi_ptrs<TOut>(p, bz, gp.second, gp.psc);
   const bool has_c = ep.C != nullptr && p.beta != 0.0f;
   const int M = p.M, N = p.N;
+  const int c_pl = PL ? ep.c_planes : 1, d_pl = PL ? ep.d_planes : 1;   // hi/lo planes (PL kernels only)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int r0 = mw + 32 * i;
@@ -712,7 +739,14 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc
       }
       if (has_c) {
         float cv[VE];
-        unpack16<TOut>(*reinterpret_cast<const uint4*>(ep.C + ((long long)gm * p.ldc + gn) * TOut::kBytes), cv);
+        const uint8_t* cp = ep.C + ((long long)gm * p.ldc + gn) * TOut::kBytes;
+        unpack16<TOut>(*reinterpret_cast<const uint4*>(cp), cv);
+        if (c_pl == 2) {      // C = hi + lo
+          float cl[VE];
+          unpack16<TOut>(*reinterpret_cast<const uint4*>(cp + p.plane * TOut::kBytes), cl);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) cv[e] += cl[e];
+        }
 #pragma unroll
         for (int e = 0; e < VE; ++e) v[e] += p.beta * cv[e];
       }
@@ -723,8 +757,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc
       }
       const int hi = LOWER ? gm - gn : VE - 1;   // symmetric: columns up to the diagonal
       if (hi >= 0) {
-        if (NT && hi >= VE - 1) store_vec_nt<TOut>(ep.D, p.ldd, gm, gn, v);
-        else store_vec<TOut>(ep.D, p.ldd, gm, gn, v, 0, hi);
+        if (NT && hi >= VE - 1 && d_pl == 1) store_vec_nt<TOut>(ep.D, p.ldd, gm, gn, v);
+        else store_planes<TOut>(ep.D, p.ldd, gm, gn, v, 0, hi, d_pl, p.plane);
         if (ep.D2) {
           float w[VE];
 #pragma unroll
@@ -750,7 +784,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc
         float v[VE];
 #pragma unroll
         for (int e = 0; e < VE; ++e) v[e] = slab[(rr + e) * S + c];
-        store_vec<TOut>(ep.D, p.ldd, gn, gm0, v, lo, VE - 1);
+        store_planes<TOut>(ep.D, p.ldd, gn, gm0, v, lo, VE - 1, d_pl, p.plane);
         if (ep.D2) store_vec<TOut>(ep.D2, p.ldd2, gn, gm0, v, lo, VE - 1);
       }
     }
@@ -764,7 +798,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N>
 constexpr int max_waves_per_eu() { return (BM / WAVES_M) * (BN / WAVES_N) >= 128 * 128 ? 1 : 8; }
 
 template <class TIn, class TB, class TOut, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BKV, bool LOWER,
-          bool NN, bool NT = false>
+          bool NN, bool NT = false, bool PL = false>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(1, max_waves_per_eu<BM, BN, WAVES_M, WAVES_N>())))
 gemm16_kernel(GemmParams p) {
@@ -818,9 +852,17 @@ gemm16_kernel(GemmParams p) {
   const int kend = split_part ? min(K, kbeg + p.kchunk) : K;
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(gp.second ? p.A2 : p.A) + (size_t)bz * p.sA * 2;
   const uint8_t* Bb = reinterpret_cast<const uint8_t*>(p.B) + (size_t)bz * p.sB * 2;
-  const int4v_t rsA = sgpr_rsrc(Ab, (uint32_t)(((size_t)(M - 1) * p.lda + K) * 2));
+  // hi/lo planes of the operands: the K loop runs once per plane pair (hi.hi, then
+  // hi.lo, then lo.hi), KTp stages each
+  // (only the PL instantiation reads the plane counts; the others run one pair)
+  const int a_pl = PL ? (gp.second ? p.a2_planes : p.a_planes) : 1, b_pl = PL ? p.b_planes : 1;
+  const int npairs = (a_pl == 2 && b_pl == 2) ? 3 : a_pl * b_pl;
+  const uint32_t plane_bytes = (uint32_t)(p.plane * 2);
+  const int4v_t rsA = sgpr_rsrc(Ab, (uint32_t)(((size_t)(M - 1) * p.lda + K + (a_pl - 1) * p.plane) * 2));
   const int4v_t rsB = NN ? sgpr_rsrc(Bb, (uint32_t)(((size_t)(K - 1) * p.ldb + N) * 2))
-                         : sgpr_rsrc(Bb, (uint32_t)(((size_t)(N - 1) * p.ldb + K) * 2));
+                         : sgpr_rsrc(Bb, (uint32_t)(((size_t)(N - 1) * p.ldb + K + (b_pl - 1) * p.plane) * 2));
+  const int KTp = (kend - kbeg + BK - 1) / BK;       // stages per plane pair
+  const int KT = KTp * npairs;
   float bmul = 1.0f;
   if constexpr (NN && TIn::kId != TB::kId) {
     bmul = p.b_mul;
@@ -830,14 +872,21 @@ gemm16_kernel(GemmParams p) {
   // load g (0 .. LOADS-1) of k-stage kt: one direct HBM -> LDS instruction (1 KB per
   // wave) into ring slot kt % NS; loads 0 .. A_INSTR-1 fill the A tile, the rest B
   auto issue_load = [&](int kt, int g) {
-    const int k0 = kbeg + kt * BK;
+    // plane pair of stage kt and its K offset; stages at or past KT load nothing
+    // (one pair: stages past the end have k0 >= kend, so their offsets are out of range)
+    const int pi = PL ? (kt >= KTp) + (kt >= 2 * KTp) : 0;
+    const int k0 = kbeg + (kt - pi * KTp) * BK;
+    const bool live = PL ? kt < KT : true;
+    const uint32_t a_add = (PL && pi > 0 && pi == npairs - 1 && a_pl == 2) ? plane_bytes : 0u;
+    const uint32_t b_add = (PL && pi == 1 && b_pl == 2) ? plane_bytes : 0u;
     const uint32_t sb = lds0 + (kt % NS) * STAGE;
     if (g < A_INSTR) {
       const int blk = g * NW + wave;
       const int q = blk * 64 + lane;                      // LDS chunk this lane fills
       const int row = q / CPR, lc = swz_k<BK>(row, q % CPR);
       const int gr = m0 + row, gk = k0 + lc * 8;
-      const uint32_t off = (gr < M && gk < kend) ? (uint32_t)(((size_t)gr * p.lda + gk) * 2) : kOutOfRange;
+      const uint32_t off = (live && gr < M && gk < kend) ? (uint32_t)(((size_t)gr * p.lda + gk) * 2) + a_add
+                                                         : kOutOfRange;
       dma16(rsA, __builtin_amdgcn_readfirstlane(sb + blk * 1024), off);
     } else {
       const int blk = (g - A_INSTR) * NW + wave;
@@ -846,11 +895,11 @@ gemm16_kernel(GemmParams p) {
       if constexpr (!NN) {
         const int row = q / CPR, lc = swz_k<BK>(row, q % CPR);
         const int gr = n0 + row, gk = k0 + lc * 8;
-        off = (gr < N && gk < kend) ? (uint32_t)(((size_t)gr * p.ldb + gk) * 2) : kOutOfRange;
+        off = (live && gr < N && gk < kend) ? (uint32_t)(((size_t)gr * p.ldb + gk) * 2) + b_add : kOutOfRange;
       } else {
         const int kr = q / NCH, lc = (q % NCH) ^ nn_swz(kr);
         const int gk = k0 + kr, gn = n0 + lc * 8;
-        off = (gk < kend && gn < N) ? (uint32_t)(((size_t)gk * p.ldb + gn) * 2) : kOutOfRange;
+        off = (live && gk < kend && gn < N) ? (uint32_t)(((size_t)gk * p.ldb + gn) * 2) : kOutOfRange;
       }
       dma16(rsB, __builtin_amdgcn_readfirstlane(sb + A_BYTES + blk * 1024), off);
     }
@@ -917,7 +966,6 @@ gemm16_kernel(GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int KT = (kend - kbeg + BK - 1) / BK;
   // fp32 partial accumulators of a split product, as float4 quads:
   // [tile][range][wave][fragment][quad][lane], so every access of a wave moves 1 KB
   // of consecutive bytes
@@ -1100,7 +1148,7 @@ gemm16_kernel(GemmParams p) {
   static_assert(NW * 32 * (Cfg::kWN + 4) * 4 <= Cfg::kLdsBytes, "epilogue slabs exceed the LDS ring");
   lds_barrier();
   float* slab = reinterpret_cast<float*>(smem16) + wave * 32 * (Cfg::kWN + 4);
-  epilogue_lds<TOut, LOWER, FM, FN, NT>(p, acc, gp, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane, slab);
+  epilogue_lds<TOut, LOWER, FM, FN, NT, PL>(p, acc, gp, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane, slab);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1147,14 +1195,35 @@ inline long long gemm_tiles(int M, int N, int bm, int bn, bool lower) {
   return lower ? tm * (tm + 1) / 2 : tm * tn;
 }
 
-// The kernels address each operand matrix through a 32-bit buffer offset.
+// The kernels address each operand matrix (both of its planes) through a 32-bit
+// buffer offset.
 inline bool operand_extents_ok(const GemmParams& p, int a_bytes, int b_bytes, bool nn) {
   if (p.M <= 0 || p.N <= 0 || p.K <= 0) return true;
   const size_t lim = size_t(1) << 31;
-  const size_t a = ((size_t)(p.M - 1) * p.lda + p.K) * a_bytes;
-  const size_t b = nn ? ((size_t)(p.K - 1) * p.ldb + p.N) * b_bytes : ((size_t)(p.N - 1) * p.ldb + p.K) * b_bytes;
+  const int apl = std::max(p.a_planes, p.a2_planes);
+  const size_t a = ((size_t)(p.M - 1) * p.lda + p.K + (size_t)(apl - 1) * p.plane) * a_bytes;
+  const size_t b = nn ? ((size_t)(p.K - 1) * p.ldb + p.N) * b_bytes
+                      : ((size_t)(p.N - 1) * p.ldb + p.K + (size_t)(p.b_planes - 1) * p.plane) * b_bytes;
   return a < lim && b < lim;
 }
+
+// Plane counts are 1 or 2; two planes need the 16-bit kernel, a symmetric product,
+// 16-bit outputs, no K split on their operands, and a plane offset.
+inline bool planes_ok(const GemmParams& p, bool k16, bool lower, bool nn, int out_bytes) {
+  const int pl[7] = {p.a_planes, p.a2_planes, p.b_planes, p.c_planes, p.c2_planes, p.d_planes, p.dp_planes};
+  bool any = false;
+  for (int v : pl) {
+    if (v != 1 && v != 2) return false;
+    any = any || v == 2;
+  }
+  if (!any) return true;
+  if (!k16 || !lower || nn || out_bytes != 2 || p.plane <= 0) return false;
+  if (p.ksplit > 1 && (p.a_planes != 1 || p.b_planes != 1)) return false;
+  return true;
+}
+
+// Plane pairs an operand pair runs (hi.hi, hi.lo, lo.hi).
+inline int plane_pairs(int a_pl, int b_pl) { return (a_pl == 2 && b_pl == 2) ? 3 : a_pl * b_pl; }
 
 // Pick the largest tile that still gives every CU at least one workgroup.  One
 // exception, for long K: when 64 x 64 tiles would need several rounds of workgroups
@@ -1206,6 +1275,22 @@ hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops
     if (attr_nt != hipSuccess) return attr_nt;
     if (nt) kern = with_nt;
   }
+  // hi/lo planes: a separate instantiation (bf16 symmetric products only), so the
+  // single-plane kernels carry none of its address arithmetic
+  bool planes = false;
+  for (int v : {p.a_planes, p.a2_planes, p.b_planes, p.c_planes, p.c2_planes, p.d_planes, p.dp_planes})
+    planes = planes || v != 1;
+  if (planes) {
+    if constexpr (k16 && LOWER && !NN && TOut::kId == GNS_BF16) {
+      void (*with_pl)(GemmParams) = gemm16_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, NS, BKV, LOWER, NN, false, true>;
+      static hipError_t attr_pl = hipFuncSetAttribute(reinterpret_cast<const void*>(with_pl),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (attr_pl != hipSuccess) return attr_pl;
+      kern = with_pl;
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   const long long tiles = gemm_tiles(p.M, p.N, BM, BN, LOWER);
@@ -1213,11 +1298,14 @@ hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops
   if (p.pair && (NN || !LOWER || !p.A2 || !p.Dp || (p.C && !p.C2))) return hipErrorInvalidValue;
   if (p.partials && (NN || !LOWER || p.n_partials < 1 || p.n_partials > kMaxPartials)) return hipErrorInvalidValue;
   if (p.ksplit > 1 && (!k16 || !LOWER || NN || p.pair || !p.part || p.kchunk % BK)) return hipErrorInvalidValue;
+  if (!planes_ok(p, k16, LOWER, NN, TOut::kBytes)) return hipErrorInvalidValue;
   const int splits = (p.ksplit > 1 && !p.reduce) ? p.ksplit : 1;
   if (flops && !p.reduce) {
-    // issued: K padded to whole stages (split ranges are whole stages but the last)
+    // issued: K padded to whole stages (split ranges are whole stages but the last),
+    // once per plane pair
     const long long kpad = ((long long)(p.K + BK - 1) / BK) * BK;
-    *flops += 2.0 * (double)tiles * BM * BN * (double)kpad * batch * products;
+    const int pairs = plane_pairs(p.a_planes, p.b_planes) + (p.pair ? plane_pairs(p.a2_planes, p.b_planes) : 0);
+    *flops += 2.0 * (double)tiles * BM * BN * (double)kpad * batch * pairs;
   }
   if (tiles == 0 || batch == 0) return hipSuccess;
   p.batch = batch;
@@ -1256,25 +1344,25 @@ hipError_t launch_cfg(GemmParams p, int batch, hipStream_t stream, double* flops
   return hipErrorInvalidValue;
 }
 
-// K split of the symmetric product: a single matrix (batch 1) with K >= 16384 whose
-// output has 32 to 127 tiles of 256 x 256 is cut into S ranges of at least 2048
-// values, S as large as the CUs allow (at most 8).  The n = 2048, K = 28672 Gram
-// product of the Dion3 workload (36 tiles) runs on 7 ranges.  A matrix with fewer
-// than 32 such tiles (n <= 1792) splits on tiles of 128 x 128 instead, when it has at
-// least 32 of those: the n = 1024, K = 28672 Gram product then runs on 36 tiles x 7
-// ranges instead of 136 unsplit 64 x 64 tiles that leave half the CUs idle.  With
-// fewer tiles each workgroup of the sum would read too many partial tiles.  Only
-// batch 1 splits: the sum order, and with it the last bits, then differ from the
-// same matrix in a batch.
+// K split of the symmetric product: a matrix with K >= 16384 whose output has 32 to
+// 127 tiles of 256 x 256 is cut into S ranges of at least 2048 values, S as large as
+// the CUs allow for one matrix (at most 8).  The n = 2048, K = 28672 Gram product of
+// the Dion3 workload (36 tiles) runs on 7 ranges.  A matrix with fewer than 32 such
+// tiles (n <= 1792) splits on tiles of 128 x 128 instead, when it has at least 32 of
+// those: the n = 1024, K = 28672 Gram product then runs on 36 tiles x 7 ranges
+// instead of 136 unsplit 64 x 64 tiles that leave half the CUs idle.  With fewer
+// tiles each workgroup of the sum would read too many partial tiles.  The plan
+// depends on n and K only, never on the batch size, so a matrix gets the same
+// summation order, and the same bits, alone and in any batch.
 constexpr int kSplitMinK = 16384, kSplitMinChunk = 2048, kSplitMinTiles = 32;
 struct SymmSplit {
   int S = 1;         // number of K ranges (1: no split)
   int kchunk = 0;    // K values per range, a whole number of stages
   int tile = 256;    // output tile edge
 };
-inline SymmSplit symm_split_plan(int batch, int n, int K) {
+inline SymmSplit symm_split_plan(int n, int K) {
   SymmSplit r;
-  if (batch != 1 || K < kSplitMinK) return r;
+  if (K < kSplitMinK) return r;
   long long tiles = gemm_tiles(n, n, 256, 256, true);
   int bk = GNS_BK_BIG;
   if (tiles < kSplitMinTiles) {

@@ -15,14 +15,14 @@ hipError_t launch_symm(gns_dtype in, gns_dtype out, const GemmParams& p, int bat
 
 size_t symm_split_bytes(int batch, int n, int K, gns_dtype in) {
   if (in == GNS_F32) return 0;
-  const SymmSplit sp = symm_split_plan(batch, n, K);
-  if (sp.S < 2) return 0;
-  return (size_t)gemm_tiles(n, n, sp.tile, sp.tile, true) * sp.S * sp.tile * sp.tile * sizeof(float);
+  const SymmSplit sp = symm_split_plan(n, K);
+  if (sp.S < 2 || batch < 1) return 0;
+  return (size_t)batch * gemm_tiles(n, n, sp.tile, sp.tile, true) * sp.S * sp.tile * sp.tile * sizeof(float);
 }
 
 hipError_t launch_symm_ws(gns_dtype in, gns_dtype out, const GemmParams& p, int batch, float* part, size_t part_bytes,
                           hipStream_t s, double* flops) {
-  const SymmSplit sp = (in == GNS_F32 || p.pair) ? SymmSplit{} : symm_split_plan(batch, p.M, p.K);
+  const SymmSplit sp = (in == GNS_F32 || p.pair) ? SymmSplit{} : symm_split_plan(p.M, p.K);
   if (sp.S < 2 || !part || part_bytes < symm_split_bytes(batch, p.M, p.K, in))
     return launch_symm(in, out, p, batch, s, flops);
   GemmParams q = p;

@@ -43,6 +43,15 @@ struct Carver {
   }
 };
 
+// With bf16 iterates, the Gram chain R, Z, Y is kept as hi/lo pairs of bf16 planes
+// (about 16 significant bits) and its products run on bf16 MFMA as hi.hi + hi.lo +
+// lo.hi; Q and the restarted X stay single bf16 planes.  A single bf16 R squares the
+// condition number of X at 8 significant bits and misses the 2e-2 output bar on
+// small and square inputs; fp16 iterates (11 bits) keep one plane.  Every n x n
+// buffer of the call then has room for two planes ([batch][2][n][n]), so one batch
+// stride serves all of them.
+int gram_planes(gns_dtype cdt) { return cdt == GNS_BF16 ? 2 : 1; }
+
 struct NsLayout {
   float* s;
   float* partials;
@@ -58,13 +67,15 @@ NsLayout ns_layout(void* base, int batch, int n, int m, gns_dtype cdt) {
   NsLayout L{};
   const size_t e = esize(cdt);
   const size_t nn = (size_t)n * n * e * batch, nm = (size_t)n * m * e * batch;
+  const size_t nn_gram = nn * gram_planes(cdt);      // every n x n Gram NS buffer, all planes
   L.s = (float*)c.take(sizeof(float) * (size_t)batch);
   L.partials = (float*)c.take(sizeof(float) * (size_t)batch * frob_partials_per_batch(n, m));
   // both Gram products of a call (and standard NS's) have K = m
   L.part_bytes = symm_split_bytes(batch, n, m, cdt);
   L.part = L.part_bytes ? (float*)c.take(L.part_bytes) : nullptr;
   const size_t common = c.off;
-  L.R = c.take(nn); L.Z = c.take(nn); L.Y = c.take(nn); L.Q0 = c.take(nn); L.Q1 = c.take(nn);
+  L.R = c.take(nn_gram); L.Z = c.take(nn_gram); L.Y = c.take(nn_gram);
+  L.Q0 = c.take(nn_gram); L.Q1 = c.take(nn_gram);
   L.Xa = c.take(nm); L.Xb = c.take(nm);
   const size_t gram_end = c.off;
   c.off = common;
@@ -187,15 +198,23 @@ int run_gram(const NsCall& c) {
   const NsLayout L = ns_layout(c.ws, c.batch, c.n, c.m, c.cdt);
   const int n = c.n, m = c.m, B = c.batch;
   const long long nn = (long long)n * n, nm = (long long)n * m;
+  const int pl = gram_planes(c.cdt);        // planes of R, Z, Y (Q: always one)
+  const long long sn = nn * pl;             // batch stride of every n x n buffer
   const float P = pow2_scale(c.cdt, n, m);
   const gns_dtype cdt = c.cdt;
   const float* s = c.s_given ? c.s_given : L.s;
   if (!c.s_given) HIP_OK(launch_frob_partials(c.X, c.xdt, c.ldx, c.sx, B, n, m, L.partials, c.stream));
+  // planes of one symmetric product: A, B, C, D of the chain (R, Z, Y) carry pl planes
+  auto chain = [&](GemmParams& g, int a, int b, int cpl, int d) {
+    g.plane = nn;
+    g.a_planes = a; g.b_planes = b; g.c_planes = cpl; g.d_planes = d;
+  };
 
   // R0 = s^2 X X^T: operands in X's dtype, result in the iterate dtype.  Without a
   // given scale, the product forms s from the partial sums and stores it to L.s.
   {
-    GemmParams g = symm_params(n, m, c.X, c.ldx, c.sx, c.X, c.ldx, c.sx, L.R, n, nn);
+    GemmParams g = symm_params(n, m, c.X, c.ldx, c.sx, c.X, c.ldx, c.sx, L.R, n, sn);
+    chain(g, 1, 1, 1, pl);
     g.alpha_pow = 2;
     if (c.s_given) {
       g.scale = s;
@@ -214,7 +233,7 @@ int run_gram(const NsCall& c) {
   auto apply_q = [&](void* out, gns_dtype odt, long long ldo, long long so, bool final_out) -> int {
     GemmParams g;
     g.M = n; g.N = m; g.K = n;
-    g.A = Q; g.lda = n; g.sA = nn;
+    g.A = Q; g.lda = n; g.sA = sn;
     g.B = cx; g.ldb = cld; g.sB = csx;
     g.D = out; g.ldd = ldo; g.sD = so;
     const float out_mul = final_out ? 1.0f : P;      // stored X-like iterates carry P
@@ -238,15 +257,17 @@ int run_gram(const NsCall& c) {
       int st = apply_q(xn, cdt, m, nm, false);
       if (st) return st;
       cx = xn; cxdt = cdt; cld = m; csx = nm; cx_orig = false;
-      GemmParams g = symm_params(n, m, cx, m, nm, cx, m, nm, L.R, n, nn);
+      GemmParams g = symm_params(n, m, cx, m, nm, cx, m, nm, L.R, n, sn);
+      chain(g, 1, 1, 1, pl);
       g.alpha = 1.0f / (P * P);
       HIP_OK(launch_symm_ws(cdt, cdt, g, B, L.part, L.part_bytes, c.stream, c.flops));
       q_identity = true;
     }
     {  // Z = c R R + b R   (and Q = Z + a I while Q is the identity)
-      GemmParams g = symm_params(n, n, L.R, n, nn, L.R, n, nn, L.Z, n, nn);
-      g.alpha = cc; g.beta = b; g.C = L.R; g.ldc = n; g.sC = nn;
-      if (q_identity) { g.D2 = Q; g.ldd2 = n; g.sD2 = nn; g.delta = a; }
+      GemmParams g = symm_params(n, n, L.R, n, sn, L.R, n, sn, L.Z, n, sn);
+      chain(g, pl, pl, pl, pl);
+      g.alpha = cc; g.beta = b; g.C = L.R; g.ldc = n; g.sC = sn;
+      if (q_identity) { g.D2 = Q; g.ldd2 = n; g.sD2 = sn; g.delta = a; }
       HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
     }
     const bool need_r = t < c.sch.steps && !restart_before(t + 1);
@@ -254,21 +275,27 @@ int run_gram(const NsCall& c) {
     // computes the pair
     const bool q_update = !q_identity;
     if (q_update) {
-      GemmParams g = symm_params(n, n, Q, n, nn, L.Z, n, nn, Qn, n, nn);
-      g.beta = a; g.C = Q; g.ldc = n; g.sC = nn;
-      if (need_r) { g.pair = 1; g.A2 = L.R; g.C2 = L.R; g.Dp = L.Y; }
+      GemmParams g = symm_params(n, n, Q, n, sn, L.Z, n, sn, Qn, n, sn);
+      chain(g, 1, pl, 1, 1);
+      g.beta = a; g.C = Q; g.ldc = n; g.sC = sn;
+      if (need_r) {
+        g.pair = 1; g.A2 = L.R; g.C2 = L.R; g.Dp = L.Y;
+        g.a2_planes = pl; g.c2_planes = pl; g.dp_planes = pl;
+      }
       HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
       std::swap(Q, Qn);
     }
     q_identity = false;
     if (need_r) {
       if (!q_update) {
-        GemmParams g1 = symm_params(n, n, L.R, n, nn, L.Z, n, nn, L.Y, n, nn);  // Y = R Z + a R
-        g1.beta = a; g1.C = L.R; g1.ldc = n; g1.sC = nn;
+        GemmParams g1 = symm_params(n, n, L.R, n, sn, L.Z, n, sn, L.Y, n, sn);  // Y = R Z + a R
+        chain(g1, pl, pl, pl, pl);
+        g1.beta = a; g1.C = L.R; g1.ldc = n; g1.sC = sn;
         HIP_OK(launch_symm(cdt, cdt, g1, B, c.stream, c.flops));
       }
-      GemmParams g2 = symm_params(n, n, L.Z, n, nn, L.Y, n, nn, L.R, n, nn);    // R = Z Y + a Y
-      g2.beta = a; g2.C = L.Y; g2.ldc = n; g2.sC = nn;
+      GemmParams g2 = symm_params(n, n, L.Z, n, sn, L.Y, n, sn, L.R, n, sn);    // R = Z Y + a Y
+      chain(g2, pl, pl, pl, pl);
+      g2.beta = a; g2.C = L.Y; g2.ldc = n; g2.sC = sn;
       HIP_OK(launch_symm(cdt, cdt, g2, B, c.stream, c.flops));
     }
   }
@@ -512,7 +539,7 @@ int dion3_gather_feedback(void* M, int N, int m, long long ld, const int* S, int
   if (st) return st;
   if (!S || !X || k < 1 || k > N || ldx < m || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
   if (ldx % 8 || !aligned16(X)) return GNS_ERR_UNSUPPORTED;
-  HIP_OK(launch_gather_feedback((uint16_t*)M, 1, N, m, ld, 0, S, k, mu, nullptr, (uint16_t*)X, ldx, stream));
+  HIP_OK(launch_gather_feedback((uint16_t*)M, 1, N, m, ld, 0, S, k, k, mu, nullptr, (uint16_t*)X, ldx, stream));
   return GNS_OK;
 }
 
@@ -523,7 +550,8 @@ int dion3_apply_update(void* W, int N, int m, long long ld, const int* S, int k,
   if (!S || !O || k < 1 || k > N || ldo < m || !std::isfinite(lr) || !std::isfinite(wd)) return GNS_ERR_INVALID_ARG;
   if (o_dtype != GNS_BF16 && o_dtype != GNS_F32) return GNS_ERR_UNSUPPORTED;
   if (ldo % 8 || !aligned16(O)) return GNS_ERR_UNSUPPORTED;
-  HIP_OK(launch_apply_update((uint16_t*)W, 1, N, m, ld, 0, S, k, O, o_dtype, ldo, lr, wd, nullptr, stream));
+  HIP_OK(launch_apply_update((uint16_t*)W, 1, N, m, ld, 0, S, k, O, o_dtype, ldo, (long long)k * ldo, lr, wd, nullptr,
+                             stream));
   return GNS_OK;
 }
 
@@ -531,16 +559,23 @@ struct Dion3Layout {
   double* score; double* sumsq; float* s; void* X; void* O; void* gns_ws; size_t gns_bytes; size_t bytes;
 };
 
+// The selected submatrix is held with kp = k rounded up to a multiple of 8 rows; the
+// extra rows are zero.  Zero rows leave the iteration's result on the other rows
+// unchanged (they add zero rows and columns to R and every polynomial in it), and
+// every kernel then works on whole 8-row groups.
+int padded_rows(int k) { return (k + 7) / 8 * 8; }
+
 static Dion3Layout dion3_layout(void* base, int batch, int N, int m, int k, gns_dtype cdt) {
   Carver c{reinterpret_cast<uint8_t*>(base), 0};
   Dion3Layout L{};
   const size_t B = (size_t)batch;
+  const int kp = padded_rows(k);
   L.score = (double*)c.take(sizeof(double) * B * N);
   L.sumsq = (double*)c.take(sizeof(double) * B * N);
   L.s = (float*)c.take(sizeof(float) * B);
-  L.X = c.take(B * k * m * 2);
-  L.O = c.take(B * k * m * 2);
-  L.gns_bytes = ns_workspace_bytes(batch, k, m, cdt);
+  L.X = c.take(B * kp * m * 2);
+  L.O = c.take(B * kp * m * 2);
+  L.gns_bytes = ns_workspace_bytes(batch, kp, m, cdt);
   L.gns_ws = c.take(L.gns_bytes);
   L.bytes = c.off;
   return L;
@@ -574,7 +609,6 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
   if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
   if (!valid_dtype(compute)) return GNS_ERR_INVALID_ARG;
   if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
-  if (k % 8) return GNS_ERR_UNSUPPORTED;
   if (O_out && !aligned16(O_out)) return GNS_ERR_UNSUPPORTED;
   // W, M and G must be distinct (each is read and written by different passes)
   const size_t span = ((size_t)(batch - 1) * (size_t)(batch > 1 ? stride : 0) + (size_t)(N - 1) * ld + m) * 2;
@@ -587,12 +621,15 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
   if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
 
-  void* O = O_out ? O_out : L.O;
-  const long long km = (long long)k * m;
-  // one batched Gram NS over the selected k x m submatrices of every entry; its
+  // the submatrices are padded to kp rows (zeros); with kp == k the caller's O_out
+  // receives O directly, else O goes to the workspace and its k rows are copied out
+  const int kp = padded_rows(k);
+  void* O = (O_out && kp == k) ? O_out : L.O;
+  const long long km = (long long)k * m, kpm = (long long)kp * m;
+  // one batched Gram NS over the selected kp x m submatrices of every entry; its
   // arguments are checked before anything is launched
-  NsCall c = make_call(L.X, GNS_BF16, m, km, O, GNS_BF16, m, km, batch, k, m, compute, &sch, L.gns_ws, L.gns_bytes,
-                       stream, nullptr);
+  NsCall c = make_call(L.X, GNS_BF16, m, kpm, O, GNS_BF16, m, kpm, batch, kp, m, compute, &sch, L.gns_ws,
+                       L.gns_bytes, stream, nullptr);
   c.s_given = L.s;
   if ((st = check_ns(c))) return st;
   if (O_out && (overlaps(O_out, (size_t)batch * km * 2, workspace, L.bytes) ||
@@ -607,10 +644,12 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
     HIP_OK(launch_topk(L.score, batch, N, k, S_out, stream));
     S = S_out;
   }
-  HIP_OK(launch_gather_feedback(Mh, batch, N, m, ld, stride, S, k, mu, dev_scalars, (uint16_t*)L.X, m, stream));
+  HIP_OK(launch_gather_feedback(Mh, batch, N, m, ld, stride, S, k, kp, mu, dev_scalars, (uint16_t*)L.X, m, stream));
   HIP_OK(launch_selected_sumsq(L.sumsq, S, batch, k, N, sch.eps, L.s, stream));
   if ((st = run_ns(c, true))) return st;
-  HIP_OK(launch_apply_update((uint16_t*)W, batch, N, m, ld, stride, S, k, O, GNS_BF16, m, lr, weight_decay,
+  if (O_out && O != O_out)
+    HIP_OK(launch_cast_scale(O, GNS_BF16, m, kpm, O_out, GNS_BF16, m, km, batch, k, m, 1.0f, nullptr, 0, stream));
+  HIP_OK(launch_apply_update((uint16_t*)W, batch, N, m, ld, stride, S, k, O, GNS_BF16, m, kpm, lr, weight_decay,
                              dev_scalars, stream));
   return GNS_OK;
 }
@@ -662,9 +701,10 @@ static Dion3ColsLayout dion3_cols_layout(void* base, int N, int m, int k, gns_dt
   L.sumsq = (double*)c.take(sizeof(double) * (size_t)m);
   L.mark = (uint8_t*)c.take((size_t)m);
   L.s = (float*)c.take(sizeof(float));
-  L.Xt = c.take((size_t)k * N * 2);
-  L.O = c.take((size_t)k * N * 2);
-  L.gns_bytes = ns_workspace_bytes(1, k, N, cdt);
+  const int kp = padded_rows(k);
+  L.Xt = c.take((size_t)kp * N * 2);
+  L.O = c.take((size_t)kp * N * 2);
+  L.gns_bytes = ns_workspace_bytes(1, kp, N, cdt);
   L.gns_ws = c.take(L.gns_bytes);
   L.bytes = c.off;
   return L;
@@ -687,7 +727,7 @@ int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld,
   if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
   if (!valid_dtype(compute)) return GNS_ERR_INVALID_ARG;
   if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
-  if (N % 8 || k % 8) return GNS_ERR_UNSUPPORTED;   // N is the row length of X^T and O
+  if (N % 8) return GNS_ERR_UNSUPPORTED;   // N is the row length of X^T and O
   if (O_out && !aligned16(O_out)) return GNS_ERR_UNSUPPORTED;
   const size_t span = ((size_t)(N - 1) * ld + m) * 2;
   if (overlaps(W, span, M, span) || overlaps(W, span, G, span) || overlaps(M, span, G, span))
@@ -699,12 +739,14 @@ int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld,
   if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
 
-  void* O = O_out ? O_out : L.O;
-  const long long kN = (long long)k * N;
-  // the k x N transpose of the selected columns: Gram NS iterates on its short side;
+  // X^T is padded to kp rows (zeros), as in the row step
+  const int kp = padded_rows(k);
+  void* O = (O_out && kp == k) ? O_out : L.O;
+  const long long kN = (long long)k * N, kpN = (long long)kp * N;
+  // the kp x N transpose of the selected columns: Gram NS iterates on its short side;
   // its arguments are checked before anything is launched
-  NsCall c = make_call(L.Xt, GNS_BF16, N, kN, O, GNS_BF16, N, kN, 1, k, N, compute, &sch, L.gns_ws, L.gns_bytes,
-                       stream, nullptr);
+  NsCall c = make_call(L.Xt, GNS_BF16, N, kpN, O, GNS_BF16, N, kpN, 1, kp, N, compute, &sch, L.gns_ws,
+                       L.gns_bytes, stream, nullptr);
   c.s_given = L.s;
   if ((st = check_ns(c))) return st;
   if (O_out && (overlaps(O_out, (size_t)kN * 2, workspace, L.bytes) || overlaps(O_out, (size_t)kN * 2, W, span) ||
@@ -715,9 +757,11 @@ int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld,
   HIP_OK(launch_accumulate_colscore(Mh, (const uint16_t*)G, N, m, ld, score_norm, L.part_s, L.part_q, L.score,
                                     L.sumsq, stream));
   HIP_OK(launch_topk(L.score, 1, m, k, S_out, stream));
-  HIP_OK(launch_gather_cols_feedback(Mh, N, m, ld, S_out, k, mu, (uint16_t*)L.Xt, N, stream));
+  HIP_OK(launch_gather_cols_feedback(Mh, N, m, ld, S_out, k, kp, mu, (uint16_t*)L.Xt, N, stream));
   HIP_OK(launch_selected_sumsq(L.sumsq, S_out, 1, k, m, sch.eps, L.s, stream));
   if ((st = run_ns(c, true))) return st;
+  if (O_out && O != O_out)
+    HIP_OK(launch_cast_scale(O, GNS_BF16, N, kpN, O_out, GNS_BF16, N, kN, 1, k, N, 1.0f, nullptr, 0, stream));
   HIP_OK(launch_update_cols((uint16_t*)W, N, m, ld, S_out, k, (const uint16_t*)O, N, lr, weight_decay, L.mark,
                             stream));
   return GNS_OK;
@@ -772,7 +816,8 @@ int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, 
   if (batch > 1 && stride < (long long)n * ld) return GNS_ERR_INVALID_ARG;
   if (batch > 1 && stride % 8) return GNS_ERR_UNSUPPORTED;
   if (nesterov != 0 && nesterov != 1) return GNS_ERR_INVALID_ARG;
-  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu) || !std::isfinite(scale))
+  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu) || !std::isfinite(scale) ||
+      scale < 0.0f)
     return GNS_ERR_INVALID_ARG;
   if (!valid_dtype(compute)) return GNS_ERR_INVALID_ARG;
   if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
@@ -788,7 +833,8 @@ int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, 
   if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
   // the update's RMS matched to AdamW's: 0.2 sqrt(max(n, m)) unless the caller gives one
-  const float sc = scale > 0.0f ? scale : 0.2f * std::sqrt((float)std::max(n, m));
+  // (scale == 0 asks for that default; a negative scale was rejected above)
+  const float sc = scale != 0.0f ? scale : 0.2f * std::sqrt((float)std::max(n, m));
 
   void* O = O_out ? O_out : L.O;
   const long long nm = (long long)n * m;

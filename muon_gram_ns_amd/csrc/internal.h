@@ -38,6 +38,15 @@ struct GemmParams {
   // runs the epilogue.
   int ksplit = 1, kchunk = 0, reduce = 0;
   float* part = nullptr;
+  // hi/lo planes (16-bit kernel only): a matrix held in 2 planes stores hi = round(v)
+  // at its address and lo = round(v - hi) `plane` elements further, so hi + lo keeps
+  // about twice the significant bits of one 16-bit value.  A product of two such
+  // matrices is hi.hi + hi.lo + lo.hi (lo.lo is below the rounding of the others),
+  // run as one K loop over the plane pairs in that order; a 2-plane C is read as
+  // hi + lo, and a 2-plane output writes both planes.  a2/c2/dp: the second product
+  // of a pair.
+  int a_planes = 1, a2_planes = 1, b_planes = 1, c_planes = 1, c2_planes = 1, d_planes = 1, dp_planes = 1;
+  long long plane = 0;
   int tiles_m = 0, tiles_n = 0;   // set by the launcher
   int batch = 0, tiles = 0;       // set by the launcher: grid = batch * tiles workgroups
 };
@@ -86,10 +95,13 @@ hipError_t launch_accumulate_score(uint16_t* M, const uint16_t* G, int batch, in
 hipError_t launch_topk(const double* score, int batch, int N, int k, int* S, hipStream_t s);
 // dev_scalars (nullable): device float[3] = {lr, wd, mu} read when the kernel runs,
 // replacing the host values.
+// X holds kx >= k rows per batch entry (rows k .. kx-1 are written as zeros).
 hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long long ld, long long stride, const int* S,
-                                  int k, float mu, const float* dev_scalars, uint16_t* X, long long ldx, hipStream_t s);
+                                  int k, int kx, float mu, const float* dev_scalars, uint16_t* X, long long ldx,
+                                  hipStream_t s);
+// O: k rows (row stride ldo) per batch entry, entries so elements apart.
 hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long ld, long long stride, const int* S, int k,
-                               const void* O, gns_dtype o_dtype, long long ldo, float lr, float wd,
+                               const void* O, gns_dtype o_dtype, long long ldo, long long so, float lr, float wd,
                                const float* dev_scalars, hipStream_t s);
 // s[b] = 1 / (sqrt(sum_i sumsq[b][S[b][i]]) + eps): the Frobenius scale of the rows S.
 hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int batch, int k, int N, float eps,
@@ -101,9 +113,10 @@ hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int batch, i
 size_t dion3_cols_partials(int N);
 hipError_t launch_accumulate_colscore(uint16_t* M, const uint16_t* G, int N, int m, long long ld, int score_norm,
                                       double* part_s, double* part_q, double* score, double* sumsq, hipStream_t s);
-// Xt (k x N, row stride ldx): row j = column S[j] of M; then M[:, S] <- bf16(mu M[:, S])
-hipError_t launch_gather_cols_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, float mu,
-                                       uint16_t* Xt, long long ldx, hipStream_t s);
+// Xt (kx x N, row stride ldx): row j < k = column S[j] of M, rows k .. kx-1 zero; then
+// M[:, S] <- bf16(mu M[:, S])
+hipError_t launch_gather_cols_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, int kx,
+                                       float mu, uint16_t* Xt, long long ldx, hipStream_t s);
 // W[:, S[j]] <- bf16(d W - lr O[j, :]^T); with wd != 0 every other column decays (mark:
 // m bytes of scratch)
 hipError_t launch_update_cols(uint16_t* W, int N, int m, long long ld, const int* S, int k, const uint16_t* O,

@@ -151,33 +151,107 @@ def test_dion3_step_repeatable(gns_mod):
         assert all(np.array_equal(a, b) for a, b in zip(r, runs[0]))
 
 
-@pytest.mark.timeout(900)
-def test_dion3_step_full_size(gns_mod):
-    """The 8192 x 28672 workload at f = 1/4 and 1/8 with l2 row scores."""
+@pytest.fixture(scope="module")
+def dion3_full():
+    """The 8192 x 28672 workload's seeded state, the oracle's accumulated momentum and
+    its row scores (l1 and l2), computed once for the module."""
     announce("dion3 8192x28672: generating inputs")
     w, g, m = synth.dion3_state()
     announce("dion3 8192x28672: oracle accumulate")
     m1 = accumulate(m, g)
     announce("dion3 8192x28672: oracle row scores")
-    sc = row_scores(m1, "l2")
-    for f in (0.25, 0.125):
-        announce(f"dion3 step 8192x28672 f={f}")
-        k = k_from_fraction(f, 8192)
-        S_ref = select_topk(sc, k)
-        W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
-        S, O = gns_mod.dion3_step(W, M, G, k, 0.01 / np.sqrt(f), weight_decay=0.0, mu=0.95, score_norm=2,
-                                  return_O=True)
-        assert np.array_equal(S.cpu().numpy(), S_ref)
-        announce(f"dion3 8192x28672 f={f}: comparing M and W")
-        assert np.array_equal(bits(M), error_feedback(m1, S_ref, 0.95))
-        rest = np.setdiff1d(np.arange(8192), S_ref)
-        assert np.array_equal(bits(W)[rest], w[rest])
-        if f == 0.125:   # one full-size orthogonalisation check (oracle cost ~1e12 flops)
-            announce(f"dion3 8192x28672 f={f}: oracle Newton-Schulz on the selected rows")
-            O_ref = newton_schulz(bf16_to_f64(m1[S_ref]))
-            e = rel_fro(to_f64(O), O_ref)
-            print(f"f={f} O rel err {e:.3e}")
-            assert e <= 2e-2
+    return {"w": w, "g": g, "m": m, "m1": m1, "l2": row_scores(m1, "l2"), "l1": row_scores(m1, "l1")}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("f,norm", [(0.25, 2), (0.125, 2), (0.25, 1)])
+def test_dion3_step_full_size(gns_mod, dion3_full, f, norm):
+    """The 8192 x 28672 workload at f = 1/4 and 1/8 with l2 row scores (the configured
+    score) and at f = 1/4 with the pages' l1 score: S, M and the unselected W rows
+    bit-exact; O within 2e-2 of float64 standard NS on the oracle's selected rows;
+    the selected W rows within one bf16 rounding plus lr times O's tolerance of the
+    oracle's update."""
+    d = dion3_full
+    w, g, m, m1 = d["w"], d["g"], d["m"], d["m1"]
+    k = k_from_fraction(f, 8192)
+    lr = 0.01 / np.sqrt(f)
+    announce(f"dion3 step 8192x28672 f={f} norm=l{norm}")
+    S_ref = select_topk(d["l2" if norm == 2 else "l1"], k)
+    W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+    S, O = gns_mod.dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=norm, return_O=True)
+    assert np.array_equal(S.cpu().numpy(), S_ref)
+    announce(f"dion3 8192x28672 f={f}: comparing M and the unselected W rows")
+    assert np.array_equal(bits(M), error_feedback(m1, S_ref, 0.95))
+    wg = bits(W)
+    rest = np.setdiff1d(np.arange(8192), S_ref)
+    assert np.array_equal(wg[rest], w[rest])
+    announce(f"dion3 8192x28672 f={f}: oracle Newton-Schulz on the {k} selected rows")
+    O_ref = newton_schulz(bf16_to_f64(m1[S_ref]))
+    e = rel_fro(to_f64(O), O_ref)
+    print(f"f={f} l{norm} O rel err {e:.3e}")
+    assert e <= 2e-2
+    announce(f"dion3 8192x28672 f={f}: selected W rows against the oracle's update")
+    w_ref_sel = weight_update(w[S_ref], np.arange(k), bf16_to_f64(f64_to_bf16_rne(O_ref)), lr, 0.0)
+    assert w_within_bound(wg[S_ref], w_ref_sel, lr, O_ref)
+
+
+@pytest.mark.parametrize("N,m,f,norm,wd", [(1000, 2048, 0.125, 2, 0.0), (1000, 2048, 0.125, 1, 0.1),
+                                           (200, 520, 0.3, 2, 0.1)])
+def test_dion3_step_any_k(gns_mod, N, m, f, norm, wd):
+    """k = ceil(f N) that is not a multiple of 8 (k = 125 and 60): the submatrix is
+    padded with zero rows inside the library.  S and M bit-exact, O within 2e-2, W
+    within O's tolerance and bit-exact on unselected rows when wd = 0."""
+    k = k_from_fraction(f, N)
+    assert k % 8 != 0
+    announce(f"dion3 step {N}x{m} f={f} (k={k}) norm={norm} wd={wd}")
+    w, g, mo = synth.dion3_state(n=N, m=m, seed=38)
+    lr = 0.01 / np.sqrt(f)
+    W, M, G = to_dev(w, "bf16"), to_dev(mo, "bf16"), to_dev(g, "bf16")
+    S, O = gns_mod.dion3_step(W, M, G, k, lr, weight_decay=wd, mu=0.95, score_norm=norm, return_O=True)
+    w_ref, m_ref, S_ref, O_ref = oracle.dion3_step(w, mo, g, k, lr, wd=wd, mu=0.95, norm="l1" if norm == 1 else "l2")
+    assert np.array_equal(S.cpu().numpy(), S_ref)
+    assert np.array_equal(bits(M), m_ref)
+    e = rel_fro(to_f64(O), O_ref)
+    print(f"O rel err {e:.3e}")
+    assert e <= 2e-2
+    wg = bits(W)
+    assert w_within_bound(wg, w_ref, lr, O_ref)
+    if wd == 0.0:
+        rest = np.setdiff1d(np.arange(N), S_ref)
+        assert np.array_equal(wg[rest], w_ref[rest])
+    # the same step without O_out takes the same path through the workspace
+    W2, M2, G2 = to_dev(w, "bf16"), to_dev(mo, "bf16"), to_dev(g, "bf16")
+    S2 = gns_mod.dion3_step(W2, M2, G2, k, lr, weight_decay=wd, mu=0.95, score_norm=norm)
+    assert np.array_equal(S2.cpu().numpy(), S_ref)
+    assert np.array_equal(bits(W2), wg) and np.array_equal(bits(M2), bits(M))
+
+
+@pytest.mark.timeout(600)
+def test_dion3_step_batched_long_k_equals_single(gns_mod):
+    """Two 1024 x 16384 states at k = 1024: the submatrices' Gram products have
+    K = 16384 and split K.  The batched step equals the single steps bitwise (the split
+    does not depend on the batch size), and entry 0 matches the oracle."""
+    import torch
+    announce("dion3 step batched 2x1024x16384 k=1024 (long K)")
+    B, N, m, k, lr = 2, 1024, 16384, 1024, 0.02
+    states = [synth.dion3_state(n=N, m=m, seed=80 + b) for b in range(B)]
+    stack = lambda i: torch.stack([to_dev(st[i], "bf16") for st in states])
+    W, G, M = stack(0), stack(1), stack(2)
+    S, O = gns_mod.dion3_step_batched(W, M, G, k, lr, weight_decay=0.1, mu=0.95, score_norm=2, return_O=True)
+    for b, (w, g, mm) in enumerate(states):
+        W1, M1, G1 = to_dev(w, "bf16"), to_dev(mm, "bf16"), to_dev(g, "bf16")
+        S1, O1 = gns_mod.dion3_step(W1, M1, G1, k, lr, weight_decay=0.1, mu=0.95, score_norm=2, return_O=True)
+        assert np.array_equal(S1.cpu().numpy(), S[b].cpu().numpy())
+        assert np.array_equal(bits(O1), bits(O[b]))
+        assert np.array_equal(bits(W1), bits(W[b])) and np.array_equal(bits(M1), bits(M[b]))
+    announce("dion3 step batched 2x1024x16384: oracle on entry 0")
+    w, g, mm = states[0]
+    w_ref, m_ref, S_ref, O_ref = oracle.dion3_step(w, mm, g, k, lr, wd=0.1, mu=0.95, norm="l2")
+    assert np.array_equal(S[0].cpu().numpy(), S_ref)
+    assert np.array_equal(bits(M[0]), m_ref)
+    e = rel_fro(to_f64(O[0]), O_ref)
+    print(f"O rel err {e:.3e}")
+    assert e <= 2e-2
 
 
 def test_dion3_step_tall_submatrix(gns_mod):
@@ -319,10 +393,11 @@ def test_dion3_step_dev_scalars_equals_host_scalars(gns_mod, wd):
 
 
 @pytest.mark.parametrize("N,cols,k,norm,wd", [(512, 256, 64, 1, 0.0), (512, 256, 64, 2, 0.1),
-                                              (200, 136, 24, 2, 0.0), (200, 136, 24, 1, 0.1)])
+                                              (200, 136, 24, 2, 0.0), (200, 136, 24, 1, 0.1),
+                                              (200, 136, 35, 2, 0.0)])
 def test_dion3_step_cols_matches_oracle(gns_mod, N, cols, k, norm, wd):
     """Column selection on a tall state, also with ragged tiles (N, k not multiples of
-    64): S and M bit-exact, O within 2e-2, W within O's tolerance (bit-exact on
+    64) and a k that is not a multiple of 8 (35): S and M bit-exact, O within 2e-2, W within O's tolerance (bit-exact on
     unselected columns when wd = 0)."""
     announce(f"dion3 column step {N}x{cols} k={k} norm={norm} wd={wd}")
     w, g, m = synth.dion3_state(n=N, m=cols, seed=32)
@@ -407,13 +482,14 @@ def test_dion3_step_zero_state(gns_mod):
     assert not np.any(bits(M) & 0x7fff)
 
 
-def test_dion3_step_smallest_k(gns_mod):
-    """k = 8, the smallest row count the step takes."""
-    announce("dion3 step k = 8 512x1024")
+@pytest.mark.parametrize("k", [1, 8])
+def test_dion3_step_smallest_k(gns_mod, k):
+    """k = 1 (a single row, padded to 8 inside the library) and k = 8."""
+    announce(f"dion3 step k = {k} 512x1024")
     w, g, m = synth.dion3_state(n=512, m=1024, seed=37)
     W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
-    S, O = gns_mod.dion3_step(W, M, G, 8, 0.02, weight_decay=0.1, mu=0.95, score_norm=1, return_O=True)
-    w_ref, m_ref, S_ref, O_ref = oracle.dion3_step(w, m, g, 8, 0.02, wd=0.1, mu=0.95, norm="l1")
+    S, O = gns_mod.dion3_step(W, M, G, k, 0.02, weight_decay=0.1, mu=0.95, score_norm=1, return_O=True)
+    w_ref, m_ref, S_ref, O_ref = oracle.dion3_step(w, m, g, k, 0.02, wd=0.1, mu=0.95, norm="l1")
     assert np.array_equal(S.cpu().numpy(), S_ref)
     assert np.array_equal(bits(M), m_ref)
     assert rel_fro(to_f64(O), O_ref) <= 2e-2

@@ -56,12 +56,15 @@ def test_muon_step_matches_oracle(gns_mod, B, n, m, nesterov, wd):
         assert w_within_bound(Wb[b], w_ref, lr * sc, o_ref)
 
 
-def test_muon_batched_equals_single_entries(gns_mod):
-    announce("muon batched == single")
-    w, g, mo = states(3, 128, 512, seed=300)
+@pytest.mark.parametrize("B,n,m", [(3, 128, 512), (2, 1024, 16384)])
+def test_muon_batched_equals_single_entries(gns_mod, B, n, m):
+    """A batch gives each entry bitwise the step of that entry alone, also at K = 16384
+    where the Gram products split K (the split depends on the shape only)."""
+    announce(f"muon batched == single {B}x{n}x{m}")
+    w, g, mo = states(B, n, m, seed=300)
     W, M, G = to_dev(w, "bf16"), to_dev(mo, "bf16"), to_dev(g, "bf16")
     O = gns_mod.muon_step(W, M, G, 0.02, weight_decay=0.1, return_O=True)
-    for b in range(3):
+    for b in range(B):
         Wi, Mi, Gi = to_dev(w[b], "bf16"), to_dev(mo[b], "bf16"), to_dev(g[b], "bf16")
         Oi = gns_mod.muon_step(Wi, Mi, Gi, 0.02, weight_decay=0.1, return_O=True)
         assert np.array_equal(bits(Oi), bits(O)[b])
@@ -134,3 +137,14 @@ def test_muon_step_on_strided_rows(gns_mod, nesterov):
     assert np.array_equal(bits(W), decay_and_update(w, bf16_to_f64(bits(O)), 0.02, 0.1, sc))
     for full in (Wf, Mf, Gf):
         assert np.array_equal(bits(full[:, m:]), pad)
+
+
+def test_muon_scale_must_be_positive(gns_mod):
+    """scale=None selects 0.2 sqrt(max(n, m)); an explicit scale must be positive (an
+    explicit 0 or a negative value is refused, not turned into the default)."""
+    w, g, mo = synth.dion3_state(n=64, m=128, seed=360)
+    W, M, G = to_dev(w, "bf16"), to_dev(mo, "bf16"), to_dev(g, "bf16")
+    for bad in (0.0, -1.0):
+        with pytest.raises(ValueError):
+            gns_mod.muon_step(W, M, G, 0.02, scale=bad)
+    assert np.array_equal(bits(W), w) and np.array_equal(bits(M), mo)

@@ -109,13 +109,16 @@ def test_gemm_and_dion3_validation():
     assert L.dion3_step_batched(*bargs(2, 64 * 256, M=FAKE + 64 * 256 * 2)) == INVALID   # M overlaps W's 2nd entry
     assert L.dion3_step_batched(*bargs(2, 64 * 256, wsb=8)) == WS
     assert L.dion3_batched_workspace_size(2, 64, 256, 16, F16) > L.dion3_workspace_size(64, 256, 16, F16)
-    # dion3 on a caller-chosen row set: null S, k > N, k not a multiple of 8, short workspace, aliasing
+    # dion3 on a caller-chosen row set: null S, k > N, short workspace, aliasing; any k is
+    # accepted (the submatrix is padded to whole 8-row groups), so k = 12 reaches the
+    # workspace check
     rargs = lambda S=FAKE * 30, k=16, W=FAKE, wsb=1 << 40: (W, FAKE * 8, FAKE * 16, 64, 256, 256, S, k, 0.02, 0.0,
                                                            0.95, F16, ctypes.byref(sched), None, FAKE * 40, wsb,
                                                            None)
     assert L.dion3_step_rows(*rargs(S=None)) == INVALID
     assert L.dion3_step_rows(*rargs(k=72)) == INVALID
-    assert L.dion3_step_rows(*rargs(k=12)) == UNSUP
+    assert L.dion3_step_rows(*rargs(k=12, wsb=8)) == WS
+    assert L.dion3_workspace_size(64, 256, 12, F16) == L.dion3_workspace_size(64, 256, 16, F16)
     assert L.dion3_step_rows(*rargs(wsb=8)) == WS
     assert L.dion3_step_rows(*rargs(W=FAKE * 8)) == INVALID                # W is M
     # dion3 with device scalars: null scalars, misaligned scalars, null S
@@ -168,6 +171,7 @@ def test_muon_validation():
     assert L.muon_step_batched(*margs(nest=2)) == INVALID
     assert L.muon_step_batched(*margs(lr=float("nan"))) == INVALID
     assert L.muon_step_batched(*margs(scale=float("inf"))) == INVALID
+    assert L.muon_step_batched(*margs(scale=-1.0)) == INVALID             # 0 = default; negative refused
     assert L.muon_step_batched(*margs(m=252, ld=256)) == UNSUP            # m not a multiple of 8
     assert L.muon_step_batched(*margs(n=60, stride=60 * 256)) == UNSUP    # n not a multiple of 8
     assert L.muon_step_batched(*margs(compute=F32)) == UNSUP
