@@ -119,6 +119,28 @@ int gns_orthogonalize_batched(const void* X, gns_dtype x_dtype, long long ldx, l
                               const gns_schedule* sched, void* workspace, size_t ws_bytes,
                               hipStream_t stream, double* issued_flops);
 
+/* gns_orthogonalize_batched for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels run on a static device array of GNS_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * inside the library instead of a caller's workspace; each GPU holds its own copy
+ * from the library's load until the process ends.  The call allocates nothing and
+ * calls no allocating routine; on its first call on a device it looks up that
+ * device's copy (hipGetSymbolAddress).  Arguments, rules and results are those of
+ * gns_orthogonalize_batched (bitwise the same output).  Errors: GNS_ERR_WORKSPACE
+ * (nothing launched; gns_last_error() says why) when gns_workspace_size(batch, n, m,
+ * compute) exceeds GNS_NOALLOC_SCRATCH_BYTES -- the 1024 x 4096 matrix fits with any
+ * iterate dtype; GNS_ERR_INVALID_ARG when `stream` belongs to another device than the
+ * current one; otherwise as gns_orthogonalize_batched.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and give undefined results, so serialise them.  A call reads no part
+ * of the array that it did not write first, so nothing needs clearing between calls. */
+#define GNS_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gns_orthogonalize_batched_noalloc(const void* X, gns_dtype x_dtype, long long ldx, long long stride_x,
+                                      void* O, gns_dtype o_dtype, long long ldo, long long stride_o,
+                                      int batch, int n, int m, gns_dtype compute,
+                                      const gns_schedule* sched, hipStream_t stream,
+                                      double* issued_flops);
+
 /* Standard quintic Newton-Schulz (A = X X^T; B = b A + c A A; X <- a X + B X) on the
  * same kernels; same arguments and rules as gns_orthogonalize_batched (the restart
  * mask and square_fallback are ignored).

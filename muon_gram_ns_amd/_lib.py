@@ -64,6 +64,8 @@ _sig("gns_workspace_size", SZ, I, I, I, I)
 _NS_ARGS = (P, I, LL, LL, P, I, LL, LL, I, I, I, I, ctypes.POINTER(Schedule), P, SZ, P, DP)
 _sig("gns_orthogonalize_batched", I, *_NS_ARGS)
 _sig("gns_newton_schulz_batched", I, *_NS_ARGS)
+_sig("gns_orthogonalize_batched_noalloc", I, P, I, LL, LL, P, I, LL, LL, I, I, I, I, ctypes.POINTER(Schedule), P, DP)
+NOALLOC_SCRATCH_BYTES = 64 << 20     # GNS_NOALLOC_SCRATCH_BYTES
 _sig("symm_gemm", I, I, I, I, F, P, LL, LL, P, LL, LL, F, P, LL, LL, F, P, LL, LL, I, I, P)
 _sig("rect_gemm", I, I, I, I, I, F, P, LL, LL, I, P, LL, LL, I, F, F, P, LL, LL, P, LL, LL, I, P)
 _sig("dion3_accumulate_score", I, P, P, I, I, LL, I, P, P, P)
@@ -224,6 +226,30 @@ def orthogonalize(X, out=None, compute="f16", schedule=None, return_flops=False,
     -> same shape/dtype as X.
     workspace: optional uint8 device tensor of >= gns_workspace_size bytes."""
     return _ns("gns_orthogonalize_batched", X, out, compute, schedule, return_flops, workspace)
+
+
+def orthogonalize_noalloc(X, out=None, compute="f16", schedule=None):
+    """orthogonalize on the library's static device scratch (gns_orthogonalize_batched_noalloc):
+    no workspace is allocated, for callers that cannot allocate.  Calls on one GPU
+    share the scratch, so they must not overlap in time."""
+    torch = _torch()
+    _dev(X)
+    squeeze = X.dim() == 2
+    X3, B, n, m, ldx, sx = _mat3(X)
+    if out is None:
+        out = torch.empty((B, n, m), dtype=X.dtype, device=X.device)
+    _expect(out, "out", device=X.device)
+    O3, Bo, no, mo, ldo, so = _mat3(out)
+    if (Bo, no, mo) != (B, n, m):
+        raise ValueError("output shape mismatch")
+    sched = schedule if schedule is not None else default_schedule()
+    st = lib.gns_orthogonalize_batched_noalloc(X3.data_ptr(), dtype_code(X3), ldx, sx, O3.data_ptr(), dtype_code(O3),
+                                               ldo, so, B, n, m, code_of(compute), ctypes.byref(sched),
+                                               _stream(X.device), None)
+    if st == -3:
+        raise GnsError(f"gns_orthogonalize_batched_noalloc: {lib.gns_last_error().decode()}")
+    check(st, "gns_orthogonalize_batched_noalloc")
+    return out.squeeze(0) if (squeeze and out.dim() == 3) else out
 
 
 def newton_schulz(X, out=None, compute="f16", schedule=None, return_flops=False, workspace=None):

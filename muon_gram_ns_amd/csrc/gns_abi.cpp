@@ -20,6 +20,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "internal.h"
 #include "muon_kernels.h"
@@ -366,6 +367,48 @@ NsCall make_call(const void* X, gns_dtype xdt, long long ldx, long long sx, void
   return c;
 }
 
+// ---- the no-allocation entry point's scratch ------------------------------------
+// gns_orthogonalize_batched_noalloc runs the workspace variant's kernels on this
+// file-scope device array instead of a caller's workspace.  Each GPU the library runs
+// on holds its own copy until the process ends.  In host code the array's name is
+// only a stand-in: its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept in g_scratch.
+constexpr size_t kScratchBytes = GNS_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  void* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device (which must be the stream's).
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  HIP_OK(hipGetDevice(&dev));
+  if (stream) {
+    hipDevice_t sdev = 0;
+    HIP_OK(hipStreamGetDevice(stream, &sdev));
+    if ((int)sdev != dev) {
+      std::snprintf(g_last_error, sizeof(g_last_error), "the stream belongs to device %d, the current device is %d",
+                    (int)sdev, dev);
+      return GNS_ERR_INVALID_ARG;
+    }
+  }
+  if (dev < 0 || dev >= kMaxDevices) return GNS_ERR_UNSUPPORTED;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    void* p = nullptr;
+    slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // this device is current
+    slot.ptr = p;
+  });
+  if (slot.err != hipSuccess) return hip_fail(slot.err, "hipGetSymbolAddress(scratch)");
+  *out = slot.ptr;
+  return GNS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -442,6 +485,29 @@ int gns_newton_schulz_batched(const void* X, gns_dtype x_dtype, long long ldx, l
   if (st) return st;
   if (batch == 0) return GNS_OK;
   return run_ns(c, false);
+}
+
+int gns_orthogonalize_batched_noalloc(const void* X, gns_dtype x_dtype, long long ldx, long long stride_x, void* O,
+                                      gns_dtype o_dtype, long long ldo, long long stride_o, int batch, int n, int m,
+                                      gns_dtype compute, const gns_schedule* sched, hipStream_t stream,
+                                      double* issued_flops) {
+  if (issued_flops) *issued_flops = 0.0;
+  if (batch < 0 || n < 1 || m < 1 || !valid_dtype(compute)) return GNS_ERR_INVALID_ARG;
+  const size_t need = ns_workspace_bytes(batch, n, m, compute);
+  if (need > kScratchBytes) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "the call needs %zu bytes of scratch, more than the %zu bytes of the static scratch", need,
+                  kScratchBytes);
+    return GNS_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  int st = scratch_address(stream, &ws);
+  if (st) return st;
+  NsCall c = make_call(X, x_dtype, ldx, stride_x, O, o_dtype, ldo, stride_o, batch, n, m, compute, sched, ws,
+                       kScratchBytes, stream, issued_flops);
+  if ((st = check_ns(c))) return st;
+  if (batch == 0) return GNS_OK;
+  return run_ns(c, true);
 }
 
 static int check_gemm_common(int batch, gns_dtype in, gns_dtype out, const void* A, long long lda, long long sA,
