@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "orthogonalized matrices/s + TFLOP/s (% bf16 MFMA peak), batched Gram NS, α=4"
+DEFAULT_WORKLOAD = "gns_1024x4096_bf16"
 PEAK_16BIT_TFLOPS = 2516.6        # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -38,10 +39,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="gns_1024x4096_bf16")
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--compute", default="f16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-extra", action="store_true",
+                   help="default workload only: skip the other workloads and the bf16-iterate timing "
+                        "that the default line carries as extra keys")
     p.add_argument("--restart-sweep", action="store_true",
                    help="only measure Gram NS error against the float64 oracle for each restart "
                         "position (fp16 and bf16 iterates) on the 1024x4096 and square 2048^2 inputs, "
@@ -126,7 +130,6 @@ def main():
                       nstd, max(2, args.warmup // 4))
     graphed_std = gns.graphed_newton_schulz(X, out=torch.empty_like(X), compute=compute, schedule=sched)
     ms_std_graph = timed_ms(graphed_std.replay, nstd, max(2, args.warmup // 4))
-    del graphed, graphed_std
 
     muon = muon_timing(gns, torch, X, compute, sched, timed_ms, nstd, max(2, args.warmup // 4), ms) \
         if w.dtype == "bf16" else None
@@ -163,6 +166,21 @@ def main():
         "roofline": roof,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(st, w, args.cpu_seconds),
     }
+    if w.name == DEFAULT_WORKLOAD and not args.no_extra and compute == "f16":
+        del graphed, graphed_std
+        # the same call with bf16 iterates (bf16 MFMA; the Gram chain in hi/lo bf16 planes)
+        ms_bf = timed_ms(lambda: gns.orthogonalize(X, out=out, compute="bf16", schedule=sched), nstd,
+                         max(2, args.warmup // 4))
+        ms_bf_std = timed_ms(lambda: gns.newton_schulz(X, out=out_std, compute="bf16", schedule=sched), nstd,
+                             max(2, args.warmup // 4))
+        _, issued_bf = gns.orthogonalize(X, out=out, compute="bf16", schedule=sched, return_flops=True)
+        line["bf16_iterates"] = {"ms_per_step": round(ms_bf, 5), "matrices_per_s": round(B / (ms_bf * 1e-3), 3),
+                                 "tflops_issued": round(issued_bf / (ms_bf * 1e-3) / 1e12, 3),
+                                 "standard_ns_ms_per_step": round(ms_bf_std, 5),
+                                 "gram_speedup": round(ms_bf_std / ms_bf, 3)}
+        del X, out, out_std
+        torch.cuda.empty_cache()
+        line["other_workloads"] = other_workloads(args, gns, F, torch, np, synth)
     print(json.dumps(line), flush=True)
 
 
@@ -216,7 +234,7 @@ def measured_dion3_traffic(workload_name):
     return t["bytes_per_launch"]
 
 
-def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, workload_name):
+def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, workload_name, per_graph=10):
     """The lower-tile symmetric MFMA product in the iterate dtype dominates a Gram NS
     call.  Its per-call launch mix (the n x n products with K = n, plus the restart
     Gram product with K = m) is replayed through the C ABI on the current stream,
@@ -240,7 +258,6 @@ def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, wor
     Z = R if square else sym(torch.randn(B, n, n, device="cuda")).to(dt)
     Xh = (torch.randn(B, n, m, device="cuda") / m ** 0.5).to(dt)
     D = torch.empty(B, n, n, device="cuda", dtype=dt)
-    per_graph = 10
     nn_desc = "A A + beta A" if square else "R Z + beta R"
     launch_mix = f"{nn_k} x (n={n}, K={n}, {nn_desc}) + {mm_k} x (n={n}, K={m}, X X^T), batch {B}"
 
@@ -377,6 +394,110 @@ def cpu_baseline(st, w, seconds):
             "cpu_model": model, "blas": blas, "nproc": os.cpu_count(),
             "sample": f"{done} x one {w.n}x{w.m} matrix of the workload, float64 standard NS (numpy/OpenBLAS), "
                       f"{el:.1f} s"}
+
+
+def sync_timed_ms(torch, fn, steps, warmup):
+    """Mean ms per call of `steps` eager calls after `warmup` untimed ones, bracketed by
+    device synchronisations."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return 1e3 * (time.perf_counter() - t0) / steps
+
+
+def other_workloads(args, gns, F, torch, np, synth):
+    """The other configurations, timed in the same run as the default line so that their
+    figures are observed by the same driver run: the 32 x 4096^2 square batch (the pages'
+    aspect-ratio-1 fallback to standard NS, and the Gram path forced), the 128 x 768x6144
+    MoE batch (alpha = 8) and the Dion3 step on the 8192 x 28672 state (f = 1/4, 1/8).
+    Each carries a roofline of its dominant kernel, timed live with HIP events on the
+    launch stream.  Inputs are synth's seeded bytes (the Dion3 state is drawn on the
+    device from a seeded generator with the workload's distribution)."""
+    res = {}
+    steps = max(3, args.steps // 20)
+    warm = 2
+    for name in ("gns_32x4096x4096_bf16", "gns_128x768x6144_bf16"):
+        t0 = time.perf_counter()
+        w = synth.workload(name)
+        st = synth.gns_batch(w)
+        gen_s = time.perf_counter() - t0
+        X = torch.from_numpy(st.view(np.int16)).view(torch.bfloat16).cuda()
+        del st
+        B, n, m = X.shape
+        out = torch.empty_like(X)
+        entry = {"batch": B, "n": n, "m": m, "alpha": m / n, "iterate_dtype": "f16", "input_generation_s": round(gen_s, 1)}
+        nominal = B * F.standard_ns_nominal(n, m)
+
+        def figures(ms, issued, alg):
+            return {"ms_per_step": round(ms, 4), "matrices_per_s": round(B / (ms * 1e-3), 3),
+                    "tflops_standard_ns_equivalent": round(nominal / (ms * 1e-3) / 1e12, 3),
+                    "tflops_algorithmic": round(alg / (ms * 1e-3) / 1e12, 3),
+                    "tflops_issued": round(issued / (ms * 1e-3) / 1e12, 3),
+                    "pct_peak_issued": round(100 * issued / (ms * 1e-3) / 1e12 / PEAK_16BIT_TFLOPS, 3)}
+
+        gram_sched = gns.default_schedule(square_fallback=False)
+        _, iss_g = gns.orthogonalize(X, out=out, schedule=gram_sched, return_flops=True)
+        ms_g = sync_timed_ms(torch, lambda: gns.orthogonalize(X, out=out, schedule=gram_sched), steps, warm)
+        _, iss_s = gns.newton_schulz(X, out=out, return_flops=True)
+        ms_s = sync_timed_ms(torch, lambda: gns.newton_schulz(X, out=out), steps, warm)
+        entry["gram_ns"] = figures(ms_g, iss_g, B * F.gram_schedule(n, m))
+        entry["standard_ns_same_kernels"] = figures(ms_s, iss_s, B * F.standard_schedule(n, m))
+        entry["gram_speedup"] = round(ms_s / ms_g, 3)
+        if n == m:
+            entry["default_call"] = ("standard NS: at aspect ratio 1 the Gram form saves nothing and the pages fall "
+                                     "back to kernelized standard NS (square_fallback = 1); gram_ns is the Gram "
+                                     "path forced (square_fallback = 0)")
+        del out
+        entry["roofline"] = dominant_kernel_roofline(gns, F, torch, B, n, m, "f16", False, 40, name, per_graph=1)
+        del X
+        torch.cuda.empty_cache()
+        res[name] = entry
+    res["dion3_8192x28672_bf16"] = dion3_figures(args, synth.workload("dion3_8192x28672_bf16"), gns, F, torch)
+    torch.cuda.empty_cache()
+    return res
+
+
+def dion3_figures(args, w, gns, F, torch, fractions=(0.25, 0.125)):
+    """Whole Dion3 steps (l2 row scores, mu = 0.95, wd = 0, lr = 0.01 / sqrt(f)) on the
+    workload's state, and the roofline of the accumulate-and-score pass (HBM-bound; the
+    largest kernel of the step)."""
+    N, m = w.n, w.m
+    gen = torch.Generator(device="cuda").manual_seed(1000 + w.index)
+    dev_bf16 = lambda: (torch.randn(N, m, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    W, G, M = dev_bf16(), dev_bf16(), dev_bf16()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    reps = max(5, args.steps // 10)
+    res = {"N": N, "m": m, "score": "l2", "mu": 0.95, "wd": 0.0, "iterate_dtype": args.compute}
+    for f in fractions:
+        k = math.ceil(f * N)
+        lr = 0.01 / f ** 0.5
+        t = timed(lambda: gns.dion3_step(W, M, G, k, lr, 0.0, 0.95, score_norm=2, compute=args.compute), reps)
+        res[f"f={f}"] = {"k": k, "ms_per_step": round(t * 1e3, 4), "steps_per_s": round(1.0 / t, 3),
+                         "gram_ns_tflops_algorithmic": round(F.gram_schedule(k, m) / t / 1e12, 2)}
+    t_acc = timed(lambda: gns.dion3_accumulate_score(M, G, 2), reps)
+    b_acc = 3.0 * N * m * 2
+    res["roofline"] = {"bound": "hbm", "kernel": "accumulate_score_kernel", "achieved": round(b_acc / t_acc / 1e9, 1),
+                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(b_acc / t_acc / 1e9 / PEAK_HBM_GBS, 4),
+                       "traffic": measured_dion3_traffic(w.name), "algorithmic_bytes_per_launch": b_acc,
+                       "avg_launch_us": round(t_acc * 1e6, 2)}
+    del W, G, M
+    return res
 
 
 def restart_sweep(gns, synth, torch, np):
