@@ -488,8 +488,13 @@ def dion3_figures(args, w, gns, F, torch, fractions=(0.25, 0.125)):
         k = math.ceil(f * N)
         lr = 0.01 / f ** 0.5
         t = timed(lambda: gns.dion3_step(W, M, G, k, lr, 0.0, 0.95, score_norm=2, compute=args.compute), reps)
+        # the same step with the selected rows read in place (no gathered copy of M[S, :])
+        inplace = gns.default_schedule(rows_in_place=True)
+        t_in = timed(lambda: gns.dion3_step(W, M, G, k, lr, 0.0, 0.95, score_norm=2, compute=args.compute,
+                                            schedule=inplace), reps)
         res[f"f={f}"] = {"k": k, "ms_per_step": round(t * 1e3, 4), "steps_per_s": round(1.0 / t, 3),
-                         "gram_ns_tflops_algorithmic": round(F.gram_schedule(k, m) / t / 1e12, 2)}
+                         "gram_ns_tflops_algorithmic": round(F.gram_schedule(k, m) / t / 1e12, 2),
+                         "rows_in_place_ms_per_step": round(t_in * 1e3, 4)}
     t_acc = timed(lambda: gns.dion3_accumulate_score(M, G, 2), reps)
     b_acc = 3.0 * N * m * 2
     res["roofline"] = {"bound": "hbm", "kernel": "accumulate_score_kernel", "achieved": round(b_acc / t_acc / 1e9, 1),
@@ -663,9 +668,16 @@ def bench_dion3(args, w):
         for _ in range(args.warmup):
             step_rows()
         t_rows = timed(step_rows, args.steps)
+        inplace = gns.default_schedule(rows_in_place=True)
+        step_in = lambda: gns.dion3_step(W, M, G, k, lr, 0.0, 0.95, score_norm=2, compute=args.compute,
+                                         schedule=inplace)
+        for _ in range(args.warmup):
+            step_in()
+        t_in = timed(step_in, args.steps)
         res[f] = {"k": k, "ms_per_step": round(t * 1e3, 4), "graph_replay_ms_per_step": round(t_graph * 1e3, 4),
                   "gram_ns_tflops_algorithmic": round(F.gram_schedule(k, m) / t / 1e12, 2),
-                  "random_rows_ms_per_step": round(t_rows * 1e3, 4)}
+                  "random_rows_ms_per_step": round(t_rows * 1e3, 4),
+                  "rows_in_place_ms_per_step": round(t_in * 1e3, 4)}
     # the HBM-bound pieces, alone (k = 2048)
     k = N // 4
     reps = max(5, args.steps)

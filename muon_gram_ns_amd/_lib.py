@@ -45,7 +45,7 @@ DP = ctypes.POINTER(ctypes.c_double)
 class Schedule(ctypes.Structure):
     _fields_ = [("steps", I), ("a", F * GNS_MAX_STEPS), ("b", F * GNS_MAX_STEPS),
                 ("c", F * GNS_MAX_STEPS), ("restart_after_mask", ctypes.c_uint), ("eps", F),
-                ("square_fallback", I)]
+                ("square_fallback", I), ("rows_in_place", I)]
 
 
 def _sig(name, res, *args):
@@ -103,7 +103,7 @@ def check(status: int, what: str):
 
 
 def default_schedule(steps=5, abc=(3.4445, -4.7750, 2.0315), restart_after=(2,), eps=1e-7,
-                     square_fallback=True) -> Schedule:
+                     square_fallback=True, rows_in_place=False) -> Schedule:
     s = Schedule()
     lib.gns_default_schedule(ctypes.byref(s))
     s.steps = steps
@@ -116,6 +116,7 @@ def default_schedule(steps=5, abc=(3.4445, -4.7750, 2.0315), restart_after=(2,),
     s.restart_after_mask = mask
     s.eps = eps
     s.square_fallback = 1 if square_fallback else 0
+    s.rows_in_place = 1 if rows_in_place else 0
     return s
 
 

@@ -366,11 +366,14 @@ hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long lon
 template <bool O_F32>
 __global__ void __launch_bounds__(kRowThreads)
 apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, const int* S, int k, const void* O,
-                    long long ldo, long long so, float lr_host, float wd_host, const float* dev_scalars, int all_rows) {
+                    long long ldo, long long so, float lr_host, float wd_host, const float* dev_scalars, int all_rows,
+                    uint16_t* Mfb, float mu_host) {
   const float lr = dev_scalars ? dev_scalars[0] : lr_host;
   const float wd = dev_scalars ? dev_scalars[1] : wd_host;
+  const float mu = dev_scalars ? dev_scalars[2] : mu_host;
   const int d_over = blockIdx.x, b = blockIdx.y;
   W += (size_t)b * stride;
+  if (Mfb) Mfb += (size_t)b * stride;
   S += (size_t)b * k;
   O = reinterpret_cast<const uint8_t*>(O) + (size_t)b * so * (O_F32 ? 4 : 2);
   int row, oi;
@@ -394,8 +397,13 @@ apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, c
   if (oi < 0 && wd == 0.0f) return;
   const float d = __fsub_rn(1.0f, __fmul_rn(lr, wd));
   uint4* wr = reinterpret_cast<uint4*>(W + (size_t)row * ld);
+  // error feedback on the same selected row, in the same pass: M[S[oi]] <- bf16(mu
+  // M[S[oi]]), the arithmetic of gather_feedback_kernel (the Gram products have read
+  // these rows already); W and M chunks are loaded together for more bytes in flight
+  uint4* mr = (Mfb && oi >= 0) ? reinterpret_cast<uint4*>(Mfb + (size_t)row * ld) : nullptr;
   for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
     uint4 v = load_nt(&wr[c]);
+    uint4 mv = mr ? load_nt(&mr[c]) : make_uint4(0u, 0u, 0u, 0u);
     uint32_t* w = reinterpret_cast<uint32_t*>(&v);
     float o[8];
     if (oi >= 0) {
@@ -426,12 +434,22 @@ apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, c
       w[i] = out;
     }
     store_nt(v, &wr[c]);
+    if (mr) {
+      uint32_t* mw = reinterpret_cast<uint32_t*>(&mv);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = f32_to_bf16_bits(__fmul_rn(mu, bf16_bits_to_f32(mw[i] & 0xffffu)));
+        const uint32_t hi = f32_to_bf16_bits(__fmul_rn(mu, bf16_bits_to_f32(mw[i] >> 16)));
+        mw[i] = lo | (hi << 16);
+      }
+      store_nt(mv, &mr[c]);
+    }
   }
 }
 
 hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long ld, long long stride, const int* S, int k,
                                const void* O, gns_dtype o_dtype, long long ldo, long long so, float lr, float wd,
-                               const float* dev_scalars, hipStream_t s) {
+                               const float* dev_scalars, hipStream_t s, uint16_t* Mfb, float mu) {
   // with the weight decay on the device the host cannot tell whether unselected rows
   // decay: cover all rows (each unselected row returns at once when wd == 0)
   const int all_rows = (dev_scalars || wd != 0.0f) ? 1 : 0;
@@ -440,10 +458,10 @@ hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long l
   clear_stale_error();
   if (o_dtype == GNS_F32)
     hipLaunchKernelGGL(apply_update_kernel<true>, dim3(blocks, batch), dim3(kRowThreads), 0, s, W, N, m, ld, stride, S,
-                       k, O, ldo, so, lr, wd, dev_scalars, all_rows);
+                       k, O, ldo, so, lr, wd, dev_scalars, all_rows, Mfb, mu);
   else
     hipLaunchKernelGGL(apply_update_kernel<false>, dim3(blocks, batch), dim3(kRowThreads), 0, s, W, N, m, ld, stride,
-                       S, k, O, ldo, so, lr, wd, dev_scalars, all_rows);
+                       S, k, O, ldo, so, lr, wd, dev_scalars, all_rows, Mfb, mu);
   return hipGetLastError();
 }
 

@@ -798,7 +798,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N>
 constexpr int max_waves_per_eu() { return (BM / WAVES_M) * (BN / WAVES_N) >= 128 * 128 ? 1 : 8; }
 
 template <class TIn, class TB, class TOut, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BKV, bool LOWER,
-          bool NN, bool NT = false, bool PL = false>
+          bool NN, bool NT = false, bool PL = false, bool IDX = false>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(1, max_waves_per_eu<BM, BN, WAVES_M, WAVES_N>())))
 gemm16_kernel(GemmParams p) {
@@ -858,9 +858,12 @@ gemm16_kernel(GemmParams p) {
   const int a_pl = PL ? (gp.second ? p.a2_planes : p.a_planes) : 1, b_pl = PL ? p.b_planes : 1;
   const int npairs = (a_pl == 2 && b_pl == 2) ? 3 : a_pl * b_pl;
   const uint32_t plane_bytes = (uint32_t)(p.plane * 2);
-  const int4v_t rsA = sgpr_rsrc(Ab, (uint32_t)(((size_t)(M - 1) * p.lda + K + (a_pl - 1) * p.plane) * 2));
-  const int4v_t rsB = NN ? sgpr_rsrc(Bb, (uint32_t)(((size_t)(K - 1) * p.ldb + N) * 2))
-                         : sgpr_rsrc(Bb, (uint32_t)(((size_t)(N - 1) * p.ldb + K + (b_pl - 1) * p.plane) * 2));
+  // an indexed operand spans its whole source matrix (src_rows rows)
+  const int a_rows_span = (IDX && !NN) ? p.src_rows : M;
+  const int b_rows_span = IDX ? p.src_rows : (NN ? K : N);
+  const int4v_t rsA = sgpr_rsrc(Ab, (uint32_t)(((size_t)(a_rows_span - 1) * p.lda + K + (a_pl - 1) * p.plane) * 2));
+  const int4v_t rsB = NN ? sgpr_rsrc(Bb, (uint32_t)(((size_t)(b_rows_span - 1) * p.ldb + N) * 2))
+                         : sgpr_rsrc(Bb, (uint32_t)(((size_t)(b_rows_span - 1) * p.ldb + K + (b_pl - 1) * p.plane) * 2));
   const int KTp = (kend - kbeg + BK - 1) / BK;       // stages per plane pair
   const int KT = KTp * npairs;
   float bmul = 1.0f;
@@ -869,9 +872,57 @@ gemm16_kernel(GemmParams p) {
     if (p.scale) for (int i = 0; i < p.b_pow; ++i) bmul *= p.scale[bz];
   }
 
+  // Indexed X rows.  Symmetric product: each lane's operand rows are the same in every
+  // stage, so their source offsets are looked up once here.  Rectangular product: the
+  // B rows change with the stage, so the batch entry's row table is copied into LDS
+  // after the ring (before any operand load; every wave waits for it and a barrier
+  // publishes it).
+  constexpr int XA = (IDX && !NN) ? A_INSTR : 1, XB = (IDX && !NN) ? B_INSTR : 1;
+  uint32_t a_roff[XA], b_roff[XB];
+  bool a_rok[XA], b_rok[XB];
+  const int* tbl = nullptr;
+  if constexpr (IDX) {
+    const int* rws = p.rows + (size_t)bz * p.rows_stride;
+    if constexpr (!NN) {
+#pragma unroll
+      for (int g = 0; g < XA; ++g) {
+        const int gr = m0 + ((g * NW + wave) * 64 + lane) / CPR;
+        const int pr = gr < p.rows_valid ? rws[gr] : -1;
+        a_rok[g] = pr >= 0 && pr < p.src_rows;
+        a_roff[g] = a_rok[g] ? (uint32_t)((size_t)pr * p.lda * 2) : 0u;
+      }
+#pragma unroll
+      for (int g = 0; g < XB; ++g) {
+        const int gr = n0 + ((g * NW + wave) * 64 + lane) / CPR;
+        const int pr = gr < p.rows_valid ? rws[gr] : -1;
+        b_rok[g] = pr >= 0 && pr < p.src_rows;
+        b_roff[g] = b_rok[g] ? (uint32_t)((size_t)pr * p.ldb * 2) : 0u;
+      }
+    } else {
+      const int4v_t rsT = sgpr_rsrc(rws, (uint32_t)p.rows_valid * 4u);
+      const int instrs = (p.rows_valid * 4 + 1023) / 1024;
+      for (int i = wave; i < instrs; i += NW)
+        dma16(rsT, __builtin_amdgcn_readfirstlane(lds0 + NS * STAGE + i * 1024), (uint32_t)(i * 64 + lane) * 16u);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      lds_barrier();
+      tbl = reinterpret_cast<const int*>(smem16 + NS * STAGE);
+    }
+  }
+
   // load g (0 .. LOADS-1) of k-stage kt: one direct HBM -> LDS instruction (1 KB per
   // wave) into ring slot kt % NS; loads 0 .. A_INSTR-1 fill the A tile, the rest B
-  auto issue_load = [&](int kt, int g) {
+  // source row of B load gb (0 .. B_INSTR-1) of stage kt of an indexed rectangular
+  // product (-1: a zero row)
+  auto nn_row = [&](int kt, int gb) -> int {
+    if constexpr (IDX && NN) {
+      const int kr = ((gb * NW + wave) * 64 + lane) / NCH;
+      const int gk = kbeg + kt * BK + kr;
+      return (kt < KT && gk < p.rows_valid) ? tbl[gk] : -1;
+    } else {
+      return -1;
+    }
+  };
+  auto issue_load = [&](int kt, int g, int pre_row = -2) {
     // plane pair of stage kt and its K offset; stages at or past KT load nothing
     // (one pair: stages past the end have k0 >= kend, so their offsets are out of range)
     const int pi = PL ? (kt >= KTp) + (kt >= 2 * KTp) : 0;
@@ -885,8 +936,11 @@ gemm16_kernel(GemmParams p) {
       const int q = blk * 64 + lane;                      // LDS chunk this lane fills
       const int row = q / CPR, lc = swz_k<BK>(row, q % CPR);
       const int gr = m0 + row, gk = k0 + lc * 8;
-      const uint32_t off = (live && gr < M && gk < kend) ? (uint32_t)(((size_t)gr * p.lda + gk) * 2) + a_add
-                                                         : kOutOfRange;
+      uint32_t off;
+      if constexpr (IDX && !NN)
+        off = (live && a_rok[g] && gk < kend) ? a_roff[g] + (uint32_t)gk * 2u : kOutOfRange;
+      else
+        off = (live && gr < M && gk < kend) ? (uint32_t)(((size_t)gr * p.lda + gk) * 2) + a_add : kOutOfRange;
       dma16(rsA, __builtin_amdgcn_readfirstlane(sb + blk * 1024), off);
     } else {
       const int blk = (g - A_INSTR) * NW + wave;
@@ -895,11 +949,21 @@ gemm16_kernel(GemmParams p) {
       if constexpr (!NN) {
         const int row = q / CPR, lc = swz_k<BK>(row, q % CPR);
         const int gr = n0 + row, gk = k0 + lc * 8;
-        off = (live && gr < N && gk < kend) ? (uint32_t)(((size_t)gr * p.ldb + gk) * 2) + b_add : kOutOfRange;
+        if constexpr (IDX)
+          off = (live && b_rok[g - A_INSTR] && gk < kend) ? b_roff[g - A_INSTR] + (uint32_t)gk * 2u : kOutOfRange;
+        else
+          off = (live && gr < N && gk < kend) ? (uint32_t)(((size_t)gr * p.ldb + gk) * 2) + b_add : kOutOfRange;
       } else {
         const int kr = q / NCH, lc = (q % NCH) ^ nn_swz(kr);
         const int gk = k0 + kr, gn = n0 + lc * 8;
-        off = (live && gk < kend && gn < N) ? (uint32_t)(((size_t)gk * p.ldb + gn) * 2) : kOutOfRange;
+        if constexpr (IDX) {
+          // k-row gk of B is source row tbl[gk] (rows past rows_valid are zeros), looked
+          // up here or, in the ping-pong schedule, one memory phase ahead
+          const int pr = pre_row >= -1 ? pre_row : ((live && gk < p.rows_valid) ? tbl[gk] : -1);
+          off = (pr >= 0 && pr < p.src_rows && gn < N) ? (uint32_t)(((size_t)pr * p.ldb + gn) * 2) : kOutOfRange;
+        } else {
+          off = (live && gk < kend && gn < N) ? (uint32_t)(((size_t)gk * p.ldb + gn) * 2) : kOutOfRange;
+        }
       }
       dma16(rsB, __builtin_amdgcn_readfirstlane(sb + A_BYTES + blk * 1024), off);
     }
@@ -1014,11 +1078,27 @@ gemm16_kernel(GemmParams p) {
     const int grp = wm;
     uint4 fa[KS][FM], fb[KS][FN];
     constexpr int kAhead = (NS - 2) * LOADS;
+    // indexed B rows: looked up one memory phase ahead, so the LDS read of the row
+    // table is done by the time the loads that use it are issued
+    int b_pre[(IDX && NN) ? B_INSTR : 1];
+    if constexpr (IDX && NN) {
+#pragma unroll
+      for (int gb = 0; gb < B_INSTR; ++gb) b_pre[gb] = nn_row(NS - 1, gb);
+    }
     auto memory_phase = [&](int i) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) read_frags(i % NS, ks, fa[ks], fb[ks]);
+      if constexpr (IDX && NN) {
 #pragma unroll
-      for (int g = 0; g < LOADS; ++g) issue_load(i + NS - 1, g);
+        for (int g = 0; g < A_INSTR; ++g) issue_load(i + NS - 1, g);
+#pragma unroll
+        for (int gb = 0; gb < B_INSTR; ++gb) issue_load(i + NS - 1, A_INSTR + gb, b_pre[gb]);
+#pragma unroll
+        for (int gb = 0; gb < B_INSTR; ++gb) b_pre[gb] = nn_row(i + NS, gb);
+      } else {
+#pragma unroll
+        for (int g = 0; g < LOADS; ++g) issue_load(i + NS - 1, g);
+      }
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));   // slot i % NS may be refilled after the barrier
     };
     auto compute_phase = [&]() {
@@ -1201,9 +1281,12 @@ inline bool operand_extents_ok(const GemmParams& p, int a_bytes, int b_bytes, bo
   if (p.M <= 0 || p.N <= 0 || p.K <= 0) return true;
   const size_t lim = size_t(1) << 31;
   const int apl = std::max(p.a_planes, p.a2_planes);
-  const size_t a = ((size_t)(p.M - 1) * p.lda + p.K + (size_t)(apl - 1) * p.plane) * a_bytes;
-  const size_t b = nn ? ((size_t)(p.K - 1) * p.ldb + p.N) * b_bytes
-                      : ((size_t)(p.N - 1) * p.ldb + p.K + (size_t)(p.b_planes - 1) * p.plane) * b_bytes;
+  // an indexed operand spans its whole source matrix
+  const int a_rows = (p.rows && !nn) ? std::max(p.src_rows, 1) : p.M;
+  const int b_rows = p.rows ? std::max(p.src_rows, 1) : (nn ? p.K : p.N);
+  const size_t a = ((size_t)(a_rows - 1) * p.lda + p.K + (size_t)(apl - 1) * p.plane) * a_bytes;
+  const size_t b = nn ? ((size_t)(b_rows - 1) * p.ldb + p.N) * b_bytes
+                      : ((size_t)(b_rows - 1) * p.ldb + p.K + (size_t)(p.b_planes - 1) * p.plane) * b_bytes;
   return a < lim && b < lim;
 }
 
@@ -1280,7 +1363,35 @@ hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops
   bool planes = false;
   for (int v : {p.a_planes, p.a2_planes, p.b_planes, p.c_planes, p.c2_planes, p.d_planes, p.dp_planes})
     planes = planes || v != 1;
-  if (planes) {
+  // indexed X rows: separate instantiations too -- the Gram product of bf16 rows
+  // (symmetric, planes handled when the output is bf16) and the rectangular product
+  // with bf16 B rows, whose row table takes LDS after the ring
+  int dyn_lds = lds;
+  if (p.rows) {
+    if (p.rows_valid < 0 || p.src_rows < 1) return hipErrorInvalidValue;
+    if constexpr (k16 && LOWER && !NN && TIn::kId == GNS_BF16 && TB::kId == GNS_BF16) {
+      constexpr bool PLX = TOut::kId == GNS_BF16;
+      if (planes && !PLX) return hipErrorInvalidValue;
+      if (p.rows_valid > p.M || p.B != p.A) return hipErrorInvalidValue;
+      void (*with_idx)(GemmParams) = gemm16_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, NS, BKV, LOWER, NN, false, PLX, true>;
+      static hipError_t attr_idx = hipFuncSetAttribute(reinterpret_cast<const void*>(with_idx),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (attr_idx != hipSuccess) return attr_idx;
+      kern = with_idx;
+    } else if constexpr (k16 && NN && !LOWER && TB::kId == GNS_BF16) {
+      if (planes || p.rows_valid > p.K || p.K > kMaxIndexedRows) return hipErrorInvalidValue;
+      constexpr int kMaxLds = 160 * 1024;
+      dyn_lds = lds + (p.K * 4 + 1023) / 1024 * 1024;
+      if (dyn_lds > kMaxLds) return hipErrorInvalidValue;
+      void (*with_idx)(GemmParams) = gemm16_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, NS, BKV, LOWER, NN, false, false, true>;
+      static hipError_t attr_idx = hipFuncSetAttribute(reinterpret_cast<const void*>(with_idx),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+      if (attr_idx != hipSuccess) return attr_idx;
+      kern = with_idx;
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (planes) {
     if constexpr (k16 && LOWER && !NN && TOut::kId == GNS_BF16) {
       void (*with_pl)(GemmParams) = gemm16_kernel<TIn, TB, TOut, BM, BN, WM_, WN_, NS, BKV, LOWER, NN, false, true>;
       static hipError_t attr_pl = hipFuncSetAttribute(reinterpret_cast<const void*>(with_pl),
@@ -1311,7 +1422,7 @@ hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops
   p.batch = batch;
   p.tiles = (int)tiles;
   clear_stale_error();
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * batch * products * splits)), dim3(threads), lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * batch * products * splits)), dim3(threads), dyn_lds, stream, p);
   return hipGetLastError();
 }
 
@@ -1391,6 +1502,7 @@ hipError_t launch_symm_split_cfg(GemmParams p, int batch, float* part, hipStream
   e = launch_sum_ranges(part, tiles, p.ksplit, BM * BM, stream);
   if (e != hipSuccess) return e;
   p.reduce = 2;
+  p.rows = nullptr;      // the epilogue launch reads no operand
   return launch_one<TIn, TIn, TOut, BM, BM, WM_, WN_, NS, BKV, true, false>(p, batch, stream, flops);
 }
 

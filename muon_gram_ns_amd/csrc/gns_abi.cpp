@@ -124,6 +124,12 @@ struct NsCall {
   hipStream_t stream;
   double* flops;
   const float* s_given;   // precomputed device scale (Dion3), or null
+  // X read through a row table (Dion3's selected rows, straight from the state): row r
+  // of entry b is source row rows[b * rows_stride + r] of the state at X (rows r >=
+  // rows_valid are zero rows); only the Gram path of a wide call reads X this way
+  const int* rows;
+  int rows_valid, src_rows;
+  long long rows_stride;
 };
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -136,6 +142,8 @@ int check_schedule(const gns_schedule& s) {
   const unsigned allowed = ((1u << s.steps) - 1u) & ~1u;    // bits 1..steps-1
   if (s.restart_after_mask & ~allowed) return GNS_ERR_INVALID_ARG;
   if (!(s.eps >= 0.0f) || !std::isfinite(s.eps)) return GNS_ERR_INVALID_ARG;
+  if (s.square_fallback != 0 && s.square_fallback != 1) return GNS_ERR_INVALID_ARG;
+  if (s.rows_in_place != 0 && s.rows_in_place != 1) return GNS_ERR_INVALID_ARG;
   for (int t = 0; t < s.steps; ++t)
     if (!std::isfinite(s.a[t]) || !std::isfinite(s.b[t]) || !std::isfinite(s.c[t])) return GNS_ERR_INVALID_ARG;
   return GNS_OK;
@@ -213,9 +221,14 @@ int run_gram(const NsCall& c) {
 
   // R0 = s^2 X X^T: operands in X's dtype, result in the iterate dtype.  Without a
   // given scale, the product forms s from the partial sums and stores it to L.s.
+  // the X operand's row table, when X is read from the Dion3 state directly
+  auto x_rows = [&](GemmParams& g) {
+    g.rows = c.rows; g.rows_valid = c.rows_valid; g.rows_stride = c.rows_stride; g.src_rows = c.src_rows;
+  };
   {
     GemmParams g = symm_params(n, m, c.X, c.ldx, c.sx, c.X, c.ldx, c.sx, L.R, n, sn);
     chain(g, 1, 1, 1, pl);
+    if (c.rows) x_rows(g);
     g.alpha_pow = 2;
     if (c.s_given) {
       g.scale = s;
@@ -238,6 +251,7 @@ int run_gram(const NsCall& c) {
     g.B = cx; g.ldb = cld; g.sB = csx;
     g.D = out; g.ldd = ldo; g.sD = so;
     const float out_mul = final_out ? 1.0f : P;      // stored X-like iterates carry P
+    if (cx_orig && c.rows) x_rows(g);
     if (cx_orig) {
       if (cxdt == cdt) {
         g.alpha = out_mul; g.scale = s; g.alpha_pow = 1;
@@ -364,6 +378,7 @@ NsCall make_call(const void* X, gns_dtype xdt, long long ldx, long long sx, void
   c.batch = batch; c.n = n; c.m = m; c.cdt = cdt;
   if (sched) c.sch = *sched; else gns_default_schedule(&c.sch);
   c.ws = ws; c.ws_bytes = ws_bytes; c.stream = stream; c.flops = flops; c.s_given = nullptr;
+  c.rows = nullptr; c.rows_valid = 0; c.src_rows = 0; c.rows_stride = 0;
   return c;
 }
 
@@ -421,6 +436,7 @@ void gns_default_schedule(gns_schedule* s) {
   s->restart_after_mask = 1u << 2;    // restart after step 2 (before step 3)
   s->eps = 1e-7f;
   s->square_fallback = 1;
+  s->rows_in_place = 0;
 }
 
 const char* gns_last_error(void) { return g_last_error; }
@@ -692,10 +708,26 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
   const int kp = padded_rows(k);
   void* O = (O_out && kp == k) ? O_out : L.O;
   const long long km = (long long)k * m, kpm = (long long)kp * m;
+  if (overlaps(workspace, L.bytes, W, span) || overlaps(workspace, L.bytes, M, span) ||
+      overlaps(workspace, L.bytes, G, span))
+    return GNS_ERR_INVALID_ARG;
+  // With rows_in_place, the selected rows are read straight from M by the Gram path's
+  // products (the submatrix X is never written; Algorithm 4 orthogonalises M[S, :]
+  // itself), and the error feedback on M[S, :] runs with the weight update, after the
+  // last read.  That needs the Gram path on a wide submatrix (a square one may fall
+  // back to standard NS, a tall one runs on a transpose), a row table that fits in LDS
+  // and a state addressable with 32-bit offsets; otherwise the rows are gathered into X
+  // first (the default: faster on MI355X, where the fresh copy sits in the Infinity
+  // Cache for the products that re-read it).
+  const bool gram_path = kp < m || (kp == m && !sch.square_fallback);
+  const bool direct = sch.rows_in_place && gram_path && kp <= kMaxIndexedRows &&
+                      ((size_t)(N - 1) * ld + m) * 2 < (size_t(1) << 31);
   // one batched Gram NS over the selected kp x m submatrices of every entry; its
   // arguments are checked before anything is launched
-  NsCall c = make_call(L.X, GNS_BF16, m, kpm, O, GNS_BF16, m, kpm, batch, kp, m, compute, &sch, L.gns_ws,
-                       L.gns_bytes, stream, nullptr);
+  NsCall c = direct ? make_call(M, GNS_BF16, ld, stride, O, GNS_BF16, m, kpm, batch, kp, m, compute, &sch, L.gns_ws,
+                                L.gns_bytes, stream, nullptr)
+                    : make_call(L.X, GNS_BF16, m, kpm, O, GNS_BF16, m, kpm, batch, kp, m, compute, &sch, L.gns_ws,
+                                L.gns_bytes, stream, nullptr);
   c.s_given = L.s;
   if ((st = check_ns(c))) return st;
   if (O_out && (overlaps(O_out, (size_t)batch * km * 2, workspace, L.bytes) ||
@@ -710,13 +742,17 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
     HIP_OK(launch_topk(L.score, batch, N, k, S_out, stream));
     S = S_out;
   }
-  HIP_OK(launch_gather_feedback(Mh, batch, N, m, ld, stride, S, k, kp, mu, dev_scalars, (uint16_t*)L.X, m, stream));
+  if (direct) {
+    c.rows = S; c.rows_valid = k; c.rows_stride = k; c.src_rows = N;
+  } else {
+    HIP_OK(launch_gather_feedback(Mh, batch, N, m, ld, stride, S, k, kp, mu, dev_scalars, (uint16_t*)L.X, m, stream));
+  }
   HIP_OK(launch_selected_sumsq(L.sumsq, S, batch, k, N, sch.eps, L.s, stream));
   if ((st = run_ns(c, true))) return st;
   if (O_out && O != O_out)
     HIP_OK(launch_cast_scale(O, GNS_BF16, m, kpm, O_out, GNS_BF16, m, km, batch, k, m, 1.0f, nullptr, 0, stream));
   HIP_OK(launch_apply_update((uint16_t*)W, batch, N, m, ld, stride, S, k, O, GNS_BF16, m, kpm, lr, weight_decay,
-                             dev_scalars, stream));
+                             dev_scalars, stream, direct ? Mh : nullptr, mu));
   return GNS_OK;
 }
 

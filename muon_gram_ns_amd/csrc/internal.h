@@ -47,6 +47,13 @@ struct GemmParams {
   // of a pair.
   int a_planes = 1, a2_planes = 1, b_planes = 1, c_planes = 1, c2_planes = 1, d_planes = 1, dp_planes = 1;
   long long plane = 0;
+  // indexed rows (16-bit kernel only): the X operand is read straight from a larger
+  // source matrix -- the A and B operands of a symmetric product (the Gram product
+  // X X^T, A == B), the B operand of a rectangular one.  Row r of batch entry b is
+  // source row rows[b * rows_stride + r]; rows r >= rows_valid, and indices outside
+  // [0, src_rows), read as zeros.  The source is addressed through A (B) with lda
+  // (ldb) and the batch stride sA (sB) as usual.
+  const int* rows = nullptr; int rows_valid = 0; long long rows_stride = 0; int src_rows = 0;
   int tiles_m = 0, tiles_n = 0;   // set by the launcher
   int batch = 0, tiles = 0;       // set by the launcher: grid = batch * tiles workgroups
 };
@@ -100,9 +107,13 @@ hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long lon
                                   int k, int kx, float mu, const float* dev_scalars, uint16_t* X, long long ldx,
                                   hipStream_t s);
 // O: k rows (row stride ldo) per batch entry, entries so elements apart.
+// Mfb (nullable): also apply the error feedback M[S] <- bf16(mu M[S]) to the same rows
+// (M with W's row stride and batch stride).
 hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long ld, long long stride, const int* S, int k,
                                const void* O, gns_dtype o_dtype, long long ldo, long long so, float lr, float wd,
-                               const float* dev_scalars, hipStream_t s);
+                               const float* dev_scalars, hipStream_t s, uint16_t* Mfb = nullptr, float mu = 0.0f);
+// Largest row count of an indexed rectangular product (its row table sits in LDS).
+constexpr int kMaxIndexedRows = 8192;
 // s[b] = 1 / (sqrt(sum_i sumsq[b][S[b][i]]) + eps): the Frobenius scale of the rows S.
 hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int batch, int k, int N, float eps,
                                  float* s_out, hipStream_t s);

@@ -193,6 +193,14 @@ def test_dion3_step_full_size(gns_mod, dion3_full, f, norm):
     announce(f"dion3 8192x28672 f={f}: selected W rows against the oracle's update")
     w_ref_sel = weight_update(w[S_ref], np.arange(k), bf16_to_f64(f64_to_bf16_rne(O_ref)), lr, 0.0)
     assert w_within_bound(wg[S_ref], w_ref_sel, lr, O_ref)
+    if f == 0.25 and norm == 2:
+        announce("dion3 8192x28672 f=0.25: the same step with the rows read in place")
+        W2, M2, G2 = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+        S2, O2 = gns_mod.dion3_step(W2, M2, G2, k, lr, weight_decay=0.0, mu=0.95, score_norm=norm, return_O=True,
+                                    schedule=gns_mod.default_schedule(rows_in_place=True))
+        assert np.array_equal(S2.cpu().numpy(), S_ref)
+        assert np.array_equal(bits(O2), bits(O)) and np.array_equal(bits(W2), wg)
+        assert np.array_equal(bits(M2), bits(M))
 
 
 @pytest.mark.parametrize("N,m,f,norm,wd", [(1000, 2048, 0.125, 2, 0.0), (1000, 2048, 0.125, 1, 0.1),
@@ -494,3 +502,62 @@ def test_dion3_step_smallest_k(gns_mod, k):
     assert np.array_equal(bits(M), m_ref)
     assert rel_fro(to_f64(O), O_ref) <= 2e-2
     assert w_within_bound(bits(W), w_ref, 0.02, O_ref)
+
+
+# ---- the selected rows read in place (no gathered copy of M[S, :]) ----
+
+def _step_bits(gns_mod, w, g, m, k, lr, wd, norm, compute, in_place, batched=False, S_rows=None, dev=False):
+    import torch
+    sched = gns_mod.default_schedule(rows_in_place=in_place)
+    if batched:
+        stack = lambda a: torch.stack([to_dev(x, "bf16") for x in a])
+        W, M, G = stack(w), stack(m), stack(g)
+        S, O = gns_mod.dion3_step_batched(W, M, G, k, lr, weight_decay=wd, mu=0.95, score_norm=norm,
+                                          compute=compute, schedule=sched, return_O=True)
+    else:
+        W, M, G = to_dev(w, "bf16"), to_dev(m, "bf16"), to_dev(g, "bf16")
+        if S_rows is not None:
+            O = gns_mod.dion3_step_rows(W, M, G, _rows_tensor(S_rows), lr, weight_decay=wd, mu=0.95, compute=compute,
+                                        schedule=sched, O=_bf16_empty(len(S_rows), w.shape[1]))
+            S = _rows_tensor(S_rows)
+        elif dev:
+            sc = torch.tensor([lr, wd, 0.95], dtype=torch.float32, device="cuda")
+            S, O = gns_mod.dion3_step_dev_scalars(W, M, G, k, sc, score_norm=norm, compute=compute, schedule=sched,
+                                                  O=_bf16_empty(k, w.shape[1]))
+        else:
+            S, O = gns_mod.dion3_step(W, M, G, k, lr, weight_decay=wd, mu=0.95, score_norm=norm, compute=compute,
+                                      schedule=sched, return_O=True)
+    torch.cuda.synchronize()
+    return S.cpu().numpy(), bits(O), bits(W), bits(M)
+
+
+@pytest.mark.parametrize("case", ["small_wd", "k125_bf16", "long_k_split", "batched", "caller_rows", "dev_scalars"])
+def test_dion3_rows_in_place_bitwise_equal(gns_mod, case):
+    """rows_in_place = 1 (the Gram products read M[S, :] through the row list, the
+    error feedback runs with the update) gives bitwise the step of the default path
+    (rows gathered into a copy first): S, O, W and M."""
+    announce(f"dion3 rows in place: {case}")
+    kw = dict(k=128, lr=0.02, wd=0.1, norm=2, compute="f16")
+    if case == "small_wd":
+        w, g, m = synth.dion3_state(n=512, m=2048, seed=90)
+    elif case == "k125_bf16":
+        w, g, m = synth.dion3_state(n=1000, m=2048, seed=91)
+        kw.update(k=125, wd=0.0, norm=1, compute="bf16")
+    elif case == "long_k_split":
+        w, g, m = synth.dion3_state(n=1024, m=16384, seed=92)
+        kw.update(k=1024)
+    elif case == "batched":
+        sts = [synth.dion3_state(n=512, m=2048, seed=93 + b) for b in range(2)]
+        w, g, m = ([st[i] for st in sts] for i in range(3))
+    elif case == "caller_rows":
+        w, g, m = synth.dion3_state(n=256, m=1024, seed=95)
+        rows = np.append(np.sort(np.random.default_rng(96).choice(256, size=23, replace=False)), 256)
+        kw.update(k=24, S_rows=rows)
+    else:
+        w, g, m = synth.dion3_state(n=512, m=2048, seed=97)
+        kw.update(dev=True)
+    extra = {x: kw.pop(x) for x in ("S_rows", "dev") if x in kw}
+    a = _step_bits(gns_mod, w, g, m, batched=case == "batched", in_place=False, **kw, **extra)
+    b = _step_bits(gns_mod, w, g, m, batched=case == "batched", in_place=True, **kw, **extra)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)

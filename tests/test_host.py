@@ -78,6 +78,10 @@ def test_validation_rejects_before_launch():
     bad = gns.default_schedule()
     bad.steps = 0
     assert ortho(sched=bad) == INVALID
+    for field in ("square_fallback", "rows_in_place"):   # flags are 0 or 1
+        bad = gns.default_schedule()
+        setattr(bad, field, 2)
+        assert ortho(sched=bad) == INVALID
     assert ortho(fn="gns_newton_schulz_batched", n=512, m=256, ldx=128) == INVALID
     assert ortho(B=0) == OK                                # empty batch: nothing to do
 
