@@ -12,8 +12,7 @@ import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# GNS_LIBRARY may name another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("GNS_LIBRARY") or os.path.join(HERE, "libgns.so")
+LIB_PATH = os.path.join(HERE, "libgns.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "gns.h")
 
 if not os.path.exists(LIB_PATH):

@@ -23,10 +23,6 @@
 #include "common.h"
 #include "internal.h"
 
-// Ping-pong schedule of the 8-wave tiles (see gemm16_kernel); 0 selects the plain loop.
-#ifndef GNS_PP
-#define GNS_PP 1
-#endif
 
 namespace gns {
 
@@ -1065,7 +1061,7 @@ gemm16_kernel(GemmParams p) {
   // (all MFMAs of one stage from registers) and a memory phase (all fragment reads of
   // the next stage, plus this wave's share of the direct loads of a later stage), so
   // each SIMD's MFMA pipe is fed by one wave while the other reads LDS.
-  constexpr bool kPingPong = GNS_PP && NW == 8 && WAVES_M == 2 && NS >= 3;
+  constexpr bool kPingPong = NW == 8 && WAVES_M == 2 && NS >= 3;
   if constexpr (kPingPong) {
     // Phases are separated by workgroup barriers.  Group 1 reads stage i in phase 2i
     // and multiplies it in phase 2i+1; group 0 runs one phase behind (reads in 2i+1,
@@ -1246,28 +1242,9 @@ gemm16_kernel(GemmParams p) {
 // products of a 128-matrix batch; with 8 waves, 3, 4 and 5 stages of 32 and 2
 // stages of 64 run within 3% of each other, and 8 or 16 stages of the small tiles
 // are slower than 4.
-#ifndef GNS_BIG_WM
-#define GNS_BIG_WM 2
-#define GNS_BIG_WN 4
-#endif
-#ifndef GNS_BK_BIG
-#define GNS_BK_BIG 32
-#endif
-#ifndef GNS_STAGES_BIG
-#define GNS_STAGES_BIG 4
-#endif
-#ifndef GNS_BK_MID
-#define GNS_BK_MID 64
-#endif
-#ifndef GNS_STAGES_MID
-#define GNS_STAGES_MID 4
-#endif
-#ifndef GNS_BK_SMALL
-#define GNS_BK_SMALL 64
-#endif
-#ifndef GNS_STAGES_SMALL
-#define GNS_STAGES_SMALL 4
-#endif
+constexpr int kBigWM = 2, kBigWN = 4, kBkBig = 32, kStagesBig = 4;
+constexpr int kBkMid = 64, kStagesMid = 4;
+constexpr int kBkSmall = 64, kStagesSmall = 4;
 enum class TileCfg { kBig = 0, kMid = 1, kSmall = 2 };
 
 inline long long gemm_tiles(int M, int N, int bm, int bn, bool lower) {
@@ -1428,14 +1405,10 @@ hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops
 
 template <class TIn, class TB, class TOut, bool LOWER, bool NN>
 hipError_t launch_cfg(GemmParams p, int batch, hipStream_t stream, double* flops) {
-#ifdef GNS_FORCE_TILE
-  const TileCfg cfg = static_cast<TileCfg>(GNS_FORCE_TILE);
-#else
   const TileCfg cfg = pick_tile(p.M, p.N, p.K, p.pair ? 2 * batch : batch, LOWER);
-#endif
   switch (cfg) {
     case TileCfg::kBig:
-      return launch_one<TIn, TB, TOut, 256, 256, GNS_BIG_WM, GNS_BIG_WN, GNS_STAGES_BIG, GNS_BK_BIG, LOWER, NN>(
+      return launch_one<TIn, TB, TOut, 256, 256, kBigWM, kBigWN, kStagesBig, kBkBig, LOWER, NN>(
           p, batch, stream, flops);
     case TileCfg::kMid:
       // A B operand converted on load (bf16 -> fp16) is converted by every wave that
@@ -1444,13 +1417,13 @@ hipError_t launch_cfg(GemmParams p, int batch, hipStream_t stream, double* flops
       // 1024 x 4096 restart product: 19.0 against 20.4 us; with an fp16 B operand the
       // 2 x 2 layout is faster (17.3 against 18.3 us).
       if constexpr (NN && TIn::kId != TB::kId)
-        return launch_one<TIn, TB, TOut, 128, 128, 1, 4, GNS_STAGES_MID, GNS_BK_MID, LOWER, NN>(p, batch, stream,
+        return launch_one<TIn, TB, TOut, 128, 128, 1, 4, kStagesMid, kBkMid, LOWER, NN>(p, batch, stream,
                                                                                              flops);
       else
-        return launch_one<TIn, TB, TOut, 128, 128, 2, 2, GNS_STAGES_MID, GNS_BK_MID, LOWER, NN>(p, batch, stream,
+        return launch_one<TIn, TB, TOut, 128, 128, 2, 2, kStagesMid, kBkMid, LOWER, NN>(p, batch, stream,
                                                                                              flops);
     case TileCfg::kSmall:
-      return launch_one<TIn, TB, TOut, 64, 64, 2, 2, GNS_STAGES_SMALL, GNS_BK_SMALL, LOWER, NN>(p, batch, stream, flops);
+      return launch_one<TIn, TB, TOut, 64, 64, 2, 2, kStagesSmall, kBkSmall, LOWER, NN>(p, batch, stream, flops);
   }
   return hipErrorInvalidValue;
 }
@@ -1475,12 +1448,12 @@ inline SymmSplit symm_split_plan(int n, int K) {
   SymmSplit r;
   if (K < kSplitMinK) return r;
   long long tiles = gemm_tiles(n, n, 256, 256, true);
-  int bk = GNS_BK_BIG;
+  int bk = kBkBig;
   if (tiles < kSplitMinTiles) {
     tiles = gemm_tiles(n, n, 128, 128, true);
     if (tiles < kSplitMinTiles) return r;
     r.tile = 128;
-    bk = GNS_BK_MID;
+    bk = kBkMid;
   }
   const long long S = std::min<long long>(std::min<long long>(256 / tiles, 8), K / kSplitMinChunk);
   if (S < 2) return SymmSplit{};
@@ -1509,8 +1482,8 @@ hipError_t launch_symm_split_cfg(GemmParams p, int batch, float* part, hipStream
 template <class TIn, class TOut>
 hipError_t launch_symm_split(GemmParams p, int batch, float* part, int tile, hipStream_t stream, double* flops) {
   if (tile == 128)
-    return launch_symm_split_cfg<TIn, TOut, 128, 2, 2, GNS_STAGES_MID, GNS_BK_MID>(p, batch, part, stream, flops);
-  return launch_symm_split_cfg<TIn, TOut, 256, GNS_BIG_WM, GNS_BIG_WN, GNS_STAGES_BIG, GNS_BK_BIG>(p, batch, part,
+    return launch_symm_split_cfg<TIn, TOut, 128, 2, 2, kStagesMid, kBkMid>(p, batch, part, stream, flops);
+  return launch_symm_split_cfg<TIn, TOut, 256, kBigWM, kBigWN, kStagesBig, kBkBig>(p, batch, part,
                                                                                                  stream, flops);
 }
 

@@ -245,12 +245,20 @@ def test_binding_rejects_mismatched_tensors_before_any_call():
 def test_missing_library_fails_loudly():
     """Without the built HIP library the package does not import: there is no CPU
     fallback to fall back on."""
+    import glob
+    import shutil
     import subprocess
     import sys
+    import tempfile
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    env = dict(os.environ, GNS_LIBRARY=os.path.join(root, "no_such_dir", "libgns.so"))
-    r = subprocess.run([sys.executable, "-c", "import muon_gram_ns_amd"], env=env, cwd=root, capture_output=True,
-                       text=True, timeout=300)
+    with tempfile.TemporaryDirectory() as tmp:
+        pkg = os.path.join(tmp, "muon_gram_ns_amd")          # the package's Python files, no libgns.so
+        os.makedirs(pkg)
+        for f in glob.glob(os.path.join(root, "muon_gram_ns_amd", "*.py")):
+            shutil.copy(f, pkg)
+        env = dict(os.environ, PYTHONPATH=tmp)
+        r = subprocess.run([sys.executable, "-c", "import muon_gram_ns_amd"], env=env, cwd=tmp, capture_output=True,
+                           text=True, timeout=300)
     assert r.returncode != 0
     assert "is missing" in r.stderr
 
