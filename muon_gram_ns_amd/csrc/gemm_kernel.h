@@ -697,9 +697,39 @@ __device__ __forceinline__ void store_vec_nt(uint8_t* base, long long ld, int ro
 // at their transposed positions.  Both triangles round the same fp32 value, so the
 // output is bitwise symmetric.  Only the slab writes index the accumulators, so
 // they stay in registers.
-template <class TOut, bool LOWER, int FM, int FN, bool NT = false, bool PL = false>
+// The C vectors one lane adds in the row pass of one 32-row fragment row of a wave
+// tile FN * 32 columns wide (both planes of a hi/lo pair), as whole 16-byte vectors.
+template <class TOut, int FN, bool PL>
+struct CRow {
+  static constexpr int VE = 16 / TOut::kBytes;                 // elements per vector
+  static constexpr int RV = FN * 32 / VE;                      // vectors per row
+  static constexpr int IT = (32 * RV + 63) / 64;               // vectors per lane
+  static constexpr int CPL = PL ? 2 : 1;
+  uint4 v[IT][CPL];
+};
+
+// Load the C vectors of fragment row r0 (wave column nw).  A vector outside the matrix
+// loads C's first vector instead, so every lane issues the same loads with no branch
+// around them, and they all stay in flight together.
+template <class TOut, int FN, bool PL>
+__device__ __forceinline__ void load_c_row(const GemmParams& p, const EpiPtrs& ep, int r0, int nw, int lane,
+                                           CRow<TOut, FN, PL>& cb) {
+  using CR = CRow<TOut, FN, PL>;
+#pragma unroll
+  for (int it = 0; it < CR::IT; ++it) {
+    const int t = lane + 64 * it;
+    const int gm = r0 + t / CR::RV, gn = nw + (t % CR::RV) * CR::VE;
+    const bool in = t < 32 * CR::RV && gm < p.M && gn < p.N;
+    const uint8_t* cp = ep.C + (in ? ((long long)gm * p.ldc + gn) * TOut::kBytes : 0);
+    cb.v[it][0] = *reinterpret_cast<const uint4*>(cp);
+    if constexpr (PL) cb.v[it][1] = *reinterpret_cast<const uint4*>(cp + (ep.c_planes == 2 ? p.plane * TOut::kBytes : 0));
+  }
+}
+
+// EARLY: the caller loaded C's first fragment row into c0 before its k-loop.
+template <class TOut, bool LOWER, int FM, int FN, bool NT = false, bool PL = false, bool EARLY = false>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc)[FM][FN], const GridPos& gp,
-                                             int mw, int nw, int lane, float* slab) {
+                                             int mw, int nw, int lane, float* slab, const CRow<TOut, FN, PL>& c0) {
   const int bz = gp.bz;
   constexpr int WN = FN * 32;
   constexpr int S = WN + 4;
@@ -710,9 +740,19 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc
   const bool has_c = ep.C != nullptr && p.beta != 0.0f;
   const int M = p.M, N = p.N;
   const int c_pl = PL ? ep.c_planes : 1, d_pl = PL ? ep.d_planes : 1;   // hi/lo planes (PL kernels only)
+  // The C vectors of a fragment row are all loaded one fragment row ahead of the row
+  // pass that adds them (the first row before the k-loop, or here), so their latency
+  // overlaps the staging and stores of the row before instead of being paid once per
+  // vector.
+  using CR = CRow<TOut, FN, PL>;
+  constexpr int IT = CR::IT, CPL = CR::CPL;
+  CR cbuf[2];
+  if constexpr (EARLY) cbuf[0] = c0;
+  else if (has_c) load_c_row<TOut, FN, PL>(p, ep, mw, nw, lane, cbuf[0]);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int r0 = mw + 32 * i;
+    if (has_c && i + 1 < FM) load_c_row<TOut, FN, PL>(p, ep, r0 + 32, nw, lane, cbuf[(i + 1) & 1]);
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -722,10 +762,12 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
     // row pass
-    for (int t = lane; t < 32 * RV; t += 64) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int t = lane + 64 * it;
       const int r = t / RV, c = (t % RV) * VE;
       const int gm = r0 + r, gn = nw + c;
-      if (gm >= M || gn >= N) continue;          // N % 8 == 0: a vector is all in or all out
+      if (t >= 32 * RV || gm >= M || gn >= N) continue;   // N % 8 == 0: a vector is all in or all out
       float* sp = slab + r * S + c;
       float v[VE];
 #pragma unroll
@@ -735,13 +777,14 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc
       }
       if (has_c) {
         float cv[VE];
-        const uint8_t* cp = ep.C + ((long long)gm * p.ldc + gn) * TOut::kBytes;
-        unpack16<TOut>(*reinterpret_cast<const uint4*>(cp), cv);
-        if (c_pl == 2) {      // C = hi + lo
-          float cl[VE];
-          unpack16<TOut>(*reinterpret_cast<const uint4*>(cp + p.plane * TOut::kBytes), cl);
+        unpack16<TOut>(cbuf[i & 1].v[it][0], cv);
+        if constexpr (PL) {
+          if (c_pl == 2) {      // C = hi + lo
+            float cl[VE];
+            unpack16<TOut>(cbuf[i & 1].v[it][CPL - 1], cl);
 #pragma unroll
-          for (int e = 0; e < VE; ++e) cv[e] += cl[e];
+            for (int e = 0; e < VE; ++e) cv[e] += cl[e];
+          }
         }
 #pragma unroll
         for (int e = 0; e < VE; ++e) v[e] += p.beta * cv[e];
@@ -771,10 +814,12 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc
     if constexpr (LOWER) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       // mirror pass: output row gn = nw + c, columns gm0 .. gm0+VE-1 from slab column c
-      for (int t = lane; t < WN * MV; t += 64) {
+#pragma unroll
+      for (int it = 0; it < (WN * MV + 63) / 64; ++it) {
+        const int t = lane + 64 * it;
         const int c = t / MV, rr = (t % MV) * VE;
         const int gn = nw + c, gm0 = r0 + rr;
-        if (gn >= N || gm0 >= M) continue;       // M % 8 == 0 and gm0 % VE == 0
+        if (t >= WN * MV || gn >= N || gm0 >= M) continue;   // M % 8 == 0 and gm0 % VE == 0
         const int lo = gn + 1 - gm0;             // strictly lower sources: gm0 + e > gn
         if (lo > VE - 1) continue;
         float v[VE];
@@ -1018,6 +1063,18 @@ gemm16_kernel(GemmParams p) {
   // this wave's loads, which complete in issue order)
   auto wait_for_stage = [&](int next, int last) { wait_vm_stages<NS - 1, LOADS>(last - next); };
 
+  // Wave tiles of one fragment row: the C vectors of the epilogue are loaded here,
+  // before any operand load, so their latency hides behind the k-loop.  The ring's
+  // vmcnt waits stay exact: these loads are older than every ring load, and a wave's
+  // loads complete in issue order.
+  constexpr bool kEarlyC = FM == 1;
+  CRow<TOut, FN, PL> c_early;
+  if constexpr (kEarlyC) {
+    const EpiPtrs ep0 = epi_ptrs<TOut>(p, bz, gp.second, gp.psc);
+    if (!split_part && ep0.C != nullptr && p.beta != 0.0f)
+      load_c_row<TOut, FN, PL>(p, ep0, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane, c_early);
+  }
+
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -1224,7 +1281,8 @@ gemm16_kernel(GemmParams p) {
   static_assert(NW * 32 * (Cfg::kWN + 4) * 4 <= Cfg::kLdsBytes, "epilogue slabs exceed the LDS ring");
   lds_barrier();
   float* slab = reinterpret_cast<float*>(smem16) + wave * 32 * (Cfg::kWN + 4);
-  epilogue_lds<TOut, LOWER, FM, FN, NT, PL>(p, acc, gp, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane, slab);
+  epilogue_lds<TOut, LOWER, FM, FN, NT, PL, kEarlyC>(p, acc, gp, m0 + wm * Cfg::kWM, n0 + wn * Cfg::kWN, lane, slab,
+                                                     c_early);
 }
 
 // ---------------------------------------------------------------------------------
