@@ -214,3 +214,125 @@ def test_dion3_step_cols_selects_columns_by_norm_and_keeps_invariants(norm):
     o_b = tbf(f64_to_bf16_rne(O.T)).float()
     ref_w = (tbf(w[:, S]).float() - torch.tensor(np.float32(0.02)) * o_b).to(torch.bfloat16)
     assert np.array_equal(w2[:, S], bits_of(ref_w))
+
+
+# ---- the same element-wise model in the f16 and f32 state formats -----------------
+
+TORCH_OF = {"f16": torch.float16, "f32": torch.float32}
+NP_OF = {"f16": np.float16, "f32": np.float32}
+
+
+def t_of(a, storage):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=NP_OF[storage]))
+
+
+@pytest.mark.parametrize("storage", ["f16", "f32"])
+def test_state_codec_rounds_once_to_nearest_even(storage):
+    """The oracle's encode (float64 -> stored format) against torch's float64 ->
+    float16/float32 conversion, and on hand-built midpoints of neighbouring stored
+    values, which must go to the neighbour with the even significand."""
+    from oracle.dion3 import _codec
+    dec, enc = _codec(storage)
+    rng = np.random.default_rng(11)
+    hi = 15 if storage == "f16" else 120
+    x = rng.standard_normal(20000) * np.exp2(rng.uniform(-hi - 12, hi + 1, 20000))
+    ref = torch.from_numpy(x).to(TORCH_OF[storage]).numpy()
+    got = enc(x)
+    assert got.dtype == NP_OF[storage]
+    assert np.array_equal(got.view(np.uint16 if storage == "f16" else np.uint32),
+                          ref.view(np.uint16 if storage == "f16" else np.uint32))
+    # midpoints between neighbours: a = stored value with an even significand, b its
+    # successor (odd); (a + b) / 2 is exact in float64 and must round back to a
+    ui = np.uint16 if storage == "f16" else np.uint32
+    bits = (rng.integers(1, 0x7000 if storage == "f16" else 0x7e000000, 4000) & ~1).astype(ui)
+    a = dec(bits.view(NP_OF[storage]))
+    b = dec((bits + 1).view(NP_OF[storage]))
+    mid = (a + b) / 2
+    assert np.array_equal(enc(mid).view(ui), bits)
+    assert np.array_equal(enc(-mid).view(ui), bits | ui(0x8000 if storage == "f16" else 0x80000000))
+    # every finite stored value decodes and encodes back to itself
+    if storage == "f16":
+        allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+        v = allb.view(np.float16)
+        fin = np.isfinite(v)
+        assert np.array_equal(enc(dec(v[fin])).view(np.uint16), allb[fin])
+
+
+@pytest.mark.parametrize("storage", ["f16", "f32"])
+def test_accumulate_matches_torch_add(storage):
+    rng = np.random.default_rng(21)
+    m = synth.to_storage(rng.standard_normal((64, 300)) * 0.02, storage)
+    g = synth.to_storage(rng.standard_normal((64, 300)) * np.exp(rng.uniform(-12, 3, (64, 300))), storage)
+    ref = (t_of(m, storage) + t_of(g, storage)).numpy()     # torch: one rounding to the format
+    assert np.array_equal(accumulate(m, g, storage).view(np.uint8), ref.view(np.uint8))
+
+
+@pytest.mark.parametrize("storage", ["f16", "f32"])
+def test_row_scores_state_formats(storage):
+    small = synth.to_storage(np.array([[1.0, -2.0, 0.5], [0.0, 0.0, -3.0]]), storage)
+    assert list(row_scores(small, "l1", storage)) == [3.5, 3.0]
+    assert list(row_scores(small, "l2", storage)) == [5.25, 9.0]
+    rng = np.random.default_rng(22)
+    m = synth.to_storage(rng.standard_normal((16, 700)) * 0.02, storage)
+    x = t_of(m, storage).double()
+    assert np.allclose(row_scores(m, "l1", storage), x.abs().sum(1).numpy(), rtol=1e-13, atol=0)
+    assert np.allclose(row_scores(m, "l2", storage), (x * x).sum(1).numpy(), rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("storage", ["f16", "f32"])
+def test_error_feedback_matches_torch_state_formats(storage):
+    rng = np.random.default_rng(23)
+    m = synth.to_storage(rng.standard_normal((40, 256)) * 0.02, storage)
+    S = np.array([0, 3, 7, 39])
+    out = error_feedback(m, S, 0.95, storage)
+    ref = t_of(m, storage).clone()
+    ref[S] = (torch.tensor(0.95, dtype=torch.float32) * t_of(m, storage)[S].float()).to(TORCH_OF[storage])
+    assert np.array_equal(out.view(np.uint8), ref.numpy().view(np.uint8))
+    rest = np.setdiff1d(np.arange(40), S)
+    assert np.array_equal(out[rest].view(np.uint8), m[rest].view(np.uint8))
+
+
+@pytest.mark.parametrize("storage", ["f16", "f32"])
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_weight_update_matches_torch_state_formats(storage, wd):
+    rng = np.random.default_rng(24)
+    w = synth.to_storage(rng.standard_normal((30, 128)) * 0.02, storage)
+    S = np.array([1, 2, 10, 29])
+    o = synth.to_storage(rng.standard_normal((4, 128)) * 0.1, storage).astype(np.float64)
+    lr = 0.02
+    out = weight_update(w, S, o, lr, wd, storage)
+    f = torch.float32
+    lr_t, wd_t = torch.tensor(lr, dtype=f), torch.tensor(wd, dtype=f)
+    d = torch.tensor(1.0, dtype=f) - lr_t * wd_t
+    wt = t_of(w, storage).float()
+    ref = (d * wt).to(TORCH_OF[storage]) if wd else t_of(w, storage).clone()
+    upd = d * wt[S] - lr_t * torch.from_numpy(o).to(f)
+    ref[S] = upd.to(TORCH_OF[storage])
+    assert np.array_equal(out.view(np.uint8), ref.numpy().view(np.uint8))
+
+
+@pytest.mark.parametrize("storage", ["f16", "f32"])
+def test_dion3_step_state_formats_invariants(storage):
+    """The error-feedback invariants of Algorithm 4 in the f16 and f32 formats, and the
+    f32 step within fp32 rounding of the unrounded (float64) step on the same state."""
+    rng = np.random.default_rng(25)
+    n, mm = 48, 256
+    w = synth.to_storage(rng.standard_normal((n, mm)) * 0.02, storage)
+    m = synth.to_storage(rng.standard_normal((n, mm)) * 0.02, storage)
+    g = synth.to_storage(rng.standard_normal((n, mm)) * 0.02, storage)
+    k = k_from_fraction(0.25, n)
+    w2, m2, S, O = dion3_step(w, m, g, k, lr=0.02, wd=0.0, mu=0.95, storage=storage)
+    m1 = accumulate(m, g, storage)
+    rest = np.setdiff1d(np.arange(n), S)
+    assert m2.dtype == NP_OF[storage] and w2.dtype == NP_OF[storage]
+    assert np.array_equal(m2[rest].view(np.uint8), m1[rest].view(np.uint8))
+    assert np.array_equal(w2[rest].view(np.uint8), w[rest].view(np.uint8))
+    sc = np.abs(m1.astype(np.float64)).sum(1)
+    assert sc[S].min() >= sc[rest].max()
+    assert np.allclose(O, newton_schulz(m1[S].astype(np.float64)), rtol=0, atol=1e-15)
+    if storage == "f32":
+        w64, m64, S64, O64 = dion3_step(w.astype(np.float64), m.astype(np.float64), g.astype(np.float64), k,
+                                        lr=0.02, wd=0.0, mu=0.95, storage="f64")
+        assert np.array_equal(S, S64)
+        assert np.allclose(w2, w64, rtol=2e-7, atol=1e-9)
+        assert np.allclose(m2, m64, rtol=2e-7, atol=1e-9)
