@@ -67,8 +67,9 @@ typedef enum { GNS_BF16 = 0, GNS_F32 = 1, GNS_F16 = 2 } gns_dtype;
  * gathered into a contiguous copy.  Both give bitwise the same results.  Measured on
  * MI355X at f = 1/4 on the 8192 x 28672 state, the copy is faster (1.56 against
  * 1.61 ms): written just before the products read it, it sits in the 256 MB Infinity
- * Cache, while the rows in place come from HBM.  The in-place path applies when the
- * submatrix is wide (k <= m, Gram path) with k <= 8192; otherwise the rows are copied.
+ * Cache, while the rows in place come from HBM.  The in-place path applies to a bf16
+ * state whose submatrix is wide (k <= m, Gram path) with k <= 8192; otherwise the rows
+ * are copied.
  * Gram Newton-Schulz: paper.rainbus.top 方法步骤详情 Algorithm 3 (restart at t = 3). */
 typedef struct {
   int steps;
@@ -190,56 +191,63 @@ int rect_gemm(int batch, int n, int k, int m, float alpha,
               hipStream_t stream);
 
 /* ---- Dion3 (row-subsampled update with error feedback) -------------------------
- * W, M, G: N x m bf16 row-major with row stride ld.  S: device int32[k], ascending
- * row indices.  Rounding model: each stored value is rounded once to bf16 (nearest
- * even); element-wise updates are fp32 op by op, no fused multiply-add.
+ * W, M, G: N x m row-major with row stride ld, all of the state type dt (GNS_BF16,
+ * GNS_F16 or GNS_F32; the caller's optimizer state).  m and ld multiples of 8, the
+ * pointers 16-byte aligned (else GNS_ERR_UNSUPPORTED).  S: device int32[k], ascending
+ * row indices.  Rounding model: each stored value is rounded once to dt (nearest even);
+ * element-wise updates are fp32 op by op, no fused multiply-add; the orthogonalised
+ * rows O are stored in dt before the update reads them.  The Gram NS reads the
+ * submatrix in dt (bf16, f16), or, for an fp32 state, a copy scaled by its Frobenius
+ * scale and rounded once to the iterate type (compute), which it normalises again.
  * [paper.rainbus.top 方法步骤详情 (3) Algorithm 4; 前置知识 error feedback] */
 
-/* M <- bf16(M + G); score[i] = sum_j |M_ij| (score_norm 1) or sum_j M_ij^2
+/* M <- fl(M + G); score[i] = sum_j |M_ij| (score_norm 1) or sum_j M_ij^2
  * (score_norm 2) of the updated M, float64 accumulation; sumsq[i] = sum_j M_ij^2
  * (float64; nullable).  score, sumsq: device double[N]. */
-int dion3_accumulate_score(void* M, const void* G, int N, int m, long long ld, int score_norm,
+int dion3_accumulate_score(void* M, const void* G, gns_dtype dt, int N, int m, long long ld, int score_norm,
                            double* score, double* sumsq, hipStream_t stream);
 
 /* S = indices of the k largest scores (ties -> lower index), written ascending.
  * 1 <= k <= N.  One workgroup; no workspace. */
 int dion3_select_topk(const double* score, int N, int k, int* S, hipStream_t stream);
 
-/* X[r, :] = M[S[r], :] (bf16, row stride ldx) and then M[S[r], :] <- bf16(mu * M[S[r], :])
+/* X[r, :] = M[S[r], :] (type dt, row stride ldx) and then M[S[r], :] <- fl(mu * M[S[r], :])
  * (error feedback: only selected rows decay).  An index S[r] outside [0, N) gives a
  * zero row X[r, :] and touches no row of M. */
-int dion3_gather_feedback(void* M, int N, int m, long long ld, const int* S, int k, float mu,
+int dion3_gather_feedback(void* M, gns_dtype dt, int N, int m, long long ld, const int* S, int k, float mu,
                           void* X, long long ldx, hipStream_t stream);
 
-/* d = fl32(1 - fl32(lr * wd)); W[S[r], :] <- bf16(fl32(d * W) - fl32(lr * O[r, :]));
- * when wd != 0 every other row W <- bf16(fl32(d * W)).  O: k x m, o_dtype bf16 or f32.
- * S must be ascending and hold distinct indices in [0, N). */
-int dion3_apply_update(void* W, int N, int m, long long ld, const int* S, int k,
+/* d = fl32(1 - fl32(lr * wd)); W[S[r], :] <- fl(fl32(d * W) - fl32(lr * O[r, :]));
+ * when wd != 0 every other row W <- fl(fl32(d * W)).  W: type dt.  O: k x m of any
+ * o_dtype, row stride ldo (a multiple of 8).  S must be ascending and hold distinct
+ * indices in [0, N). */
+int dion3_apply_update(void* W, gns_dtype dt, int N, int m, long long ld, const int* S, int k,
                        const void* O, gns_dtype o_dtype, long long ldo,
                        float lr, float wd, hipStream_t stream);
 
-/* Workspace bytes needed by dion3_step. */
-size_t dion3_workspace_size(int N, int m, int k, gns_dtype compute);
+/* Workspace bytes needed by dion3_step for a state of type dt (it holds the selected
+ * submatrix and its orthogonalisation in dt); 0 for invalid arguments. */
+size_t dion3_workspace_size(int N, int m, int k, gns_dtype dt, gns_dtype compute);
 
-/* One Dion3 step (in place on W and M):
+/* One Dion3 step (in place on W and M of state type dt):
  *   M <- M + G; S = top-k rows by score (score_norm 1 = l1 as on the pages, 2 = l2);
  *   X = M[S, :]; O = GramNS(X) (sched, compute as in gns_orthogonalize_batched, the
  *   Frobenius norm taken from the per-row sums of squares); W <- decay + row update
  *   with lr (the caller passes lr = eta / sqrt(f)); M[S, :] <- mu M[S, :].
- * S_out: device int32[k] (ascending).  O_out: nullable device bf16 [k][m] (row stride
- * m) receiving O; it must not overlap W, M, G or the workspace.  1 <= k <= N, any k
+ * S_out: device int32[k] (ascending).  O_out: nullable device [k][m] of type dt (row
+ * stride m) receiving O; it must not overlap W, M, G or the workspace.  1 <= k <= N, any k
  * (k = ceil(f N) on the pages): the submatrix is held with k rounded up to a multiple
  * of 8 rows, the extra rows zero, which leaves O's k rows unchanged.  With k > m the
  * k x m submatrix is orthogonalized through its transpose, as in
  * gns_orthogonalize_batched.  Every argument, including those of the
  * Gram NS on the submatrix, is checked before the first launch. */
-int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int k,
+int dion3_step(void* W, void* M, const void* G, gns_dtype dt, int N, int m, long long ld, int k,
                float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
                const gns_schedule* sched, int* S_out, void* O_out,
                void* workspace, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes needed by dion3_step_batched. */
-size_t dion3_batched_workspace_size(int batch, int N, int m, int k, gns_dtype compute);
+/* Workspace bytes needed by dion3_step_batched (state type dt). */
+size_t dion3_batched_workspace_size(int batch, int N, int m, int k, gns_dtype dt, gns_dtype compute);
 
 /* dion3_step on `batch` same-shape N x m states at once (W, M, G: [batch][N][ld], entry
  * b at offset b * stride elements, stride >= N * ld): per entry the same scores, top-k,
@@ -247,12 +255,12 @@ size_t dion3_batched_workspace_size(int batch, int N, int m, int k, gns_dtype co
  * orthogonalized by one batched Gram NS (one launch per step for all entries, the
  * single-GPU form of the pages' megabatching of same-shape parameters)
  * [paper.rainbus.top 方法步骤详情 (3) and (4); m.montaan.com summary].
- * S_out: device int32 [batch][k] (each row ascending).  O_out: nullable device bf16
- * [batch][k][m].  W, M and G must not overlap.  Each entry's result is bitwise the
+ * S_out: device int32 [batch][k] (each row ascending).  O_out: nullable device
+ * [batch][k][m] of type dt.  W, M and G must not overlap.  Each entry's result is bitwise the
  * result of dion3_step on that entry alone: every product's summation order depends
  * on the matrix shape only, never on the batch size (a long-K Gram product that splits
  * K splits the same way in any batch).  Errors as dion3_step. */
-int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m, long long ld,
+int dion3_step_batched(void* W, void* M, const void* G, gns_dtype dt, int batch, int N, int m, long long ld,
                        long long stride, int k, float lr, float weight_decay, float mu,
                        int score_norm, gns_dtype compute, const gns_schedule* sched, int* S_out,
                        void* O_out, void* workspace, size_t ws_bytes, hipStream_t stream);
@@ -267,16 +275,16 @@ int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m,
  * S: device int32[k], distinct indices in [0, N), ascending; the library cannot check
  * this without a host synchronisation.  An index outside [0, N) reads as a zero row of
  * X and updates nothing; repeated or unordered indices give unspecified W and M (no
- * out-of-bounds access).  O_out: nullable device bf16 [k][m].  Workspace:
- * dion3_workspace_size(N, m, k, compute).  1 <= k <= N (any k, as dion3_step); other
+ * out-of-bounds access).  O_out: nullable device [k][m] of type dt.  Workspace:
+ * dion3_workspace_size(N, m, k, dt, compute).  1 <= k <= N (any k, as dion3_step); other
  * errors as dion3_step. */
-int dion3_step_rows(void* W, void* M, const void* G, int N, int m, long long ld, const int* S, int k,
+int dion3_step_rows(void* W, void* M, const void* G, gns_dtype dt, int N, int m, long long ld, const int* S, int k,
                     float lr, float weight_decay, float mu, gns_dtype compute,
                     const gns_schedule* sched, void* O_out, void* workspace, size_t ws_bytes,
                     hipStream_t stream);
 
-/* Workspace bytes needed by dion3_step_cols. */
-size_t dion3_cols_workspace_size(int N, int m, int k, gns_dtype compute);
+/* Workspace bytes needed by dion3_step_cols (state type dt). */
+size_t dion3_cols_workspace_size(int N, int m, int k, gns_dtype dt, gns_dtype compute);
 
 /* One Dion3 step that subsamples columns instead of rows (in place on W and M): the
  * pages let f select rows or columns [paper.rainbus.top 核心方法 and 方法步骤详情 (3);
@@ -288,11 +296,11 @@ size_t dion3_cols_workspace_size(int N, int m, int k, gns_dtype compute);
  * The columns are scored, gathered (into the k x N transpose of the submatrix, with
  * the error feedback applied in place) and updated in the state's own row-major
  * layout.  S_out: device int32[k], ascending column indices.
- * O_out: nullable device bf16 [k][N]: row j is the update of column S[j] (the
+ * O_out: nullable device [k][N] of type dt: row j is the update of column S[j] (the
  * transpose of the orthogonalised N x k submatrix).  1 <= k <= m (any k, padded as in
  * dion3_step), N a multiple of 8; W, M, G must not overlap; other errors as
  * dion3_step. */
-int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld, int k,
+int dion3_step_cols(void* W, void* M, const void* G, gns_dtype dt, int N, int m, long long ld, int k,
                     float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
                     const gns_schedule* sched, int* S_out, void* O_out,
                     void* workspace, size_t ws_bytes, hipStream_t stream);
@@ -306,7 +314,7 @@ int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld,
  * update launch covers all N rows, since the host cannot see whether the weight decay
  * is zero; without decay each unselected row returns at once.  lr_wd_mu must be 4-byte
  * aligned (else GNS_ERR_UNSUPPORTED); other arguments and errors as dion3_step. */
-int dion3_step_dev_scalars(void* W, void* M, const void* G, int N, int m, long long ld, int k,
+int dion3_step_dev_scalars(void* W, void* M, const void* G, gns_dtype dt, int N, int m, long long ld, int k,
                            const float* lr_wd_mu, int score_norm, gns_dtype compute,
                            const gns_schedule* sched, int* S_out, void* O_out,
                            void* workspace, size_t ws_bytes, hipStream_t stream);

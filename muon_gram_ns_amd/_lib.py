@@ -67,18 +67,19 @@ _sig("gns_orthogonalize_batched_noalloc", I, P, I, LL, LL, P, I, LL, LL, I, I, I
 NOALLOC_SCRATCH_BYTES = 64 << 20     # GNS_NOALLOC_SCRATCH_BYTES
 _sig("symm_gemm", I, I, I, I, F, P, LL, LL, P, LL, LL, F, P, LL, LL, F, P, LL, LL, I, I, P)
 _sig("rect_gemm", I, I, I, I, I, F, P, LL, LL, I, P, LL, LL, I, F, F, P, LL, LL, P, LL, LL, I, P)
-_sig("dion3_accumulate_score", I, P, P, I, I, LL, I, P, P, P)
+_sig("dion3_accumulate_score", I, P, P, I, I, I, LL, I, P, P, P)
 _sig("dion3_select_topk", I, P, I, I, P, P)
-_sig("dion3_gather_feedback", I, P, I, I, LL, P, I, F, P, LL, P)
-_sig("dion3_apply_update", I, P, I, I, LL, P, I, P, I, LL, F, F, P)
-_sig("dion3_workspace_size", SZ, I, I, I, I)
-_sig("dion3_step", I, P, P, P, I, I, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
-_sig("dion3_batched_workspace_size", SZ, I, I, I, I, I)
-_sig("dion3_step_batched", I, P, P, P, I, I, I, LL, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
-_sig("dion3_step_rows", I, P, P, P, I, I, LL, P, I, F, F, F, I, ctypes.POINTER(Schedule), P, P, SZ, P)
-_sig("dion3_step_dev_scalars", I, P, P, P, I, I, LL, I, P, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
-_sig("dion3_cols_workspace_size", SZ, I, I, I, I)
-_sig("dion3_step_cols", I, P, P, P, I, I, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
+_sig("dion3_gather_feedback", I, P, I, I, I, LL, P, I, F, P, LL, P)
+_sig("dion3_apply_update", I, P, I, I, I, LL, P, I, P, I, LL, F, F, P)
+_sig("dion3_workspace_size", SZ, I, I, I, I, I)
+_sig("dion3_step", I, P, P, P, I, I, I, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
+_sig("dion3_batched_workspace_size", SZ, I, I, I, I, I, I)
+_sig("dion3_step_batched", I, P, P, P, I, I, I, I, LL, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ,
+     P)
+_sig("dion3_step_rows", I, P, P, P, I, I, I, LL, P, I, F, F, F, I, ctypes.POINTER(Schedule), P, P, SZ, P)
+_sig("dion3_step_dev_scalars", I, P, P, P, I, I, I, LL, I, P, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
+_sig("dion3_cols_workspace_size", SZ, I, I, I, I, I)
+_sig("dion3_step_cols", I, P, P, P, I, I, I, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
 _sig("muon_workspace_size", SZ, I, I, I, I, I)
 _sig("muon_step_batched", I, P, P, P, I, I, I, LL, LL, F, F, F, I, F, I, ctypes.POINTER(Schedule), P, P, SZ, P)
 
@@ -362,6 +363,25 @@ def _bf16_rows(x, name):
     return _rows(x)
 
 
+def _state_rows(x, name):
+    """[N, m] rows of a Dion3 state tensor (bf16, fp16 or fp32) -> (N, m, ld, dtype code)."""
+    torch = _torch()
+    _dev(x)
+    if x.dtype not in (torch.bfloat16, torch.float16, torch.float32):
+        raise ValueError(f"{name} must be bf16, fp16 or fp32")
+    return (*_rows(x), dtype_code(x))
+
+
+def _same_state(W, M, G):
+    """W, M and G of one Dion3 state: same dtype, shape, device and row stride."""
+    N, m, ld, dt = _state_rows(W, "W")
+    for t, name in ((M, "M"), (G, "G")):
+        _expect(t, name, dtype=W.dtype, shape=W.shape, device=W.device)
+        if _rows(t)[2] != ld:
+            raise ValueError("W, M, G must share the row stride")
+    return N, m, ld, dt
+
+
 def _index_vector(S, k_max, device):
     torch = _torch()
     _expect(S, "S", dtype=torch.int32, device=device)
@@ -372,13 +392,13 @@ def _index_vector(S, k_max, device):
 
 def dion3_accumulate_score(M, G, score_norm=1):
     torch = _torch()
-    N, m, ld = _bf16_rows(M, "M")
-    _expect(G, "G", dtype=torch.bfloat16, shape=M.shape, device=M.device)
+    N, m, ld, dt = _state_rows(M, "M")
+    _expect(G, "G", dtype=M.dtype, shape=M.shape, device=M.device)
     if _rows(G)[2] != ld:
         raise ValueError("M and G must share the row stride")
     score = torch.empty(N, dtype=torch.float64, device=M.device)
     sumsq = torch.empty(N, dtype=torch.float64, device=M.device)
-    check(lib.dion3_accumulate_score(M.data_ptr(), G.data_ptr(), N, m, ld, score_norm, score.data_ptr(),
+    check(lib.dion3_accumulate_score(M.data_ptr(), G.data_ptr(), dt, N, m, ld, score_norm, score.data_ptr(),
                                      sumsq.data_ptr(), _stream(M.device)), "dion3_accumulate_score")
     return score, sumsq
 
@@ -396,53 +416,49 @@ def dion3_select_topk(score, k):
 
 def dion3_gather_feedback(M, S, mu):
     torch = _torch()
-    N, m, ld = _bf16_rows(M, "M")
+    N, m, ld, dt = _state_rows(M, "M")
     k = _index_vector(S, N, M.device)
     X = torch.empty((k, m), dtype=M.dtype, device=M.device)
-    check(lib.dion3_gather_feedback(M.data_ptr(), N, m, ld, S.data_ptr(), k, mu, X.data_ptr(), m,
+    check(lib.dion3_gather_feedback(M.data_ptr(), dt, N, m, ld, S.data_ptr(), k, mu, X.data_ptr(), m,
                                     _stream(M.device)), "dion3_gather_feedback")
     return X
 
 
 def dion3_apply_update(W, S, O, lr, wd):
     torch = _torch()
-    N, m, ld = _bf16_rows(W, "W")
+    N, m, ld, dt = _state_rows(W, "W")
     k = _index_vector(S, N, W.device)
     _expect(O, "O", device=W.device)
-    if O.dtype not in (torch.bfloat16, torch.float32) or O.dim() != 2 or O.shape[0] != k or O.shape[1] != m \
-            or O.stride(1) != 1:
-        raise ValueError("O must be a [k, m] bf16 or fp32 tensor with contiguous rows")
-    check(lib.dion3_apply_update(W.data_ptr(), N, m, ld, S.data_ptr(), k, O.data_ptr(), dtype_code(O),
+    if O.dtype not in (torch.bfloat16, torch.float16, torch.float32) or O.dim() != 2 or O.shape[0] != k \
+            or O.shape[1] != m or O.stride(1) != 1:
+        raise ValueError("O must be a [k, m] bf16, fp16 or fp32 tensor with contiguous rows")
+    check(lib.dion3_apply_update(W.data_ptr(), dt, N, m, ld, S.data_ptr(), k, O.data_ptr(), dtype_code(O),
                                  O.stride(0), lr, wd, _stream(W.device)), "dion3_apply_update")
     return W
 
 
 def dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute="f16", schedule=None,
                return_O=False, S=None, O=None, workspace=None):
-    """One Dion3 step in place on W and M; returns S (and O when return_O).  S ([k]
-    int32), O ([k, m] bf16) and workspace may be given (fixed buffers for graph
-    replay)."""
+    """One Dion3 step in place on W and M (bf16, fp16 or fp32, one dtype for W, M, G);
+    returns S (and O when return_O).  S ([k] int32), O ([k, m], the state's dtype) and
+    workspace may be given (fixed buffers for graph replay)."""
     torch = _torch()
-    N, m, ld = _bf16_rows(W, "W")
-    _expect(M, "M", dtype=torch.bfloat16, shape=W.shape, device=W.device)
-    _expect(G, "G", dtype=torch.bfloat16, shape=W.shape, device=W.device)
-    if _rows(M)[2] != ld or _rows(G)[2] != ld:
-        raise ValueError("W, M, G must share the row stride")
+    N, m, ld, dt = _same_state(W, M, G)
     cdt = code_of(compute)
     if S is None:
         S = torch.empty(k, dtype=torch.int32, device=W.device)
     _expect(S, "S", dtype=torch.int32, shape=(k,), device=W.device)
     if return_O and O is None:
-        O = torch.empty((k, m), dtype=torch.bfloat16, device=W.device)
+        O = torch.empty((k, m), dtype=W.dtype, device=W.device)
     if O is not None:
-        _expect(O, "O", dtype=torch.bfloat16, shape=(k, m), device=W.device)
+        _expect(O, "O", dtype=W.dtype, shape=(k, m), device=W.device)
         if not O.is_contiguous():
             raise ValueError("O must be contiguous")
     if not S.is_contiguous():
         raise ValueError("S must be contiguous")
     sched = schedule if schedule is not None else default_schedule()
-    ws = _workspace_arg(workspace, lib.dion3_workspace_size(N, m, k, cdt), W.device)
-    check(lib.dion3_step(W.data_ptr(), M.data_ptr(), G.data_ptr(), N, m, ld, k, lr, weight_decay, mu,
+    ws = _workspace_arg(workspace, lib.dion3_workspace_size(N, m, k, dt, cdt), W.device)
+    check(lib.dion3_step(W.data_ptr(), M.data_ptr(), G.data_ptr(), dt, N, m, ld, k, lr, weight_decay, mu,
                          score_norm, cdt, ctypes.byref(sched), S.data_ptr(),
                          O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
                          _stream(W.device)), "dion3_step")
@@ -451,30 +467,27 @@ def dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute=
 
 def dion3_step_cols(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute="f16", schedule=None,
                     return_O=False, S=None, O=None, workspace=None):
-    """One Dion3 step on the k columns of largest score of the [N, m] bf16 state (in
-    place on W and M).  Returns S ([k] int32, ascending column indices) and, when
-    return_O or O is given, O ([k, N] bf16: row j is the update of column S[j])."""
+    """One Dion3 step on the k columns of largest score of the [N, m] state (bf16, fp16
+    or fp32; in place on W and M).  Returns S ([k] int32, ascending column indices)
+    and, when return_O or O is given, O ([k, N] in the state's dtype: row j is the
+    update of column S[j])."""
     torch = _torch()
-    N, m, ld = _bf16_rows(W, "W")
-    _expect(M, "M", dtype=torch.bfloat16, shape=W.shape, device=W.device)
-    _expect(G, "G", dtype=torch.bfloat16, shape=W.shape, device=W.device)
-    if _rows(M)[2] != ld or _rows(G)[2] != ld:
-        raise ValueError("W, M, G must share the row stride")
+    N, m, ld, dt = _same_state(W, M, G)
     if S is None:
         S = torch.empty(k, dtype=torch.int32, device=W.device)
     _expect(S, "S", dtype=torch.int32, shape=(k,), device=W.device)
     if return_O and O is None:
-        O = torch.empty((k, N), dtype=torch.bfloat16, device=W.device)
+        O = torch.empty((k, N), dtype=W.dtype, device=W.device)
     if O is not None:
-        _expect(O, "O", dtype=torch.bfloat16, shape=(k, N), device=W.device)
+        _expect(O, "O", dtype=W.dtype, shape=(k, N), device=W.device)
         if not O.is_contiguous():
             raise ValueError("O must be contiguous")
     if not S.is_contiguous():
         raise ValueError("S must be contiguous")
     cdt = code_of(compute)
     sched = schedule if schedule is not None else default_schedule()
-    ws = _workspace_arg(workspace, lib.dion3_cols_workspace_size(N, m, k, cdt), W.device)
-    check(lib.dion3_step_cols(W.data_ptr(), M.data_ptr(), G.data_ptr(), N, m, ld, k, lr, weight_decay, mu,
+    ws = _workspace_arg(workspace, lib.dion3_cols_workspace_size(N, m, k, dt, cdt), W.device)
+    check(lib.dion3_step_cols(W.data_ptr(), M.data_ptr(), G.data_ptr(), dt, N, m, ld, k, lr, weight_decay, mu,
                               score_norm, cdt, ctypes.byref(sched), S.data_ptr(),
                               O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
                               _stream(W.device)), "dion3_step_cols")
@@ -487,11 +500,7 @@ def dion3_step_dev_scalars(W, M, G, k, scalars, score_norm=1, compute="f16", sch
     float32 device tensor [lr, weight_decay, mu] (for steps replayed from a HIP graph
     under a schedule).  Returns S (and O when O is given)."""
     torch = _torch()
-    N, m, ld = _bf16_rows(W, "W")
-    _expect(M, "M", dtype=torch.bfloat16, shape=W.shape, device=W.device)
-    _expect(G, "G", dtype=torch.bfloat16, shape=W.shape, device=W.device)
-    if _rows(M)[2] != ld or _rows(G)[2] != ld:
-        raise ValueError("W, M, G must share the row stride")
+    N, m, ld, dt = _same_state(W, M, G)
     _expect(scalars, "scalars", dtype=torch.float32, shape=(3,), device=W.device)
     if not scalars.is_contiguous():
         raise ValueError("scalars must be contiguous")
@@ -499,15 +508,15 @@ def dion3_step_dev_scalars(W, M, G, k, scalars, score_norm=1, compute="f16", sch
         S = torch.empty(k, dtype=torch.int32, device=W.device)
     _expect(S, "S", dtype=torch.int32, shape=(k,), device=W.device)
     if O is not None:
-        _expect(O, "O", dtype=torch.bfloat16, shape=(k, m), device=W.device)
+        _expect(O, "O", dtype=W.dtype, shape=(k, m), device=W.device)
         if not O.is_contiguous():
             raise ValueError("O must be contiguous")
     if not S.is_contiguous():
         raise ValueError("S must be contiguous")
     cdt = code_of(compute)
     sched = schedule if schedule is not None else default_schedule()
-    ws = _workspace_arg(workspace, lib.dion3_workspace_size(N, m, k, cdt), W.device)
-    check(lib.dion3_step_dev_scalars(W.data_ptr(), M.data_ptr(), G.data_ptr(), N, m, ld, k, scalars.data_ptr(),
+    ws = _workspace_arg(workspace, lib.dion3_workspace_size(N, m, k, dt, cdt), W.device)
+    check(lib.dion3_step_dev_scalars(W.data_ptr(), M.data_ptr(), G.data_ptr(), dt, N, m, ld, k, scalars.data_ptr(),
                                      score_norm, cdt, ctypes.byref(sched), S.data_ptr(),
                                      O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
                                      _stream(W.device)), "dion3_step_dev_scalars")
@@ -518,25 +527,21 @@ def dion3_step_rows(W, M, G, S, lr, weight_decay=0.0, mu=0.95, compute="f16", sc
                     workspace=None):
     """One Dion3 step in place on W and M on the caller's row set S (a [k] int32 device
     tensor of distinct ascending row indices, e.g. drawn at random).  Returns O
-    ([k, m] bf16) when O is given, else None."""
+    ([k, m] in the state's dtype) when O is given, else None."""
     torch = _torch()
-    N, m, ld = _bf16_rows(W, "W")
-    _expect(M, "M", dtype=torch.bfloat16, shape=W.shape, device=W.device)
-    _expect(G, "G", dtype=torch.bfloat16, shape=W.shape, device=W.device)
-    if _rows(M)[2] != ld or _rows(G)[2] != ld:
-        raise ValueError("W, M, G must share the row stride")
+    N, m, ld, dt = _same_state(W, M, G)
     _expect(S, "S", dtype=torch.int32, device=W.device)
     if S.dim() != 1 or not S.is_contiguous():
         raise ValueError("S must be a contiguous 1-D int32 tensor")
     k = S.shape[0]
     if O is not None:
-        _expect(O, "O", dtype=torch.bfloat16, shape=(k, m), device=W.device)
+        _expect(O, "O", dtype=W.dtype, shape=(k, m), device=W.device)
         if not O.is_contiguous():
             raise ValueError("O must be contiguous")
     cdt = code_of(compute)
     sched = schedule if schedule is not None else default_schedule()
-    ws = _workspace_arg(workspace, lib.dion3_workspace_size(N, m, k, cdt), W.device)
-    check(lib.dion3_step_rows(W.data_ptr(), M.data_ptr(), G.data_ptr(), N, m, ld, S.data_ptr(), k, lr,
+    ws = _workspace_arg(workspace, lib.dion3_workspace_size(N, m, k, dt, cdt), W.device)
+    check(lib.dion3_step_rows(W.data_ptr(), M.data_ptr(), G.data_ptr(), dt, N, m, ld, S.data_ptr(), k, lr,
                               weight_decay, mu, cdt, ctypes.byref(sched),
                               O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
                               _stream(W.device)), "dion3_step_rows")
@@ -545,17 +550,21 @@ def dion3_step_rows(W, M, G, S, lr, weight_decay=0.0, mu=0.95, compute="f16", sc
 
 def dion3_step_batched(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, compute="f16", schedule=None,
                        return_O=False, S=None, O=None, workspace=None):
-    """One Dion3 step on each of the [B, N, m] bf16 states W, M (in place) with gradients
-    G; the B selected k x m submatrices are orthogonalized by one batched Gram NS.
-    Returns S [B, k] int32 (and O [B, k, m] when return_O or O is given)."""
+    """One Dion3 step on each of the [B, N, m] states W, M (bf16, fp16 or fp32; in place)
+    with gradients G; the B selected k x m submatrices are orthogonalized by one batched
+    Gram NS.  Returns S [B, k] int32 (and O [B, k, m] in the state's dtype when return_O
+    or O is given)."""
     torch = _torch()
-    _expect(_dev(W), "W", dtype=torch.bfloat16)
+    _dev(W)
+    if W.dtype not in (torch.bfloat16, torch.float16, torch.float32):
+        raise ValueError("W must be bf16, fp16 or fp32")
+    dt = dtype_code(W)
     if W.dim() != 3 or W.stride(2) != 1:
         raise ValueError("W must be a [B, N, m] tensor with contiguous rows")
     B, N, m = W.shape
     ld, stride = W.stride(1), W.stride(0)
     for t, name in ((M, "M"), (G, "G")):
-        _expect(t, name, dtype=torch.bfloat16, shape=W.shape, device=W.device)
+        _expect(t, name, dtype=W.dtype, shape=W.shape, device=W.device)
         if t.stride() != W.stride():
             raise ValueError("W, M, G must share their strides")
     cdt = code_of(compute)
@@ -563,14 +572,14 @@ def dion3_step_batched(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, 
         S = torch.empty((B, k), dtype=torch.int32, device=W.device)
     _expect(S, "S", dtype=torch.int32, shape=(B, k), device=W.device)
     if return_O and O is None:
-        O = torch.empty((B, k, m), dtype=torch.bfloat16, device=W.device)
+        O = torch.empty((B, k, m), dtype=W.dtype, device=W.device)
     if O is not None:
-        _expect(O, "O", dtype=torch.bfloat16, shape=(B, k, m), device=W.device)
+        _expect(O, "O", dtype=W.dtype, shape=(B, k, m), device=W.device)
     if not S.is_contiguous() or (O is not None and not O.is_contiguous()):
         raise ValueError("S and O must be contiguous")
     sched = schedule if schedule is not None else default_schedule()
-    ws = _workspace_arg(workspace, lib.dion3_batched_workspace_size(B, N, m, k, cdt), W.device)
-    check(lib.dion3_step_batched(W.data_ptr(), M.data_ptr(), G.data_ptr(), B, N, m, ld, stride, k, lr,
+    ws = _workspace_arg(workspace, lib.dion3_batched_workspace_size(B, N, m, k, dt, cdt), W.device)
+    check(lib.dion3_step_batched(W.data_ptr(), M.data_ptr(), G.data_ptr(), dt, B, N, m, ld, stride, k, lr,
                                  weight_decay, mu, score_norm, cdt, ctypes.byref(sched), S.data_ptr(),
                                  O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
                                  _stream(W.device)), "dion3_step_batched")

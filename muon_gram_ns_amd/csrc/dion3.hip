@@ -7,10 +7,15 @@
 // (error feedback, same page, 前置知识).
 //
 // Rounding model (the pages do not fix it; this is the reading the oracle emulates):
-// W, M, G are bf16; each stored value is rounded once, to nearest even, from fp32
-// results computed op by op.  This file is compiled with -ffp-contract=off and uses
-// explicit __fmul_rn/__fsub_rn so no multiply-add is fused.  Row scores accumulate
-// in fp64 (the per-element terms are exact in fp64).
+// W, M, G are stored in one state type T (bf16, f16 or fp32); each stored value is
+// rounded once, to nearest even, from fp32 results computed op by op.  This file is
+// compiled with -ffp-contract=off and uses explicit __fmul_rn/__fsub_rn so no
+// multiply-add is fused.  Row scores accumulate in fp64 (the per-element terms are
+// exact in fp64).  Every kernel moves the state in 16-byte chunks: 8 elements of a
+// 16-bit type or 4 fp32 elements.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -34,11 +39,76 @@ __device__ __forceinline__ double block_sum_f64(double v, double* sh) {
   return t;
 }
 
-// ---- M <- bf16(M + G); per-row score and sum of squares ---------------------------
-// One workgroup per row.  Each thread takes chunks c, c+256, c+512, ... of 8 values;
-// four chunks' loads are issued before any is used (more bytes in flight per wave),
-// and the chunks are then summed in that same order, so each thread's fp64 sums do
-// not depend on the unrolling.
+// Raw bits of element i of a 16-byte chunk of T, and the chunk holding given element
+// bits.
+template <class T>
+__device__ __forceinline__ uint32_t elem_bits(const uint4& c, int i) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&c);
+  if constexpr (T::kBytes == 4) return w[i];
+  else return (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu);
+}
+template <class T>
+__device__ __forceinline__ uint4 pack_bits(const uint32_t (&b)[T::kPerChunk]) {
+  uint4 c;
+  uint32_t* w = reinterpret_cast<uint32_t*>(&c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (T::kBytes == 4) w[i] = b[i];
+    else w[i] = b[2 * i] | (b[2 * i + 1] << 16);
+  }
+  return c;
+}
+// An fp32 result rounded to T (bits).  For f16 the value first passes through an empty
+// asm statement: without it the compiler may merge the fp32 operation that produced it
+// and the conversion into one mixed-precision instruction (v_fma_mix*), which rounds
+// the exact result once to f16 instead of rounding the fp32 result, and differs from
+// that on ties.
+template <class T>
+__device__ __forceinline__ uint32_t round_to(float x) {
+  if constexpr (T::kId == GNS_F16) asm volatile("" : "+v"(x));
+  return T::from_f32(x);
+}
+
+// The elements of a chunk widened to fp32, and the chunk of fp32 values each rounded
+// once to T.
+template <class T>
+__device__ __forceinline__ void unpack(const uint4& c, float (&v)[T::kPerChunk]) {
+#pragma unroll
+  for (int i = 0; i < T::kPerChunk; ++i) v[i] = T::to_f32(elem_bits<T>(c, i));
+}
+template <class T>
+__device__ __forceinline__ uint4 pack(const float (&v)[T::kPerChunk]) {
+  uint32_t b[T::kPerChunk];
+#pragma unroll
+  for (int i = 0; i < T::kPerChunk; ++i) b[i] = round_to<T>(v[i]);
+  return pack_bits<T>(b);
+}
+
+template <class T>
+__device__ __forceinline__ uint4* row_chunks(void* base, long long elems) {
+  return reinterpret_cast<uint4*>(static_cast<uint8_t*>(base) + (size_t)elems * T::kBytes);
+}
+template <class T>
+__device__ __forceinline__ const uint4* row_chunks(const void* base, long long elems) {
+  return reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(base) + (size_t)elems * T::kBytes);
+}
+
+// The launchers take the state type at run time: call f with a tag of that type.
+template <class F>
+hipError_t with_state_type(gns_dtype dt, F&& f) {
+  switch (dt) {
+    case GNS_BF16: return f(TBF16{});
+    case GNS_F16: return f(TF16{});
+    case GNS_F32: return f(TF32{});
+  }
+  return hipErrorInvalidValue;
+}
+
+// ---- M <- fl(M + G); per-row score and sum of squares -------------------------------
+// One workgroup per row.  Each thread takes chunks c, c+512, c+1024, ...; four chunks'
+// loads are issued before any is used (more bytes in flight per wave), and the chunks
+// are then summed in that same order, so each thread's fp64 sums do not depend on the
+// unrolling.
 // Streaming accesses of the state (each element read and written once per pass):
 // non-temporal loads and stores.  Measured on MI355X on the 8192 x 28672 bf16 state,
 // the accumulate pass goes from 5.2 to 5.8 TB/s with them (torch's in-place add on
@@ -55,38 +125,38 @@ __device__ __forceinline__ void store_nt(const uint4& v, uint4* p) {
 
 constexpr int kAccUnroll = 4;
 
-__device__ __forceinline__ uint4 accumulate_chunk(uint4 mv, const uint4& gv, int score_norm, double& acc_s,
+template <class T>
+__device__ __forceinline__ uint4 accumulate_chunk(const uint4& mv, const uint4& gv, int score_norm, double& acc_s,
                                                   double& acc_q) {
-  uint32_t* mw = reinterpret_cast<uint32_t*>(&mv);
-  const uint32_t* gw = reinterpret_cast<const uint32_t*>(&gv);
+  constexpr int E = T::kPerChunk;
+  float a[E], g[E];
+  unpack<T>(mv, a);
+  unpack<T>(gv, g);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t out = 0;
+  for (int i = 0; i < E; ++i) a[i] = __fadd_rn(a[i], g[i]);
+  const uint4 out = pack<T>(a);
+  float st[E];
+  unpack<T>(out, st);                 // the stored (rounded) values
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float a = bf16_bits_to_f32((mw[i] >> (16 * h)) & 0xffffu);
-      const float g = bf16_bits_to_f32((gw[i] >> (16 * h)) & 0xffffu);
-      const uint32_t nb = f32_to_bf16_bits(__fadd_rn(a, g));
-      out |= nb << (16 * h);
-      const double v = (double)bf16_bits_to_f32(nb);
-      acc_s += (score_norm == 1) ? fabs(v) : v * v;
-      acc_q += v * v;
-    }
-    mw[i] = out;
+  for (int i = 0; i < E; ++i) {
+    const double v = (double)st[i];
+    acc_s += (score_norm == 1) ? fabs(v) : v * v;
+    acc_q += v * v;
   }
-  return mv;
+  return out;
 }
 
+template <class T>
 __global__ void __launch_bounds__(kRowThreads)
-accumulate_score_kernel(uint16_t* M, const uint16_t* G, int N, int m, long long ld, long long stride, int score_norm,
+accumulate_score_kernel(void* M, const void* G, int N, int m, long long ld, long long stride, int score_norm,
                         double* score, double* sumsq) {
   __shared__ double sh[kRowThreads / 64];
   const int r = blockIdx.x, b = blockIdx.y;
-  uint4* mr = reinterpret_cast<uint4*>(M + (size_t)b * stride + (size_t)r * ld);
-  const uint4* gr = reinterpret_cast<const uint4*>(G + (size_t)b * stride + (size_t)r * ld);
+  uint4* mr = row_chunks<T>(M, (long long)b * stride + (long long)r * ld);
+  const uint4* gr = row_chunks<T>(G, (long long)b * stride + (long long)r * ld);
   score += (size_t)b * N;
   if (sumsq) sumsq += (size_t)b * N;
-  const int nch = m / 8;
+  const int nch = m / T::kPerChunk;
   double acc_s = 0.0, acc_q = 0.0;
   for (int c0 = threadIdx.x; c0 < nch; c0 += kAccUnroll * kRowThreads) {
     uint4 mv[kAccUnroll], gv[kAccUnroll];
@@ -101,7 +171,7 @@ accumulate_score_kernel(uint16_t* M, const uint16_t* G, int N, int m, long long 
 #pragma unroll
     for (int u = 0; u < kAccUnroll; ++u) {
       const int c = c0 + u * kRowThreads;
-      if (c < nch) store_nt(accumulate_chunk(mv[u], gv[u], score_norm, acc_s, acc_q), &mr[c]);
+      if (c < nch) store_nt(accumulate_chunk<T>(mv[u], gv[u], score_norm, acc_s, acc_q), &mr[c]);
     }
   }
   const double ts = block_sum_f64(acc_s, sh);
@@ -112,13 +182,16 @@ accumulate_score_kernel(uint16_t* M, const uint16_t* G, int N, int m, long long 
   }
 }
 
-hipError_t launch_accumulate_score(uint16_t* M, const uint16_t* G, int batch, int N, int m, long long ld,
+hipError_t launch_accumulate_score(void* M, const void* G, gns_dtype dt, int batch, int N, int m, long long ld,
                                    long long stride, int score_norm, double* score, double* sumsq, hipStream_t s) {
   if (N <= 0 || batch <= 0) return hipSuccess;
-  clear_stale_error();
-  hipLaunchKernelGGL(accumulate_score_kernel, dim3(N, batch), dim3(kRowThreads), 0, s, M, G, N, m, ld, stride,
-                     score_norm, score, sumsq);
-  return hipGetLastError();
+  return with_state_type(dt, [&](auto tag) {
+    using T = decltype(tag);
+    clear_stale_error();
+    hipLaunchKernelGGL(accumulate_score_kernel<T>, dim3(N, batch), dim3(kRowThreads), 0, s, M, G, N, m, ld, stride,
+                       score_norm, score, sumsq);
+    return hipGetLastError();
+  });
 }
 
 // ---- top-k rows: radix select on the fp64 bit patterns, then ordered compaction ----
@@ -323,59 +396,82 @@ hipError_t launch_topk(const double* score, int batch, int N, int k, int* S, hip
   return hipGetLastError();
 }
 
-// ---- X[r] = M[S[r]]; M[S[r]] <- bf16(mu * M[S[r]]) ----------------------------------
-// X holds kx >= k rows per batch entry: rows k .. kx-1 (the padding of the submatrix
-// to a whole number of 8-row groups) are written as zeros.
+// ---- X[r] = M[S[r]]; M[S[r]] <- fl(mu * M[S[r]]) -------------------------------------
+// X (state type) holds kx >= k rows per batch entry: rows k .. kx-1 (the padding of the
+// submatrix to a whole number of 8-row groups) are written as zeros.
+template <class T>
 __global__ void __launch_bounds__(kRowThreads)
-gather_feedback_kernel(uint16_t* M, int N, int m, long long ld, long long stride, const int* S, int k, int kx,
-                       float mu_host, const float* dev_scalars, uint16_t* X, long long ldx) {
+gather_feedback_kernel(void* M, int N, int m, long long ld, long long stride, const int* S, int k, int kx,
+                       float mu_host, const float* dev_scalars, void* X, long long ldx) {
+  constexpr int E = T::kPerChunk;
   const int r = blockIdx.x, b = blockIdx.y;
   const float mu = dev_scalars ? dev_scalars[2] : mu_host;
   const int src = r < k ? S[(size_t)b * k + r] : -1;
-  uint4* xr = reinterpret_cast<uint4*>(X + ((size_t)b * kx + r) * ldx);
+  uint4* xr = row_chunks<T>(X, ((long long)b * kx + r) * ldx);
+  const int nch = m / E;
   if (src < 0 || src >= N) {           // padding row, or an index out of range: a zero row of X, M untouched
-    for (int c = threadIdx.x; c < m / 8; c += kRowThreads) xr[c] = make_uint4(0u, 0u, 0u, 0u);
+    for (int c = threadIdx.x; c < nch; c += kRowThreads) xr[c] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
-  uint4* mr = reinterpret_cast<uint4*>(M + (size_t)b * stride + (size_t)src * ld);
-  for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
-    uint4 v = load_nt(&mr[c]);
+  uint4* mr = row_chunks<T>(M, (long long)b * stride + (long long)src * ld);
+  for (int c = threadIdx.x; c < nch; c += kRowThreads) {
+    const uint4 v = load_nt(&mr[c]);
     xr[c] = v;
-    uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+    float x[E];
+    unpack<T>(v, x);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = f32_to_bf16_bits(__fmul_rn(mu, bf16_bits_to_f32(w[i] & 0xffffu)));
-      const uint32_t hi = f32_to_bf16_bits(__fmul_rn(mu, bf16_bits_to_f32(w[i] >> 16)));
-      w[i] = lo | (hi << 16);
-    }
-    store_nt(v, &mr[c]);
+    for (int i = 0; i < E; ++i) x[i] = __fmul_rn(mu, x[i]);
+    store_nt(pack<T>(x), &mr[c]);
   }
 }
 
-hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long long ld, long long stride, const int* S,
-                                  int k, int kx, float mu, const float* dev_scalars, uint16_t* X, long long ldx,
-                                  hipStream_t s) {
-  if (k <= 0 || batch <= 0 || kx < k) return k <= 0 || batch <= 0 ? hipSuccess : hipErrorInvalidValue;
-  clear_stale_error();
-  hipLaunchKernelGGL(gather_feedback_kernel, dim3(kx, batch), dim3(kRowThreads), 0, s, M, N, m, ld, stride, S, k, kx,
-                     mu, dev_scalars, X, ldx);
-  return hipGetLastError();
+hipError_t launch_gather_feedback(void* M, gns_dtype dt, int batch, int N, int m, long long ld, long long stride,
+                                  const int* S, int k, int kx, float mu, const float* dev_scalars, void* X,
+                                  long long ldx, hipStream_t s) {
+  if (k <= 0 || batch <= 0) return hipSuccess;
+  if (kx < k) return hipErrorInvalidValue;
+  return with_state_type(dt, [&](auto tag) {
+    using T = decltype(tag);
+    clear_stale_error();
+    hipLaunchKernelGGL(gather_feedback_kernel<T>, dim3(kx, batch), dim3(kRowThreads), 0, s, M, N, m, ld, stride, S,
+                       k, kx, mu, dev_scalars, X, ldx);
+    return hipGetLastError();
+  });
+}
+
+// E elements of O (type TO) from p, widened to fp32: whole 16-byte chunks, or half of
+// one (4 fp32 state elements against a 16-bit O).
+template <class TO, int E>
+__device__ __forceinline__ void load_o(const uint8_t* p, float (&o)[E]) {
+  constexpr int PER = TO::kPerChunk;
+  if constexpr (E >= PER) {
+#pragma unroll
+    for (int q = 0; q < E / PER; ++q) {
+      const uint4 c = reinterpret_cast<const uint4*>(p)[q];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[q * PER + i] = TO::to_f32(elem_bits<TO>(c, i));
+    }
+  } else {
+    const uint2 h = *reinterpret_cast<const uint2*>(p);
+    const uint4 c = make_uint4(h.x, h.y, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = TO::to_f32(elem_bits<TO>(c, i));
+  }
 }
 
 // ---- weight decay + selected-row update, one rounding per element --------------------
-template <bool O_F32>
+template <class T, class TO>
 __global__ void __launch_bounds__(kRowThreads)
-apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, const int* S, int k, const void* O,
+apply_update_kernel(void* W, int N, int m, long long ld, long long stride, const int* S, int k, const void* O,
                     long long ldo, long long so, float lr_host, float wd_host, const float* dev_scalars, int all_rows,
-                    uint16_t* Mfb, float mu_host) {
+                    void* Mfb, float mu_host) {
+  constexpr int E = T::kPerChunk;
   const float lr = dev_scalars ? dev_scalars[0] : lr_host;
   const float wd = dev_scalars ? dev_scalars[1] : wd_host;
   const float mu = dev_scalars ? dev_scalars[2] : mu_host;
   const int d_over = blockIdx.x, b = blockIdx.y;
-  W += (size_t)b * stride;
-  if (Mfb) Mfb += (size_t)b * stride;
   S += (size_t)b * k;
-  O = reinterpret_cast<const uint8_t*>(O) + (size_t)b * so * (O_F32 ? 4 : 2);
+  const uint8_t* Ob = static_cast<const uint8_t*>(O) + (size_t)b * so * TO::kBytes;
   int row, oi;
   if (all_rows) {
     row = d_over;
@@ -396,73 +492,53 @@ apply_update_kernel(uint16_t* W, int N, int m, long long ld, long long stride, c
   // an unselected row without weight decay keeps its bits (d = 1 would not change it)
   if (oi < 0 && wd == 0.0f) return;
   const float d = __fsub_rn(1.0f, __fmul_rn(lr, wd));
-  uint4* wr = reinterpret_cast<uint4*>(W + (size_t)row * ld);
-  // error feedback on the same selected row, in the same pass: M[S[oi]] <- bf16(mu
+  uint4* wr = row_chunks<T>(W, (long long)b * stride + (long long)row * ld);
+  // error feedback on the same selected row, in the same pass: M[S[oi]] <- fl(mu
   // M[S[oi]]), the arithmetic of gather_feedback_kernel (the Gram products have read
   // these rows already); W and M chunks are loaded together for more bytes in flight
-  uint4* mr = (Mfb && oi >= 0) ? reinterpret_cast<uint4*>(Mfb + (size_t)row * ld) : nullptr;
-  for (int c = threadIdx.x; c < m / 8; c += kRowThreads) {
-    uint4 v = load_nt(&wr[c]);
-    uint4 mv = mr ? load_nt(&mr[c]) : make_uint4(0u, 0u, 0u, 0u);
-    uint32_t* w = reinterpret_cast<uint32_t*>(&v);
-    float o[8];
-    if (oi >= 0) {
-      if constexpr (O_F32) {
-        const float4* op = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(O) + (size_t)oi * ldo + (size_t)c * 8);
-        const float4 a = op[0], b = op[1];
-        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-      } else {
-        const uint4 q = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(O) + (size_t)oi * ldo)[c];
-        const uint32_t* qw = reinterpret_cast<const uint32_t*>(&q);
+  uint4* mr = (Mfb && oi >= 0) ? row_chunks<T>(Mfb, (long long)b * stride + (long long)row * ld) : nullptr;
+  for (int c = threadIdx.x; c < m / E; c += kRowThreads) {
+    const uint4 v = load_nt(&wr[c]);
+    const uint4 mv = mr ? load_nt(&mr[c]) : make_uint4(0u, 0u, 0u, 0u);
+    float o[E];
+    if (oi >= 0) load_o<TO, E>(Ob + ((size_t)oi * ldo + (size_t)c * E) * TO::kBytes, o);
+    float x[E];
+    unpack<T>(v, x);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[2 * i] = bf16_bits_to_f32(qw[i] & 0xffffu);
-          o[2 * i + 1] = bf16_bits_to_f32(qw[i] >> 16);
-        }
-      }
+    for (int i = 0; i < E; ++i) {
+      float y = __fmul_rn(d, x[i]);
+      if (oi >= 0) y = __fsub_rn(y, __fmul_rn(lr, o[i]));
+      x[i] = y;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t out = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float x = bf16_bits_to_f32((w[i] >> (16 * h)) & 0xffffu);
-        float y = __fmul_rn(d, x);
-        if (oi >= 0) y = __fsub_rn(y, __fmul_rn(lr, o[2 * i + h]));
-        out |= f32_to_bf16_bits(y) << (16 * h);
-      }
-      w[i] = out;
-    }
-    store_nt(v, &wr[c]);
+    store_nt(pack<T>(x), &wr[c]);
     if (mr) {
-      uint32_t* mw = reinterpret_cast<uint32_t*>(&mv);
+      float mm[E];
+      unpack<T>(mv, mm);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = f32_to_bf16_bits(__fmul_rn(mu, bf16_bits_to_f32(mw[i] & 0xffffu)));
-        const uint32_t hi = f32_to_bf16_bits(__fmul_rn(mu, bf16_bits_to_f32(mw[i] >> 16)));
-        mw[i] = lo | (hi << 16);
-      }
-      store_nt(mv, &mr[c]);
+      for (int i = 0; i < E; ++i) mm[i] = __fmul_rn(mu, mm[i]);
+      store_nt(pack<T>(mm), &mr[c]);
     }
   }
 }
 
-hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long ld, long long stride, const int* S, int k,
-                               const void* O, gns_dtype o_dtype, long long ldo, long long so, float lr, float wd,
-                               const float* dev_scalars, hipStream_t s, uint16_t* Mfb, float mu) {
+hipError_t launch_apply_update(void* W, gns_dtype dt, int batch, int N, int m, long long ld, long long stride,
+                               const int* S, int k, const void* O, gns_dtype o_dtype, long long ldo, long long so,
+                               float lr, float wd, const float* dev_scalars, hipStream_t s, void* Mfb, float mu) {
   // with the weight decay on the device the host cannot tell whether unselected rows
   // decay: cover all rows (each unselected row returns at once when wd == 0)
   const int all_rows = (dev_scalars || wd != 0.0f) ? 1 : 0;
   const int blocks = all_rows ? N : k;
   if (blocks <= 0 || batch <= 0) return hipSuccess;
-  clear_stale_error();
-  if (o_dtype == GNS_F32)
-    hipLaunchKernelGGL(apply_update_kernel<true>, dim3(blocks, batch), dim3(kRowThreads), 0, s, W, N, m, ld, stride, S,
-                       k, O, ldo, so, lr, wd, dev_scalars, all_rows, Mfb, mu);
-  else
-    hipLaunchKernelGGL(apply_update_kernel<false>, dim3(blocks, batch), dim3(kRowThreads), 0, s, W, N, m, ld, stride,
-                       S, k, O, ldo, so, lr, wd, dev_scalars, all_rows, Mfb, mu);
-  return hipGetLastError();
+  return with_state_type(dt, [&](auto tag) {
+    using T = decltype(tag);
+    return with_state_type(o_dtype, [&](auto otag) {
+      using TO = decltype(otag);
+      clear_stale_error();
+      hipLaunchKernelGGL((apply_update_kernel<T, TO>), dim3(blocks, batch), dim3(kRowThreads), 0, s, W, N, m, ld,
+                         stride, S, k, O, ldo, so, lr, wd, dev_scalars, all_rows, Mfb, mu);
+      return hipGetLastError();
+    });
+  });
 }
 
 // ---- s = 1 / (sqrt(sum_i sumsq[S[i]]) + eps) ------------------------------------------
@@ -511,20 +587,31 @@ constexpr int kColThreads = 256;
 constexpr int kColRowsPerPart = 128;   // rows summed into one partial column score
 constexpr int kColTile = 64;
 
-// M <- bf16(M + G) and, per column, fp64 sums over a block of kColRowsPerPart rows:
+// Element storage of T in LDS tiles: its raw bits, rows padded by 4 bytes so a wave's
+// 64 lanes reading one tile column hit distinct banks.
+template <class T>
+struct ColTile {
+  using Bits = typename std::conditional<T::kBytes == 4, uint32_t, uint16_t>::type;
+  static constexpr int kPad = 4 / T::kBytes;
+  Bits v[kColTile][kColTile + kPad];
+};
+
+// M <- fl(M + G) and, per column, fp64 sums over a block of kColRowsPerPart rows:
 // part_s[rb][col] (|x| or x^2 by score_norm) and part_q[rb][col] (x^2).  Thread =
-// one 16-byte chunk (8 columns); rows in ascending order, four loaded at a time.
+// one 16-byte chunk of columns; rows in ascending order, four loaded at a time.
+template <class T>
 __global__ void __launch_bounds__(kColThreads)
-accumulate_colscore_kernel(uint16_t* M, const uint16_t* G, int N, int m, long long ld, int score_norm,
-                           double* part_s, double* part_q) {
+accumulate_colscore_kernel(void* M, const void* G, int N, int m, long long ld, int score_norm, double* part_s,
+                           double* part_q) {
+  constexpr int E = T::kPerChunk;
   const int c = blockIdx.x * kColThreads + threadIdx.x;
-  const int nch = m / 8;
+  const int nch = m / E;
   if (c >= nch) return;
   const int rb = blockIdx.y;
   const int i0 = rb * kColRowsPerPart, i1 = min(N, i0 + kColRowsPerPart);
-  double s[8], q[8];
+  double s[E], q[E];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = q[e] = 0.0;
+  for (int e = 0; e < E; ++e) s[e] = q[e] = 0.0;
   constexpr int U = 4;
   for (int ib = i0; ib < i1; ib += U) {
     uint4 mv[U], gv[U];
@@ -532,39 +619,35 @@ accumulate_colscore_kernel(uint16_t* M, const uint16_t* G, int N, int m, long lo
     for (int u = 0; u < U; ++u) {
       const int i = ib + u;
       if (i < i1) {
-        mv[u] = load_nt(reinterpret_cast<const uint4*>(M + (size_t)i * ld) + c);
-        gv[u] = load_nt(reinterpret_cast<const uint4*>(G + (size_t)i * ld) + c);
+        mv[u] = load_nt(row_chunks<T>(M, (long long)i * ld) + c);
+        gv[u] = load_nt(row_chunks<T>(G, (long long)i * ld) + c);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = ib + u;
       if (i >= i1) continue;
-      uint32_t* mw = reinterpret_cast<uint32_t*>(&mv[u]);
-      const uint32_t* gw = reinterpret_cast<const uint32_t*>(&gv[u]);
+      float a[E], g[E];
+      unpack<T>(mv[u], a);
+      unpack<T>(gv[u], g);
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        uint32_t out = 0;
+      for (int e = 0; e < E; ++e) a[e] = __fadd_rn(a[e], g[e]);
+      const uint4 out = pack<T>(a);
+      float st[E];
+      unpack<T>(out, st);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float a = bf16_bits_to_f32((mw[e2] >> (16 * h)) & 0xffffu);
-          const float g = bf16_bits_to_f32((gw[e2] >> (16 * h)) & 0xffffu);
-          const uint32_t nb = f32_to_bf16_bits(__fadd_rn(a, g));
-          out |= nb << (16 * h);
-          const double v = (double)bf16_bits_to_f32(nb);
-          const int e = 2 * e2 + h;
-          s[e] += (score_norm == 1) ? fabs(v) : v * v;
-          q[e] += v * v;
-        }
-        mw[e2] = out;
+      for (int e = 0; e < E; ++e) {
+        const double v = (double)st[e];
+        s[e] += (score_norm == 1) ? fabs(v) : v * v;
+        q[e] += v * v;
       }
-      store_nt(mv[u], reinterpret_cast<uint4*>(M + (size_t)i * ld) + c);
+      store_nt(out, row_chunks<T>(M, (long long)i * ld) + c);
     }
   }
-  double* ps = part_s + (size_t)rb * m + 8 * (size_t)c;
-  double* pq = part_q + (size_t)rb * m + 8 * (size_t)c;
+  double* ps = part_s + (size_t)rb * m + (size_t)E * c;
+  double* pq = part_q + (size_t)rb * m + (size_t)E * c;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < E; ++e) {
     ps[e] = s[e];
     pq[e] = q[e];
   }
@@ -584,12 +667,14 @@ reduce_colscore_kernel(const double* part_s, const double* part_q, int nparts, i
   sumsq[col] = q;
 }
 
-// Xt[j, i] = M[i, S[j]] (Xt: k x N, row stride ldx) and M[i, S[j]] <- bf16(mu M[i, S[j]]).
+// Xt[j, i] = M[i, S[j]] (Xt: k x N, row stride ldx) and M[i, S[j]] <- fl(mu M[i, S[j]]).
 // An index S[j] outside [0, m) gives a zero row of Xt and touches M nowhere.
+template <class T>
 __global__ void __launch_bounds__(kColThreads)
-gather_cols_feedback_kernel(uint16_t* M, int N, int m, long long ld, const int* S, int k, int kx, float mu,
-                            uint16_t* Xt, long long ldx) {
-  __shared__ __align__(16) uint16_t tile[kColTile][kColTile + 2];   // [j][i]; rows of 132 bytes
+gather_cols_feedback_kernel(void* M, int N, int m, long long ld, const int* S, int k, int kx, float mu, void* Xt,
+                            long long ldx) {
+  using Bits = typename ColTile<T>::Bits;
+  __shared__ __align__(16) ColTile<T> tile;    // [j][i]
   const int j0 = blockIdx.x * kColTile, i0 = blockIdx.y * kColTile;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int j = j0 + lane;
@@ -597,45 +682,51 @@ gather_cols_feedback_kernel(uint16_t* M, int N, int m, long long ld, const int* 
   const bool ok = col >= 0 && col < m;
   for (int r = w; r < kColTile; r += kColThreads / 64) {
     const int i = i0 + r;
-    uint16_t x = 0;
+    Bits x = 0;
     if (ok && i < N) {
-      uint16_t* p = M + (size_t)i * ld + col;
+      Bits* p = static_cast<Bits*>(M) + (size_t)i * ld + col;
       x = *p;
-      *p = (uint16_t)f32_to_bf16_bits(__fmul_rn(mu, bf16_bits_to_f32(x)));
+      *p = (Bits)round_to<T>(__fmul_rn(mu, T::to_f32(x)));
     }
-    tile[lane][r] = x;
+    tile.v[lane][r] = x;
   }
   __syncthreads();
-  // row jr of the tile, 16 values from column 16 q: two 16-byte stores; rows k .. kx-1
+  // row jr of the tile, 16 values from column 16 q, in 16-byte stores; rows k .. kx-1
   // (padding to a whole number of 8-row groups) are written as zeros
   const int jr = threadIdx.x >> 2, qd = threadIdx.x & 3;
   if (j0 + jr >= kx) return;
-  const uint32_t* t32 = reinterpret_cast<const uint32_t*>(&tile[jr][0]);
+  const uint32_t* t32 = reinterpret_cast<const uint32_t*>(&tile.v[jr][0]);
+  constexpr int E = T::kPerChunk;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int a = 16 * qd + 8 * h;                   // tile column (even: 4-byte aligned)
-    if (i0 + a >= N) continue;                       // N % 8 == 0: 8 values all in or all out
-    const uint4 v = make_uint4(t32[a / 2], t32[a / 2 + 1], t32[a / 2 + 2], t32[a / 2 + 3]);
-    *reinterpret_cast<uint4*>(Xt + (size_t)(j0 + jr) * ldx + i0 + a) = v;
+  for (int h = 0; h < 16 / E; ++h) {
+    const int a = 16 * qd + E * h;                   // tile column of the chunk's first element
+    if (i0 + a >= N) continue;                       // N % 8 == 0: a chunk is all in or all out
+    const int w0 = a * T::kBytes / 4;
+    const uint4 v = make_uint4(t32[w0], t32[w0 + 1], t32[w0 + 2], t32[w0 + 3]);
+    *row_chunks<T>(Xt, (long long)(j0 + jr) * ldx + i0 + a) = v;
   }
 }
 
-// W[i, S[j]] <- bf16(fl32(d W) - fl32(lr O[j, i])), d = fl32(1 - fl32(lr wd)); O: k x N
-// (row stride ldo).  An index S[j] outside [0, m) updates nothing.
+// W[i, S[j]] <- fl(fl32(d W) - fl32(lr O[j, i])), d = fl32(1 - fl32(lr wd)); O: k x N
+// (row stride ldo, state type).  An index S[j] outside [0, m) updates nothing.
+template <class T>
 __global__ void __launch_bounds__(kColThreads)
-update_cols_kernel(uint16_t* W, int N, int m, long long ld, const int* S, int k, const uint16_t* O, long long ldo,
-                   float lr, float wd) {
-  __shared__ __align__(16) uint16_t tile[kColTile][kColTile + 2];   // [j][i]
+update_cols_kernel(void* W, int N, int m, long long ld, const int* S, int k, const void* O, long long ldo, float lr,
+                   float wd) {
+  using Bits = typename ColTile<T>::Bits;
+  __shared__ __align__(16) ColTile<T> tile;    // [j][i]
+  constexpr int E = T::kPerChunk;
   const int j0 = blockIdx.x * kColTile, i0 = blockIdx.y * kColTile;
   {
     const int jr = threadIdx.x >> 2, qd = threadIdx.x & 3;
-    uint32_t* t32 = reinterpret_cast<uint32_t*>(&tile[jr][0]);
+    uint32_t* t32 = reinterpret_cast<uint32_t*>(&tile.v[jr][0]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int a = 16 * qd + 8 * h;
+    for (int h = 0; h < 16 / E; ++h) {
+      const int a = 16 * qd + E * h;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (j0 + jr < k && i0 + a < N) v = *reinterpret_cast<const uint4*>(O + (size_t)(j0 + jr) * ldo + i0 + a);
-      t32[a / 2] = v.x; t32[a / 2 + 1] = v.y; t32[a / 2 + 2] = v.z; t32[a / 2 + 3] = v.w;
+      if (j0 + jr < k && i0 + a < N) v = *row_chunks<T>(O, (long long)(j0 + jr) * ldo + i0 + a);
+      const int w0 = a * T::kBytes / 4;
+      t32[w0] = v.x; t32[w0 + 1] = v.y; t32[w0 + 2] = v.z; t32[w0 + 3] = v.w;
     }
   }
   __syncthreads();
@@ -647,10 +738,10 @@ update_cols_kernel(uint16_t* W, int N, int m, long long ld, const int* S, int k,
   for (int r = w; r < kColTile; r += kColThreads / 64) {
     const int i = i0 + r;
     if (i >= N) break;
-    uint16_t* p = W + (size_t)i * ld + col;
-    const float x = bf16_bits_to_f32(*p);
-    const float o = bf16_bits_to_f32(tile[lane][r]);
-    *p = (uint16_t)f32_to_bf16_bits(__fsub_rn(__fmul_rn(d, x), __fmul_rn(lr, o)));
+    Bits* p = static_cast<Bits*>(W) + (size_t)i * ld + col;
+    const float x = T::to_f32(*p);
+    const float o = T::to_f32(tile.v[lane][r]);
+    *p = (Bits)round_to<T>(__fsub_rn(__fmul_rn(d, x), __fmul_rn(lr, o)));
   }
 }
 
@@ -666,74 +757,84 @@ __global__ void __launch_bounds__(kColThreads) set_marks_kernel(uint8_t* mark, i
   if (col >= 0 && col < m) mark[col] = 1;
 }
 
-// W[i, c] <- bf16(fl32(d W[i, c])) for every column c not marked (decoupled weight decay)
+// W[i, c] <- fl(fl32(d W[i, c])) for every column c not marked (decoupled weight decay);
+// marked columns keep their bits
+template <class T>
 __global__ void __launch_bounds__(kColThreads)
-decay_unmarked_kernel(uint16_t* W, int N, int m, long long ld, const uint8_t* mark, float lr, float wd) {
+decay_unmarked_kernel(void* W, int N, int m, long long ld, const uint8_t* mark, float lr, float wd) {
+  constexpr int E = T::kPerChunk;
   const int c = blockIdx.x * kColThreads + threadIdx.x;   // 16-byte chunk
-  if (c >= m / 8) return;
+  if (c >= m / E) return;
   const float d = __fsub_rn(1.0f, __fmul_rn(lr, wd));
   for (int i = blockIdx.y; i < N; i += gridDim.y) {
-    uint4* p = reinterpret_cast<uint4*>(W + (size_t)i * ld) + c;
-    uint4 v = load_nt(p);
-    uint32_t* vw = reinterpret_cast<uint32_t*>(&v);
+    uint4* p = row_chunks<T>(W, (long long)i * ld) + c;
+    const uint4 v = load_nt(p);
+    uint32_t nb[E];
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      uint32_t out = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t bits = (vw[e2] >> (16 * h)) & 0xffffu;
-        const int col = 8 * c + 2 * e2 + h;
-        const uint32_t nb = mark[col] ? bits : f32_to_bf16_bits(__fmul_rn(d, bf16_bits_to_f32(bits)));
-        out |= nb << (16 * h);
-      }
-      vw[e2] = out;
+    for (int e = 0; e < E; ++e) {
+      const uint32_t bits = elem_bits<T>(v, e);
+      nb[e] = mark[E * c + e] ? bits : round_to<T>(__fmul_rn(d, T::to_f32(bits)));
     }
-    store_nt(v, p);
+    store_nt(pack_bits<T>(nb), p);
   }
 }
 
 size_t dion3_cols_partials(int N) { return (size_t)((N + kColRowsPerPart - 1) / kColRowsPerPart); }
 
-hipError_t launch_accumulate_colscore(uint16_t* M, const uint16_t* G, int N, int m, long long ld, int score_norm,
-                                      double* part_s, double* part_q, double* score, double* sumsq, hipStream_t s) {
+hipError_t launch_accumulate_colscore(void* M, const void* G, gns_dtype dt, int N, int m, long long ld,
+                                      int score_norm, double* part_s, double* part_q, double* score, double* sumsq,
+                                      hipStream_t s) {
   if (N <= 0 || m <= 0) return hipSuccess;
   const int nparts = (int)dion3_cols_partials(N);
-  clear_stale_error();
-  hipLaunchKernelGGL(accumulate_colscore_kernel, dim3((m / 8 + kColThreads - 1) / kColThreads, nparts),
-                     dim3(kColThreads), 0, s, M, G, N, m, ld, score_norm, part_s, part_q);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(reduce_colscore_kernel, dim3((m + kColThreads - 1) / kColThreads), dim3(kColThreads), 0, s,
-                     part_s, part_q, nparts, m, score, sumsq);
-  return hipGetLastError();
-}
-
-hipError_t launch_gather_cols_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, int kx,
-                                       float mu, uint16_t* Xt, long long ldx, hipStream_t s) {
-  if (k <= 0 || N <= 0) return hipSuccess;
-  if (kx < k) return hipErrorInvalidValue;
-  clear_stale_error();
-  hipLaunchKernelGGL(gather_cols_feedback_kernel, dim3((kx + kColTile - 1) / kColTile, (N + kColTile - 1) / kColTile),
-                     dim3(kColThreads), 0, s, M, N, m, ld, S, k, kx, mu, Xt, ldx);
-  return hipGetLastError();
-}
-
-hipError_t launch_update_cols(uint16_t* W, int N, int m, long long ld, const int* S, int k, const uint16_t* O,
-                              long long ldo, float lr, float wd, uint8_t* mark, hipStream_t s) {
-  if (k <= 0 || N <= 0) return hipSuccess;
-  clear_stale_error();
-  if (wd != 0.0f) {
-    hipLaunchKernelGGL(clear_marks_kernel, dim3((m + kColThreads - 1) / kColThreads), dim3(kColThreads), 0, s, mark, m);
-    hipLaunchKernelGGL(set_marks_kernel, dim3((k + kColThreads - 1) / kColThreads), dim3(kColThreads), 0, s, mark, m,
-                       S, k);
-    hipLaunchKernelGGL(decay_unmarked_kernel, dim3((m / 8 + kColThreads - 1) / kColThreads, std::min(N, 4096)),
-                       dim3(kColThreads), 0, s, W, N, m, ld, mark, lr, wd);
+  return with_state_type(dt, [&](auto tag) {
+    using T = decltype(tag);
+    clear_stale_error();
+    const int nch = m / T::kPerChunk;
+    hipLaunchKernelGGL(accumulate_colscore_kernel<T>, dim3((nch + kColThreads - 1) / kColThreads, nparts),
+                       dim3(kColThreads), 0, s, M, G, N, m, ld, score_norm, part_s, part_q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(update_cols_kernel, dim3((k + kColTile - 1) / kColTile, (N + kColTile - 1) / kColTile),
-                     dim3(kColThreads), 0, s, W, N, m, ld, S, k, O, ldo, lr, wd);
-  return hipGetLastError();
+    hipLaunchKernelGGL(reduce_colscore_kernel, dim3((m + kColThreads - 1) / kColThreads), dim3(kColThreads), 0, s,
+                       part_s, part_q, nparts, m, score, sumsq);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_gather_cols_feedback(void* M, gns_dtype dt, int N, int m, long long ld, const int* S, int k, int kx,
+                                       float mu, void* Xt, long long ldx, hipStream_t s) {
+  if (k <= 0 || N <= 0) return hipSuccess;
+  if (kx < k) return hipErrorInvalidValue;
+  return with_state_type(dt, [&](auto tag) {
+    using T = decltype(tag);
+    clear_stale_error();
+    hipLaunchKernelGGL(gather_cols_feedback_kernel<T>,
+                       dim3((kx + kColTile - 1) / kColTile, (N + kColTile - 1) / kColTile), dim3(kColThreads), 0, s, M,
+                       N, m, ld, S, k, kx, mu, Xt, ldx);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_update_cols(void* W, gns_dtype dt, int N, int m, long long ld, const int* S, int k, const void* O,
+                              long long ldo, float lr, float wd, uint8_t* mark, hipStream_t s) {
+  if (k <= 0 || N <= 0) return hipSuccess;
+  return with_state_type(dt, [&](auto tag) {
+    using T = decltype(tag);
+    clear_stale_error();
+    if (wd != 0.0f) {
+      const int nch = m / T::kPerChunk;
+      hipLaunchKernelGGL(clear_marks_kernel, dim3((m + kColThreads - 1) / kColThreads), dim3(kColThreads), 0, s, mark,
+                         m);
+      hipLaunchKernelGGL(set_marks_kernel, dim3((k + kColThreads - 1) / kColThreads), dim3(kColThreads), 0, s, mark, m,
+                         S, k);
+      hipLaunchKernelGGL(decay_unmarked_kernel<T>, dim3((nch + kColThreads - 1) / kColThreads, std::min(N, 4096)),
+                         dim3(kColThreads), 0, s, W, N, m, ld, mark, lr, wd);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(update_cols_kernel<T>, dim3((k + kColTile - 1) / kColTile, (N + kColTile - 1) / kColTile),
+                       dim3(kColThreads), 0, s, W, N, m, ld, S, k, O, ldo, lr, wd);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace gns

@@ -592,20 +592,20 @@ int rect_gemm(int batch, int n, int k, int m, float alpha, const void* A, long l
 
 // ---- Dion3 ------------------------------------------------------------------------
 
-static int check_dion3_matrix(const void* P, int N, int m, long long ld) {
-  if (!P || N < 1 || m < 1 || ld < m) return GNS_ERR_INVALID_ARG;
+static int check_dion3_matrix(const void* P, gns_dtype dt, int N, int m, long long ld) {
+  if (!P || !valid_dtype(dt) || N < 1 || m < 1 || ld < m) return GNS_ERR_INVALID_ARG;
   if (m % 8 || ld % 8 || !aligned16(P)) return GNS_ERR_UNSUPPORTED;
   return GNS_OK;
 }
 
-int dion3_accumulate_score(void* M, const void* G, int N, int m, long long ld, int score_norm, double* score,
-                           double* sumsq, hipStream_t stream) {
-  int st = check_dion3_matrix(M, N, m, ld);
+int dion3_accumulate_score(void* M, const void* G, gns_dtype dt, int N, int m, long long ld, int score_norm,
+                           double* score, double* sumsq, hipStream_t stream) {
+  int st = check_dion3_matrix(M, dt, N, m, ld);
   if (st) return st;
-  st = check_dion3_matrix(G, N, m, ld);
+  st = check_dion3_matrix(G, dt, N, m, ld);
   if (st) return st;
   if (!score || (score_norm != 1 && score_norm != 2)) return GNS_ERR_INVALID_ARG;
-  HIP_OK(launch_accumulate_score((uint16_t*)M, (const uint16_t*)G, 1, N, m, ld, 0, score_norm, score, sumsq, stream));
+  HIP_OK(launch_accumulate_score(M, G, dt, 1, N, m, ld, 0, score_norm, score, sumsq, stream));
   return GNS_OK;
 }
 
@@ -615,31 +615,37 @@ int dion3_select_topk(const double* score, int N, int k, int* S, hipStream_t str
   return GNS_OK;
 }
 
-int dion3_gather_feedback(void* M, int N, int m, long long ld, const int* S, int k, float mu, void* X, long long ldx,
-                          hipStream_t stream) {
-  int st = check_dion3_matrix(M, N, m, ld);
+int dion3_gather_feedback(void* M, gns_dtype dt, int N, int m, long long ld, const int* S, int k, float mu, void* X,
+                          long long ldx, hipStream_t stream) {
+  int st = check_dion3_matrix(M, dt, N, m, ld);
   if (st) return st;
   if (!S || !X || k < 1 || k > N || ldx < m || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
   if (ldx % 8 || !aligned16(X)) return GNS_ERR_UNSUPPORTED;
-  HIP_OK(launch_gather_feedback((uint16_t*)M, 1, N, m, ld, 0, S, k, k, mu, nullptr, (uint16_t*)X, ldx, stream));
+  HIP_OK(launch_gather_feedback(M, dt, 1, N, m, ld, 0, S, k, k, mu, nullptr, X, ldx, stream));
   return GNS_OK;
 }
 
-int dion3_apply_update(void* W, int N, int m, long long ld, const int* S, int k, const void* O, gns_dtype o_dtype,
-                       long long ldo, float lr, float wd, hipStream_t stream) {
-  int st = check_dion3_matrix(W, N, m, ld);
+int dion3_apply_update(void* W, gns_dtype dt, int N, int m, long long ld, const int* S, int k, const void* O,
+                       gns_dtype o_dtype, long long ldo, float lr, float wd, hipStream_t stream) {
+  int st = check_dion3_matrix(W, dt, N, m, ld);
   if (st) return st;
   if (!S || !O || k < 1 || k > N || ldo < m || !std::isfinite(lr) || !std::isfinite(wd)) return GNS_ERR_INVALID_ARG;
-  if (o_dtype != GNS_BF16 && o_dtype != GNS_F32) return GNS_ERR_UNSUPPORTED;
+  if (!valid_dtype(o_dtype)) return GNS_ERR_INVALID_ARG;
   if (ldo % 8 || !aligned16(O)) return GNS_ERR_UNSUPPORTED;
-  HIP_OK(launch_apply_update((uint16_t*)W, 1, N, m, ld, 0, S, k, O, o_dtype, ldo, (long long)k * ldo, lr, wd, nullptr,
+  HIP_OK(launch_apply_update(W, dt, 1, N, m, ld, 0, S, k, O, o_dtype, ldo, (long long)k * ldo, lr, wd, nullptr,
                              stream));
   return GNS_OK;
 }
 
 struct Dion3Layout {
-  double* score; double* sumsq; float* s; void* X; void* O; void* gns_ws; size_t gns_bytes; size_t bytes;
+  double* score; double* sumsq; float* s; void* X; void* Xc; void* O; void* gns_ws; size_t gns_bytes; size_t bytes;
 };
+
+// An fp32 state meets the 16-bit iterates through a copy of the submatrix scaled by
+// its Frobenius scale and rounded once to the iterate type (the iteration reads a
+// 16-bit X with 16-bit iterates); the iteration then normalises that copy itself,
+// whose norm is 1 up to the rounding.
+static bool dion3_casts_x(gns_dtype dt) { return dt == GNS_F32; }
 
 // The selected submatrix is held with kp = k rounded up to a multiple of 8 rows; the
 // extra rows are zero.  Zero rows leave the iteration's result on the other rows
@@ -647,7 +653,7 @@ struct Dion3Layout {
 // every kernel then works on whole 8-row groups.
 int padded_rows(int k) { return (k + 7) / 8 * 8; }
 
-static Dion3Layout dion3_layout(void* base, int batch, int N, int m, int k, gns_dtype cdt) {
+static Dion3Layout dion3_layout(void* base, int batch, int N, int m, int k, gns_dtype dt, gns_dtype cdt) {
   Carver c{reinterpret_cast<uint8_t*>(base), 0};
   Dion3Layout L{};
   const size_t B = (size_t)batch;
@@ -655,35 +661,37 @@ static Dion3Layout dion3_layout(void* base, int batch, int N, int m, int k, gns_
   L.score = (double*)c.take(sizeof(double) * B * N);
   L.sumsq = (double*)c.take(sizeof(double) * B * N);
   L.s = (float*)c.take(sizeof(float) * B);
-  L.X = c.take(B * kp * m * 2);
-  L.O = c.take(B * kp * m * 2);
+  L.X = c.take(B * kp * m * esize(dt));
+  L.Xc = dion3_casts_x(dt) ? c.take(B * kp * m * esize(cdt)) : nullptr;
+  L.O = c.take(B * kp * m * esize(dt));
   L.gns_bytes = ns_workspace_bytes(batch, kp, m, cdt);
   L.gns_ws = c.take(L.gns_bytes);
   L.bytes = c.off;
   return L;
 }
 
-size_t dion3_batched_workspace_size(int batch, int N, int m, int k, gns_dtype compute) {
-  if (batch < 1 || N < 1 || m < 1 || k < 1 || !valid_dtype(compute)) return 0;
-  return dion3_layout(nullptr, batch, N, m, k, compute).bytes;
+size_t dion3_batched_workspace_size(int batch, int N, int m, int k, gns_dtype dt, gns_dtype compute) {
+  if (batch < 1 || N < 1 || m < 1 || k < 1 || !valid_dtype(dt) || !valid_dtype(compute)) return 0;
+  return dion3_layout(nullptr, batch, N, m, k, dt, compute).bytes;
 }
 
-size_t dion3_workspace_size(int N, int m, int k, gns_dtype compute) {
-  return dion3_batched_workspace_size(1, N, m, k, compute);
+size_t dion3_workspace_size(int N, int m, int k, gns_dtype dt, gns_dtype compute) {
+  return dion3_batched_workspace_size(1, N, m, k, dt, compute);
 }
 
 // One Dion3 step over `batch` states: the rows are the top-k by score (S_in null; S
 // receives them) or the caller's set S_in.
-static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, long long ld, long long stride, int k,
+static int dion3_run(void* W, void* M, const void* G, gns_dtype dt, int batch, int N, int m, long long ld,
+                     long long stride, int k,
                      float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
                      const gns_schedule* sched, const int* S_in, int* S_out, void* O_out, void* workspace,
                      size_t ws_bytes, hipStream_t stream, const float* dev_scalars = nullptr) {
   if (batch < 0) return GNS_ERR_INVALID_ARG;
   if (batch == 0) return GNS_OK;
-  int st = check_dion3_matrix(W, N, m, ld);
+  int st = check_dion3_matrix(W, dt, N, m, ld);
   if (st) return st;
-  if ((st = check_dion3_matrix(M, N, m, ld))) return st;
-  if ((st = check_dion3_matrix(G, N, m, ld))) return st;
+  if ((st = check_dion3_matrix(M, dt, N, m, ld))) return st;
+  if ((st = check_dion3_matrix(G, dt, N, m, ld))) return st;
   if (batch > 1 && stride < (long long)N * ld) return GNS_ERR_INVALID_ARG;
   if (batch > 1 && stride % 8) return GNS_ERR_UNSUPPORTED;
   if ((!S_in && !S_out) || k < 1 || k > N) return GNS_ERR_INVALID_ARG;
@@ -693,13 +701,14 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
   if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
   if (O_out && !aligned16(O_out)) return GNS_ERR_UNSUPPORTED;
   // W, M and G must be distinct (each is read and written by different passes)
-  const size_t span = ((size_t)(batch - 1) * (size_t)(batch > 1 ? stride : 0) + (size_t)(N - 1) * ld + m) * 2;
+  const size_t es = esize(dt);
+  const size_t span = ((size_t)(batch - 1) * (size_t)(batch > 1 ? stride : 0) + (size_t)(N - 1) * ld + m) * es;
   if (overlaps(W, span, M, span) || overlaps(W, span, G, span) || overlaps(M, span, G, span))
     return GNS_ERR_INVALID_ARG;
   gns_schedule sch;
   if (sched) sch = *sched; else gns_default_schedule(&sch);
   if ((st = check_schedule(sch))) return st;
-  const Dion3Layout L = dion3_layout(workspace, batch, N, m, k, compute);
+  const Dion3Layout L = dion3_layout(workspace, batch, N, m, k, dt, compute);
   if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
 
@@ -715,28 +724,29 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
   // products (the submatrix X is never written; Algorithm 4 orthogonalises M[S, :]
   // itself), and the error feedback on M[S, :] runs with the weight update, after the
   // last read.  That needs the Gram path on a wide submatrix (a square one may fall
-  // back to standard NS, a tall one runs on a transpose), a row table that fits in LDS
-  // and a state addressable with 32-bit offsets; otherwise the rows are gathered into X
-  // first (the default: faster on MI355X, where the fresh copy sits in the Infinity
-  // Cache for the products that re-read it).
+  // back to standard NS, a tall one runs on a transpose), a bf16 state (the indexed
+  // products read bf16 rows), a row table that fits in LDS and a state addressable with
+  // 32-bit offsets; otherwise the rows are gathered into X first (the default: faster
+  // on MI355X, where the fresh copy sits in the Infinity Cache for the products that
+  // re-read it).
   const bool gram_path = kp < m || (kp == m && !sch.square_fallback);
-  const bool direct = sch.rows_in_place && gram_path && kp <= kMaxIndexedRows &&
-                      ((size_t)(N - 1) * ld + m) * 2 < (size_t(1) << 31);
-  // one batched Gram NS over the selected kp x m submatrices of every entry; its
-  // arguments are checked before anything is launched
-  NsCall c = direct ? make_call(M, GNS_BF16, ld, stride, O, GNS_BF16, m, kpm, batch, kp, m, compute, &sch, L.gns_ws,
+  const bool direct = sch.rows_in_place && dt == GNS_BF16 && gram_path && kp <= kMaxIndexedRows &&
+                      ((size_t)(N - 1) * ld + m) * es < (size_t(1) << 31);
+  // one batched Gram NS over the selected kp x m submatrices of every entry (input and
+  // output in the state type); its arguments are checked before anything is launched
+  const bool cast_x = dion3_casts_x(dt);
+  NsCall c = direct ? make_call(M, dt, ld, stride, O, dt, m, kpm, batch, kp, m, compute, &sch, L.gns_ws,
                                 L.gns_bytes, stream, nullptr)
-                    : make_call(L.X, GNS_BF16, m, kpm, O, GNS_BF16, m, kpm, batch, kp, m, compute, &sch, L.gns_ws,
-                                L.gns_bytes, stream, nullptr);
-  c.s_given = L.s;
+                    : make_call(cast_x ? L.Xc : L.X, cast_x ? compute : dt, m, kpm, O, dt, m, kpm, batch, kp, m,
+                                compute, &sch, L.gns_ws, L.gns_bytes, stream, nullptr);
+  c.s_given = cast_x ? nullptr : L.s;
   if ((st = check_ns(c))) return st;
-  if (O_out && (overlaps(O_out, (size_t)batch * km * 2, workspace, L.bytes) ||
-                overlaps(O_out, (size_t)batch * km * 2, W, span) || overlaps(O_out, (size_t)batch * km * 2, M, span) ||
-                overlaps(O_out, (size_t)batch * km * 2, G, span)))
+  const size_t o_bytes = (size_t)batch * km * es;
+  if (O_out && (overlaps(O_out, o_bytes, workspace, L.bytes) || overlaps(O_out, o_bytes, W, span) ||
+                overlaps(O_out, o_bytes, M, span) || overlaps(O_out, o_bytes, G, span)))
     return GNS_ERR_INVALID_ARG;
 
-  uint16_t* Mh = (uint16_t*)M;
-  HIP_OK(launch_accumulate_score(Mh, (const uint16_t*)G, batch, N, m, ld, stride, score_norm, L.score, L.sumsq, stream));
+  HIP_OK(launch_accumulate_score(M, G, dt, batch, N, m, ld, stride, score_norm, L.score, L.sumsq, stream));
   const int* S = S_in;
   if (!S_in) {
     HIP_OK(launch_topk(L.score, batch, N, k, S_out, stream));
@@ -745,40 +755,42 @@ static int dion3_run(void* W, void* M, const void* G, int batch, int N, int m, l
   if (direct) {
     c.rows = S; c.rows_valid = k; c.rows_stride = k; c.src_rows = N;
   } else {
-    HIP_OK(launch_gather_feedback(Mh, batch, N, m, ld, stride, S, k, kp, mu, dev_scalars, (uint16_t*)L.X, m, stream));
+    HIP_OK(launch_gather_feedback(M, dt, batch, N, m, ld, stride, S, k, kp, mu, dev_scalars, L.X, m, stream));
   }
   HIP_OK(launch_selected_sumsq(L.sumsq, S, batch, k, N, sch.eps, L.s, stream));
+  if (cast_x)
+    HIP_OK(launch_cast_scale(L.X, dt, m, kpm, L.Xc, compute, m, kpm, batch, kp, m, 1.0f, L.s, 1, stream));
   if ((st = run_ns(c, true))) return st;
   if (O_out && O != O_out)
-    HIP_OK(launch_cast_scale(O, GNS_BF16, m, kpm, O_out, GNS_BF16, m, km, batch, k, m, 1.0f, nullptr, 0, stream));
-  HIP_OK(launch_apply_update((uint16_t*)W, batch, N, m, ld, stride, S, k, O, GNS_BF16, m, kpm, lr, weight_decay,
-                             dev_scalars, stream, direct ? Mh : nullptr, mu));
+    HIP_OK(launch_cast_scale(O, dt, m, kpm, O_out, dt, m, km, batch, k, m, 1.0f, nullptr, 0, stream));
+  HIP_OK(launch_apply_update(W, dt, batch, N, m, ld, stride, S, k, O, dt, m, kpm, lr, weight_decay, dev_scalars,
+                             stream, direct ? M : nullptr, mu));
   return GNS_OK;
 }
 
-int dion3_step_batched(void* W, void* M, const void* G, int batch, int N, int m, long long ld, long long stride, int k,
-                       float lr, float weight_decay, float mu, int score_norm, gns_dtype compute,
-                       const gns_schedule* sched, int* S_out, void* O_out, void* workspace, size_t ws_bytes,
-                       hipStream_t stream) {
+int dion3_step_batched(void* W, void* M, const void* G, gns_dtype dt, int batch, int N, int m, long long ld,
+                       long long stride, int k, float lr, float weight_decay, float mu, int score_norm,
+                       gns_dtype compute, const gns_schedule* sched, int* S_out, void* O_out, void* workspace,
+                       size_t ws_bytes, hipStream_t stream) {
   if (!S_out) return GNS_ERR_INVALID_ARG;
-  return dion3_run(W, M, G, batch, N, m, ld, stride, k, lr, weight_decay, mu, score_norm, compute, sched, nullptr,
-                   S_out, O_out, workspace, ws_bytes, stream);
+  return dion3_run(W, M, G, dt, batch, N, m, ld, stride, k, lr, weight_decay, mu, score_norm, compute, sched,
+                   nullptr, S_out, O_out, workspace, ws_bytes, stream);
 }
 
-int dion3_step(void* W, void* M, const void* G, int N, int m, long long ld, int k, float lr, float weight_decay,
-               float mu, int score_norm, gns_dtype compute, const gns_schedule* sched, int* S_out, void* O_out,
-               void* workspace, size_t ws_bytes, hipStream_t stream) {
-  return dion3_step_batched(W, M, G, 1, N, m, ld, (long long)N * ld, k, lr, weight_decay, mu, score_norm, compute,
-                            sched, S_out, O_out, workspace, ws_bytes, stream);
+int dion3_step(void* W, void* M, const void* G, gns_dtype dt, int N, int m, long long ld, int k, float lr,
+               float weight_decay, float mu, int score_norm, gns_dtype compute, const gns_schedule* sched, int* S_out,
+               void* O_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return dion3_step_batched(W, M, G, dt, 1, N, m, ld, (long long)N * ld, k, lr, weight_decay, mu, score_norm,
+                            compute, sched, S_out, O_out, workspace, ws_bytes, stream);
 }
 
-int dion3_step_dev_scalars(void* W, void* M, const void* G, int N, int m, long long ld, int k,
+int dion3_step_dev_scalars(void* W, void* M, const void* G, gns_dtype dt, int N, int m, long long ld, int k,
                            const float* lr_wd_mu, int score_norm, gns_dtype compute, const gns_schedule* sched,
                            int* S_out, void* O_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!S_out || !lr_wd_mu) return GNS_ERR_INVALID_ARG;
   if ((uintptr_t)lr_wd_mu & 3u) return GNS_ERR_UNSUPPORTED;
   // the host scalars are placeholders (finite, as checked); the kernels read the device values
-  return dion3_run(W, M, G, 1, N, m, ld, (long long)N * ld, k, 0.0f, 0.0f, 0.0f, score_norm, compute, sched,
+  return dion3_run(W, M, G, dt, 1, N, m, ld, (long long)N * ld, k, 0.0f, 0.0f, 0.0f, score_norm, compute, sched,
                    nullptr, S_out, O_out, workspace, ws_bytes, stream, lr_wd_mu);
 }
 
@@ -789,11 +801,11 @@ struct Dion3ColsLayout {
   double *part_s, *part_q, *score, *sumsq;
   uint8_t* mark;
   float* s;
-  void *Xt, *O, *gns_ws;
+  void *Xt, *Xtc, *O, *gns_ws;
   size_t gns_bytes, bytes;
 };
 
-static Dion3ColsLayout dion3_cols_layout(void* base, int N, int m, int k, gns_dtype cdt) {
+static Dion3ColsLayout dion3_cols_layout(void* base, int N, int m, int k, gns_dtype dt, gns_dtype cdt) {
   Carver c{reinterpret_cast<uint8_t*>(base), 0};
   Dion3ColsLayout L{};
   const size_t parts = dion3_cols_partials(N) * (size_t)m;
@@ -804,26 +816,27 @@ static Dion3ColsLayout dion3_cols_layout(void* base, int N, int m, int k, gns_dt
   L.mark = (uint8_t*)c.take((size_t)m);
   L.s = (float*)c.take(sizeof(float));
   const int kp = padded_rows(k);
-  L.Xt = c.take((size_t)kp * N * 2);
-  L.O = c.take((size_t)kp * N * 2);
+  L.Xt = c.take((size_t)kp * N * esize(dt));
+  L.Xtc = dion3_casts_x(dt) ? c.take((size_t)kp * N * esize(cdt)) : nullptr;
+  L.O = c.take((size_t)kp * N * esize(dt));
   L.gns_bytes = ns_workspace_bytes(1, kp, N, cdt);
   L.gns_ws = c.take(L.gns_bytes);
   L.bytes = c.off;
   return L;
 }
 
-size_t dion3_cols_workspace_size(int N, int m, int k, gns_dtype compute) {
-  if (N < 1 || m < 1 || k < 1 || !valid_dtype(compute)) return 0;
-  return dion3_cols_layout(nullptr, N, m, k, compute).bytes;
+size_t dion3_cols_workspace_size(int N, int m, int k, gns_dtype dt, gns_dtype compute) {
+  if (N < 1 || m < 1 || k < 1 || !valid_dtype(dt) || !valid_dtype(compute)) return 0;
+  return dion3_cols_layout(nullptr, N, m, k, dt, compute).bytes;
 }
 
-int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld, int k, float lr, float weight_decay,
-                    float mu, int score_norm, gns_dtype compute, const gns_schedule* sched, int* S_out, void* O_out,
-                    void* workspace, size_t ws_bytes, hipStream_t stream) {
-  int st = check_dion3_matrix(W, N, m, ld);
+int dion3_step_cols(void* W, void* M, const void* G, gns_dtype dt, int N, int m, long long ld, int k, float lr,
+                    float weight_decay, float mu, int score_norm, gns_dtype compute, const gns_schedule* sched,
+                    int* S_out, void* O_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dion3_matrix(W, dt, N, m, ld);
   if (st) return st;
-  if ((st = check_dion3_matrix(M, N, m, ld))) return st;
-  if ((st = check_dion3_matrix(G, N, m, ld))) return st;
+  if ((st = check_dion3_matrix(M, dt, N, m, ld))) return st;
+  if ((st = check_dion3_matrix(G, dt, N, m, ld))) return st;
   if (!S_out || k < 1 || k > m) return GNS_ERR_INVALID_ARG;
   if (score_norm != 1 && score_norm != 2) return GNS_ERR_INVALID_ARG;
   if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu)) return GNS_ERR_INVALID_ARG;
@@ -831,13 +844,14 @@ int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld,
   if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
   if (N % 8) return GNS_ERR_UNSUPPORTED;   // N is the row length of X^T and O
   if (O_out && !aligned16(O_out)) return GNS_ERR_UNSUPPORTED;
-  const size_t span = ((size_t)(N - 1) * ld + m) * 2;
+  const size_t es = esize(dt);
+  const size_t span = ((size_t)(N - 1) * ld + m) * es;
   if (overlaps(W, span, M, span) || overlaps(W, span, G, span) || overlaps(M, span, G, span))
     return GNS_ERR_INVALID_ARG;
   gns_schedule sch;
   if (sched) sch = *sched; else gns_default_schedule(&sch);
   if ((st = check_schedule(sch))) return st;
-  const Dion3ColsLayout L = dion3_cols_layout(workspace, N, m, k, compute);
+  const Dion3ColsLayout L = dion3_cols_layout(workspace, N, m, k, dt, compute);
   if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
 
@@ -847,35 +861,35 @@ int dion3_step_cols(void* W, void* M, const void* G, int N, int m, long long ld,
   const long long kN = (long long)k * N, kpN = (long long)kp * N;
   // the kp x N transpose of the selected columns: Gram NS iterates on its short side;
   // its arguments are checked before anything is launched
-  NsCall c = make_call(L.Xt, GNS_BF16, N, kpN, O, GNS_BF16, N, kpN, 1, kp, N, compute, &sch, L.gns_ws,
-                       L.gns_bytes, stream, nullptr);
-  c.s_given = L.s;
+  const bool cast_x = dion3_casts_x(dt);
+  NsCall c = make_call(cast_x ? L.Xtc : L.Xt, cast_x ? compute : dt, N, kpN, O, dt, N, kpN, 1, kp, N, compute, &sch,
+                       L.gns_ws, L.gns_bytes, stream, nullptr);
+  c.s_given = cast_x ? nullptr : L.s;
   if ((st = check_ns(c))) return st;
-  if (O_out && (overlaps(O_out, (size_t)kN * 2, workspace, L.bytes) || overlaps(O_out, (size_t)kN * 2, W, span) ||
-                overlaps(O_out, (size_t)kN * 2, M, span) || overlaps(O_out, (size_t)kN * 2, G, span)))
+  const size_t o_bytes = (size_t)kN * es;
+  if (O_out && (overlaps(O_out, o_bytes, workspace, L.bytes) || overlaps(O_out, o_bytes, W, span) ||
+                overlaps(O_out, o_bytes, M, span) || overlaps(O_out, o_bytes, G, span)))
     return GNS_ERR_INVALID_ARG;
 
-  uint16_t* Mh = (uint16_t*)M;
-  HIP_OK(launch_accumulate_colscore(Mh, (const uint16_t*)G, N, m, ld, score_norm, L.part_s, L.part_q, L.score,
-                                    L.sumsq, stream));
+  HIP_OK(launch_accumulate_colscore(M, G, dt, N, m, ld, score_norm, L.part_s, L.part_q, L.score, L.sumsq, stream));
   HIP_OK(launch_topk(L.score, 1, m, k, S_out, stream));
-  HIP_OK(launch_gather_cols_feedback(Mh, N, m, ld, S_out, k, kp, mu, (uint16_t*)L.Xt, N, stream));
+  HIP_OK(launch_gather_cols_feedback(M, dt, N, m, ld, S_out, k, kp, mu, L.Xt, N, stream));
   HIP_OK(launch_selected_sumsq(L.sumsq, S_out, 1, k, m, sch.eps, L.s, stream));
+  if (cast_x) HIP_OK(launch_cast_scale(L.Xt, dt, N, kpN, L.Xtc, compute, N, kpN, 1, kp, N, 1.0f, L.s, 1, stream));
   if ((st = run_ns(c, true))) return st;
   if (O_out && O != O_out)
-    HIP_OK(launch_cast_scale(O, GNS_BF16, N, kpN, O_out, GNS_BF16, N, kN, 1, k, N, 1.0f, nullptr, 0, stream));
-  HIP_OK(launch_update_cols((uint16_t*)W, N, m, ld, S_out, k, (const uint16_t*)O, N, lr, weight_decay, L.mark,
-                            stream));
+    HIP_OK(launch_cast_scale(O, dt, N, kpN, O_out, dt, N, kN, 1, k, N, 1.0f, nullptr, 0, stream));
+  HIP_OK(launch_update_cols(W, dt, N, m, ld, S_out, k, O, N, lr, weight_decay, L.mark, stream));
   return GNS_OK;
 }
 
-int dion3_step_rows(void* W, void* M, const void* G, int N, int m, long long ld, const int* S, int k, float lr,
-                    float weight_decay, float mu, gns_dtype compute, const gns_schedule* sched, void* O_out,
+int dion3_step_rows(void* W, void* M, const void* G, gns_dtype dt, int N, int m, long long ld, const int* S, int k,
+                    float lr, float weight_decay, float mu, gns_dtype compute, const gns_schedule* sched, void* O_out,
                     void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!S) return GNS_ERR_INVALID_ARG;
   // the sums of squares of the rows (score_norm 2) give the submatrix's Frobenius norm
-  return dion3_run(W, M, G, 1, N, m, ld, (long long)N * ld, k, lr, weight_decay, mu, 2, compute, sched, S, nullptr,
-                   O_out, workspace, ws_bytes, stream);
+  return dion3_run(W, M, G, dt, 1, N, m, ld, (long long)N * ld, k, lr, weight_decay, mu, 2, compute, sched, S,
+                   nullptr, O_out, workspace, ws_bytes, stream);
 }
 
 // Muon step workspace: the row sums of squares and the scale of each matrix, U (the
@@ -911,10 +925,10 @@ int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, 
                       const gns_schedule* sched, void* O_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (batch < 0) return GNS_ERR_INVALID_ARG;
   if (batch == 0) return GNS_OK;
-  int st = check_dion3_matrix(W, n, m, ld);
+  int st = check_dion3_matrix(W, GNS_BF16, n, m, ld);
   if (st) return st;
-  if ((st = check_dion3_matrix(M, n, m, ld))) return st;
-  if ((st = check_dion3_matrix(G, n, m, ld))) return st;
+  if ((st = check_dion3_matrix(M, GNS_BF16, n, m, ld))) return st;
+  if ((st = check_dion3_matrix(G, GNS_BF16, n, m, ld))) return st;
   if (batch > 1 && stride < (long long)n * ld) return GNS_ERR_INVALID_ARG;
   if (batch > 1 && stride % 8) return GNS_ERR_UNSUPPORTED;
   if (nesterov != 0 && nesterov != 1) return GNS_ERR_INVALID_ARG;

@@ -96,22 +96,24 @@ hipError_t launch_transpose(const void* X, gns_dtype dt, long long ldx, long lon
 
 // Dion3 element-wise kernels (dion3.hip), over `batch` same-shape N x m matrices whose
 // entries are `stride` elements apart; per-entry vectors (score, sumsq: N; S: k;
-// X, O: k rows; s: 1) are packed back to back.
-hipError_t launch_accumulate_score(uint16_t* M, const uint16_t* G, int batch, int N, int m, long long ld,
+// X, O: k rows; s: 1) are packed back to back.  The state (W, M, G, and X, which
+// holds rows of M) has the element type dt: bf16, f16 or fp32.
+hipError_t launch_accumulate_score(void* M, const void* G, gns_dtype dt, int batch, int N, int m, long long ld,
                                    long long stride, int score_norm, double* score, double* sumsq, hipStream_t s);
 hipError_t launch_topk(const double* score, int batch, int N, int k, int* S, hipStream_t s);
 // dev_scalars (nullable): device float[3] = {lr, wd, mu} read when the kernel runs,
 // replacing the host values.
 // X holds kx >= k rows per batch entry (rows k .. kx-1 are written as zeros).
-hipError_t launch_gather_feedback(uint16_t* M, int batch, int N, int m, long long ld, long long stride, const int* S,
-                                  int k, int kx, float mu, const float* dev_scalars, uint16_t* X, long long ldx,
-                                  hipStream_t s);
-// O: k rows (row stride ldo) per batch entry, entries so elements apart.
-// Mfb (nullable): also apply the error feedback M[S] <- bf16(mu M[S]) to the same rows
-// (M with W's row stride and batch stride).
-hipError_t launch_apply_update(uint16_t* W, int batch, int N, int m, long long ld, long long stride, const int* S, int k,
-                               const void* O, gns_dtype o_dtype, long long ldo, long long so, float lr, float wd,
-                               const float* dev_scalars, hipStream_t s, uint16_t* Mfb = nullptr, float mu = 0.0f);
+hipError_t launch_gather_feedback(void* M, gns_dtype dt, int batch, int N, int m, long long ld, long long stride,
+                                  const int* S, int k, int kx, float mu, const float* dev_scalars, void* X,
+                                  long long ldx, hipStream_t s);
+// O: k rows (row stride ldo, element type o_dtype) per batch entry, entries so
+// elements apart.  Mfb (nullable): also apply the error feedback M[S] <- fl(mu M[S]) to
+// the same rows (M with W's row stride, batch stride and element type).
+hipError_t launch_apply_update(void* W, gns_dtype dt, int batch, int N, int m, long long ld, long long stride,
+                               const int* S, int k, const void* O, gns_dtype o_dtype, long long ldo, long long so,
+                               float lr, float wd, const float* dev_scalars, hipStream_t s, void* Mfb = nullptr,
+                               float mu = 0.0f);
 // Largest row count of an indexed rectangular product (its row table sits in LDS).
 constexpr int kMaxIndexedRows = 8192;
 // s[b] = 1 / (sqrt(sum_i sumsq[b][S[b][i]]) + eps): the Frobenius scale of the rows S.
@@ -122,15 +124,16 @@ hipError_t launch_selected_sumsq(const double* sumsq, const int* S, int batch, i
 // Partial column sums: dion3_cols_partials(N) blocks of m doubles each, for the score
 // and for the sum of squares.
 size_t dion3_cols_partials(int N);
-hipError_t launch_accumulate_colscore(uint16_t* M, const uint16_t* G, int N, int m, long long ld, int score_norm,
-                                      double* part_s, double* part_q, double* score, double* sumsq, hipStream_t s);
-// Xt (kx x N, row stride ldx): row j < k = column S[j] of M, rows k .. kx-1 zero; then
-// M[:, S] <- bf16(mu M[:, S])
-hipError_t launch_gather_cols_feedback(uint16_t* M, int N, int m, long long ld, const int* S, int k, int kx,
-                                       float mu, uint16_t* Xt, long long ldx, hipStream_t s);
-// W[:, S[j]] <- bf16(d W - lr O[j, :]^T); with wd != 0 every other column decays (mark:
-// m bytes of scratch)
-hipError_t launch_update_cols(uint16_t* W, int N, int m, long long ld, const int* S, int k, const uint16_t* O,
+hipError_t launch_accumulate_colscore(void* M, const void* G, gns_dtype dt, int N, int m, long long ld,
+                                      int score_norm, double* part_s, double* part_q, double* score, double* sumsq,
+                                      hipStream_t s);
+// Xt (kx x N, row stride ldx, type dt): row j < k = column S[j] of M, rows k .. kx-1
+// zero; then M[:, S] <- fl(mu M[:, S])
+hipError_t launch_gather_cols_feedback(void* M, gns_dtype dt, int N, int m, long long ld, const int* S, int k, int kx,
+                                       float mu, void* Xt, long long ldx, hipStream_t s);
+// W[:, S[j]] <- fl(d W - lr O[j, :]^T) (O: type dt); with wd != 0 every other column
+// decays (mark: m bytes of scratch)
+hipError_t launch_update_cols(void* W, gns_dtype dt, int N, int m, long long ld, const int* S, int k, const void* O,
                               long long ldo, float lr, float wd, uint8_t* mark, hipStream_t s);
 
 }  // namespace gns

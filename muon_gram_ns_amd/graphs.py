@@ -76,9 +76,9 @@ def graphed_dion3_step(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, 
     torch = _lib._torch()
     N, m, _ = _lib._rows(W)
     S = torch.empty(k, dtype=torch.int32, device=W.device)
-    O = torch.empty((k, m), dtype=torch.bfloat16, device=W.device) if return_O else None
-    ws = torch.empty(max(int(_lib.lib.dion3_workspace_size(N, m, k, _lib.code_of(compute))), 256),
-                     dtype=torch.uint8, device=W.device)
+    O = torch.empty((k, m), dtype=W.dtype, device=W.device) if return_O else None
+    ws = torch.empty(max(int(_lib.lib.dion3_workspace_size(N, m, k, _lib.dtype_code(W), _lib.code_of(compute))),
+                         256), dtype=torch.uint8, device=W.device)
     sched = schedule if schedule is not None else _lib.default_schedule()
     scalars = None
     if device_scalars:

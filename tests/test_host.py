@@ -99,53 +99,64 @@ def test_gemm_and_dion3_validation():
                        FAKE * 2, 64, 0, BF16, None) == INVALID
     # dion3: k > N, bad norm, short workspace
     sched = gns.default_schedule()
-    args = lambda k, norm=1, wsb=1 << 40: (FAKE, FAKE * 2, FAKE * 3, 64, 256, 256, k, 0.02, 0.0, 0.95, norm, F16,
-                                            ctypes.byref(sched), FAKE * 4, None, FAKE * 5, wsb, None)
+    args = lambda k, norm=1, wsb=1 << 40, dt=BF16: (FAKE, FAKE * 2, FAKE * 3, dt, 64, 256, 256, k, 0.02, 0.0, 0.95,
+                                                    norm, F16, ctypes.byref(sched), FAKE * 4, None, FAKE * 5, wsb,
+                                                    None)
     assert L.dion3_step(*args(65)) == INVALID
     assert L.dion3_step(*args(16, norm=3)) == INVALID
     assert L.dion3_step(*args(16, wsb=8)) == WS
+    # the state dtype: bf16, f16 and f32 reach the workspace check; any other value is
+    # refused; an f32 state needs the larger workspace
+    assert L.dion3_step(*args(16, wsb=8, dt=F16)) == WS
+    assert L.dion3_step(*args(16, wsb=8, dt=F32)) == WS
+    assert L.dion3_step(*args(16, dt=7)) == INVALID
+    assert L.dion3_workspace_size(64, 256, 16, F32, F16) > L.dion3_workspace_size(64, 256, 16, BF16, F16)
+    assert L.dion3_workspace_size(64, 256, 16, F16, F16) == L.dion3_workspace_size(64, 256, 16, BF16, F16)
+    assert L.dion3_workspace_size(64, 256, 16, 7, F16) == 0
     # batched dion3: empty batch, short batch stride, aliased state, short workspace
     bargs = lambda B, stride, W=FAKE, M=FAKE * 8, G=FAKE * 16, wsb=1 << 40: (
-        W, M, G, B, 64, 256, 256, stride, 16, 0.02, 0.0, 0.95, 1, F16, ctypes.byref(sched), FAKE * 30, None,
+        W, M, G, BF16, B, 64, 256, 256, stride, 16, 0.02, 0.0, 0.95, 1, F16, ctypes.byref(sched), FAKE * 30, None,
         FAKE * 40, wsb, None)
     assert L.dion3_step_batched(*bargs(0, 0)) == OK
     assert L.dion3_step_batched(*bargs(2, 64 * 256 - 8)) == INVALID
     assert L.dion3_step_batched(*bargs(2, 64 * 256, M=FAKE + 64 * 256 * 2)) == INVALID   # M overlaps W's 2nd entry
     assert L.dion3_step_batched(*bargs(2, 64 * 256, wsb=8)) == WS
-    assert L.dion3_batched_workspace_size(2, 64, 256, 16, F16) > L.dion3_workspace_size(64, 256, 16, F16)
+    assert L.dion3_batched_workspace_size(2, 64, 256, 16, BF16, F16) > L.dion3_workspace_size(64, 256, 16, BF16,
+                                                                                               F16)
     # dion3 on a caller-chosen row set: null S, k > N, short workspace, aliasing; any k is
     # accepted (the submatrix is padded to whole 8-row groups), so k = 12 reaches the
     # workspace check
-    rargs = lambda S=FAKE * 30, k=16, W=FAKE, wsb=1 << 40: (W, FAKE * 8, FAKE * 16, 64, 256, 256, S, k, 0.02, 0.0,
-                                                           0.95, F16, ctypes.byref(sched), None, FAKE * 40, wsb,
+    rargs = lambda S=FAKE * 30, k=16, W=FAKE, wsb=1 << 40: (W, FAKE * 8, FAKE * 16, BF16, 64, 256, 256, S, k, 0.02,
+                                                           0.0, 0.95, F16, ctypes.byref(sched), None, FAKE * 40, wsb,
                                                            None)
     assert L.dion3_step_rows(*rargs(S=None)) == INVALID
     assert L.dion3_step_rows(*rargs(k=72)) == INVALID
     assert L.dion3_step_rows(*rargs(k=12, wsb=8)) == WS
-    assert L.dion3_workspace_size(64, 256, 12, F16) == L.dion3_workspace_size(64, 256, 16, F16)
+    assert L.dion3_workspace_size(64, 256, 12, BF16, F16) == L.dion3_workspace_size(64, 256, 16, BF16, F16)
     assert L.dion3_step_rows(*rargs(wsb=8)) == WS
     assert L.dion3_step_rows(*rargs(W=FAKE * 8)) == INVALID                # W is M
     # dion3 with device scalars: null scalars, misaligned scalars, null S
-    dargs = lambda sc=FAKE * 50, S=FAKE * 30: (FAKE, FAKE * 8, FAKE * 16, 64, 256, 256, 16, sc, 1, F16,
+    dargs = lambda sc=FAKE * 50, S=FAKE * 30: (FAKE, FAKE * 8, FAKE * 16, BF16, 64, 256, 256, 16, sc, 1, F16,
                                               ctypes.byref(sched), S, None, FAKE * 40, 1 << 40, None)
     assert L.dion3_step_dev_scalars(*dargs(sc=None)) == INVALID
     assert L.dion3_step_dev_scalars(*dargs(sc=FAKE * 50 + 2)) == UNSUP
     assert L.dion3_step_dev_scalars(*dargs(S=None)) == INVALID
     # dion3 on columns: k > m, N not a multiple of 8, short workspace
-    cargs = lambda k=16, N=64, wsb=1 << 40: (FAKE, FAKE * 8, FAKE * 16, N, 256, 256, k, 0.02, 0.0, 0.95, 1, F16,
-                                            ctypes.byref(sched), FAKE * 30, None, FAKE * 40, wsb, None)
+    cargs = lambda k=16, N=64, wsb=1 << 40: (FAKE, FAKE * 8, FAKE * 16, BF16, N, 256, 256, k, 0.02, 0.0, 0.95, 1,
+                                            F16, ctypes.byref(sched), FAKE * 30, None, FAKE * 40, wsb, None)
     assert L.dion3_step_cols(*cargs(k=264)) == INVALID
     assert L.dion3_step_cols(*cargs(N=60)) == UNSUP
     assert L.dion3_step_cols(*cargs(wsb=8)) == WS
-    assert L.dion3_cols_workspace_size(64, 256, 16, F16) > 2 * 16 * 64 * 2 + 2 * 256 * 8
+    assert L.dion3_cols_workspace_size(64, 256, 16, BF16, F16) > 2 * 16 * 64 * 2 + 2 * 256 * 8
+    assert L.dion3_cols_workspace_size(64, 256, 16, F32, F16) > L.dion3_cols_workspace_size(64, 256, 16, BF16, F16)
     # O_out overlapping the workspace or the state is rejected before anything runs
     # (without a GPU, a launch would report GNS_ERR_HIP instead)
-    oargs = lambda O: (FAKE, FAKE * 8, FAKE * 16, 64, 256, 256, 16, 0.02, 0.0, 0.95, 1, F16, ctypes.byref(sched),
-                       FAKE * 30, O, FAKE * 40, 1 << 30, None)
+    oargs = lambda O: (FAKE, FAKE * 8, FAKE * 16, BF16, 64, 256, 256, 16, 0.02, 0.0, 0.95, 1, F16,
+                       ctypes.byref(sched), FAKE * 30, O, FAKE * 40, 1 << 30, None)
     assert L.dion3_step(*oargs(FAKE * 40 + 4096)) == INVALID            # inside the workspace
     assert L.dion3_step(*oargs(FAKE * 8)) == INVALID                    # O is M
-    coargs = lambda O: (FAKE, FAKE * 8, FAKE * 16, 64, 256, 256, 16, 0.02, 0.0, 0.95, 1, F16, ctypes.byref(sched),
-                        FAKE * 30, O, FAKE * 40, 1 << 30, None)
+    coargs = lambda O: (FAKE, FAKE * 8, FAKE * 16, BF16, 64, 256, 256, 16, 0.02, 0.0, 0.95, 1, F16,
+                        ctypes.byref(sched), FAKE * 30, O, FAKE * 40, 1 << 30, None)
     assert L.dion3_step_cols(*coargs(FAKE * 40 + 4096)) == INVALID
     assert L.dion3_step_cols(*coargs(FAKE)) == INVALID                  # O is W
     assert L.dion3_select_topk(FAKE, 10, 11, FAKE, None) == INVALID
@@ -200,7 +211,7 @@ def test_workspace_sizes_grow_with_problem():
     assert 0 < a < b and a < c
     # 5 n x n iterates + 2 X-shaped buffers in fp16, plus small scalars
     assert a >= (5 * 1024 * 1024 + 2 * 1024 * 4096) * 2
-    assert L.dion3_workspace_size(8192, 28672, 2048, F16) > 2 * 2048 * 28672 * 2
+    assert L.dion3_workspace_size(8192, 28672, 2048, BF16, F16) > 2 * 2048 * 28672 * 2
 
 
 def test_pages_flop_savings():
