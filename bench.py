@@ -495,6 +495,17 @@ def dion3_figures(args, w, gns, F, torch, fractions=(0.25, 0.125)):
         res[f"f={f}"] = {"k": k, "ms_per_step": round(t * 1e3, 4), "steps_per_s": round(1.0 / t, 3),
                          "gram_ns_tflops_algorithmic": round(F.gram_schedule(k, m) / t / 1e12, 2),
                          "rows_in_place_ms_per_step": round(t_in * 1e3, 4)}
+    if 0.25 in fractions:
+        # the f = 1/4 step on an fp32 state (W, M, G in fp32; the submatrix reaches the
+        # 16-bit iterates through a scaled copy), and its accumulate-and-score pass
+        k = math.ceil(0.25 * N)
+        W32, G32, M32 = W.float(), G.float(), M.float()
+        t32 = timed(lambda: gns.dion3_step(W32, M32, G32, k, 0.02, 0.0, 0.95, score_norm=2, compute=args.compute),
+                    reps)
+        t32_acc = timed(lambda: gns.dion3_accumulate_score(M32, G32, 2), reps)
+        res["f=0.25"]["fp32_state_ms_per_step"] = round(t32 * 1e3, 4)
+        res["f=0.25"]["fp32_state_accumulate_GB_s"] = round(3.0 * N * m * 4 / t32_acc / 1e9, 1)
+        del W32, G32, M32
     t_acc = timed(lambda: gns.dion3_accumulate_score(M, G, 2), reps)
     b_acc = 3.0 * N * m * 2
     res["roofline"] = {"bound": "hbm", "kernel": "accumulate_score_kernel", "achieved": round(b_acc / t_acc / 1e9, 1),
@@ -700,6 +711,18 @@ def bench_dion3(args, w):
               "select_topk": {"us": round(t_sel * 1e6, 2)},
               "gather_feedback": {"us": round(t_gat * 1e6, 2), "bytes": b_gat, "GB_s": round(b_gat / t_gat / 1e9, 1)},
               "apply_update": {"us": round(t_upd * 1e6, 2), "bytes": b_upd, "GB_s": round(b_upd / t_upd / 1e9, 1)}}
+    # the f = 1/4 step and its accumulate pass on an fp32 state (W, M, G in fp32)
+    W32, G32, M32 = W.float(), G.float(), M.float()
+    k = N // 4
+    step32 = lambda: gns.dion3_step(W32, M32, G32, k, 0.02, 0.0, 0.95, score_norm=2, compute=args.compute)
+    for _ in range(args.warmup):
+        step32()
+    t32 = timed(step32, args.steps)
+    t32_acc = timed(lambda: gns.dion3_accumulate_score(M32, G32, 2), reps)
+    fp32_state = {"k": k, "ms_per_step": round(t32 * 1e3, 4),
+                  "accumulate_score": {"us": round(t32_acc * 1e6, 2), "bytes": 2 * b_acc,
+                                       "GB_s": round(2 * b_acc / t32_acc / 1e9, 1)}}
+    del W32, G32, M32
     ms = res[0.25]["ms_per_step"]
     roof = {"bound": "hbm", "kernel": "accumulate_score_kernel", "achieved": pieces["accumulate_score"]["GB_s"],
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pieces["accumulate_score"]["GB_s"] / PEAK_HBM_GBS, 4),
@@ -716,6 +739,7 @@ def bench_dion3(args, w):
                       "config": {"workload": w.name, "N": N, "m": m, "score": "l2", "mu": 0.95, "wd": 0.0,
                                  "fractions": res},
                       "hbm_pieces_k2048": pieces, "hbm_reference_same_tensors": reference,
+                      "fp32_state_f_quarter": fp32_state,
                       "megabatch_f_quarter": mega, "tall_state_columns_vs_rows": tall,
                       "roofline": roof, "cpu_baseline": cpu}), flush=True)
 

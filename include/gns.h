@@ -319,8 +319,9 @@ int dion3_step_dev_scalars(void* W, void* M, const void* G, gns_dtype dt, int N,
                            const gns_schedule* sched, int* S_out, void* O_out,
                            void* workspace, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes needed by muon_step_batched (0 for invalid arguments). */
-size_t muon_workspace_size(int batch, int n, int m, gns_dtype compute, int nesterov);
+/* Workspace bytes needed by muon_step_batched on a state of type dt (0 for invalid
+ * arguments). */
+size_t muon_workspace_size(int batch, int n, int m, gns_dtype dt, gns_dtype compute, int nesterov);
 
 /* One Muon step on `batch` same-shape n x m matrices ("Muon: Orthogonalized Momentum
  * and Why It Trains LLMs 2x Cheaper", the step listed after "Doing an SVD without an
@@ -335,19 +336,22 @@ size_t muon_workspace_size(int batch, int n, int m, gns_dtype compute, int neste
  * scale == 0 selects 0.2 sqrt(max(n, m)) (fp32), which matches the update's RMS to
  * AdamW's; a negative scale is GNS_ERR_INVALID_ARG.  Dion3 with every row selected is
  * this step without the lookahead.
- * W, M, G: device bf16 [batch][n][ld], entry b at offset b * stride elements
- * (stride >= n * ld when batch > 1); they must not overlap.  Each stored value (M, U,
- * O, W) is rounded once to bf16 from fp32 arithmetic done op by op.
- * O_out: nullable device bf16 [batch][n][m] (contiguous) that receives O; it must not
- * overlap W, M, G or the workspace.  Workspace: muon_workspace_size(batch, n, m,
- * compute, nesterov) bytes, 16-byte aligned, owned by the caller.  Asynchronous on
+ * W, M, G: device [batch][n][ld] of the state type dt (GNS_BF16, GNS_F16 or GNS_F32,
+ * one type for the three), entry b at offset b * stride elements (stride >= n * ld
+ * when batch > 1); they must not overlap.  Each stored value (M, U, O, W) is rounded
+ * once to dt from fp32 arithmetic done op by op; an fp32 U reaches the 16-bit iterates
+ * through a copy scaled by its Frobenius scale and rounded once to the iterate type.
+ * O_out: nullable device [batch][n][m] of type dt (contiguous) that receives O; it must
+ * not overlap W, M, G or the workspace.  Workspace: muon_workspace_size(batch, n, m,
+ * dt, compute, nesterov) bytes, 16-byte aligned, owned by the caller.  Asynchronous on
  * `stream`; no host synchronisation.
  * Errors (nothing is launched): GNS_ERR_INVALID_ARG for a null matrix, n or m < 1,
  * ld < m, a short stride, overlapping buffers, nesterov not 0 or 1, a negative
  * scale, or a non-finite scalar; GNS_ERR_UNSUPPORTED for n, m, ld or stride not a
- * multiple of 8, a pointer not 16-byte aligned, or compute = GNS_F32; GNS_ERR_WORKSPACE for a short or null
- * workspace; GNS_ERR_HIP for a launch failure (gns_last_error() describes it). */
-int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, long long ld,
+ * multiple of 8, a pointer not 16-byte aligned, or compute = GNS_F32; GNS_ERR_WORKSPACE
+ * for a short or null workspace; GNS_ERR_HIP for a launch failure (gns_last_error()
+ * describes it). */
+int muon_step_batched(void* W, void* M, const void* G, gns_dtype dt, int batch, int n, int m, long long ld,
                       long long stride, float lr, float weight_decay, float mu, int nesterov,
                       float scale, gns_dtype compute, const gns_schedule* sched, void* O_out,
                       void* workspace, size_t ws_bytes, hipStream_t stream);

@@ -80,8 +80,8 @@ _sig("dion3_step_rows", I, P, P, P, I, I, I, LL, P, I, F, F, F, I, ctypes.POINTE
 _sig("dion3_step_dev_scalars", I, P, P, P, I, I, I, LL, I, P, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
 _sig("dion3_cols_workspace_size", SZ, I, I, I, I, I)
 _sig("dion3_step_cols", I, P, P, P, I, I, I, LL, I, F, F, F, I, I, ctypes.POINTER(Schedule), P, P, P, SZ, P)
-_sig("muon_workspace_size", SZ, I, I, I, I, I)
-_sig("muon_step_batched", I, P, P, P, I, I, I, LL, LL, F, F, F, I, F, I, ctypes.POINTER(Schedule), P, P, SZ, P)
+_sig("muon_workspace_size", SZ, I, I, I, I, I, I)
+_sig("muon_step_batched", I, P, P, P, I, I, I, I, LL, LL, F, F, F, I, F, I, ctypes.POINTER(Schedule), P, P, SZ, P)
 
 
 def header_functions() -> list[str]:
@@ -357,12 +357,6 @@ def _rows(x):
     return x.shape[0], x.shape[1], x.stride(0)
 
 
-def _bf16_rows(x, name):
-    torch = _torch()
-    _expect(_dev(x), name, dtype=torch.bfloat16)
-    return _rows(x)
-
-
 def _state_rows(x, name):
     """[N, m] rows of a Dion3 state tensor (bf16, fp16 or fp32) -> (N, m, ld, dtype code)."""
     torch = _torch()
@@ -586,42 +580,45 @@ def dion3_step_batched(W, M, G, k, lr, weight_decay=0.0, mu=0.95, score_norm=1, 
     return (S, O) if O is not None else S
 
 
-def muon_workspace_size(batch, n, m, compute="f16", nesterov=True) -> int:
-    return int(lib.muon_workspace_size(batch, n, m, code_of(compute), 1 if nesterov else 0))
+def muon_workspace_size(batch, n, m, compute="f16", nesterov=True, dtype="bf16") -> int:
+    return int(lib.muon_workspace_size(batch, n, m, code_of(dtype), code_of(compute), 1 if nesterov else 0))
 
 
 def muon_step(W, M, G, lr, weight_decay=0.0, mu=0.95, nesterov=True, scale=None, compute="f16", schedule=None,
               return_O=False, O=None, workspace=None):
-    """One Muon step on the bf16 matrices W, M (updated in place) with gradients G, each
-    [n, m] or [B, n, m] with contiguous rows and shared strides: M <- mu M + G; O =
-    GramNS(G + mu M) (nesterov) or GramNS(M); W <- (1 - lr wd) W - lr scale O, scale
-    = 0.2 sqrt(max(n, m)) unless given.  Returns O ([.., n, m] bf16) when return_O or O
-    is given, else None."""
+    """One Muon step on the matrices W, M (updated in place) with gradients G, each
+    [n, m] or [B, n, m] with contiguous rows and shared strides, all bf16, fp16 or fp32:
+    M <- mu M + G; O = GramNS(G + mu M) (nesterov) or GramNS(M); W <- (1 - lr wd) W -
+    lr scale O, scale = 0.2 sqrt(max(n, m)) unless given.  Returns O ([.., n, m], the
+    state's dtype) when return_O or O is given, else None."""
     torch = _torch()
-    _expect(_dev(W), "W", dtype=torch.bfloat16)
+    _dev(W)
+    if W.dtype not in (torch.bfloat16, torch.float16, torch.float32):
+        raise ValueError("W must be bf16, fp16 or fp32")
+    dt = dtype_code(W)
     if W.dim() not in (2, 3) or W.stride(-1) != 1:
         raise ValueError("W must be an [n, m] or [B, n, m] tensor with contiguous rows")
     W3 = W if W.dim() == 3 else W.unsqueeze(0)
     B, n, m = W3.shape
     ld, stride = W3.stride(1), W3.stride(0)
     for t, name in ((M, "M"), (G, "G")):
-        _expect(t, name, dtype=torch.bfloat16, shape=W.shape, device=W.device)
+        _expect(t, name, dtype=W.dtype, shape=W.shape, device=W.device)
         if t.stride() != W.stride():
             raise ValueError("W, M, G must share their strides")
     cdt = code_of(compute)
     if return_O and O is None:
-        O = torch.empty(W.shape, dtype=torch.bfloat16, device=W.device)
+        O = torch.empty(W.shape, dtype=W.dtype, device=W.device)
     if O is not None:
-        _expect(O, "O", dtype=torch.bfloat16, shape=W.shape, device=W.device)
+        _expect(O, "O", dtype=W.dtype, shape=W.shape, device=W.device)
         if not O.is_contiguous():
             raise ValueError("O must be contiguous")
     if scale is not None and not float(scale) > 0.0:
         raise ValueError(f"scale must be positive (None selects 0.2 sqrt(max(n, m))), got {scale}")
     sched = schedule if schedule is not None else default_schedule()
     nest = 1 if nesterov else 0
-    ws = _workspace_arg(workspace, lib.muon_workspace_size(B, n, m, cdt, nest), W.device)
-    check(lib.muon_step_batched(W.data_ptr(), M.data_ptr(), G.data_ptr(), B, n, m, ld, stride, lr, weight_decay, mu,
-                                nest, 0.0 if scale is None else float(scale), cdt, ctypes.byref(sched),
+    ws = _workspace_arg(workspace, lib.muon_workspace_size(B, n, m, dt, cdt, nest), W.device)
+    check(lib.muon_step_batched(W.data_ptr(), M.data_ptr(), G.data_ptr(), dt, B, n, m, ld, stride, lr, weight_decay,
+                                mu, nest, 0.0 if scale is None else float(scale), cdt, ctypes.byref(sched),
                                 O.data_ptr() if O is not None else None, ws.data_ptr(), ws.numel(),
                                 _stream(W.device)), "muon_step_batched")
     return O

@@ -645,7 +645,7 @@ struct Dion3Layout {
 // its Frobenius scale and rounded once to the iterate type (the iteration reads a
 // 16-bit X with 16-bit iterates); the iteration then normalises that copy itself,
 // whose norm is 1 up to the rounding.
-static bool dion3_casts_x(gns_dtype dt) { return dt == GNS_F32; }
+static bool state_casts_x(gns_dtype dt) { return dt == GNS_F32; }
 
 // The selected submatrix is held with kp = k rounded up to a multiple of 8 rows; the
 // extra rows are zero.  Zero rows leave the iteration's result on the other rows
@@ -662,7 +662,7 @@ static Dion3Layout dion3_layout(void* base, int batch, int N, int m, int k, gns_
   L.sumsq = (double*)c.take(sizeof(double) * B * N);
   L.s = (float*)c.take(sizeof(float) * B);
   L.X = c.take(B * kp * m * esize(dt));
-  L.Xc = dion3_casts_x(dt) ? c.take(B * kp * m * esize(cdt)) : nullptr;
+  L.Xc = state_casts_x(dt) ? c.take(B * kp * m * esize(cdt)) : nullptr;
   L.O = c.take(B * kp * m * esize(dt));
   L.gns_bytes = ns_workspace_bytes(batch, kp, m, cdt);
   L.gns_ws = c.take(L.gns_bytes);
@@ -734,7 +734,7 @@ static int dion3_run(void* W, void* M, const void* G, gns_dtype dt, int batch, i
                       ((size_t)(N - 1) * ld + m) * es < (size_t(1) << 31);
   // one batched Gram NS over the selected kp x m submatrices of every entry (input and
   // output in the state type); its arguments are checked before anything is launched
-  const bool cast_x = dion3_casts_x(dt);
+  const bool cast_x = state_casts_x(dt);
   NsCall c = direct ? make_call(M, dt, ld, stride, O, dt, m, kpm, batch, kp, m, compute, &sch, L.gns_ws,
                                 L.gns_bytes, stream, nullptr)
                     : make_call(cast_x ? L.Xc : L.X, cast_x ? compute : dt, m, kpm, O, dt, m, kpm, batch, kp, m,
@@ -817,7 +817,7 @@ static Dion3ColsLayout dion3_cols_layout(void* base, int N, int m, int k, gns_dt
   L.s = (float*)c.take(sizeof(float));
   const int kp = padded_rows(k);
   L.Xt = c.take((size_t)kp * N * esize(dt));
-  L.Xtc = dion3_casts_x(dt) ? c.take((size_t)kp * N * esize(cdt)) : nullptr;
+  L.Xtc = state_casts_x(dt) ? c.take((size_t)kp * N * esize(cdt)) : nullptr;
   L.O = c.take((size_t)kp * N * esize(dt));
   L.gns_bytes = ns_workspace_bytes(1, kp, N, cdt);
   L.gns_ws = c.take(L.gns_bytes);
@@ -861,7 +861,7 @@ int dion3_step_cols(void* W, void* M, const void* G, gns_dtype dt, int N, int m,
   const long long kN = (long long)k * N, kpN = (long long)kp * N;
   // the kp x N transpose of the selected columns: Gram NS iterates on its short side;
   // its arguments are checked before anything is launched
-  const bool cast_x = dion3_casts_x(dt);
+  const bool cast_x = state_casts_x(dt);
   NsCall c = make_call(cast_x ? L.Xtc : L.Xt, cast_x ? compute : dt, N, kpN, O, dt, N, kpN, 1, kp, N, compute, &sch,
                        L.gns_ws, L.gns_bytes, stream, nullptr);
   c.s_given = cast_x ? nullptr : L.s;
@@ -894,41 +894,48 @@ int dion3_step_rows(void* W, void* M, const void* G, gns_dtype dt, int N, int m,
 
 // Muon step workspace: the row sums of squares and the scale of each matrix, U (the
 // lookahead, only with nesterov), O, then the Gram NS workspace of the batch.
+// Muon step workspace: the row sums of squares and the scale of each matrix, U (the
+// lookahead, only with nesterov) and O in the state type, the scaled 16-bit copy of
+// the matrix the iteration reads (fp32 states only, as for Dion3), then the Gram NS
+// workspace of the batch.
 struct MuonLayout {
   double* rowsq;
   float* s;
-  void *U, *O, *gns_ws;
+  void *U, *Xc, *O, *gns_ws;
   size_t gns_bytes, bytes;
 };
 
-static MuonLayout muon_layout(void* base, int batch, int n, int m, gns_dtype cdt, int nesterov) {
+static MuonLayout muon_layout(void* base, int batch, int n, int m, gns_dtype dt, gns_dtype cdt, int nesterov) {
   Carver c{reinterpret_cast<uint8_t*>(base), 0};
   MuonLayout L{};
   const size_t elems = (size_t)batch * n * m;
   L.rowsq = (double*)c.take(sizeof(double) * (size_t)batch * n);
   L.s = (float*)c.take(sizeof(float) * (size_t)batch);
-  L.U = nesterov ? c.take(elems * 2) : nullptr;
-  L.O = c.take(elems * 2);
+  L.U = nesterov ? c.take(elems * esize(dt)) : nullptr;
+  L.Xc = state_casts_x(dt) ? c.take(elems * esize(cdt)) : nullptr;
+  L.O = c.take(elems * esize(dt));
   L.gns_bytes = ns_workspace_bytes(batch, n, m, cdt);
   L.gns_ws = c.take(L.gns_bytes);
   L.bytes = c.off;
   return L;
 }
 
-size_t muon_workspace_size(int batch, int n, int m, gns_dtype compute, int nesterov) {
-  if (batch < 1 || n < 1 || m < 1 || !valid_dtype(compute) || (nesterov != 0 && nesterov != 1)) return 0;
-  return muon_layout(nullptr, batch, n, m, compute, nesterov).bytes;
+size_t muon_workspace_size(int batch, int n, int m, gns_dtype dt, gns_dtype compute, int nesterov) {
+  if (batch < 1 || n < 1 || m < 1 || !valid_dtype(dt) || !valid_dtype(compute) || (nesterov != 0 && nesterov != 1))
+    return 0;
+  return muon_layout(nullptr, batch, n, m, dt, compute, nesterov).bytes;
 }
 
-int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, long long ld, long long stride,
-                      float lr, float weight_decay, float mu, int nesterov, float scale, gns_dtype compute,
-                      const gns_schedule* sched, void* O_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+int muon_step_batched(void* W, void* M, const void* G, gns_dtype dt, int batch, int n, int m, long long ld,
+                      long long stride, float lr, float weight_decay, float mu, int nesterov, float scale,
+                      gns_dtype compute, const gns_schedule* sched, void* O_out, void* workspace, size_t ws_bytes,
+                      hipStream_t stream) {
   if (batch < 0) return GNS_ERR_INVALID_ARG;
   if (batch == 0) return GNS_OK;
-  int st = check_dion3_matrix(W, GNS_BF16, n, m, ld);
+  int st = check_dion3_matrix(W, dt, n, m, ld);
   if (st) return st;
-  if ((st = check_dion3_matrix(M, GNS_BF16, n, m, ld))) return st;
-  if ((st = check_dion3_matrix(G, GNS_BF16, n, m, ld))) return st;
+  if ((st = check_dion3_matrix(M, dt, n, m, ld))) return st;
+  if ((st = check_dion3_matrix(G, dt, n, m, ld))) return st;
   if (batch > 1 && stride < (long long)n * ld) return GNS_ERR_INVALID_ARG;
   if (batch > 1 && stride % 8) return GNS_ERR_UNSUPPORTED;
   if (nesterov != 0 && nesterov != 1) return GNS_ERR_INVALID_ARG;
@@ -939,13 +946,14 @@ int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, 
   if (compute == GNS_F32) return GNS_ERR_UNSUPPORTED;
   if (O_out && !aligned16(O_out)) return GNS_ERR_UNSUPPORTED;
   // W, M and G must be distinct (each is read and written by different passes)
-  const size_t span = ((size_t)(batch - 1) * (size_t)(batch > 1 ? stride : 0) + (size_t)(n - 1) * ld + m) * 2;
+  const size_t es = esize(dt);
+  const size_t span = ((size_t)(batch - 1) * (size_t)(batch > 1 ? stride : 0) + (size_t)(n - 1) * ld + m) * es;
   if (overlaps(W, span, M, span) || overlaps(W, span, G, span) || overlaps(M, span, G, span))
     return GNS_ERR_INVALID_ARG;
   gns_schedule sch;
   if (sched) sch = *sched; else gns_default_schedule(&sch);
   if ((st = check_schedule(sch))) return st;
-  const MuonLayout L = muon_layout(workspace, batch, n, m, compute, nesterov);
+  const MuonLayout L = muon_layout(workspace, batch, n, m, dt, compute, nesterov);
   if (!workspace || ws_bytes < L.bytes) return GNS_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GNS_ERR_UNSUPPORTED;
   // the update's RMS matched to AdamW's: 0.2 sqrt(max(n, m)) unless the caller gives one
@@ -954,25 +962,28 @@ int muon_step_batched(void* W, void* M, const void* G, int batch, int n, int m, 
 
   void* O = O_out ? O_out : L.O;
   const long long nm = (long long)n * m;
-  // the batched Gram NS of U (or of M itself without the lookahead); its arguments
-  // are checked before anything is launched
-  NsCall c = nesterov ? make_call(L.U, GNS_BF16, m, nm, O, GNS_BF16, m, nm, batch, n, m, compute, &sch, L.gns_ws,
-                                  L.gns_bytes, stream, nullptr)
-                      : make_call(M, GNS_BF16, ld, stride, O, GNS_BF16, m, nm, batch, n, m, compute, &sch, L.gns_ws,
-                                  L.gns_bytes, stream, nullptr);
+  // the batched Gram NS of U (or of M itself without the lookahead), or of their
+  // scaled 16-bit copy for an fp32 state; its arguments are checked before anything is
+  // launched
+  const void* src = nesterov ? L.U : M;
+  const long long lds = nesterov ? m : ld, ss = nesterov ? nm : stride;
+  const bool cast_x = state_casts_x(dt);
+  NsCall c = cast_x ? make_call(L.Xc, compute, m, nm, O, dt, m, nm, batch, n, m, compute, &sch, L.gns_ws,
+                                L.gns_bytes, stream, nullptr)
+                    : make_call(src, dt, lds, ss, O, dt, m, nm, batch, n, m, compute, &sch, L.gns_ws, L.gns_bytes,
+                                stream, nullptr);
   // the momentum pass also forms each matrix's Frobenius scale
-  c.s_given = L.s;
+  c.s_given = cast_x ? nullptr : L.s;
   if ((st = check_ns(c))) return st;
-  if (O_out && (overlaps(O_out, (size_t)batch * nm * 2, workspace, L.bytes) ||
-                overlaps(O_out, (size_t)batch * nm * 2, W, span) || overlaps(O_out, (size_t)batch * nm * 2, M, span) ||
-                overlaps(O_out, (size_t)batch * nm * 2, G, span)))
+  const size_t o_bytes = (size_t)batch * nm * es;
+  if (O_out && (overlaps(O_out, o_bytes, workspace, L.bytes) || overlaps(O_out, o_bytes, W, span) ||
+                overlaps(O_out, o_bytes, M, span) || overlaps(O_out, o_bytes, G, span)))
     return GNS_ERR_INVALID_ARG;
 
-  HIP_OK(launch_muon_momentum((uint16_t*)M, (const uint16_t*)G, batch, n, m, ld, stride, mu, (uint16_t*)L.U, m, nm,
-                              L.rowsq, sch.eps, L.s, stream));
+  HIP_OK(launch_muon_momentum(M, G, dt, batch, n, m, ld, stride, mu, L.U, m, nm, L.rowsq, sch.eps, L.s, stream));
+  if (cast_x) HIP_OK(launch_cast_scale(src, dt, lds, ss, L.Xc, compute, m, nm, batch, n, m, 1.0f, L.s, 1, stream));
   if ((st = run_ns(c, true))) return st;
-  HIP_OK(launch_muon_update((uint16_t*)W, batch, n, m, ld, stride, (const uint16_t*)O, m, nm, lr, weight_decay, sc,
-                            stream));
+  HIP_OK(launch_muon_update(W, dt, batch, n, m, ld, stride, O, m, nm, lr, weight_decay, sc, stream));
   return GNS_OK;
 }
 

@@ -1,4 +1,4 @@
-"""GPU parity of the Dion3 step on f16 and fp32 states against the oracle.
+"""GPU parity of the Dion3 and Muon steps on f16 and fp32 states against the oracle.
 
 The state type is the caller's (W, M, G in one dtype); the oracle follows the same
 rounding model in that format (one rounding to the state type after each fp32
@@ -184,3 +184,27 @@ def test_dion3_step_batched_f16_equals_single(gns_mod):
         assert same(host(O, "f16"), host(Ob[b], "f16"))
         assert same(host(W, "f16"), host(Wb[b], "f16"))
         assert same(host(M, "f16"), host(Mb[b], "f16"))
+
+
+# ---- the Muon step on f16 and fp32 states ---------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+@pytest.mark.parametrize("B,n,m,nesterov,wd", [(2, 136, 200, True, 0.1), (1, 256, 64, False, 0.0),
+                                              (2, 128, 128, True, 0.0)])
+def test_muon_step_state_types(gns_mod, dt, B, n, m, nesterov, wd):
+    announce(f"muon step {dt} B={B} {n}x{m} nesterov={nesterov} wd={wd}")
+    rng = np.random.default_rng(60 + n + m)
+    w, g, mo = (np.stack([synth.to_storage(rng.standard_normal((n, m)) * 0.02, dt) for _ in range(B)])
+                for _ in range(3))
+    lr, mu = 0.02, 0.95
+    W, M, G = to_dev(w, dt), to_dev(mo, dt), to_dev(g, dt)
+    O = gns_mod.muon_step(W, M, G, lr, weight_decay=wd, mu=mu, nesterov=nesterov, return_O=True)
+    assert O.dtype == W.dtype
+    Wh, Mh, Oh = host(W, dt), host(M, dt), host(O, dt)
+    sc = float(oracle.muon_scale(n, m))
+    for b in range(B):
+        w_ref, m_ref, o_ref = oracle.muon_step(w[b], mo[b], g[b], lr, wd=wd, mu=mu, nesterov=nesterov, storage=dt)
+        assert same(Mh[b], m_ref)
+        assert rel_fro(Oh[b].astype(np.float64), o_ref) <= 2e-2
+        assert same(Wh[b], oracle.decay_and_update(w[b], Oh[b].astype(np.float64), lr, wd, sc, dt))
+        assert w_within_bound(Wh[b], w_ref, lr * sc, o_ref, dt)

@@ -173,9 +173,9 @@ def test_muon_validation():
     HIP = -4
 
     def margs(B=2, n=64, m=256, ld=256, stride=64 * 256, W=FAKE, M=FAKE * 8, G=FAKE * 16, nest=1, lr=0.02,
-              scale=0.0, compute=F16, O=None, ws=FAKE * 40, wsb=1 << 40):
-        return (W, M, G, B, n, m, ld, stride, lr, 0.0, 0.95, nest, scale, compute, ctypes.byref(sched), O, ws, wsb,
-                None)
+              scale=0.0, compute=F16, O=None, ws=FAKE * 40, wsb=1 << 40, dt=BF16):
+        return (W, M, G, dt, B, n, m, ld, stride, lr, 0.0, 0.95, nest, scale, compute, ctypes.byref(sched), O, ws,
+                wsb, None)
 
     assert L.muon_step_batched(*margs(B=0)) == OK
     assert L.muon_step_batched(*margs(B=-1)) == INVALID
@@ -195,13 +195,17 @@ def test_muon_validation():
     assert L.muon_step_batched(*margs(wsb=8)) == WS
     assert L.muon_step_batched(*margs(O=FAKE * 40 + 4096)) == INVALID     # O inside the workspace
     assert L.muon_step_batched(*margs(O=FAKE * 8)) == INVALID             # O is M
+    assert L.muon_step_batched(*margs(dt=7)) == INVALID                   # not a state type
+    assert L.muon_step_batched(*margs(dt=F32, wsb=8)) == WS               # fp32 and f16 states accepted
+    assert L.muon_step_batched(*margs(dt=F16, wsb=8)) == WS
     import torch
     if torch.cuda.device_count() == 0:
         assert L.muon_step_batched(*margs()) == HIP                       # valid: reaches the launch
         assert L.muon_step_batched(*margs(nest=0, B=1, n=512, m=64, ld=64, stride=0)) == HIP   # tall, no lookahead
-    with_u = L.muon_workspace_size(2, 64, 256, F16, 1)
-    assert with_u - L.muon_workspace_size(2, 64, 256, F16, 0) >= 2 * 64 * 256 * 2
-    assert L.muon_workspace_size(2, 64, 256, F16, 2) == 0
+    with_u = L.muon_workspace_size(2, 64, 256, BF16, F16, 1)
+    assert with_u - L.muon_workspace_size(2, 64, 256, BF16, F16, 0) >= 2 * 64 * 256 * 2
+    assert L.muon_workspace_size(2, 64, 256, BF16, F16, 2) == 0
+    assert L.muon_workspace_size(2, 64, 256, F32, F16, 1) > with_u
 
 
 def test_workspace_sizes_grow_with_problem():

@@ -15,6 +15,7 @@ import json
 import os
 
 import numpy as np
+import pytest
 import torch
 
 import synth
@@ -121,3 +122,56 @@ def test_decay_and_update_rounding_matches_torch_float32():
     d = torch.tensor(np.float32(1.0)) - lr32 * wd32
     ref = (d * tbf(w).float() - (lr32 * sc32) * torch.from_numpy(o.astype(np.float32))).to(torch.bfloat16)
     assert np.array_equal(got, ref.view(torch.int16).numpy().view(np.uint16))
+
+
+# ---- the same model in the f16 and f32 state formats ---------------------------------
+
+TORCH_OF = {"f16": torch.float16, "f32": torch.float32}
+
+
+@pytest.mark.parametrize("storage", ["f16", "f32"])
+@pytest.mark.parametrize("nesterov", [False, True])
+def test_momentum_matches_torch_state_formats(storage, nesterov):
+    rng = np.random.default_rng(71)
+    m = synth.to_storage(rng.standard_normal((24, 200)) * 0.02, storage)
+    g = synth.to_storage(rng.standard_normal((24, 200)) * 0.02, storage)
+    m_new, u = momentum(m, g, 0.95, nesterov, storage)
+    f, dt = torch.float32, TORCH_OF[storage]
+    mu = torch.tensor(0.95, dtype=f)
+    mt, gt = torch.from_numpy(m).float(), torch.from_numpy(g).float()
+    ref_m = (mu * mt + gt).to(dt)
+    assert np.array_equal(m_new.view(np.uint8), ref_m.numpy().view(np.uint8))
+    ref_u = (gt + mu * ref_m.float()).to(dt) if nesterov else ref_m
+    assert np.array_equal(u.view(np.uint8), ref_u.numpy().view(np.uint8))
+
+
+@pytest.mark.parametrize("storage", ["f16", "f32"])
+def test_decay_and_update_matches_torch_state_formats(storage):
+    rng = np.random.default_rng(72)
+    w = synth.to_storage(rng.standard_normal((24, 200)) * 0.02, storage)
+    o = synth.to_storage(rng.standard_normal((24, 200)) * 0.1, storage).astype(np.float64)
+    lr, wd, sc = 0.02, 0.1, float(muon_scale(24, 200))
+    out = decay_and_update(w, o, lr, wd, sc, storage)
+    f = torch.float32
+    lr_t, wd_t, sc_t = (torch.tensor(v, dtype=f) for v in (lr, wd, sc))
+    d = torch.tensor(1.0, dtype=f) - lr_t * wd_t
+    ref = (d * torch.from_numpy(w).float() - (lr_t * sc_t) * torch.from_numpy(o).to(f)).to(TORCH_OF[storage])
+    assert np.array_equal(out.view(np.uint8), ref.numpy().view(np.uint8))
+
+
+def test_muon_step_f32_within_rounding_of_the_unrounded_step():
+    rng = np.random.default_rng(73)
+    w, m, g = (synth.to_storage(rng.standard_normal((48, 160)) * 0.02, "f32") for _ in range(3))
+    w32, m32, o32 = muon_step(w, m, g, 0.02, wd=0.1, storage="f32")
+    w64, m64, o64 = muon_step(w.astype(np.float64), m.astype(np.float64), g.astype(np.float64), 0.02, wd=0.1,
+                              storage="f64")
+    assert w32.dtype == np.float32 and m32.dtype == np.float32
+    # a few fp32 roundings of the terms (fp32 mu, the product, the sum), bounded by the
+    # terms' magnitudes, not the result's (mu M and G may cancel)
+    u = 2.0 ** -24
+    m_bound = 4 * u * (0.95 * np.abs(m.astype(np.float64)) + np.abs(g.astype(np.float64)))
+    assert np.all(np.abs(m32 - m64) <= m_bound)
+    assert np.allclose(o32, o64, rtol=0, atol=1e-5)
+    sc = float(muon_scale(48, 160))
+    w_bound = 4 * u * (np.abs(w.astype(np.float64)) + 0.02 * sc * np.abs(o64)) + 0.02 * sc * 1e-5
+    assert np.all(np.abs(w32 - w64) <= w_bound)
