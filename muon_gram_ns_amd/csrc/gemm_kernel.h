@@ -5,8 +5,7 @@
 // computed tile is also written transposed above the diagonal, which halves the
 // multiply work for a symmetric result ("Dion3: Full-Stack Orthogonal Updates",
 // paper.rainbus.top, 前置知识 "symmetric GEMM kernel" and 方法步骤详情 (2)).  The
-// epilogue forms alpha*acc + beta*C + gamma*I in fp32 before a single rounding, and
-// can emit a second output shifted by delta*I (Q_1 = Z_1 + a_1 I in Gram NS).
+// epilogue forms alpha*acc + beta*C + gamma*I in fp32 before a single rounding.
 //
 // Both kernels read their operands as rows that are contiguous along K:
 //   NT  (symmetric): A is n x K, B is n x K; D = A B^T.  With B symmetric and K = n
@@ -149,11 +148,11 @@ __device__ __forceinline__ uint4 convert_chunk(uint4 c, float mul) {
 }
 
 // Epilogue element group: row gm, columns gn .. gn+3 of the output tile.
-// v = alpha' acc + beta C + gamma [diag] is written to D (and D2 = v + delta [diag]);
+// v = alpha' acc + beta C + gamma [diag] is written to D;
 // symmetric outputs write the lower-triangle elements and their mirror images, so D
 // is bitwise symmetric.  N % 4 == 0, so gn < N covers gn .. gn+3.
 template <class TOut, bool LOWER>
-__device__ __forceinline__ void emit_row4(const GemmParams& p, uint8_t* Db, uint8_t* D2b, const uint8_t* Cb,
+__device__ __forceinline__ void emit_row4(const GemmParams& p, uint8_t* Db, const uint8_t* Cb,
                                           float alpha, int gm, int gn, const float* a4) {
   if (gm >= p.M || gn >= p.N) return;
   float v[4];
@@ -184,27 +183,11 @@ __device__ __forceinline__ void emit_row4(const GemmParams& p, uint8_t* Db, uint
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (gn + e < gm) store1<TOut>(Db, (long long)(gn + e) * p.ldd + gm, v[e]);
-    if (D2b) {
-      float w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = v[e] + ((gn + e == gm) ? p.delta : 0.0f);
-      if (all_lower) {
-        store4<TOut>(D2b, (long long)gm * p.ldd2 + gn, w);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (gn + e <= gm) store1<TOut>(D2b, (long long)gm * p.ldd2 + gn + e, w[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (gn + e < gm) store1<TOut>(D2b, (long long)(gn + e) * p.ldd2 + gm, w[e]);
-    }
   }
 }
 
 struct EpiPtrs {
   uint8_t* D;
-  uint8_t* D2;
   const uint8_t* C;
   float alpha;
   int c_planes, d_planes;     // 1, or 2 for a hi/lo pair of planes
@@ -246,7 +229,6 @@ __device__ __forceinline__ EpiPtrs epi_ptrs(const GemmParams& p, int bz, bool se
   void* D = second ? p.Dp : p.D;
   const void* C = second ? p.C2 : p.C;
   e.D = reinterpret_cast<uint8_t*>(D) + (size_t)bz * p.sD * TOut::kBytes;
-  e.D2 = (p.D2 && !second) ? reinterpret_cast<uint8_t*>(p.D2) + (size_t)bz * p.sD2 * TOut::kBytes : nullptr;
   e.C = C ? reinterpret_cast<const uint8_t*>(C) + (size_t)bz * p.sC * TOut::kBytes : nullptr;
   e.c_planes = second ? p.c2_planes : p.c_planes;
   e.d_planes = second ? p.dp_planes : p.d_planes;
@@ -291,7 +273,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x4_t (&acc)[FM]
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       float a4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      emit_row4<TOut, LOWER>(p, e.D, e.D2, e.C, e.alpha, mw + i * 16 + (lane & 15), nw + j * 16 + 4 * (lane >> 4), a4);
+      emit_row4<TOut, LOWER>(p, e.D, e.C, e.alpha, mw + i * 16 + (lane & 15), nw + j * 16 + 4 * (lane >> 4), a4);
     }
 }
 
@@ -691,8 +673,8 @@ __device__ __forceinline__ void store_vec_nt(uint8_t* base, long long ld, int ro
 // rows (one fragment row): the raw fp32 accumulators go to a per-wave slab
 // [32][WN + 4] (the padding spreads the 16 rows of a 128-bit access over distinct
 // banks); the row pass forms v = alpha acc + beta C + gamma [diagonal] for 16-byte
-// vectors along the output rows, stores them with coalesced 16-byte writes (D, and
-// D2 = v + delta [diagonal]) and puts v back in the slab; for a symmetric output the
+// vectors along the output rows, stores them with coalesced 16-byte writes and puts
+// v back in the slab; for a symmetric output the
 // mirror pass reads the slab down its columns and writes the strictly-lower elements
 // at their transposed positions.  Both triangles round the same fp32 value, so the
 // output is bitwise symmetric.  Only the slab writes index the accumulators, so
@@ -798,12 +780,6 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc
       if (hi >= 0) {
         if (NT && hi >= VE - 1 && d_pl == 1) store_vec_nt<TOut>(ep.D, p.ldd, gm, gn, v);
         else store_planes<TOut>(ep.D, p.ldd, gm, gn, v, 0, hi, d_pl, p.plane);
-        if (ep.D2) {
-          float w[VE];
-#pragma unroll
-          for (int e = 0; e < VE; ++e) w[e] = v[e] + ((gn + e == gm) ? p.delta : 0.0f);
-          store_vec<TOut>(ep.D2, p.ldd2, gm, gn, w, 0, hi);
-        }
       }
       if constexpr (LOWER) {
 #pragma unroll
@@ -826,7 +802,6 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x16_t (&acc
 #pragma unroll
         for (int e = 0; e < VE; ++e) v[e] = slab[(rr + e) * S + c];
         store_planes<TOut>(ep.D, p.ldd, gn, gm0, v, lo, VE - 1, d_pl, p.plane);
-        if (ep.D2) store_vec<TOut>(ep.D2, p.ldd2, gn, gm0, v, lo, VE - 1);
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

@@ -278,24 +278,27 @@ int run_gram(const NsCall& c) {
       HIP_OK(launch_symm_ws(cdt, cdt, g, B, L.part, L.part_bytes, c.stream, c.flops));
       q_identity = true;
     }
-    {  // Z = c R R + b R   (and Q = Z + a I while Q is the identity)
-      GemmParams g = symm_params(n, n, L.R, n, sn, L.R, n, sn, L.Z, n, sn);
+    // Za = Z + a I = a I + b R + c R R, stored once (its diagonal rounded with the
+    // rest): every later use of Z in the step is through Z + a I -- Q Za, R Za and
+    // Za Y -- so those products need no beta C term.  While Q is the identity Za is
+    // also the new Q, so it goes straight to Q's buffer.
+    void* za = q_identity ? Q : L.Z;
+    {
+      GemmParams g = symm_params(n, n, L.R, n, sn, L.R, n, sn, za, n, sn);
       chain(g, pl, pl, pl, pl);
-      g.alpha = cc; g.beta = b; g.C = L.R; g.ldc = n; g.sC = sn;
-      if (q_identity) { g.D2 = Q; g.ldd2 = n; g.sD2 = sn; g.delta = a; }
+      g.alpha = cc; g.beta = b; g.C = L.R; g.ldc = n; g.sC = sn; g.gamma = a;
       HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
     }
     const bool need_r = t < c.sch.steps && !restart_before(t + 1);
-    // Q <- Q Z + a Q and Y = R Z + a R read the same Z: with both needed, one launch
-    // computes the pair
+    // Q <- Q Za and Y = R Za read the same Za: with both needed, one launch computes
+    // the pair
     const bool q_update = !q_identity;
     if (q_update) {
-      GemmParams g = symm_params(n, n, Q, n, sn, L.Z, n, sn, Qn, n, sn);
+      GemmParams g = symm_params(n, n, Q, n, sn, za, n, sn, Qn, n, sn);
       chain(g, 1, pl, 1, 1);
-      g.beta = a; g.C = Q; g.ldc = n; g.sC = sn;
       if (need_r) {
-        g.pair = 1; g.A2 = L.R; g.C2 = L.R; g.Dp = L.Y;
-        g.a2_planes = pl; g.c2_planes = pl; g.dp_planes = pl;
+        g.pair = 1; g.A2 = L.R; g.Dp = L.Y;
+        g.a2_planes = pl; g.dp_planes = pl;
       }
       HIP_OK(launch_symm(cdt, cdt, g, B, c.stream, c.flops));
       std::swap(Q, Qn);
@@ -303,14 +306,12 @@ int run_gram(const NsCall& c) {
     q_identity = false;
     if (need_r) {
       if (!q_update) {
-        GemmParams g1 = symm_params(n, n, L.R, n, sn, L.Z, n, sn, L.Y, n, sn);  // Y = R Z + a R
+        GemmParams g1 = symm_params(n, n, L.R, n, sn, za, n, sn, L.Y, n, sn);     // Y = R Za
         chain(g1, pl, pl, pl, pl);
-        g1.beta = a; g1.C = L.R; g1.ldc = n; g1.sC = sn;
         HIP_OK(launch_symm(cdt, cdt, g1, B, c.stream, c.flops));
       }
-      GemmParams g2 = symm_params(n, n, L.Z, n, sn, L.Y, n, sn, L.R, n, sn);    // R = Z Y + a Y
+      GemmParams g2 = symm_params(n, n, za, n, sn, L.Y, n, sn, L.R, n, sn);       // R = Za Y
       chain(g2, pl, pl, pl, pl);
-      g2.beta = a; g2.C = L.Y; g2.ldc = n; g2.sC = sn;
       HIP_OK(launch_symm(cdt, cdt, g2, B, c.stream, c.flops));
     }
   }
@@ -318,7 +319,8 @@ int run_gram(const NsCall& c) {
 }
 
 // Standard quintic NS on the same kernels: X0 = P s X (iterate dtype), then per step
-// A = X X^T / P^2, B = c A A + b A, X <- B X + a X; finally O = X / P.
+// A = X X^T / P^2, Ba = a I + b A + c A A, X <- Ba X (= a X + (b A + c A A) X);
+// finally O = X / P.
 int run_standard(const NsCall& c) {
   const NsLayout L = ns_layout(c.ws, c.batch, c.n, c.m, c.cdt);
   const int n = c.n, m = c.m, B = c.batch;
@@ -333,14 +335,14 @@ int run_standard(const NsCall& c) {
     GemmParams g1 = symm_params(n, m, cur, m, nm, cur, m, nm, L.A, n, nn);
     g1.alpha = 1.0f / (P * P);
     HIP_OK(launch_symm_ws(c.cdt, c.cdt, g1, B, L.part, L.part_bytes, c.stream, c.flops));
+    // Ba stored once (its diagonal rounded with the rest), so the X update reads no C
     GemmParams g2 = symm_params(n, n, L.A, n, nn, L.A, n, nn, L.Bm, n, nn);
-    g2.alpha = cc; g2.beta = b; g2.C = L.A; g2.ldc = n; g2.sC = nn;
+    g2.alpha = cc; g2.beta = b; g2.C = L.A; g2.ldc = n; g2.sC = nn; g2.gamma = a;
     HIP_OK(launch_symm(c.cdt, c.cdt, g2, B, c.stream, c.flops));
     GemmParams g3;
     g3.M = n; g3.N = m; g3.K = n;
     g3.A = L.Bm; g3.lda = n; g3.sA = nn;
     g3.B = cur; g3.ldb = m; g3.sB = nm;
-    g3.C = cur; g3.ldc = m; g3.sC = nm; g3.beta = a;
     g3.D = nxt; g3.ldd = m; g3.sD = nm;
     HIP_OK(launch_rect(c.cdt, c.cdt, c.cdt, g3, B, c.stream, c.flops));
     std::swap(cur, nxt);

@@ -11,21 +11,19 @@ namespace gns {
 //   symmetric (NT, lower tiles):  D = alpha' A B^T + beta C + gamma I, A,B: M x K
 //   rectangular (NN):             D = alpha' A B + beta C,            A: M x K, B: K x N
 // alpha' = alpha * scale[b]^alpha_pow.  NN with B of another 16-bit type converts
-// B on load after multiplying by b_mul * scale[b]^b_pow.  D2 (symmetric only,
-// nullable) receives the same values + delta on the diagonal.
+// B on load after multiplying by b_mul * scale[b]^b_pow.
 struct GemmParams {
   int M = 0, N = 0, K = 0;
   const void* A = nullptr; long long lda = 0, sA = 0;
   const void* B = nullptr; long long ldb = 0, sB = 0;
   const void* C = nullptr; long long ldc = 0, sC = 0;
   void* D = nullptr; long long ldd = 0, sD = 0;
-  void* D2 = nullptr; long long ldd2 = 0, sD2 = 0;
-  float alpha = 1.f, beta = 0.f, gamma = 0.f, delta = 0.f;
+  float alpha = 1.f, beta = 0.f, gamma = 0.f;
   const float* scale = nullptr; int alpha_pow = 0;
   float b_mul = 1.f; int b_pow = 0;
   // pair (symmetric only): one launch also computes D' = alpha' A' B^T + beta C' for
   // the same B, shapes and coefficients; workgroups of batch index >= batch take
-  // (A2, C2, Dp) at the same strides.  D2 is not written for the second product.
+  // (A2, C2, Dp) at the same strides.
   int pair = 0;
   const void* A2 = nullptr; const void* C2 = nullptr; void* Dp = nullptr;
   // partials (symmetric only, instead of scale): scale[b] = 1 / (sqrt(sum of the

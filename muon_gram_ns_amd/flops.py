@@ -54,10 +54,10 @@ def gram_schedule(n: int, m: int, T: int = 5, restart_after=(2,)) -> float:
             q_identity = True
         f += sym(n, n)                                # Z = c R R + b R (Q = Z + aI free)
         if not q_identity:
-            f += sym(n, n)                            # Q <- Q Z + a Q
+            f += sym(n, n)                            # Q <- Q (Z + a I)
         q_identity = False
         if t < T and (t + 1) not in restarts:
-            f += 2 * sym(n, n)                        # Y = R Z + a R ; R = Z Y + a Y
+            f += 2 * sym(n, n)                        # Y = R (Z + a I) ; R = (Z + a I) Y
     return f + rect(n, n, m)                          # O = Q X
 
 
