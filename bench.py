@@ -243,29 +243,37 @@ def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, wor
 
     The roof is the lower of the MFMA peak and arithmetic intensity x HBM bandwidth,
     with the algorithmic flops (n(n+1)K per product) and algorithmic bytes of the mix:
-    an n x n product with K = n reads its two distinct n x n operands (the beta C
-    term is one of them) and writes one; the Gram product reads X once and writes
-    n x n.  At n = 1024 the intensity is below the ridge (~315 flop/B), so the roof
-    is HBM and `achieved` is algorithmic GB/s; the MFMA fraction is given beside it."""
+    a product of one n x n operand (Za = c R R + b R + a I, read as A, B and the beta C
+    term) reads it once and writes one; a product of two distinct n x n operands reads
+    both and writes one; the Gram product reads X once and writes n x n.  At n = 1024
+    the intensity is below the ridge (~315 flop/B), so the roof is HBM and `achieved`
+    is algorithmic GB/s; the MFMA fraction is given beside it."""
     dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[compute]
     e = torch.tensor([], dtype=dt).element_size()
-    # Gram NS (T=5, restart after 2), n x n products per call: t1: Z, Y, R (3); t2: Z, Q (2);
-    # t3: Z, Y, R (3); t4: Z, Q, Y, R (4); t5: Z, Q (2) = 14; plus the Gram product of the
-    # restarted X (K = m).  Standard NS: per step one X X^T (K = m) and one A A (K = n).
-    nn_k, mm_k = (5, 5) if square else (14, 1)
+    # Gram NS (T=5, restart after 2), n x n products per call: one Za per step (5) and
+    # 9 products of two operands without a C term (t1: Y = R Za, R = Za Y; t2: Q Za;
+    # t3: Y, R; t4: Q Za and R Za in one paired launch, R; t5: Q Za); plus the Gram
+    # product of the restarted X (K = m).  Standard NS: per step one X X^T (K = m) and
+    # one Ba = c A A + b A + a I (K = n).
     sym = lambda t: (t + t.transpose(1, 2)) * 0.5
     R = sym(torch.randn(B, n, n, device="cuda")).to(dt)
-    Z = R if square else sym(torch.randn(B, n, n, device="cuda")).to(dt)
+    Z = sym(torch.randn(B, n, n, device="cuda")).to(dt)
     Xh = (torch.randn(B, n, m, device="cuda") / m ** 0.5).to(dt)
     D = torch.empty(B, n, n, device="cuda", dtype=dt)
-    nn_desc = "A A + beta A" if square else "R Z + beta R"
-    launch_mix = f"{nn_k} x (n={n}, K={n}, {nn_desc}) + {mm_k} x (n={n}, K={m}, X X^T), batch {B}"
+    groups = [(5, "self"), (5, "gram")] if square else [(5, "self"), (9, "pair"), (1, "gram")]
+    desc = {"self": f"K={n}, c R R + b R + a I", "pair": f"K={n}, R Z", "gram": f"K={m}, X X^T"}
+    launch_mix = " + ".join(f"{k} x (n={n}, {desc[kind]})" for k, kind in groups) + f", batch {B}"
+    launches = sum(k for k, _ in groups)
 
     def mix():
-        for _ in range(nn_k):
-            gns.symm_gemm(R, Z, C=R, alpha=2.0, beta=-4.0, out=D)
-        for _ in range(mm_k):
-            gns.symm_gemm(Xh, Xh, out=D)
+        for k, kind in groups:
+            for _ in range(k):
+                if kind == "self":
+                    gns.symm_gemm(R, R, C=R, alpha=2.0, beta=-4.0, gamma=3.0, out=D)
+                elif kind == "pair":
+                    gns.symm_gemm(R, Z, out=D)
+                else:
+                    gns.symm_gemm(Xh, Xh, out=D)
 
     for _ in range(3):
         mix()
@@ -277,11 +285,11 @@ def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, wor
             for _ in range(per_graph):
                 mix()
         run = graph.replay
-        launches_per_run = per_graph * (nn_k + mm_k)
+        launches_per_run = per_graph * launches
     except Exception as exc:  # capture unavailable: eager launches, host overhead included
         timing = f"eager launches (graph capture failed: {type(exc).__name__})"
         run = mix
-        launches_per_run = nn_k + mm_k
+        launches_per_run = launches
     reps = max(5, steps // (4 * per_graph))
     run()
     stream = torch.cuda.current_stream()
@@ -293,10 +301,10 @@ def dominant_kernel_roofline(gns, F, torch, B, n, m, compute, square, steps, wor
     ev.record(stream)
     torch.cuda.synchronize()
     avg_s = s.elapsed_time(ev) * 1e-3 / (reps * launches_per_run)
-    alg_flops = B * (nn_k * F.sym(n, n) + mm_k * F.sym(n, m)) / (nn_k + mm_k)
-    nn_bytes = (2 if square else 3) * n * n * e
-    mm_bytes = (n * m + n * n) * e
-    alg_bytes = B * (nn_k * nn_bytes + mm_k * mm_bytes) / (nn_k + mm_k)
+    flops_of = {"self": F.sym(n, n), "pair": F.sym(n, n), "gram": F.sym(n, m)}
+    bytes_of = {"self": 2 * n * n * e, "pair": 3 * n * n * e, "gram": (n * m + n * n) * e}
+    alg_flops = B * sum(k * flops_of[kind] for k, kind in groups) / launches
+    alg_bytes = B * sum(k * bytes_of[kind] for k, kind in groups) / launches
     intensity = alg_flops / alg_bytes
     tflops = alg_flops / avg_s / 1e12
     gbs = alg_bytes / avg_s / 1e9
