@@ -1270,6 +1270,8 @@ gemm16_kernel(GemmParams p) {
 //   mid:   128 x 128, 4 waves of 64 x 64, 4 stages of 64 (128 KB)
 //   small:  64 x 64,  4 waves of 32 x 32, 4 stages of 64 (64 KB), for problems with
 //          few tiles
+//   tri96:  96 x 96,  3 waves of 32 x 96, 3 stages of 64 (72 KB), lower-triangle
+//          products of n of about 2048 (see pick_tile)
 // Measured on MI355X (alone, fp16 operands): the 8-wave big tile beats 4 waves of
 // 128 x 128 (one per SIMD) by 8-10% on 4096^3 products and by 30% on the n = 768
 // products of a 128-matrix batch; with 8 waves, 3, 4 and 5 stages of 32 and 2
@@ -1277,8 +1279,8 @@ gemm16_kernel(GemmParams p) {
 // are slower than 4.
 constexpr int kBigWM = 2, kBigWN = 4, kBkBig = 32, kStagesBig = 4;
 constexpr int kBkMid = 64, kStagesMid = 4;
-constexpr int kBkSmall = 64, kStagesSmall = 4;
-enum class TileCfg { kBig = 0, kMid = 1, kSmall = 2 };
+constexpr int kBkSmall = 64, kStagesSmall = 4, kStagesTri96 = 3;
+enum class TileCfg { kBig = 0, kMid = 1, kSmall = 2, kTri96 = 3 };
 
 inline long long gemm_tiles(int M, int N, int bm, int bn, bool lower) {
   const long long tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
@@ -1331,6 +1333,15 @@ inline TileCfg pick_tile(int M, int N, int K, int batch, bool lower) {
   const long long mid = (long long)batch * gemm_tiles(M, N, 128, 128, lower);
   const long long small = (long long)batch * gemm_tiles(M, N, 64, 64, lower);
   if (big >= kCUs) return TileCfg::kBig;
+  // Lower-triangle products of n of about 2048: 64 x 64 tiles (528 of them at n =
+  // 2048) fill two workgroups per CU with a tail of 16, and every CU brings 16 KB per
+  // stage per workgroup through its load path for 32 flop/B.  96 x 96 tiles (253 at
+  // n = 2048, three waves of 32 x 96) fill one round at 48 flop/B.  Measured on MI355X:
+  // the n = 2048, K = 2048 product 20.96 against 24.65 us, the Gram NS of a 2048 x 28672
+  // submatrix 1.115-1.119 against 1.176-1.177 ms, bitwise the same result (every
+  // element's k order does not depend on the tile).
+  const long long tri96 = (long long)batch * gemm_tiles(M, N, 96, 96, lower);
+  if (lower && M >= 1792 && small > 2 * kCUs && tri96 <= 2 * kCUs) return TileCfg::kTri96;
   if (mid >= kCUs) return TileCfg::kMid;
   if (K >= kLongK && small > kCUs) return TileCfg::kMid;
   return TileCfg::kSmall;
@@ -1457,6 +1468,12 @@ hipError_t launch_cfg(GemmParams p, int batch, hipStream_t stream, double* flops
                                                                                              flops);
     case TileCfg::kSmall:
       return launch_one<TIn, TB, TOut, 64, 64, 2, 2, kStagesSmall, kBkSmall, LOWER, NN>(p, batch, stream, flops);
+    case TileCfg::kTri96:
+      // 3 stages (72 KB): two workgroups share a CU when a paired launch doubles the grid
+      if constexpr (LOWER && TIn::kBytes == 2)
+        return launch_one<TIn, TB, TOut, 96, 96, 3, 1, kStagesTri96, kBkSmall, LOWER, NN>(p, batch, stream, flops);
+      else
+        return launch_one<TIn, TB, TOut, 64, 64, 2, 2, kStagesSmall, kBkSmall, LOWER, NN>(p, batch, stream, flops);
   }
   return hipErrorInvalidValue;
 }

@@ -53,6 +53,25 @@ def test_symm_gemm_parity(gns_mod, in_dt, out_dt, n, k):
     assert bool((Dh == Dh.transpose(1, 2)).all()), "output not bitwise symmetric"
 
 
+@pytest.mark.parametrize("n,k,batch", [(2000, 200, 1), (2048, 136, 2)])
+def test_symm_gemm_tri96_tiles(gns_mod, n, k, batch):
+    """Lower-triangle products with n of about 2048 run on 96 x 96 tiles (ragged at
+    n = 2000 and 2048: the last tile row holds 80 and 32 rows); the paired-size grid of
+    two matrices takes two workgroups per CU."""
+    announce(f"symm_gemm 96-tiles n={n} k={k} batch={batch}")
+    rng = np.random.default_rng(n + k)
+    a_st, a = stored(rng, (batch, n, k), "f16")
+    b_st, b = stored(rng, (batch, n, k), "f16")
+    c_st, c = stored(rng, (batch, n, n), "f16")
+    A, B, C = to_dev(a_st, "f16"), to_dev(b_st, "f16"), to_dev(c_st, "f16")
+    D = gns_mod.symm_gemm(A, B, C, alpha=0.75, beta=-0.5, gamma=1.25, out_dtype="f16")
+    got = to_f64(D)
+    ref = symm_gemm_ref(a, b, c, alpha=0.75, beta=-0.5, gamma=1.25)
+    check(got, ref, TOL["f16"])
+    Dh = D.cpu()
+    assert bool((Dh == Dh.transpose(1, 2)).all()), "output not bitwise symmetric"
+
+
 @pytest.mark.parametrize("in_dt", ["bf16", "f16", "f32"])
 def test_syrk_same_operand(gns_mod, in_dt):
     announce(f"syrk {in_dt}")
