@@ -1338,8 +1338,9 @@ inline TileCfg pick_tile(int M, int N, int K, int batch, bool lower) {
   // stage per workgroup through its load path for 32 flop/B.  96 x 96 tiles (253 at
   // n = 2048, three waves of 32 x 96) fill one round at 48 flop/B.  Measured on MI355X:
   // the n = 2048, K = 2048 product 20.96 against 24.65 us, the Gram NS of a 2048 x 28672
-  // submatrix 1.115-1.119 against 1.176-1.177 ms, bitwise the same result (every
-  // element's k order does not depend on the tile).
+  // submatrix 1.129-1.133 against 1.194-1.196 ms and the 8192 x 28672 Dion3 step at
+  // f = 1/4 1.466 against 1.531 ms, bitwise the same result (every element's k order
+  // does not depend on the tile).
   const long long tri96 = (long long)batch * gemm_tiles(M, N, 96, 96, lower);
   if (lower && M >= 1792 && small > 2 * kCUs && tri96 <= 2 * kCUs) return TileCfg::kTri96;
   if (mid >= kCUs) return TileCfg::kMid;
