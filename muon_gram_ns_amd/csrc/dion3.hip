@@ -335,26 +335,45 @@ hipError_t launch_topk(const double* score, int batch, int N, int k, int* S, hip
 // ---- X[r] = M[S[r]]; M[S[r]] <- fl(mu * M[S[r]]) -------------------------------------
 // X (state type) holds kx >= k rows per batch entry: rows k .. kx-1 (the padding of the
 // submatrix to a whole number of 8-row groups) are written as zeros.
+// Xh (bf16 state only, nullable): also the fp16 copy fl16(fl32(fl32(hP s[b]) x)) of the
+// same rows, with X's row stride -- the restart product's operand, so that product
+// reads fp16 instead of converting bf16 on every load (the same two roundings as that
+// conversion, so the values are bitwise those it would form).
 template <class T>
 __global__ void __launch_bounds__(kRowThreads)
 gather_feedback_kernel(void* M, int N, int m, long long ld, long long stride, const int* S, int k, int kx,
-                       float mu_host, const float* dev_scalars, void* X, long long ldx) {
+                       float mu_host, const float* dev_scalars, void* X, long long ldx, void* Xh,
+                       const float* hs, float hP) {
   constexpr int E = T::kPerChunk;
+  constexpr bool kHalfCopy = T::kId == GNS_BF16;
   const int r = blockIdx.x, b = blockIdx.y;
   const float mu = dev_scalars ? dev_scalars[2] : mu_host;
   const int src = r < k ? S[(size_t)b * k + r] : -1;
   uint4* xr = row_chunks<T>(X, ((long long)b * kx + r) * ldx);
+  uint4* hr = (kHalfCopy && Xh) ? row_chunks<TF16>(Xh, ((long long)b * kx + r) * ldx) : nullptr;
   const int nch = m / E;
   if (src < 0 || src >= N) {           // padding row, or an index out of range: a zero row of X, M untouched
-    for (int c = threadIdx.x; c < nch; c += kRowThreads) xr[c] = make_uint4(0u, 0u, 0u, 0u);
+    for (int c = threadIdx.x; c < nch; c += kRowThreads) {
+      xr[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (hr) hr[c] = make_uint4(0u, 0u, 0u, 0u);
+    }
     return;
   }
+  const float hmul = hr ? __fmul_rn(hP, hs[b]) : 0.0f;
   uint4* mr = row_chunks<T>(M, (long long)b * stride + (long long)src * ld);
   for (int c = threadIdx.x; c < nch; c += kRowThreads) {
     const uint4 v = load_nt(&mr[c]);
     xr[c] = v;
     float x[E];
     unpack<T>(v, x);
+    if constexpr (kHalfCopy) {
+      if (hr) {
+        float h[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) h[i] = __fmul_rn(x[i], hmul);
+        hr[c] = pack<TF16>(h);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < E; ++i) x[i] = __fmul_rn(mu, x[i]);
     store_nt(pack<T>(x), &mr[c]);
@@ -363,14 +382,15 @@ gather_feedback_kernel(void* M, int N, int m, long long ld, long long stride, co
 
 hipError_t launch_gather_feedback(void* M, gns_dtype dt, int batch, int N, int m, long long ld, long long stride,
                                   const int* S, int k, int kx, float mu, const float* dev_scalars, void* X,
-                                  long long ldx, hipStream_t s) {
+                                  long long ldx, hipStream_t s, void* Xh, const float* hs, float hP) {
   if (k <= 0 || batch <= 0) return hipSuccess;
   if (kx < k) return hipErrorInvalidValue;
+  if (Xh && (dt != GNS_BF16 || !hs)) return hipErrorInvalidValue;
   return with_state_type(dt, [&](auto tag) {
     using T = decltype(tag);
     clear_stale_error();
     hipLaunchKernelGGL(gather_feedback_kernel<T>, dim3(kx, batch), dim3(kRowThreads), 0, s, M, N, m, ld, stride, S,
-                       k, kx, mu, dev_scalars, X, ldx);
+                       k, kx, mu, dev_scalars, X, ldx, Xh, hs, hP);
     return hipGetLastError();
   });
 }

@@ -101,10 +101,13 @@ hipError_t launch_accumulate_score(void* M, const void* G, gns_dtype dt, int bat
 hipError_t launch_topk(const double* score, int batch, int N, int k, int* S, hipStream_t s);
 // dev_scalars (nullable): device float[3] = {lr, wd, mu} read when the kernel runs,
 // replacing the host values.
-// X holds kx >= k rows per batch entry (rows k .. kx-1 are written as zeros).
+// X holds kx >= k rows per batch entry (rows k .. kx-1 are written as zeros).  Xh
+// (bf16 state only, nullable): also written, the fp16 copy fl16(fl32(hP hs[b]) x) of
+// the same rows with X's row stride.
 hipError_t launch_gather_feedback(void* M, gns_dtype dt, int batch, int N, int m, long long ld, long long stride,
                                   const int* S, int k, int kx, float mu, const float* dev_scalars, void* X,
-                                  long long ldx, hipStream_t s);
+                                  long long ldx, hipStream_t s, void* Xh = nullptr, const float* hs = nullptr,
+                                  float hP = 1.0f);
 // O: k rows (row stride ldo, element type o_dtype) per batch entry, entries so
 // elements apart.  Mfb (nullable): also apply the error feedback M[S] <- fl(mu M[S]) to
 // the same rows (M with W's row stride, batch stride and element type).
