@@ -662,12 +662,18 @@ struct Dion3Layout {
 // whose norm is 1 up to the rounding.
 static bool state_casts_x(gns_dtype dt) { return dt == GNS_F32; }
 
-// A bf16 state with fp16 iterates: the gather also writes the selected rows as the
-// fp16 copy P s X that the restart and final products read instead of converting the
-// bf16 rows on every load (the Gram products keep the bf16 rows, so the step stays
-// bitwise the step that reads the rows in place).  Measured on MI355X on the 8192 x
-// 28672 state at f = 1/4: 1.477 against 1.493 ms per step.
-static bool state_half_copy(gns_dtype dt, gns_dtype cdt) { return dt == GNS_BF16 && cdt == GNS_F16; }
+// A bf16 state with fp16 iterates and at least 2048 selected rows: the gather also
+// writes the selected rows as the fp16 copy P s X that the restart and final products
+// read instead of converting the bf16 rows on every load (each 256 x 256 tile row of
+// the product converts them once; the Gram products keep the bf16 rows, so the step
+// stays bitwise the step that reads the rows in place).  Measured on MI355X: the
+// 8192 x 28672 state at k = 2048 1.476 against 1.490 ms per step; at k = 1024 no
+// change; 16 states of 2048 x 8192 at k = 512 0.963 against 0.928 ms, so fewer rows
+// keep the conversion.
+constexpr int kHalfCopyMinRows = 2048;
+static bool state_half_copy(gns_dtype dt, gns_dtype cdt, int kp) {
+  return dt == GNS_BF16 && cdt == GNS_F16 && kp >= kHalfCopyMinRows;
+}
 
 // The selected submatrix is held with kp = k rounded up to a multiple of 8 rows; the
 // extra rows are zero.  Zero rows leave the iteration's result on the other rows
@@ -685,7 +691,7 @@ static Dion3Layout dion3_layout(void* base, int batch, int N, int m, int k, gns_
   L.s = (float*)c.take(sizeof(float) * B);
   L.X = c.take(B * kp * m * esize(dt));
   L.Xc = state_casts_x(dt) ? c.take(B * kp * m * esize(cdt)) : nullptr;
-  L.Xh = state_half_copy(dt, cdt) ? c.take(B * kp * m * 2) : nullptr;
+  L.Xh = state_half_copy(dt, cdt, kp) ? c.take(B * kp * m * 2) : nullptr;
   L.O = c.take(B * kp * m * esize(dt));
   L.gns_bytes = ns_workspace_bytes(batch, kp, m, cdt);
   L.gns_ws = c.take(L.gns_bytes);

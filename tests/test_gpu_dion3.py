@@ -531,7 +531,8 @@ def _step_bits(gns_mod, w, g, m, k, lr, wd, norm, compute, in_place, batched=Fal
     return S.cpu().numpy(), bits(O), bits(W), bits(M)
 
 
-@pytest.mark.parametrize("case", ["small_wd", "k125_bf16", "long_k_split", "batched", "caller_rows", "dev_scalars"])
+@pytest.mark.parametrize("case", ["small_wd", "k125_bf16", "long_k_split", "batched", "caller_rows", "dev_scalars",
+                                  "k2047_half_copy"])
 def test_dion3_rows_in_place_bitwise_equal(gns_mod, case):
     """rows_in_place = 1 (the Gram products read M[S, :] through the row list, the
     error feedback runs with the update) gives bitwise the step of the default path
@@ -549,6 +550,11 @@ def test_dion3_rows_in_place_bitwise_equal(gns_mod, case):
     elif case == "batched":
         sts = [synth.dion3_state(n=512, m=2048, seed=93 + b) for b in range(2)]
         w, g, m = ([st[i] for st in sts] for i in range(3))
+    elif case == "k2047_half_copy":
+        # 2048 padded rows: the gathered path also writes the fp16 copy that the restart
+        # and final products read; reading the rows in place converts them on load
+        w, g, m = synth.dion3_state(n=4096, m=4096, seed=98)
+        kw.update(k=2047)
     elif case == "caller_rows":
         w, g, m = synth.dion3_state(n=256, m=1024, seed=95)
         rows = np.append(np.sort(np.random.default_rng(96).choice(256, size=23, replace=False)), 256)

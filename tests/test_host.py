@@ -111,9 +111,14 @@ def test_gemm_and_dion3_validation():
     assert L.dion3_step(*args(16, wsb=8, dt=F32)) == WS
     assert L.dion3_step(*args(16, dt=7)) == INVALID
     assert L.dion3_workspace_size(64, 256, 16, F32, F16) > L.dion3_workspace_size(64, 256, 16, BF16, F16)
-    # a bf16 state with fp16 iterates also holds the fp16 copy of the selected rows
-    assert L.dion3_workspace_size(64, 256, 16, BF16, F16) == L.dion3_workspace_size(64, 256, 16, F16, F16) + 16 * 256 * 2
-    assert L.dion3_workspace_size(64, 256, 16, F16, BF16) == L.dion3_workspace_size(64, 256, 16, BF16, BF16)
+    assert L.dion3_workspace_size(64, 256, 16, F16, F16) == L.dion3_workspace_size(64, 256, 16, BF16, F16)
+    # with at least 2048 selected rows a bf16 state with fp16 iterates also holds the
+    # fp16 copy of the selected rows
+    assert (L.dion3_workspace_size(4096, 256, 2048, BF16, F16)
+            == L.dion3_workspace_size(4096, 256, 2048, F16, F16) + 2048 * 256 * 2)
+    assert L.dion3_workspace_size(4096, 256, 2047, BF16, F16) == L.dion3_workspace_size(4096, 256, 2047, F16, F16) \
+        + 2048 * 256 * 2
+    assert L.dion3_workspace_size(4096, 256, 2040, BF16, F16) == L.dion3_workspace_size(4096, 256, 2040, F16, F16)
     assert L.dion3_workspace_size(64, 256, 16, 7, F16) == 0
     # batched dion3: empty batch, short batch stride, aliased state, short workspace
     bargs = lambda B, stride, W=FAKE, M=FAKE * 8, G=FAKE * 16, wsb=1 << 40: (
