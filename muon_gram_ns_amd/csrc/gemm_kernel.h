@@ -25,8 +25,9 @@
 
 namespace gns {
 
+// (the hardware square root is within an ulp or two; the loops correct the estimate)
 __device__ __forceinline__ void tri_decode(int t, int& i, int& j) {
-  int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+  int r = (int)((__builtin_amdgcn_sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
   while ((r + 1) * (r + 2) / 2 <= t) ++r;
   while (r * (r + 1) / 2 > t) --r;
   i = r;
@@ -58,8 +59,10 @@ __device__ __forceinline__ void lower_tile_grouped(int t, int tiles, int G, int&
   int idx = t - R0 * (R0 + 1) / 2;
   const int full = (R0 + 1) * gm;
   if (idx < full) {
-    tn = idx / gm;
-    tm = R0 + idx % gm;
+    // a whole group (every one but possibly the last) divides by the constant G
+    const int q = gm == G ? idx / G : idx / gm;
+    tn = q;
+    tm = R0 + idx - q * gm;
   } else {
     idx -= full;
     int k = 1;
@@ -194,27 +197,39 @@ struct EpiPtrs {
 };
 
 // The Frobenius scale of batch entry bz from its partial sums of squares (at most
-// 1024): lane l adds partials l, l + 64, ... in order (16 independent loads, one
-// latency), then an xor butterfly, whose result is bitwise the same in every lane
-// (each level adds the same two values in either order), so every wave and
-// workgroup forms the same s.  1 when the launch has no partials.
+// 1024): lane l adds partials l, l + 64, ... in order, then an xor butterfly, whose
+// result is bitwise the same in every lane (each level adds the same two values in
+// either order), so every wave and workgroup forms the same s.  The loads are split
+// from the sum so a kernel can issue them first and form s after its k-loop: all 16
+// are issued at once, without branches (indices past n_partials load the last partial
+// and count as zero).
 constexpr int kMaxPartials = 1024;
-__device__ __forceinline__ float scale_from_partials(const GemmParams& p, int bz) {
-  if (!p.partials) return 1.0f;
+constexpr int kPartialsPerLane = kMaxPartials / 64;
+__device__ __forceinline__ void load_partials(const GemmParams& p, int bz, float (&v)[kPartialsPerLane]) {
   const int lane = threadIdx.x & 63;
   const float* q = p.partials + (size_t)bz * p.n_partials;
-  float v[kMaxPartials / 64];
 #pragma unroll
-  for (int r = 0; r < kMaxPartials / 64; ++r) {
-    const int i = lane + 64 * r;
-    v[r] = i < p.n_partials ? q[i] : 0.0f;
-  }
+  for (int r = 0; r < kPartialsPerLane; ++r) v[r] = q[min(lane + 64 * r, p.n_partials - 1)];
+}
+__device__ __forceinline__ float scale_of_partials(const GemmParams& p, const float (&v)[kPartialsPerLane]) {
+  const int lane = threadIdx.x & 63;
   float t = 0.f;
 #pragma unroll
-  for (int r = 0; r < kMaxPartials / 64; ++r) t += v[r];
+  for (int r = 0; r < kPartialsPerLane; ++r) t += lane + 64 * r < p.n_partials ? v[r] : 0.0f;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
   return 1.0f / (sqrtf(t) + p.eps);
+}
+// 1 when the launch has no partials
+__device__ __forceinline__ float scale_from_partials(const GemmParams& p, int bz) {
+  if (!p.partials) return 1.0f;
+  float v[kPartialsPerLane];
+  load_partials(p, bz, v);
+  return scale_of_partials(p, v);
+}
+// tile 0 of each batch entry publishes the scale (read by later launches only)
+__device__ __forceinline__ void publish_scale(const GemmParams& p, int bz, int tile, bool second, float psc) {
+  if (p.partials && p.s_out && !second && tile == 0 && threadIdx.x == 0) p.s_out[bz] = psc;
 }
 
 template <class TOut>
@@ -237,27 +252,40 @@ __device__ __forceinline__ EpiPtrs epi_ptrs(const GemmParams& p, int bz, bool se
 
 // Flat workgroup id -> (batch entry, second product of a pair, tile), with the XCD
 // remap applied over all batch * tiles (* 2 for a pair) workgroups; psc is the scale
-// formed from partial sums (1 without).
+// formed from partial sums (1 without; with_scale false leaves it to the caller).
+// The divisions by run-time counts are skipped when there is one K range or one
+// (batch entry, product), the common cases.
 struct GridPos {
   int bz, tile, ks;     // ks: K range of a split partial launch (0 otherwise)
   bool second;
   float psc;
 };
-__device__ __forceinline__ GridPos grid_pos(const GemmParams& p) {
+__device__ __forceinline__ GridPos grid_pos(const GemmParams& p, bool with_scale = true) {
   const int splits = (p.ksplit > 1 && !p.reduce) ? p.ksplit : 1;
-  const int total = p.batch * p.tiles * (p.pair ? 2 : 1) * splits;
+  const int entries = p.batch * (p.pair ? 2 : 1);
+  const int total = entries * p.tiles * splits;
   const int rid0 = xcd_remap((int)blockIdx.x, total);
   GridPos g;
-  g.ks = __builtin_amdgcn_readfirstlane(rid0 % splits);
-  const int rid = rid0 / splits;
-  int bz = __builtin_amdgcn_readfirstlane(rid / p.tiles);
-  g.tile = __builtin_amdgcn_readfirstlane(rid - bz * p.tiles);
+  int rid = rid0;
+  g.ks = 0;
+  if (splits > 1) {
+    g.ks = __builtin_amdgcn_readfirstlane(rid0 % splits);
+    rid = rid0 / splits;
+  }
+  int bz = 0;
+  g.tile = rid;
+  if (entries > 1) {
+    bz = __builtin_amdgcn_readfirstlane(rid / p.tiles);
+    g.tile = __builtin_amdgcn_readfirstlane(rid - bz * p.tiles);
+  }
   g.second = p.pair && bz >= p.batch;
   if (g.second) bz -= p.batch;
   g.bz = bz;
-  g.psc = scale_from_partials(p, bz);
-  // tile 0 of each batch entry publishes the scale (read by later launches only)
-  if (p.partials && p.s_out && !g.second && g.tile == 0 && threadIdx.x == 0) p.s_out[bz] = g.psc;
+  g.psc = 1.0f;
+  if (with_scale) {
+    g.psc = scale_from_partials(p, bz);
+    publish_scale(p, bz, g.tile, g.second, g.psc);
+  }
   return g;
 }
 
@@ -850,9 +878,18 @@ gemm16_kernel(GemmParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  // block-level indices are uniform; readfirstlane keeps them in scalar registers
-  const GridPos gp = grid_pos(p);
+  // block-level indices are uniform; readfirstlane keeps them in scalar registers.
+  // The Frobenius scale of a product with partial sums only enters the epilogue: up
+  // to 128 x 128 tiles its loads are issued here and s is formed after the k-loop
+  // (the 256 x 256 tile has no registers to spare and forms it first).
+  constexpr bool kDeferScale = BM <= 128;
+  GridPos gp = grid_pos(p, !kDeferScale);
   const int bz = gp.bz, tile = gp.tile;
+  const bool defer_scale = kDeferScale && p.partials != nullptr && !(p.ksplit > 1 && !p.reduce);
+  float pv[kDeferScale ? kPartialsPerLane : 1];
+  if constexpr (kDeferScale) {
+    if (defer_scale) load_partials(p, bz, pv);
+  }
   int tm, tn;
   constexpr int kGroup = BM >= 256 ? 4 : 8;
   if constexpr (LOWER) {
@@ -1252,6 +1289,13 @@ gemm16_kernel(GemmParams p) {
     return;
   }
 
+  if constexpr (kDeferScale) {
+    if (defer_scale) {
+      gp.psc = scale_of_partials(p, pv);
+      publish_scale(p, bz, tile, gp.second, gp.psc);
+    }
+  }
+
   // every wave is done with the operand ring: reuse it for the epilogue slabs
   static_assert(NW * 32 * (Cfg::kWN + 4) * 4 <= Cfg::kLdsBytes, "epilogue slabs exceed the LDS ring");
   lds_barrier();
@@ -1348,6 +1392,14 @@ inline TileCfg pick_tile(int M, int N, int K, int batch, bool lower) {
   return TileCfg::kSmall;
 }
 
+// hi/lo plane pairs anywhere in the product
+inline bool any_planes(const GemmParams& p) {
+  bool planes = false;
+  for (int v : {p.a_planes, p.a2_planes, p.b_planes, p.c_planes, p.c2_planes, p.d_planes, p.dp_planes})
+    planes = planes || v != 1;
+  return planes;
+}
+
 constexpr double kNonTemporalOutBytes = 128.0 * (1 << 20);
 
 template <class TIn, class TB, class TOut, int BM, int BN, int WM_, int WN_, int NS, int BKV, bool LOWER, bool NN>
@@ -1382,9 +1434,7 @@ hipError_t launch_one(GemmParams p, int batch, hipStream_t stream, double* flops
   }
   // hi/lo planes: a separate instantiation (bf16 symmetric products only), so the
   // single-plane kernels carry none of its address arithmetic
-  bool planes = false;
-  for (int v : {p.a_planes, p.a2_planes, p.b_planes, p.c_planes, p.c2_planes, p.d_planes, p.dp_planes})
-    planes = planes || v != 1;
+  const bool planes = any_planes(p);
   // indexed X rows: separate instantiations too -- the Gram product of bf16 rows
   // (symmetric, planes handled when the output is bf16) and the rectangular product
   // with bf16 B rows, whose row table takes LDS after the ring
