@@ -417,6 +417,29 @@ def sync_timed_ms(torch, fn, steps, warmup):
     return 1e3 * (time.perf_counter() - t0) / steps
 
 
+def square_gemm_reference(gns, torch, batch, n, steps, warmup):
+    """The n x n x n products of the square batch on their own: this library's
+    rectangular kernel and torch.bmm (the vendor's GEMM library) on the same contiguous
+    fp16 operands, timed alike, so the MFMA fraction has a reference on this machine."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4096)
+    A = (torch.randn(batch, n, n, device="cuda", generator=g) * n ** -0.5).half()
+    Bm = torch.randn(batch, n, n, device="cuda", generator=g).half()
+    D = torch.empty_like(A)
+    flops = 2.0 * batch * float(n) ** 3
+
+    def fig(ms):
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"ms": round(ms, 4), "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_16BIT_TFLOPS, 2)}
+
+    lib = fig(sync_timed_ms(torch, lambda: gns.rect_gemm(A, Bm, out=D), steps, warmup))
+    vendor = fig(sync_timed_ms(torch, lambda: torch.bmm(A, Bm, out=D), steps, warmup))
+    del A, Bm, D
+    torch.cuda.empty_cache()
+    return {"shape": f"{batch} x ({n} x {n}) @ ({n} x {n}), fp16 in and out, fp32 accumulation",
+            "library_rect_gemm": lib, "torch_bmm": vendor}
+
+
 def other_workloads(args, gns, F, torch, np, synth):
     """The other configurations, timed in the same run as the default line so that their
     figures are observed by the same driver run: the 32 x 4096^2 square batch (the pages'
@@ -460,6 +483,7 @@ def other_workloads(args, gns, F, torch, np, synth):
             entry["mfma_goal"] = {"pct_of_peak": 60.0, "pct_peak_issued": best, "met": best >= 60.0,
                                   "note": "goal for n >= 4096: 60% of the dense fp16/bf16 MFMA peak; under load "
                                           "these products run at about 1.6 GHz with the MFMA pipe 61-67% busy"}
+            entry["gemm_reference"] = square_gemm_reference(gns, torch, B, n, steps, warm)
         if n == m:
             entry["default_call"] = ("standard NS: at aspect ratio 1 the Gram form saves nothing and the pages fall "
                                      "back to kernelized standard NS (square_fallback = 1); gram_ns is the Gram "
