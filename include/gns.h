@@ -330,8 +330,10 @@ size_t muon_workspace_size(int batch, int n, int m, gns_dtype dt, gns_dtype comp
  *   U  = G + mu M  with nesterov = 1  (lookahead on the updated M); U = M with 0
  *   O  = GramNS(U)                    (the schedule and iterate dtype of
  *                                      gns_orthogonalize_batched; a tall U runs on U^T;
- *                                      ||U||_F from fp64 row sums formed in the
- *                                      momentum pass)
+ *                                      ||U||_F from row sums of squares formed in
+ *                                      the momentum pass: fp64, rounded to fp32
+ *                                      partial sums of the Gram product for a
+ *                                      16-bit state with n <= 1024)
  *   W <- (1 - lr weight_decay) W - lr scale O   (decoupled decay first, in place)
  * scale == 0 selects 0.2 sqrt(max(n, m)) (fp32), which matches the update's RMS to
  * AdamW's; a negative scale is GNS_ERR_INVALID_ARG.  Dion3 with every row selected is

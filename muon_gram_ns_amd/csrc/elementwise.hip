@@ -93,15 +93,20 @@ hipError_t launch_frob_partials(const void* X, gns_dtype dt, long long ldx, long
   return hipGetLastError();
 }
 
+hipError_t launch_frob_finish(const float* partials, int P, int batch, float eps, float* s_out, hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  clear_stale_error();
+  hipLaunchKernelGGL(frob_finish_kernel, dim3(batch), dim3(kRedThreads), 0, stream, partials, P, eps, s_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_frob(const void* X, gns_dtype dt, long long ldx, long long stride_x, int batch, int n,
                        int m, float eps, float* s_out, float* partials, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
   const int P = frob_partials_per_batch(n, m);
   hipError_t e = launch_frob_partials(X, dt, ldx, stride_x, batch, n, m, partials, stream);
   if (e != hipSuccess) return e;
-  clear_stale_error();
-  hipLaunchKernelGGL(frob_finish_kernel, dim3(batch), dim3(kRedThreads), 0, stream, partials, P, eps, s_out);
-  return hipGetLastError();
+  return launch_frob_finish(partials, P, batch, eps, s_out, stream);
 }
 
 // ---- scaled cast: Y = mul * scale[b]^pow * X, converted element by element --------

@@ -203,7 +203,6 @@ struct EpiPtrs {
 // from the sum so a kernel can issue them first and form s after its k-loop: all 16
 // are issued at once, without branches (indices past n_partials load the last partial
 // and count as zero).
-constexpr int kMaxPartials = 1024;
 constexpr int kPartialsPerLane = kMaxPartials / 64;
 __device__ __forceinline__ void load_partials(const GemmParams& p, int bz, float (&v)[kPartialsPerLane]) {
   const int lane = threadIdx.x & 63;

@@ -124,6 +124,10 @@ struct NsCall {
   hipStream_t stream;
   double* flops;
   const float* s_given;   // precomputed device scale (Dion3), or null
+  // partial sums of squares of each entry already formed on the device (the Muon
+  // momentum pass's row sums), [batch][n_partials_given], n_partials_given <=
+  // kMaxPartials: they replace the Frobenius pass over X; null when absent
+  const float* partials_given; int n_partials_given;
   // X read through a row table (Dion3's selected rows, straight from the state): row r
   // of entry b is source row rows[b * rows_stride + r] of the state at X (rows r >=
   // rows_valid are zero rows); only the Gram path of a wide call reads X this way
@@ -216,7 +220,8 @@ int run_gram(const NsCall& c) {
   const float P = pow2_scale(c.cdt, n, m);
   const gns_dtype cdt = c.cdt;
   const float* s = c.s_given ? c.s_given : L.s;
-  if (!c.s_given) HIP_OK(launch_frob_partials(c.X, c.xdt, c.ldx, c.sx, B, n, m, L.partials, c.stream));
+  if (!c.s_given && !c.partials_given)
+    HIP_OK(launch_frob_partials(c.X, c.xdt, c.ldx, c.sx, B, n, m, L.partials, c.stream));
   // planes of one symmetric product: A, B, C, D of the chain (R, Z, Y) carry pl planes
   auto chain = [&](GemmParams& g, int a, int b, int cpl, int d) {
     g.plane = nn;
@@ -237,7 +242,9 @@ int run_gram(const NsCall& c) {
     if (c.s_given) {
       g.scale = s;
     } else {
-      g.partials = L.partials; g.n_partials = frob_partials_per_batch(n, m); g.eps = c.sch.eps; g.s_out = L.s;
+      g.partials = c.partials_given ? c.partials_given : L.partials;
+      g.n_partials = c.partials_given ? c.n_partials_given : frob_partials_per_batch(n, m);
+      g.eps = c.sch.eps; g.s_out = L.s;
     }
     HIP_OK(launch_symm_ws(c.xdt, cdt, g, B, L.part, L.part_bytes, c.stream, c.flops));
   }
@@ -338,7 +345,10 @@ int run_standard(const NsCall& c) {
   const long long nn = (long long)n * n, nm = (long long)n * m;
   const float P = pow2_scale(c.cdt, n, m);
   const float* s = c.s_given ? c.s_given : L.s;
-  if (!c.s_given) HIP_OK(launch_frob(c.X, c.xdt, c.ldx, c.sx, B, n, m, c.sch.eps, L.s, L.partials, c.stream));
+  if (!c.s_given && c.partials_given)
+    HIP_OK(launch_frob_finish(c.partials_given, c.n_partials_given, B, c.sch.eps, L.s, c.stream));
+  else if (!c.s_given)
+    HIP_OK(launch_frob(c.X, c.xdt, c.ldx, c.sx, B, n, m, c.sch.eps, L.s, L.partials, c.stream));
   HIP_OK(launch_cast_scale(c.X, c.xdt, c.ldx, c.sx, L.Sa, c.cdt, m, nm, B, n, m, P, s, 1, c.stream));
   void* cur = L.Sa; void* nxt = L.Sb;
   for (int t = 1; t <= c.sch.steps; ++t) {
@@ -391,6 +401,7 @@ NsCall make_call(const void* X, gns_dtype xdt, long long ldx, long long sx, void
   c.batch = batch; c.n = n; c.m = m; c.cdt = cdt;
   if (sched) c.sch = *sched; else gns_default_schedule(&c.sch);
   c.ws = ws; c.ws_bytes = ws_bytes; c.stream = stream; c.flops = flops; c.s_given = nullptr;
+  c.partials_given = nullptr; c.n_partials_given = 0;
   c.rows = nullptr; c.rows_valid = 0; c.src_rows = 0; c.rows_stride = 0;
   c.Xh = nullptr; c.ldxh = 0; c.sxh = 0;
   return c;
@@ -935,6 +946,7 @@ int dion3_step_rows(void* W, void* M, const void* G, gns_dtype dt, int N, int m,
 // workspace of the batch.
 struct MuonLayout {
   double* rowsq;
+  float* rowsq32;        // the row sums rounded to fp32: the Gram products' partial sums
   float* s;
   void *U, *Xc, *O, *gns_ws;
   size_t gns_bytes, bytes;
@@ -945,6 +957,7 @@ static MuonLayout muon_layout(void* base, int batch, int n, int m, gns_dtype dt,
   MuonLayout L{};
   const size_t elems = (size_t)batch * n * m;
   L.rowsq = (double*)c.take(sizeof(double) * (size_t)batch * n);
+  L.rowsq32 = (float*)c.take(sizeof(float) * (size_t)batch * n);
   L.s = (float*)c.take(sizeof(float) * (size_t)batch);
   L.U = nesterov ? c.take(elems * esize(dt)) : nullptr;
   L.Xc = state_casts_x(dt) ? c.take(elems * esize(cdt)) : nullptr;
@@ -1007,15 +1020,25 @@ int muon_step_batched(void* W, void* M, const void* G, gns_dtype dt, int batch, 
                                 L.gns_bytes, stream, nullptr)
                     : make_call(src, dt, lds, ss, O, dt, m, nm, batch, n, m, compute, &sch, L.gns_ws, L.gns_bytes,
                                 stream, nullptr);
-  // the momentum pass also forms each matrix's Frobenius scale
-  c.s_given = cast_x ? nullptr : L.s;
+  // The momentum pass also forms what the Frobenius scale needs: for a 16-bit state
+  // its row sums (at most kMaxPartials rows) are the Gram products' partial sums, so
+  // no pass over U and no scale launch precede Gram NS; otherwise it forms the scale
+  // itself (an fp32 state's 16-bit copy is scaled by it).
+  const bool rows_as_partials = !cast_x && n <= kMaxPartials;
+  c.s_given = (cast_x || rows_as_partials) ? nullptr : L.s;
+  if (rows_as_partials) {
+    c.partials_given = L.rowsq32;
+    c.n_partials_given = n;
+  }
   if ((st = check_ns(c))) return st;
   const size_t o_bytes = (size_t)batch * nm * es;
   if (O_out && (overlaps(O_out, o_bytes, workspace, L.bytes) || overlaps(O_out, o_bytes, W, span) ||
                 overlaps(O_out, o_bytes, M, span) || overlaps(O_out, o_bytes, G, span)))
     return GNS_ERR_INVALID_ARG;
 
-  HIP_OK(launch_muon_momentum(M, G, dt, batch, n, m, ld, stride, mu, L.U, m, nm, L.rowsq, sch.eps, L.s, stream));
+  HIP_OK(launch_muon_momentum(M, G, dt, batch, n, m, ld, stride, mu, L.U, m, nm, L.rowsq,
+                              rows_as_partials ? L.rowsq32 : nullptr, sch.eps, rows_as_partials ? nullptr : L.s,
+                              stream));
   if (cast_x) HIP_OK(launch_cast_scale(src, dt, lds, ss, L.Xc, compute, m, nm, batch, n, m, 1.0f, L.s, 1, stream));
   if ((st = run_ns(c, true))) return st;
   HIP_OK(launch_muon_update(W, dt, batch, n, m, ld, stride, O, m, nm, lr, weight_decay, sc, stream));

@@ -72,6 +72,10 @@ bool rect_pair_supported(gns_dtype a, gns_dtype b);
 
 // Frobenius scale: partial sums of squares, then s[b] = 1 / (sqrt(sum) + eps).
 int frob_partials_per_batch(int n, int m);
+// at most this many partial sums per batch entry feed a Gram product's Frobenius scale
+constexpr int kMaxPartials = 1024;
+// s_out[b] = 1 / (sqrt(sum of the P partials of entry b) + eps)
+hipError_t launch_frob_finish(const float* partials, int P, int batch, float eps, float* s_out, hipStream_t stream);
 hipError_t launch_frob(const void* X, gns_dtype dt, long long ldx, long long stride_x, int batch,
                        int n, int m, float eps, float* s_out, float* partials, hipStream_t stream);
 // ... only the partial sums (frob_partials_per_batch of them per batch entry), for a

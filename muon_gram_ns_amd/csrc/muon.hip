@@ -51,11 +51,12 @@ __device__ __forceinline__ double muon_block_sum(double v, double* sh) {
 // M' = fl(fl32(mu M) + G);  U = fl(G + fl32(mu M')) when U is given.  M and G share
 // the row stride ld and matrix stride; U is [batch][n][ldu].  rowsq[b][r] receives the
 // fp64 sum of squares of row r of the matrix the orthogonalisation reads (U, or M'
-// without the lookahead), so its Frobenius norm needs no further pass.
+// without the lookahead), so its Frobenius norm needs no further pass over it; rowsq32
+// (when non-null) the same sums rounded to fp32.
 template <class T>
 __global__ void __launch_bounds__(kMuonThreads)
 muon_momentum_kernel(void* M, const void* G, int n, int m, long long ld, long long stride, float mu, void* U,
-                     long long ldu, long long su, double* rowsq) {
+                     long long ldu, long long su, double* rowsq, float* rowsq32) {
   constexpr int E = T::kPerChunk;
   __shared__ double sh[kMuonThreads / 64];
   const int r = blockIdx.x, b = blockIdx.y;
@@ -88,7 +89,10 @@ muon_momentum_kernel(void* M, const void* G, int n, int m, long long ld, long lo
     }
   }
   const double t = muon_block_sum(acc, sh);
-  if (threadIdx.x == 0) rowsq[(size_t)b * n + r] = t;
+  if (threadIdx.x == 0) {
+    rowsq[(size_t)b * n + r] = t;
+    if (rowsq32) rowsq32[(size_t)b * n + r] = (float)t;
+  }
 }
 
 // s[b] = 1 / (sqrt(sum_r rowsq[b][r]) + eps), one workgroup per matrix; each thread
@@ -108,15 +112,15 @@ muon_scale_kernel(const double* rowsq, int n, float eps, float* s) {
 
 hipError_t launch_muon_momentum(void* M, const void* G, gns_dtype dt, int batch, int n, int m, long long ld,
                                 long long stride, float mu, void* U, long long ldu, long long su, double* rowsq,
-                                float eps, float* s_out, hipStream_t s) {
+                                float* rowsq32, float eps, float* s_out, hipStream_t s) {
   if (batch <= 0 || n <= 0) return hipSuccess;
   return with_state_type(dt, [&](auto tag) {
     using T = decltype(tag);
     clear_stale_error();
     hipLaunchKernelGGL(muon_momentum_kernel<T>, dim3(n, batch), dim3(kMuonThreads), 0, s, M, G, n, m, ld, stride,
-                       mu, U, ldu, su, rowsq);
+                       mu, U, ldu, su, rowsq, rowsq32);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !s_out) return e;
     hipLaunchKernelGGL(muon_scale_kernel, dim3(batch), dim3(kMuonThreads), 0, s, rowsq, n, eps, s_out);
     return hipGetLastError();
   });
