@@ -880,7 +880,8 @@ gemm16_kernel(GemmParams p) {
   // block-level indices are uniform; readfirstlane keeps them in scalar registers.
   // The Frobenius scale of a product with partial sums only enters the epilogue: up
   // to 128 x 128 tiles its loads are issued here and s is formed after the k-loop
-  // (the 256 x 256 tile has no registers to spare and forms it first).
+  // (the 256 x 256 tile forms it first: a microsecond of setup is small beside its
+  // products, and its registers stay for the ping-pong schedule).
   constexpr bool kDeferScale = BM <= 128;
   GridPos gp = grid_pos(p, !kDeferScale);
   const int bz = gp.bz, tile = gp.tile;
