@@ -36,8 +36,12 @@ def w_within_bound(w_gpu_bits, w_ref_bits, lr_eff, o_ref, o_tol=2e-2):
 
 @pytest.mark.parametrize("B,n,m,nesterov,wd", [(1, 64, 256, True, 0.0), (3, 136, 200, False, 0.1),
                                               (2, 256, 64, True, 0.1), (1, 1024, 4096, True, 0.0),
-                                              (2, 256, 256, True, 0.1), (2, 256, 256, False, 0.0)])
+                                              (2, 256, 256, True, 0.1), (2, 256, 256, False, 0.0),
+                                              (1, 1032, 512, True, 0.1)])
 def test_muon_step_matches_oracle(gns_mod, B, n, m, nesterov, wd):
+    """Shapes cover the Gram path fed by the momentum pass's row sums (n <= 1024: wide,
+    tall through the transpose, square through standard NS) and, at n = 1032, the
+    separate scale launch."""
     announce(f"muon step B={B} {n}x{m} nesterov={nesterov} wd={wd}")
     w, g, mo = states(B, n, m, seed=200 + n)
     lr, mu = 0.02, 0.95
