@@ -142,6 +142,38 @@ def test_rect_gemm_tile_configs(gns_mod, batch, n, k, m, expect):
         check(to_f64(D[i]), rect_gemm_ref(a[i], bc, alpha=2.0), TOL["f32"])
 
 
+@pytest.mark.parametrize("out_dt", ["f16", "bf16"])
+def test_epilogue_paths_agree_bitwise(gns_mod, out_dt):
+    """The epilogue of the 64 x 64 tiles (C loaded before the k-loop, one fragment row
+    per wave) and that of the 128 x 128 tiles (C loaded in the epilogue, two fragment
+    rows) form the same values: the same matrices in a batch large enough for 128 x 128
+    tiles give bitwise the same output, with C, beta and gamma (symmetric) and with C
+    and beta (rectangular)."""
+    import torch
+    announce(f"epilogue paths {out_dt}")
+    rng = np.random.default_rng(520)
+    n, k, m = 520, 136, 1032
+    a_st, a = stored(rng, (1, n, k), "f16")
+    b_st, b = stored(rng, (1, n, k), "f16")
+    c_st, c = stored(rng, (1, n, n), out_dt)
+    r_st, r = stored(rng, (1, k, m), "f16")
+    e_st, e = stored(rng, (1, n, m), out_dt)
+    A, B, C = to_dev(a_st, "f16"), to_dev(b_st, "f16"), to_dev(c_st, out_dt)
+    Rb, E = to_dev(r_st, "f16"), to_dev(e_st, out_dt)
+    D = gns_mod.symm_gemm(A, B, C, alpha=0.75, beta=-0.5, gamma=1.25, out_dtype=out_dt)      # 45 tiles of 64
+    check(to_f64(D[0]), symm_gemm_ref(a[0], b[0], c[0], alpha=0.75, beta=-0.5, gamma=1.25), TOL[out_dt])
+    D18 = gns_mod.symm_gemm(A.repeat(18, 1, 1), B.repeat(18, 1, 1), C.repeat(18, 1, 1), alpha=0.75, beta=-0.5,
+                            gamma=1.25, out_dtype=out_dt)                                    # 270 tiles of 128
+    assert all(torch.equal(D18[i].view(torch.int16), D[0].view(torch.int16)) for i in (0, 17))
+    Dh = D.cpu()
+    assert bool((Dh == Dh.transpose(1, 2)).all())
+    F = gns_mod.rect_gemm(A, Rb, E, alpha=1.5, beta=0.25, out_dtype=out_dt)                 # 9 x 17 tiles of 64
+    check(to_f64(F[0]), rect_gemm_ref(a[0], r[0], e[0], alpha=1.5, beta=0.25), TOL[out_dt])
+    F6 = gns_mod.rect_gemm(A.repeat(6, 1, 1), Rb.repeat(6, 1, 1), E.repeat(6, 1, 1), alpha=1.5, beta=0.25,
+                           out_dtype=out_dt)                                                 # 6 x 45 tiles of 128
+    assert all(torch.equal(F6[i].view(torch.int16), F[0].view(torch.int16)) for i in (0, 5))
+
+
 def test_binding_rejects_operands_the_abi_cannot_check(gns_mod):
     """C in a dtype other than the output's (or a wrongly shaped output) is refused
     by the binding before any launch: the ABI only receives raw pointers."""
